@@ -1,0 +1,147 @@
+"""Seeded synthetic inputs for the decode-attention step.
+
+This module is shared by the GPU path's tests and bench and by the CPU
+oracle's tests.  It only draws random numbers and lays them out; it contains
+none of the attention arithmetic, so neither side can lean on the other
+through it.
+
+Recipe (the same for every workload):
+  * one ``torch.Generator`` on the generating device, seeded with the
+    workload's seed;
+  * draw order: sequence lengths (ragged workloads only), then q, then K,
+    then V;
+  * q, K and V are drawn as float32 N(0, 1) and rounded to bfloat16 with
+    round-to-nearest-even (``Tensor.to(torch.bfloat16)``);
+  * an optional power-of-two multiplier on q (exact in bfloat16) makes the
+    softmax peaky;
+  * ragged lengths are iid uniform integers in ``[len_lo, len_hi]``, both ends
+    included; the cache is allocated at ``Lmax`` regardless;
+  * optionally the padding (positions >= the sequence's length) is poisoned
+    with the bfloat16 quiet-NaN pattern 0x7FC0 so that any read of it shows.
+
+The same seed on a different device yields different (but equally valid)
+numbers; a test that compares two implementations always hands both the same
+tensors, copied if needed, never two separate draws.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import torch
+
+BF16_QNAN_BITS = 0x7FC0
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape and input distribution of one decode step."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    Lmax: int
+    seed: int
+    len_lo: int | None = None   # None: every sequence has length Lmax
+    len_hi: int | None = None
+    q_mult: float = 1.0
+    description: str = ""
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(D), rounded to float32 (the value the library receives)."""
+        return float(torch.tensor(1.0 / math.sqrt(self.D), dtype=torch.float32))
+
+    @property
+    def ragged(self) -> bool:
+        return self.len_lo is not None
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five decode workloads.  Shapes follow the attention shapes the source
+# pages discuss: PaLM 540B multiquery attention (48 query heads sharing one
+# 256-wide key/value head), a 70B-class grouped-query model (64 query heads,
+# 8 key/value heads, head size 128), a ragged batch, and a long-context MQA
+# case that forces the sequence axis to be split.
+WORKLOADS: dict[str, Workload] = {
+    "tiny": Workload("tiny", B=1, Hq=8, Hkv=1, D=64, Lmax=128, seed=0,
+                     description="tiny MQA decode B=1 Hq=8 Hkv=1 D=64 len=128"),
+    "palm": Workload("palm", B=64, Hq=48, Hkv=1, D=256, Lmax=2048, seed=1,
+                     description="PaLM-540B-shaped MQA decode B=64 Hq=48 Hkv=1 D=256 len=2048"),
+    "gqa70b": Workload("gqa70b", B=32, Hq=64, Hkv=8, D=128, Lmax=4096, seed=2,
+                       description="70B-class GQA decode B=32 Hq=64 Hkv=8 D=128 len=4096"),
+    "ragged": Workload("ragged", B=256, Hq=32, Hkv=8, D=128, Lmax=8192, seed=3,
+                       len_lo=1, len_hi=8192,
+                       description="ragged GQA decode B=256 Hq=32 Hkv=8 D=128 len~U[1,8192] Lmax=8192"),
+    "long": Workload("long", B=4, Hq=48, Hkv=1, D=256, Lmax=131072, seed=4, q_mult=4.0,
+                     description="long-context MQA decode B=4 Hq=48 Hkv=1 D=256 len=131072, q*4"),
+}
+
+
+def draw_lengths(w: Workload, gen: torch.Generator, device) -> torch.Tensor:
+    if w.ragged:
+        return torch.randint(w.len_lo, w.len_hi + 1, (w.B,), generator=gen,
+                             device=device, dtype=torch.int32)
+    return torch.full((w.B,), w.Lmax, dtype=torch.int32, device=device)
+
+
+def _randn_bf16(shape, gen, device) -> torch.Tensor:
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def poison_padding_(cache: torch.Tensor, seq_lens: torch.Tensor) -> torch.Tensor:
+    """Overwrite positions >= seq_lens[b] of a [B, Lmax, H, D] cache with bf16 NaN."""
+    B, Lmax = cache.shape[0], cache.shape[1]
+    pos = torch.arange(Lmax, device=cache.device, dtype=torch.int32).view(1, Lmax)
+    pad = (pos >= seq_lens.to(cache.device).view(B, 1)).view(B, Lmax, 1, 1)
+    cache.view(torch.int16).masked_fill_(pad, BF16_QNAN_BITS)
+    return cache
+
+
+def make_inputs(w: Workload, device="cpu", seed: int | None = None,
+                poison_padding: bool = False, seq_lens=None) -> dict:
+    """Draw q, K, V (bf16) and seq_lens (int32) for workload ``w`` on ``device``.
+
+    ``seq_lens`` overrides the drawn lengths (the draw still happens, so the
+    q/K/V streams do not shift).
+    """
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed if seed is None else int(seed))
+    lens = draw_lengths(w, gen, device)
+    if seq_lens is not None:
+        lens = torch.as_tensor(seq_lens, dtype=torch.int32).to(device).reshape(w.B).contiguous()
+    q = _randn_bf16((w.B, w.Hq, w.D), gen, device)
+    if w.q_mult != 1.0:
+        q = q * w.q_mult
+    k = _randn_bf16((w.B, w.Lmax, w.Hkv, w.D), gen, device)
+    v = _randn_bf16((w.B, w.Lmax, w.Hkv, w.D), gen, device)
+    if poison_padding:
+        poison_padding_(k, lens)
+        poison_padding_(v, lens)
+    return {"q": q, "k": k, "v": v, "seq_lens": lens, "scale": w.scale}
+
+
+def make_prefill_inputs(w: Workload, device="cpu", seed: int | None = None,
+                        poison_padding: bool = False) -> dict:
+    """Like :func:`make_inputs` but with one query per position: q_seq [B, Lmax, Hq, D]."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed if seed is None else int(seed))
+    lens = draw_lengths(w, gen, device)
+    q = _randn_bf16((w.B, w.Lmax, w.Hq, w.D), gen, device)
+    if w.q_mult != 1.0:
+        q = q * w.q_mult
+    k = _randn_bf16((w.B, w.Lmax, w.Hkv, w.D), gen, device)
+    v = _randn_bf16((w.B, w.Lmax, w.Hkv, w.D), gen, device)
+    if poison_padding:
+        poison_padding_(k, lens)
+        poison_padding_(v, lens)
+    return {"q_seq": q, "k": k, "v": v, "seq_lens": lens, "scale": w.scale}

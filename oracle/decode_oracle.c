@@ -1,0 +1,232 @@
+/*
+ * Plain CPU fp64 oracle for one decode step of multi-query / grouped-query
+ * attention against a KV cache, plus the textbook causal attention that the
+ * cache replaces.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library.  It is deliberately slow and literal: every loop follows
+ * the definition, with no blocking, fusion or reordering.
+ *
+ * What it computes (sources, restated):
+ *  - "How To Scale Your Model", Part 7 "Transformer Inference" (passage that
+ *    introduces the KV cache): each token's key and value projections are
+ *    written once into a cache; a later token forms its dot products q_i.k_j
+ *    against the cached keys, and a token attends only to earlier tokens and
+ *    itself.
+ *  - "Efficiently Scaling Transformer Inference", section 3.4, "Attention
+ *    Layer Partitioning": with multiquery attention all query heads share one
+ *    key head and one value head; a decode step brings one query token per
+ *    sequence and computes dot-product attention Q K^T against the cache.
+ *  - "Tensor Parallelism: Splitting Operations Across GPUs", sections
+ *    "Splitting attention by head" (each head has its own softmax and its own
+ *    weighted sum of values) and "The GQA ceiling: a worked memory audit"
+ *    (grouped-query attention: consecutive groups of query heads share one
+ *    key/value head).
+ *
+ * Readings where the pages are silent:
+ *  - query head h uses key/value head h / (Hq / Hkv);
+ *  - the logits are scale * q.k with `scale` supplied by the caller;
+ *  - a sequence of length 0 produces an all-zero output row;
+ *  - positions >= seq_lens[b] are never read (they may hold anything).
+ *
+ * Inputs are raw bfloat16 bit patterns (uint16_t).  Each value is widened to
+ * double exactly: the 16 bits are the top half of an IEEE binary32.
+ *
+ * Parity pins for every function here live in the CPU test suite (closed
+ * forms, a library attention routine in float64, invariants, and the
+ * decode == last-causal-row identity).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Exact widening of one bfloat16 bit pattern. */
+static double bf16_bits_to_double(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int check_shape(int B, int Hq, int Hkv, int D, int Lmax)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Lmax < 0) return -1;
+    if (Hq % Hkv != 0) return -2;
+    return 0;
+}
+
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * One decode step.
+ *   q        [B, Hq, D]          bf16 bits
+ *   k, v     [B, Lmax, Hkv, D]   bf16 bits (the cache; position-major)
+ *   seq_lens [B]                 each in [0, Lmax]
+ *   out      [B, Hq, D]          double, fully written
+ *   lse      [B, Hq] or NULL     natural-log log-sum-exp of the scaled logits
+ *                                (-INFINITY when the sequence is empty)
+ * For each (b, h) with n = seq_lens[b] and g = h / (Hq / Hkv):
+ *   s_j   = scale * sum_d q[b,h,d] * k[b,j,g,d]          for j in [0, n)
+ *   w_j   = exp(s_j - max_j s_j)
+ *   out   = (sum_j w_j * v[b,j,g,:]) / (sum_j w_j)
+ * Returns 0 on success, a negative code on a bad shape or length.
+ */
+int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                  const int32_t *seq_lens, int B, int Hq, int Hkv, int D,
+                  int Lmax, double scale, double *out, double *lse)
+{
+    int rc = check_shape(B, Hq, Hkv, D, Lmax);
+    if (rc) return rc;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || seq_lens[b] > Lmax) return -3;
+
+    const int G = Hq / Hkv;
+    const long long pairs = (long long)B * Hq;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < pairs; ++bh) {
+        const int b = (int)(bh / Hq);
+        const int h = (int)(bh % Hq);
+        const int g = h / G;
+        const int n = seq_lens[b];
+        double *o = out + ((size_t)b * Hq + h) * D;
+
+        if (n == 0) {
+            for (int d = 0; d < D; ++d) o[d] = 0.0;
+            if (lse) lse[bh] = -INFINITY;
+            continue;
+        }
+
+        double *s = (double *)malloc((size_t)n * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const uint16_t *qrow = q + ((size_t)b * Hq + h) * D;
+
+        /* logits */
+        for (int j = 0; j < n; ++j) {
+            const uint16_t *krow = k + (((size_t)b * Lmax + j) * Hkv + g) * D;
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += bf16_bits_to_double(qrow[d]) * bf16_bits_to_double(krow[d]);
+            s[j] = scale * acc;
+        }
+
+        /* softmax weights, shifted by the maximum for range safety */
+        double m = s[0];
+        for (int j = 1; j < n; ++j)
+            if (s[j] > m) m = s[j];
+        double Z = 0.0;
+        for (int j = 0; j < n; ++j) {
+            s[j] = exp(s[j] - m);
+            Z += s[j];
+        }
+
+        /* weighted sum of the value rows */
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        for (int j = 0; j < n; ++j) {
+            const uint16_t *vrow = v + (((size_t)b * Lmax + j) * Hkv + g) * D;
+            for (int d = 0; d < D; ++d)
+                o[d] += s[j] * bf16_bits_to_double(vrow[d]);
+        }
+        for (int d = 0; d < D; ++d) o[d] /= Z;
+        if (lse) lse[bh] = m + log(Z);
+        free(s);
+    }
+    return failed ? -4 : 0;
+}
+
+/*
+ * Full causal self-attention over a whole sequence, recomputed with no cache
+ * (the work the KV cache avoids).
+ *   q_seq   [B, Lmax, Hq, D]   bf16 bits: one query per position
+ *   k, v    [B, Lmax, Hkv, D]  bf16 bits
+ *   seq_lens[B]
+ *   out_seq [B, Lmax, Hq, D]   double; row i < n attends positions 0..i,
+ *                              rows i >= n are zero.
+ * Written as the textbook masked form: the full score row S[i, 0..n) is
+ * built, entries with j > i are set to -infinity, then a row softmax and the
+ * product with V follow.  It deliberately does not reuse the decode loop.
+ */
+int oracle_causal_prefill(const uint16_t *q_seq, const uint16_t *k,
+                          const uint16_t *v, const int32_t *seq_lens, int B,
+                          int Hq, int Hkv, int D, int Lmax, double scale,
+                          double *out_seq)
+{
+    int rc = check_shape(B, Hq, Hkv, D, Lmax);
+    if (rc) return rc;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || seq_lens[b] > Lmax) return -3;
+
+    const int G = Hq / Hkv;
+    const long long rows = (long long)B * Lmax * Hq;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long long r = 0; r < rows; ++r) {
+        const int h = (int)(r % Hq);
+        const int i = (int)((r / Hq) % Lmax);
+        const int b = (int)(r / ((long long)Hq * Lmax));
+        const int n = seq_lens[b];
+        double *o = out_seq + (size_t)r * D;
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (i >= n) continue;
+
+        const int kvh = h / G;
+        double *S = (double *)malloc((size_t)n * sizeof(double));
+        if (!S) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const uint16_t *qrow = q_seq + (size_t)r * D;
+        for (int j = 0; j < n; ++j) {
+            const uint16_t *krow = k + (((size_t)b * Lmax + j) * Hkv + kvh) * D;
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += bf16_bits_to_double(qrow[d]) * bf16_bits_to_double(krow[d]);
+            S[j] = (j > i) ? -INFINITY : scale * acc;
+        }
+        double rowmax = -INFINITY;
+        for (int j = 0; j < n; ++j)
+            if (S[j] > rowmax) rowmax = S[j];
+        double denom = 0.0;
+        for (int j = 0; j < n; ++j) denom += exp(S[j] - rowmax);
+        for (int j = 0; j < n; ++j) {
+            const double p = exp(S[j] - rowmax) / denom;
+            if (p == 0.0) continue; /* masked entries: never touch their V */
+            const uint16_t *vrow = v + (((size_t)b * Lmax + j) * Hkv + kvh) * D;
+            for (int d = 0; d < D; ++d) o[d] += p * bf16_bits_to_double(vrow[d]);
+        }
+        free(S);
+    }
+    return failed ? -4 : 0;
+}
