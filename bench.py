@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: steps/s and achieved HBM bandwidth on one MI355X.
+
+One step = one decode step of the whole batch (split-K kernel, plus the
+combine kernel when sequences are split), inputs resident in HBM.  Default
+workload: PaLM-540B-shaped MQA decode (B=64, Hq=48, Hkv=1, D=256, len 2048).
+
+To keep the memory-side Infinity Cache (256 MB) from serving repeated reads,
+the timed loop rotates through enough distinct q/K/V sets to cover at least
+768 MiB, so every step reads its K/V from HBM.
+
+Prints ONE JSON line (rank 0, N=1):
+  value        decode steps per second over the timed steps
+  roofline     the split-K kernel's algorithmic K+V bytes per launch divided by
+               its mean duration (HIP events recorded by the library around
+               that launch, on the stream it runs on) against the 8 TB/s HBM peak;
+               `traffic` is the HBM bytes per launch measured by rocprofv3 PMC
+               counters (profiles/traffic_<workload>.txt) when those counters
+               were taken on the current kernel sources, else null
+  cpu_baseline the CPU fp64 oracle on the host's cores on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0
+MALL_DEFEAT_BYTES = 768 * 2 ** 20
+KERNEL_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "combine.hip", "kernel_common.hpp", "abi.cpp", "plan.cpp"]
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "gqa_decode_attention_mqa_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, launches_per_step: int = 1):
+    """HBM bytes per split-K launch from committed PMC summaries, if still current."""
+    path = ROOT / "profiles" / ("traffic_%s.txt" % workload)
+    if not path.exists():
+        return None
+    fields = {}
+    for line in path.read_text().splitlines():
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha():
+        return None
+    try:
+        return float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="palm", choices=["tiny", "palm", "gqa70b", "ragged", "long"])
+    ap.add_argument("--variant", default=None, choices=[None, "auto", "valu", "mfma"])
+    ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times (PMC calibration) and exit")
+    return ap.parse_args(argv)
+
+
+def copy_probe(nbytes: int):
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 5}))
+
+
+def cpu_baseline(w, inp, target_s: float):
+    """The oracle, as it stands, on whole decode steps of set 0 (or a prefix of the batch)."""
+    import oracle
+    q, k, v, lens = inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu()
+    threads = oracle.max_threads()
+    # time one sequence first to size the sample
+    t0 = time.perf_counter()
+    oracle.decode(q[:1], k[:1], v[:1], lens[:1], inp["scale"])
+    one = max(time.perf_counter() - t0, 1e-6)
+    per_seq_lens = lens.double()
+    # sequences to run: whole steps when they fit in the budget, else a prefix of the batch
+    est_step = one * float(per_seq_lens.sum()) / max(float(per_seq_lens[0]), 1.0)
+    if est_step <= target_s:
+        reps = max(1, int(target_s / max(est_step, 1e-6)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.decode(q, k, v, lens, inp["scale"])
+        dt = time.perf_counter() - t0
+        steps = reps
+        sample = "%d whole decode step(s) of the %s workload (B=%d)" % (reps, w.name, w.B)
+    else:
+        nseq = max(1, int(w.B * target_s / est_step))
+        t0 = time.perf_counter()
+        oracle.decode(q[:nseq], k[:nseq], v[:nseq], lens[:nseq], inp["scale"])
+        dt = time.perf_counter() - t0
+        steps = float(lens[:nseq].double().sum() / lens.double().sum())
+        sample = "first %d of %d sequences of one %s decode step, scaled by their share of positions" % (
+            nseq, w.B, w.name)
+    return {"value": steps / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": sample + "; fp64 C oracle, OpenMP over (sequence, head)", "seconds": round(dt, 3)}
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (requested --gpus %d); the multi-GPU sharding "
+              "of the decode step is described in DESIGN.md but not built." % args.gpus, file=sys.stderr)
+        return 2
+    import torch
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return 0
+
+    from gqa_decode_attention_mqa_amd import binding
+    from gqa_decode_attention_mqa_amd.traffic import decode_step_kv_bytes
+    from gqa_decode_attention_mqa_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = binding.load_library()
+
+    base = make_inputs(w, device=dev)
+    lens = base["seq_lens"]
+    set_bytes = 2 * w.B * w.Lmax * w.Hkv * w.D * 2
+    nsets = max(1, math.ceil(MALL_DEFEAT_BYTES / set_bytes))
+    sets = [base] + [make_inputs(w, device=dev, seed=w.seed + 1000 * i, seq_lens=lens) for i in range(1, nsets)]
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk)
+
+    calls = []
+    for s in sets:
+        calls.append((s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(), s["seq_lens"].data_ptr(),
+                      out.data_ptr(), w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, sptr))
+    fn = lib.mqa_decode_attention_ex
+
+    def step(i, opts):
+        st = fn(*calls[i % nsets], binding.ctypes.byref(opts))
+        if st != 0:
+            raise RuntimeError("decode failed: %s" % lib.mqa_last_error().decode())
+
+    plain = binding.make_opts(args.variant, args.chunk)
+    for i in range(args.warmup):
+        step(i, plain)
+    torch.cuda.synchronize()
+
+    # per-step events around the split-K kernel, recorded by the library on its stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    opts = [binding.make_opts(args.variant, args.chunk, None, b.cuda_event, e.cuda_event) for b, e in evs]
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        step(i, opts[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    kern_ms = [b.elapsed_time(e) for b, e in evs]
+    kern_ms.sort()
+    mean_kern_ms = sum(kern_ms) / len(kern_ms)
+    median_kern_ms = kern_ms[len(kern_ms) // 2]
+
+    ms_per_step = total_ms / args.steps
+    kv_bytes = decode_step_kv_bytes(lens.cpu().tolist(), w.Hkv, w.D)
+    achieved = kv_bytes / (mean_kern_ms * 1e-3) / 1e9
+    traffic = read_traffic(w.name)
+
+    result = {
+        "metric": "decode-attention steps/sec and achieved HBM GB/s (% of MI355X peak)",
+        "value": round(1000.0 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.description,
+            "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "Lmax": w.Lmax,
+            "seq_lens_sum": int(lens.sum().item()),
+            "kv_bytes_per_step": kv_bytes,
+            "buffer_sets_rotated": nsets,
+            "plan": plan,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "split-K decode (%s)" % plan["variant"],
+            "kernel_mean_us": round(mean_kern_ms * 1e3, 3),
+            "kernel_median_us": round(median_kern_ms * 1e3, 3),
+            "step_kv_gbs": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, base, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

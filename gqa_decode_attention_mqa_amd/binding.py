@@ -1,0 +1,199 @@
+"""Thin ctypes binding of ``libmqa_decode.so`` for torch tensors.
+
+Argument marshalling only: shapes and dtypes are checked, device pointers and
+torch's current HIP stream are handed to the C ABI (``include/mqa_decode.h``),
+and every step of the computation runs in the library's kernels.  There is no
+fallback: if the library is missing or a call fails, an exception says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import re
+from pathlib import Path
+
+import torch
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libmqa_decode.so"
+HEADER_PATH = _PKG.parent / "include" / "mqa_decode.h"
+
+MQA_OK = 0
+VARIANTS = {"auto": 0, "valu": 1, "mfma": 2}
+VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
+COMBINE = {"auto": 0, "separate": 1, "fused": 2}
+
+
+class MqaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__("%s failed with status %d: %s" % (where, status, detail))
+
+
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int), ("chunk", ctypes.c_int), ("combine", ctypes.c_int),
+                ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int), ("chunk", ctypes.c_int), ("max_splits", ctypes.c_int),
+                ("combine", ctypes.c_int), ("head_blocks", ctypes.c_int),
+                ("grid_main", ctypes.c_longlong), ("block_main", ctypes.c_int),
+                ("grid_combine", ctypes.c_longlong), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise ImportError("libmqa_decode.so is not built at %s; run "
+                          "`python -m gqa_decode_attention_mqa_amd.build` (or __graft_entry__.build())" % LIB_PATH)
+    lib = ctypes.CDLL(str(LIB_PATH))
+    vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    ints = [ctypes.c_int] * 5
+    lib.mqa_decode_attention.argtypes = [vp, vp, vp, i32p, f32p] + ints + [ctypes.c_float, vp]
+    lib.mqa_decode_attention.restype = ctypes.c_int
+    lib.mqa_decode_attention_ex.argtypes = [vp, vp, vp, i32p, f32p] + ints + \
+        [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
+    lib.mqa_decode_attention_ex.restype = ctypes.c_int
+    lib.mqa_prefill_attention.argtypes = [vp, vp, vp, i32p, f32p] + ints + [ctypes.c_float, vp]
+    lib.mqa_prefill_attention.restype = ctypes.c_int
+    lib.mqa_decode_plan.argtypes = ints + [ctypes.c_float, ctypes.POINTER(DecodeOpts), ctypes.POINTER(PlanInfo)]
+    lib.mqa_decode_plan.restype = ctypes.c_int
+    lib.mqa_status_string.argtypes = [ctypes.c_int]
+    lib.mqa_status_string.restype = ctypes.c_char_p
+    lib.mqa_last_error.argtypes = []
+    lib.mqa_last_error.restype = ctypes.c_char_p
+    lib.mqa_release_workspaces.argtypes = []
+    lib.mqa_release_workspaces.restype = None
+    lib.mqa_version.argtypes = []
+    lib.mqa_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions ``include/mqa_decode.h`` declares."""
+    text = HEADER_PATH.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mqa_\w+)\s*\(", text, flags=re.M)))
+
+
+def _check(status: int, where: str):
+    if status != MQA_OK:
+        lib = load_library()
+        raise MqaError(status, where, "%s (%s)" % (lib.mqa_status_string(status).decode(),
+                                                   lib.mqa_last_error().decode()))
+
+
+def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None) -> DecodeOpts:
+    o = DecodeOpts()
+    o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant or 0)
+    o.chunk = int(chunk or 0)
+    o.combine = COMBINE[combine] if isinstance(combine, str) else int(combine or 0)
+    o.ev_main_begin = ev_begin
+    o.ev_main_end = ev_end
+    return o
+
+
+def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None) -> dict:
+    """The library's launch plan for a decode call of this shape (host only)."""
+    lib = load_library()
+    info = PlanInfo()
+    opts = make_opts(variant, chunk, combine)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.mqa_decode_plan(B, Hq, Hkv, D, Lmax, sc, ctypes.byref(opts), ctypes.byref(info)),
+           "mqa_decode_plan")
+    return {"variant": VARIANT_NAMES.get(info.variant, info.variant), "chunk": info.chunk,
+            "max_splits": info.max_splits, "combine": info.combine, "head_blocks": info.head_blocks,
+            "grid_main": info.grid_main, "block_main": info.block_main,
+            "grid_combine": info.grid_combine, "workspace_bytes": info.workspace_bytes}
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtype, ndim: int, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+           scale: float | None = None, out: torch.Tensor | None = None, variant=None, chunk=None,
+           combine=None, events=None) -> torch.Tensor:
+    """One decode step.  q [B,Hq,D] bf16, caches [B,Lmax,Hkv,D] bf16, seq_lens [B] int32 -> fp32 [B,Hq,D].
+
+    Runs on torch's current stream of q's device.  ``events`` = (begin, end)
+    torch.cuda.Event pair recorded around the split-K kernel alone.
+    """
+    if q.device.type != "cuda":
+        raise ValueError("decode runs on the GPU; q is on %s" % q.device)
+    dev = q.device
+    _require(q, "q", torch.bfloat16, 3, dev)
+    _require(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _require(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    Bk, Lmax, Hkv, Dk = k_cache.shape
+    if v_cache.shape != k_cache.shape or Bk != B or Dk != D or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch: q %s, k %s, v %s, seq_lens %s" % (
+            tuple(q.shape), tuple(k_cache.shape), tuple(v_cache.shape), tuple(seq_lens.shape)))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, 3, dev)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must have shape %s" % ((B, Hq, D),))
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    ev_b = ev_e = None
+    if events is not None:
+        ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e)
+    lib = load_library()
+    st = lib.mqa_decode_attention_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                     seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D, Lmax,
+                                     sc, _stream_ptr(dev), ctypes.byref(opts))
+    _check(st, "mqa_decode_attention")
+    return out
+
+
+def prefill(q_seq: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+            scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal attention with no cache: q_seq [B,Lmax,Hq,D] bf16 -> fp32 [B,Lmax,Hq,D]."""
+    if q_seq.device.type != "cuda":
+        raise ValueError("prefill runs on the GPU; q_seq is on %s" % q_seq.device)
+    dev = q_seq.device
+    _require(q_seq, "q_seq", torch.bfloat16, 4, dev)
+    _require(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _require(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, Lmax, Hq, D = q_seq.shape
+    if k_cache.shape[:2] != (B, Lmax) or k_cache.shape[3] != D or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q_seq and the caches")
+    Hkv = k_cache.shape[2]
+    if out is None:
+        out = torch.empty((B, Lmax, Hq, D), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, 4, dev)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    lib = load_library()
+    st = lib.mqa_prefill_attention(q_seq.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D, Lmax, sc,
+                                   _stream_ptr(dev))
+    _check(st, "mqa_prefill_attention")
+    return out
+
+
+def release_workspaces():
+    load_library().mqa_release_workspaces()

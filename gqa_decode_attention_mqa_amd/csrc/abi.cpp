@@ -1,0 +1,206 @@
+// C ABI of the decode library: argument checks, workspace cache, launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/mqa_decode.h"
+#include "kernel_common.hpp"
+#include "launch.hpp"
+#include "plan.hpp"
+
+namespace {
+
+using mqa::Plan;
+
+// Split-K scratch, one buffer per (device, stream), grown on demand.
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+
+mqa_status hip_fail(hipError_t e, const char* what) {
+    mqa::set_error(std::string(what) + ": " + hipGetErrorString(e));
+    return MQA_ERR_HIP;
+}
+
+mqa_status get_workspace(hipStream_t stream, size_t bytes, void** out) {
+    *out = nullptr;
+    if (bytes == 0) return MQA_OK;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
+    if (ws.bytes < bytes) {
+        if (ws.ptr) {
+            // The old buffer may still be read by work queued on this stream.
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            e = hipFree(ws.ptr);
+            ws.ptr = nullptr;
+            ws.bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+        }
+        void* p = nullptr;
+        e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) {
+            mqa::set_error(std::string("hipMalloc of split-K workspace failed: ") + hipGetErrorString(e));
+            return MQA_ERR_WORKSPACE;
+        }
+        ws.ptr = p;
+        ws.bytes = bytes;
+    }
+    *out = ws.ptr;
+    return MQA_OK;
+}
+
+mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_lens, float* out,
+               int B, int Hq, int Hkv, int D, int Lmax, float scale, void* stream_ptr,
+               const mqa_decode_opts* opts, bool causal) {
+    mqa::set_error("");
+    Plan plan;
+    mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, causal, &plan);
+    if (st != MQA_OK) return st;
+    st = mqa::check_pointers(B, Lmax, q, k, v, seq_lens, out);
+    if (st != MQA_OK) return st;
+    if (B == 0) return MQA_OK;
+
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    void* ws = nullptr;
+    st = get_workspace(stream, plan.workspace_bytes, &ws);
+    if (st != MQA_OK) return st;
+
+    mqa::DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.part_o = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_o_offset) : nullptr;
+    a.part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_lse_offset) : nullptr;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.Lmax = Lmax;
+    a.G = plan.G;
+    a.chunk = plan.chunk;
+    a.max_splits = plan.max_splits;
+    a.causal = causal ? 1 : 0;
+    a.qk_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+
+    hipError_t e;
+    if (opts && opts->ev_main_begin) {
+        e = hipEventRecord(static_cast<hipEvent_t>(opts->ev_main_begin), stream);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    e = (plan.variant == MQA_VARIANT_MFMA) ? mqa::launch_decode_mfma(plan, a, stream)
+                                           : mqa::launch_decode_valu(plan, a, stream);
+    if (e != hipSuccess) return hip_fail(e, "split-K kernel launch");
+    if (opts && opts->ev_main_end) {
+        e = hipEventRecord(static_cast<hipEvent_t>(opts->ev_main_end), stream);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    if (plan.combine == 1) {
+        mqa::CombineArgs c{};
+        c.part_o = a.part_o;
+        c.part_lse = a.part_lse;
+        c.seq_lens = seq_lens;
+        c.out = out;
+        c.Hq = Hq;
+        c.Hkv = Hkv;
+        c.D = D;
+        c.Lmax = Lmax;
+        c.G = plan.G;
+        c.chunk = plan.chunk;
+        c.max_splits = plan.max_splits;
+        c.causal = a.causal;
+        e = mqa::launch_combine(plan, c, stream);
+        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    }
+    return MQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mqa_status mqa_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
+                                int D, int Lmax, float scale, void* stream) {
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, nullptr, false);
+}
+
+mqa_status mqa_decode_attention_ex(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
+                                   int D, int Lmax, float scale, void* stream,
+                                   const mqa_decode_opts* opts) {
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false);
+}
+
+mqa_status mqa_prefill_attention(const void* q_seq, const void* k_cache, const void* v_cache,
+                                 const int32_t* seq_lens, float* out_seq, int B, int Hq, int Hkv,
+                                 int D, int Lmax, float scale, void* stream) {
+    return run(q_seq, k_cache, v_cache, seq_lens, out_seq, B, Hq, Hkv, D, Lmax, scale, stream,
+               nullptr, true);
+}
+
+mqa_status mqa_decode_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
+                           const mqa_decode_opts* opts, mqa_plan_info* info) {
+    mqa::set_error("");
+    Plan p;
+    const mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, false, &p);
+    if (st != MQA_OK) return st;
+    if (info) {
+        info->variant = p.variant;
+        info->chunk = p.chunk;
+        info->max_splits = p.max_splits;
+        info->combine = p.combine;
+        info->head_blocks = p.head_blocks;
+        info->grid_main = p.grid_main * p.head_blocks;
+        info->block_main = p.block_main;
+        info->grid_combine = p.grid_combine;
+        info->workspace_bytes = p.workspace_bytes;
+    }
+    return MQA_OK;
+}
+
+const char* mqa_status_string(mqa_status s) {
+    switch (s) {
+        case MQA_OK: return "ok";
+        case MQA_ERR_NULL: return "null pointer argument";
+        case MQA_ERR_SHAPE: return "invalid shape";
+        case MQA_ERR_UNSUPPORTED: return "unsupported shape";
+        case MQA_ERR_ALIGN: return "misaligned pointer";
+        case MQA_ERR_WORKSPACE: return "workspace allocation failed";
+        case MQA_ERR_HIP: return "HIP runtime error";
+        case MQA_ERR_ARG: return "invalid argument";
+    }
+    return "unknown status";
+}
+
+const char* mqa_last_error(void) { return mqa::last_error(); }
+
+void mqa_release_workspaces(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    for (auto& kv : g_ws) {
+        if (kv.second.ptr) {
+            int prev = 0;
+            (void)hipGetDevice(&prev);
+            (void)hipSetDevice(kv.first.first);
+            (void)hipFree(kv.second.ptr);
+            (void)hipSetDevice(prev);
+        }
+    }
+    g_ws.clear();
+}
+
+int mqa_version(void) { return 100; }
+
+}  // extern "C"

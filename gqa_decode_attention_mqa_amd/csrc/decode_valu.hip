@@ -1,0 +1,246 @@
+// Split-K decode attention on the vector ALU, for small head groups.
+//
+// When only a few query heads share a key/value head (grouped-query attention
+// with a small group, "How To Scale Your Model", Part 7 "Transformer
+// Inference", passage on shrinking the KV cache), the q.K and P.V products are
+// too thin for a 16-wide matrix tile, so they run as bf16 dot products
+// (v_dot2_f32_bf16) with fp32 accumulation.
+//
+// Layout: a cache row of D bf16 is spread over RL = D/8 lanes, each holding 8
+// consecutive elements (one 128-bit load), so a wave covers RS = 64/RL
+// positions per load instruction and every load is fully coalesced.  The q.K
+// dot product of a position is summed across its RL lanes with DPP row
+// permutations (the sum lands in every lane of the row, which is where P.V
+// needs the weight).  Each wave keeps its own online softmax (base 2) over the
+// positions it visits; the four waves merge by log-sum-exp through LDS at the
+// end of the chunk.  P.V pairs two positions of the same column into one
+// v_dot2 after a v_perm_b32, with P rounded to bf16 (the row sum uses the same
+// rounded weights).
+#include "kernel_common.hpp"
+#include "launch.hpp"
+
+namespace mqa {
+
+template <int RL>
+__device__ __forceinline__ float row_sum(float x) {
+    x += dpp_f32<kDppQuadXor1>(x);
+    x += dpp_f32<kDppQuadXor2>(x);
+    x += dpp_f32<kDppRowHalfMirror>(x);
+    if constexpr (RL >= 16) x += dpp_f32<kDppRowMirror>(x);
+    if constexpr (RL >= 32) x += shfl_xor_f32(x, 16);
+    return x;
+}
+
+// Reduction over the lanes that share a column slot but sit in different rows.
+template <int RL, bool MAX>
+__device__ __forceinline__ float across_rows(float x) {
+    if constexpr (RL <= 8) {
+        const float y = dpp_f32<kDppRowRor8>(x);
+        x = MAX ? fmaxf(x, y) : x + y;
+    }
+    if constexpr (RL <= 16) {
+        const float y = shfl_xor_f32(x, 16);
+        x = MAX ? fmaxf(x, y) : x + y;
+    }
+    {
+        const float y = shfl_xor_f32(x, 32);
+        x = MAX ? fmaxf(x, y) : x + y;
+    }
+    return x;
+}
+
+template <int D, int GB>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+    constexpr int NW = 4;
+    constexpr int RL = D / 8;      // lanes per cache row
+    constexpr int RS = 64 / RL;    // rows per load instruction
+    constexpr int NB = 4;          // load instructions per block (even: P.V pairs them)
+    constexpr int WB = NB * RS;    // positions per wave block
+    __shared__ float mrg_m[NW][GB];
+    __shared__ float mrg_l[NW][GB];
+    __shared__ __attribute__((aligned(16))) float mrg_o[NW][GB][D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int rl = lane % RL, rr = lane / RL;
+
+    const long long x = blockIdx.x;
+    const int s = (int)(x % a.max_splits);
+    const long long unit = x / a.max_splits;
+    const int kvh = (int)(unit % a.Hkv);
+    const long long row = unit / a.Hkv;
+    const int g0 = blockIdx.y * GB;
+    const int gcnt = min(GB, a.G - g0);
+
+    int b, len;
+    row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
+    const int p0 = s * a.chunk;
+    if (s > 0 && p0 >= len) return;
+    const int p1 = min(p0 + a.chunk, len);
+    const int nsplit = len > 0 ? (len + a.chunk - 1) / a.chunk : 1;
+
+    // q for this lane's 8 columns of every head in the block, as bf16 pairs.
+    uint32_t qv[GB][4];
+    const uint16_t* qrow = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D + 8 * rl;
+#pragma unroll
+    for (int gg = 0; gg < GB; ++gg) {
+        u32x4_t t = {0u, 0u, 0u, 0u};
+        if (gg < gcnt) t = load_u32x4(qrow + (size_t)gg * D);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qv[gg][c] = t[c];
+    }
+
+    const size_t pos_stride = (size_t)a.Hkv * D;
+    const uint16_t* kbase = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D + 8 * rl;
+    const uint16_t* vbase = a.v + ((size_t)b * a.Lmax * a.Hkv + kvh) * D + 8 * rl;
+    const float qk = a.qk_log2;
+
+    float m[GB], l[GB], o[GB][8];
+#pragma unroll
+    for (int gg = 0; gg < GB; ++gg) {
+        m[gg] = -INFINITY;
+        l[gg] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[gg][j] = 0.f;
+    }
+
+    const int nblk = p1 > p0 ? (p1 - p0 + WB - 1) / WB : 0;
+    for (int blk = w; blk < nblk; blk += NW) {
+        const int t0 = p0 + blk * WB;
+        u32x4_t kr[NB], vr[NB];
+#pragma unroll
+        for (int st = 0; st < NB; ++st) {
+            const int t = t0 + st * RS + rr;
+            const bool ok = t < p1;
+            kr[st] = ok ? load_u32x4(kbase + (size_t)t * pos_stride) : u32x4_t{0u, 0u, 0u, 0u};
+            vr[st] = ok ? load_u32x4(vbase + (size_t)t * pos_stride) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        // logits (base-2 units), masked past the end
+        float sc[NB][GB];
+#pragma unroll
+        for (int st = 0; st < NB; ++st) {
+            const bool ok = t0 + st * RS + rr < p1;
+#pragma unroll
+            for (int gg = 0; gg < GB; ++gg) {
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc = dot2_bf16(qv[gg][c], kr[st][c], acc);
+                acc = row_sum<RL>(acc);
+                sc[st][gg] = ok ? acc * qk : -INFINITY;
+            }
+        }
+        // online softmax update for the block
+        uint32_t pbits[NB][GB];
+#pragma unroll
+        for (int gg = 0; gg < GB; ++gg) {
+            float mx = sc[0][gg];
+#pragma unroll
+            for (int st = 1; st < NB; ++st) mx = fmaxf(mx, sc[st][gg]);
+            mx = across_rows<RL, true>(mx);
+            const float m_new = fmaxf(m[gg], mx);
+            const float alpha = __builtin_amdgcn_exp2f(m[gg] - m_new);
+            m[gg] = m_new;
+            float lsum = 0.f;
+#pragma unroll
+            for (int st = 0; st < NB; ++st) {
+                pbits[st][gg] = f32_to_bf16_bits(__builtin_amdgcn_exp2f(sc[st][gg] - m_new));
+                lsum += bf16_bits_to_f32(pbits[st][gg]);
+            }
+            l[gg] = l[gg] * alpha + lsum;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[gg][j] *= alpha;
+        }
+        // P.V: two positions of one column per v_dot2
+#pragma unroll
+        for (int st = 0; st < NB; st += 2) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t lo = perm_b32(vr[st + 1][c], vr[st][c], kPermLoHalves);
+                const uint32_t hi = perm_b32(vr[st + 1][c], vr[st][c], kPermHiHalves);
+#pragma unroll
+                for (int gg = 0; gg < GB; ++gg) {
+                    const uint32_t pp = pack_bf16x2(pbits[st][gg], pbits[st + 1][gg]);
+                    o[gg][2 * c] = dot2_bf16(pp, lo, o[gg][2 * c]);
+                    o[gg][2 * c + 1] = dot2_bf16(pp, hi, o[gg][2 * c + 1]);
+                }
+            }
+        }
+    }
+
+    // Sum the rows of the wave (same softmax state in every row).
+#pragma unroll
+    for (int gg = 0; gg < GB; ++gg) {
+        l[gg] = across_rows<RL, false>(l[gg]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[gg][j] = across_rows<RL, false>(o[gg][j]);
+    }
+    if (rr == 0) {
+#pragma unroll
+        for (int gg = 0; gg < GB; ++gg) {
+            f32x4_t lo4 = {o[gg][0], o[gg][1], o[gg][2], o[gg][3]};
+            f32x4_t hi4 = {o[gg][4], o[gg][5], o[gg][6], o[gg][7]};
+            *reinterpret_cast<f32x4_t*>(&mrg_o[w][gg][8 * rl]) = lo4;
+            *reinterpret_cast<f32x4_t*>(&mrg_o[w][gg][8 * rl + 4]) = hi4;
+        }
+        if (rl == 0) {
+#pragma unroll
+            for (int gg = 0; gg < GB; ++gg) {
+                mrg_m[w][gg] = m[gg];
+                mrg_l[w][gg] = l[gg];
+            }
+        }
+    }
+    __syncthreads();
+
+    // Log-sum-exp merge of the four waves, then normalise and store.
+    const bool direct = nsplit == 1;
+    for (int idx = tid; idx < gcnt * D; idx += 256) {
+        const int gg = idx / D, d = idx % D;
+        float M = mrg_m[0][gg];
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, mrg_m[ww][gg]);
+        float O = 0.f, L = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float sw = __builtin_amdgcn_exp2f(mrg_m[ww][gg] - M);
+                O += sw * mrg_o[ww][gg][d];
+                L += sw * mrg_l[ww][gg];
+            }
+        }
+        const int gh = g0 + gg;
+        const float val = L > 0.f ? O / L : 0.f;
+        if (direct) {
+            a.out[((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D + d] = val;
+        } else {
+            const size_t part = ((size_t)unit * a.max_splits + s) * a.G + gh;
+            a.part_o[part * D + d] = val;
+            if (d == 0) a.part_lse[part] = M + __log2f(L);
+        }
+    }
+}
+
+template <int D>
+static hipError_t launch_valu_d(const Plan& p, const DecodeArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)p.grid_main, (unsigned)p.head_blocks);
+    const dim3 block(256);
+    switch (p.heads_per_block) {
+        case 1: hipLaunchKernelGGL((decode_valu_kernel<D, 1>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((decode_valu_kernel<D, 2>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_valu_kernel<D, 4>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((decode_valu_kernel<D, 8>), grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_valu(const Plan& p, const DecodeArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 64: return launch_valu_d<64>(p, a, stream);
+        case 128: return launch_valu_d<128>(p, a, stream);
+        case 256: return launch_valu_d<256>(p, a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace mqa

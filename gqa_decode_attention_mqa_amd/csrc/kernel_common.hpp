@@ -1,0 +1,116 @@
+// Device-side definitions shared by the decode kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mqa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// Arguments of the split-K decode kernels, passed by value.
+//
+// A "row" is one query token: row r of a decode call is sequence r; in the
+// causal (prefill) form row r is position t = r % Lmax of sequence
+// b = r / Lmax and attends positions 0..t.  A "unit" is (row, kv head); a
+// unit's positions are cut into chunks of `chunk` positions, one workgroup per
+// (unit, chunk, head block).
+struct DecodeArgs {
+    const uint16_t* q;         // bf16 [rows, Hq, D]
+    const uint16_t* k;         // bf16 [B, Lmax, Hkv, D]
+    const uint16_t* v;         // bf16 [B, Lmax, Hkv, D]
+    const int32_t* seq_lens;   // [B]
+    float* out;                // fp32 [rows, Hq, D]
+    float* part_o;             // fp32 [rows * Hkv * max_splits, G, D], O / l per chunk
+    float* part_lse;           // fp32 [rows * Hkv * max_splits, G], m + log2(l) (base 2)
+    int Hq, Hkv, D, Lmax, G;
+    int chunk, max_splits;
+    int causal;                // 0 decode, 1 causal rows
+    float qk_log2;             // scale * log2(e): logits are kept in base-2 units
+};
+
+struct CombineArgs {
+    const float* part_o;
+    const float* part_lse;
+    const int32_t* seq_lens;
+    float* out;
+    int Hq, Hkv, D, Lmax, G;
+    int chunk, max_splits;
+    int causal;
+};
+
+// Attended length of a row, with seq_lens clamped to [0, Lmax].
+__device__ __forceinline__ void row_extent(const int32_t* seq_lens, long long row, int Lmax,
+                                           int causal, int* b_out, int* len_out) {
+    int b, len;
+    if (causal) {
+        b = (int)(row / Lmax);
+        const int t = (int)(row % Lmax);
+        int lb = seq_lens[b];
+        lb = lb < 0 ? 0 : (lb > Lmax ? Lmax : lb);
+        len = t < lb ? t + 1 : 0;
+    } else {
+        b = (int)row;
+        int lb = seq_lens[b];
+        len = lb < 0 ? 0 : (lb > Lmax ? Lmax : lb);
+    }
+    *b_out = b;
+    *len_out = len;
+}
+
+// Round-to-nearest-even float -> bf16 bits (inputs here are finite or +0).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(uint32_t lo_bits, uint32_t hi_bits) {
+    return (lo_bits & 0xFFFFu) | (hi_bits << 16);
+}
+
+// DPP lane permutations used inside 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within each 8-lane half row
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within each 16-lane row
+constexpr int kDppRowRor8 = 0x128;       // lane i <- lane (i+8) mod 16 within the row
+
+__device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
+    return __shfl_xor(x, mask, 64);
+}
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// v_perm_b32 byte select: result bytes = sel over {hi: bytes 4..7, lo: bytes 0..3}.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+constexpr uint32_t kPermLoHalves = 0x05040100u;  // (lo.lo16) | (hi.lo16 << 16)
+constexpr uint32_t kPermHiHalves = 0x07060302u;  // (lo.hi16) | (hi.hi16 << 16)
+
+__device__ __forceinline__ u32x4_t load_u32x4(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ u32x2_t load_u32x2(const uint16_t* p) {
+    return *reinterpret_cast<const u32x2_t*>(p);
+}
+
+}  // namespace mqa

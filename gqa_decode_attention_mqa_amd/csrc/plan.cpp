@@ -1,0 +1,127 @@
+// Host-side argument checks and launch planning (no HIP calls).
+#include "plan.hpp"
+
+#include <cmath>
+#include <cstdlib>
+#include <string>
+
+namespace mqa {
+
+namespace {
+thread_local std::string g_last_error;
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+long long round_up(long long a, long long b) { return ceil_div(a, b) * b; }
+
+mqa_status fail(mqa_status s, const std::string& msg) {
+    set_error(msg);
+    return s;
+}
+
+// Workgroups the planner aims for when it picks the chunk size: enough to
+// give every CU at least two resident workgroups.
+constexpr long long kTargetWorkgroups = 2LL * kComputeUnits;
+// Chunk bounds: below 256 positions the partial outputs cost more traffic than
+// the split saves; above 2048 a ragged batch balances poorly.
+constexpr long long kMinChunk = 256;
+constexpr long long kMaxChunk = 2048;
+// Largest grid the launcher accepts (work-items must stay below 2^32).
+constexpr long long kMaxGrid = (1LL << 24) - 1;
+}  // namespace
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+const char* last_error() { return g_last_error.c_str(); }
+
+mqa_status check_pointers(int B, int Lmax, const void* q, const void* k, const void* v,
+                          const int32_t* seq_lens, const float* out) {
+    if (B == 0) return MQA_OK;
+    if (!q || !seq_lens || !out)
+        return fail(MQA_ERR_NULL, "q, seq_lens and out must be non-NULL");
+    if (Lmax > 0 && (!k || !v))
+        return fail(MQA_ERR_NULL, "k_cache and v_cache must be non-NULL when Lmax > 0");
+    auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out))
+        return fail(MQA_ERR_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0)
+        return fail(MQA_ERR_ALIGN, "seq_lens must be 4-byte aligned");
+    return MQA_OK;
+}
+
+mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
+                     const mqa_decode_opts* opts, bool causal, Plan* plan) {
+    if (B < 0 || Lmax < 0)
+        return fail(MQA_ERR_SHAPE, "B and Lmax must be >= 0");
+    if (Hq <= 0 || Hkv <= 0 || D <= 0)
+        return fail(MQA_ERR_SHAPE, "Hq, Hkv and D must be > 0");
+    if (Hq % Hkv != 0)
+        return fail(MQA_ERR_SHAPE, "Hq must be a multiple of Hkv");
+    if (D != 64 && D != 128 && D != 256)
+        return fail(MQA_ERR_UNSUPPORTED, "head size D must be 64, 128 or 256");
+    if (!std::isfinite(scale))
+        return fail(MQA_ERR_ARG, "scale must be finite");
+
+    mqa_decode_opts o{};
+    if (opts) o = *opts;
+    if (o.variant < MQA_VARIANT_AUTO || o.variant > MQA_VARIANT_MFMA)
+        return fail(MQA_ERR_ARG, "unknown variant");
+    if (o.chunk < 0 || (o.chunk > 0 && o.chunk % kChunkQuantum != 0))
+        return fail(MQA_ERR_ARG, "chunk must be 0 or a positive multiple of 128");
+    if (o.combine < 0 || o.combine > 2)
+        return fail(MQA_ERR_ARG, "combine must be 0, 1 or 2");
+    if (o.combine == 2)
+        return fail(MQA_ERR_ARG, "the fused combine is not available in this build");
+
+    Plan p;
+    p.G = Hq / Hkv;
+    p.variant = o.variant;
+    if (p.variant == MQA_VARIANT_AUTO)
+        p.variant = (p.G >= kMfmaHeadsPerTile) ? MQA_VARIANT_MFMA : MQA_VARIANT_VALU;
+
+    if (p.variant == MQA_VARIANT_MFMA) {
+        const int heads = p.G < kMfmaMaxHeads ? p.G : kMfmaMaxHeads;
+        p.heads_per_block = (int)round_up(heads, kMfmaHeadsPerTile);
+    } else {
+        int gb = 1;
+        while (gb < p.G && gb < kValuMaxHeads) gb *= 2;
+        p.heads_per_block = gb;
+    }
+    p.head_blocks = (int)ceil_div(p.G, p.heads_per_block);
+
+    p.rows = causal ? (long long)B * Lmax : (long long)B;
+    const long long units = p.rows * Hkv * p.head_blocks;
+
+    if (o.chunk > 0) {
+        p.chunk = o.chunk;
+    } else if (units == 0 || Lmax == 0) {
+        p.chunk = kChunkQuantum;
+    } else {
+        long long c = round_up(ceil_div((long long)Lmax * units, kTargetWorkgroups), kChunkQuantum);
+        if (c < kMinChunk) c = kMinChunk;
+        if (c > kMaxChunk) c = kMaxChunk;
+        const long long whole = round_up(Lmax, kChunkQuantum);
+        if (c > whole) c = whole;
+        p.chunk = (int)c;
+    }
+    p.max_splits = Lmax > 0 ? (int)ceil_div(Lmax, p.chunk) : 1;
+    if (p.max_splits < 1) p.max_splits = 1;
+
+    p.grid_main = p.rows * Hkv * p.max_splits;
+    p.block_main = 256;
+    if (p.grid_main > kMaxGrid || p.head_blocks > 65535)
+        return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (grid limit)");
+
+    if (p.max_splits > 1 && p.rows > 0) {
+        p.combine = (o.combine == 2) ? 2 : 1;
+        p.grid_combine = (p.combine == 1) ? p.rows * Hq : 0;
+        if (p.grid_combine > kMaxGrid)
+            return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (combine grid limit)");
+        const size_t parts = (size_t)p.rows * Hkv * p.max_splits * p.G;
+        p.part_o_offset = 0;
+        p.part_lse_offset = round_up((long long)(parts * D * sizeof(float)), 256);
+        p.workspace_bytes = p.part_lse_offset + round_up((long long)(parts * sizeof(float)), 256);
+    }
+    *plan = p;
+    return MQA_OK;
+}
+
+}  // namespace mqa

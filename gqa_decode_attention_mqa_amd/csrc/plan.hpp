@@ -1,0 +1,58 @@
+// Host-side argument checks and launch planning for the decode library.
+// This translation unit makes no HIP call, so every check can run on a
+// machine without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/mqa_decode.h"
+
+namespace mqa {
+
+// Number of compute units the planner sizes grids for (MI355X: 256 CUs in
+// 8 XCDs of 32).
+constexpr int kComputeUnits = 256;
+// Every chunk is a multiple of this many positions, the largest tile any
+// kernel steps through.
+constexpr int kChunkQuantum = 128;
+// Query heads per MFMA tile along the N dimension.
+constexpr int kMfmaHeadsPerTile = 16;
+// Most query heads one MFMA workgroup serves (four 16-head tiles).
+constexpr int kMfmaMaxHeads = 64;
+// Most query heads one VALU workgroup serves.
+constexpr int kValuMaxHeads = 8;
+
+struct Plan {
+    int variant = MQA_VARIANT_VALU;  // resolved, never AUTO
+    int G = 0;                       // query heads per kv head
+    int heads_per_block = 0;         // padded heads a workgroup serves
+    int head_blocks = 1;             // workgroups per (row, kv head, chunk) along heads
+    int chunk = 0;                   // positions per split
+    int max_splits = 1;              // ceil(Lmax / chunk), >= 1
+    int combine = 0;                 // 0 none, 1 separate kernel, 2 fused
+    long long rows = 0;              // query rows: B (decode) or B * Lmax (prefill)
+    long long grid_main = 0;         // workgroups along x of the split kernel
+    int block_main = 256;
+    long long grid_combine = 0;
+    size_t workspace_bytes = 0;      // partial outputs + partial LSEs
+    size_t part_o_offset = 0;        // byte offsets inside the workspace
+    size_t part_lse_offset = 0;
+};
+
+// Thread-local last-error text.
+void set_error(const std::string& msg);
+const char* last_error();
+
+// Checks sizes, scale and options; on success fills `plan`.  `rows` is B for
+// a decode call and B * Lmax for the causal (prefill) form.
+mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
+                     const mqa_decode_opts* opts, bool causal, Plan* plan);
+
+// Pointer checks: non-NULL when B > 0 (the caches only when Lmax > 0), 16-byte
+// alignment of the bf16/fp32 arrays.
+mqa_status check_pointers(int B, int Lmax, const void* q, const void* k, const void* v,
+                          const int32_t* seq_lens, const float* out);
+
+}  // namespace mqa

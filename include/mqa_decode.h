@@ -1,0 +1,167 @@
+/*
+ * mqa_decode.h -- C ABI of the MI355X (gfx950) decode-step attention library.
+ *
+ * The operation: one autoregressive decode step of multi-query or
+ * grouped-query attention against a KV cache.  Each of B sequences brings one
+ * new query token with Hq heads; groups of G = Hq / Hkv consecutive query heads
+ * share one of Hkv key/value heads.  For sequence b with n = seq_lens[b] cached
+ * positions and query head h (key/value head g = h / G):
+ *
+ *     s_j    = scale * sum_d q[b,h,d] * k_cache[b,j,g,d]        j = 0 .. n-1
+ *     out[b,h,:] = sum_j softmax(s)_j * v_cache[b,j,g,:]
+ *
+ * Sources (restated, not quoted):
+ *  - "Efficiently Scaling Transformer Inference", section 3.4, "Attention
+ *    Layer Partitioning": multiquery attention shares one key/value head
+ *    among all query heads; in decode the query is one token per sequence and
+ *    attention Q K^T is computed locally against that sequence's cache.
+ *  - "How To Scale Your Model", Part 7 "Transformer Inference": the KV cache
+ *    holds each earlier token's key and value projections and a new token
+ *    takes its q.k products against them (passage introducing the cache);
+ *    grouped-query attention shares each key/value head among several query
+ *    heads (passage on shrinking the KV cache); a ragged kernel reads only the
+ *    non-padding part of the cache (passage on ragged HBM reads).
+ *  - "Tensor Parallelism: Splitting Operations Across GPUs", "Splitting
+ *    attention by head": every head has its own softmax and weighted sum.
+ *
+ * Conventions chosen where the pages are silent:
+ *  - the new token's own key/value is already stored at position n-1;
+ *  - n == 0 gives an all-zero output row;
+ *  - seq_lens values outside [0, Lmax] are clamped to that range on the
+ *    device (reading them on the host would need a synchronisation);
+ *  - cache positions >= n are never read and may hold anything (NaN included).
+ *
+ * Memory: every pointer argument is device memory owned by the caller.  The
+ * library keeps no pointer after a call returns except inside work already
+ * enqueued on `stream`.  Split-K scratch (partial outputs and log-sum-exps) is
+ * owned by the library, cached per (device, stream), grown on demand with
+ * hipMalloc (which synchronises the device) and freed by
+ * mqa_release_workspaces().
+ *
+ * Errors: every argument check happens on the host before any HIP call, so
+ * the checks can run on a machine with no GPU.  No call aborts or throws; a
+ * failure returns a status and mqa_last_error() holds a thread-local message.
+ *
+ * All calls are asynchronous with respect to the host: results are valid once
+ * `stream` has been synchronised.  `stream` is a hipStream_t passed as void*
+ * (NULL = the default stream).
+ */
+#ifndef MQA_DECODE_H
+#define MQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mqa_status {
+    MQA_OK = 0,
+    MQA_ERR_NULL = 1,        /* a required pointer is NULL (caches only when Lmax > 0)     */
+    MQA_ERR_SHAPE = 2,       /* a size is negative, Hq/Hkv/D is 0, or Hq % Hkv != 0        */
+    MQA_ERR_UNSUPPORTED = 3, /* D not in {64, 128, 256}, or a size beyond the index range  */
+    MQA_ERR_ALIGN = 4,       /* q / k_cache / v_cache / out not 16-byte aligned            */
+    MQA_ERR_WORKSPACE = 5,   /* split-K scratch could not be allocated                    */
+    MQA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed                */
+    MQA_ERR_ARG = 7          /* a non-finite scale or an invalid option value             */
+} mqa_status;
+
+/* Kernel family for the q.K^T and P.V products. */
+typedef enum mqa_variant {
+    MQA_VARIANT_AUTO = 0, /* planner's choice by group size G = Hq / Hkv                    */
+    MQA_VARIANT_VALU = 1, /* vector-ALU dot products (small groups)                        */
+    MQA_VARIANT_MFMA = 2  /* bf16 matrix-core tiles, 16 query heads per tile (large groups) */
+} mqa_variant;
+
+/* Optional knobs for mqa_decode_attention_ex; zero-initialise for defaults. */
+typedef struct mqa_decode_opts {
+    int variant;          /* mqa_variant                                                */
+    int chunk;            /* positions per split-K chunk; 0 = planner's choice.  Must be
+                             a positive multiple of 128 when set.                        */
+    int combine;          /* 0 = planner's choice, 1 = separate combine kernel,
+                             2 = combine fused into the split kernel (last chunk of
+                             each (sequence, kv head) merges the partials)                */
+    void *ev_main_begin;  /* optional hipEvent_t recorded on `stream` right before the
+                             split-K kernel launch (for timing that kernel alone)         */
+    void *ev_main_end;    /* optional hipEvent_t recorded right after it                  */
+} mqa_decode_opts;
+
+/* What the planner decided for a shape (host-only query, no HIP call). */
+typedef struct mqa_plan_info {
+    int variant;              /* MQA_VARIANT_VALU or MQA_VARIANT_MFMA                  */
+    int chunk;                /* positions per split-K chunk                           */
+    int max_splits;           /* ceil(Lmax / chunk), at least 1                        */
+    int combine;              /* 1 = separate kernel, 2 = fused, 0 = none needed       */
+    int head_blocks;          /* query-head blocks per kv head (VALU path: ceil(G/8))  */
+    long long grid_main;      /* workgroups of the split-K kernel                      */
+    int block_main;           /* threads per workgroup of the split-K kernel           */
+    long long grid_combine;   /* workgroups of the combine kernel (0 if none)          */
+    size_t workspace_bytes;   /* split-K scratch the call needs                        */
+} mqa_plan_info;
+
+/*
+ * One decode step.
+ *   q         bf16 [B, Hq, D], contiguous (D innermost)
+ *   k_cache   bf16 [B, Lmax, Hkv, D], contiguous: position-major per sequence
+ *   v_cache   bf16 [B, Lmax, Hkv, D], contiguous
+ *   seq_lens  int32 [B]: cached positions per sequence (device memory)
+ *   out       fp32 [B, Hq, D], contiguous; fully overwritten
+ *   scale     multiplier of q.k (typically 1/sqrt(D)); must be finite
+ * B == 0 is a no-op (pointers may then be NULL).  Lmax == 0 is allowed: every
+ * output row is zero and k_cache / v_cache may be NULL.
+ */
+mqa_status mqa_decode_attention(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *seq_lens, float *out, int B, int Hq, int Hkv,
+                                int D, int Lmax, float scale, void *stream);
+
+/* Same as mqa_decode_attention with explicit options (opts may be NULL). */
+mqa_status mqa_decode_attention_ex(const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *seq_lens, float *out, int B, int Hq,
+                                   int Hkv, int D, int Lmax, float scale, void *stream,
+                                   const mqa_decode_opts *opts);
+
+/*
+ * Causal attention over whole sequences with no cache, the computation a KV
+ * cache replaces ("How To Scale Your Model", Part 7, passage introducing the
+ * KV cache: a token attends only to itself and earlier tokens).  Row t of
+ * sequence b (t < seq_lens[b]) attends positions 0..t; its result equals a
+ * decode step at length t+1 with query q_seq[b,t].  Rows t >= seq_lens[b] are
+ * written as zeros.  Correctness-grade: it runs the decode kernels once per
+ * row, so it is not a fast prefill.
+ *   q_seq    bf16 [B, Lmax, Hq, D]
+ *   k_cache  bf16 [B, Lmax, Hkv, D];  v_cache likewise
+ *   seq_lens int32 [B] (device)
+ *   out_seq  fp32 [B, Lmax, Hq, D]
+ */
+mqa_status mqa_prefill_attention(const void *q_seq, const void *k_cache, const void *v_cache,
+                                 const int32_t *seq_lens, float *out_seq, int B, int Hq,
+                                 int Hkv, int D, int Lmax, float scale, void *stream);
+
+/*
+ * Host-only validation and planning for a decode call with these sizes and
+ * options: runs every argument check mqa_decode_attention runs (pointers are
+ * not inspected) and, on success, fills *info when info is non-NULL.
+ * Makes no HIP call.
+ */
+mqa_status mqa_decode_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
+                           const mqa_decode_opts *opts, mqa_plan_info *info);
+
+/* Static description of a status code (never NULL). */
+const char *mqa_status_string(mqa_status status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char *mqa_last_error(void);
+
+/* Frees every cached split-K workspace.  Must not race with calls in flight:
+ * synchronise the streams that used the library first. */
+void mqa_release_workspaces(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int mqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQA_DECODE_H */

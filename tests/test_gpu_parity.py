@@ -1,0 +1,209 @@
+"""GPU parity: the HIP library against the CPU fp64 oracle, element by element.
+
+Bar (floating point): every output element satisfies
+    |gpu - oracle| <= 1e-2 + 1e-2 * |oracle|
+(max-abs 1e-2 and max-relative 1e-2, in fp32 output against bf16 inputs).
+Both sides always receive the same bf16 tensors (the GPU copy is moved to the
+host for the oracle); padding beyond each sequence's length is poisoned with
+NaN so a read of it shows.
+
+Small cases cover several tiles, ragged tails, every head size, both kernel
+families, forced split sizes (so the combine kernel runs) and edge cases.  The
+five full-size workloads run in the launch configuration the benchmark uses;
+there the oracle checks a sample of sequences.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gqa_decode_attention_mqa_amd import binding
+from gqa_decode_attention_mqa_amd.workloads import WORKLOADS, Workload, make_inputs, make_prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+RTOL = 1e-2
+DEV = "cuda:0"
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def check_close(gpu, ref, what=""):
+    g = gpu.detach().to("cpu", torch.float64).numpy() if isinstance(gpu, torch.Tensor) else gpu
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.isfinite(g).all(), "%s: non-finite output" % what
+    err = np.abs(g - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    assert not bad.any(), "%s: %d elements out of tolerance, max abs err %.3g" % (what, int(bad.sum()), err.max())
+    return float(err.max())
+
+
+def run_case(w: Workload, variant=None, chunk=None, seq_lens=None, poison=True):
+    inp = to_dev(make_inputs(w, poison_padding=poison, seq_lens=seq_lens))
+    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], variant=variant, chunk=chunk)
+    torch.cuda.synchronize()
+    ref = oracle.decode(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
+    return check_close(out, ref, "%s variant=%s chunk=%s" % (w, variant, chunk))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()
+    yield
+    binding.release_workspaces()
+
+
+def test_tiny_workload_full():
+    print("case tiny", flush=True)
+    run_case(WORKLOADS["tiny"])
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (3, 1), (4, 2), (8, 1), (16, 1), (48, 1), (20, 2), (64, 1), (80, 1)])
+def test_small_shapes(variant, D, G, Hkv):
+    seed = 1000 + D + 7 * G + Hkv + (0 if variant == "mfma" else 1)
+    w = Workload("small", B=3, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=700, seed=seed, len_lo=1, len_hi=700)
+    print("case small", variant, D, G, Hkv, flush=True)
+    # single chunk (direct write) and forced splits (combine kernel) on the same inputs
+    run_case(w, variant=variant)
+    run_case(w, variant=variant, chunk=128)
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+def test_edge_lengths(variant):
+    w = Workload("edges", B=8, Hq=16, Hkv=2, D=128, Lmax=300, seed=77)
+    lens = [0, 1, 2, 63, 64, 65, 299, 300]
+    print("case edges", variant, flush=True)
+    run_case(w, variant=variant, seq_lens=lens)
+    run_case(w, variant=variant, chunk=128, seq_lens=lens)
+
+
+def test_lengths_outside_the_cache_are_clamped():
+    w = Workload("clamp", B=3, Hq=8, Hkv=1, D=64, Lmax=200, seed=78)
+    inp = to_dev(make_inputs(w, seq_lens=[-5, 200, 200]))
+    inp["seq_lens"][2] = 10_000
+    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    ref = oracle.decode(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), [0, 200, 200], inp["scale"])
+    check_close(out, ref, "clamp")
+
+
+def test_empty_batch_and_empty_cache():
+    q = torch.zeros((0, 8, 64), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((0, 16, 1, 64), dtype=torch.bfloat16, device=DEV)
+    out = binding.decode(q, kv, kv, torch.zeros((0,), dtype=torch.int32, device=DEV))
+    assert out.shape == (0, 8, 64)
+    q = torch.randn((2, 8, 64), device=DEV).to(torch.bfloat16)
+    kv = torch.zeros((2, 0, 1, 64), dtype=torch.bfloat16, device=DEV)
+    out = binding.decode(q, kv, kv, torch.zeros((2,), dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), torch.zeros((2, 8, 64)))
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+def test_bitwise_deterministic(variant):
+    w = Workload("det", B=4, Hq=48, Hkv=1, D=256, Lmax=1500, seed=79)
+    inp = to_dev(make_inputs(w))
+    outs = [binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], variant=variant, chunk=256)
+            .clone() for _ in range(5)]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_identical_keys_give_mean_of_values():
+    w = Workload("same-k", B=2, Hq=48, Hkv=1, D=256, Lmax=1000, seed=80, len_lo=500, len_hi=1000)
+    inp = to_dev(make_inputs(w))
+    inp["k"][:] = inp["k"][:, :1].clone()
+    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"]).cpu().double()
+    for b in range(w.B):
+        n = int(inp["seq_lens"][b])
+        mean = inp["v"][b, :n].double().mean(dim=0).cpu()          # [1, D]
+        err = (out[b] - mean).abs().max().item()
+        assert err <= ATOL, err
+
+
+def test_dominant_logit_selects_its_value_row():
+    w = Workload("dom", B=1, Hq=16, Hkv=16, D=128, Lmax=2000, seed=81)
+    inp = make_inputs(w)
+    stars = [(h * 97 + 13) % 2000 for h in range(16)]
+    for h, js in enumerate(stars):
+        inp["k"][0, js, h] = (inp["q"][0, h].float() * 8.0).to(torch.bfloat16)
+    inp = to_dev(inp)
+    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"]).cpu().double()
+    for h, js in enumerate(stars):
+        err = (out[0, h] - inp["v"][0, js, h].cpu().double()).abs().max().item()
+        assert err <= ATOL, (h, err)
+
+
+def test_runs_on_a_side_stream():
+    w = Workload("stream", B=4, Hq=8, Hkv=1, D=128, Lmax=900, seed=82)
+    inp = to_dev(make_inputs(w))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], chunk=128)
+    s.synchronize()
+    ref = oracle.decode(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
+    check_close(out, ref, "side stream")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,Lmax", [(2, 8, 1, 64, 150), (2, 48, 1, 256, 130), (3, 16, 4, 128, 97)])
+def test_prefill_matches_oracle_causal_attention(B, Hq, Hkv, D, Lmax):
+    w = Workload("pf", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, seed=83 + D, len_lo=1, len_hi=Lmax)
+    inp = to_dev(make_prefill_inputs(w, poison_padding=True))
+    print("case prefill", B, Hq, Hkv, D, Lmax, flush=True)
+    out = binding.prefill(inp["q_seq"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    torch.cuda.synchronize()
+    ref = oracle.causal_prefill(inp["q_seq"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(),
+                                inp["scale"])
+    check_close(out, ref, "prefill")
+    # decode at each sequence's full length equals the last prefill row
+    lens = inp["seq_lens"].cpu()
+    q_last = torch.stack([inp["q_seq"][b, int(lens[b]) - 1] for b in range(B)]).contiguous()
+    dec = binding.decode(q_last, inp["k"], inp["v"], inp["seq_lens"], inp["scale"]).cpu()
+    last = torch.stack([out[b, int(lens[b]) - 1].cpu() for b in range(B)])
+    assert (dec - last).abs().max().item() <= ATOL
+
+
+# ------------------------------------------------------ full-size workloads
+
+SAMPLES = {"tiny": None, "palm": 8, "gqa70b": 6, "ragged": 12, "long": 1}
+
+
+def sample_indices(lens: torch.Tensor, count):
+    B = lens.numel()
+    if count is None or count >= B:
+        return list(range(B))
+    order = torch.argsort(lens.cpu())
+    picks = {int(order[0]), int(order[-1]), 0, B - 1}
+    g = torch.Generator().manual_seed(1234)
+    for i in torch.randperm(B, generator=g).tolist():
+        if len(picks) >= count:
+            break
+        picks.add(i)
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name", ["tiny", "palm", "gqa70b", "ragged", "long"])
+def test_full_size_workload_sampled(name):
+    w = WORKLOADS[name]
+    print("case full", name, flush=True)
+    inp = make_inputs(w, device=DEV, poison_padding=w.ragged)
+    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    torch.cuda.synchronize()
+    idx = sample_indices(inp["seq_lens"], SAMPLES[name])
+    sel = torch.tensor(idx, device=DEV)
+    q = inp["q"].index_select(0, sel).cpu()
+    k = inp["k"].index_select(0, sel).cpu()
+    v = inp["v"].index_select(0, sel).cpu()
+    lens = inp["seq_lens"].index_select(0, sel).cpu()
+    ref = oracle.decode(q, k, v, lens, inp["scale"])
+    err = check_close(out.index_select(0, sel), ref, name)
+    print("full %s: %d sequences checked, max abs err %.3g" % (name, len(idx), err), flush=True)
+    assert torch.isfinite(out).all()

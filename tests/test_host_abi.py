@@ -1,0 +1,115 @@
+"""CPU tests of the C ABI's host side: symbols, argument checks and planning.
+
+No GPU is needed: every check in the library runs on the host before any HIP
+call, and mqa_decode_plan makes no HIP call at all.  Calls here only use
+invalid arguments (or NULL data with B == 0), so nothing is ever launched.
+"""
+import ctypes
+import math
+
+import pytest
+
+from gqa_decode_attention_mqa_amd import binding
+
+lib = binding.load_library()
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP, ERR_ARG = range(8)
+
+
+def test_every_declared_symbol_is_exported():
+    names = binding.declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    for s in range(8):
+        assert lib.mqa_status_string(s)
+    assert lib.mqa_status_string(99) == b"unknown status"
+    assert lib.mqa_version() >= 100
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails its checks first
+
+
+def call(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, D=128, Lmax=64, scale=0.1, opts=None):
+    return lib.mqa_decode_attention_ex(q, k, v, lens, out, B, Hq, Hkv, D, Lmax, scale, None,
+                                       ctypes.byref(opts) if opts is not None else None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=0), ERR_NULL), (dict(k=0), ERR_NULL), (dict(v=0), ERR_NULL),
+    (dict(lens=0), ERR_NULL), (dict(out=0), ERR_NULL),
+    (dict(Hq=7), ERR_SHAPE), (dict(Hkv=0), ERR_SHAPE), (dict(Hq=0), ERR_SHAPE),
+    (dict(B=-1), ERR_SHAPE), (dict(Lmax=-3), ERR_SHAPE), (dict(D=0), ERR_SHAPE),
+    (dict(D=96), ERR_UNSUPPORTED), (dict(D=512), ERR_UNSUPPORTED),
+    (dict(q=FAKE + 8), ERR_ALIGN), (dict(k=FAKE + 2), ERR_ALIGN), (dict(out=FAKE + 4), ERR_ALIGN),
+    (dict(lens=FAKE + 2), ERR_ALIGN),
+    (dict(scale=math.inf), ERR_ARG), (dict(scale=math.nan), ERR_ARG),
+])
+def test_invalid_arguments_are_rejected_before_any_hip_call(kw, expect):
+    assert call(**kw) == expect
+    assert lib.mqa_last_error()
+
+
+@pytest.mark.parametrize("opts,expect", [
+    (dict(variant=3), ERR_ARG), (dict(variant=-1), ERR_ARG),
+    (dict(chunk=100), ERR_ARG), (dict(chunk=-128), ERR_ARG),
+    (dict(combine=5), ERR_ARG), (dict(combine=2), ERR_ARG),
+])
+def test_invalid_options_are_rejected(opts, expect):
+    assert call(opts=binding.make_opts(**opts)) == expect
+
+
+def test_empty_batch_is_a_no_op_even_with_null_pointers():
+    assert call(q=0, k=0, v=0, lens=0, out=0, B=0) == OK
+    assert lib.mqa_prefill_attention(0, 0, 0, 0, 0, 0, 8, 1, 64, 16, 0.125, None) == OK
+
+
+def test_prefill_checks_arguments_too():
+    assert lib.mqa_prefill_attention(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 6, 4, 64, 16, 0.1, None) == ERR_SHAPE
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,Lmax", [
+    (1, 8, 1, 64, 128), (64, 48, 1, 256, 2048), (32, 64, 8, 128, 4096),
+    (256, 32, 8, 128, 8192), (4, 48, 1, 256, 131072), (3, 80, 1, 128, 1000), (2, 6, 2, 64, 1),
+    (5, 8, 8, 256, 0),
+])
+def test_plan_invariants(B, Hq, Hkv, D, Lmax):
+    p = binding.plan(B, Hq, Hkv, D, Lmax)
+    G = Hq // Hkv
+    assert p["chunk"] > 0 and p["chunk"] % 128 == 0
+    assert p["max_splits"] >= 1 and p["chunk"] * p["max_splits"] >= Lmax
+    assert (p["max_splits"] - 1) * p["chunk"] < max(Lmax, 1)
+    assert p["variant"] == ("mfma" if G >= 16 else "valu")
+    per_block = min(G, 64) if p["variant"] == "mfma" else min(G, 8)
+    assert p["head_blocks"] * per_block >= G
+    assert p["grid_main"] == B * Hkv * p["max_splits"] * p["head_blocks"]
+    if p["max_splits"] > 1:
+        assert p["combine"] == 1 and p["grid_combine"] == B * Hq
+        assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (D + 1) * 4
+    else:
+        assert p["combine"] == 0 and p["workspace_bytes"] == 0
+
+
+def test_forced_variant_and_chunk_are_honoured():
+    p = binding.plan(4, 8, 1, 128, 1000, variant="mfma", chunk=256)
+    assert p["variant"] == "mfma" and p["chunk"] == 256 and p["max_splits"] == 4
+    p = binding.plan(4, 48, 1, 256, 1000, variant="valu")
+    assert p["variant"] == "valu" and p["head_blocks"] == 6
+
+
+def test_chunk_schedule_covers_every_valid_position_once():
+    """The split kernel gives workgroup (unit, s) positions [s*chunk, min((s+1)*chunk, len))."""
+    Lmax = 8192
+    p = binding.plan(256, 32, 8, 128, Lmax)
+    C, S = p["chunk"], p["max_splits"]
+    for n in [0, 1, 127, 128, 129, C - 1, C, C + 1, Lmax - 1, Lmax]:
+        seen = []
+        for s in range(S):
+            p0 = s * C
+            if s > 0 and p0 >= n:
+                continue
+            seen.extend(range(p0, min(p0 + C, n)))
+        assert seen == list(range(n))
