@@ -169,6 +169,9 @@ def main(argv=None):
 
     # per-step events around the split-K kernel, recorded by the library on its stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for b, e in evs:  # torch creates the HIP event on first record; the library re-records it
+        b.record(stream)
+        e.record(stream)
     opts = [binding.make_opts(args.variant, args.chunk, None, b.cuda_event, e.cuda_event) for b, e in evs]
     t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

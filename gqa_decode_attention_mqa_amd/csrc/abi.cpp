@@ -54,6 +54,13 @@ mqa_status get_workspace(hipStream_t stream, size_t bytes, void** out) {
             mqa::set_error(std::string("hipMalloc of split-K workspace failed: ") + hipGetErrorString(e));
             return MQA_ERR_WORKSPACE;
         }
+        // The fused combine's arrival counters must start at zero; every call
+        // leaves them at zero again, so this is needed once per allocation.
+        e = hipMemset(p, 0, bytes);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e, "hipMemset of split-K workspace");
+        }
         ws.ptr = p;
         ws.bytes = bytes;
     }
@@ -85,6 +92,9 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.out = out;
     a.part_o = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_o_offset) : nullptr;
     a.part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_lse_offset) : nullptr;
+    a.counters = ws ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + plan.counters_offset) : nullptr;
+    a.units = plan.rows * Hkv;
+    a.fused = plan.combine == 2 ? 1 : 0;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.D = D;

@@ -1,18 +1,26 @@
-// Log-sum-exp merge of split-K partials.
+// Log-sum-exp merge of split-K partials (separate kernel, for many splits).
 //
 // A sequence whose positions were cut into n chunks has, per query head, n
 // normalised partial outputs O_s = (sum_{j in s} w_j v_j) / l_s and base-2
 // log-sum-exps lse_s = m_s + log2(l_s).  With M = max_s lse_s the full result is
 //     out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M),
-// an exact identity of softmax over a partition of the positions.  The chunks
-// are visited in ascending order, so the result is bitwise reproducible for a
-// given plan.  One workgroup per (row, query head); threads run along d.
+// an exact identity of softmax over a partition of the positions.
+//
+// One workgroup per (row, query head), 256 threads.  Thread t owns a 16-byte
+// column slot (t mod D/4) and the chunks s = t div (D/4), step 256/(D/4), so
+// several chunks are read in parallel; the per-thread sums are then added in a
+// fixed order through LDS, so the result is bitwise reproducible for a plan.
 #include "kernel_common.hpp"
 #include "launch.hpp"
 
 namespace mqa {
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+    __shared__ float s_max[4];
+    __shared__ __attribute__((aligned(16))) f32x4_t s_acc[256];
+    __shared__ float s_w[256];
+
+    const int tid = threadIdx.x;
     const long long rh = blockIdx.x;
     const int h = (int)(rh % a.Hq);
     const long long row = rh / a.Hq;
@@ -27,24 +35,42 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const float* po = a.part_o + first * a.D;
     const size_t step = (size_t)a.G;  // partials of consecutive splits are G heads apart
 
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lse[s * step]);
+    // M = max over chunks (threads stride over the chunks, then a block max)
+    float m = -INFINITY;
+    for (int s = tid; s < nsplit; s += 256) m = fmaxf(m, lse[s * step]);
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((tid & 63) == 0) s_max[tid >> 6] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
 
-    float* dst = a.out + ((size_t)row * a.Hq + h) * a.D;
-    for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
-        float acc = 0.f, wsum = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float wgt = __builtin_amdgcn_exp2f(lse[s * step] - M);
-            acc += wgt * po[s * step * a.D + d];
-            wsum += wgt;
+    const int slots = a.D / 4;          // 16, 32 or 64
+    const int lanes_per_slot = 256 / slots;
+    const int slot = tid % slots, sl = tid / slots;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+#pragma unroll 4
+    for (int s = sl; s < nsplit; s += lanes_per_slot) {
+        const float wgt = __builtin_amdgcn_exp2f(lse[s * step] - M);
+        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(po + s * step * a.D + 4 * slot);
+        acc += wgt * o;
+        wsum += wgt;
+    }
+    s_acc[tid] = acc;
+    s_w[tid] = wsum;
+    __syncthreads();
+    if (sl == 0) {
+        for (int j = 1; j < lanes_per_slot; ++j) {
+            acc += s_acc[j * slots + slot];
+            wsum += s_w[j * slots + slot];
         }
-        dst[d] = acc / wsum;
+        float* dst = a.out + ((size_t)row * a.Hq + h) * a.D;
+        *reinterpret_cast<f32x4_t*>(dst + 4 * slot) = acc * (1.f / wsum);
     }
 }
 
 hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream) {
     if (p.grid_combine <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.grid_combine), dim3(a.D), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ struct MfmaCfg {
     static_assert(TILE % (16 * NW) == 0, "q.K tiles must cover the tile");
     static_assert(PVK >= 1, "each P.V wave needs a whole 32-position k-step");
     static_assert(LDS_BYTES <= 65536, "static LDS budget");
+    static_assert(BODY_BYTES >= (kFusedMaxSplits + 2) * GP * 4, "fused-combine weights fit in the body");
 };
 
 template <int D, int NG>
@@ -68,9 +69,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const int lane = tid & 63, w = tid >> 6;
     const int li = lane & 15, kg = lane >> 4;
 
-    const long long x = blockIdx.x;
-    const int s = (int)(x % a.max_splits);
-    const long long unit = x / a.max_splits;
+    long long unit;
+    int s;
+    map_block(blockIdx.x, a.units, a.max_splits, &unit, &s);
     const int kvh = (int)(unit % a.Hkv);
     const long long row = unit / a.Hkv;
     const int g0 = blockIdx.y * C::GP;
@@ -91,7 +92,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         if (g < gcnt) val = load_u32x4(qrow + (size_t)g * D + dc * 8);
         *reinterpret_cast<u32x4_t*>(qs + g * C::QLD + dc * 8) = val;
     }
-    __syncthreads();
 
     const size_t pos_stride = (size_t)a.Hkv * D;  // elements between consecutive positions
     const uint16_t* kbase = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
@@ -99,6 +99,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const int ds = w % C::WD, ts = w / C::WD;
     const int vcol = 64 * ds + 4 * li;        // this lane's 4 V columns in P.V
     const float qk = a.qk_log2;
+    const int last = p1 - 1;                  // loads past the end re-read this row
 
     float m_run[NG], l_run[NG];
     f32x4_t oacc[4][NG];
@@ -110,25 +111,23 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         for (int j = 0; j < 4; ++j) oacc[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    u32x4_t kreg[C::QKM][C::KS];
-    u32x2_t vreg[C::PVK][8];
-
+    // Loads are unconditional: a position at or past p1 is clamped to the last
+    // valid row.  Its logit is masked to -inf (so its weight is exactly 0 and the
+    // clamped V row adds nothing); padding is never read.
     auto load_tile = [&](int tile0, u32x4_t (&kr)[C::QKM][C::KS], u32x2_t (&vr)[C::PVK][8]) {
 #pragma unroll
         for (int mq = 0; mq < C::QKM; ++mq) {
-            const int t = tile0 + 16 * (w * C::QKM + mq) + li;
-            const bool ok = t < p1;
+            const int t = min(tile0 + 16 * (w * C::QKM + mq) + li, last);
             const uint16_t* src = kbase + (size_t)t * pos_stride + kg * 8;
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks)
-                kr[mq][ks] = ok ? load_u32x4(src + ks * 32) : u32x4_t{0u, 0u, 0u, 0u};
+            for (int ks = 0; ks < C::KS; ++ks) kr[mq][ks] = load_nt_u32x4(src + ks * 32);
         }
 #pragma unroll
         for (int kk = 0; kk < C::PVK; ++kk) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int t = tile0 + ts * (C::TILE / C::WT) + 32 * kk + 8 * kg + e;
-                vr[kk][e] = (t < p1) ? load_u32x2(vbase + (size_t)t * pos_stride + vcol) : u32x2_t{0u, 0u};
+                const int t = min(tile0 + ts * (C::TILE / C::WT) + 32 * kk + 8 * kg + e, last);
+                vr[kk][e] = load_nt_u32x2(vbase + (size_t)t * pos_stride + vcol);
             }
         }
     };
@@ -150,7 +149,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             }
         }
         // ---- scale, mask the ragged tail, per-wave maximum per head
-        float sv[C::QKM][NG][4];
         float wmax[NG];
 #pragma unroll
         for (int n = 0; n < NG; ++n) {
@@ -161,7 +159,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int t = tile0 + 16 * (w * C::QKM + mq) + 4 * kg + r;
                     const float val = (t < p1) ? sacc[mq][n][r] * qk : -INFINITY;
-                    sv[mq][n][r] = val;
+                    sacc[mq][n][r] = val;
                     mx = fmaxf(mx, val);
                 }
             mx = fmaxf(mx, shfl_xor_f32(mx, 16));
@@ -192,7 +190,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 uint32_t pb[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    pb[r] = f32_to_bf16_bits(__builtin_amdgcn_exp2f(sv[mq][n][r] - m_run[n]));
+                    pb[r] = f32_to_bf16_bits(__builtin_amdgcn_exp2f(sacc[mq][n][r] - m_run[n]));
                     lsum += bf16_bits_to_f32(pb[r]);
                 }
                 u32x2_t packed = {pack_bf16x2(pb[0], pb[1]), pack_bf16x2(pb[2], pb[3])};
@@ -227,22 +225,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         }
     };
 
-    if (p0 < p1) load_tile(p0, kreg, vreg);
-    for (int tile0 = p0; tile0 < p1; tile0 += C::TILE) {
-        u32x4_t knext[C::QKM][C::KS];
-        u32x2_t vnext[C::PVK][8];
-        const bool more = tile0 + C::TILE < p1;
-        if (more) load_tile(tile0 + C::TILE, knext, vnext);
-        compute_tile(tile0, kreg, vreg);
-        if (more) {
-#pragma unroll
-            for (int mq = 0; mq < C::QKM; ++mq)
-#pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks) kreg[mq][ks] = knext[mq][ks];
-#pragma unroll
-            for (int kk = 0; kk < C::PVK; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vreg[kk][e] = vnext[kk][e];
+    // Two register stages: while a tile is computed, the next one is in flight.
+    if (p0 < p1) {
+        u32x4_t kA[C::QKM][C::KS], kB[C::QKM][C::KS];
+        u32x2_t vA[C::PVK][8], vB[C::PVK][8];
+        load_tile(p0, kA, vA);
+        __syncthreads();  // q staged
+        int tile0 = p0;
+        while (true) {
+            load_tile(tile0 + C::TILE, kB, vB);
+            compute_tile(tile0, kA, vA);
+            tile0 += C::TILE;
+            if (tile0 >= p1) break;
+            load_tile(tile0 + C::TILE, kA, vA);
+            compute_tile(tile0, kB, vB);
+            tile0 += C::TILE;
+            if (tile0 >= p1) break;
         }
     }
 
@@ -269,51 +267,58 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 for (int r = 0; r < 4; ++r) dst[((j * NG + n) * 4 + r) * 64 + lane] = oacc[j][n][r];
     }
     __syncthreads();
-    if (ts != 0) return;
-
-    float inv_l[NG], lse2[NG];
-#pragma unroll
-    for (int n = 0; n < NG; ++n) {
-        float L = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < C::NW; ++ww) L += red[ww * C::GP + 16 * n + li];
-        inv_l[n] = L > 0.f ? 1.f / L : 0.f;
-        lse2[n] = m_run[n] + __log2f(L);
-    }
-    if (C::WT > 1) {
-#pragma unroll
-        for (int tt = 1; tt < C::WT; ++tt) {
-            const float* src = merge + (size_t)((tt - 1) * C::WD + ds) * (4 * NG * 4 * 64);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int n = 0; n < NG; ++n)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) oacc[j][n][r] += src[((j * NG + n) * 4 + r) * 64 + lane];
-        }
-    }
 
     const bool direct = nsplit == 1;
+    if (ts == 0) {
+        float inv_l[NG], lse2[NG];
 #pragma unroll
-    for (int n = 0; n < NG; ++n) {
-        const int g = 16 * n + li;
-        if (g >= gcnt) continue;
-        const int gh = g0 + g;  // head index inside the group
-        float* dst;
-        if (direct)
-            dst = a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D;
-        else
-            dst = a.part_o + (((size_t)unit * a.max_splits + s) * a.G + gh) * D;
+        for (int n = 0; n < NG; ++n) {
+            float L = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int d = 64 * ds + 16 * kg + 4 * r;
-            f32x4_t o4 = {oacc[0][n][r] * inv_l[n], oacc[1][n][r] * inv_l[n],
-                          oacc[2][n][r] * inv_l[n], oacc[3][n][r] * inv_l[n]};
-            *reinterpret_cast<f32x4_t*>(dst + d) = o4;
+            for (int ww = 0; ww < C::NW; ++ww) L += red[ww * C::GP + 16 * n + li];
+            inv_l[n] = L > 0.f ? 1.f / L : 0.f;
+            lse2[n] = m_run[n] + __log2f(L);
         }
-        if (!direct && ds == 0 && kg == 0)
-            a.part_lse[((size_t)unit * a.max_splits + s) * a.G + gh] = lse2[n];
+        if (C::WT > 1) {
+#pragma unroll
+            for (int tt = 1; tt < C::WT; ++tt) {
+                const float* src = merge + (size_t)((tt - 1) * C::WD + ds) * (4 * NG * 4 * 64);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int n = 0; n < NG; ++n)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) oacc[j][n][r] += src[((j * NG + n) * 4 + r) * 64 + lane];
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+            const int g = 16 * n + li;
+            if (g >= gcnt) continue;
+            const int gh = g0 + g;  // head index inside the group
+            float* dst;
+            if (direct)
+                dst = a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D;
+            else
+                dst = a.part_o + (((size_t)unit * a.max_splits + s) * a.G + gh) * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 64 * ds + 16 * kg + 4 * r;
+                f32x4_t o4 = {oacc[0][n][r] * inv_l[n], oacc[1][n][r] * inv_l[n],
+                              oacc[2][n][r] * inv_l[n], oacc[3][n][r] * inv_l[n]};
+                *reinterpret_cast<f32x4_t*>(dst + d) = o4;
+            }
+            if (!direct && ds == 0 && kg == 0)
+                a.part_lse[((size_t)unit * a.max_splits + s) * a.G + gh] = lse2[n];
+        }
     }
+    if (direct || !a.fused) return;
+    // ---- fused combine: the last chunk of this (row, kv head, head block) merges all partials
+    int* flag = reinterpret_cast<int*>(red);
+    if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, flag)) return;
+    float* wts = reinterpret_cast<float*>(smem + C::RED_BYTES);
+    fused_combine(a, unit, nsplit, g0, gcnt, a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D,
+                  wts, C::GP);
 }
 
 template <int D>

@@ -59,14 +59,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     __shared__ float mrg_m[NW][GB];
     __shared__ float mrg_l[NW][GB];
     __shared__ __attribute__((aligned(16))) float mrg_o[NW][GB][D];
+    __shared__ int s_flag;
+    static_assert(NW * D >= kFusedMaxSplits + 2, "fused-combine weights fit in mrg_o");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int rl = lane % RL, rr = lane / RL;
 
-    const long long x = blockIdx.x;
-    const int s = (int)(x % a.max_splits);
-    const long long unit = x / a.max_splits;
+    long long unit;
+    int s;
+    map_block(blockIdx.x, a.units, a.max_splits, &unit, &s);
     const int kvh = (int)(unit % a.Hkv);
     const long long row = unit / a.Hkv;
     const int g0 = blockIdx.y * GB;
@@ -108,12 +110,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     for (int blk = w; blk < nblk; blk += NW) {
         const int t0 = p0 + blk * WB;
         u32x4_t kr[NB], vr[NB];
+        // Unconditional loads; a position past the end re-reads the last valid row,
+        // whose logit is masked to -inf below (weight exactly 0).
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
-            const int t = t0 + st * RS + rr;
-            const bool ok = t < p1;
-            kr[st] = ok ? load_u32x4(kbase + (size_t)t * pos_stride) : u32x4_t{0u, 0u, 0u, 0u};
-            vr[st] = ok ? load_u32x4(vbase + (size_t)t * pos_stride) : u32x4_t{0u, 0u, 0u, 0u};
+            const int t = min(t0 + st * RS + rr, p1 - 1);
+            kr[st] = load_nt_u32x4(kbase + (size_t)t * pos_stride);
+            vr[st] = load_nt_u32x4(vbase + (size_t)t * pos_stride);
         }
         // logits (base-2 units), masked past the end
         float sc[NB][GB];
@@ -218,6 +221,11 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             if (d == 0) a.part_lse[part] = M + __log2f(L);
         }
     }
+    if (direct || !a.fused) return;
+    // Fused combine: the last chunk of this (row, kv head, head block) merges all partials.
+    if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, &s_flag)) return;
+    fused_combine(a, unit, nsplit, g0, gcnt, a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D,
+                  &mrg_o[0][0][0], GB);
 }
 
 template <int D>

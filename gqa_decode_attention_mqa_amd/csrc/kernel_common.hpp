@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "plan.hpp"
+
 namespace mqa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -27,9 +29,13 @@ struct DecodeArgs {
     float* out;                // fp32 [rows, Hq, D]
     float* part_o;             // fp32 [rows * Hkv * max_splits, G, D], O / l per chunk
     float* part_lse;           // fp32 [rows * Hkv * max_splits, G], m + log2(l) (base 2)
+    uint32_t* counters;        // [rows * Hkv * head_blocks] arrival counters (fused combine);
+                               // zero between calls: the last arriving chunk resets its counter
+    long long units;           // rows * Hkv
     int Hq, Hkv, D, Lmax, G;
     int chunk, max_splits;
     int causal;                // 0 decode, 1 causal rows
+    int fused;                 // 1: the last chunk of a unit merges the partials itself
     float qk_log2;             // scale * log2(e): logits are kept in base-2 units
 };
 
@@ -60,6 +66,31 @@ __device__ __forceinline__ void row_extent(const int32_t* seq_lens, long long ro
     }
     *b_out = b;
     *len_out = len;
+}
+
+// Workgroup -> (unit, chunk).  Consecutive workgroup ids are dispatched to the
+// 8 XCDs in turn (id mod 8), and each XCD has its own L2.  When the number of
+// units is a multiple of 8, all chunks of a unit are given ids with the same
+// residue mod 8, so they run on one XCD and their partials meet in one L2.
+__device__ __forceinline__ void map_block(long long x, long long units, int max_splits,
+                                          long long* unit, int* split) {
+    if ((units & 7) == 0) {
+        const long long r = x >> 3;
+        *split = (int)(r % max_splits);
+        *unit = (r / max_splits) * 8 + (x & 7);
+    } else {
+        *unit = x / max_splits;
+        *split = (int)(x % max_splits);
+    }
+}
+
+// Streaming 128/64-bit loads that bypass cache retention (K/V rows are read
+// exactly once).
+__device__ __forceinline__ u32x4_t load_nt_u32x4(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ u32x2_t load_nt_u32x2(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
 }
 
 // Round-to-nearest-even float -> bf16 bits (inputs here are finite or +0).
@@ -105,6 +136,62 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
 }
 constexpr uint32_t kPermLoHalves = 0x05040100u;  // (lo.lo16) | (hi.lo16 << 16)
 constexpr uint32_t kPermHiHalves = 0x07060302u;  // (lo.hi16) | (hi.hi16 << 16)
+
+// Fused log-sum-exp combine, run by the last chunk of a unit to arrive.  The
+// caller has already written its own partial.  Returns after every thread of
+// the workgroup has finished (it contains barriers: call it from all threads).
+//   wts: LDS scratch of kFusedMaxSplits * gp + 2 * gp floats, gp >= gcnt.
+__device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long unit, int nsplit,
+                                              int g0, int gcnt, float* out_row, float* wts, int gp) {
+    const int tid = threadIdx.x;
+    const int nthreads = blockDim.x;
+    float* Mg = wts + kFusedMaxSplits * gp;
+    float* Wg = Mg + gp;
+    const size_t base = (size_t)unit * a.max_splits * a.G;  // partial (unit, split 0, head 0)
+    if (tid < gcnt) {
+        float M = -INFINITY;
+        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_lse[base + (size_t)s * a.G + g0 + tid]);
+        float W = 0.f;
+        for (int s = 0; s < nsplit; ++s) {
+            const float w = __builtin_amdgcn_exp2f(a.part_lse[base + (size_t)s * a.G + g0 + tid] - M);
+            wts[s * gp + tid] = w;
+            W += w;
+        }
+        Mg[tid] = M;
+        Wg[tid] = 1.f / W;
+    }
+    __syncthreads();
+    const int D = a.D;
+    const int slots = gcnt * (D / 4);
+    for (int idx = tid; idx < slots; idx += nthreads) {
+        const int g = idx / (D / 4), d4 = idx % (D / 4);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < nsplit; ++s) {
+            const f32x4_t o = *reinterpret_cast<const f32x4_t*>(
+                a.part_o + (base + (size_t)s * a.G + g0 + g) * D + 4 * d4);
+            acc += wts[s * gp + g] * o;
+        }
+        *reinterpret_cast<f32x4_t*>(out_row + (size_t)g * D + 4 * d4) = acc * Wg[g];
+    }
+}
+
+// Arrival bookkeeping of the fused combine: returns true in every thread of
+// the last workgroup to finish a chunk of this unit (and resets the counter).
+// The caller must have written its partial before calling.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int nsplit, int* flag_lds) {
+    __threadfence();  // release this workgroup's partial to the device
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = atomicAdd(counter, 1u);
+        const int last = old == (uint32_t)(nsplit - 1);
+        if (last) atomicExch(counter, 0u);
+        *flag_lds = last;
+    }
+    __syncthreads();
+    const bool last = *flag_lds != 0;
+    if (last) __threadfence();  // acquire the other chunks' partials
+    return last;
+}
 
 __device__ __forceinline__ u32x4_t load_u32x4(const uint16_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);

@@ -68,8 +68,6 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         return fail(MQA_ERR_ARG, "chunk must be 0 or a positive multiple of 128");
     if (o.combine < 0 || o.combine > 2)
         return fail(MQA_ERR_ARG, "combine must be 0, 1 or 2");
-    if (o.combine == 2)
-        return fail(MQA_ERR_ARG, "the fused combine is not available in this build");
 
     Plan p;
     p.G = Hq / Hkv;
@@ -111,14 +109,21 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (grid limit)");
 
     if (p.max_splits > 1 && p.rows > 0) {
-        p.combine = (o.combine == 2) ? 2 : 1;
+        if (o.combine == 2 && p.max_splits > kFusedMaxSplits)
+            return fail(MQA_ERR_ARG, "the fused combine handles at most 16 chunks per sequence");
+        if (o.combine == 0)
+            p.combine = p.max_splits <= kFusedMaxSplits ? 2 : 1;
+        else
+            p.combine = o.combine;
         p.grid_combine = (p.combine == 1) ? p.rows * Hq : 0;
         if (p.grid_combine > kMaxGrid)
             return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (combine grid limit)");
         const size_t parts = (size_t)p.rows * Hkv * p.max_splits * p.G;
+        const size_t counters = (size_t)p.rows * Hkv * p.head_blocks;
         p.part_o_offset = 0;
         p.part_lse_offset = round_up((long long)(parts * D * sizeof(float)), 256);
-        p.workspace_bytes = p.part_lse_offset + round_up((long long)(parts * sizeof(float)), 256);
+        p.counters_offset = p.part_lse_offset + round_up((long long)(parts * sizeof(float)), 256);
+        p.workspace_bytes = p.counters_offset + round_up((long long)(counters * sizeof(uint32_t)), 256);
     }
     *plan = p;
     return MQA_OK;

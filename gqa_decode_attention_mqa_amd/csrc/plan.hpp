@@ -23,6 +23,8 @@ constexpr int kMfmaHeadsPerTile = 16;
 constexpr int kMfmaMaxHeads = 64;
 // Most query heads one VALU workgroup serves.
 constexpr int kValuMaxHeads = 8;
+// Most chunks per unit the fused combine handles (its weights live in LDS).
+constexpr int kFusedMaxSplits = 16;
 
 struct Plan {
     int variant = MQA_VARIANT_VALU;  // resolved, never AUTO
@@ -36,9 +38,10 @@ struct Plan {
     long long grid_main = 0;         // workgroups along x of the split kernel
     int block_main = 256;
     long long grid_combine = 0;
-    size_t workspace_bytes = 0;      // partial outputs + partial LSEs
+    size_t workspace_bytes = 0;      // partial outputs + partial LSEs + arrival counters
     size_t part_o_offset = 0;        // byte offsets inside the workspace
     size_t part_lse_offset = 0;
+    size_t counters_offset = 0;      // uint32 per (row, kv head, head block); must start at zero
 };
 
 // Thread-local last-error text.

@@ -79,9 +79,11 @@ typedef struct mqa_decode_opts {
     int variant;          /* mqa_variant                                                */
     int chunk;            /* positions per split-K chunk; 0 = planner's choice.  Must be
                              a positive multiple of 128 when set.                        */
-    int combine;          /* 0 = planner's choice, 1 = separate combine kernel,
-                             2 = combine fused into the split kernel (last chunk of
-                             each (sequence, kv head) merges the partials)                */
+    int combine;          /* 0 = planner's choice (fused when a sequence has at most 16
+                             chunks, else separate), 1 = separate combine kernel,
+                             2 = combine fused into the split kernel: the last chunk of
+                             each (sequence, kv head) to finish merges the partials
+                             (at most 16 chunks per sequence, else MQA_ERR_ARG)          */
     void *ev_main_begin;  /* optional hipEvent_t recorded on `stream` right before the
                              split-K kernel launch (for timing that kernel alone)         */
     void *ev_main_end;    /* optional hipEvent_t recorded right after it                  */

@@ -43,12 +43,13 @@ def check_close(gpu, ref, what=""):
     return float(err.max())
 
 
-def run_case(w: Workload, variant=None, chunk=None, seq_lens=None, poison=True):
+def run_case(w: Workload, variant=None, chunk=None, seq_lens=None, poison=True, combine=None):
     inp = to_dev(make_inputs(w, poison_padding=poison, seq_lens=seq_lens))
-    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], variant=variant, chunk=chunk)
+    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], variant=variant, chunk=chunk,
+                         combine=combine)
     torch.cuda.synchronize()
     ref = oracle.decode(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
-    return check_close(out, ref, "%s variant=%s chunk=%s" % (w, variant, chunk))
+    return check_close(out, ref, "%s variant=%s chunk=%s combine=%s" % (w, variant, chunk, combine))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -67,14 +68,17 @@ def test_tiny_workload_full():
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
 @pytest.mark.parametrize("D", [64, 128, 256])
-@pytest.mark.parametrize("G,Hkv", [(1, 2), (3, 1), (4, 2), (8, 1), (16, 1), (48, 1), (20, 2), (64, 1), (80, 1)])
-def test_small_shapes(variant, D, G, Hkv):
+@pytest.mark.parametrize("G,Hkv,B", [(1, 2, 3), (3, 1, 3), (4, 2, 4), (8, 1, 3), (16, 1, 8), (48, 1, 3),
+                                     (20, 2, 3), (64, 1, 3), (80, 1, 3)])
+def test_small_shapes(variant, D, G, Hkv, B):
     seed = 1000 + D + 7 * G + Hkv + (0 if variant == "mfma" else 1)
-    w = Workload("small", B=3, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=700, seed=seed, len_lo=1, len_hi=700)
-    print("case small", variant, D, G, Hkv, flush=True)
-    # single chunk (direct write) and forced splits (combine kernel) on the same inputs
+    w = Workload("small", B=B, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=700, seed=seed, len_lo=1, len_hi=700)
+    print("case small", variant, D, G, Hkv, B, flush=True)
+    # planner's chunk, then forced 128-position chunks merged by the fused
+    # combine and by the separate combine kernel, all on the same inputs
     run_case(w, variant=variant)
     run_case(w, variant=variant, chunk=128)
+    run_case(w, variant=variant, chunk=128, combine="separate")
 
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
@@ -84,6 +88,19 @@ def test_edge_lengths(variant):
     print("case edges", variant, flush=True)
     run_case(w, variant=variant, seq_lens=lens)
     run_case(w, variant=variant, chunk=128, seq_lens=lens)
+    run_case(w, variant=variant, chunk=128, seq_lens=lens, combine="separate")
+
+
+@pytest.mark.parametrize("combine", ["fused", "separate"])
+def test_many_chunks_and_shape_changes_reuse_the_workspace(combine):
+    """Fused arrival counters must be back at zero after every call, whatever the shape."""
+    cases = [Workload("ws1", B=8, Hq=48, Hkv=1, D=256, Lmax=2000, seed=90, len_lo=1, len_hi=2000),
+             Workload("ws2", B=16, Hq=16, Hkv=2, D=128, Lmax=1900, seed=91, len_lo=1000, len_hi=1900),
+             Workload("ws3", B=8, Hq=48, Hkv=1, D=256, Lmax=2000, seed=92, len_lo=1, len_hi=2000)]
+    for w in cases:
+        for variant in ("mfma", "valu"):
+            print("case ws", w.name, combine, variant, flush=True)
+            run_case(w, variant=variant, chunk=128, combine=combine)
 
 
 def test_lengths_outside_the_cache_are_clamped():

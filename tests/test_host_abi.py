@@ -56,10 +56,17 @@ def test_invalid_arguments_are_rejected_before_any_hip_call(kw, expect):
 @pytest.mark.parametrize("opts,expect", [
     (dict(variant=3), ERR_ARG), (dict(variant=-1), ERR_ARG),
     (dict(chunk=100), ERR_ARG), (dict(chunk=-128), ERR_ARG),
-    (dict(combine=5), ERR_ARG), (dict(combine=2), ERR_ARG),
+    (dict(combine=5), ERR_ARG), (dict(combine=-1), ERR_ARG),
 ])
 def test_invalid_options_are_rejected(opts, expect):
     assert call(opts=binding.make_opts(**opts)) == expect
+
+
+def test_fused_combine_is_refused_beyond_its_split_limit():
+    # 100000 positions in chunks of 128 -> 782 chunks > 16
+    assert call(Lmax=100000, opts=binding.make_opts(chunk=128, combine=2)) == ERR_ARG
+    assert binding.plan(2, 8, 2, 128, 100000, chunk=128)["combine"] == 1
+    assert binding.plan(2, 8, 2, 128, 2048, chunk=128)["combine"] == 2
 
 
 def test_empty_batch_is_a_no_op_even_with_null_pointers():
@@ -87,8 +94,10 @@ def test_plan_invariants(B, Hq, Hkv, D, Lmax):
     assert p["head_blocks"] * per_block >= G
     assert p["grid_main"] == B * Hkv * p["max_splits"] * p["head_blocks"]
     if p["max_splits"] > 1:
-        assert p["combine"] == 1 and p["grid_combine"] == B * Hq
-        assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (D + 1) * 4
+        fused = p["max_splits"] <= 16
+        assert p["combine"] == (2 if fused else 1)
+        assert p["grid_combine"] == (0 if fused else B * Hq)
+        assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (D + 1) * 4 + B * Hkv * 4
     else:
         assert p["combine"] == 0 and p["workspace_bytes"] == 0
 
