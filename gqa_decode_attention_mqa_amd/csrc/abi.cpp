@@ -17,10 +17,15 @@ namespace {
 
 using mqa::Plan;
 
-// Split-K scratch, one buffer per (device, stream), grown on demand.
+// Split-K scratch per (device, stream), grown on demand: one buffer for the
+// partial outputs and LSEs, and a separate one for the fused combine's arrival
+// counters.  The counters are zeroed when allocated and every call leaves them
+// at zero, so nothing else may ever write that buffer.
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
+    uint32_t* counters = nullptr;
+    size_t ncounters = 0;
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
@@ -30,19 +35,25 @@ mqa_status hip_fail(hipError_t e, const char* what) {
     return MQA_ERR_HIP;
 }
 
-mqa_status get_workspace(hipStream_t stream, size_t bytes, void** out) {
+mqa_status get_workspace(hipStream_t stream, size_t bytes, size_t ncounters, void** out,
+                         uint32_t** counters_out) {
     *out = nullptr;
-    if (bytes == 0) return MQA_OK;
+    *counters_out = nullptr;
+    if (bytes == 0 && ncounters == 0) return MQA_OK;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
-    if (ws.bytes < bytes) {
+    const bool grow_parts = ws.bytes < bytes;
+    const bool grow_counters = ws.ncounters < ncounters;
+    if ((grow_parts && ws.ptr) || (grow_counters && ws.counters)) {
+        // The old buffers may still be in use by work queued on this stream.
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    }
+    if (grow_parts) {
         if (ws.ptr) {
-            // The old buffer may still be read by work queued on this stream.
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
             e = hipFree(ws.ptr);
             ws.ptr = nullptr;
             ws.bytes = 0;
@@ -54,17 +65,32 @@ mqa_status get_workspace(hipStream_t stream, size_t bytes, void** out) {
             mqa::set_error(std::string("hipMalloc of split-K workspace failed: ") + hipGetErrorString(e));
             return MQA_ERR_WORKSPACE;
         }
-        // The fused combine's arrival counters must start at zero; every call
-        // leaves them at zero again, so this is needed once per allocation.
-        e = hipMemset(p, 0, bytes);
-        if (e != hipSuccess) {
-            (void)hipFree(p);
-            return hip_fail(e, "hipMemset of split-K workspace");
-        }
         ws.ptr = p;
         ws.bytes = bytes;
     }
+    if (grow_counters) {
+        if (ws.counters) {
+            e = hipFree(ws.counters);
+            ws.counters = nullptr;
+            ws.ncounters = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+        }
+        void* p = nullptr;
+        e = hipMalloc(&p, ncounters * sizeof(uint32_t));
+        if (e != hipSuccess) {
+            mqa::set_error(std::string("hipMalloc of arrival counters failed: ") + hipGetErrorString(e));
+            return MQA_ERR_WORKSPACE;
+        }
+        e = hipMemset(p, 0, ncounters * sizeof(uint32_t));
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e, "hipMemset of arrival counters");
+        }
+        ws.counters = static_cast<uint32_t*>(p);
+        ws.ncounters = ncounters;
+    }
     *out = ws.ptr;
+    *counters_out = ws.counters;
     return MQA_OK;
 }
 
@@ -81,7 +107,8 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
     void* ws = nullptr;
-    st = get_workspace(stream, plan.workspace_bytes, &ws);
+    uint32_t* counters = nullptr;
+    st = get_workspace(stream, plan.workspace_bytes, plan.counters, &ws, &counters);
     if (st != MQA_OK) return st;
 
     mqa::DecodeArgs a{};
@@ -92,7 +119,7 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.out = out;
     a.part_o = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_o_offset) : nullptr;
     a.part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_lse_offset) : nullptr;
-    a.counters = ws ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + plan.counters_offset) : nullptr;
+    a.counters = counters;
     a.units = plan.rows * Hkv;
     a.fused = plan.combine == 2 ? 1 : 0;
     a.Hq = Hq;
@@ -200,11 +227,12 @@ const char* mqa_last_error(void) { return mqa::last_error(); }
 void mqa_release_workspaces(void) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     for (auto& kv : g_ws) {
-        if (kv.second.ptr) {
+        if (kv.second.ptr || kv.second.counters) {
             int prev = 0;
             (void)hipGetDevice(&prev);
             (void)hipSetDevice(kv.first.first);
-            (void)hipFree(kv.second.ptr);
+            if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+            if (kv.second.counters) (void)hipFree(kv.second.counters);
             (void)hipSetDevice(prev);
         }
     }

@@ -119,11 +119,10 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         if (p.grid_combine > kMaxGrid)
             return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (combine grid limit)");
         const size_t parts = (size_t)p.rows * Hkv * p.max_splits * p.G;
-        const size_t counters = (size_t)p.rows * Hkv * p.head_blocks;
         p.part_o_offset = 0;
         p.part_lse_offset = round_up((long long)(parts * D * sizeof(float)), 256);
-        p.counters_offset = p.part_lse_offset + round_up((long long)(parts * sizeof(float)), 256);
-        p.workspace_bytes = p.counters_offset + round_up((long long)(counters * sizeof(uint32_t)), 256);
+        p.workspace_bytes = p.part_lse_offset + round_up((long long)(parts * sizeof(float)), 256);
+        p.counters = (p.combine == 2) ? (size_t)p.rows * Hkv * p.head_blocks : 0;
     }
     *plan = p;
     return MQA_OK;

@@ -38,10 +38,12 @@ struct Plan {
     long long grid_main = 0;         // workgroups along x of the split kernel
     int block_main = 256;
     long long grid_combine = 0;
-    size_t workspace_bytes = 0;      // partial outputs + partial LSEs + arrival counters
+    size_t workspace_bytes = 0;      // partial outputs + partial LSEs
     size_t part_o_offset = 0;        // byte offsets inside the workspace
     size_t part_lse_offset = 0;
-    size_t counters_offset = 0;      // uint32 per (row, kv head, head block); must start at zero
+    size_t counters = 0;             // arrival counters (uint32, one per (row, kv head, head
+                                     // block)), kept in a buffer of their own that is zero
+                                     // between calls
 };
 
 // Thread-local last-error text.

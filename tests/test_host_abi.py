@@ -97,7 +97,7 @@ def test_plan_invariants(B, Hq, Hkv, D, Lmax):
         fused = p["max_splits"] <= 16
         assert p["combine"] == (2 if fused else 1)
         assert p["grid_combine"] == (0 if fused else B * Hq)
-        assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (D + 1) * 4 + B * Hkv * 4
+        assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (D + 1) * 4
     else:
         assert p["combine"] == 0 and p["workspace_bytes"] == 0
 
