@@ -71,6 +71,7 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default="palm", choices=["tiny", "palm", "gqa70b", "ragged", "long"])
     ap.add_argument("--variant", default=None, choices=[None, "auto", "valu", "mfma"])
     ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--combine", default=None, choices=[None, "auto", "separate", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -149,7 +150,7 @@ def main(argv=None):
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
-    plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk)
+    plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk, args.combine)
 
     calls = []
     for s in sets:
@@ -162,7 +163,7 @@ def main(argv=None):
         if st != 0:
             raise RuntimeError("decode failed: %s" % lib.mqa_last_error().decode())
 
-    plain = binding.make_opts(args.variant, args.chunk)
+    plain = binding.make_opts(args.variant, args.chunk, args.combine)
     for i in range(args.warmup):
         step(i, plain)
     torch.cuda.synchronize()
@@ -172,7 +173,7 @@ def main(argv=None):
     for b, e in evs:  # torch creates the HIP event on first record; the library re-records it
         b.record(stream)
         e.record(stream)
-    opts = [binding.make_opts(args.variant, args.chunk, None, b.cuda_event, e.cuda_event) for b, e in evs]
+    opts = [binding.make_opts(args.variant, args.chunk, args.combine, b.cuda_event, e.cuda_event) for b, e in evs]
     t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_begin.record(stream)

@@ -179,7 +179,9 @@ __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long uni
 // the last workgroup to finish a chunk of this unit (and resets the counter).
 // The caller must have written its partial before calling.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, int nsplit, int* flag_lds) {
-    __threadfence();  // release this workgroup's partial to the device
+    // Release only (write back, no invalidate): an acquire here would drop the
+    // XCD's whole L2 under every other workgroup still streaming K/V.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t old = atomicAdd(counter, 1u);
@@ -189,7 +191,7 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int nsplit, int* 
     }
     __syncthreads();
     const bool last = *flag_lds != 0;
-    if (last) __threadfence();  // acquire the other chunks' partials
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other chunks' partials
     return last;
 }
 

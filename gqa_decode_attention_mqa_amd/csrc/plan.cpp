@@ -18,13 +18,17 @@ mqa_status fail(mqa_status s, const std::string& msg) {
     return s;
 }
 
-// Workgroups the planner aims for when it picks the chunk size: enough to
-// give every CU at least two resident workgroups.
-constexpr long long kTargetWorkgroups = 2LL * kComputeUnits;
+// Workgroups the planner aims for when it picks the chunk size: one per CU.
+// Measured on MI355X, more, shorter chunks lose to the extra partial traffic
+// (PaLM-shaped MQA: chunk 512 -> 39.6 us, 256 -> 48.8 us, 1024 -> 55.9 us;
+// long-context MQA: 2048 -> 110 us, 1024 -> 122 us, 4096 -> 186 us).
+constexpr long long kTargetWorkgroups = kComputeUnits;
 // Chunk bounds: below 256 positions the partial outputs cost more traffic than
-// the split saves; above 2048 a ragged batch balances poorly.
+// the split saves; longer chunks balance a ragged batch poorly (the vector
+// kernel, used for ragged small-group batches, gets the tighter bound).
 constexpr long long kMinChunk = 256;
-constexpr long long kMaxChunk = 2048;
+constexpr long long kMaxChunkMfma = 2048;
+constexpr long long kMaxChunkValu = 1024;
 // Largest grid the launcher accepts (work-items must stay below 2^32).
 constexpr long long kMaxGrid = (1LL << 24) - 1;
 }  // namespace
@@ -73,7 +77,7 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     p.G = Hq / Hkv;
     p.variant = o.variant;
     if (p.variant == MQA_VARIANT_AUTO)
-        p.variant = (p.G >= kMfmaHeadsPerTile) ? MQA_VARIANT_MFMA : MQA_VARIANT_VALU;
+        p.variant = (p.G >= kMfmaMinGroup) ? MQA_VARIANT_MFMA : MQA_VARIANT_VALU;
 
     if (p.variant == MQA_VARIANT_MFMA) {
         const int heads = p.G < kMfmaMaxHeads ? p.G : kMfmaMaxHeads;
@@ -94,8 +98,9 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         p.chunk = kChunkQuantum;
     } else {
         long long c = round_up(ceil_div((long long)Lmax * units, kTargetWorkgroups), kChunkQuantum);
+        const long long cmax = p.variant == MQA_VARIANT_MFMA ? kMaxChunkMfma : kMaxChunkValu;
         if (c < kMinChunk) c = kMinChunk;
-        if (c > kMaxChunk) c = kMaxChunk;
+        if (c > cmax) c = cmax;
         const long long whole = round_up(Lmax, kChunkQuantum);
         if (c > whole) c = whole;
         p.chunk = (int)c;
@@ -111,10 +116,10 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     if (p.max_splits > 1 && p.rows > 0) {
         if (o.combine == 2 && p.max_splits > kFusedMaxSplits)
             return fail(MQA_ERR_ARG, "the fused combine handles at most 16 chunks per sequence");
-        if (o.combine == 0)
-            p.combine = p.max_splits <= kFusedMaxSplits ? 2 : 1;
-        else
-            p.combine = o.combine;
+        // Default: the separate combine kernel.  The fused form needs an
+        // agent-scope release (an L2 write-back) in every workgroup, which
+        // measured 2-3x slower on MI355X.
+        p.combine = (o.combine == 0) ? 1 : o.combine;
         p.grid_combine = (p.combine == 1) ? p.rows * Hq : 0;
         if (p.grid_combine > kMaxGrid)
             return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (combine grid limit)");

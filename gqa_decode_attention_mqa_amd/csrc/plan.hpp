@@ -19,6 +19,11 @@ constexpr int kComputeUnits = 256;
 constexpr int kChunkQuantum = 128;
 // Query heads per MFMA tile along the N dimension.
 constexpr int kMfmaHeadsPerTile = 16;
+// Smallest group (query heads per kv head) sent to the matrix-core kernel by
+// default.  Measured on MI355X: at G = 8 the 16-row tile (half filled) beats
+// the vector kernel (95.5 us vs 128 us for B=32, Hkv=8, D=128, len 4096); at
+// G = 4 the vector kernel wins (790 us vs 944 us on the ragged batch).
+constexpr int kMfmaMinGroup = 5;
 // Most query heads one MFMA workgroup serves (four 16-head tiles).
 constexpr int kMfmaMaxHeads = 64;
 // Most query heads one VALU workgroup serves.

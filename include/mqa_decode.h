@@ -36,7 +36,9 @@
  * enqueued on `stream`.  Split-K scratch (partial outputs and log-sum-exps) is
  * owned by the library, cached per (device, stream), grown on demand with
  * hipMalloc (which synchronises the device) and freed by
- * mqa_release_workspaces().
+ * mqa_release_workspaces(); so are the fused combine's arrival counters,
+ * zeroed once when allocated and left at zero by every call.  Warm the
+ * library up with a call of the largest shape before capturing a graph.
  *
  * Errors: every argument check happens on the host before any HIP call, so
  * the checks can run on a machine with no GPU.  No call aborts or throws; a
@@ -69,7 +71,7 @@ typedef enum mqa_status {
 
 /* Kernel family for the q.K^T and P.V products. */
 typedef enum mqa_variant {
-    MQA_VARIANT_AUTO = 0, /* planner's choice by group size G = Hq / Hkv                    */
+    MQA_VARIANT_AUTO = 0, /* planner's choice by group size G = Hq / Hkv: VALU for G <= 4  */
     MQA_VARIANT_VALU = 1, /* vector-ALU dot products (small groups)                        */
     MQA_VARIANT_MFMA = 2  /* bf16 matrix-core tiles, 16 query heads per tile (large groups) */
 } mqa_variant;
@@ -79,8 +81,8 @@ typedef struct mqa_decode_opts {
     int variant;          /* mqa_variant                                                */
     int chunk;            /* positions per split-K chunk; 0 = planner's choice.  Must be
                              a positive multiple of 128 when set.                        */
-    int combine;          /* 0 = planner's choice (fused when a sequence has at most 16
-                             chunks, else separate), 1 = separate combine kernel,
+    int combine;          /* 0 = planner's choice (the separate kernel),
+                             1 = separate combine kernel,
                              2 = combine fused into the split kernel: the last chunk of
                              each (sequence, kv head) to finish merges the partials
                              (at most 16 chunks per sequence, else MQA_ERR_ARG)          */

@@ -78,7 +78,7 @@ def test_small_shapes(variant, D, G, Hkv, B):
     # combine and by the separate combine kernel, all on the same inputs
     run_case(w, variant=variant)
     run_case(w, variant=variant, chunk=128)
-    run_case(w, variant=variant, chunk=128, combine="separate")
+    run_case(w, variant=variant, chunk=128, combine="fused")
 
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
@@ -88,7 +88,7 @@ def test_edge_lengths(variant):
     print("case edges", variant, flush=True)
     run_case(w, variant=variant, seq_lens=lens)
     run_case(w, variant=variant, chunk=128, seq_lens=lens)
-    run_case(w, variant=variant, chunk=128, seq_lens=lens, combine="separate")
+    run_case(w, variant=variant, chunk=128, seq_lens=lens, combine="fused")
 
 
 @pytest.mark.parametrize("combine", ["fused", "separate"])

@@ -66,7 +66,7 @@ def test_fused_combine_is_refused_beyond_its_split_limit():
     # 100000 positions in chunks of 128 -> 782 chunks > 16
     assert call(Lmax=100000, opts=binding.make_opts(chunk=128, combine=2)) == ERR_ARG
     assert binding.plan(2, 8, 2, 128, 100000, chunk=128)["combine"] == 1
-    assert binding.plan(2, 8, 2, 128, 2048, chunk=128)["combine"] == 2
+    assert binding.plan(2, 8, 2, 128, 2048, chunk=128, combine="fused")["combine"] == 2
 
 
 def test_empty_batch_is_a_no_op_even_with_null_pointers():
@@ -89,14 +89,12 @@ def test_plan_invariants(B, Hq, Hkv, D, Lmax):
     assert p["chunk"] > 0 and p["chunk"] % 128 == 0
     assert p["max_splits"] >= 1 and p["chunk"] * p["max_splits"] >= Lmax
     assert (p["max_splits"] - 1) * p["chunk"] < max(Lmax, 1)
-    assert p["variant"] == ("mfma" if G >= 16 else "valu")
+    assert p["variant"] == ("mfma" if G >= 5 else "valu")
     per_block = min(G, 64) if p["variant"] == "mfma" else min(G, 8)
     assert p["head_blocks"] * per_block >= G
     assert p["grid_main"] == B * Hkv * p["max_splits"] * p["head_blocks"]
     if p["max_splits"] > 1:
-        fused = p["max_splits"] <= 16
-        assert p["combine"] == (2 if fused else 1)
-        assert p["grid_combine"] == (0 if fused else B * Hq)
+        assert p["combine"] == 1 and p["grid_combine"] == B * Hq
         assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (D + 1) * 4
     else:
         assert p["combine"] == 0 and p["workspace_bytes"] == 0
@@ -107,6 +105,17 @@ def test_forced_variant_and_chunk_are_honoured():
     assert p["variant"] == "mfma" and p["chunk"] == 256 and p["max_splits"] == 4
     p = binding.plan(4, 48, 1, 256, 1000, variant="valu")
     assert p["variant"] == "valu" and p["head_blocks"] == 6
+
+
+def test_default_plans_of_the_five_workloads():
+    """The defaults are the measured best choices on MI355X."""
+    assert binding.plan(64, 48, 1, 256, 2048)["chunk"] == 512
+    assert binding.plan(4, 48, 1, 256, 131072)["chunk"] == 2048
+    g = binding.plan(32, 64, 8, 128, 4096)
+    assert g["variant"] == "mfma" and g["chunk"] == 2048
+    r = binding.plan(256, 32, 8, 128, 8192)
+    assert r["variant"] == "valu" and r["chunk"] == 1024
+    assert binding.plan(1, 8, 1, 64, 128)["max_splits"] == 1
 
 
 def test_chunk_schedule_covers_every_valid_position_once():
