@@ -132,18 +132,16 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.causal = causal ? 1 : 0;
     a.qk_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
+    hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->ev_main_begin) : nullptr;
+    hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->ev_main_end) : nullptr;
     hipError_t e;
-    if (opts && opts->ev_main_begin) {
-        e = hipEventRecord(static_cast<hipEvent_t>(opts->ev_main_begin), stream);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
-    e = (plan.variant == MQA_VARIANT_MFMA) ? mqa::launch_decode_mfma(plan, a, stream)
-                                           : mqa::launch_decode_valu(plan, a, stream);
+    if (plan.variant == MQA_VARIANT_VALU)
+        e = mqa::launch_decode_valu(plan, a, stream, ev0, ev1);
+    else if (plan.heads_per_block > mqa::kMfmaHeadsPerTile)
+        e = mqa::launch_decode_mfma_heads(plan, a, stream, ev0, ev1);  // one wave per 16 heads
+    else
+        e = mqa::launch_decode_mfma(plan, a, stream, ev0, ev1);        // waves split the positions
     if (e != hipSuccess) return hip_fail(e, "split-K kernel launch");
-    if (opts && opts->ev_main_end) {
-        e = hipEventRecord(static_cast<hipEvent_t>(opts->ev_main_end), stream);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
     if (plan.combine == 1) {
         mqa::CombineArgs c{};
         c.part_o = a.part_o;

@@ -27,6 +27,9 @@
 // The chunk ends by normalising; a sequence that fits in one chunk writes its
 // output directly, otherwise the chunk writes O/l and its base-2 log-sum-exp
 // for the combine kernel.
+#include <atomic>
+#include <type_traits>
+
 #include "kernel_common.hpp"
 #include "launch.hpp"
 
@@ -34,39 +37,41 @@ namespace mqa {
 
 template <int D, int NG>
 struct MfmaCfg {
-    static constexpr int NW = 4;                         // waves per workgroup
-    static constexpr int WD = D / 64;                    // waves along d in P.V
-    static constexpr int WT = NW / WD;                   // waves along positions in P.V
-    static constexpr int TILE = (32 * WT > 64) ? 32 * WT : 64;
-    static constexpr int QKM = TILE / (16 * NW);         // 16-position M tiles per wave in q.K
-    static constexpr int PVK = TILE / WT / 32;           // 32-position k-steps per wave in P.V
-    static constexpr int KS = D / 32;                    // k-steps over d in q.K
-    static constexpr int GP = 16 * NG;                   // heads per workgroup (padded)
-    static constexpr int QLD = D + 8;                    // LDS row pitch of q (bf16)
-    static constexpr int PLD = TILE + 8;                 // LDS row pitch of P^T (bf16)
-    static constexpr int RED_BYTES = NW * GP * 4;
+    static constexpr int NW = 4;             // waves per workgroup, each independent in the main loop
+    // 16-row S^T tiles per step: two (P.V on 16x16x32, 8 k-slots) while the
+    // registers allow, one (P.V on 16x16x16, 4 k-slots) for D = 256.
+    static constexpr int MQ = (D >= 256) ? 1 : 2;
+    static constexpr int STEP = 16 * MQ;     // positions a wave takes per step
+    static constexpr int KSL = 4 * MQ;       // k-slots of the P.V tile per lane group
+    static constexpr int KS = D / 32;        // k-steps over d in q.K
+    static constexpr int DPL = D / 16;       // V columns per lane = M tiles of O^T
+    static constexpr int GP = 16 * NG;       // heads per workgroup (padded)
+    static constexpr int QLD = D + 8;        // LDS row pitch of q (bf16)
+    static constexpr int ACC = DPL * NG;     // O^T accumulator tiles per lane (4 floats each)
     static constexpr int Q_BYTES = GP * QLD * 2;
-    static constexpr int P_BYTES = GP * PLD * 2;
-    static constexpr int MERGE_BYTES = (WT - 1) * WD * 4 * NG * 4 * 64 * 4;
-    static constexpr int BODY_BYTES = (Q_BYTES + P_BYTES) > MERGE_BYTES ? (Q_BYTES + P_BYTES) : MERGE_BYTES;
-    static constexpr int LDS_BYTES = RED_BYTES + BODY_BYTES;
-    static_assert(TILE % (16 * NW) == 0, "q.K tiles must cover the tile");
-    static_assert(PVK >= 1, "each P.V wave needs a whole 32-position k-step");
-    static_assert(LDS_BYTES <= 65536, "static LDS budget");
+    static constexpr int OLD = D + 4;                        // LDS row pitch of an O exchange region (fp32)
+    static constexpr int REGION_BYTES = GP * OLD * 4;        // one wave's O, row-major [head][d]
+    static constexpr int ML_BYTES = 2 * NW * GP * 4;        // running max and row sum per wave
+    static constexpr int BODY_BYTES = (2 * REGION_BYTES > Q_BYTES) ? 2 * REGION_BYTES : Q_BYTES;
+    static constexpr int LDS_BYTES = ML_BYTES + BODY_BYTES;
+    static_assert(D % 64 == 0, "head size");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
     static_assert(BODY_BYTES >= (kFusedMaxSplits + 2) * GP * 4, "fused-combine weights fit in the body");
 };
 
 template <int D, int NG>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     using C = MfmaCfg<D, NG>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
-    float* red = reinterpret_cast<float*>(smem);
-    uint16_t* qs = reinterpret_cast<uint16_t*>(smem + C::RED_BYTES);
-    uint16_t* ps = qs + C::GP * C::QLD;
-    float* merge = reinterpret_cast<float*>(smem + C::RED_BYTES);
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float* m_lds = reinterpret_cast<float*>(smem);           // [NW][GP]
+    float* l_lds = m_lds + C::NW * C::GP;                    // [NW][GP]
+    unsigned char* body = smem + C::ML_BYTES;
+    uint16_t* qs = reinterpret_cast<uint16_t*>(body);        // q, during the main loop
+    float* region0 = reinterpret_cast<float*>(body);         // O^T exchange, after it
+    float* region1 = reinterpret_cast<float*>(body + C::REGION_BYTES);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (wave-uniform)
     const int li = lane & 15, kg = lane >> 4;
 
     long long unit;
@@ -79,64 +84,111 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
+    // Workgroup-uniform; stated so the compiler keeps them (and the buffer
+    // descriptors built from them) in scalar registers.
+    b = __builtin_amdgcn_readfirstlane(b);
+    len = __builtin_amdgcn_readfirstlane(len);
     const int p0 = s * a.chunk;
     if (s > 0 && p0 >= len) return;  // whole workgroup: this chunk is past the end
     const int p1 = min(p0 + a.chunk, len);
     const int nsplit = len > 0 ? (len + a.chunk - 1) / a.chunk : 1;
 
-    // Stage this block's query heads (bf16, zero rows past the group) in LDS.
-    const uint16_t* qrow = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D;
-    for (int c = tid; c < C::GP * (D / 8); c += 256) {
-        const int g = c / (D / 8), dc = c % (D / 8);
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (g < gcnt) val = load_u32x4(qrow + (size_t)g * D + dc * 8);
-        *reinterpret_cast<u32x4_t*>(qs + g * C::QLD + dc * 8) = val;
-    }
-
     const size_t pos_stride = (size_t)a.Hkv * D;  // elements between consecutive positions
-    const uint16_t* kbase = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
-    const uint16_t* vbase = a.v + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
-    const int ds = w % C::WD, ts = w / C::WD;
-    const int vcol = 64 * ds + 4 * li;        // this lane's 4 V columns in P.V
+    const int rowbytes = (int)(pos_stride * 2);
+    const uint16_t* kseq = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;  // position 0 of this head
+    const uint16_t* vseq = a.v + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
     const float qk = a.qk_log2;
-    const int last = p1 - 1;                  // loads past the end re-read this row
+
+    // Lane offsets inside a step (loop invariant).  The S^T accumulator of M
+    // tile mq gives lane group kg the positions 16*mq + 4*kg + r, r < 4; these
+    // positions are the k-slots (element e = 4*mq + r) of the P^T operand of
+    // P.V, so V rows are loaded in the same order.
+    constexpr int MQ = C::MQ, KSL = C::KSL;
+    using pv_t = typename std::conditional<MQ == 2, u32x4_t, u32x2_t>::type;
+    const int koff0 = li * rowbytes + kg * 16;                 // + 16*mq*rowbytes, + 64*ks
+    int voff[KSL];
+#pragma unroll
+    for (int e = 0; e < KSL; ++e) voff[e] = (16 * (e / 4) + 4 * kg + (e % 4)) * rowbytes + li * (C::DPL * 2);
+
+    // K rows of one step: [mq][ks] -> 16 bytes of row 16*mq + li, d = 32*ks + 8*kg ...
+    u32x4_t kr[MQ][C::KS];
+    // V rows of one step: KSL rows (k-slots) x DPL columns d = DPL*li + c.
+    constexpr int VW = C::DPL / 2;  // dwords of V per row per lane
+    uint32_t vr[KSL][VW];
+
+    auto load_k = [&](int st) {
+        const int rows = max(0, min(C::STEP, p1 - st));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(kseq + (size_t)st * pos_stride, rows * rowbytes);
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) kr[mq][ks] = buffer_load_u32x4(rs, koff0 + 16 * mq * rowbytes + 64 * ks);
+    };
+    auto load_v = [&](int st) {
+        const int rows = max(0, min(C::STEP, p1 - st));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(vseq + (size_t)st * pos_stride, rows * rowbytes);
+#pragma unroll
+        for (int e = 0; e < KSL; ++e) {
+            if constexpr (VW >= 4) {
+#pragma unroll
+                for (int j = 0; j < VW / 4; ++j) {
+                    const u32x4_t t4 = buffer_load_u32x4(rs, voff[e] + 16 * j);
+                    vr[e][4 * j] = t4.x;
+                    vr[e][4 * j + 1] = t4.y;
+                    vr[e][4 * j + 2] = t4.z;
+                    vr[e][4 * j + 3] = t4.w;
+                }
+            } else {
+                const u32x2_t t2 = buffer_load_u32x2(rs, voff[e]);
+                vr[e][0] = t2.x;
+                vr[e][1] = t2.y;
+            }
+        }
+    };
+
+    // q is fetched first and the first K/V step right behind it: the q staging
+    // below then waits only for q (loads complete in order), while K/V stream in.
+    constexpr int QV = (C::GP * (D / 8) + 255) / 256;  // 16-byte pieces of q per thread
+    const uint16_t* qrow = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D;
+    u32x4_t qv[QV];
+#pragma unroll
+    for (int i = 0; i < QV; ++i) {
+        const int c = tid + 256 * i;
+        const int g = c / (D / 8), dc = c % (D / 8);
+        qv[i] = u32x4_t{0u, 0u, 0u, 0u};
+        if (c < C::GP * (D / 8) && g < gcnt) qv[i] = load_u32x4(qrow + (size_t)g * D + dc * 8);
+    }
+    int st = p0 + C::STEP * w;
+    load_k(st);
+    load_v(st);
+#pragma unroll
+    for (int i = 0; i < QV; ++i) {
+        const int c = tid + 256 * i;
+        if (c < C::GP * (D / 8))
+            *reinterpret_cast<u32x4_t*>(qs + (c / (D / 8)) * C::QLD + (c % (D / 8)) * 8) = qv[i];
+    }
+    __syncthreads();
 
     float m_run[NG], l_run[NG];
-    f32x4_t oacc[4][NG];
+    f32x4_t oacc[C::DPL][NG];
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
         m_run[n] = -INFINITY;
         l_run[n] = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) oacc[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < C::DPL; ++j) oacc[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Loads are unconditional: a position at or past p1 is clamped to the last
-    // valid row.  Its logit is masked to -inf (so its weight is exactly 0 and the
-    // clamped V row adds nothing); padding is never read.
-    auto load_tile = [&](int tile0, u32x4_t (&kr)[C::QKM][C::KS], u32x2_t (&vr)[C::PVK][8]) {
+    // ---- main loop: this wave's steps st, st + 4*STEP, ...; no cross-wave sync
+    while (st < p1) {
+        // Keeps the q^T reads below inside the loop: hoisted, they would pin
+        // KS * NG * 4 registers for the whole loop (96 for 48 heads of 256).
+        asm volatile("" ::: "memory");
+        const int nxt = st + C::NW * C::STEP;
+        // S^T = K q^T
+        f32x4_t sacc[MQ][NG];
 #pragma unroll
-        for (int mq = 0; mq < C::QKM; ++mq) {
-            const int t = min(tile0 + 16 * (w * C::QKM + mq) + li, last);
-            const uint16_t* src = kbase + (size_t)t * pos_stride + kg * 8;
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) kr[mq][ks] = load_nt_u32x4(src + ks * 32);
-        }
-#pragma unroll
-        for (int kk = 0; kk < C::PVK; ++kk) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = min(tile0 + ts * (C::TILE / C::WT) + 32 * kk + 8 * kg + e, last);
-                vr[kk][e] = load_nt_u32x2(vbase + (size_t)t * pos_stride + vcol);
-            }
-        }
-    };
-
-    auto compute_tile = [&](int tile0, const u32x4_t (&kr)[C::QKM][C::KS], const u32x2_t (&vr)[C::PVK][8]) {
-        // ---- S^T = K q^T
-        f32x4_t sacc[C::QKM][NG];
-#pragma unroll
-        for (int mq = 0; mq < C::QKM; ++mq)
+        for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
             for (int n = 0; n < NG; ++n) sacc[mq][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -145,201 +197,245 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             for (int n = 0; n < NG; ++n) {
                 const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(qs + (16 * n + li) * C::QLD + ks * 32 + kg * 8);
 #pragma unroll
-                for (int mq = 0; mq < C::QKM; ++mq) sacc[mq][n] = mfma_16x16x32_bf16(kr[mq][ks], bq, sacc[mq][n]);
+                for (int mq = 0; mq < MQ; ++mq) sacc[mq][n] = mfma_16x16x32_bf16(kr[mq][ks], bq, sacc[mq][n]);
             }
         }
-        // ---- scale, mask the ragged tail, per-wave maximum per head
-        float wmax[NG];
-#pragma unroll
-        for (int n = 0; n < NG; ++n) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mq = 0; mq < C::QKM; ++mq)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = tile0 + 16 * (w * C::QKM + mq) + 4 * kg + r;
-                    const float val = (t < p1) ? sacc[mq][n][r] * qk : -INFINITY;
-                    sacc[mq][n][r] = val;
-                    mx = fmaxf(mx, val);
-                }
-            mx = fmaxf(mx, shfl_xor_f32(mx, 16));
-            mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-            wmax[n] = mx;
-        }
-        if (kg == 0) {
-#pragma unroll
-            for (int n = 0; n < NG; ++n) red[w * C::GP + 16 * n + li] = wmax[n];
-        }
-        __syncthreads();
-        float alpha[NG];
-#pragma unroll
-        for (int n = 0; n < NG; ++n) {
-            float tmax = red[16 * n + li];
-#pragma unroll
-            for (int ww = 1; ww < C::NW; ++ww) tmax = fmaxf(tmax, red[ww * C::GP + 16 * n + li]);
-            const float m_new = fmaxf(m_run[n], tmax);
-            alpha[n] = __builtin_amdgcn_exp2f(m_run[n] - m_new);
-            m_run[n] = m_new;
-        }
-        // ---- P = exp2(S - m), bf16, transposed into LDS; row sums of the rounded values
-#pragma unroll
-        for (int n = 0; n < NG; ++n) {
-            float lsum = 0.f;
-#pragma unroll
-            for (int mq = 0; mq < C::QKM; ++mq) {
-                uint32_t pb[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pb[r] = f32_to_bf16_bits(__builtin_amdgcn_exp2f(sacc[mq][n][r] - m_run[n]));
-                    lsum += bf16_bits_to_f32(pb[r]);
-                }
-                u32x2_t packed = {pack_bf16x2(pb[0], pb[1]), pack_bf16x2(pb[2], pb[3])};
-                *reinterpret_cast<u32x2_t*>(ps + (16 * n + li) * C::PLD + 16 * (w * C::QKM + mq) + 4 * kg) = packed;
-            }
-            l_run[n] = l_run[n] * alpha[n] + lsum;
-        }
-        __syncthreads();
-        // ---- O^T = alpha * O^T + V^T P^T
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int n = 0; n < NG; ++n) oacc[j][n] = oacc[j][n] * alpha[n];
-#pragma unroll
-        for (int kk = 0; kk < C::PVK; ++kk) {
-            u32x4_t va[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x2_t r0 = vr[kk][2 * c], r1 = vr[kk][2 * c + 1];
-                va[0][c] = perm_b32(r1.x, r0.x, kPermLoHalves);
-                va[1][c] = perm_b32(r1.x, r0.x, kPermHiHalves);
-                va[2][c] = perm_b32(r1.y, r0.y, kPermLoHalves);
-                va[3][c] = perm_b32(r1.y, r0.y, kPermHiHalves);
-            }
-#pragma unroll
-            for (int n = 0; n < NG; ++n) {
-                const u32x4_t pbv = *reinterpret_cast<const u32x4_t*>(
-                    ps + (16 * n + li) * C::PLD + ts * (C::TILE / C::WT) + 32 * kk + 8 * kg);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) oacc[j][n] = mfma_16x16x32_bf16(va[j], pbv, oacc[j][n]);
-            }
-        }
-    };
+        load_k(nxt);  // the next step's K streams in under softmax and P.V
 
-    // Two register stages: while a tile is computed, the next one is in flight.
-    if (p0 < p1) {
-        u32x4_t kA[C::QKM][C::KS], kB[C::QKM][C::KS];
-        u32x2_t vA[C::PVK][8], vB[C::PVK][8];
-        load_tile(p0, kA, vA);
-        __syncthreads();  // q staged
-        int tile0 = p0;
-        while (true) {
-            load_tile(tile0 + C::TILE, kB, vB);
-            compute_tile(tile0, kA, vA);
-            tile0 += C::TILE;
-            if (tile0 >= p1) break;
-            load_tile(tile0 + C::TILE, kA, vA);
-            compute_tile(tile0, kB, vB);
-            tile0 += C::TILE;
-            if (tile0 >= p1) break;
-        }
-    }
-
-    // ---- epilogue: row sums across lane groups and waves, merge P.V position slices
+        // scale to base-2 units; mask past the end (last step only)
 #pragma unroll
-    for (int n = 0; n < NG; ++n) {
-        float l = l_run[n];
-        l += shfl_xor_f32(l, 16);
-        l += shfl_xor_f32(l, 32);
-        l_run[n] = l;
-    }
-    __syncthreads();  // every wave is done with q, P and the maxima
-    if (kg == 0) {
-#pragma unroll
-        for (int n = 0; n < NG; ++n) red[w * C::GP + 16 * n + li] = l_run[n];
-    }
-    if (C::WT > 1 && ts > 0) {
-        float* dst = merge + (size_t)((ts - 1) * C::WD + ds) * (4 * NG * 4 * 64);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
             for (int n = 0; n < NG; ++n)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dst[((j * NG + n) * 4 + r) * 64 + lane] = oacc[j][n][r];
-    }
-    __syncthreads();
-
-    const bool direct = nsplit == 1;
-    if (ts == 0) {
-        float inv_l[NG], lse2[NG];
+                for (int r = 0; r < 4; ++r) sacc[mq][n][r] *= qk;
+        if (st + C::STEP > p1) {
+#pragma unroll
+            for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool ok = st + 16 * mq + 4 * kg + r < p1;
+#pragma unroll
+                    for (int n = 0; n < NG; ++n) sacc[mq][n][r] = ok ? sacc[mq][n][r] : -INFINITY;
+                }
+        }
+        // online softmax with lazy rescaling; P^T operand built in registers
+        pv_t pb[NG];
+        float alpha[NG];
+        bool any_rescale = false;
 #pragma unroll
         for (int n = 0; n < NG; ++n) {
-            float L = 0.f;
+            float mx = fmaxf(fmaxf(sacc[0][n][0], sacc[0][n][1]), fmaxf(sacc[0][n][2], sacc[0][n][3]));
 #pragma unroll
-            for (int ww = 0; ww < C::NW; ++ww) L += red[ww * C::GP + 16 * n + li];
-            inv_l[n] = L > 0.f ? 1.f / L : 0.f;
-            lse2[n] = m_run[n] + __log2f(L);
+            for (int mq = 1; mq < MQ; ++mq)
+                mx = fmaxf(mx, fmaxf(fmaxf(sacc[mq][n][0], sacc[mq][n][1]), fmaxf(sacc[mq][n][2], sacc[mq][n][3])));
+            mx = max_xor32(max_xor16(mx));
+            const bool moved = mx > m_run[n] + kRescaleSlack;
+            alpha[n] = moved ? __builtin_amdgcn_exp2f(m_run[n] - mx) : 1.f;
+            m_run[n] = moved ? mx : m_run[n];
+            any_rescale |= moved;
+            float lsum = 0.f;
+#pragma unroll
+            for (int mq = 0; mq < MQ; ++mq) {
+                const uint32_t lo = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][n][0] - m_run[n]),
+                                                   __builtin_amdgcn_exp2f(sacc[mq][n][1] - m_run[n]));
+                const uint32_t hi = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][n][2] - m_run[n]),
+                                                   __builtin_amdgcn_exp2f(sacc[mq][n][3] - m_run[n]));
+                pb[n][2 * mq] = lo;
+                pb[n][2 * mq + 1] = hi;
+                lsum += (bf16_lo_f32(lo) + bf16_hi_f32(lo)) + (bf16_lo_f32(hi) + bf16_hi_f32(hi));
+            }
+            l_run[n] = l_run[n] * alpha[n] + lsum;
         }
-        if (C::WT > 1) {
+        if (__any(any_rescale)) {
 #pragma unroll
-            for (int tt = 1; tt < C::WT; ++tt) {
-                const float* src = merge + (size_t)((tt - 1) * C::WD + ds) * (4 * NG * 4 * 64);
+            for (int j = 0; j < C::DPL; ++j)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int n = 0; n < NG; ++n) oacc[j][n] = oacc[j][n] * alpha[n];
+        }
+        // O^T += V^T P^T: column c of this lane's V rows is M tile c (row li <-> d = DPL*li + c)
 #pragma unroll
-                    for (int n = 0; n < NG; ++n)
+        for (int wd = 0; wd < VW; ++wd) {
+            pv_t va_even, va_odd;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) oacc[j][n][r] += src[((j * NG + n) * 4 + r) * 64 + lane];
+            for (int m = 0; m < KSL / 2; ++m) {
+                va_even[m] = perm_b32(vr[2 * m + 1][wd], vr[2 * m][wd], kPermLoHalves);
+                va_odd[m] = perm_b32(vr[2 * m + 1][wd], vr[2 * m][wd], kPermHiHalves);
+            }
+#pragma unroll
+            for (int n = 0; n < NG; ++n) {
+                oacc[2 * wd][n] = mfma_pv(va_even, pb[n], oacc[2 * wd][n]);
+                oacc[2 * wd + 1][n] = mfma_pv(va_odd, pb[n], oacc[2 * wd + 1][n]);
             }
         }
+        load_v(nxt);
+        st = nxt;
+    }
+
+    // ---- merge the four waves' (m, l, O) by log-sum-exp, through LDS
+#pragma unroll
+    for (int n = 0; n < NG; ++n) l_run[n] = sum_xor32(sum_xor16(l_run[n]));  // whole wave, head li
+    if (kg == 0) {
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+            m_lds[w * C::GP + 16 * n + li] = m_run[n];
+            l_lds[w * C::GP + 16 * n + li] = l_run[n];
+        }
+    }
+    // Row-major exchange: accumulator (c, n, r) of lane (li, kg) is head
+    // 16*n + li, columns DPL*(4*kg + r) + c, so each (n, r) is DPL consecutive
+    // floats written or read as 16-byte pieces.
+    auto region_ptr = [&](float* reg, int n, int r, int q4) {
+        return reinterpret_cast<f32x4_t*>(reg + (16 * n + li) * C::OLD + C::DPL * (4 * kg + r) + 4 * q4);
+    };
+    auto store_region = [&](float* reg, const float* scale) {
+#pragma unroll
+        for (int n = 0; n < NG; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q4 = 0; q4 < C::DPL / 4; ++q4)
+                    *region_ptr(reg, n, r, q4) = f32x4_t{oacc[4 * q4][n][r], oacc[4 * q4 + 1][n][r],
+                                                         oacc[4 * q4 + 2][n][r], oacc[4 * q4 + 3][n][r]} * scale[n];
+    };
+    __syncthreads();  // all waves left the main loop: q is dead, regions may overwrite it
+    if (w >= 2) {
+        float ones[NG];
+#pragma unroll
+        for (int n = 0; n < NG; ++n) ones[n] = 1.f;
+        store_region(w == 2 ? region0 : region1, ones);
+    }
+    __syncthreads();
+    if (w < 2) {
+        // wave w absorbs wave w + 2
+        const float* reg = w == 0 ? region0 : region1;
+        float sa[NG], sb[NG];
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+            const float mo = m_lds[(w + 2) * C::GP + 16 * n + li];
+            const float lo = l_lds[(w + 2) * C::GP + 16 * n + li];
+            const float M = fmaxf(m_run[n], mo);
+            sa[n] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[n] - M);
+            sb[n] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - M);
+            l_run[n] = sa[n] * l_run[n] + sb[n] * lo;
+            m_run[n] = M;
+        }
+#pragma unroll
+        for (int n = 0; n < NG; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int q4 = 0; q4 < C::DPL / 4; ++q4) {
+                    const f32x4_t o = *region_ptr(const_cast<float*>(reg), n, r, q4);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        oacc[4 * q4 + c][n][r] = sa[n] * oacc[4 * q4 + c][n][r] + sb[n] * o[c];
+                }
+        if (kg == 0) {
+#pragma unroll
+            for (int n = 0; n < NG; ++n) {
+                m_lds[w * C::GP + 16 * n + li] = m_run[n];
+                l_lds[w * C::GP + 16 * n + li] = l_run[n];
+            }
+        }
+    }
+    __syncthreads();
+    // Waves 0 and 1 hold the pairs (0,2) and (1,3): each writes its share of
+    // the normalised result, 2^(m_w - M) / L * O_w, to its own region.
+    float lse2[NG], scale[NG];
+    if (w < 2) {
 #pragma unroll
         for (int n = 0; n < NG; ++n) {
             const int g = 16 * n + li;
-            if (g >= gcnt) continue;
-            const int gh = g0 + g;  // head index inside the group
-            float* dst;
-            if (direct)
-                dst = a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D;
-            else
-                dst = a.part_o + (((size_t)unit * a.max_splits + s) * a.G + gh) * D;
+            const float m0 = m_lds[g], m1 = m_lds[C::GP + g];
+            const float M = fmaxf(m0, m1);
+            const float s0 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+            const float s1 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+            const float L = s0 * l_lds[g] + s1 * l_lds[C::GP + g];
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            scale[n] = (w == 0 ? s0 : s1) * inv;
+            lse2[n] = M + __log2f(L);
+        }
+    }
+    __syncthreads();  // m_lds / l_lds have been read; regions 0 and 1 are free
+    if (w < 2) {
+        store_region(w == 0 ? region0 : region1, scale);
+        if (w == 0 && kg == 0) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d = 64 * ds + 16 * kg + 4 * r;
-                f32x4_t o4 = {oacc[0][n][r] * inv_l[n], oacc[1][n][r] * inv_l[n],
-                              oacc[2][n][r] * inv_l[n], oacc[3][n][r] * inv_l[n]};
-                *reinterpret_cast<f32x4_t*>(dst + d) = o4;
-            }
-            if (!direct && ds == 0 && kg == 0)
-                a.part_lse[((size_t)unit * a.max_splits + s) * a.G + gh] = lse2[n];
+            for (int n = 0; n < NG; ++n) m_lds[16 * n + li] = lse2[n];
+        }
+    }
+    __syncthreads();
+
+    // ---- store: every thread, contiguous rows (region0 + region1)
+    const bool direct = nsplit == 1;
+    for (int idx = tid; idx < gcnt * (D / 4); idx += 256) {
+        const int g = idx / (D / 4), d = 4 * (idx % (D / 4));
+        const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(region0 + g * C::OLD + d) +
+                           *reinterpret_cast<const f32x4_t*>(region1 + g * C::OLD + d);
+        const int gh = g0 + g;
+        if (direct) {
+            *reinterpret_cast<f32x4_t*>(a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D + d) = o4;
+        } else {
+            const size_t part = ((size_t)unit * a.max_splits + s) * a.G + gh;
+            *reinterpret_cast<f32x4_t*>(a.part_o + part * D + d) = o4;
+            if (d == 0) a.part_lse[part] = m_lds[g];
         }
     }
     if (direct || !a.fused) return;
     // ---- fused combine: the last chunk of this (row, kv head, head block) merges all partials
-    int* flag = reinterpret_cast<int*>(red);
+    int* flag = reinterpret_cast<int*>(m_lds);
+    __syncthreads();  // m_lds is reused as the arrival flag
     if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, flag)) return;
-    float* wts = reinterpret_cast<float*>(smem + C::RED_BYTES);
+    float* wts = reinterpret_cast<float*>(body);
     fused_combine(a, unit, nsplit, g0, gcnt, a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D,
                   wts, C::GP);
 }
 
-template <int D>
-static hipError_t launch_mfma_d(const Plan& p, const DecodeArgs& a, hipStream_t stream) {
+template <int D, int NG>
+static hipError_t launch_one(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                             hipEvent_t ev1) {
+    constexpr int lds = MfmaCfg<D, NG>::LDS_BYTES;
+    if (lds > 64 * 1024) {
+        // More than 64 KB of LDS must be opted into, once per device.
+        static std::atomic<uint64_t> done_mask{0};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const uint64_t bit = 1ull << (dev & 63);
+        if (!(done_mask.load() & bit)) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<D, NG>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) return e;
+            done_mask.fetch_or(bit);
+        }
+    }
     const dim3 grid((unsigned)p.grid_main, (unsigned)p.head_blocks);
     const dim3 block(256);
-    switch (p.heads_per_block / 16) {
-        case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_mfma_kernel<D, 2>), grid, block, 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((decode_mfma_kernel<D, 3>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4>), grid, block, 0, stream, a); break;
-        default: return hipErrorInvalidValue;
+    if (ev0 || ev1) {
+        // The dispatch packet itself records the two events, so their interval is
+        // the kernel's execution time (no launch or queueing overhead).
+        hipExtLaunchKernelGGL((decode_mfma_kernel<D, NG>), grid, block, lds, stream, ev0, ev1, 0, a);
+    } else {
+        hipLaunchKernelGGL((decode_mfma_kernel<D, NG>), grid, block, lds, stream, a);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream) {
+template <int D>
+static hipError_t launch_mfma_d(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                                hipEvent_t ev1) {
+    // Groups of more than 16 heads go to the one-wave-per-16-heads kernel.
+    if (p.heads_per_block != 16) return hipErrorInvalidValue;
+    return launch_one<D, 1>(p, a, stream, ev0, ev1);
+}
+
+hipError_t launch_decode_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                              hipEvent_t ev1) {
     switch (a.D) {
-        case 64: return launch_mfma_d<64>(p, a, stream);
-        case 128: return launch_mfma_d<128>(p, a, stream);
-        case 256: return launch_mfma_d<256>(p, a, stream);
+        case 64: return launch_mfma_d<64>(p, a, stream, ev0, ev1);
+        case 128: return launch_mfma_d<128>(p, a, stream, ev0, ev1);
+        case 256: return launch_mfma_d<256>(p, a, stream, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }

@@ -27,25 +27,21 @@ __device__ __forceinline__ float row_sum(float x) {
     x += dpp_f32<kDppQuadXor2>(x);
     x += dpp_f32<kDppRowHalfMirror>(x);
     if constexpr (RL >= 16) x += dpp_f32<kDppRowMirror>(x);
-    if constexpr (RL >= 32) x += shfl_xor_f32(x, 16);
+    if constexpr (RL >= 32) x = sum_xor16(x);
     return x;
 }
 
-// Reduction over the lanes that share a column slot but sit in different rows.
+// Reduction over the lanes that share a column slot but sit in different rows
+// (lane i meets lanes i^RL, ..., i^32): DPP inside a 16-lane row, permlane
+// swaps across rows.
 template <int RL, bool MAX>
 __device__ __forceinline__ float across_rows(float x) {
     if constexpr (RL <= 8) {
         const float y = dpp_f32<kDppRowRor8>(x);
         x = MAX ? fmaxf(x, y) : x + y;
     }
-    if constexpr (RL <= 16) {
-        const float y = shfl_xor_f32(x, 16);
-        x = MAX ? fmaxf(x, y) : x + y;
-    }
-    {
-        const float y = shfl_xor_f32(x, 32);
-        x = MAX ? fmaxf(x, y) : x + y;
-    }
+    if constexpr (RL <= 16) x = MAX ? max_xor16(x) : sum_xor16(x);
+    x = MAX ? max_xor32(x) : sum_xor32(x);
     return x;
 }
 
@@ -63,7 +59,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     static_assert(NW * D >= kFusedMaxSplits + 2, "fused-combine weights fit in mrg_o");
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (wave-uniform)
     const int rl = lane % RL, rr = lane / RL;
 
     long long unit;
@@ -76,6 +72,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
+    // Workgroup-uniform; stated so the compiler keeps them (and the buffer
+    // descriptors built from them) in scalar registers.
+    b = __builtin_amdgcn_readfirstlane(b);
+    len = __builtin_amdgcn_readfirstlane(len);
     const int p0 = s * a.chunk;
     if (s > 0 && p0 >= len) return;
     const int p1 = min(p0 + a.chunk, len);
@@ -93,9 +93,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     }
 
     const size_t pos_stride = (size_t)a.Hkv * D;
-    const uint16_t* kbase = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D + 8 * rl;
-    const uint16_t* vbase = a.v + ((size_t)b * a.Lmax * a.Hkv + kvh) * D + 8 * rl;
+    const int rowbytes = (int)(pos_stride * 2);
+    const uint16_t* kseq = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
+    const uint16_t* vseq = a.v + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
     const float qk = a.qk_log2;
+    // Byte offset of this lane's 8 columns in row st*RS + rr of a block.
+    int off[NB];
+#pragma unroll
+    for (int st = 0; st < NB; ++st) off[st] = (st * RS + rr) * rowbytes + rl * 16;
 
     float m[GB], l[GB], o[GB][8];
 #pragma unroll
@@ -109,49 +114,61 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const int nblk = p1 > p0 ? (p1 - p0 + WB - 1) / WB : 0;
     for (int blk = w; blk < nblk; blk += NW) {
         const int t0 = p0 + blk * WB;
+        // Buffer range ends at the last valid row: rows past it read as zero
+        // without a memory access, and their logits are masked below.
+        const int rows = min(WB, p1 - t0);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kseq + (size_t)t0 * pos_stride, rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vseq + (size_t)t0 * pos_stride, rows * rowbytes);
         u32x4_t kr[NB], vr[NB];
-        // Unconditional loads; a position past the end re-reads the last valid row,
-        // whose logit is masked to -inf below (weight exactly 0).
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
-            const int t = min(t0 + st * RS + rr, p1 - 1);
-            kr[st] = load_nt_u32x4(kbase + (size_t)t * pos_stride);
-            vr[st] = load_nt_u32x4(vbase + (size_t)t * pos_stride);
+            kr[st] = buffer_load_u32x4(krs, off[st]);
+            vr[st] = buffer_load_u32x4(vrs, off[st]);
         }
         // logits (base-2 units), masked past the end
+        const bool tail = rows < WB;
         float sc[NB][GB];
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
-            const bool ok = t0 + st * RS + rr < p1;
+            const bool ok = !tail || st * RS + rr < rows;
 #pragma unroll
             for (int gg = 0; gg < GB; ++gg) {
                 float acc = 0.f;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) acc = dot2_bf16(qv[gg][c], kr[st][c], acc);
-                acc = row_sum<RL>(acc);
-                sc[st][gg] = ok ? acc * qk : -INFINITY;
+                acc = row_sum<RL>(acc) * qk;
+                sc[st][gg] = ok ? acc : -INFINITY;
             }
         }
-        // online softmax update for the block
-        uint32_t pbits[NB][GB];
+        // online softmax update for the block, with lazy rescaling
+        uint32_t pp[NB / 2][GB];
+        bool any_rescale = false;
+        float alpha[GB];
 #pragma unroll
         for (int gg = 0; gg < GB; ++gg) {
             float mx = sc[0][gg];
 #pragma unroll
             for (int st = 1; st < NB; ++st) mx = fmaxf(mx, sc[st][gg]);
             mx = across_rows<RL, true>(mx);
-            const float m_new = fmaxf(m[gg], mx);
-            const float alpha = __builtin_amdgcn_exp2f(m[gg] - m_new);
-            m[gg] = m_new;
+            const bool moved = mx > m[gg] + kRescaleSlack;
+            alpha[gg] = moved ? __builtin_amdgcn_exp2f(m[gg] - mx) : 1.f;
+            m[gg] = moved ? mx : m[gg];
+            any_rescale |= moved;
             float lsum = 0.f;
 #pragma unroll
-            for (int st = 0; st < NB; ++st) {
-                pbits[st][gg] = f32_to_bf16_bits(__builtin_amdgcn_exp2f(sc[st][gg] - m_new));
-                lsum += bf16_bits_to_f32(pbits[st][gg]);
+            for (int st = 0; st < NB; st += 2) {
+                const uint32_t pair = pack2_bf16_rne(__builtin_amdgcn_exp2f(sc[st][gg] - m[gg]),
+                                                     __builtin_amdgcn_exp2f(sc[st + 1][gg] - m[gg]));
+                pp[st / 2][gg] = pair;
+                lsum += bf16_lo_f32(pair) + bf16_hi_f32(pair);
             }
-            l[gg] = l[gg] * alpha + lsum;
+            l[gg] = l[gg] * alpha[gg] + lsum;
+        }
+        if (__any(any_rescale)) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[gg][j] *= alpha;
+            for (int gg = 0; gg < GB; ++gg)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[gg][j] *= alpha[gg];
         }
         // P.V: two positions of one column per v_dot2
 #pragma unroll
@@ -162,9 +179,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                 const uint32_t hi = perm_b32(vr[st + 1][c], vr[st][c], kPermHiHalves);
 #pragma unroll
                 for (int gg = 0; gg < GB; ++gg) {
-                    const uint32_t pp = pack_bf16x2(pbits[st][gg], pbits[st + 1][gg]);
-                    o[gg][2 * c] = dot2_bf16(pp, lo, o[gg][2 * c]);
-                    o[gg][2 * c + 1] = dot2_bf16(pp, hi, o[gg][2 * c + 1]);
+                    o[gg][2 * c] = dot2_bf16(pp[st / 2][gg], lo, o[gg][2 * c]);
+                    o[gg][2 * c + 1] = dot2_bf16(pp[st / 2][gg], hi, o[gg][2 * c + 1]);
                 }
             }
         }
@@ -228,25 +244,36 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                   &mrg_o[0][0][0], GB);
 }
 
-template <int D>
-static hipError_t launch_valu_d(const Plan& p, const DecodeArgs& a, hipStream_t stream) {
+template <int D, int GB>
+static hipError_t launch_one(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                             hipEvent_t ev1) {
     const dim3 grid((unsigned)p.grid_main, (unsigned)p.head_blocks);
     const dim3 block(256);
-    switch (p.heads_per_block) {
-        case 1: hipLaunchKernelGGL((decode_valu_kernel<D, 1>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((decode_valu_kernel<D, 2>), grid, block, 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_valu_kernel<D, 4>), grid, block, 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((decode_valu_kernel<D, 8>), grid, block, 0, stream, a); break;
-        default: return hipErrorInvalidValue;
-    }
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL((decode_valu_kernel<D, GB>), grid, block, 0, stream, ev0, ev1, 0, a);
+    else
+        hipLaunchKernelGGL((decode_valu_kernel<D, GB>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_valu(const Plan& p, const DecodeArgs& a, hipStream_t stream) {
+template <int D>
+static hipError_t launch_valu_d(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                                hipEvent_t ev1) {
+    switch (p.heads_per_block) {
+        case 1: return launch_one<D, 1>(p, a, stream, ev0, ev1);
+        case 2: return launch_one<D, 2>(p, a, stream, ev0, ev1);
+        case 4: return launch_one<D, 4>(p, a, stream, ev0, ev1);
+        case 8: return launch_one<D, 8>(p, a, stream, ev0, ev1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_valu(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                              hipEvent_t ev1) {
     switch (a.D) {
-        case 64: return launch_valu_d<64>(p, a, stream);
-        case 128: return launch_valu_d<128>(p, a, stream);
-        case 256: return launch_valu_d<256>(p, a, stream);
+        case 64: return launch_valu_d<64>(p, a, stream, ev0, ev1);
+        case 128: return launch_valu_d<128>(p, a, stream, ev0, ev1);
+        case 256: return launch_valu_d<256>(p, a, stream, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }

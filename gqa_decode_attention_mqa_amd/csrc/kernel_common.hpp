@@ -93,6 +93,72 @@ __device__ __forceinline__ u32x2_t load_nt_u32x2(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
 }
 
+// Buffer resources: raw (unstructured) buffers whose range check makes an
+// access at or beyond num_records bytes return zero without touching memory.
+constexpr int kBufferFlags = 0x00020000;   // 32-bit data format, as gfx9 raw buffers expect
+constexpr int kCachePolicyNT = 2;          // non-temporal: K/V rows are read exactly once
+
+// `base` and `num_bytes` must be uniform across the wave; they are moved to
+// scalar registers explicitly, or the compiler would wrap every load in a
+// loop over distinct descriptors.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_bytes) {
+    const uint64_t addr = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, __builtin_amdgcn_readfirstlane(num_bytes), kBufferFlags);
+}
+__device__ __forceinline__ u32x4_t buffer_load_u32x4(__amdgpu_buffer_rsrc_t r, int voffset) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, kCachePolicyNT));
+}
+__device__ __forceinline__ u32x2_t buffer_load_u32x2(__amdgpu_buffer_rsrc_t r, int voffset) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voffset, 0, kCachePolicyNT));
+}
+
+// Reductions across the 16-lane rows of a wave without LDS: v_permlane16_swap
+// pairs row 0 with 1 and 2 with 3 (lane i meets lane i^16), v_permlane32_swap
+// pairs the two halves (lane i meets lane i^32).  Each returns both values.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Two floats -> packed bf16 pair with hardware round-to-nearest-even
+// (v_cvt_pk_bf16_f32); `a` lands in the low half.
+__device__ __forceinline__ uint32_t pack2_bf16_rne(float a, float b) {
+    bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo_f32(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most STAGES * PER
+// vector-memory operations of this wave are outstanding, leaving the LDS and
+// export counters unconstrained.  Counts above the 6-bit field wait longer,
+// which is always safe.
+template <int STAGES, int PER>
+constexpr int kVmcntStages() {
+    constexpr int n = STAGES * PER > 63 ? 63 : STAGES * PER;
+    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+// Lazy rescaling of the online softmax: the running maximum of a head only
+// moves when a tile's maximum exceeds it by more than this many (base-2)
+// units, so exp2(s - m) <= 2^8 and the accumulators are rescaled rarely.
+constexpr float kRescaleSlack = 8.0f;
+
 // Round-to-nearest-even float -> bf16 bits (inputs here are finite or +0).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -123,6 +189,20 @@ __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
 __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 16x16x16 bf16 tile: 4 k-slots per lane (lane group kg holds k = 4*kg .. 4*kg+3).
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma_16x16x16_bf16(const u32x2_t& a, const u32x2_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+// P.V tile over the k-slots of one step: 8 (two 16-row S^T tiles) or 4 (one).
+__device__ __forceinline__ f32x4_t mfma_pv(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+    return mfma_16x16x32_bf16(a, b, c);
+}
+__device__ __forceinline__ f32x4_t mfma_pv(const u32x2_t& a, const u32x2_t& b, const f32x4_t& c) {
+    return mfma_16x16x16_bf16(a, b, c);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

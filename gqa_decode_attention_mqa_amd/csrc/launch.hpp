@@ -1,6 +1,7 @@
 // Kernel launchers (defined in the .hip files, called by the C ABI layer).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kernel_common.hpp"
@@ -8,10 +9,16 @@
 
 namespace mqa {
 
-// Split-K kernel on matrix cores (any group size; 16 heads per tile).
-hipError_t launch_decode_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream);
+// Split-K kernel on matrix cores (any group size; 16 heads per tile).  When
+// ev0/ev1 are non-null the dispatch itself records them around the kernel.
+hipError_t launch_decode_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                              hipEvent_t ev1);
+// Split-K kernel on matrix cores with one wave per 16 heads (groups of 32+).
+hipError_t launch_decode_mfma_heads(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                                    hipEvent_t ev1);
 // Split-K kernel on the vector ALU (groups of up to 8 heads per workgroup).
-hipError_t launch_decode_valu(const Plan& p, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_valu(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                              hipEvent_t ev1);
 // Log-sum-exp merge of the per-chunk partials of split sequences.
 hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream);
 

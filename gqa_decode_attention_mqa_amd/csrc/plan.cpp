@@ -63,6 +63,9 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         return fail(MQA_ERR_UNSUPPORTED, "head size D must be 64, 128 or 256");
     if (!std::isfinite(scale))
         return fail(MQA_ERR_ARG, "scale must be finite");
+    // Kernels address a tile of up to 128 positions through 32-bit buffer offsets.
+    if ((long long)Hkv * D * 2 * kChunkQuantum > 0x7FFFFFFFLL)
+        return fail(MQA_ERR_UNSUPPORTED, "Hkv * D too large for 32-bit tile offsets");
 
     mqa_decode_opts o{};
     if (opts) o = *opts;

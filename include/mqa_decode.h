@@ -86,9 +86,9 @@ typedef struct mqa_decode_opts {
                              2 = combine fused into the split kernel: the last chunk of
                              each (sequence, kv head) to finish merges the partials
                              (at most 16 chunks per sequence, else MQA_ERR_ARG)          */
-    void *ev_main_begin;  /* optional hipEvent_t recorded on `stream` right before the
-                             split-K kernel launch (for timing that kernel alone)         */
-    void *ev_main_end;    /* optional hipEvent_t recorded right after it                  */
+    void *ev_main_begin;  /* optional hipEvent_t pair recorded by the split-K kernel's own
+                             dispatch (hipExtLaunchKernelGGL) at its start and end, so  */
+    void *ev_main_end;    /* their interval is that kernel's execution time alone      */
 } mqa_decode_opts;
 
 /* What the planner decided for a shape (host-only query, no HIP call). */
