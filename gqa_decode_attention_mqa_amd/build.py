@@ -24,6 +24,10 @@ SOURCES = ["abi.cpp", "plan.cpp", "decode_mfma.hip", "decode_mfma_hs.hip", "deco
 COMMON = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # matrix-core accumulators in ordinary VGPRs: the online-softmax
+          # rescale touches them with vector ALU ops, and AGPR accumulators
+          # cost a copy in and out around every product
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", str(ROOT / "include")]
 
 

@@ -4,25 +4,27 @@
 // 48-head multiquery attention of PaLM 540B in "Efficiently Scaling
 // Transformer Inference", section 3.4, "Attention Layer Partitioning") a
 // workgroup of NG waves owns (query row, kv head, chunk of positions, block of
-// 16*NG heads).  Wave w owns heads 16w .. 16w+15 for every position of the
-// chunk, so no two waves ever need to merge softmax state.  The chunk's K and
-// V rows are read from HBM exactly once per workgroup into an LDS ring of
+// 16*NG heads).  Wave w < NG owns heads 16w .. 16w+15 for every position of
+// the chunk, so no two waves ever need to merge softmax state.  The chunk's K
+// and V rows are read from HBM exactly once per workgroup into an LDS ring of
 // STAGES tiles of 32 positions, with direct buffer-to-LDS loads (no registers
-// hold data in flight); every wave then reads the whole tile from LDS.
+// hold data in flight, and STAGES - 2 tiles are in flight at once); every
+// compute wave then reads the whole tile from LDS.  All waves share the loads
+// evenly; with three compute waves a fourth wave only loads.
 //
-// Per tile, in each wave:
+// Per tile, in each compute wave:
 //   * S^T = K q^T on 16x16x32 bf16 tiles: A = two 16-row K tiles (read from
 //     LDS), B = this wave's q^T (registers).  Head g = lane mod 16.
 //   * base-2 online softmax with lazy rescaling; the two S^T accumulators are
 //     exactly the 8 k-slots per lane of the P^T operand of P.V.
-//   * O^T += V^T P^T on 16x16x32 tiles: V rows read from LDS and transposed
-//     in registers with v_perm_b32 (row = d, 8 positions per lane).
-// LDS layout of a tile: row t of D bf16 = D/8 chunks of 16 bytes; chunk c of
-// row t sits in slot c ^ (t mod 8).  The direct loads realise the swizzle by
-// choosing, for each lane's 16-byte LDS slot, the global chunk that belongs
-// there.  Rows at or past the end of the chunk are out of the buffer range and
-// arrive as zeros; their logits are masked, so padding is never read.
+//   * O^T += V^T P^T on 16x16x32 tiles: the V^T operand is read from LDS with
+//     gfx950's transposing LDS reads (ds_read_b64_tr_b16), so no lane shuffles.
+// The loop is software-pipelined by one tile: q.K of the next tile is issued
+// together with P.V of the current one.
+// Rows at or past the end of the chunk are out of the buffer range and arrive
+// as zeros; their logits are masked, so padding is never read.
 #include <atomic>
+#include <type_traits>
 
 #include "kernel_common.hpp"
 #include "launch.hpp"
@@ -31,32 +33,89 @@ namespace mqa {
 
 template <int D, int NG>
 struct HsCfg {
-    static constexpr int NW = NG;                    // waves = 16-head tiles
+    // NG compute waves (one per 16-head tile); three of them get a fourth,
+    // load-only wave so that every wave issues the same number of loads.
+    static constexpr int NW = NG == 3 ? 4 : NG;
     static constexpr int THREADS = 64 * NW;
     static constexpr int STEP = 32;                  // positions per tile
-    static constexpr int STAGES = 4;                 // tiles in the LDS ring
+    static constexpr int STAGES = D == 256 ? 5 : 4;  // tiles in the LDS ring (D = 256: all 160 KB)
+    static_assert(STAGES >= 4, "two tiles in use and at least one more in flight");
     static constexpr int KS = D / 32;                // k-steps over d in q.K
-    static constexpr int DPL = D / 16;               // V columns per lane = M tiles of O^T
+    static constexpr int MT = D / 16;                // 16-row tiles of O^T
     static constexpr int CPR = D / 8;                // 16-byte chunks per row
     static constexpr int TILE_BYTES = STEP * D * 2;  // K (or V) bytes of one tile
     static constexpr int LOADS = TILE_BYTES / 1024;  // wave-wide 16-byte loads per tile (K or V)
-    static constexpr int KPW = (LOADS + NW - 1) / NW;  // K loads (and V loads) each wave issues per tile
-    static constexpr int PER_WAVE = 2 * KPW;           // every wave issues exactly this many
-    static constexpr bool SPARE = LOADS % NW != 0;     // some waves issue out-of-range fillers
-    static constexpr int RING_BYTES = STAGES * 2 * TILE_BYTES;
-    static constexpr int LDS_BYTES = RING_BYTES + (SPARE ? 1024 : 0);
+    static constexpr int KPW = LOADS / NW;           // K loads (and as many V loads) per wave per tile
+    static constexpr int PER_WAVE = 2 * KPW;
+    static constexpr int LDS_BYTES = STAGES * 2 * TILE_BYTES;
     static_assert(D >= 64 && D % 64 == 0, "head size");
+    static_assert(LOADS % NW == 0, "every wave issues the same number of loads");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
     static_assert(LDS_BYTES >= (kFusedMaxSplits + 2) * 16 * NG * 4, "fused-combine weights fit");
 };
 
+// LDS layout of a tile: row t (D bf16) is D/8 chunks of 16 bytes, and chunk
+// c of row t sits in slot c ^ swz_key(t).  The key takes all eight values over
+// any eight consecutive rows (the K reads of eight lanes hit eight different
+// 16-byte bank groups), and over rows 4i .. 4i+3 it takes four values that
+// differ above bit 0 (the transposing V reads of a 16-lane group, two
+// adjacent chunks of four rows, hit 128 distinct bytes of banks).
+__device__ __forceinline__ int swz_key(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
 // LDS byte offset of chunk c of row t inside a tile.
 template <int CPR>
 __device__ __forceinline__ int swz(int t, int c) {
-    return (t * CPR + (c ^ (t & 7))) * 16;
+    return (t * CPR + (c ^ swz_key(t))) * 16;
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS byte address of a pointer into this kernel's dynamic LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// gfx950 transposing LDS read of 16-bit elements (ds_read_b64_tr_b16) at
+// LDS byte address addr + OFF.  In each group of 16 lanes, lane i receives
+// element (i mod 4) of the 8-byte rows addressed by lanes 4j + i/4 of its
+// group, j = 0..3 (checked on MI355X).
+//
+// Issued through inline asm: the compiler builtin makes the compiler wait for
+// every buffer-to-LDS load in flight before each such read, which would
+// drain the ring.  The compiler does not know this asm reads LDS, so the
+// caller must wait for it (s_waitcnt lgkmcnt) and tie the results to that
+// wait before using them; any LDS wait the compiler emits for its own reads
+// stays correct, since unknown later LDS reads only make it wait longer.
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read_tr16_b64_asm(uint32_t addr) {
+    u32x2_t r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// The V^T operands of one tile: for 16-row tile m of d, the transposing reads
+// at rows `lo` and `hi` (the lane's two groups of four positions).  Returns
+// once every read has landed, with the results tied to that wait.
+template <int MT>
+__device__ __forceinline__ void read_vt_tile(uint32_t vbase, const int (&alo)[4], const int (&ahi)[4],
+                                             u32x2_t (&lo)[MT], u32x2_t (&hi)[MT]) {
+    static_for<0, MT>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        lo[m] = ds_read_tr16_b64_asm<128 * (m >> 2)>(vbase + alo[m & 3]);
+        hi[m] = ds_read_tr16_b64_asm<128 * (m >> 2)>(vbase + ahi[m & 3]);
+    });
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(lo[m]), "+v"(hi[m]));
+}
 
 template <int D, int NG>
 __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
@@ -104,11 +163,8 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
 
     // Issue this wave's share of the loads of tile `tile` into ring slot tile % STAGES.
     // Load jj (0 .. LOADS-1) covers 1 KB of the K tile and, with a second
-    // load, the same 1 KB of the V tile; wave w issues jj = w, w + NW, ...
-    // Every wave issues KPW of each, so all waves keep the same count of loads
-    // in flight: a jj past the tile is a filler whose offset is out of range
-    // (it reads nothing and writes zeros to a spare 1 KB past the ring).
-    constexpr unsigned kOutOfRange = 0x7FFFFFF0u;  // the planner bounds 128 rows of K to 2^31 bytes
+    // load, the same 1 KB of the V tile; wave w issues jj = w, w + NW, ...,
+    // KPW of each, so all waves keep the same count of loads in flight.
     auto issue_tile = [&](int tile) {
         const int t0 = p0 + tile * C::STEP;
         const int rows = max(0, min(C::STEP, p1 - t0));
@@ -118,49 +174,39 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < C::KPW; ++i) {
             const int jj = w + C::NW * i;
-            const bool real = !C::SPARE || jj < C::LOADS;
             const int p = jj * 64 + lane;  // 16-byte LDS slot in the tile
             const int t = p / C::CPR, cs = p % C::CPR;
-            const unsigned voff = real ? (unsigned)(t * rowbytes + ((cs ^ (t & 7)) * 16)) : kOutOfRange;
-            unsigned char* dst = real ? slot + jj * 1024 : smem + C::RING_BYTES;
-            unsigned char* vdst = real ? dst + C::TILE_BYTES : dst;
+            const int voff = t * rowbytes + ((cs ^ swz_key(t)) * 16);
+            unsigned char* dst = slot + jj * 1024;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)dst, 16, voff, 0, 0, kCachePolicyNT);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)vdst, 16, voff, 0, 0, kCachePolicyNT);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dst + C::TILE_BYTES), 16, voff, 0, 0,
+                                                     kCachePolicyNT);
         }
     };
-
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4_t oacc[C::DPL];
-#pragma unroll
-    for (int j = 0; j < C::DPL; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const float qk = a.qk_log2;
-
-    // Prologue: STAGES - 1 tiles in flight (tiles past the end read nothing).
-    // q was issued first, so waiting until only the prologue's loads remain
-    // guarantees q without waiting for any tile.
-#pragma unroll
-    for (int t = 0; t < C::STAGES - 1; ++t) issue_tile(t);
-    __builtin_amdgcn_s_waitcnt(kVmcntStages<C::STAGES - 1, C::PER_WAVE>());
-
-    for (int tile = 0; tile < ntiles; ++tile) {
-        // Tile `tile` has landed once at most (STAGES - 2) later tiles of this
-        // wave are still outstanding, and this wave's reads of the previous
-        // tile are done once no LDS read is pending.  The barrier then
-        // publishes every wave's part and frees the slot refilled below.  A
-        // plain s_barrier, not __syncthreads: the latter's release fence also
-        // waits for the loads still in flight to the ring.
-        __builtin_amdgcn_s_waitcnt(kVmcntStages<C::STAGES - 2, C::PER_WAVE>() & ~(0xF << 8));
+    // Tile `tile` and everything before it has landed once at most `later`
+    // tiles issued after it are still outstanding in this wave; no LDS read of
+    // this wave is pending either.  The barrier then publishes every wave's
+    // part of the ring.  A plain s_barrier, not __syncthreads: the latter's
+    // release fence would also wait for the loads still in flight to the ring.
+    auto ring_sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(kVmcntStages<C::STAGES - 3, C::PER_WAVE>() & ~(0xF << 8));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue_tile(tile + C::STAGES - 1);
+    };
 
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t oacc[C::MT];  // O^T tile m: rows d = 16m .. 16m+15, column = head
+#pragma unroll
+    for (int j = 0; j < C::MT; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float qk = a.qk_log2;
+
+    // S^T = K q^T for one tile: A = two 16-row K tiles read from LDS, B = q^T.
+    // Accumulator lane (li, kg), element r of tile mq: head li, position 16mq + 4kg + r.
+    auto qk_tile = [&](int tile, f32x4_t (&sacc)[2]) {
         const unsigned char* kt = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
-        const unsigned char* vt = kt + C::TILE_BYTES;
-        const int st = p0 + tile * C::STEP;
-
-        // ---- S^T = K q^T (two 16-row tiles)
-        f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        sacc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
@@ -170,7 +216,11 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
                 sacc[mq] = mfma_16x16x32_bf16(ka, qb[ks], sacc[mq]);
             }
         }
-        // ---- scale, mask the tail, lazy online softmax, P^T in registers
+    };
+    // Scale, mask the tail, lazy online softmax; P^T of the tile in registers.
+    // Returns whether the running maximum moved (then O must be rescaled by alpha).
+    auto softmax_tile = [&](int tile, f32x4_t (&sacc)[2], u32x4_t& pb, float& alpha) {
+        const int st = p0 + tile * C::STEP;
 #pragma unroll
         for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
@@ -186,9 +236,8 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
                          fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
         mx = max_xor32(max_xor16(mx));
         const bool moved = mx > m_run + kRescaleSlack;
-        const float alpha = moved ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+        alpha = moved ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
         m_run = moved ? mx : m_run;
-        u32x4_t pb;
         float lsum = 0.f;
 #pragma unroll
         for (int mq = 0; mq < 2; ++mq) {
@@ -201,44 +250,74 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
             lsum += (bf16_lo_f32(lo) + bf16_hi_f32(lo)) + (bf16_lo_f32(hi) + bf16_hi_f32(hi));
         }
         l_run = l_run * alpha + lsum;
-        if (__any(moved)) {
+        return __any(moved);
+    };
+    // O^T += V^T P^T for one tile.  The A operand (row d = 16m + li, eight
+    // positions per lane group) comes straight from LDS with transposing
+    // reads: in each 16-lane group, lane 4j + b points at the 8 bytes
+    // d = 16m + 4b .. +3 of position row j, and lane li receives column
+    // 16m + li of the four rows.  Element e of lane group kg is position
+    // 16*(e/4) + 4*kg + e%4, the order of the P^T operand.
+    //   Chunk 2m + x (x = 0, 1) of row t sits at the slot of chunk
+    // 2(m mod 4) + x plus 8 (m div 4), since the swizzle key is below 8, so
+    // four address registers per row and constant offsets cover all m.
+    const int tr_j = li >> 2, tr_b = li & 3;
+    const int tr_tlo = 4 * kg + tr_j, tr_thi = 16 + 4 * kg + tr_j;
+    int tr_lo[4], tr_hi[4];
 #pragma unroll
-            for (int j = 0; j < C::DPL; ++j) oacc[j] = oacc[j] * alpha;
+    for (int mm = 0; mm < 4; ++mm) {
+        const int c = 2 * mm + (tr_b >> 1), half = (tr_b & 1) * 8;
+        tr_lo[mm] = swz<C::CPR>(tr_tlo, c) + half;
+        tr_hi[mm] = swz<C::CPR>(tr_thi, c) + half;
+    }
+    auto pv_tile = [&](int tile, const u32x4_t& pb) {
+        const uint32_t vbase = lds_addr(smem + (tile % C::STAGES) * 2 * C::TILE_BYTES + C::TILE_BYTES);
+        u32x2_t lo[C::MT], hi[C::MT];
+        read_vt_tile<C::MT>(vbase, tr_lo, tr_hi, lo, hi);
+#pragma unroll
+        for (int m = 0; m < C::MT; ++m) {
+            const u32x4_t va = {lo[m].x, lo[m].y, hi[m].x, hi[m].y};
+            oacc[m] = mfma_16x16x32_bf16(va, pb, oacc[m]);
         }
+    };
 
-        // ---- O^T += V^T P^T.  Element e of lane group kg is position
-        // 16*(e/4) + 4*kg + e%4; lane li holds columns DPL*li .. DPL*li + DPL-1.
-        constexpr int VW = C::DPL / 2;  // dwords per row per lane
-        uint32_t vr[8][VW];
+    // Prologue: tiles 0 .. STAGES-3 in flight (tiles past the end read
+    // nothing).  q was issued first, so waiting until only those loads remain
+    // guarantees q without waiting for any tile.
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = 16 * (e / 4) + 4 * kg + (e % 4);
-            if constexpr (VW >= 4) {
-#pragma unroll
-                for (int h = 0; h < VW / 4; ++h) {
-                    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vt + swz<C::CPR>(t, (VW / 4) * li + h));
-                    vr[e][4 * h] = x.x;
-                    vr[e][4 * h + 1] = x.y;
-                    vr[e][4 * h + 2] = x.z;
-                    vr[e][4 * h + 3] = x.w;
-                }
-            } else {
-                // D = 64: 8 bytes per lane, half of chunk li/2
-                const u32x2_t x = *reinterpret_cast<const u32x2_t*>(vt + swz<C::CPR>(t, li >> 1) + 8 * (li & 1));
-                vr[e][0] = x.x;
-                vr[e][1] = x.y;
-            }
+    for (int t = 0; t < C::STAGES - 2; ++t) issue_tile(t);
+    __builtin_amdgcn_s_waitcnt(kVmcntStages<C::STAGES - 2, C::PER_WAVE>());
+
+    // Software pipeline: step `tile` reads V of `tile` (P.V with the P^T made
+    // in the previous step) and K of `tile` + 1 (q.K and its softmax), so the
+    // matrix cores and the vector ALU overlap inside each wave.  Ring slots
+    // in use during a step: `tile` and `tile` + 1; the step refills the slot
+    // of `tile` - 1 with `tile` + STAGES - 1, so STAGES - 2 tiles stay in flight.
+    u32x4_t pb = {0u, 0u, 0u, 0u};
+    if (ntiles > 0) {
+        ring_sync();  // tile 0 landed
+        issue_tile(C::STAGES - 2);
+        if (w < NG) {
+            f32x4_t sacc[2];
+            qk_tile(0, sacc);
+            float alpha;
+            softmax_tile(0, sacc, pb, alpha);  // O is still zero: no rescale
         }
+    }
+    for (int tile = 0; tile < ntiles; ++tile) {
+        ring_sync();  // tile + 1 landed (a no-op read past the end)
+        issue_tile(tile + C::STAGES - 1);
+        if (w >= NG) continue;  // the load-only wave
+        const bool next = tile + 1 < ntiles;
+        f32x4_t sacc[2];
+        if (next) qk_tile(tile + 1, sacc);
+        pv_tile(tile, pb);
+        if (next) {
+            float alpha;
+            if (softmax_tile(tile + 1, sacc, pb, alpha)) {
 #pragma unroll
-        for (int wd = 0; wd < VW; ++wd) {
-            u32x4_t va_even, va_odd;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                va_even[m] = perm_b32(vr[2 * m + 1][wd], vr[2 * m][wd], kPermLoHalves);
-                va_odd[m] = perm_b32(vr[2 * m + 1][wd], vr[2 * m][wd], kPermHiHalves);
+                for (int m = 0; m < C::MT; ++m) oacc[m] = oacc[m] * alpha;
             }
-            oacc[2 * wd] = mfma_16x16x32_bf16(va_even, pb, oacc[2 * wd]);
-            oacc[2 * wd + 1] = mfma_16x16x32_bf16(va_odd, pb, oacc[2 * wd + 1]);
         }
     }
 
@@ -251,21 +330,17 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
     const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
     const bool direct = nsplit == 1;
     const int g = 16 * w + li;  // head inside the block
-    if (g < gcnt) {
+    if (w < NG && g < gcnt) {
         const int gh = g0 + g;
         float* dst;
         if (direct)
             dst = a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D;
         else
             dst = a.part_o + (((size_t)unit * a.max_splits + s) * a.G + gh) * D;
+        // accumulator rows 4kg .. 4kg+3 of tile m are d = 16m + 4kg .. +3
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int q4 = 0; q4 < C::DPL / 4; ++q4) {
-                const int d = C::DPL * (4 * kg + r) + 4 * q4;
-                *reinterpret_cast<f32x4_t*>(dst + d) =
-                    f32x4_t{oacc[4 * q4][r], oacc[4 * q4 + 1][r], oacc[4 * q4 + 2][r], oacc[4 * q4 + 3][r]} * inv_l;
-            }
+        for (int m = 0; m < C::MT; ++m)
+            *reinterpret_cast<f32x4_t*>(dst + 16 * m + 4 * kg) = oacc[m] * inv_l;
         if (!direct && kg == 0)
             a.part_lse[((size_t)unit * a.max_splits + s) * a.G + gh] = m_run + __log2f(l_run);
     }
