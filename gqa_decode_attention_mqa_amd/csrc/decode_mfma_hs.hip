@@ -33,9 +33,13 @@ namespace mqa {
 
 template <int D, int NG>
 struct HsCfg {
-    // NG compute waves (one per 16-head tile); three of them get a fourth,
-    // load-only wave so that every wave issues the same number of loads.
-    static constexpr int NW = NG == 3 ? 4 : NG;
+    // NG compute waves (one per 16-head tile) and NL load-only waves.  The
+    // loads of a tile all leave right after the ring barrier and queue in the
+    // CU's address unit; a wave stalls until its own are accepted, so they are
+    // kept off the compute waves.  Two loaders keep three tiles in flight
+    // within the 63 loads a wave can have outstanding.
+    static constexpr int NL = 2;
+    static constexpr int NW = NG + NL;
     static constexpr int THREADS = 64 * NW;
     static constexpr int STEP = 32;                  // positions per tile
     static constexpr int STAGES = D == 256 ? 5 : 4;  // tiles in the LDS ring (D = 256: all 160 KB)
@@ -45,11 +49,12 @@ struct HsCfg {
     static constexpr int CPR = D / 8;                // 16-byte chunks per row
     static constexpr int TILE_BYTES = STEP * D * 2;  // K (or V) bytes of one tile
     static constexpr int LOADS = TILE_BYTES / 1024;  // wave-wide 16-byte loads per tile (K or V)
-    static constexpr int KPW = LOADS / NW;           // K loads (and as many V loads) per wave per tile
-    static constexpr int PER_WAVE = 2 * KPW;
+    static constexpr int KPW = LOADS / NL;           // K loads (and as many V loads) per loader per tile
+    static constexpr int PER_WAVE = 2 * KPW;         // loads a loader issues per tile
     static constexpr int LDS_BYTES = STAGES * 2 * TILE_BYTES;
     static_assert(D >= 64 && D % 64 == 0, "head size");
-    static_assert(LOADS % NW == 0, "every wave issues the same number of loads");
+    static_assert(LOADS % NL == 0, "every loader issues the same number of loads");
+    static_assert((STAGES - 2) * PER_WAVE <= 63, "loads in flight fit a wave's counter");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
     static_assert(LDS_BYTES >= (kFusedMaxSplits + 2) * 16 * NG * 4, "fused-combine weights fit");
 };
@@ -118,7 +123,7 @@ __device__ __forceinline__ void read_vt_tile(uint32_t vbase, const int (&alo)[4]
 }
 
 template <int D, int NG>
-__global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(384) void decode_mfma_hs_kernel(DecodeArgs a) {
     using C = HsCfg<D, NG>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -149,23 +154,30 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
     const uint16_t* kseq = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
     const uint16_t* vseq = a.v + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
 
-    // This wave's q^T operand (B of q.K): lane (li, kg), k-step ks holds
+    // A compute wave's q^T operand (B of q.K): lane (li, kg), k-step ks holds
     // q[head 16w + li][32 ks + 8 kg .. +8]; heads past the group read as zero.
     u32x4_t qb[C::KS];
-    {
+    if (w >= NG) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    } else {
         const uint16_t* qblk = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D;
         const __amdgpu_buffer_rsrc_t qr = make_rsrc(qblk, gcnt * D * 2);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
             qb[ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                                       qr, (16 * w + li) * D * 2 + ks * 64 + kg * 16, 0, 0));
+        // A compute wave can do nothing before q; waiting here also tells the
+        // compiler that no load is pending into registers the loop reads.
+        __builtin_amdgcn_s_waitcnt(kVmcntStages<0, 0>());
     }
 
-    // Issue this wave's share of the loads of tile `tile` into ring slot tile % STAGES.
-    // Load jj (0 .. LOADS-1) covers 1 KB of the K tile and, with a second
-    // load, the same 1 KB of the V tile; wave w issues jj = w, w + NW, ...,
-    // KPW of each, so all waves keep the same count of loads in flight.
+    // Issue a loader's share of the loads of tile `tile` into ring slot
+    // tile % STAGES (compute waves issue nothing).  Load jj (0 .. LOADS-1)
+    // covers 1 KB of the K tile and, with a second load, the same 1 KB of the
+    // V tile; loader l issues jj = l, l + NL, ..., KPW of each.
     auto issue_tile = [&](int tile) {
+        if (w < NG) return;
         const int t0 = p0 + tile * C::STEP;
         const int rows = max(0, min(C::STEP, p1 - t0));
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kseq + (size_t)t0 * pos_stride, rows * rowbytes);
@@ -173,7 +185,7 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
         unsigned char* slot = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::KPW; ++i) {
-            const int jj = w + C::NW * i;
+            const int jj = (w - NG) + C::NL * i;
             const int p = jj * 64 + lane;  // 16-byte LDS slot in the tile
             const int t = p / C::CPR, cs = p % C::CPR;
             const int voff = t * rowbytes + ((cs ^ swz_key(t)) * 16);
@@ -183,10 +195,10 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
                                                      kCachePolicyNT);
         }
     };
-    // Tile `tile` and everything before it has landed once at most `later`
-    // tiles issued after it are still outstanding in this wave; no LDS read of
-    // this wave is pending either.  The barrier then publishes every wave's
-    // part of the ring.  A plain s_barrier, not __syncthreads: the latter's
+    // In a loader, the next tile and everything before it have landed once
+    // at most STAGES - 3 later tiles are outstanding; in every wave no LDS read
+    // is pending.  The barrier then publishes the loaders' tiles and frees the
+    // slot refilled next.  A plain s_barrier, not __syncthreads: the latter's
     // release fence would also wait for the loads still in flight to the ring.
     auto ring_sync = [&]() {
         __builtin_amdgcn_s_waitcnt(kVmcntStages<C::STAGES - 3, C::PER_WAVE>() & ~(0xF << 8));
@@ -281,12 +293,9 @@ __global__ __launch_bounds__(256) void decode_mfma_hs_kernel(DecodeArgs a) {
         }
     };
 
-    // Prologue: tiles 0 .. STAGES-3 in flight (tiles past the end read
-    // nothing).  q was issued first, so waiting until only those loads remain
-    // guarantees q without waiting for any tile.
+    // Prologue: tiles 0 .. STAGES-3 in flight (tiles past the end read nothing).
 #pragma unroll
     for (int t = 0; t < C::STAGES - 2; ++t) issue_tile(t);
-    __builtin_amdgcn_s_waitcnt(kVmcntStages<C::STAGES - 2, C::PER_WAVE>());
 
     // Software pipeline: step `tile` reads V of `tile` (P.V with the P^T made
     // in the previous step) and K of `tile` + 1 (q.K and its softmax), so the
