@@ -1,4 +1,4 @@
-// Log-sum-exp merge of split-K partials (separate kernel, for many splits).
+// Log-sum-exp merge of split-K partials (separate kernels).
 //
 // A sequence whose positions were cut into n chunks has, per query head, n
 // normalised partial outputs O_s = (sum_{j in s} w_j v_j) / l_s and base-2
@@ -6,7 +6,7 @@
 //     out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M),
 // an exact identity of softmax over a partition of the positions.
 //
-// One workgroup per (row, query head), 256 threads.  Thread t owns a 16-byte
+// Many chunks: one workgroup per (row, query head), 256 threads.  Thread t owns a 16-byte
 // column slot (t mod D/4) and the chunks s = t div (D/4), step 256/(D/4), so
 // several chunks are read in parallel; the per-thread sums are then added in a
 // fixed order through LDS, so the result is bitwise reproducible for a plan.
@@ -68,9 +68,75 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
 }
 
+// Few chunks per sequence (at most kCombineFewMaxSplits): one thread per
+// (query head, 16-byte column slot), 1024/D heads per workgroup.  Each thread
+// issues the loads of every chunk's LSE and slot at once (indices clamped to
+// the sequence's chunks, so every load is in bounds) and merges them in
+// ascending chunk order, so the result is bitwise reproducible for a plan.
+template <int D>
+__global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long long nheads) {
+    constexpr int SLOTS = D / 4;
+    constexpr int HPB = 256 / SLOTS;
+    constexpr int S = kCombineFewMaxSplits;
+    const int tid = threadIdx.x;
+    const long long gh = (long long)blockIdx.x * HPB + tid / SLOTS;  // row * Hq + h
+    if (gh >= nheads) return;
+    const int slot = tid % SLOTS;
+    const int h = (int)(gh % a.Hq);
+    const long long row = gh / a.Hq;
+    int b, len;
+    row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
+    const int nsplit = len > 0 ? (len + a.chunk - 1) / a.chunk : 1;
+    if (nsplit <= 1) return;  // written directly by the split kernel
+
+    const int kvh = h / a.G, g = h % a.G;
+    const size_t first = ((size_t)(row * a.Hkv + kvh) * a.max_splits) * a.G + g;  // split 0
+    const size_t step = (size_t)a.G;  // partials of consecutive splits are G heads apart
+    float l[S];
+    f32x4_t o[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int sc = s < nsplit ? s : nsplit - 1;
+        l[s] = a.part_lse[first + sc * step];
+        o[s] = *reinterpret_cast<const f32x4_t*>(a.part_o + (first + sc * step) * D + 4 * slot);
+    }
+    float M = l[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) M = fmaxf(M, l[s]);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const float wgt = s < nsplit ? __builtin_amdgcn_exp2f(l[s] - M) : 0.f;
+        acc += wgt * o[s];
+        wsum += wgt;
+    }
+    float* dst = a.out + ((size_t)row * a.Hq + h) * D;
+    *reinterpret_cast<f32x4_t*>(dst + 4 * slot) = acc * (1.f / wsum);
+}
+
 hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream) {
     if (p.grid_combine <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a);
+    if (p.max_splits <= kCombineFewMaxSplits) {
+        const long long nheads = p.rows * a.Hq;
+        switch (a.D) {
+            case 64:
+                hipLaunchKernelGGL(combine_few_kernel<64>, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a,
+                                   nheads);
+                break;
+            case 128:
+                hipLaunchKernelGGL(combine_few_kernel<128>, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a,
+                                   nheads);
+                break;
+            case 256:
+                hipLaunchKernelGGL(combine_few_kernel<256>, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a,
+                                   nheads);
+                break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -123,7 +123,12 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         // agent-scope release (an L2 write-back) in every workgroup, which
         // measured 2-3x slower on MI355X.
         p.combine = (o.combine == 0) ? 1 : o.combine;
-        p.grid_combine = (p.combine == 1) ? p.rows * Hq : 0;
+        if (p.combine != 1)
+            p.grid_combine = 0;
+        else if (p.max_splits <= kCombineFewMaxSplits)
+            p.grid_combine = ceil_div(p.rows * Hq, combine_heads_per_block(D));
+        else
+            p.grid_combine = p.rows * Hq;
         if (p.grid_combine > kMaxGrid)
             return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (combine grid limit)");
         const size_t parts = (size_t)p.rows * Hkv * p.max_splits * p.G;

@@ -30,6 +30,12 @@ constexpr int kMfmaMaxHeads = 64;
 constexpr int kValuMaxHeads = 8;
 // Most chunks per unit the fused combine handles (its weights live in LDS).
 constexpr int kFusedMaxSplits = 16;
+// Up to this many chunks per sequence the combine kernel keeps every chunk of
+// a column slot in registers (one thread per (query head, 16-byte slot));
+// beyond it, threads of a workgroup split the chunks of one head.
+constexpr int kCombineFewMaxSplits = 8;
+// Query heads per workgroup of the few-chunk combine (256 threads, D/4 each).
+constexpr int combine_heads_per_block(int D) { return 1024 / D; }
 
 struct Plan {
     int variant = MQA_VARIANT_VALU;  // resolved, never AUTO

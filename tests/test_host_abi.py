@@ -94,7 +94,11 @@ def test_plan_invariants(B, Hq, Hkv, D, Lmax):
     assert p["head_blocks"] * per_block >= G
     assert p["grid_main"] == B * Hkv * p["max_splits"] * p["head_blocks"]
     if p["max_splits"] > 1:
-        assert p["combine"] == 1 and p["grid_combine"] == B * Hq
+        assert p["combine"] == 1
+        if p["max_splits"] <= 8:   # few chunks: one thread per (head, 16-byte slot), 1024/D heads per block
+            assert p["grid_combine"] == -(-B * Hq // (1024 // D))
+        else:                      # many chunks: one workgroup per (row, head)
+            assert p["grid_combine"] == B * Hq
         assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (D + 1) * 4
     else:
         assert p["combine"] == 0 and p["workspace_bytes"] == 0
