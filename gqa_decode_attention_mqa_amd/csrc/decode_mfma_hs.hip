@@ -55,6 +55,7 @@ struct HsCfg {
     static_assert(D >= 64 && D % 64 == 0, "head size");
     static_assert(LOADS % NL == 0, "every loader issues the same number of loads");
     static_assert((STAGES - 2) * PER_WAVE <= 63, "loads in flight fit a wave's counter");
+    static_assert(NG * 16 * (D + 4) * 4 <= LDS_BYTES, "the output transpose fits in the ring");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
     static_assert(LDS_BYTES >= (kFusedMaxSplits + 2) * 16 * NG * 4, "fused-combine weights fit");
 };
@@ -334,24 +335,38 @@ __global__ __launch_bounds__(384) void decode_mfma_hs_kernel(DecodeArgs a) {
     // is released (the ring's tail loads read nothing, so this is quick).
     __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- epilogue: this wave's 16 heads, no merge with other waves
+    // ---- epilogue: this wave's 16 heads, no merge with other waves.  The
+    // accumulators hold four consecutive d of one head per lane; they go
+    // through LDS (the ring is free now) so that every store instruction
+    // writes whole contiguous head rows.  LDS rows are padded by 16 bytes so
+    // the transposing writes hit distinct banks.
     l_run = sum_xor32(sum_xor16(l_run));
     const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
     const bool direct = nsplit == 1;
-    const int g = 16 * w + li;  // head inside the block
-    if (w < NG && g < gcnt) {
-        const int gh = g0 + g;
-        float* dst;
-        if (direct)
-            dst = a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D;
-        else
-            dst = a.part_o + (((size_t)unit * a.max_splits + s) * a.G + gh) * D;
-        // accumulator rows 4kg .. 4kg+3 of tile m are d = 16m + 4kg .. +3
+    constexpr int ROWF = D + 4;  // floats per padded LDS row
+    __syncthreads();             // every wave is done with the ring
+    if (w < NG) {
+        float* ot = reinterpret_cast<float*>(smem) + w * 16 * ROWF;
+        // accumulator rows 4kg .. 4kg+3 of tile m are d = 16m + 4kg .. +3 of head li
 #pragma unroll
         for (int m = 0; m < C::MT; ++m)
-            *reinterpret_cast<f32x4_t*>(dst + 16 * m + 4 * kg) = oacc[m] * inv_l;
-        if (!direct && kg == 0)
-            a.part_lse[((size_t)unit * a.max_splits + s) * a.G + gh] = m_run + __log2f(l_run);
+            *reinterpret_cast<f32x4_t*>(ot + li * ROWF + 16 * m + 4 * kg) = oacc[m] * inv_l;
+        const size_t head0 = (size_t)kvh * a.G + g0 + 16 * w;  // first query head of this wave
+        float* dst = direct ? a.out + ((size_t)row * a.Hq + head0) * D
+                            : a.part_o + (((size_t)unit * a.max_splits + s) * a.G + g0 + 16 * w) * D;
+        constexpr int LPR = D / 4;       // lanes per row, 16 bytes each
+        constexpr int RPI = 64 / LPR;    // rows per store instruction
+        const int hr = lane / LPR, c = lane % LPR;
+#pragma unroll
+        for (int h0 = 0; h0 < 16; h0 += RPI) {
+            const int h = h0 + hr;
+            if (16 * w + h < gcnt)
+                *reinterpret_cast<f32x4_t*>(dst + (size_t)h * D + 4 * c) =
+                    *reinterpret_cast<const f32x4_t*>(ot + h * ROWF + 4 * c);
+        }
+        const int g = 16 * w + li;  // head inside the block
+        if (!direct && kg == 0 && g < gcnt)
+            a.part_lse[((size_t)unit * a.max_splits + s) * a.G + g0 + g] = m_run + __log2f(l_run);
     }
     if (direct || !a.fused) return;
     // ---- fused combine: the last chunk of this (row, kv head, head block) merges all partials
