@@ -37,7 +37,7 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBS = 8000.0
 MALL_DEFEAT_BYTES = 768 * 2 ** 20
 MAX_SETS = 64  # tiny problems live in cache whatever the rotation
-KERNEL_SOURCES = ["decode_mfma.hip", "decode_mfma_hs.hip", "decode_valu.hip", "combine.hip", "kernel_common.hpp",
+KERNEL_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "combine.hip", "kernel_common.hpp",
                   "abi.cpp", "plan.cpp"]
 
 

@@ -137,10 +137,8 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     hipError_t e;
     if (plan.variant == MQA_VARIANT_VALU)
         e = mqa::launch_decode_valu(plan, a, stream, ev0, ev1);
-    else if (plan.heads_per_block > mqa::kMfmaHeadsPerTile)
-        e = mqa::launch_decode_mfma_heads(plan, a, stream, ev0, ev1);  // one wave per 16 heads
     else
-        e = mqa::launch_decode_mfma(plan, a, stream, ev0, ev1);        // waves split the positions
+        e = mqa::launch_decode_mfma(plan, a, stream, ev0, ev1);
     if (e != hipSuccess) return hip_fail(e, "split-K kernel launch");
     if (plan.combine == 1) {
         mqa::CombineArgs c{};

@@ -1,32 +1,29 @@
-// Split-K decode attention on bf16 matrix cores (v_mfma_f32_16x16x32_bf16).
+// Split-K decode attention on bf16 matrix cores, one wave per 16 query heads.
 //
-// For groups of at least 16 query heads per key/value head the two products
-// of a decode step are dense enough for matrix tiles: one workgroup owns
-// (query row, kv head, chunk of positions, block of up to 64 heads) and reads
-// each K/V row of its chunk exactly once for all of its heads.  This is the
-// single-device form of the batch-sharded multiquery layout of "Efficiently
-// Scaling Transformer Inference", section 3.4, "Attention Layer
-// Partitioning": attention for a sequence is computed where its cache lives,
-// and the shared key/value head is never replicated or re-read per query head.
+// For groups of more than four query heads per key/value head (e.g. the
+// 48-head multiquery attention of PaLM 540B in "Efficiently Scaling
+// Transformer Inference", section 3.4, "Attention Layer Partitioning", or the
+// 8-head groups of grouped-query attention) a workgroup owns (query row, kv
+// head, chunk of positions, block of 16*NG heads, NG = 1..4).  Compute wave
+// w < NG owns heads 16w .. 16w+15 for every position of the chunk, so no two
+// waves ever merge softmax state; groups below 16 pad the head tile.  The
+// chunk's K and V rows are read from HBM exactly once per workgroup into an
+// LDS ring of STAGES tiles of 32 positions by two load-only waves, with
+// direct buffer-to-LDS loads (no registers hold data in flight, and
+// STAGES - 2 tiles are in flight at once); every compute wave then reads the
+// whole tile from LDS.
 //
-// Per tile of TILE positions (4 waves, 256 threads):
-//   * S^T = K q^T: each wave takes 16 (or 32) positions as the M dimension;
-//     its K rows load straight from HBM into the A-operand layout (row = lane
-//     mod 16, 8 contiguous d per lane = one 128-bit load); q^T is the B operand,
-//     read from LDS.  The accumulator puts head g = lane mod 16 in every lane
-//     group, so each lane holds 4 positions of one head.
-//   * online softmax in base 2 (log2(e) folded into the logit scale): the tile
-//     maximum per head is combined across waves through LDS, P = exp2(S - m)
-//     is rounded to bf16 and written to LDS transposed ([head][position]).
-//   * O^T += V^T P^T: each wave owns 64 columns of d (and, for D < 256, a slice
-//     of the tile's positions).  V rows are loaded as 8-byte pieces and
-//     transposed in registers with v_perm_b32 into the A operand (row = d,
-//     8 consecutive positions per lane); P^T is the B operand from LDS.  The
-//     accumulator's column is again the head, so the rescale by
-//     exp2(m_old - m_new) happens in-lane.
-// The chunk ends by normalising; a sequence that fits in one chunk writes its
-// output directly, otherwise the chunk writes O/l and its base-2 log-sum-exp
-// for the combine kernel.
+// Per tile, in each compute wave:
+//   * S^T = K q^T on 16x16x32 bf16 tiles: A = two 16-row K tiles (read from
+//     LDS), B = this wave's q^T (registers).  Head g = lane mod 16.
+//   * base-2 online softmax with lazy rescaling; the two S^T accumulators are
+//     exactly the 8 k-slots per lane of the P^T operand of P.V.
+//   * O^T += V^T P^T on 16x16x32 tiles: the V^T operand is read from LDS with
+//     gfx950's transposing LDS reads (ds_read_b64_tr_b16), so no lane shuffles.
+// The loop is software-pipelined by one tile: q.K of the next tile is issued
+// together with P.V of the current one.
+// Rows at or past the end of the chunk are out of the buffer range and arrive
+// as zeros; their logits are masked, so padding is never read.
 #include <atomic>
 #include <type_traits>
 
@@ -37,41 +34,103 @@ namespace mqa {
 
 template <int D, int NG>
 struct MfmaCfg {
-    static constexpr int NW = 4;             // waves per workgroup, each independent in the main loop
-    // 16-row S^T tiles per step: two (P.V on 16x16x32, 8 k-slots) while the
-    // registers allow, one (P.V on 16x16x16, 4 k-slots) for D = 256.
-    static constexpr int MQ = (D >= 256) ? 1 : 2;
-    static constexpr int STEP = 16 * MQ;     // positions a wave takes per step
-    static constexpr int KSL = 4 * MQ;       // k-slots of the P.V tile per lane group
-    static constexpr int KS = D / 32;        // k-steps over d in q.K
-    static constexpr int DPL = D / 16;       // V columns per lane = M tiles of O^T
-    static constexpr int GP = 16 * NG;       // heads per workgroup (padded)
-    static constexpr int QLD = D + 8;        // LDS row pitch of q (bf16)
-    static constexpr int ACC = DPL * NG;     // O^T accumulator tiles per lane (4 floats each)
-    static constexpr int Q_BYTES = GP * QLD * 2;
-    static constexpr int OLD = D + 4;                        // LDS row pitch of an O exchange region (fp32)
-    static constexpr int REGION_BYTES = GP * OLD * 4;        // one wave's O, row-major [head][d]
-    static constexpr int ML_BYTES = 2 * NW * GP * 4;        // running max and row sum per wave
-    static constexpr int BODY_BYTES = (2 * REGION_BYTES > Q_BYTES) ? 2 * REGION_BYTES : Q_BYTES;
-    static constexpr int LDS_BYTES = ML_BYTES + BODY_BYTES;
-    static_assert(D % 64 == 0, "head size");
+    // NG compute waves (one per 16-head tile) and NL load-only waves.  The
+    // loads of a tile all leave right after the ring barrier and queue in the
+    // CU's address unit; a wave stalls until its own are accepted, so they are
+    // kept off the compute waves.  Two loaders keep three tiles in flight
+    // within the 63 loads a wave can have outstanding.
+    static constexpr int NL = 2;
+    static constexpr int NW = NG + NL;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int STEP = 32;                  // positions per tile
+    static constexpr int STAGES = D == 256 ? 5 : 4;  // tiles in the LDS ring (D = 256: all 160 KB)
+    static_assert(STAGES >= 4, "two tiles in use and at least one more in flight");
+    static constexpr int KS = D / 32;                // k-steps over d in q.K
+    static constexpr int MT = D / 16;                // 16-row tiles of O^T
+    static constexpr int CPR = D / 8;                // 16-byte chunks per row
+    static constexpr int TILE_BYTES = STEP * D * 2;  // K (or V) bytes of one tile
+    static constexpr int LOADS = TILE_BYTES / 1024;  // wave-wide 16-byte loads per tile (K or V)
+    static constexpr int KPW = LOADS / NL;           // K loads (and as many V loads) per loader per tile
+    static constexpr int PER_WAVE = 2 * KPW;         // loads a loader issues per tile
+    static constexpr int LDS_BYTES = STAGES * 2 * TILE_BYTES;
+    static_assert(D >= 64 && D % 64 == 0, "head size");
+    static_assert(LOADS % NL == 0, "every loader issues the same number of loads");
+    static_assert((STAGES - 2) * PER_WAVE <= 63, "loads in flight fit a wave's counter");
+    static_assert(NG * 16 * (D + 4) * 4 <= LDS_BYTES, "the output transpose fits in the ring");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
-    static_assert(BODY_BYTES >= (kFusedMaxSplits + 2) * GP * 4, "fused-combine weights fit in the body");
+    static_assert(LDS_BYTES >= (kFusedMaxSplits + 2) * 16 * NG * 4, "fused-combine weights fit");
 };
 
+// LDS layout of a tile: row t (D bf16) is D/8 chunks of 16 bytes, and chunk
+// c of row t sits in slot c ^ swz_key(t).  The key takes all eight values over
+// any eight consecutive rows (the K reads of eight lanes hit eight different
+// 16-byte bank groups), and over rows 4i .. 4i+3 it takes four values that
+// differ above bit 0 (the transposing V reads of a 16-lane group, two
+// adjacent chunks of four rows, hit 128 distinct bytes of banks).
+__device__ __forceinline__ int swz_key(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// LDS byte offset of chunk c of row t inside a tile.
+template <int CPR>
+__device__ __forceinline__ int swz(int t, int c) {
+    return (t * CPR + (c ^ swz_key(t))) * 16;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS byte address of a pointer into this kernel's dynamic LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// gfx950 transposing LDS read of 16-bit elements (ds_read_b64_tr_b16) at
+// LDS byte address addr + OFF.  In each group of 16 lanes, lane i receives
+// element (i mod 4) of the 8-byte rows addressed by lanes 4j + i/4 of its
+// group, j = 0..3 (checked on MI355X).
+//
+// Issued through inline asm: the compiler builtin makes the compiler wait for
+// every buffer-to-LDS load in flight before each such read, which would
+// drain the ring.  The compiler does not know this asm reads LDS, so the
+// caller must wait for it (s_waitcnt lgkmcnt) and tie the results to that
+// wait before using them; any LDS wait the compiler emits for its own reads
+// stays correct, since unknown later LDS reads only make it wait longer.
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read_tr16_b64_asm(uint32_t addr) {
+    u32x2_t r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// The V^T operands of one tile: for 16-row tile m of d, the transposing reads
+// at rows `lo` and `hi` (the lane's two groups of four positions).  Returns
+// once every read has landed, with the results tied to that wait.
+template <int MT>
+__device__ __forceinline__ void read_vt_tile(uint32_t vbase, const int (&alo)[4], const int (&ahi)[4],
+                                             u32x2_t (&lo)[MT], u32x2_t (&hi)[MT]) {
+    static_for<0, MT>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        lo[m] = ds_read_tr16_b64_asm<128 * (m >> 2)>(vbase + alo[m & 3]);
+        hi[m] = ds_read_tr16_b64_asm<128 * (m >> 2)>(vbase + ahi[m & 3]);
+    });
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(lo[m]), "+v"(hi[m]));
+}
+
 template <int D, int NG>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     using C = MfmaCfg<D, NG>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float* m_lds = reinterpret_cast<float*>(smem);           // [NW][GP]
-    float* l_lds = m_lds + C::NW * C::GP;                    // [NW][GP]
-    unsigned char* body = smem + C::ML_BYTES;
-    uint16_t* qs = reinterpret_cast<uint16_t*>(body);        // q, during the main loop
-    float* region0 = reinterpret_cast<float*>(body);         // O^T exchange, after it
-    float* region1 = reinterpret_cast<float*>(body + C::REGION_BYTES);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (wave-uniform)
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, kg = lane >> 4;
 
     long long unit;
@@ -79,325 +138,253 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     map_block(blockIdx.x, a.units, a.max_splits, &unit, &s);
     const int kvh = (int)(unit % a.Hkv);
     const long long row = unit / a.Hkv;
-    const int g0 = blockIdx.y * C::GP;
-    const int gcnt = min(C::GP, a.G - g0);
+    const int g0 = blockIdx.y * 16 * NG;
+    const int gcnt = min(16 * NG, a.G - g0);
 
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
-    // Workgroup-uniform; stated so the compiler keeps them (and the buffer
-    // descriptors built from them) in scalar registers.
     b = __builtin_amdgcn_readfirstlane(b);
     len = __builtin_amdgcn_readfirstlane(len);
     const int p0 = s * a.chunk;
     if (s > 0 && p0 >= len) return;  // whole workgroup: this chunk is past the end
     const int p1 = min(p0 + a.chunk, len);
     const int nsplit = len > 0 ? (len + a.chunk - 1) / a.chunk : 1;
+    const int ntiles = p1 > p0 ? (p1 - p0 + C::STEP - 1) / C::STEP : 0;
 
-    const size_t pos_stride = (size_t)a.Hkv * D;  // elements between consecutive positions
+    const size_t pos_stride = (size_t)a.Hkv * D;
     const int rowbytes = (int)(pos_stride * 2);
-    const uint16_t* kseq = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;  // position 0 of this head
+    const uint16_t* kseq = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
     const uint16_t* vseq = a.v + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
-    const float qk = a.qk_log2;
 
-    // Lane offsets inside a step (loop invariant).  The S^T accumulator of M
-    // tile mq gives lane group kg the positions 16*mq + 4*kg + r, r < 4; these
-    // positions are the k-slots (element e = 4*mq + r) of the P^T operand of
-    // P.V, so V rows are loaded in the same order.
-    constexpr int MQ = C::MQ, KSL = C::KSL;
-    using pv_t = typename std::conditional<MQ == 2, u32x4_t, u32x2_t>::type;
-    const int koff0 = li * rowbytes + kg * 16;                 // + 16*mq*rowbytes, + 64*ks
-    int voff[KSL];
+    // A compute wave's q^T operand (B of q.K): lane (li, kg), k-step ks holds
+    // q[head 16w + li][32 ks + 8 kg .. +8]; heads past the group read as zero.
+    u32x4_t qb[C::KS];
+    if (w >= NG) {
 #pragma unroll
-    for (int e = 0; e < KSL; ++e) voff[e] = (16 * (e / 4) + 4 * kg + (e % 4)) * rowbytes + li * (C::DPL * 2);
+        for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    } else {
+        const uint16_t* qblk = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D;
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(qblk, gcnt * D * 2);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+            qb[ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      qr, (16 * w + li) * D * 2 + ks * 64 + kg * 16, 0, 0));
+        // A compute wave can do nothing before q; waiting here also tells the
+        // compiler that no load is pending into registers the loop reads.
+        __builtin_amdgcn_s_waitcnt(kVmcntStages<0, 0>());
+    }
 
-    // K rows of one step: [mq][ks] -> 16 bytes of row 16*mq + li, d = 32*ks + 8*kg ...
-    u32x4_t kr[MQ][C::KS];
-    // V rows of one step: KSL rows (k-slots) x DPL columns d = DPL*li + c.
-    constexpr int VW = C::DPL / 2;  // dwords of V per row per lane
-    uint32_t vr[KSL][VW];
-
-    auto load_k = [&](int st) {
-        const int rows = max(0, min(C::STEP, p1 - st));
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(kseq + (size_t)st * pos_stride, rows * rowbytes);
+    // Issue a loader's share of the loads of tile `tile` into ring slot
+    // tile % STAGES (compute waves issue nothing).  Load jj (0 .. LOADS-1)
+    // covers 1 KB of the K tile and, with a second load, the same 1 KB of the
+    // V tile; loader l issues jj = l, l + NL, ..., KPW of each.
+    auto issue_tile = [&](int tile) {
+        if (w < NG) return;
+        const int t0 = p0 + tile * C::STEP;
+        const int rows = max(0, min(C::STEP, p1 - t0));
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kseq + (size_t)t0 * pos_stride, rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vseq + (size_t)t0 * pos_stride, rows * rowbytes);
+        unsigned char* slot = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
 #pragma unroll
-        for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) kr[mq][ks] = buffer_load_u32x4(rs, koff0 + 16 * mq * rowbytes + 64 * ks);
-    };
-    auto load_v = [&](int st) {
-        const int rows = max(0, min(C::STEP, p1 - st));
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(vseq + (size_t)st * pos_stride, rows * rowbytes);
-#pragma unroll
-        for (int e = 0; e < KSL; ++e) {
-            if constexpr (VW >= 4) {
-#pragma unroll
-                for (int j = 0; j < VW / 4; ++j) {
-                    const u32x4_t t4 = buffer_load_u32x4(rs, voff[e] + 16 * j);
-                    vr[e][4 * j] = t4.x;
-                    vr[e][4 * j + 1] = t4.y;
-                    vr[e][4 * j + 2] = t4.z;
-                    vr[e][4 * j + 3] = t4.w;
-                }
-            } else {
-                const u32x2_t t2 = buffer_load_u32x2(rs, voff[e]);
-                vr[e][0] = t2.x;
-                vr[e][1] = t2.y;
-            }
+        for (int i = 0; i < C::KPW; ++i) {
+            const int jj = (w - NG) + C::NL * i;
+            const int p = jj * 64 + lane;  // 16-byte LDS slot in the tile
+            const int t = p / C::CPR, cs = p % C::CPR;
+            const int voff = t * rowbytes + ((cs ^ swz_key(t)) * 16);
+            unsigned char* dst = slot + jj * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)dst, 16, voff, 0, 0, kCachePolicyNT);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dst + C::TILE_BYTES), 16, voff, 0, 0,
+                                                     kCachePolicyNT);
         }
     };
-
-    // q is fetched first and the first K/V step right behind it: the q staging
-    // below then waits only for q (loads complete in order), while K/V stream in.
-    constexpr int QV = (C::GP * (D / 8) + 255) / 256;  // 16-byte pieces of q per thread
-    const uint16_t* qrow = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D;
-    u32x4_t qv[QV];
-#pragma unroll
-    for (int i = 0; i < QV; ++i) {
-        const int c = tid + 256 * i;
-        const int g = c / (D / 8), dc = c % (D / 8);
-        qv[i] = u32x4_t{0u, 0u, 0u, 0u};
-        if (c < C::GP * (D / 8) && g < gcnt) qv[i] = load_u32x4(qrow + (size_t)g * D + dc * 8);
-    }
-    int st = p0 + C::STEP * w;
-    load_k(st);
-    load_v(st);
-#pragma unroll
-    for (int i = 0; i < QV; ++i) {
-        const int c = tid + 256 * i;
-        if (c < C::GP * (D / 8))
-            *reinterpret_cast<u32x4_t*>(qs + (c / (D / 8)) * C::QLD + (c % (D / 8)) * 8) = qv[i];
-    }
-    __syncthreads();
-
-    float m_run[NG], l_run[NG];
-    f32x4_t oacc[C::DPL][NG];
-#pragma unroll
-    for (int n = 0; n < NG; ++n) {
-        m_run[n] = -INFINITY;
-        l_run[n] = 0.f;
-#pragma unroll
-        for (int j = 0; j < C::DPL; ++j) oacc[j][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // ---- main loop: this wave's steps st, st + 4*STEP, ...; no cross-wave sync
-    while (st < p1) {
-        // Keeps the q^T reads below inside the loop: hoisted, they would pin
-        // KS * NG * 4 registers for the whole loop (96 for 48 heads of 256).
+    // In a loader, the next tile and everything before it have landed once
+    // at most STAGES - 3 later tiles are outstanding; in every wave no LDS read
+    // is pending.  The barrier then publishes the loaders' tiles and frees the
+    // slot refilled next.  A plain s_barrier, not __syncthreads: the latter's
+    // release fence would also wait for the loads still in flight to the ring.
+    auto ring_sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(kVmcntStages<C::STAGES - 3, C::PER_WAVE>() & ~(0xF << 8));
         asm volatile("" ::: "memory");
-        const int nxt = st + C::NW * C::STEP;
-        // S^T = K q^T
-        f32x4_t sacc[MQ][NG];
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t oacc[C::MT];  // O^T tile m: rows d = 16m .. 16m+15, column = head
 #pragma unroll
-        for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-            for (int n = 0; n < NG; ++n) sacc[mq][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::MT; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float qk = a.qk_log2;
+
+    // S^T = K q^T for one tile: A = two 16-row K tiles read from LDS, B = q^T.
+    // Accumulator lane (li, kg), element r of tile mq: head li, position 16mq + 4kg + r.
+    auto qk_tile = [&](int tile, f32x4_t (&sacc)[2]) {
+        const unsigned char* kt = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
+        sacc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-            for (int n = 0; n < NG; ++n) {
-                const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(qs + (16 * n + li) * C::QLD + ks * 32 + kg * 8);
-#pragma unroll
-                for (int mq = 0; mq < MQ; ++mq) sacc[mq][n] = mfma_16x16x32_bf16(kr[mq][ks], bq, sacc[mq][n]);
+            for (int mq = 0; mq < 2; ++mq) {
+                const int t = 16 * mq + li;
+                const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kt + swz<C::CPR>(t, 4 * ks + kg));
+                sacc[mq] = mfma_16x16x32_bf16(ka, qb[ks], sacc[mq]);
             }
         }
-        load_k(nxt);  // the next step's K streams in under softmax and P.V
-
-        // scale to base-2 units; mask past the end (last step only)
+    };
+    // Scale, mask the tail, lazy online softmax; P^T of the tile in registers.
+    // Returns whether the running maximum moved (then O must be rescaled by alpha).
+    auto softmax_tile = [&](int tile, f32x4_t (&sacc)[2], u32x4_t& pb, float& alpha) {
+        const int st = p0 + tile * C::STEP;
 #pragma unroll
-        for (int mq = 0; mq < MQ; ++mq)
+        for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
-            for (int n = 0; n < NG; ++n)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sacc[mq][n][r] *= qk;
+            for (int r = 0; r < 4; ++r) sacc[mq][r] *= qk;
         if (st + C::STEP > p1) {
 #pragma unroll
-            for (int mq = 0; mq < MQ; ++mq)
+            for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool ok = st + 16 * mq + 4 * kg + r < p1;
-#pragma unroll
-                    for (int n = 0; n < NG; ++n) sacc[mq][n][r] = ok ? sacc[mq][n][r] : -INFINITY;
-                }
+                for (int r = 0; r < 4; ++r)
+                    sacc[mq][r] = (st + 16 * mq + 4 * kg + r < p1) ? sacc[mq][r] : -INFINITY;
         }
-        // online softmax with lazy rescaling; P^T operand built in registers
-        pv_t pb[NG];
-        float alpha[NG];
-        bool any_rescale = false;
+        float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+        mx = max_xor32(max_xor16(mx));
+        const bool moved = mx > m_run + kRescaleSlack;
+        alpha = moved ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+        m_run = moved ? mx : m_run;
+        float lsum = 0.f;
 #pragma unroll
-        for (int n = 0; n < NG; ++n) {
-            float mx = fmaxf(fmaxf(sacc[0][n][0], sacc[0][n][1]), fmaxf(sacc[0][n][2], sacc[0][n][3]));
+        for (int mq = 0; mq < 2; ++mq) {
+            const uint32_t lo = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][0] - m_run),
+                                               __builtin_amdgcn_exp2f(sacc[mq][1] - m_run));
+            const uint32_t hi = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][2] - m_run),
+                                               __builtin_amdgcn_exp2f(sacc[mq][3] - m_run));
+            pb[2 * mq] = lo;
+            pb[2 * mq + 1] = hi;
+            lsum += (bf16_lo_f32(lo) + bf16_hi_f32(lo)) + (bf16_lo_f32(hi) + bf16_hi_f32(hi));
+        }
+        l_run = l_run * alpha + lsum;
+        return __any(moved);
+    };
+    // O^T += V^T P^T for one tile.  The A operand (row d = 16m + li, eight
+    // positions per lane group) comes straight from LDS with transposing
+    // reads: in each 16-lane group, lane 4j + b points at the 8 bytes
+    // d = 16m + 4b .. +3 of position row j, and lane li receives column
+    // 16m + li of the four rows.  Element e of lane group kg is position
+    // 16*(e/4) + 4*kg + e%4, the order of the P^T operand.
+    //   Chunk 2m + x (x = 0, 1) of row t sits at the slot of chunk
+    // 2(m mod 4) + x plus 8 (m div 4), since the swizzle key is below 8, so
+    // four address registers per row and constant offsets cover all m.
+    const int tr_j = li >> 2, tr_b = li & 3;
+    const int tr_tlo = 4 * kg + tr_j, tr_thi = 16 + 4 * kg + tr_j;
+    int tr_lo[4], tr_hi[4];
 #pragma unroll
-            for (int mq = 1; mq < MQ; ++mq)
-                mx = fmaxf(mx, fmaxf(fmaxf(sacc[mq][n][0], sacc[mq][n][1]), fmaxf(sacc[mq][n][2], sacc[mq][n][3])));
-            mx = max_xor32(max_xor16(mx));
-            const bool moved = mx > m_run[n] + kRescaleSlack;
-            alpha[n] = moved ? __builtin_amdgcn_exp2f(m_run[n] - mx) : 1.f;
-            m_run[n] = moved ? mx : m_run[n];
-            any_rescale |= moved;
-            float lsum = 0.f;
+    for (int mm = 0; mm < 4; ++mm) {
+        const int c = 2 * mm + (tr_b >> 1), half = (tr_b & 1) * 8;
+        tr_lo[mm] = swz<C::CPR>(tr_tlo, c) + half;
+        tr_hi[mm] = swz<C::CPR>(tr_thi, c) + half;
+    }
+    auto pv_tile = [&](int tile, const u32x4_t& pb) {
+        const uint32_t vbase = lds_addr(smem + (tile % C::STAGES) * 2 * C::TILE_BYTES + C::TILE_BYTES);
+        u32x2_t lo[C::MT], hi[C::MT];
+        read_vt_tile<C::MT>(vbase, tr_lo, tr_hi, lo, hi);
 #pragma unroll
-            for (int mq = 0; mq < MQ; ++mq) {
-                const uint32_t lo = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][n][0] - m_run[n]),
-                                                   __builtin_amdgcn_exp2f(sacc[mq][n][1] - m_run[n]));
-                const uint32_t hi = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][n][2] - m_run[n]),
-                                                   __builtin_amdgcn_exp2f(sacc[mq][n][3] - m_run[n]));
-                pb[n][2 * mq] = lo;
-                pb[n][2 * mq + 1] = hi;
-                lsum += (bf16_lo_f32(lo) + bf16_hi_f32(lo)) + (bf16_lo_f32(hi) + bf16_hi_f32(hi));
+        for (int m = 0; m < C::MT; ++m) {
+            const u32x4_t va = {lo[m].x, lo[m].y, hi[m].x, hi[m].y};
+            oacc[m] = mfma_16x16x32_bf16(va, pb, oacc[m]);
+        }
+    };
+
+    // Prologue: tiles 0 .. STAGES-3 in flight (tiles past the end read nothing).
+#pragma unroll
+    for (int t = 0; t < C::STAGES - 2; ++t) issue_tile(t);
+
+    // Software pipeline: step `tile` reads V of `tile` (P.V with the P^T made
+    // in the previous step) and K of `tile` + 1 (q.K and its softmax), so the
+    // matrix cores and the vector ALU overlap inside each wave.  Ring slots
+    // in use during a step: `tile` and `tile` + 1; the step refills the slot
+    // of `tile` - 1 with `tile` + STAGES - 1, so STAGES - 2 tiles stay in flight.
+    u32x4_t pb = {0u, 0u, 0u, 0u};
+    if (ntiles > 0) {
+        ring_sync();  // tile 0 landed
+        issue_tile(C::STAGES - 2);
+        if (w < NG) {
+            f32x4_t sacc[2];
+            qk_tile(0, sacc);
+            float alpha;
+            softmax_tile(0, sacc, pb, alpha);  // O is still zero: no rescale
+        }
+    }
+    for (int tile = 0; tile < ntiles; ++tile) {
+        ring_sync();  // tile + 1 landed (a no-op read past the end)
+        issue_tile(tile + C::STAGES - 1);
+        if (w >= NG) continue;  // the load-only wave
+        const bool next = tile + 1 < ntiles;
+        f32x4_t sacc[2];
+        if (next) qk_tile(tile + 1, sacc);
+        pv_tile(tile, pb);
+        if (next) {
+            float alpha;
+            if (softmax_tile(tile + 1, sacc, pb, alpha)) {
+#pragma unroll
+                for (int m = 0; m < C::MT; ++m) oacc[m] = oacc[m] * alpha;
             }
-            l_run[n] = l_run[n] * alpha[n] + lsum;
         }
-        if (__any(any_rescale)) {
-#pragma unroll
-            for (int j = 0; j < C::DPL; ++j)
-#pragma unroll
-                for (int n = 0; n < NG; ++n) oacc[j][n] = oacc[j][n] * alpha[n];
-        }
-        // O^T += V^T P^T: column c of this lane's V rows is M tile c (row li <-> d = DPL*li + c)
-#pragma unroll
-        for (int wd = 0; wd < VW; ++wd) {
-            pv_t va_even, va_odd;
-#pragma unroll
-            for (int m = 0; m < KSL / 2; ++m) {
-                va_even[m] = perm_b32(vr[2 * m + 1][wd], vr[2 * m][wd], kPermLoHalves);
-                va_odd[m] = perm_b32(vr[2 * m + 1][wd], vr[2 * m][wd], kPermHiHalves);
-            }
-#pragma unroll
-            for (int n = 0; n < NG; ++n) {
-                oacc[2 * wd][n] = mfma_pv(va_even, pb[n], oacc[2 * wd][n]);
-                oacc[2 * wd + 1][n] = mfma_pv(va_odd, pb[n], oacc[2 * wd + 1][n]);
-            }
-        }
-        load_v(nxt);
-        st = nxt;
     }
 
-    // ---- merge the four waves' (m, l, O) by log-sum-exp, through LDS
-#pragma unroll
-    for (int n = 0; n < NG; ++n) l_run[n] = sum_xor32(sum_xor16(l_run[n]));  // whole wave, head li
-    if (kg == 0) {
-#pragma unroll
-        for (int n = 0; n < NG; ++n) {
-            m_lds[w * C::GP + 16 * n + li] = m_run[n];
-            l_lds[w * C::GP + 16 * n + li] = l_run[n];
-        }
-    }
-    // Row-major exchange: accumulator (c, n, r) of lane (li, kg) is head
-    // 16*n + li, columns DPL*(4*kg + r) + c, so each (n, r) is DPL consecutive
-    // floats written or read as 16-byte pieces.
-    auto region_ptr = [&](float* reg, int n, int r, int q4) {
-        return reinterpret_cast<f32x4_t*>(reg + (16 * n + li) * C::OLD + C::DPL * (4 * kg + r) + 4 * q4);
-    };
-    auto store_region = [&](float* reg, const float* scale) {
-#pragma unroll
-        for (int n = 0; n < NG; ++n)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int q4 = 0; q4 < C::DPL / 4; ++q4)
-                    *region_ptr(reg, n, r, q4) = f32x4_t{oacc[4 * q4][n][r], oacc[4 * q4 + 1][n][r],
-                                                         oacc[4 * q4 + 2][n][r], oacc[4 * q4 + 3][n][r]} * scale[n];
-    };
-    __syncthreads();  // all waves left the main loop: q is dead, regions may overwrite it
-    if (w >= 2) {
-        float ones[NG];
-#pragma unroll
-        for (int n = 0; n < NG; ++n) ones[n] = 1.f;
-        store_region(w == 2 ? region0 : region1, ones);
-    }
-    __syncthreads();
-    if (w < 2) {
-        // wave w absorbs wave w + 2
-        const float* reg = w == 0 ? region0 : region1;
-        float sa[NG], sb[NG];
-#pragma unroll
-        for (int n = 0; n < NG; ++n) {
-            const float mo = m_lds[(w + 2) * C::GP + 16 * n + li];
-            const float lo = l_lds[(w + 2) * C::GP + 16 * n + li];
-            const float M = fmaxf(m_run[n], mo);
-            sa[n] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[n] - M);
-            sb[n] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - M);
-            l_run[n] = sa[n] * l_run[n] + sb[n] * lo;
-            m_run[n] = M;
-        }
-#pragma unroll
-        for (int n = 0; n < NG; ++n)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int q4 = 0; q4 < C::DPL / 4; ++q4) {
-                    const f32x4_t o = *region_ptr(const_cast<float*>(reg), n, r, q4);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        oacc[4 * q4 + c][n][r] = sa[n] * oacc[4 * q4 + c][n][r] + sb[n] * o[c];
-                }
-        if (kg == 0) {
-#pragma unroll
-            for (int n = 0; n < NG; ++n) {
-                m_lds[w * C::GP + 16 * n + li] = m_run[n];
-                l_lds[w * C::GP + 16 * n + li] = l_run[n];
-            }
-        }
-    }
-    __syncthreads();
-    // Waves 0 and 1 hold the pairs (0,2) and (1,3): each writes its share of
-    // the normalised result, 2^(m_w - M) / L * O_w, to its own region.
-    float lse2[NG], scale[NG];
-    if (w < 2) {
-#pragma unroll
-        for (int n = 0; n < NG; ++n) {
-            const int g = 16 * n + li;
-            const float m0 = m_lds[g], m1 = m_lds[C::GP + g];
-            const float M = fmaxf(m0, m1);
-            const float s0 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
-            const float s1 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-            const float L = s0 * l_lds[g] + s1 * l_lds[C::GP + g];
-            const float inv = L > 0.f ? 1.f / L : 0.f;
-            scale[n] = (w == 0 ? s0 : s1) * inv;
-            lse2[n] = M + __log2f(L);
-        }
-    }
-    __syncthreads();  // m_lds / l_lds have been read; regions 0 and 1 are free
-    if (w < 2) {
-        store_region(w == 0 ? region0 : region1, scale);
-        if (w == 0 && kg == 0) {
-#pragma unroll
-            for (int n = 0; n < NG; ++n) m_lds[16 * n + li] = lse2[n];
-        }
-    }
-    __syncthreads();
+    // No buffer->LDS load of this workgroup may still be landing when its LDS
+    // is released (the ring's tail loads read nothing, so this is quick).
+    __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- store: every thread, contiguous rows (region0 + region1)
+    // ---- epilogue: this wave's 16 heads, no merge with other waves.  The
+    // accumulators hold four consecutive d of one head per lane; they go
+    // through LDS (the ring is free now) so that every store instruction
+    // writes whole contiguous head rows.  LDS rows are padded by 16 bytes so
+    // the transposing writes hit distinct banks.
+    l_run = sum_xor32(sum_xor16(l_run));
+    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
     const bool direct = nsplit == 1;
-    for (int idx = tid; idx < gcnt * (D / 4); idx += 256) {
-        const int g = idx / (D / 4), d = 4 * (idx % (D / 4));
-        const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(region0 + g * C::OLD + d) +
-                           *reinterpret_cast<const f32x4_t*>(region1 + g * C::OLD + d);
-        const int gh = g0 + g;
-        if (direct) {
-            *reinterpret_cast<f32x4_t*>(a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D + d) = o4;
-        } else {
-            const size_t part = ((size_t)unit * a.max_splits + s) * a.G + gh;
-            *reinterpret_cast<f32x4_t*>(a.part_o + part * D + d) = o4;
-            if (d == 0) a.part_lse[part] = m_lds[g];
+    constexpr int ROWF = D + 4;  // floats per padded LDS row
+    __syncthreads();             // every wave is done with the ring
+    if (w < NG) {
+        float* ot = reinterpret_cast<float*>(smem) + w * 16 * ROWF;
+        // accumulator rows 4kg .. 4kg+3 of tile m are d = 16m + 4kg .. +3 of head li
+#pragma unroll
+        for (int m = 0; m < C::MT; ++m)
+            *reinterpret_cast<f32x4_t*>(ot + li * ROWF + 16 * m + 4 * kg) = oacc[m] * inv_l;
+        const size_t head0 = (size_t)kvh * a.G + g0 + 16 * w;  // first query head of this wave
+        float* dst = direct ? a.out + ((size_t)row * a.Hq + head0) * D
+                            : a.part_o + (((size_t)unit * a.max_splits + s) * a.G + g0 + 16 * w) * D;
+        constexpr int LPR = D / 4;       // lanes per row, 16 bytes each
+        constexpr int RPI = 64 / LPR;    // rows per store instruction
+        const int hr = lane / LPR, c = lane % LPR;
+#pragma unroll
+        for (int h0 = 0; h0 < 16; h0 += RPI) {
+            const int h = h0 + hr;
+            if (16 * w + h < gcnt)
+                *reinterpret_cast<f32x4_t*>(dst + (size_t)h * D + 4 * c) =
+                    *reinterpret_cast<const f32x4_t*>(ot + h * ROWF + 4 * c);
         }
+        const int g = 16 * w + li;  // head inside the block
+        if (!direct && kg == 0 && g < gcnt)
+            a.part_lse[((size_t)unit * a.max_splits + s) * a.G + g0 + g] = m_run + __log2f(l_run);
     }
     if (direct || !a.fused) return;
     // ---- fused combine: the last chunk of this (row, kv head, head block) merges all partials
-    int* flag = reinterpret_cast<int*>(m_lds);
-    __syncthreads();  // m_lds is reused as the arrival flag
+    __syncthreads();
+    int* flag = reinterpret_cast<int*>(smem);
     if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, flag)) return;
-    float* wts = reinterpret_cast<float*>(body);
+    float* wts = reinterpret_cast<float*>(smem + 16);
     fused_combine(a, unit, nsplit, g0, gcnt, a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D,
-                  wts, C::GP);
+                  wts, 16 * NG);
 }
 
 template <int D, int NG>
-static hipError_t launch_one(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
-                             hipEvent_t ev1) {
-    constexpr int lds = MfmaCfg<D, NG>::LDS_BYTES;
+static hipError_t launch_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+    using C = MfmaCfg<D, NG>;
+    constexpr int lds = C::LDS_BYTES;
     if (lds > 64 * 1024) {
-        // More than 64 KB of LDS must be opted into, once per device.
         static std::atomic<uint64_t> done_mask{0};
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
@@ -411,27 +398,28 @@ static hipError_t launch_one(const Plan& p, const DecodeArgs& a, hipStream_t str
         }
     }
     const dim3 grid((unsigned)p.grid_main, (unsigned)p.head_blocks);
-    const dim3 block(256);
-    if (ev0 || ev1) {
-        // The dispatch packet itself records the two events, so their interval is
-        // the kernel's execution time (no launch or queueing overhead).
+    const dim3 block(C::THREADS);
+    if (ev0 || ev1)
         hipExtLaunchKernelGGL((decode_mfma_kernel<D, NG>), grid, block, lds, stream, ev0, ev1, 0, a);
-    } else {
+    else
         hipLaunchKernelGGL((decode_mfma_kernel<D, NG>), grid, block, lds, stream, a);
-    }
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_mfma_d(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
-                                hipEvent_t ev1) {
-    // Groups of more than 16 heads go to the one-wave-per-16-heads kernel.
-    if (p.heads_per_block != 16) return hipErrorInvalidValue;
-    return launch_one<D, 1>(p, a, stream, ev0, ev1);
+                              hipEvent_t ev1) {
+    switch (p.heads_per_block / 16) {
+        case 1: return launch_mfma<D, 1>(p, a, stream, ev0, ev1);
+        case 2: return launch_mfma<D, 2>(p, a, stream, ev0, ev1);
+        case 3: return launch_mfma<D, 3>(p, a, stream, ev0, ev1);
+        case 4: return launch_mfma<D, 4>(p, a, stream, ev0, ev1);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_decode_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
-                              hipEvent_t ev1) {
+                                    hipEvent_t ev1) {
     switch (a.D) {
         case 64: return launch_mfma_d<64>(p, a, stream, ev0, ev1);
         case 128: return launch_mfma_d<128>(p, a, stream, ev0, ev1);

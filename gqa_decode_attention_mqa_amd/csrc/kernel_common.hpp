@@ -84,15 +84,6 @@ __device__ __forceinline__ void map_block(long long x, long long units, int max_
     }
 }
 
-// Streaming 128/64-bit loads that bypass cache retention (K/V rows are read
-// exactly once).
-__device__ __forceinline__ u32x4_t load_nt_u32x4(const uint16_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
-__device__ __forceinline__ u32x2_t load_nt_u32x2(const uint16_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-}
-
 // Buffer resources: raw (unstructured) buffers whose range check makes an
 // access at or beyond num_records bytes return zero without touching memory.
 constexpr int kBufferFlags = 0x00020000;   // 32-bit data format, as gfx9 raw buffers expect
@@ -110,9 +101,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 __device__ __forceinline__ u32x4_t buffer_load_u32x4(__amdgpu_buffer_rsrc_t r, int voffset) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, kCachePolicyNT));
-}
-__device__ __forceinline__ u32x2_t buffer_load_u32x2(__amdgpu_buffer_rsrc_t r, int voffset) {
-    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voffset, 0, kCachePolicyNT));
 }
 
 // Reductions across the 16-lane rows of a wave without LDS: v_permlane16_swap
@@ -159,18 +147,6 @@ constexpr int kVmcntStages() {
 // units, so exp2(s - m) <= 2^8 and the accumulators are rescaled rarely.
 constexpr float kRescaleSlack = 8.0f;
 
-// Round-to-nearest-even float -> bf16 bits (inputs here are finite or +0).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(uint32_t lo_bits, uint32_t hi_bits) {
-    return (lo_bits & 0xFFFFu) | (hi_bits << 16);
-}
-
 // DPP lane permutations used inside 16-lane rows.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -182,27 +158,9 @@ constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within each 8-lan
 constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within each 16-lane row
 constexpr int kDppRowRor8 = 0x128;       // lane i <- lane (i+8) mod 16 within the row
 
-__device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
-    return __shfl_xor(x, mask, 64);
-}
-
 __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-// 16x16x16 bf16 tile: 4 k-slots per lane (lane group kg holds k = 4*kg .. 4*kg+3).
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4_t mfma_16x16x16_bf16(const u32x2_t& a, const u32x2_t& b, const f32x4_t& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
-}
-// P.V tile over the k-slots of one step: 8 (two 16-row S^T tiles) or 4 (one).
-__device__ __forceinline__ f32x4_t mfma_pv(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
-    return mfma_16x16x32_bf16(a, b, c);
-}
-__device__ __forceinline__ f32x4_t mfma_pv(const u32x2_t& a, const u32x2_t& b, const f32x4_t& c) {
-    return mfma_16x16x16_bf16(a, b, c);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -277,9 +235,6 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int nsplit, int* 
 
 __device__ __forceinline__ u32x4_t load_u32x4(const uint16_t* p) {
     return *reinterpret_cast<const u32x4_t*>(p);
-}
-__device__ __forceinline__ u32x2_t load_u32x2(const uint16_t* p) {
-    return *reinterpret_cast<const u32x2_t*>(p);
 }
 
 }  // namespace mqa

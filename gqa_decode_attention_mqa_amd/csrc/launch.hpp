@@ -9,13 +9,11 @@
 
 namespace mqa {
 
-// Split-K kernel on matrix cores (any group size; 16 heads per tile).  When
-// ev0/ev1 are non-null the dispatch itself records them around the kernel.
+// Split-K kernel on matrix cores: one wave per 16 query heads, K/V streamed
+// through an LDS ring.  When ev0/ev1 are non-null the dispatch itself records
+// them around the kernel.
 hipError_t launch_decode_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                               hipEvent_t ev1);
-// Split-K kernel on matrix cores with one wave per 16 heads (groups of 32+).
-hipError_t launch_decode_mfma_heads(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
-                                    hipEvent_t ev1);
 // Split-K kernel on the vector ALU (groups of up to 8 heads per workgroup).
 hipError_t launch_decode_valu(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                               hipEvent_t ev1);
