@@ -108,17 +108,22 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// The V^T operands of one tile: for 16-row tile m of d, the transposing reads
-// at rows `lo` and `hi` (the lane's two groups of four positions).  Returns
-// once every read has landed, with the results tied to that wait.
+// Issue the V^T operand reads of one tile: for 16-row tile m of d, the
+// transposing reads at rows `lo` and `hi` (the lane's two groups of four
+// positions).  The results are valid only after wait_vt_tile.
 template <int MT>
-__device__ __forceinline__ void read_vt_tile(uint32_t vbase, const int (&alo)[4], const int (&ahi)[4],
-                                             u32x2_t (&lo)[MT], u32x2_t (&hi)[MT]) {
+__device__ __forceinline__ void issue_vt_tile(uint32_t vbase, const int (&alo)[4], const int (&ahi)[4],
+                                              u32x2_t (&lo)[MT], u32x2_t (&hi)[MT]) {
     static_for<0, MT>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         lo[m] = ds_read_tr16_b64_asm<128 * (m >> 2)>(vbase + alo[m & 3]);
         hi[m] = ds_read_tr16_b64_asm<128 * (m >> 2)>(vbase + ahi[m & 3]);
     });
+}
+// Wait until every LDS read of this wave has landed and tie the V^T operands
+// to that wait, so no use of them can be scheduled before it.
+template <int MT>
+__device__ __forceinline__ void wait_vt_tile(u32x2_t (&lo)[MT], u32x2_t (&hi)[MT]) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(lo[m]), "+v"(hi[m]));
@@ -217,19 +222,26 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
 
     // S^T = K q^T for one tile: A = two 16-row K tiles read from LDS, B = q^T.
     // Accumulator lane (li, kg), element r of tile mq: head li, position 16mq + 4kg + r.
+    // Even and odd k-steps accumulate separately (four independent chains on
+    // the matrix pipe), summed at the end.
     auto qk_tile = [&](int tile, f32x4_t (&sacc)[2]) {
         const unsigned char* kt = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
-        sacc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t part[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int mq = 0; mq < 2; ++mq) part[h][mq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq) {
                 const int t = 16 * mq + li;
                 const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kt + swz<C::CPR>(t, 4 * ks + kg));
-                sacc[mq] = mfma_16x16x32_bf16(ka, qb[ks], sacc[mq]);
+                part[ks & 1][mq] = mfma_16x16x32_bf16(ka, qb[ks], part[ks & 1][mq]);
             }
         }
+        sacc[0] = part[0][0] + part[1][0];
+        sacc[1] = part[0][1] + part[1][1];
     };
     // Scale, mask the tail, lazy online softmax; P^T of the tile in registers.
     // Returns whether the running maximum moved (then O must be rescaled by alpha).
@@ -284,10 +296,12 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         tr_lo[mm] = swz<C::CPR>(tr_tlo, c) + half;
         tr_hi[mm] = swz<C::CPR>(tr_thi, c) + half;
     }
-    auto pv_tile = [&](int tile, const u32x4_t& pb) {
+    auto pv_issue = [&](int tile, u32x2_t (&lo)[C::MT], u32x2_t (&hi)[C::MT]) {
         const uint32_t vbase = lds_addr(smem + (tile % C::STAGES) * 2 * C::TILE_BYTES + C::TILE_BYTES);
-        u32x2_t lo[C::MT], hi[C::MT];
-        read_vt_tile<C::MT>(vbase, tr_lo, tr_hi, lo, hi);
+        issue_vt_tile<C::MT>(vbase, tr_lo, tr_hi, lo, hi);
+    };
+    auto pv_mma = [&](const u32x4_t& pb, u32x2_t (&lo)[C::MT], u32x2_t (&hi)[C::MT]) {
+        wait_vt_tile<C::MT>(lo, hi);
 #pragma unroll
         for (int m = 0; m < C::MT; ++m) {
             const u32x4_t va = {lo[m].x, lo[m].y, hi[m].x, hi[m].y};
@@ -320,9 +334,12 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         issue_tile(tile + C::STAGES - 1);
         if (w >= NG) continue;  // the load-only wave
         const bool next = tile + 1 < ntiles;
+        // V of this tile is read first so it lands while q.K of the next runs
+        u32x2_t vlo[C::MT], vhi[C::MT];
+        pv_issue(tile, vlo, vhi);
         f32x4_t sacc[2];
         if (next) qk_tile(tile + 1, sacc);
-        pv_tile(tile, pb);
+        pv_mma(pb, vlo, vhi);
         if (next) {
             float alpha;
             if (softmax_tile(tile + 1, sacc, pb, alpha)) {
