@@ -112,7 +112,8 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     if (p.max_splits < 1) p.max_splits = 1;
 
     p.grid_main = p.rows * Hkv * p.max_splits;
-    p.block_main = 256;
+    // matrix cores: one compute wave per 16 heads plus two load-only waves
+    p.block_main = p.variant == MQA_VARIANT_MFMA ? 64 * (p.heads_per_block / kMfmaHeadsPerTile + 2) : 256;
     if (p.grid_main > kMaxGrid || p.head_blocks > 65535)
         return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (grid limit)");
 

@@ -93,6 +93,8 @@ def test_plan_invariants(B, Hq, Hkv, D, Lmax):
     per_block = min(G, 64) if p["variant"] == "mfma" else min(G, 8)
     assert p["head_blocks"] * per_block >= G
     assert p["grid_main"] == B * Hkv * p["max_splits"] * p["head_blocks"]
+    # matrix cores: a compute wave per 16 heads and two load-only waves; vector ALU: four waves
+    assert p["block_main"] == (64 * (-(-per_block // 16) + 2) if p["variant"] == "mfma" else 256)
     if p["max_splits"] > 1:
         assert p["combine"] == 1
         if p["max_splits"] <= 8:   # few chunks: one thread per (head, 16-byte slot), 1024/D heads per block
