@@ -117,8 +117,8 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.v = static_cast<const uint16_t*>(v);
     a.seq_lens = seq_lens;
     a.out = out;
-    a.part_o = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_o_offset) : nullptr;
-    a.part_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + plan.part_lse_offset) : nullptr;
+    a.part_o = ws ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + plan.part_o_offset) : nullptr;
+    a.part_ml = ws ? reinterpret_cast<mqa::f32x2_t*>(static_cast<char*>(ws) + plan.part_ml_offset) : nullptr;
     a.counters = counters;
     a.units = plan.rows * Hkv;
     a.fused = plan.combine == 2 ? 1 : 0;
@@ -143,7 +143,7 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     if (plan.combine == 1) {
         mqa::CombineArgs c{};
         c.part_o = a.part_o;
-        c.part_lse = a.part_lse;
+        c.part_ml = a.part_ml;
         c.seq_lens = seq_lens;
         c.out = out;
         c.Hq = Hq;

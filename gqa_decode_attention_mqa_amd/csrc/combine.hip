@@ -1,19 +1,26 @@
 // Log-sum-exp merge of split-K partials (separate kernels).
 //
 // A sequence whose positions were cut into n chunks has, per query head, n
-// normalised partial outputs O_s = (sum_{j in s} w_j v_j) / l_s and base-2
-// log-sum-exps lse_s = m_s + log2(l_s).  With M = max_s lse_s the full result is
+// normalised partial outputs O_s = (sum_{j in s} w_j v_j) / l_s (stored as
+// fp16 scaled by 2^-e_s, see kernel_common.hpp) and base-2 log-sum-exps
+// lse_s = m_s + log2(l_s).  With M = max_s lse_s the full result is
 //     out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M),
 // an exact identity of softmax over a partition of the positions.
 //
-// Many chunks: one workgroup per (row, query head), 256 threads.  Thread t owns a 16-byte
-// column slot (t mod D/4) and the chunks s = t div (D/4), step 256/(D/4), so
+// Many chunks: one workgroup per (row, query head), 256 threads.  Thread t owns
+// a slot of four columns (t mod D/4) and the chunks s = t div (D/4), step 256/(D/4), so
 // several chunks are read in parallel; the per-thread sums are then added in a
 // fixed order through LDS, so the result is bitwise reproducible for a plan.
 #include "kernel_common.hpp"
 #include "launch.hpp"
 
 namespace mqa {
+
+// Stored partial slot -> fp32: four fp16 values scaled back by 2^e.
+__device__ __forceinline__ f32x4_t unpack_partial4(u32x2_t h, int e) {
+    return f32x4_t{__builtin_amdgcn_ldexpf(f16_lo_f32(h.x), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.x), e),
+                   __builtin_amdgcn_ldexpf(f16_lo_f32(h.y), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.y), e)};
+}
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     __shared__ float s_max[4];
@@ -31,13 +38,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
     const int kvh = h / a.G, g = h % a.G;
     const size_t first = ((size_t)(row * a.Hkv + kvh) * a.max_splits) * a.G + g;  // split 0
-    const float* lse = a.part_lse + first;
-    const float* po = a.part_o + first * a.D;
+    const f32x2_t* ml = a.part_ml + first;
+    const uint16_t* po = a.part_o + first * a.D;
     const size_t step = (size_t)a.G;  // partials of consecutive splits are G heads apart
 
     // M = max over chunks (threads stride over the chunks, then a block max)
     float m = -INFINITY;
-    for (int s = tid; s < nsplit; s += 256) m = fmaxf(m, lse[s * step]);
+    for (int s = tid; s < nsplit; s += 256) m = fmaxf(m, ml[s * step].x);
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     if ((tid & 63) == 0) s_max[tid >> 6] = m;
     __syncthreads();
@@ -50,9 +57,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     float wsum = 0.f;
 #pragma unroll 4
     for (int s = sl; s < nsplit; s += lanes_per_slot) {
-        const float wgt = __builtin_amdgcn_exp2f(lse[s * step] - M);
-        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(po + s * step * a.D + 4 * slot);
-        acc += wgt * o;
+        const f32x2_t mle = ml[s * step];
+        const float wgt = __builtin_amdgcn_exp2f(mle.x - M);
+        const u32x2_t hv = *reinterpret_cast<const u32x2_t*>(po + s * step * a.D + 4 * slot);
+        acc += wgt * unpack_partial4(hv, (int)mle.y);
         wsum += wgt;
     }
     s_acc[tid] = acc;
@@ -69,13 +77,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 // Few chunks per sequence (at most kCombineFewMaxSplits): one thread per
-// (query head, 16-byte column slot), 1024/D heads per workgroup.  Each thread
-// issues the loads of every chunk's LSE and slot at once (indices clamped to
-// the sequence's chunks, so every load is in bounds) and merges them in
-// ascending chunk order, so the result is bitwise reproducible for a plan.
+// (query head, 8-value column slot), 2048/D heads per workgroup.  Each thread
+// issues the loads of every chunk's {lse, e} and slot at once (indices
+// clamped to the sequence's chunks, so every load is in bounds) and merges
+// them in ascending chunk order, so the result is bitwise reproducible for a
+// plan.
 template <int D>
 __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long long nheads) {
-    constexpr int SLOTS = D / 4;
+    constexpr int SLOTS = D / 8;
     constexpr int HPB = 256 / SLOTS;
     constexpr int S = kCombineFewMaxSplits;
     const int tid = threadIdx.x;
@@ -92,27 +101,31 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
     const int kvh = h / a.G, g = h % a.G;
     const size_t first = ((size_t)(row * a.Hkv + kvh) * a.max_splits) * a.G + g;  // split 0
     const size_t step = (size_t)a.G;  // partials of consecutive splits are G heads apart
-    float l[S];
-    f32x4_t o[S];
+    f32x2_t ml[S];
+    u32x4_t o[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int sc = s < nsplit ? s : nsplit - 1;
-        l[s] = a.part_lse[first + sc * step];
-        o[s] = *reinterpret_cast<const f32x4_t*>(a.part_o + (first + sc * step) * D + 4 * slot);
+        ml[s] = a.part_ml[first + sc * step];
+        o[s] = *reinterpret_cast<const u32x4_t*>(a.part_o + (first + sc * step) * D + 8 * slot);
     }
-    float M = l[0];
+    float M = ml[0].x;
 #pragma unroll
-    for (int s = 1; s < S; ++s) M = fmaxf(M, l[s]);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 1; s < S; ++s) M = fmaxf(M, ml[s].x);
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        const float wgt = s < nsplit ? __builtin_amdgcn_exp2f(l[s] - M) : 0.f;
-        acc += wgt * o[s];
+        const float wgt = s < nsplit ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
+        const int e = (int)ml[s].y;
+        acc0 += wgt * unpack_partial4(u32x2_t{o[s].x, o[s].y}, e);
+        acc1 += wgt * unpack_partial4(u32x2_t{o[s].z, o[s].w}, e);
         wsum += wgt;
     }
-    float* dst = a.out + ((size_t)row * a.Hq + h) * D;
-    *reinterpret_cast<f32x4_t*>(dst + 4 * slot) = acc * (1.f / wsum);
+    float* dst = a.out + ((size_t)row * a.Hq + h) * D + 8 * slot;
+    const float inv = 1.f / wsum;
+    *reinterpret_cast<f32x4_t*>(dst) = acc0 * inv;
+    *reinterpret_cast<f32x4_t*>(dst + 4) = acc1 * inv;
 }
 
 hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream) {

@@ -58,7 +58,7 @@ struct MfmaCfg {
     static_assert((STAGES - 2) * PER_WAVE <= 63, "loads in flight fit a wave's counter");
     static_assert(NG * 16 * (D + 4) * 4 <= LDS_BYTES, "the output transpose fits in the ring");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
-    static_assert(LDS_BYTES >= (kFusedMaxSplits + 2) * 16 * NG * 4, "fused-combine weights fit");
+    static_assert(LDS_BYTES >= (2 * kFusedMaxSplits + 2) * 16 * NG * 4 + 16, "fused-combine scratch fits");
 };
 
 // LDS layout of a tile: row t (D bf16) is D/8 chunks of 16 bytes, and chunk
@@ -357,34 +357,63 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     // accumulators hold four consecutive d of one head per lane; they go
     // through LDS (the ring is free now) so that every store instruction
     // writes whole contiguous head rows.  LDS rows are padded by 16 bytes so
-    // the transposing writes hit distinct banks.
+    // the transposing writes spread over the banks.  A sequence that fits in
+    // one chunk writes fp32 output; a chunk of a longer one writes its fp16
+    // partial row scaled by 2^-e, and {lse, e}.
     l_run = sum_xor32(sum_xor16(l_run));
     const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
     const bool direct = nsplit == 1;
-    constexpr int ROWF = D + 4;  // floats per padded LDS row
-    __syncthreads();             // every wave is done with the ring
+    __syncthreads();  // every wave is done with the ring
     if (w < NG) {
-        float* ot = reinterpret_cast<float*>(smem) + w * 16 * ROWF;
-        // accumulator rows 4kg .. 4kg+3 of tile m are d = 16m + 4kg .. +3 of head li
-#pragma unroll
-        for (int m = 0; m < C::MT; ++m)
-            *reinterpret_cast<f32x4_t*>(ot + li * ROWF + 16 * m + 4 * kg) = oacc[m] * inv_l;
-        const size_t head0 = (size_t)kvh * a.G + g0 + 16 * w;  // first query head of this wave
-        float* dst = direct ? a.out + ((size_t)row * a.Hq + head0) * D
-                            : a.part_o + (((size_t)unit * a.max_splits + s) * a.G + g0 + 16 * w) * D;
-        constexpr int LPR = D / 4;       // lanes per row, 16 bytes each
-        constexpr int RPI = 64 / LPR;    // rows per store instruction
-        const int hr = lane / LPR, c = lane % LPR;
-#pragma unroll
-        for (int h0 = 0; h0 < 16; h0 += RPI) {
-            const int h = h0 + hr;
-            if (16 * w + h < gcnt)
-                *reinterpret_cast<f32x4_t*>(dst + (size_t)h * D + 4 * c) =
-                    *reinterpret_cast<const f32x4_t*>(ot + h * ROWF + 4 * c);
-        }
         const int g = 16 * w + li;  // head inside the block
-        if (!direct && kg == 0 && g < gcnt)
-            a.part_lse[((size_t)unit * a.max_splits + s) * a.G + g0 + g] = m_run + __log2f(l_run);
+        if (direct) {
+            constexpr int ROWF = D + 4;  // floats per padded LDS row
+            float* ot = reinterpret_cast<float*>(smem) + w * 16 * ROWF;
+            // accumulator rows 4kg .. 4kg+3 of tile m are d = 16m + 4kg .. +3 of head li
+#pragma unroll
+            for (int m = 0; m < C::MT; ++m)
+                *reinterpret_cast<f32x4_t*>(ot + li * ROWF + 16 * m + 4 * kg) = oacc[m] * inv_l;
+            float* dst = a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0 + 16 * w) * D;
+            constexpr int LPR = D / 4;     // lanes per row, 16 bytes each
+            constexpr int RPI = 64 / LPR;  // rows per store instruction
+            const int hr = lane / LPR, c = lane % LPR;
+#pragma unroll
+            for (int h0 = 0; h0 < 16; h0 += RPI) {
+                const int h = h0 + hr;
+                if (16 * w + h < gcnt)
+                    *reinterpret_cast<f32x4_t*>(dst + (size_t)h * D + 4 * c) =
+                        *reinterpret_cast<const f32x4_t*>(ot + h * ROWF + 4 * c);
+            }
+        } else {
+            float mx = 0.f;
+#pragma unroll
+            for (int m = 0; m < C::MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(oacc[m][r]));
+            const int e = scale_exponent(max_xor32(max_xor16(mx)) * inv_l);
+            constexpr int ROWH = D + 8;  // halves per padded LDS row
+            uint16_t* ot = reinterpret_cast<uint16_t*>(smem) + w * 16 * ROWH;
+#pragma unroll
+            for (int m = 0; m < C::MT; ++m) {
+                const f32x4_t x = oacc[m] * inv_l;
+                const u32x2_t pk = {pack2_f16_rne(__builtin_amdgcn_ldexpf(x[0], -e), __builtin_amdgcn_ldexpf(x[1], -e)),
+                                    pack2_f16_rne(__builtin_amdgcn_ldexpf(x[2], -e), __builtin_amdgcn_ldexpf(x[3], -e))};
+                *reinterpret_cast<u32x2_t*>(ot + li * ROWH + 16 * m + 4 * kg) = pk;
+            }
+            const size_t part0 = ((size_t)unit * a.max_splits + s) * a.G + g0 + 16 * w;  // this wave's first head
+            uint16_t* dst = a.part_o + part0 * D;
+            constexpr int LPR = D / 8;     // lanes per row, 16 bytes (8 halves) each
+            constexpr int RPI = 64 / LPR;  // rows per store instruction
+            const int hr = lane / LPR, c = lane % LPR;
+#pragma unroll
+            for (int h0 = 0; h0 < 16; h0 += RPI) {
+                const int h = h0 + hr;
+                if (16 * w + h < gcnt)
+                    *reinterpret_cast<u32x4_t*>(dst + (size_t)h * D + 8 * c) =
+                        *reinterpret_cast<const u32x4_t*>(ot + h * ROWH + 8 * c);
+            }
+            if (kg == 0 && g < gcnt) a.part_ml[part0 + li] = f32x2_t{m_run + __log2f(l_run), (float)e};
+        }
     }
     if (direct || !a.fused) return;
     // ---- fused combine: the last chunk of this (row, kv head, head block) merges all partials

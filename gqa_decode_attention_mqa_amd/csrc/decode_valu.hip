@@ -56,7 +56,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     __shared__ float mrg_l[NW][GB];
     __shared__ __attribute__((aligned(16))) float mrg_o[NW][GB][D];
     __shared__ int s_flag;
-    static_assert(NW * D >= kFusedMaxSplits + 2, "fused-combine weights fit in mrg_o");
+    __shared__ unsigned s_amax[GB];  // per head: largest |output| (fp32 bits) of a partial row
+    static_assert(NW * D >= 2 * kFusedMaxSplits + 2, "fused-combine scratch fits in mrg_o");
+    static_assert(D % 64 == 0, "a wave of the merge covers one head row");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (wave-uniform)
@@ -209,32 +211,67 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             }
         }
     }
+    if (tid < GB) s_amax[tid] = 0u;
     __syncthreads();
 
-    // Log-sum-exp merge of the four waves, then normalise and store.
+    // Log-sum-exp merge of the four waves, then normalise and store.  Thread
+    // t merges values idx = t + 256k (head idx / D, column idx % D), so every
+    // wave's 64 values belong to one head.  A chunk of a split sequence stores
+    // its fp16 partial row scaled by 2^-e (e from the row's largest value).
     const bool direct = nsplit == 1;
-    for (int idx = tid; idx < gcnt * D; idx += 256) {
-        const int gg = idx / D, d = idx % D;
-        float M = mrg_m[0][gg];
+    constexpr int VPT = (GB * D + 255) / 256;  // merged values per thread
+    float val[VPT];
+    float lse[VPT];
 #pragma unroll
-        for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, mrg_m[ww][gg]);
-        float O = 0.f, L = 0.f;
-        if (M != -INFINITY) {
+    for (int k = 0; k < VPT; ++k) {
+        const int idx = tid + 256 * k;
+        val[k] = 0.f;
+        lse[k] = -INFINITY;
+        if (idx < gcnt * D) {
+            const int gg = idx / D, d = idx % D;
+            float M = mrg_m[0][gg];
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float sw = __builtin_amdgcn_exp2f(mrg_m[ww][gg] - M);
-                O += sw * mrg_o[ww][gg][d];
-                L += sw * mrg_l[ww][gg];
+            for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, mrg_m[ww][gg]);
+            float O = 0.f, L = 0.f;
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    const float sw = __builtin_amdgcn_exp2f(mrg_m[ww][gg] - M);
+                    O += sw * mrg_o[ww][gg][d];
+                    L += sw * mrg_l[ww][gg];
+                }
+            }
+            val[k] = L > 0.f ? O / L : 0.f;
+            lse[k] = M + __log2f(L);
+        }
+    }
+    if (direct) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int idx = tid + 256 * k;
+            if (idx < gcnt * D) {
+                const int gh = g0 + idx / D;
+                a.out[((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D + idx % D] = val[k];
             }
         }
-        const int gh = g0 + gg;
-        const float val = L > 0.f ? O / L : 0.f;
-        if (direct) {
-            a.out[((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D + d] = val;
-        } else {
-            const size_t part = ((size_t)unit * a.max_splits + s) * a.G + gh;
-            a.part_o[part * D + d] = val;
-            if (d == 0) a.part_lse[part] = M + __log2f(L);
+    } else {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int idx = tid + 256 * k;
+            const float mx = wave_max(fabsf(val[k]));
+            if (lane == 0 && idx < gcnt * D) atomicMax(&s_amax[idx / D], __float_as_uint(mx));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int idx = tid + 256 * k;
+            if (idx < gcnt * D) {
+                const int gg = idx / D, d = idx % D;
+                const int e = scale_exponent(__uint_as_float(s_amax[gg]));
+                const size_t part = ((size_t)unit * a.max_splits + s) * a.G + g0 + gg;
+                a.part_o[part * D + d] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(val[k], -e));
+                if (d == 0) a.part_ml[part] = f32x2_t{lse[k], (float)e};
+            }
         }
     }
     if (direct || !a.fused) return;

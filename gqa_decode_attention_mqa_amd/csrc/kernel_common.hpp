@@ -13,6 +13,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 
 // Arguments of the split-K decode kernels, passed by value.
 //
@@ -27,8 +28,8 @@ struct DecodeArgs {
     const uint16_t* v;         // bf16 [B, Lmax, Hkv, D]
     const int32_t* seq_lens;   // [B]
     float* out;                // fp32 [rows, Hq, D]
-    float* part_o;             // fp32 [rows * Hkv * max_splits, G, D], O / l per chunk
-    float* part_lse;           // fp32 [rows * Hkv * max_splits, G], m + log2(l) (base 2)
+    uint16_t* part_o;          // fp16 [rows * Hkv * max_splits, G, D]: O / l / 2^e per chunk
+    f32x2_t* part_ml;          // [rows * Hkv * max_splits, G]: {m + log2(l) (base 2), e}
     uint32_t* counters;        // [rows * Hkv * head_blocks] arrival counters (fused combine);
                                // zero between calls: the last arriving chunk resets its counter
     long long units;           // rows * Hkv
@@ -40,8 +41,8 @@ struct DecodeArgs {
 };
 
 struct CombineArgs {
-    const float* part_o;
-    const float* part_lse;
+    const uint16_t* part_o;
+    const f32x2_t* part_ml;
     const int32_t* seq_lens;
     float* out;
     int Hq, Hkv, D, Lmax, G;
@@ -147,6 +148,25 @@ constexpr int kVmcntStages() {
 // units, so exp2(s - m) <= 2^8 and the accumulators are rescaled rarely.
 constexpr float kRescaleSlack = 8.0f;
 
+// Partial outputs of split chunks are stored as fp16, each (chunk, head) row
+// divided by 2^e, the smallest power of two above its largest magnitude, so
+// every stored value lies in (-1, 1): the fp16 range can never overflow and
+// the rounding is at most 2^-11 of the row's largest value.  e travels with
+// the chunk's log-sum-exp; the combine restores values with an exact ldexp.
+__device__ __forceinline__ int scale_exponent(float max_abs) {
+    return max_abs > 0.f ? __builtin_amdgcn_frexp_expf(max_abs) : 0;
+}
+__device__ __forceinline__ uint32_t pack2_f16_rne(float a, float b) {
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ float f16_lo_f32(uint32_t pair) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi_f32(uint32_t pair) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
+}
+
 // DPP lane permutations used inside 16-lane rows.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -157,6 +177,15 @@ constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within each 8-lane half row
 constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within each 16-lane row
 constexpr int kDppRowRor8 = 0x128;       // lane i <- lane (i+8) mod 16 within the row
+
+// Maximum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+    x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+    return max_xor32(max_xor16(x));
+}
 
 __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -178,7 +207,7 @@ constexpr uint32_t kPermHiHalves = 0x07060302u;  // (lo.hi16) | (hi.hi16 << 16)
 // Fused log-sum-exp combine, run by the last chunk of a unit to arrive.  The
 // caller has already written its own partial.  Returns after every thread of
 // the workgroup has finished (it contains barriers: call it from all threads).
-//   wts: LDS scratch of kFusedMaxSplits * gp + 2 * gp floats, gp >= gcnt.
+//   wts: LDS scratch of 2 * kFusedMaxSplits * gp + 2 * gp floats, gp >= gcnt.
 __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long unit, int nsplit,
                                               int g0, int gcnt, float* out_row, float* wts, int gp) {
     const int tid = threadIdx.x;
@@ -186,13 +215,16 @@ __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long uni
     float* Mg = wts + kFusedMaxSplits * gp;
     float* Wg = Mg + gp;
     const size_t base = (size_t)unit * a.max_splits * a.G;  // partial (unit, split 0, head 0)
+    int* ex = reinterpret_cast<int*>(Wg + gp);  // kFusedMaxSplits * gp scale exponents
     if (tid < gcnt) {
         float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_lse[base + (size_t)s * a.G + g0 + tid]);
+        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_ml[base + (size_t)s * a.G + g0 + tid].x);
         float W = 0.f;
         for (int s = 0; s < nsplit; ++s) {
-            const float w = __builtin_amdgcn_exp2f(a.part_lse[base + (size_t)s * a.G + g0 + tid] - M);
+            const f32x2_t ml = a.part_ml[base + (size_t)s * a.G + g0 + tid];
+            const float w = __builtin_amdgcn_exp2f(ml.x - M);
             wts[s * gp + tid] = w;
+            ex[s * gp + tid] = (int)ml.y;
             W += w;
         }
         Mg[tid] = M;
@@ -205,8 +237,10 @@ __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long uni
         const int g = idx / (D / 4), d4 = idx % (D / 4);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < nsplit; ++s) {
-            const f32x4_t o = *reinterpret_cast<const f32x4_t*>(
-                a.part_o + (base + (size_t)s * a.G + g0 + g) * D + 4 * d4);
+            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(a.part_o + (base + (size_t)s * a.G + g0 + g) * D + 4 * d4);
+            const int e = ex[s * gp + g];
+            const f32x4_t o = {__builtin_amdgcn_ldexpf(f16_lo_f32(h.x), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.x), e),
+                               __builtin_amdgcn_ldexpf(f16_lo_f32(h.y), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.y), e)};
             acc += wts[s * gp + g] * o;
         }
         *reinterpret_cast<f32x4_t*>(out_row + (size_t)g * D + 4 * d4) = acc * Wg[g];

@@ -133,9 +133,9 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         if (p.grid_combine > kMaxGrid)
             return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (combine grid limit)");
         const size_t parts = (size_t)p.rows * Hkv * p.max_splits * p.G;
-        p.part_o_offset = 0;
-        p.part_lse_offset = round_up((long long)(parts * D * sizeof(float)), 256);
-        p.workspace_bytes = p.part_lse_offset + round_up((long long)(parts * sizeof(float)), 256);
+        p.part_o_offset = 0;  // fp16 partial rows, then {lse, e} pairs
+        p.part_ml_offset = round_up((long long)(parts * D * sizeof(uint16_t)), 256);
+        p.workspace_bytes = p.part_ml_offset + round_up((long long)(parts * 2 * sizeof(float)), 256);
         p.counters = (p.combine == 2) ? (size_t)p.rows * Hkv * p.head_blocks : 0;
     }
     *plan = p;

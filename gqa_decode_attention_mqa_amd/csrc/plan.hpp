@@ -34,8 +34,8 @@ constexpr int kFusedMaxSplits = 16;
 // a column slot in registers (one thread per (query head, 16-byte slot));
 // beyond it, threads of a workgroup split the chunks of one head.
 constexpr int kCombineFewMaxSplits = 8;
-// Query heads per workgroup of the few-chunk combine (256 threads, D/4 each).
-constexpr int combine_heads_per_block(int D) { return 1024 / D; }
+// Query heads per workgroup of the few-chunk combine (256 threads, D/8 each).
+constexpr int combine_heads_per_block(int D) { return 2048 / D; }
 
 struct Plan {
     int variant = MQA_VARIANT_VALU;  // resolved, never AUTO
@@ -51,7 +51,7 @@ struct Plan {
     long long grid_combine = 0;
     size_t workspace_bytes = 0;      // partial outputs + partial LSEs
     size_t part_o_offset = 0;        // byte offsets inside the workspace
-    size_t part_lse_offset = 0;
+    size_t part_ml_offset = 0;
     size_t counters = 0;             // arrival counters (uint32, one per (row, kv head, head
                                      // block)), kept in a buffer of their own that is zero
                                      // between calls

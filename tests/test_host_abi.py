@@ -97,11 +97,12 @@ def test_plan_invariants(B, Hq, Hkv, D, Lmax):
     assert p["block_main"] == (64 * (-(-per_block // 16) + 2) if p["variant"] == "mfma" else 256)
     if p["max_splits"] > 1:
         assert p["combine"] == 1
-        if p["max_splits"] <= 8:   # few chunks: one thread per (head, 16-byte slot), 1024/D heads per block
-            assert p["grid_combine"] == -(-B * Hq // (1024 // D))
+        if p["max_splits"] <= 8:   # few chunks: one thread per (head, 8 columns), 2048/D heads per block
+            assert p["grid_combine"] == -(-B * Hq // (2048 // D))
         else:                      # many chunks: one workgroup per (row, head)
             assert p["grid_combine"] == B * Hq
-        assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (D + 1) * 4
+        # fp16 partial rows plus an {lse, exponent} float pair per (chunk, head)
+        assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (2 * D + 8)
     else:
         assert p["combine"] == 0 and p["workspace_bytes"] == 0
 
