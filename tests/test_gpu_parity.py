@@ -103,6 +103,26 @@ def test_many_chunks_and_shape_changes_reuse_the_workspace(combine):
             run_case(w, variant=variant, chunk=128, combine=combine)
 
 
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("vscale", [2.0 ** 20, 2.0 ** -20])
+def test_split_partials_keep_range_and_precision(variant, vscale):
+    """Split chunks store fp16 partials scaled per (chunk, head); V far outside the fp16 range
+    (and far below it) must come back exact up to that rounding.  Attention is linear in V, so
+    the output is compared after dividing by the (power-of-two, hence exact) scale."""
+    w = Workload("range", B=3, Hq=8, Hkv=2, D=128, Lmax=900, seed=84, len_lo=300, len_hi=900)
+    inp = to_dev(make_inputs(w))
+    inp["v"] = (inp["v"].float() * vscale).to(torch.bfloat16)
+    ref = oracle.decode(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
+    for combine in ("separate", "fused"):
+        print("case range", variant, vscale, combine, flush=True)
+        out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], variant=variant,
+                             chunk=128, combine=combine)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        err = check_close(out.double() / vscale, ref / vscale, "range %s %g %s" % (variant, vscale, combine))
+        assert err <= 2e-3 * float(np.abs(ref / vscale).max()) + 1e-3
+
+
 def test_lengths_outside_the_cache_are_clamped():
     w = Workload("clamp", B=3, Hq=8, Hkv=1, D=64, Lmax=200, seed=78)
     inp = to_dev(make_inputs(w, seq_lens=[-5, 200, 200]))
