@@ -114,19 +114,27 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     }
 
     const int nblk = p1 > p0 ? (p1 - p0 + WB - 1) / WB : 0;
-    for (int blk = w; blk < nblk; blk += NW) {
-        const int t0 = p0 + blk * WB;
-        // Buffer range ends at the last valid row: rows past it read as zero
-        // without a memory access, and their logits are masked below.
-        const int rows = min(WB, p1 - t0);
+    // Issue the loads of block `blk` (of this wave's blocks w, w + NW, ...).
+    // The buffer range ends at the last valid row: rows past it, and whole
+    // blocks past the chunk, read as zero without a memory access.
+    auto load_block = [&](int blk, u32x4_t (&kr)[NB], u32x4_t (&vr)[NB]) {
+        const int t0 = __builtin_amdgcn_readfirstlane(p0 + blk * WB);
+        // rows = clamp(p1 - t0, 0, WB) on the scalar unit: the compiler's
+        // vector clamp (v_med3) lands in a register of a load still in
+        // flight and forces a wait on it.
+        int rows;
+        asm("s_sub_i32 %0, %1, %2\n\ts_max_i32 %0, %0, 0\n\ts_min_i32 %0, %0, %3"
+            : "=s"(rows) : "s"(p1), "s"(t0), "i"(WB));
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kseq + (size_t)t0 * pos_stride, rows * rowbytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vseq + (size_t)t0 * pos_stride, rows * rowbytes);
-        u32x4_t kr[NB], vr[NB];
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
             kr[st] = buffer_load_u32x4(krs, off[st]);
             vr[st] = buffer_load_u32x4(vrs, off[st]);
         }
+    };
+    auto compute_block = [&](int blk, const u32x4_t (&kr)[NB], const u32x4_t (&vr)[NB]) {
+        const int rows = min(WB, p1 - (p0 + blk * WB));
         // logits (base-2 units), masked past the end
         const bool tail = rows < WB;
         float sc[NB][GB];
@@ -186,6 +194,17 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                 }
             }
         }
+    };
+    // Double-buffered: the loads of a wave's next block are in flight while
+    // it computes the current one (two register sets, alternating).
+    u32x4_t ka[NB], va[NB], kb[NB], vb[NB];
+    if (w < nblk) load_block(w, ka, va);
+    for (int blk = w; blk < nblk; blk += 2 * NW) {
+        load_block(blk + NW, kb, vb);
+        compute_block(blk, ka, va);
+        if (blk + NW >= nblk) break;
+        load_block(blk + 2 * NW, ka, va);
+        compute_block(blk + NW, kb, vb);
     }
 
     // Sum the rows of the wave (same softmax state in every row).
