@@ -118,13 +118,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     // The buffer range ends at the last valid row: rows past it, and whole
     // blocks past the chunk, read as zero without a memory access.
     auto load_block = [&](int blk, u32x4_t (&kr)[NB], u32x4_t (&vr)[NB]) {
-        const int t0 = __builtin_amdgcn_readfirstlane(p0 + blk * WB);
-        // rows = clamp(p1 - t0, 0, WB) on the scalar unit: the compiler's
-        // vector clamp (v_med3) lands in a register of a load still in
-        // flight and forces a wait on it.
-        int rows;
-        asm("s_sub_i32 %0, %1, %2\n\ts_max_i32 %0, %0, 0\n\ts_min_i32 %0, %0, %3"
-            : "=s"(rows) : "s"(p1), "s"(t0), "i"(WB));
+        const int t0 = p0 + blk * WB;
+        const int rows = max(0, min(WB, p1 - t0));
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kseq + (size_t)t0 * pos_stride, rows * rowbytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vseq + (size_t)t0 * pos_stride, rows * rowbytes);
 #pragma unroll

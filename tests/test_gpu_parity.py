@@ -68,7 +68,7 @@ def test_tiny_workload_full():
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
 @pytest.mark.parametrize("D", [64, 128, 256])
-@pytest.mark.parametrize("G,Hkv,B", [(1, 2, 3), (3, 1, 3), (4, 2, 4), (8, 1, 3), (16, 1, 8), (48, 1, 3),
+@pytest.mark.parametrize("G,Hkv,B", [(1, 2, 3), (2, 3, 5), (3, 1, 3), (4, 2, 4), (8, 1, 3), (16, 1, 8), (48, 1, 3),
                                      (20, 2, 3), (64, 1, 3), (80, 1, 3)])
 def test_small_shapes(variant, D, G, Hkv, B):
     seed = 1000 + D + 7 * G + Hkv + (0 if variant == "mfma" else 1)
@@ -79,6 +79,28 @@ def test_small_shapes(variant, D, G, Hkv, B):
     run_case(w, variant=variant)
     run_case(w, variant=variant, chunk=128)
     run_case(w, variant=variant, chunk=128, combine="fused")
+
+
+def _random_shapes(n, seed):
+    """Seeded random decode shapes: B <= 8, G in {1, 2, 4, 8, 16, 48}, D in {64, 128, 256}, lengths 0..3000."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4, 8, 16, 48]))
+        Hkv = int(rng.choice([1, 2, 4])) if G <= 16 else 1
+        D = int(rng.choice([64, 128, 256]))
+        B = int(rng.integers(1, 9))
+        Lmax = int(rng.integers(1, 3001))
+        shapes.append((B, G * Hkv, Hkv, D, Lmax, 5000 + 17 * seed + i))
+    return shapes
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,Lmax,seed", _random_shapes(12, 1))
+def test_random_shapes(B, Hq, Hkv, D, Lmax, seed):
+    w = Workload("rand", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, seed=seed, len_lo=0, len_hi=Lmax)
+    print("case random", B, Hq, Hkv, D, Lmax, seed, flush=True)
+    run_case(w)                  # the planner's choice
+    run_case(w, chunk=128)       # many chunks, both combine kernels
 
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
