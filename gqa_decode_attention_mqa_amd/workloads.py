@@ -145,3 +145,57 @@ def make_prefill_inputs(w: Workload, device="cpu", seed: int | None = None,
         poison_padding_(k, lens)
         poison_padding_(v, lens)
     return {"q_seq": q, "k": k, "v": v, "seq_lens": lens, "scale": w.scale}
+
+
+def page_contiguous_cache(inp: dict, page_size: int, seed: int, spare_pages: int = 0,
+                          poison_spare: bool = True) -> dict:
+    """Move the contiguous caches of ``inp`` (from :func:`make_inputs`) into a paged pool.
+
+    Each sequence b gets ceil(len_b / page_size) physical pages, in a seeded
+    random order over the whole pool, plus ``spare_pages`` unused pages
+    (bf16 NaN when ``poison_spare``).  block_table [B, max_blocks] holds the
+    physical page of each logical block; entries past a sequence's last block
+    are -1 and must never be read.  Rows of a sequence's last page past its
+    length keep the cache's padding.  Adds ``k_pages``, ``v_pages``,
+    ``block_table``, ``page_size`` and ``num_pages`` to a copy of ``inp``.
+    """
+    k, v, lens = inp["k"], inp["v"], inp["seq_lens"]
+    B, Lmax, Hkv, D = k.shape
+    device = k.device
+    max_blocks = max(1, -(-Lmax // page_size))
+    lens_cpu = lens.to("cpu").tolist()
+    nblocks = [-(-n // page_size) for n in lens_cpu]
+    used = sum(nblocks)
+    num_pages = used + spare_pages
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    perm = torch.randperm(max(num_pages, 1), generator=gen)[:num_pages].tolist()
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    # padded contiguous caches so every block of page_size rows exists
+    padded_len = max_blocks * page_size
+    if padded_len > Lmax:
+        fill = torch.full((B, padded_len - Lmax, Hkv, D), 0, dtype=k.dtype, device=device)
+        fill.view(torch.int16).fill_(BF16_QNAN_BITS)
+        kc, vc = torch.cat([k, fill], 1), torch.cat([v, fill.clone()], 1)
+    else:
+        kc, vc = k, v
+    k_pages = torch.empty((max(num_pages, 1), page_size, Hkv, D), dtype=k.dtype, device=device)
+    v_pages = torch.empty_like(k_pages)
+    if poison_spare:
+        k_pages.view(torch.int16).fill_(BF16_QNAN_BITS)
+        v_pages.view(torch.int16).fill_(BF16_QNAN_BITS)
+    else:
+        k_pages.zero_()
+        v_pages.zero_()
+    i = 0
+    for b in range(B):
+        for blk in range(nblocks[b]):
+            page = perm[i]
+            i += 1
+            table[b, blk] = page
+            k_pages[page] = kc[b, blk * page_size:(blk + 1) * page_size]
+            v_pages[page] = vc[b, blk * page_size:(blk + 1) * page_size]
+    out = dict(inp)
+    out.update({"k_pages": k_pages, "v_pages": v_pages, "block_table": table.to(device),
+                "page_size": page_size, "num_pages": num_pages})
+    return out

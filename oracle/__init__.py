@@ -52,6 +52,9 @@ def _load():
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_causal_prefill.argtypes = [u16p, u16p, u16p, i32p] + [ctypes.c_int] * 5 + \
             [ctypes.c_double, f64p]
+        lib.oracle_decode_paged.argtypes = [u16p, u16p, u16p, i32p, i32p] + [ctypes.c_int] * 7 + \
+            [ctypes.c_double, f64p]
+        lib.oracle_decode_paged.restype = ctypes.c_int
         lib.oracle_causal_prefill.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_set_threads.restype = ctypes.c_int
@@ -121,6 +124,27 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, return_lse: bool = False
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments (code %d)" % rc)
     return (out, lse) if return_lse else out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float):
+    """fp64 decode step over a paged cache.  q [B,Hq,D], pages [num_pages,page_size,Hkv,D],
+    block_table [B,max_blocks] int32, seq_lens [B].  Returns ``out`` [B,Hq,D] float64."""
+    qb, kb, vb = _bits(q), _bits(k_pages), _bits(v_pages)
+    lens = _lens(seq_lens)
+    table = _lens(block_table)
+    B, Hq, D = qb.shape
+    num_pages, page_size, Hkv, Dk = kb.shape
+    if vb.shape != kb.shape or Dk != D or lens.shape != (B,) or table.ndim != 2 or table.shape[0] != B:
+        raise ValueError("inconsistent shapes q%s pages%s table%s lens%s" % (qb.shape, kb.shape, table.shape,
+                                                                           lens.shape))
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = _load().oracle_decode_paged(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+                                     _ptr(vb, ctypes.c_uint16), _ptr(table, ctypes.c_int32),
+                                     _ptr(lens, ctypes.c_int32), B, Hq, Hkv, D, num_pages, page_size,
+                                     table.shape[1], float(scale), _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_decode_paged rejected its arguments (code %d)" % rc)
+    return out
 
 
 def causal_prefill(q_seq, k_cache, v_cache, seq_lens, scale: float):

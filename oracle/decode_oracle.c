@@ -165,6 +165,99 @@ int oracle_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 }
 
 /*
+ * One decode step over a paged cache ("Machine Learning Engineering and AI
+ * Systems at Scale", section "The key and value cache": fixed-size blocks of
+ * positions and a per-sequence block table mapping logical positions to
+ * physical blocks; "How To Scale Your Model", Part 7, passage on ragged reads
+ * and paged attention).
+ *   k_pages, v_pages [num_pages, page_size, Hkv, D]  bf16 bits
+ *   block_table      [B, max_blocks]: physical page of each block of
+ *                    page_size logical positions; entries past a sequence's
+ *                    last block are never read
+ *   seq_lens         [B], each in [0, max_blocks * page_size]
+ * Position j of sequence b is row (j mod page_size) of page
+ * block_table[b][j / page_size].  The attention itself is the one of
+ * oracle_decode, step for step.  Returns 0, or a negative code on a bad shape,
+ * length or page index.
+ */
+int oracle_decode_paged(const uint16_t *q, const uint16_t *k_pages,
+                        const uint16_t *v_pages, const int32_t *block_table,
+                        const int32_t *seq_lens, int B, int Hq, int Hkv, int D,
+                        int num_pages, int page_size, int max_blocks,
+                        double scale, double *out)
+{
+    if (num_pages < 0 || page_size <= 0 || max_blocks < 0) return -1;
+    int rc = check_shape(B, Hq, Hkv, D, 0);
+    if (rc) return rc;
+    for (int b = 0; b < B; ++b) {
+        const int n = seq_lens[b];
+        if (n < 0 || (long long)n > (long long)max_blocks * page_size) return -3;
+        for (int blk = 0; blk * page_size < n; ++blk) {
+            const int page = block_table[(size_t)b * max_blocks + blk];
+            if (page < 0 || page >= num_pages) return -5;
+        }
+    }
+
+    const int G = Hq / Hkv;
+    const long long pairs = (long long)B * Hq;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < pairs; ++bh) {
+        const int b = (int)(bh / Hq);
+        const int h = (int)(bh % Hq);
+        const int g = h / G;
+        const int n = seq_lens[b];
+        const int32_t *table = block_table + (size_t)b * max_blocks;
+        double *o = out + ((size_t)b * Hq + h) * D;
+
+        if (n == 0) {
+            for (int d = 0; d < D; ++d) o[d] = 0.0;
+            continue;
+        }
+        double *s = (double *)malloc((size_t)n * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const uint16_t *qrow = q + ((size_t)b * Hq + h) * D;
+
+        /* logits, each key row found through the block table */
+        for (int j = 0; j < n; ++j) {
+            const size_t row = (size_t)table[j / page_size] * page_size + (size_t)(j % page_size);
+            const uint16_t *krow = k_pages + (row * Hkv + g) * D;
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += bf16_bits_to_double(qrow[d]) * bf16_bits_to_double(krow[d]);
+            s[j] = scale * acc;
+        }
+
+        /* softmax weights, shifted by the maximum for range safety */
+        double m = s[0];
+        for (int j = 1; j < n; ++j)
+            if (s[j] > m) m = s[j];
+        double Z = 0.0;
+        for (int j = 0; j < n; ++j) {
+            s[j] = exp(s[j] - m);
+            Z += s[j];
+        }
+
+        /* weighted sum of the value rows, found the same way */
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        for (int j = 0; j < n; ++j) {
+            const size_t row = (size_t)table[j / page_size] * page_size + (size_t)(j % page_size);
+            const uint16_t *vrow = v_pages + (row * Hkv + g) * D;
+            for (int d = 0; d < D; ++d)
+                o[d] += s[j] * bf16_bits_to_double(vrow[d]);
+        }
+        for (int d = 0; d < D; ++d) o[d] /= Z;
+        free(s);
+    }
+    return failed ? -4 : 0;
+}
+
+/*
  * Full causal self-attention over a whole sequence, recomputed with no cache
  * (the work the KV cache avoids).
  *   q_seq   [B, Lmax, Hq, D]   bf16 bits: one query per position

@@ -27,7 +27,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from gqa_decode_attention_mqa_amd.workloads import Workload, make_inputs, make_prefill_inputs
+from gqa_decode_attention_mqa_amd.workloads import Workload, make_inputs, make_prefill_inputs, page_contiguous_cache
 
 TIGHT = 1e-12
 
@@ -320,3 +320,64 @@ def test_oracle_rejects_bad_shapes():
     q = torch.zeros((1, 4, 8), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         oracle.decode(q, k, k, [5], 1.0)              # length beyond Lmax
+
+
+# ------------------------------------------------------------ paged cache
+
+
+@pytest.mark.parametrize("page_size", [1, 3, 32, 64])
+def test_paged_oracle_equals_contiguous_for_any_page_order(page_size):
+    """Paging only moves rows: the paged oracle on a randomly permuted pool equals the
+    (independently pinned) contiguous oracle exactly, for every page size."""
+    w = Workload("pg", B=4, Hq=8, Hkv=2, D=64, Lmax=200, seed=301, len_lo=0, len_hi=200)
+    inp = make_inputs(w, poison_padding=True)
+    pg = page_contiguous_cache(inp, page_size, seed=7, spare_pages=5)
+    ref = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    got = oracle.decode_paged(inp["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], inp["seq_lens"],
+                              inp["scale"])
+    assert np.array_equal(got, ref)
+
+
+def test_paged_oracle_reversed_single_position_pages():
+    """page_size 1 with each sequence's positions stored in reverse page order."""
+    w = Workload("pg1", B=2, Hq=4, Hkv=1, D=64, Lmax=17, seed=302)
+    inp = make_inputs(w)
+    B, L, Hkv, D = inp["k"].shape
+    k_pages = torch.empty((B * L, 1, Hkv, D), dtype=torch.bfloat16)
+    v_pages = torch.empty_like(k_pages)
+    table = torch.empty((B, L), dtype=torch.int32)
+    for b in range(B):
+        for j in range(L):
+            page = (B * L - 1) - (b * L + j)
+            table[b, j] = page
+            k_pages[page, 0] = inp["k"][b, j]
+            v_pages[page, 0] = inp["v"][b, j]
+    ref = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    got = oracle.decode_paged(inp["q"], k_pages, v_pages, table, inp["seq_lens"], inp["scale"])
+    assert np.array_equal(got, ref)
+
+
+def test_paged_oracle_shared_prefix_pages():
+    """Two sequences whose block tables point at the same physical pages (a shared prefix)
+    and carry the same query see exactly the same attention."""
+    w = Workload("pgs", B=2, Hq=4, Hkv=1, D=64, Lmax=96, seed=303)
+    inp = make_inputs(w)
+    pg = page_contiguous_cache(inp, 32, seed=9)
+    table = pg["block_table"].clone()
+    table[1] = table[0]
+    q = inp["q"].clone()
+    q[1] = q[0]
+    out = oracle.decode_paged(q, pg["k_pages"], pg["v_pages"], table, inp["seq_lens"], inp["scale"])
+    assert np.array_equal(out[0], out[1])
+    ref = oracle.decode(q[:1], inp["k"][:1], inp["v"][:1], inp["seq_lens"][:1], inp["scale"])
+    assert np.array_equal(out[:1], ref)
+
+
+def test_paged_oracle_rejects_bad_page_index():
+    w = Workload("pgb", B=1, Hq=4, Hkv=1, D=64, Lmax=64, seed=304)
+    inp = make_inputs(w)
+    pg = page_contiguous_cache(inp, 32, seed=1)
+    table = pg["block_table"].clone()
+    table[0, 1] = pg["num_pages"]  # one past the pool
+    with pytest.raises(ValueError):
+        oracle.decode_paged(inp["q"], pg["k_pages"], pg["v_pages"], table, inp["seq_lens"], inp["scale"])
