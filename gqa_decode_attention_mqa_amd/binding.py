@@ -58,6 +58,9 @@ def load_library():
     ints = [ctypes.c_int] * 5
     lib.mqa_decode_attention.argtypes = [vp, vp, vp, i32p, f32p] + ints + [ctypes.c_float, vp]
     lib.mqa_decode_attention.restype = ctypes.c_int
+    lib.mqa_decode_attention_paged.argtypes = [vp, vp, vp, i32p, i32p, f32p] + [ctypes.c_int] * 7 + \
+        [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
+    lib.mqa_decode_attention_paged.restype = ctypes.c_int
     lib.mqa_decode_attention_ex.argtypes = [vp, vp, vp, i32p, f32p] + ints + \
         [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
     lib.mqa_decode_attention_ex.restype = ctypes.c_int
@@ -166,6 +169,41 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
                                      seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D, Lmax,
                                      sc, _stream_ptr(dev), ctypes.byref(opts))
     _check(st, "mqa_decode_attention")
+    return out
+
+
+def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                 seq_lens: torch.Tensor, scale: float | None = None, out: torch.Tensor | None = None,
+                 variant=None, chunk=None, combine=None, events=None) -> torch.Tensor:
+    """One decode step over a paged cache.  q [B,Hq,D] bf16, pages [num_pages,page_size,Hkv,D] bf16,
+    block_table [B,max_blocks] int32, seq_lens [B] int32 -> fp32 [B,Hq,D]."""
+    if q.device.type != "cuda":
+        raise ValueError("decode_paged runs on the GPU; q is on %s" % q.device)
+    dev = q.device
+    _require(q, "q", torch.bfloat16, 3, dev)
+    _require(k_pages, "k_pages", torch.bfloat16, 4, dev)
+    _require(v_pages, "v_pages", torch.bfloat16, 4, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if v_pages.shape != k_pages.shape or Dk != D or seq_lens.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("shape mismatch: q %s, pages %s, block_table %s, seq_lens %s" % (
+            tuple(q.shape), tuple(k_pages.shape), tuple(block_table.shape), tuple(seq_lens.shape)))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, 3, dev)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    ev_b = ev_e = None
+    if events is not None:
+        ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e)
+    lib = load_library()
+    st = lib.mqa_decode_attention_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                        block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                                        B, Hq, Hkv, D, num_pages, page_size, block_table.shape[1],
+                                        sc, _stream_ptr(dev), ctypes.byref(opts))
+    _check(st, "mqa_decode_attention_paged")
     return out
 
 

@@ -96,7 +96,7 @@ mqa_status get_workspace(hipStream_t stream, size_t bytes, size_t ncounters, voi
 
 mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_lens, float* out,
                int B, int Hq, int Hkv, int D, int Lmax, float scale, void* stream_ptr,
-               const mqa_decode_opts* opts, bool causal) {
+               const mqa_decode_opts* opts, bool causal, const mqa::PagedCache* paged = nullptr) {
     mqa::set_error("");
     Plan plan;
     mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, causal, &plan);
@@ -120,6 +120,12 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.part_o = ws ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + plan.part_o_offset) : nullptr;
     a.part_ml = ws ? reinterpret_cast<mqa::f32x2_t*>(static_cast<char*>(ws) + plan.part_ml_offset) : nullptr;
     a.counters = counters;
+    if (paged) {
+        a.block_table = paged->block_table;
+        a.page_shift = paged->page_shift;
+        a.max_blocks = paged->max_blocks;
+        a.num_pages = paged->num_pages;
+    }
     a.units = plan.rows * Hkv;
     a.fused = plan.combine == 2 ? 1 : 0;
     a.Hq = Hq;
@@ -175,6 +181,19 @@ mqa_status mqa_decode_attention_ex(const void* q, const void* k_cache, const voi
                                    int D, int Lmax, float scale, void* stream,
                                    const mqa_decode_opts* opts) {
     return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false);
+}
+
+mqa_status mqa_decode_attention_paged(const void* q, const void* k_pages, const void* v_pages,
+                                      const int32_t* block_table, const int32_t* seq_lens, float* out,
+                                      int B, int Hq, int Hkv, int D, int num_pages, int page_size,
+                                      int max_blocks, float scale, void* stream,
+                                      const mqa_decode_opts* opts) {
+    mqa::set_error("");
+    mqa::PagedCache pc{};
+    int Lmax = 0;
+    const mqa_status st = mqa::check_paged(B, block_table, num_pages, page_size, max_blocks, &pc, &Lmax);
+    if (st != MQA_OK) return st;
+    return run(q, k_pages, v_pages, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false, &pc);
 }
 
 mqa_status mqa_prefill_attention(const void* q_seq, const void* k_cache, const void* v_cache,
@@ -235,6 +254,6 @@ void mqa_release_workspaces(void) {
     g_ws.clear();
 }
 
-int mqa_version(void) { return 100; }
+int mqa_version(void) { return 110; }
 
 }  // extern "C"

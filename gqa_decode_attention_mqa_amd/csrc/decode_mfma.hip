@@ -158,8 +158,6 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
 
     const size_t pos_stride = (size_t)a.Hkv * D;
     const int rowbytes = (int)(pos_stride * 2);
-    const uint16_t* kseq = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
-    const uint16_t* vseq = a.v + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
 
     // A compute wave's q^T operand (B of q.K): lane (li, kg), k-step ks holds
     // q[head 16w + li][32 ks + 8 kg .. +8]; heads past the group read as zero.
@@ -187,8 +185,8 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         if (w < NG) return;
         const int t0 = p0 + tile * C::STEP;
         const int rows = max(0, min(C::STEP, p1 - t0));
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kseq + (size_t)t0 * pos_stride, rows * rowbytes);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vseq + (size_t)t0 * pos_stride, rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows > 0 ? kv_rows(a.k, a, b, kvh, t0) : a.k, rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows > 0 ? kv_rows(a.v, a, b, kvh, t0) : a.v, rows * rowbytes);
         unsigned char* slot = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::KPW; ++i) {

@@ -96,8 +96,6 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
     const size_t pos_stride = (size_t)a.Hkv * D;
     const int rowbytes = (int)(pos_stride * 2);
-    const uint16_t* kseq = a.k + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
-    const uint16_t* vseq = a.v + ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
     const float qk = a.qk_log2;
     // Byte offset of this lane's 8 columns in row st*RS + rr of a block.
     int off[NB];
@@ -120,8 +118,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     auto load_block = [&](int blk, u32x4_t (&kr)[NB], u32x4_t (&vr)[NB]) {
         const int t0 = p0 + blk * WB;
         const int rows = max(0, min(WB, p1 - t0));
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kseq + (size_t)t0 * pos_stride, rows * rowbytes);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vseq + (size_t)t0 * pos_stride, rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows > 0 ? kv_rows(a.k, a, b, kvh, t0) : a.k, rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows > 0 ? kv_rows(a.v, a, b, kvh, t0) : a.v, rows * rowbytes);
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
             kr[st] = buffer_load_u32x4(krs, off[st]);

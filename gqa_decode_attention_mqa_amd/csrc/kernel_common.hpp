@@ -30,6 +30,9 @@ struct DecodeArgs {
     float* out;                // fp32 [rows, Hq, D]
     uint16_t* part_o;          // fp16 [rows * Hkv * max_splits, G, D]: O / l / 2^e per chunk
     f32x2_t* part_ml;          // [rows * Hkv * max_splits, G]: {m + log2(l) (base 2), e}
+    const int32_t* block_table;  // paged cache: [B, max_blocks] physical page per block of
+                                 // 2^page_shift positions; NULL for the contiguous layout
+    int page_shift, max_blocks, num_pages;
     uint32_t* counters;        // [rows * Hkv * head_blocks] arrival counters (fused combine);
                                // zero between calls: the last arriving chunk resets its counter
     long long units;           // rows * Hkv
@@ -49,6 +52,25 @@ struct CombineArgs {
     int chunk, max_splits;
     int causal;
 };
+
+// Base of the cache rows t0, t0 + 1, ... of kv head kvh of sequence b; the
+// rows a caller reads from it never straddle a page (pages hold a power of two
+// >= 32 positions, and every tile or block starts at a multiple of its own
+// size <= 32).  Only called for rows below the sequence length, so the block
+// table entry read is one of the sequence's own; page indices outside the pool
+// are clamped into it, so a bad table gives wrong data, never a stray read.
+__device__ __forceinline__ const uint16_t* kv_rows(const uint16_t* cache, const DecodeArgs& a, int b, int kvh,
+                                                   int t0) {
+    size_t row;
+    if (a.block_table) {
+        int page = a.block_table[(size_t)b * a.max_blocks + (t0 >> a.page_shift)];
+        page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+        row = ((size_t)page << a.page_shift) + (size_t)(t0 & ((1 << a.page_shift) - 1));
+    } else {
+        row = (size_t)b * a.Lmax + t0;
+    }
+    return cache + (row * a.Hkv + kvh) * a.D;
+}
 
 // Attended length of a row, with seq_lens clamped to [0, Lmax].
 __device__ __forceinline__ void row_extent(const int32_t* seq_lens, long long row, int Lmax,

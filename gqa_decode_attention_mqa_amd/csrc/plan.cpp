@@ -51,6 +51,28 @@ mqa_status check_pointers(int B, int Lmax, const void* q, const void* k, const v
     return MQA_OK;
 }
 
+mqa_status check_paged(int B, const int32_t* block_table, int num_pages, int page_size, int max_blocks,
+                       PagedCache* pc, int* Lmax) {
+    if (num_pages < 0 || max_blocks < 0 || page_size <= 0)
+        return fail(MQA_ERR_SHAPE, "num_pages and max_blocks must be >= 0 and page_size > 0");
+    if (page_size < 32 || (page_size & (page_size - 1)) != 0)
+        return fail(MQA_ERR_UNSUPPORTED, "page_size must be a power of two >= 32");
+    const long long L = (long long)max_blocks * page_size;
+    if (L > 0x7FFFFFFFLL)
+        return fail(MQA_ERR_UNSUPPORTED, "max_blocks * page_size exceeds the int range");
+    if (B > 0 && L > 0) {
+        if (!block_table) return fail(MQA_ERR_NULL, "block_table must be non-NULL");
+        if ((reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
+            return fail(MQA_ERR_ALIGN, "block_table must be 4-byte aligned");
+        if (num_pages == 0) return fail(MQA_ERR_SHAPE, "the page pool is empty");
+    }
+    int shift = 0;
+    while ((1 << shift) < page_size) ++shift;
+    *pc = PagedCache{block_table, num_pages, page_size, max_blocks, shift};
+    *Lmax = (int)L;
+    return MQA_OK;
+}
+
 mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                      const mqa_decode_opts* opts, bool causal, Plan* plan) {
     if (B < 0 || Lmax < 0)

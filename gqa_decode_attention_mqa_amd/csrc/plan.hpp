@@ -66,6 +66,19 @@ const char* last_error();
 mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                      const mqa_decode_opts* opts, bool causal, Plan* plan);
 
+// A paged cache as the kernels see it (see check_paged).
+struct PagedCache {
+    const int32_t* block_table;
+    int num_pages, page_size, max_blocks, page_shift;
+};
+
+// Paged-cache checks: page_size a power of two >= 32, counts >= 0, the
+// logical length max_blocks * page_size within int, a non-NULL 4-byte aligned
+// block table and a non-empty pool when any position can be attended.  On
+// success fills `pc` and the logical maximum length `Lmax`.
+mqa_status check_paged(int B, const int32_t* block_table, int num_pages, int page_size, int max_blocks,
+                       PagedCache* pc, int* Lmax);
+
 // Pointer checks: non-NULL when B > 0 (the caches only when Lmax > 0), 16-byte
 // alignment of the bf16/fp32 arrays.
 mqa_status check_pointers(int B, int Lmax, const void* q, const void* k, const void* v,

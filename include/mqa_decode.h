@@ -126,6 +126,32 @@ mqa_status mqa_decode_attention_ex(const void *q, const void *k_cache, const voi
                                    const mqa_decode_opts *opts);
 
 /*
+ * One decode step over a paged KV cache.  Instead of one contiguous
+ * [Lmax, Hkv, D] region per sequence, the cache is a pool of fixed-size pages
+ * and a per-sequence block table maps logical positions to physical pages
+ * ("Machine Learning Engineering and AI Systems at Scale", section "The key
+ * and value cache": blocks of a few tokens, a per-sequence block table, and
+ * shared prefixes as shared blocks; "How To Scale Your Model", Part 7, the
+ * passage on ragged reads and paged attention).
+ *   k_pages, v_pages  bf16 [num_pages, page_size, Hkv, D], contiguous
+ *   block_table       int32 [B, max_blocks]: position j of sequence b is row
+ *                     j % page_size of page block_table[b][j / page_size]
+ *   seq_lens          int32 [B], clamped on the device to [0, max_blocks * page_size]
+ *   q, out, scale     as for mqa_decode_attention
+ *   opts              optional, as for mqa_decode_attention_ex (may be NULL)
+ * page_size must be a power of two >= 32 (MQA_ERR_UNSUPPORTED otherwise).
+ * Only the block table entries of a sequence's first ceil(len / page_size)
+ * blocks are read; several sequences may share pages.  A page index outside
+ * [0, num_pages) is clamped into the pool on the device (wrong data, never an
+ * out-of-range read).  Errors and ownership as for mqa_decode_attention.
+ */
+mqa_status mqa_decode_attention_paged(const void *q, const void *k_pages, const void *v_pages,
+                                      const int32_t *block_table, const int32_t *seq_lens, float *out,
+                                      int B, int Hq, int Hkv, int D, int num_pages, int page_size,
+                                      int max_blocks, float scale, void *stream,
+                                      const mqa_decode_opts *opts);
+
+/*
  * Causal attention over whole sequences with no cache, the computation a KV
  * cache replaces ("How To Scale Your Model", Part 7, passage introducing the
  * KV cache: a token attends only to itself and earlier tokens).  Row t of

@@ -20,7 +20,8 @@ import torch
 
 import oracle
 from gqa_decode_attention_mqa_amd import binding
-from gqa_decode_attention_mqa_amd.workloads import WORKLOADS, Workload, make_inputs, make_prefill_inputs
+from gqa_decode_attention_mqa_amd.workloads import (WORKLOADS, Workload, make_inputs, make_prefill_inputs,
+                                                    page_contiguous_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -228,6 +229,79 @@ def test_prefill_matches_oracle_causal_attention(B, Hq, Hkv, D, Lmax):
     dec = binding.decode(q_last, inp["k"], inp["v"], inp["seq_lens"], inp["scale"]).cpu()
     last = torch.stack([out[b, int(lens[b]) - 1].cpu() for b in range(B)])
     assert (dec - last).abs().max().item() <= ATOL
+
+
+# ------------------------------------------------------------ paged cache
+
+
+def paged_inputs(w: Workload, page_size: int, seed: int, spare_pages: int = 3):
+    """Seeded paged pool (NaN padding and spare pages) built on the CPU, then moved to the GPU."""
+    inp = make_inputs(w, poison_padding=True)
+    pg = page_contiguous_cache(inp, page_size, seed=seed, spare_pages=spare_pages)
+    return pg, to_dev(pg)
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("page_size", [32, 64, 128, 256])
+@pytest.mark.parametrize("G,Hkv,D", [(8, 2, 128), (4, 2, 64), (48, 1, 256)])
+def test_paged_matches_paged_oracle(variant, page_size, G, Hkv, D):
+    w = Workload("paged", B=5, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=1000, seed=400 + page_size + D + G,
+                 len_lo=0, len_hi=1000)
+    pg, dev = paged_inputs(w, page_size, seed=page_size + G)
+    ref = oracle.decode_paged(pg["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], pg["seq_lens"], pg["scale"])
+    for chunk, combine in ((None, None), (128, "separate"), (128, "fused")):
+        print("case paged", variant, page_size, G, Hkv, D, chunk, combine, flush=True)
+        out = binding.decode_paged(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], dev["seq_lens"],
+                                   dev["scale"], variant=variant, chunk=chunk, combine=combine)
+        torch.cuda.synchronize()
+        check_close(out, ref, "paged %s page %d G %d D %d chunk %s %s" % (variant, page_size, G, D, chunk, combine))
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+def test_paged_equals_contiguous_bitwise(variant):
+    """Same data, same plan (max_blocks * page_size == Lmax): the paged kernels read the same
+    tiles through the block table and must produce identical bits."""
+    w = Workload("pgeq", B=6, Hq=16, Hkv=2, D=128, Lmax=1024, seed=450, len_lo=1, len_hi=1024)
+    pg, dev = paged_inputs(w, 64, seed=3)
+    for chunk in (None, 128):
+        a = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant, chunk=chunk)
+        b = binding.decode_paged(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], dev["seq_lens"],
+                                 dev["scale"], variant=variant, chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_paged_shared_prefix():
+    """Two sequences whose block tables point at the same pages, with the same query, agree exactly."""
+    w = Workload("pgsh", B=2, Hq=48, Hkv=1, D=256, Lmax=512, seed=451)
+    pg, dev = paged_inputs(w, 128, seed=4, spare_pages=0)
+    table = dev["block_table"].clone()
+    table[1] = table[0]
+    q = dev["q"].clone()
+    q[1] = q[0]
+    out = binding.decode_paged(q, dev["k_pages"], dev["v_pages"], table, dev["seq_lens"], dev["scale"], chunk=128)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], out[1])
+    ref = oracle.decode_paged(q.cpu(), pg["k_pages"], pg["v_pages"], table.cpu(), pg["seq_lens"], pg["scale"])
+    check_close(out, ref, "shared prefix")
+
+
+def test_paged_full_size_ragged_sampled():
+    """The ragged workload on a page pool of 64-position pages (pool = the used pages only)."""
+    w = WORKLOADS["ragged"]
+    print("case full paged ragged", flush=True)
+    inp = make_inputs(w, device=DEV)
+    pg = page_contiguous_cache(inp, 64, seed=5)
+    del inp["k"], inp["v"]
+    out = binding.decode_paged(pg["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], pg["seq_lens"], pg["scale"])
+    torch.cuda.synchronize()
+    idx = sample_indices(pg["seq_lens"], 8)
+    sel = torch.tensor(idx, device=DEV)
+    ref = oracle.decode_paged(pg["q"].index_select(0, sel).cpu(), pg["k_pages"].cpu(), pg["v_pages"].cpu(),
+                              pg["block_table"].index_select(0, sel).cpu(), pg["seq_lens"].index_select(0, sel).cpu(),
+                              pg["scale"])
+    err = check_close(out.index_select(0, sel), ref, "paged ragged")
+    print("full paged ragged: %d sequences checked, max abs err %.3g" % (len(idx), err), flush=True)
 
 
 # ------------------------------------------------------ full-size workloads

@@ -138,3 +138,26 @@ def test_chunk_schedule_covers_every_valid_position_once():
                 continue
             seen.extend(range(p0, min(p0 + C, n)))
         assert seen == list(range(n))
+
+
+def paged_call(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, D=128,
+               num_pages=16, page_size=64, max_blocks=4, scale=0.1):
+    return lib.mqa_decode_attention_paged(q, k, v, table, lens, out, B, Hq, Hkv, D, num_pages, page_size,
+                                          max_blocks, scale, None, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(page_size=48), ERR_UNSUPPORTED), (dict(page_size=16), ERR_UNSUPPORTED), (dict(page_size=96), ERR_UNSUPPORTED),
+    (dict(page_size=0), ERR_SHAPE), (dict(page_size=-64), ERR_SHAPE),
+    (dict(num_pages=-1), ERR_SHAPE), (dict(max_blocks=-1), ERR_SHAPE), (dict(num_pages=0), ERR_SHAPE),
+    (dict(table=0), ERR_NULL), (dict(table=FAKE + 2), ERR_ALIGN),
+    (dict(page_size=1 << 20, max_blocks=1 << 12), ERR_UNSUPPORTED),
+    (dict(k=0), ERR_NULL), (dict(q=FAKE + 8), ERR_ALIGN), (dict(Hq=7), ERR_SHAPE), (dict(D=96), ERR_UNSUPPORTED),
+])
+def test_paged_arguments_are_rejected_before_any_hip_call(kw, expect):
+    assert paged_call(**kw) == expect
+    assert lib.mqa_last_error()
+
+
+def test_paged_empty_batch_is_a_no_op():
+    assert paged_call(q=0, k=0, v=0, table=0, lens=0, out=0, B=0) == OK
