@@ -75,6 +75,9 @@ def parse_args(argv=None):
     ap.add_argument("--variant", default=None, choices=[None, "auto", "valu", "mfma"])
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--combine", default=None, choices=[None, "auto", "separate", "fused"])
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="run the paged-cache entry point on a pool of pages of this many positions "
+                         "(a power of two >= 32; the pool holds the used pages only); 0 = contiguous cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -138,7 +141,7 @@ def main(argv=None):
 
     from gqa_decode_attention_mqa_amd import binding
     from gqa_decode_attention_mqa_amd.traffic import decode_step_kv_bytes
-    from gqa_decode_attention_mqa_amd.workloads import WORKLOADS, make_inputs
+    from gqa_decode_attention_mqa_amd.workloads import WORKLOADS, make_inputs, page_contiguous_cache
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -156,10 +159,25 @@ def main(argv=None):
     plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk, args.combine)
 
     calls = []
-    for s in sets:
-        calls.append((s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(), s["seq_lens"].data_ptr(),
-                      out.data_ptr(), w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, sptr))
-    fn = lib.mqa_decode_attention_ex
+    if args.page_size:
+        # each set's caches move into a pool of pages in a seeded random order
+        # (pages of one sequence are scattered over the pool)
+        cpu_set = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in base.items()} \
+            if not args.no_cpu_baseline else None
+        for i, s in enumerate(sets):
+            pg = page_contiguous_cache(s, args.page_size, seed=w.seed + 7 * i, poison_spare=False)
+            del s["k"], s["v"], pg["k"], pg["v"]
+            s.update(pg)
+            calls.append((s["q"].data_ptr(), s["k_pages"].data_ptr(), s["v_pages"].data_ptr(),
+                          s["block_table"].data_ptr(), s["seq_lens"].data_ptr(), out.data_ptr(), w.B, w.Hq,
+                          w.Hkv, w.D, s["num_pages"], args.page_size, s["block_table"].shape[1], w.scale, sptr))
+        fn = lib.mqa_decode_attention_paged
+    else:
+        cpu_set = None
+        for s in sets:
+            calls.append((s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(), s["seq_lens"].data_ptr(),
+                          out.data_ptr(), w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, sptr))
+        fn = lib.mqa_decode_attention_ex
 
     def step(i, opts):
         st = fn(*calls[i % nsets], binding.ctypes.byref(opts))
@@ -200,7 +218,7 @@ def main(argv=None):
     ms_per_step = total_ms / args.steps
     kv_bytes = decode_step_kv_bytes(lens.cpu().tolist(), w.Hkv, w.D)
     achieved = kv_bytes / (mean_kern_ms * 1e-3) / 1e9
-    traffic = read_traffic(w.name)
+    traffic = read_traffic(w.name + ("_paged%d" % args.page_size if args.page_size else ""))
 
     result = {
         "metric": "decode-attention steps/sec and achieved HBM GB/s (% of MI355X peak)",
@@ -216,7 +234,9 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": w.description,
+            "workload": w.description + (" (paged cache, %d-position pages)" % args.page_size
+                                         if args.page_size else ""),
+            "page_size": args.page_size or None,
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "Lmax": w.Lmax,
             "seq_lens_sum": int(lens.sum().item()),
             "kv_bytes_per_step": kv_bytes,
@@ -238,7 +258,7 @@ def main(argv=None):
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, base, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, cpu_set if cpu_set is not None else base, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

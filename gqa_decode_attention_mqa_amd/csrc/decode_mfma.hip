@@ -181,12 +181,30 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     // tile % STAGES (compute waves issue nothing).  Load jj (0 .. LOADS-1)
     // covers 1 KB of the K tile and, with a second load, the same 1 KB of the
     // V tile; loader l issues jj = l, l + NL, ..., KPW of each.
+    // Paged cache: a loader keeps the chunk's page indices in its lanes (lane
+    // i: block (p0 >> page_shift) + i) when they fit in a wave, so no block
+    // table load sits on the issue path; otherwise each tile looks it up.
+    const int blk0 = a.block_table ? (p0 >> a.page_shift) : 0;
+    const int nblk = (a.block_table && p1 > p0) ? ((p1 - 1) >> a.page_shift) - blk0 + 1 : 0;
+    const bool pages_in_lanes = nblk > 0 && nblk <= 64;
+    int chunk_page = 0;
+    if (pages_in_lanes && w >= NG) {
+        if (lane < nblk) chunk_page = a.block_table[(size_t)b * a.max_blocks + blk0 + lane];
+        // the first tile's address needs it anyway; waiting here also tells the
+        // compiler that no load into it is pending inside the loop
+        __builtin_amdgcn_s_waitcnt(kVmcntStages<0, 0>());
+    }
+    auto tile_rows = [&](const uint16_t* cache, int t0) {
+        if (pages_in_lanes)
+            return page_rows(cache, a, __builtin_amdgcn_readlane(chunk_page, (t0 >> a.page_shift) - blk0), kvh, t0);
+        return kv_rows(cache, a, b, kvh, t0);
+    };
     auto issue_tile = [&](int tile) {
         if (w < NG) return;
         const int t0 = p0 + tile * C::STEP;
         const int rows = max(0, min(C::STEP, p1 - t0));
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows > 0 ? kv_rows(a.k, a, b, kvh, t0) : a.k, rows * rowbytes);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows > 0 ? kv_rows(a.v, a, b, kvh, t0) : a.v, rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows > 0 ? tile_rows(a.k, t0) : a.k, rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows > 0 ? tile_rows(a.v, t0) : a.v, rows * rowbytes);
         unsigned char* slot = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::KPW; ++i) {

@@ -59,17 +59,17 @@ struct CombineArgs {
 // size <= 32).  Only called for rows below the sequence length, so the block
 // table entry read is one of the sequence's own; page indices outside the pool
 // are clamped into it, so a bad table gives wrong data, never a stray read.
+__device__ __forceinline__ const uint16_t* page_rows(const uint16_t* cache, const DecodeArgs& a, int page, int kvh,
+                                                     int t0) {
+    page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+    const size_t row = ((size_t)page << a.page_shift) + (size_t)(t0 & ((1 << a.page_shift) - 1));
+    return cache + (row * a.Hkv + kvh) * a.D;
+}
 __device__ __forceinline__ const uint16_t* kv_rows(const uint16_t* cache, const DecodeArgs& a, int b, int kvh,
                                                    int t0) {
-    size_t row;
-    if (a.block_table) {
-        int page = a.block_table[(size_t)b * a.max_blocks + (t0 >> a.page_shift)];
-        page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-        row = ((size_t)page << a.page_shift) + (size_t)(t0 & ((1 << a.page_shift) - 1));
-    } else {
-        row = (size_t)b * a.Lmax + t0;
-    }
-    return cache + (row * a.Hkv + kvh) * a.D;
+    if (a.block_table)
+        return page_rows(cache, a, a.block_table[(size_t)b * a.max_blocks + (t0 >> a.page_shift)], kvh, t0);
+    return cache + (((size_t)b * a.Lmax + t0) * a.Hkv + kvh) * a.D;
 }
 
 // Attended length of a row, with seq_lens clamped to [0, Lmax].
