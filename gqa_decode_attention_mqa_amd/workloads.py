@@ -105,6 +105,16 @@ def poison_padding_(cache: torch.Tensor, seq_lens: torch.Tensor) -> torch.Tensor
     return cache
 
 
+def poison_positions_below_(cache: torch.Tensor, first: torch.Tensor) -> torch.Tensor:
+    """Overwrite positions < first[b] of a [B, Lmax, H, D] cache with bf16 NaN
+    (used to show that positions outside a sliding window are never read)."""
+    B, Lmax = cache.shape[0], cache.shape[1]
+    pos = torch.arange(Lmax, device=cache.device, dtype=torch.int32).view(1, Lmax)
+    below = (pos < first.to(cache.device).view(B, 1)).view(B, Lmax, 1, 1)
+    cache.view(torch.int16).masked_fill_(below, BF16_QNAN_BITS)
+    return cache
+
+
 def make_inputs(w: Workload, device="cpu", seed: int | None = None,
                 poison_padding: bool = False, seq_lens=None) -> dict:
     """Draw q, K, V (bf16) and seq_lens (int32) for workload ``w`` on ``device``.

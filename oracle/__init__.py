@@ -56,6 +56,10 @@ def _load():
             [ctypes.c_double, f64p]
         lib.oracle_decode_paged.restype = ctypes.c_int
         lib.oracle_causal_prefill.restype = ctypes.c_int
+        lib.oracle_decode_window.argtypes = [u16p, u16p, u16p, i32p] + [ctypes.c_int] * 6 + \
+            [ctypes.c_double, f64p]
+        lib.oracle_local_prefill.argtypes = [u16p, u16p, u16p, i32p] + [ctypes.c_int] * 6 + \
+            [ctypes.c_double, f64p]
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_set_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
@@ -161,4 +165,42 @@ def causal_prefill(q_seq, k_cache, v_cache, seq_lens, scale: float):
                                        B, Hq, Hkv, D, Lmax, float(scale), _ptr(out, ctypes.c_double))
     if rc != 0:
         raise ValueError("oracle_causal_prefill rejected its arguments (code %d)" % rc)
+    return out
+
+
+def decode_window(q, k_cache, v_cache, seq_lens, window: int, scale: float):
+    """fp64 decode step with a sliding window: sequence b attends positions
+    max(0, n - window) .. n - 1.  Shapes as :func:`decode`.  Returns ``out`` [B,Hq,D]."""
+    qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+    lens = _lens(seq_lens)
+    B, Hq, D = qb.shape
+    Bk, Lmax, Hkv, Dk = kb.shape
+    if vb.shape != kb.shape or Bk != B or Dk != D or lens.shape != (B,):
+        raise ValueError("inconsistent shapes q%s k%s v%s lens%s" % (qb.shape, kb.shape, vb.shape, lens.shape))
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = _load().oracle_decode_window(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+                                      _ptr(vb, ctypes.c_uint16), _ptr(lens, ctypes.c_int32),
+                                      B, Hq, Hkv, D, Lmax, int(window), float(scale),
+                                      _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_decode_window rejected its arguments (code %d)" % rc)
+    return out
+
+
+def local_prefill(q_seq, k_cache, v_cache, seq_lens, window: int, scale: float):
+    """fp64 sliding-window causal attention with no cache (row i attends
+    i - window < j <= i).  q_seq [B,Lmax,Hq,D] -> [B,Lmax,Hq,D]."""
+    qb, kb, vb = _bits(q_seq), _bits(k_cache), _bits(v_cache)
+    lens = _lens(seq_lens)
+    B, Lmax, Hq, D = qb.shape
+    Bk, Lk, Hkv, Dk = kb.shape
+    if vb.shape != kb.shape or (Bk, Lk, Dk) != (B, Lmax, D) or lens.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    out = np.empty((B, Lmax, Hq, D), dtype=np.float64)
+    rc = _load().oracle_local_prefill(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+                                      _ptr(vb, ctypes.c_uint16), _ptr(lens, ctypes.c_int32),
+                                      B, Hq, Hkv, D, Lmax, int(window), float(scale),
+                                      _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_local_prefill rejected its arguments (code %d)" % rc)
     return out

@@ -258,6 +258,149 @@ int oracle_decode_paged(const uint16_t *q, const uint16_t *k_pages,
 }
 
 /*
+ * One decode step with local (sliding-window) attention ("How To Scale Your
+ * Model", Part 7 "Transformer Inference", passage on mixing in local attention
+ * layers: local attention caps the context a token sees, its mask being a
+ * diagonal strip rather than a triangle).  A strip of width `window` seen from
+ * the newest position n-1 covers positions max(0, n - window) .. n-1, so for
+ * each (b, h), with lo = max(0, n - window):
+ *   s_j   = scale * sum_d q[b,h,d] * k[b,j,g,d]          for j in [lo, n)
+ *   out   = sum_{j in [lo, n)} softmax(s)_j * v[b,j,g,:]
+ * Positions below lo are never read.  window >= 1; shapes as oracle_decode.
+ * Returns 0, or a negative code on a bad shape, length or window.
+ */
+int oracle_decode_window(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const int32_t *seq_lens, int B, int Hq, int Hkv, int D,
+                         int Lmax, int window, double scale, double *out)
+{
+    int rc = check_shape(B, Hq, Hkv, D, Lmax);
+    if (rc) return rc;
+    if (window < 1) return -6;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || seq_lens[b] > Lmax) return -3;
+
+    const int G = Hq / Hkv;
+    const long long pairs = (long long)B * Hq;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < pairs; ++bh) {
+        const int b = (int)(bh / Hq);
+        const int h = (int)(bh % Hq);
+        const int g = h / G;
+        const int n = seq_lens[b];
+        const int lo = n > window ? n - window : 0;
+        double *o = out + ((size_t)b * Hq + h) * D;
+
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (n == 0) continue;
+
+        double *s = (double *)malloc((size_t)(n - lo) * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const uint16_t *qrow = q + ((size_t)b * Hq + h) * D;
+
+        /* logits of the positions inside the window; s[j - lo] is position j */
+        for (int j = lo; j < n; ++j) {
+            const uint16_t *krow = k + (((size_t)b * Lmax + j) * Hkv + g) * D;
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += bf16_bits_to_double(qrow[d]) * bf16_bits_to_double(krow[d]);
+            s[j - lo] = scale * acc;
+        }
+
+        double m = s[0];
+        for (int j = lo + 1; j < n; ++j)
+            if (s[j - lo] > m) m = s[j - lo];
+        double Z = 0.0;
+        for (int j = lo; j < n; ++j) {
+            s[j - lo] = exp(s[j - lo] - m);
+            Z += s[j - lo];
+        }
+
+        for (int j = lo; j < n; ++j) {
+            const uint16_t *vrow = v + (((size_t)b * Lmax + j) * Hkv + g) * D;
+            for (int d = 0; d < D; ++d)
+                o[d] += s[j - lo] * bf16_bits_to_double(vrow[d]);
+        }
+        for (int d = 0; d < D; ++d) o[d] /= Z;
+        free(s);
+    }
+    return failed ? -4 : 0;
+}
+
+/*
+ * Local (sliding-window) causal attention over whole sequences with no cache,
+ * as the pages describe it for training and prefill: the score matrix is
+ * masked to a diagonal strip of width `window` (row i keeps columns j with
+ * i - window < j <= i), then a row softmax and the product with V.  Written
+ * in the same masked full-matrix form as oracle_causal_prefill, independently
+ * of the decode loops.  Shapes as oracle_causal_prefill; rows i >= n are zero.
+ */
+int oracle_local_prefill(const uint16_t *q_seq, const uint16_t *k,
+                         const uint16_t *v, const int32_t *seq_lens, int B,
+                         int Hq, int Hkv, int D, int Lmax, int window,
+                         double scale, double *out_seq)
+{
+    int rc = check_shape(B, Hq, Hkv, D, Lmax);
+    if (rc) return rc;
+    if (window < 1) return -6;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || seq_lens[b] > Lmax) return -3;
+
+    const int G = Hq / Hkv;
+    const long long rows = (long long)B * Lmax * Hq;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long long r = 0; r < rows; ++r) {
+        const int h = (int)(r % Hq);
+        const int i = (int)((r / Hq) % Lmax);
+        const int b = (int)(r / ((long long)Hq * Lmax));
+        const int n = seq_lens[b];
+        double *o = out_seq + (size_t)r * D;
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (i >= n) continue;
+
+        const int kvh = h / G;
+        double *S = (double *)malloc((size_t)n * sizeof(double));
+        if (!S) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const uint16_t *qrow = q_seq + (size_t)r * D;
+        for (int j = 0; j < n; ++j) {
+            if (j > i || j <= i - window) { /* outside the strip */
+                S[j] = -INFINITY;
+                continue;
+            }
+            const uint16_t *krow = k + (((size_t)b * Lmax + j) * Hkv + kvh) * D;
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += bf16_bits_to_double(qrow[d]) * bf16_bits_to_double(krow[d]);
+            S[j] = scale * acc;
+        }
+        double rowmax = -INFINITY;
+        for (int j = 0; j < n; ++j)
+            if (S[j] > rowmax) rowmax = S[j];
+        double denom = 0.0;
+        for (int j = 0; j < n; ++j) denom += exp(S[j] - rowmax);
+        for (int j = 0; j < n; ++j) {
+            if (S[j] == -INFINITY) continue; /* masked entries: never touch their V */
+            const double p = exp(S[j] - rowmax) / denom;
+            const uint16_t *vrow = v + (((size_t)b * Lmax + j) * Hkv + kvh) * D;
+            for (int d = 0; d < D; ++d) o[d] += p * bf16_bits_to_double(vrow[d]);
+        }
+        free(S);
+    }
+    return failed ? -4 : 0;
+}
+
+/*
  * Full causal self-attention over a whole sequence, recomputed with no cache
  * (the work the KV cache avoids).
  *   q_seq   [B, Lmax, Hq, D]   bf16 bits: one query per position

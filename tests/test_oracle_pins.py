@@ -27,7 +27,8 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from gqa_decode_attention_mqa_amd.workloads import Workload, make_inputs, make_prefill_inputs, page_contiguous_cache
+from gqa_decode_attention_mqa_amd.workloads import (Workload, make_inputs, make_prefill_inputs, page_contiguous_cache,
+                                                    poison_positions_below_)
 
 TIGHT = 1e-12
 
@@ -381,3 +382,129 @@ def test_paged_oracle_rejects_bad_page_index():
     table[0, 1] = pg["num_pages"]  # one past the pool
     with pytest.raises(ValueError):
         oracle.decode_paged(inp["q"], pg["k_pages"], pg["v_pages"], table, inp["seq_lens"], inp["scale"])
+
+
+# ------------------------------------------------------ sliding-window (local) attention
+#
+# "How To Scale Your Model", Part 7, passage on mixing in local attention
+# layers: a local layer masks attention to a diagonal strip instead of a
+# triangle.  Decode with window W at length n attends max(0, n - W) .. n - 1.
+
+def _window_start(lens, window):
+    return torch.clamp(lens.to(torch.int64) - window, min=0).to(torch.int32)
+
+
+@pytest.mark.parametrize("window", [1, 2, 5, 16, 40, 1000])
+def test_window_decode_equals_full_decode_on_the_shifted_cache(window):
+    # Moving positions lo .. n-1 to the front and decoding the whole shorter
+    # cache must give the windowed result: pins the first attended position.
+    w = Workload("win-shift", B=4, Hq=8, Hkv=2, D=16, Lmax=40, seed=81, len_lo=0, len_hi=40)
+    inp = make_inputs(w, poison_padding=True)
+    lens = inp["seq_lens"]
+    out = oracle.decode_window(inp["q"], inp["k"], inp["v"], lens, window, inp["scale"])
+    lo = _window_start(lens, window)
+    ks, vs = torch.zeros_like(inp["k"]), torch.zeros_like(inp["v"])
+    for b in range(w.B):
+        n, a = int(lens[b]), int(lo[b])
+        ks[b, :n - a] = inp["k"][b, a:n]
+        vs[b, :n - a] = inp["v"][b, a:n]
+    ref = oracle.decode(inp["q"], ks, vs, lens - lo, inp["scale"])
+    np.testing.assert_allclose(out, ref, rtol=0, atol=TIGHT)
+
+
+def test_window_at_least_the_length_is_plain_decode():
+    w = Workload("win-wide", B=3, Hq=8, Hkv=1, D=32, Lmax=30, seed=82, len_lo=0, len_hi=30)
+    inp = make_inputs(w, poison_padding=True)
+    full = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    for window in (30, 31, 1 << 20):
+        out = oracle.decode_window(inp["q"], inp["k"], inp["v"], inp["seq_lens"], window, inp["scale"])
+        assert np.array_equal(out, full)
+
+
+def test_window_of_one_returns_the_newest_value_row_exactly():
+    w = Workload("win-one", B=4, Hq=6, Hkv=3, D=8, Lmax=12, seed=83, len_lo=1, len_hi=12)
+    inp = make_inputs(w, poison_padding=True)
+    out = oracle.decode_window(inp["q"], inp["k"], inp["v"], inp["seq_lens"], 1, inp["scale"])
+    for b in range(w.B):
+        n = int(inp["seq_lens"][b])
+        expect = f64(inp["v"][b, n - 1]).repeat_interleave(w.G, dim=0).numpy()
+        assert np.array_equal(out[b], expect)
+
+
+def test_positions_before_the_window_are_never_read():
+    w = Workload("win-nan", B=4, Hq=8, Hkv=2, D=16, Lmax=50, seed=84, len_lo=1, len_hi=50)
+    clean = make_inputs(w, poison_padding=True)
+    dirty = make_inputs(w, poison_padding=True)
+    lo = _window_start(dirty["seq_lens"], 9)
+    poison_positions_below_(dirty["k"], lo)
+    poison_positions_below_(dirty["v"], lo)
+    a = oracle.decode_window(clean["q"], clean["k"], clean["v"], clean["seq_lens"], 9, clean["scale"])
+    b = oracle.decode_window(dirty["q"], dirty["k"], dirty["v"], dirty["seq_lens"], 9, dirty["scale"])
+    assert np.isfinite(b).all() and np.array_equal(a, b)
+
+
+def brute_force_window(q, k, v, lens, window, scale):
+    qn, kn, vn = (f64(t).numpy() for t in (q, k, v))
+    B, Hq, D = qn.shape
+    G = Hq // kn.shape[2]
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        n = int(lens[b])
+        keep = [j for j in range(n) if j > n - 1 - window]  # the strip seen from row n - 1
+        for h in range(Hq):
+            if not keep:
+                continue
+            s = [scale * math.fsum(qn[b, h, d] * kn[b, j, h // G, d] for d in range(D)) for j in keep]
+            m = max(s)
+            wts = [math.exp(x - m) for x in s]
+            Z = math.fsum(wts)
+            for d in range(D):
+                out[b, h, d] = math.fsum(wt * vn[b, j, h // G, d] for wt, j in zip(wts, keep)) / Z
+    return out
+
+
+@pytest.mark.parametrize("seed,window", [(0, 1), (1, 3), (2, 4), (3, 7), (4, 8)])
+def test_window_brute_force_tiny(seed, window):
+    w = Workload("win-bf", B=3, Hq=4, Hkv=2, D=5, Lmax=9, seed=90 + seed, len_lo=0, len_hi=9)
+    inp = make_inputs(w, poison_padding=True)
+    out = oracle.decode_window(inp["q"], inp["k"], inp["v"], inp["seq_lens"], window, inp["scale"])
+    ref = brute_force_window(inp["q"], inp["k"], inp["v"], inp["seq_lens"], window, inp["scale"])
+    np.testing.assert_allclose(out, ref, rtol=0, atol=TIGHT)
+
+
+@pytest.mark.parametrize("window", [1, 4, 11])
+def test_local_prefill_matches_library_attention_with_a_band_mask(window):
+    B, Hq, Hkv, D, Lmax = 2, 8, 2, 16, 21
+    w = Workload("lpf", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, seed=95, len_lo=1, len_hi=Lmax)
+    inp = make_prefill_inputs(w, poison_padding=True)
+    out = oracle.local_prefill(inp["q_seq"], inp["k"], inp["v"], inp["seq_lens"], window, inp["scale"])
+    for b in range(B):
+        n = int(inp["seq_lens"][b])
+        i = torch.arange(n).view(n, 1)
+        j = torch.arange(n).view(1, n)
+        band = (j <= i) & (j > i - window)                     # True = attend
+        qb = f64(inp["q_seq"][b, :n]).permute(1, 0, 2).unsqueeze(0)
+        kb = f64(inp["k"][b, :n]).permute(1, 0, 2).unsqueeze(0)
+        vb = f64(inp["v"][b, :n]).permute(1, 0, 2).unsqueeze(0)
+        ref = F.scaled_dot_product_attention(qb, kb, vb, attn_mask=band, scale=inp["scale"], enable_gqa=True)
+        np.testing.assert_allclose(out[b, :n], ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=TIGHT)
+        assert np.array_equal(out[b, n:], np.zeros_like(out[b, n:]))
+
+
+@pytest.mark.parametrize("window", [1, 6, 13, 64])
+def test_window_decode_equals_last_row_of_local_attention(window):
+    w = Workload("win-eq", B=4, Hq=12, Hkv=3, D=16, Lmax=26, seed=96, len_lo=1, len_hi=26)
+    inp = make_prefill_inputs(w, poison_padding=True)
+    full = oracle.local_prefill(inp["q_seq"], inp["k"], inp["v"], inp["seq_lens"], window, inp["scale"])
+    lens = inp["seq_lens"]
+    q_last = torch.stack([inp["q_seq"][b, int(lens[b]) - 1] for b in range(w.B)])
+    dec = oracle.decode_window(q_last, inp["k"], inp["v"], lens, window, inp["scale"])
+    for b in range(w.B):
+        np.testing.assert_allclose(dec[b], full[b, int(lens[b]) - 1], rtol=0, atol=TIGHT)
+
+
+def test_window_oracle_rejects_a_window_below_one():
+    w = Workload("win-bad", B=1, Hq=2, Hkv=1, D=4, Lmax=4, seed=97)
+    inp = make_inputs(w)
+    with pytest.raises(ValueError):
+        oracle.decode_window(inp["q"], inp["k"], inp["v"], inp["seq_lens"], 0, inp["scale"])
