@@ -6,8 +6,8 @@ combine kernel when sequences are split), inputs resident in HBM.  Default
 workload: PaLM-540B-shaped MQA decode (B=64, Hq=48, Hkv=1, D=256, len 2048).
 
 To keep the memory-side Infinity Cache (256 MB) from serving repeated reads,
-the timed loop rotates through enough distinct q/K/V sets to cover at least
-768 MiB, so every step reads its K/V from HBM.
+the timed loop rotates through enough distinct q/K/V sets that the K/V bytes
+the steps read cover at least 768 MiB, so every step reads its K/V from HBM.
 
 Prints ONE JSON line (rank 0, N=1):
   value        decode steps per second over the timed steps
@@ -78,6 +78,9 @@ def parse_args(argv=None):
     ap.add_argument("--page-size", type=int, default=0,
                     help="run the paged-cache entry point on a pool of pages of this many positions "
                          "(a power of two >= 32; the pool holds the used pages only); 0 = contiguous cache")
+    ap.add_argument("--window", type=int, default=0,
+                    help="local (sliding-window) attention: each sequence attends its last WINDOW positions; "
+                         "0 = every cached position")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -96,32 +99,36 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 5}))
 
 
-def cpu_baseline(w, inp, target_s: float):
+def cpu_baseline(w, inp, target_s: float, window: int = 0):
     """The oracle, as it stands, on whole decode steps of set 0 (or a prefix of the batch)."""
     import oracle
     q, k, v, lens = inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu()
     threads = oracle.max_threads()
+    if window:
+        run = lambda qq, kk, vv, ll: oracle.decode_window(qq, kk, vv, ll, window, inp["scale"])
+    else:
+        run = lambda qq, kk, vv, ll: oracle.decode(qq, kk, vv, ll, inp["scale"])
     # time one sequence first to size the sample
     t0 = time.perf_counter()
-    oracle.decode(q[:1], k[:1], v[:1], lens[:1], inp["scale"])
+    run(q[:1], k[:1], v[:1], lens[:1])
     one = max(time.perf_counter() - t0, 1e-6)
-    per_seq_lens = lens.double()
+    per_seq_lens = lens.double().clamp(max=window) if window else lens.double()
     # sequences to run: whole steps when they fit in the budget, else a prefix of the batch
     est_step = one * float(per_seq_lens.sum()) / max(float(per_seq_lens[0]), 1.0)
     if est_step <= target_s:
         reps = max(1, int(target_s / max(est_step, 1e-6)))
         t0 = time.perf_counter()
         for _ in range(reps):
-            oracle.decode(q, k, v, lens, inp["scale"])
+            run(q, k, v, lens)
         dt = time.perf_counter() - t0
         steps = reps
         sample = "%d whole decode step(s) of the %s workload (B=%d)" % (reps, w.name, w.B)
     else:
         nseq = max(1, int(w.B * target_s / est_step))
         t0 = time.perf_counter()
-        oracle.decode(q[:nseq], k[:nseq], v[:nseq], lens[:nseq], inp["scale"])
+        run(q[:nseq], k[:nseq], v[:nseq], lens[:nseq])
         dt = time.perf_counter() - t0
-        steps = float(lens[:nseq].double().sum() / lens.double().sum())
+        steps = float(per_seq_lens[:nseq].sum() / per_seq_lens.sum())
         sample = "first %d of %d sequences of one %s decode step, scaled by their share of positions" % (
             nseq, w.B, w.name)
     return {"value": steps / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
@@ -150,13 +157,16 @@ def main(argv=None):
 
     base = make_inputs(w, device=dev)
     lens = base["seq_lens"]
-    set_bytes = 2 * w.B * w.Lmax * w.Hkv * w.D * 2
-    nsets = min(MAX_SETS, max(1, math.ceil(MALL_DEFEAT_BYTES / set_bytes)))
+    # positions attended: all of them, or the last `window` of each sequence
+    attended = [min(n, args.window) if args.window else n for n in lens.cpu().tolist()]
+    set_bytes = decode_step_kv_bytes(attended, w.Hkv, w.D)  # bytes one step reads from a set
+    nsets = min(MAX_SETS, max(1, math.ceil(MALL_DEFEAT_BYTES / max(set_bytes, 1))))
     sets = [base] + [make_inputs(w, device=dev, seed=w.seed + 1000 * i, seq_lens=lens) for i in range(1, nsets)]
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
-    plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk, args.combine)
+    plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk, args.combine,
+                        window=args.window)
 
     calls = []
     if args.page_size:
@@ -184,7 +194,7 @@ def main(argv=None):
         if st != 0:
             raise RuntimeError("decode failed: %s" % lib.mqa_last_error().decode())
 
-    plain = binding.make_opts(args.variant, args.chunk, args.combine)
+    plain = binding.make_opts(args.variant, args.chunk, args.combine, window=args.window)
     for i in range(args.warmup):
         step(i, plain)
     torch.cuda.synchronize()
@@ -201,7 +211,7 @@ def main(argv=None):
         e.record(stream)
     opts = [plain] * args.steps
     for i, (b, e) in zip(sampled, evs):
-        opts[i] = binding.make_opts(args.variant, args.chunk, args.combine, b.cuda_event, e.cuda_event)
+        opts[i] = binding.make_opts(args.variant, args.chunk, args.combine, b.cuda_event, e.cuda_event, args.window)
     t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_begin.record(stream)
@@ -216,9 +226,10 @@ def main(argv=None):
     median_kern_ms = kern_ms[len(kern_ms) // 2]
 
     ms_per_step = total_ms / args.steps
-    kv_bytes = decode_step_kv_bytes(lens.cpu().tolist(), w.Hkv, w.D)
+    kv_bytes = decode_step_kv_bytes(attended, w.Hkv, w.D)
     achieved = kv_bytes / (mean_kern_ms * 1e-3) / 1e9
-    traffic = read_traffic(w.name + ("_paged%d" % args.page_size if args.page_size else ""))
+    traffic = read_traffic(w.name + ("_paged%d" % args.page_size if args.page_size else "")
+                           + ("_window%d" % args.window if args.window else ""))
 
     result = {
         "metric": "decode-attention steps/sec and achieved HBM GB/s (% of MI355X peak)",
@@ -235,10 +246,13 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": w.description + (" (paged cache, %d-position pages)" % args.page_size
-                                         if args.page_size else ""),
+                                         if args.page_size else "")
+                        + (" (sliding window of %d positions)" % args.window if args.window else ""),
             "page_size": args.page_size or None,
+            "window": args.window or None,
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "Lmax": w.Lmax,
             "seq_lens_sum": int(lens.sum().item()),
+            "attended_positions": int(sum(attended)),
             "kv_bytes_per_step": kv_bytes,
             "buffer_sets_rotated": nsets,
             "plan": plan,
@@ -258,7 +272,8 @@ def main(argv=None):
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, cpu_set if cpu_set is not None else base, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, cpu_set if cpu_set is not None else base, args.cpu_seconds,
+                                              args.window)
     print(json.dumps(result), flush=True)
     return 0
 

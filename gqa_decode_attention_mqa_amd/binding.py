@@ -32,7 +32,8 @@ class MqaError(RuntimeError):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("chunk", ctypes.c_int), ("combine", ctypes.c_int),
-                ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p)]
+                ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p),
+                ("window", ctypes.c_int)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -61,6 +62,8 @@ def load_library():
     lib.mqa_decode_attention_paged.argtypes = [vp, vp, vp, i32p, i32p, f32p] + [ctypes.c_int] * 7 + \
         [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
     lib.mqa_decode_attention_paged.restype = ctypes.c_int
+    lib.mqa_decode_attention_window.argtypes = [vp, vp, vp, i32p, f32p] + ints + [ctypes.c_int, ctypes.c_float, vp]
+    lib.mqa_decode_attention_window.restype = ctypes.c_int
     lib.mqa_decode_attention_ex.argtypes = [vp, vp, vp, i32p, f32p] + ints + \
         [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
     lib.mqa_decode_attention_ex.restype = ctypes.c_int
@@ -93,8 +96,9 @@ def _check(status: int, where: str):
                                                    lib.mqa_last_error().decode()))
 
 
-def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None) -> DecodeOpts:
+def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None, window=None) -> DecodeOpts:
     o = DecodeOpts()
+    o.window = int(window or 0)
     o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant or 0)
     o.chunk = int(chunk or 0)
     o.combine = COMBINE[combine] if isinstance(combine, str) else int(combine or 0)
@@ -103,11 +107,11 @@ def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None
     return o
 
 
-def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None) -> dict:
+def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None, window=None) -> dict:
     """The library's launch plan for a decode call of this shape (host only)."""
     lib = load_library()
     info = PlanInfo()
-    opts = make_opts(variant, chunk, combine)
+    opts = make_opts(variant, chunk, combine, window=window)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.mqa_decode_plan(B, Hq, Hkv, D, Lmax, sc, ctypes.byref(opts), ctypes.byref(info)),
            "mqa_decode_plan")
@@ -136,11 +140,12 @@ def _require(t: torch.Tensor, name: str, dtype, ndim: int, device):
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
            scale: float | None = None, out: torch.Tensor | None = None, variant=None, chunk=None,
-           combine=None, events=None) -> torch.Tensor:
+           combine=None, events=None, window=None) -> torch.Tensor:
     """One decode step.  q [B,Hq,D] bf16, caches [B,Lmax,Hkv,D] bf16, seq_lens [B] int32 -> fp32 [B,Hq,D].
 
     Runs on torch's current stream of q's device.  ``events`` = (begin, end)
-    torch.cuda.Event pair recorded around the split-K kernel alone.
+    torch.cuda.Event pair recorded around the split-K kernel alone.  ``window``
+    (> 0) restricts each sequence to its last ``window`` positions.
     """
     if q.device.type != "cuda":
         raise ValueError("decode runs on the GPU; q is on %s" % q.device)
@@ -163,7 +168,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
     ev_b = ev_e = None
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
-    opts = make_opts(variant, chunk, combine, ev_b, ev_e)
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window)
     lib = load_library()
     st = lib.mqa_decode_attention_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                      seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D, Lmax,
@@ -174,7 +179,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
 
 def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
                  seq_lens: torch.Tensor, scale: float | None = None, out: torch.Tensor | None = None,
-                 variant=None, chunk=None, combine=None, events=None) -> torch.Tensor:
+                 variant=None, chunk=None, combine=None, events=None, window=None) -> torch.Tensor:
     """One decode step over a paged cache.  q [B,Hq,D] bf16, pages [num_pages,page_size,Hkv,D] bf16,
     block_table [B,max_blocks] int32, seq_lens [B] int32 -> fp32 [B,Hq,D]."""
     if q.device.type != "cuda":
@@ -197,13 +202,43 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
     ev_b = ev_e = None
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
-    opts = make_opts(variant, chunk, combine, ev_b, ev_e)
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window)
     lib = load_library()
     st = lib.mqa_decode_attention_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                                         block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                                         B, Hq, Hkv, D, num_pages, page_size, block_table.shape[1],
                                         sc, _stream_ptr(dev), ctypes.byref(opts))
     _check(st, "mqa_decode_attention_paged")
+    return out
+
+
+def decode_window(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                  window: int, scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step with a sliding window through ``mqa_decode_attention_window``:
+    sequence b attends its last ``window`` positions.  Shapes as :func:`decode`."""
+    if q.device.type != "cuda":
+        raise ValueError("decode_window runs on the GPU; q is on %s" % q.device)
+    dev = q.device
+    _require(q, "q", torch.bfloat16, 3, dev)
+    _require(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _require(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _require(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    Bk, Lmax, Hkv, Dk = k_cache.shape
+    if v_cache.shape != k_cache.shape or Bk != B or Dk != D or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch: q %s, k %s, v %s, seq_lens %s" % (
+            tuple(q.shape), tuple(k_cache.shape), tuple(v_cache.shape), tuple(seq_lens.shape)))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, 3, dev)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must have shape %s" % ((B, Hq, D),))
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    lib = load_library()
+    st = lib.mqa_decode_attention_window(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                         seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D, Lmax,
+                                         int(window), sc, _stream_ptr(dev))
+    _check(st, "mqa_decode_attention_window")
     return out
 
 

@@ -136,6 +136,7 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.chunk = plan.chunk;
     a.max_splits = plan.max_splits;
     a.causal = causal ? 1 : 0;
+    a.window = plan.window;
     a.qk_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
     hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->ev_main_begin) : nullptr;
@@ -160,6 +161,7 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
         c.chunk = plan.chunk;
         c.max_splits = plan.max_splits;
         c.causal = a.causal;
+        c.window = a.window;
         e = mqa::launch_combine(plan, c, stream);
         if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
     }
@@ -181,6 +183,18 @@ mqa_status mqa_decode_attention_ex(const void* q, const void* k_cache, const voi
                                    int D, int Lmax, float scale, void* stream,
                                    const mqa_decode_opts* opts) {
     return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false);
+}
+
+mqa_status mqa_decode_attention_window(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
+                                       int D, int Lmax, int window, float scale, void* stream) {
+    if (window < 1) {
+        mqa::set_error("window must be >= 1");
+        return MQA_ERR_ARG;
+    }
+    mqa_decode_opts o{};
+    o.window = window;
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, false);
 }
 
 mqa_status mqa_decode_attention_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -254,6 +268,6 @@ void mqa_release_workspaces(void) {
     g_ws.clear();
 }
 
-int mqa_version(void) { return 110; }
+int mqa_version(void) { return 120; }
 
 }  // extern "C"

@@ -150,10 +150,11 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
     b = __builtin_amdgcn_readfirstlane(b);
     len = __builtin_amdgcn_readfirstlane(len);
-    const int p0 = s * a.chunk;
-    if (s > 0 && p0 >= len) return;  // whole workgroup: this chunk is past the end
-    const int p1 = min(p0 + a.chunk, len);
-    const int nsplit = len > 0 ? (len + a.chunk - 1) / a.chunk : 1;
+    const ChunkSpan span = chunk_span(a.window, a.chunk, len, s);
+    if (s > 0 && span.p0 >= len) return;  // whole workgroup: this chunk is past the end
+    // Sliding window: rows lo - 32 < t < lo of the first tile lie before it;
+    // they are loaded as zeros and masked.
+    const int lo = span.lo, p0 = span.p0, p1 = span.p1, nsplit = span.nsplit;
     const int ntiles = p1 > p0 ? (p1 - p0 + C::STEP - 1) / C::STEP : 0;
 
     const size_t pos_stride = (size_t)a.Hkv * D;
@@ -203,6 +204,7 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         if (w < NG) return;
         const int t0 = p0 + tile * C::STEP;
         const int rows = max(0, min(C::STEP, p1 - t0));
+        const int skip = lo - t0;  // rows before a sliding window (> 0 in the first tile only)
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows > 0 ? tile_rows(a.k, t0) : a.k, rows * rowbytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows > 0 ? tile_rows(a.v, t0) : a.v, rows * rowbytes);
         unsigned char* slot = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
             const int jj = (w - NG) + C::NL * i;
             const int p = jj * 64 + lane;  // 16-byte LDS slot in the tile
             const int t = p / C::CPR, cs = p % C::CPR;
-            const int voff = t * rowbytes + ((cs ^ swz_key(t)) * 16);
+            const int voff = t < skip ? kOutOfRange : t * rowbytes + ((cs ^ swz_key(t)) * 16);
             unsigned char* dst = slot + jj * 1024;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)dst, 16, voff, 0, 0, kCachePolicyNT);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dst + C::TILE_BYTES), 16, voff, 0, 0,
@@ -267,12 +269,14 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
             for (int r = 0; r < 4; ++r) sacc[mq][r] *= qk;
-        if (st + C::STEP > p1) {
+        if (st + C::STEP > p1 || st < lo) {
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sacc[mq][r] = (st + 16 * mq + 4 * kg + r < p1) ? sacc[mq][r] : -INFINITY;
+                for (int r = 0; r < 4; ++r) {
+                    const int t = st + 16 * mq + 4 * kg + r;
+                    sacc[mq][r] = (t < p1 && t >= lo) ? sacc[mq][r] : -INFINITY;
+                }
         }
         float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                          fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));

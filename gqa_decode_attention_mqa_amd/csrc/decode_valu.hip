@@ -78,10 +78,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     // descriptors built from them) in scalar registers.
     b = __builtin_amdgcn_readfirstlane(b);
     len = __builtin_amdgcn_readfirstlane(len);
-    const int p0 = s * a.chunk;
-    if (s > 0 && p0 >= len) return;
-    const int p1 = min(p0 + a.chunk, len);
-    const int nsplit = len > 0 ? (len + a.chunk - 1) / a.chunk : 1;
+    const ChunkSpan span = chunk_span(a.window, a.chunk, len, s);
+    if (s > 0 && span.p0 >= len) return;
+    // Blocks start at the block holding the first attended position (a
+    // multiple of WB, which divides 32), so every block has a valid row.
+    const int lo = span.lo;
+    const int p0 = max(span.p0, lo & ~(WB - 1));
+    const int p1 = span.p1;
+    const int nsplit = span.nsplit;
 
     // q for this lane's 8 columns of every head in the block, as bf16 pairs.
     uint32_t qv[GB][4];
@@ -114,26 +118,31 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const int nblk = p1 > p0 ? (p1 - p0 + WB - 1) / WB : 0;
     // Issue the loads of block `blk` (of this wave's blocks w, w + NW, ...).
     // The buffer range ends at the last valid row: rows past it, and whole
-    // blocks past the chunk, read as zero without a memory access.
+    // blocks past the chunk, read as zero without a memory access; so do rows
+    // before a sliding window's first position (out-of-range offsets).
     auto load_block = [&](int blk, u32x4_t (&kr)[NB], u32x4_t (&vr)[NB]) {
         const int t0 = p0 + blk * WB;
         const int rows = max(0, min(WB, p1 - t0));
+        const int skip = lo - t0;  // rows of the block before the window (> 0 in its first block only)
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows > 0 ? kv_rows(a.k, a, b, kvh, t0) : a.k, rows * rowbytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows > 0 ? kv_rows(a.v, a, b, kvh, t0) : a.v, rows * rowbytes);
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
-            kr[st] = buffer_load_u32x4(krs, off[st]);
-            vr[st] = buffer_load_u32x4(vrs, off[st]);
+            const int o = st * RS + rr < skip ? kOutOfRange : off[st];
+            kr[st] = buffer_load_u32x4(krs, o);
+            vr[st] = buffer_load_u32x4(vrs, o);
         }
     };
     auto compute_block = [&](int blk, const u32x4_t (&kr)[NB], const u32x4_t (&vr)[NB]) {
-        const int rows = min(WB, p1 - (p0 + blk * WB));
-        // logits (base-2 units), masked past the end
-        const bool tail = rows < WB;
+        const int t0 = p0 + blk * WB;
+        const int rows = min(WB, p1 - t0);
+        const int skip = lo - t0;
+        // logits (base-2 units), masked outside [lo, p1)
+        const bool edge = rows < WB || skip > 0;
         float sc[NB][GB];
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
-            const bool ok = !tail || st * RS + rr < rows;
+            const bool ok = !edge || (st * RS + rr < rows && st * RS + rr >= skip);
 #pragma unroll
             for (int gg = 0; gg < GB; ++gg) {
                 float acc = 0.f;

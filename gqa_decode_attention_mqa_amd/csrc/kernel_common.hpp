@@ -39,6 +39,7 @@ struct DecodeArgs {
     int Hq, Hkv, D, Lmax, G;
     int chunk, max_splits;
     int causal;                // 0 decode, 1 causal rows
+    int window;                // > 0: sliding window, a row of length n attends n-window .. n-1
     int fused;                 // 1: the last chunk of a unit merges the partials itself
     float qk_log2;             // scale * log2(e): logits are kept in base-2 units
 };
@@ -51,7 +52,33 @@ struct CombineArgs {
     int Hq, Hkv, D, Lmax, G;
     int chunk, max_splits;
     int causal;
+    int window;
 };
+
+// Buffer offset that lies past the range of every tile descriptor (a tile spans
+// at most 32 rows of at most 2^24 bytes): a load from it returns zero and
+// touches no memory.
+constexpr int kOutOfRange = 0x40000000;
+
+// Positions covered by chunk s of a row that attends `len` positions.  Without
+// a window, chunk s is [s * chunk, (s + 1) * chunk) cut at len.  With a window
+// of W positions (local attention: the row sees only its last W positions) the
+// first attended position is lo = len - W; the chunks then start at lo rounded
+// down to a multiple of 32, so tiles and pages keep their alignment, and the
+// kernels read positions below lo as zero and mask them.  nsplit is the number
+// of chunks that hold positions (1 for an empty row).
+struct ChunkSpan {
+    int lo, p0, p1, nsplit;
+};
+__device__ __forceinline__ ChunkSpan chunk_span(int window, int chunk, int len, int s) {
+    ChunkSpan c;
+    c.lo = (window > 0 && len > window) ? len - window : 0;
+    const int base = c.lo & ~31;
+    c.p0 = base + s * chunk;
+    c.p1 = min(c.p0 + chunk, len);
+    c.nsplit = len > base ? (len - base + chunk - 1) / chunk : 1;
+    return c;
+}
 
 // Base of the cache rows t0, t0 + 1, ... of kv head kvh of sequence b; the
 // rows a caller reads from it never straddle a page (pages hold a power of two

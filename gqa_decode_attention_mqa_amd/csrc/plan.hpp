@@ -43,7 +43,9 @@ struct Plan {
     int heads_per_block = 0;         // padded heads a workgroup serves
     int head_blocks = 1;             // workgroups per (row, kv head, chunk) along heads
     int chunk = 0;                   // positions per split
-    int max_splits = 1;              // ceil(Lmax / chunk), >= 1
+    int max_splits = 1;              // ceil(span / chunk), >= 1 (span: Lmax, or
+                                     // min(Lmax, window + 31) with a sliding window)
+    int window = 0;                  // sliding window (0 = none)
     int combine = 0;                 // 0 none, 1 separate kernel, 2 fused
     long long rows = 0;              // query rows: B (decode) or B * Lmax (prefill)
     long long grid_main = 0;         // workgroups along x of the split kernel

@@ -89,13 +89,18 @@ typedef struct mqa_decode_opts {
     void *ev_main_begin;  /* optional hipEvent_t pair recorded by the split-K kernel's own
                              dispatch (hipExtLaunchKernelGGL) at its start and end, so  */
     void *ev_main_end;    /* their interval is that kernel's execution time alone      */
+    int window;           /* 0 = attend every cached position; W > 0 = local (sliding-
+                             window) attention: a sequence of length n attends positions
+                             max(0, n - W) .. n-1 only, and earlier positions are never
+                             read (see mqa_decode_attention_window); < 0 is MQA_ERR_ARG  */
 } mqa_decode_opts;
 
 /* What the planner decided for a shape (host-only query, no HIP call). */
 typedef struct mqa_plan_info {
     int variant;              /* MQA_VARIANT_VALU or MQA_VARIANT_MFMA                  */
     int chunk;                /* positions per split-K chunk                           */
-    int max_splits;           /* ceil(Lmax / chunk), at least 1                        */
+    int max_splits;           /* chunks per sequence: ceil(span / chunk), at least 1, where
+                                 span = Lmax, or min(Lmax, window + 31) with a window  */
     int combine;              /* 1 = separate kernel, 2 = fused, 0 = none needed       */
     int head_blocks;          /* query-head blocks per kv head (VALU path: ceil(G/8))  */
     long long grid_main;      /* workgroups of the split-K kernel                      */
@@ -124,6 +129,27 @@ mqa_status mqa_decode_attention_ex(const void *q, const void *k_cache, const voi
                                    const int32_t *seq_lens, float *out, int B, int Hq,
                                    int Hkv, int D, int Lmax, float scale, void *stream,
                                    const mqa_decode_opts *opts);
+
+/*
+ * One decode step with local (sliding-window) attention ("How To Scale Your
+ * Model", Part 7 "Transformer Inference", passage on mixing in local attention
+ * layers: a local layer caps the context a token sees, its attention mask
+ * being a diagonal strip of fixed width instead of a triangle).  Seen from the
+ * newest position n-1 the strip holds the last `window` positions, so
+ * sequence b attends positions max(0, n - window) .. n-1 with n = seq_lens[b]:
+ *
+ *     out[b,h,:] = sum_{j = max(0, n-window)}^{n-1} softmax(s)_j * v_cache[b,j,g,:]
+ *
+ * Positions before the window are never read and may hold anything.  The
+ * work and the bytes read are those of min(n, window) positions per sequence.
+ * window must be >= 1 (MQA_ERR_ARG otherwise); a window of at least Lmax is
+ * the plain decode step.  Other arguments, errors and ownership as for
+ * mqa_decode_attention.  The same window is available on the other decode
+ * calls through mqa_decode_opts.window.
+ */
+mqa_status mqa_decode_attention_window(const void *q, const void *k_cache, const void *v_cache,
+                                       const int32_t *seq_lens, float *out, int B, int Hq, int Hkv,
+                                       int D, int Lmax, int window, float scale, void *stream);
 
 /*
  * One decode step over a paged KV cache.  Instead of one contiguous

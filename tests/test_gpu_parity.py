@@ -21,7 +21,7 @@ import torch
 import oracle
 from gqa_decode_attention_mqa_amd import binding
 from gqa_decode_attention_mqa_amd.workloads import (WORKLOADS, Workload, make_inputs, make_prefill_inputs,
-                                                    page_contiguous_cache)
+                                                    page_contiguous_cache, poison_positions_below_)
 
 pytestmark = pytest.mark.gpu
 
@@ -302,6 +302,85 @@ def test_paged_full_size_ragged_sampled():
                               pg["scale"])
     err = check_close(out.index_select(0, sel), ref, "paged ragged")
     print("full paged ragged: %d sequences checked, max abs err %.3g" % (len(idx), err), flush=True)
+
+
+# ------------------------------------------------------ sliding window (local attention)
+
+def window_inputs(w: Workload, window: int):
+    """Seeded inputs whose positions before each sequence's window (and past its end) hold NaN."""
+    inp = make_inputs(w, poison_padding=True)
+    lo = torch.clamp(inp["seq_lens"].to(torch.int64) - window, min=0).to(torch.int32)
+    poison_positions_below_(inp["k"], lo)
+    poison_positions_below_(inp["v"], lo)
+    return inp
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("window", [1, 31, 32, 33, 100, 333, 999])
+@pytest.mark.parametrize("G,Hkv,D", [(8, 2, 128), (4, 2, 64), (48, 1, 256), (2, 3, 128)])
+def test_window_matches_window_oracle(variant, window, G, Hkv, D):
+    w = Workload("win", B=6, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=1000, seed=500 + window + D + G,
+                 len_lo=0, len_hi=1000)
+    inp = window_inputs(w, window)
+    ref = oracle.decode_window(inp["q"], inp["k"], inp["v"], inp["seq_lens"], window, inp["scale"])
+    dev = to_dev(inp)
+    for chunk, combine in ((None, None), (128, "separate"), (128, "fused")):
+        print("case window", variant, window, G, Hkv, D, chunk, combine, flush=True)
+        out = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant,
+                             chunk=chunk, combine=combine, window=window)
+        torch.cuda.synchronize()
+        check_close(out, ref, "window %d %s G %d D %d chunk %s %s" % (window, variant, G, D, chunk, combine))
+
+
+def test_window_entry_point_and_wide_window():
+    """mqa_decode_attention_window agrees with the option form bit for bit, and a
+    window of at least Lmax gives the plain decode step's bits."""
+    w = Workload("win-ep", B=5, Hq=32, Hkv=8, D=128, Lmax=900, seed=520, len_lo=0, len_hi=900)
+    dev = to_dev(make_inputs(w, poison_padding=True))
+    a = binding.decode_window(dev["q"], dev["k"], dev["v"], dev["seq_lens"], 257, dev["scale"])
+    b = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], window=257)
+    full = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"])
+    wide = binding.decode_window(dev["q"], dev["k"], dev["v"], dev["seq_lens"], 900, dev["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(full, wide)
+    ref = oracle.decode_window(dev["q"].cpu(), dev["k"].cpu(), dev["v"].cpu(), dev["seq_lens"].cpu(), 257,
+                               dev["scale"])
+    check_close(a, ref, "window entry point")
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("page_size,window", [(32, 45), (64, 64), (128, 500)])
+def test_window_on_a_paged_cache(variant, page_size, window):
+    w = Workload("win-pg", B=5, Hq=16, Hkv=2, D=128, Lmax=1000, seed=530 + page_size, len_lo=0, len_hi=1000)
+    inp = window_inputs(w, window)
+    ref = oracle.decode_window(inp["q"], inp["k"], inp["v"], inp["seq_lens"], window, inp["scale"])
+    pg = to_dev(page_contiguous_cache(inp, page_size, seed=page_size, spare_pages=2))
+    for chunk in (None, 128):
+        print("case window paged", variant, page_size, window, chunk, flush=True)
+        out = binding.decode_paged(pg["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], pg["seq_lens"],
+                                   pg["scale"], variant=variant, chunk=chunk, window=window)
+        torch.cuda.synchronize()
+        check_close(out, ref, "window paged %s page %d W %d chunk %s" % (variant, page_size, window, chunk))
+
+
+@pytest.mark.parametrize("name,window", [("ragged", 4096), ("palm", 1024)])
+def test_window_full_size_sampled(name, window):
+    w = WORKLOADS[name]
+    print("case full window", name, window, flush=True)
+    inp = make_inputs(w, device=DEV, poison_padding=w.ragged)
+    lo = torch.clamp(inp["seq_lens"].to(torch.int64) - window, min=0).to(torch.int32)
+    poison_positions_below_(inp["k"], lo)
+    poison_positions_below_(inp["v"], lo)
+    out = binding.decode_window(inp["q"], inp["k"], inp["v"], inp["seq_lens"], window, inp["scale"])
+    torch.cuda.synchronize()
+    idx = sample_indices(inp["seq_lens"], SAMPLES[name])
+    sel = torch.tensor(idx, device=DEV)
+    ref = oracle.decode_window(inp["q"].index_select(0, sel).cpu(), inp["k"].index_select(0, sel).cpu(),
+                               inp["v"].index_select(0, sel).cpu(), inp["seq_lens"].index_select(0, sel).cpu(),
+                               window, inp["scale"])
+    err = check_close(out.index_select(0, sel), ref, "%s window %d" % (name, window))
+    print("full %s window %d: %d sequences checked, max abs err %.3g" % (name, window, len(idx), err), flush=True)
 
 
 # ------------------------------------------------------ full-size workloads

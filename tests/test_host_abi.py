@@ -140,6 +140,53 @@ def test_chunk_schedule_covers_every_valid_position_once():
         assert seen == list(range(n))
 
 
+@pytest.mark.parametrize("window", [1, 31, 32, 33, 100, 1000, 4096, 8191, 8192, 9000])
+def test_window_schedule_covers_the_window_once(window):
+    """With a window W the split kernels start chunk s at base + s*chunk, where
+    base is the first attended position lo = max(0, n - W) rounded down to a
+    multiple of 32, and mask positions below lo.  Every position of [lo, n)
+    must fall in exactly one chunk s < max_splits, chunk starts must stay
+    32-aligned (tiles and pages), and the plan's splits must bound the span."""
+    Lmax = 8192
+    p = binding.plan(256, 32, 8, 128, Lmax, window=window)
+    C, S = p["chunk"], p["max_splits"]
+    assert S == -(-min(Lmax, window + 31) // C)
+    for n in sorted({0, 1, 31, 32, 33, window - 1, window, window + 1, window + 31, window + 32,
+                     Lmax - 33, Lmax - 1, Lmax} & set(range(0, Lmax + 1))):
+        lo = max(0, n - window)
+        base = lo & ~31
+        nsplit = -(-(n - base) // C) if n > base else 1
+        assert nsplit <= S
+        seen = []
+        for s in range(S):
+            p0 = base + s * C
+            assert p0 % 32 == 0
+            if s > 0 and p0 >= n:
+                continue
+            assert s < nsplit or n == 0
+            seen.extend(t for t in range(p0, min(p0 + C, n)) if t >= lo)
+        assert seen == list(range(lo, n))
+
+
+def test_window_arguments():
+    assert lib.mqa_decode_attention_window(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 0, 0.1, None) == ERR_ARG
+    assert lib.mqa_decode_attention_window(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, -5, 0.1, None) == ERR_ARG
+    assert b"window" in lib.mqa_last_error()
+    with pytest.raises(binding.MqaError):
+        binding.plan(2, 8, 2, 128, 64, window=-1)
+    # a window of at least Lmax plans exactly like no window
+    assert binding.plan(8, 32, 8, 128, 4096, window=4096) == binding.plan(8, 32, 8, 128, 4096)
+    assert binding.plan(8, 32, 8, 128, 4096, window=1 << 30) == binding.plan(8, 32, 8, 128, 4096)
+    assert binding.plan(2, 8, 1, 64, 600, window=600) == binding.plan(2, 8, 1, 64, 600)
+    # chunks sized for the window itself: PaLM-shaped batch, W = 1024 -> 256-position chunks
+    # (four per window, plus one for the alignment slack)
+    p = binding.plan(64, 48, 1, 256, 2048, window=1024)
+    assert p["chunk"] == 256 and p["max_splits"] == 5
+    # the window bounds the grid: 8 chunks of 512 without it, at most 2 with W = 512
+    assert binding.plan(64, 48, 1, 256, 4096, chunk=512)["max_splits"] == 8
+    assert binding.plan(64, 48, 1, 256, 4096, chunk=512, window=512)["max_splits"] == 2
+
+
 def paged_call(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, D=128,
                num_pages=16, page_size=64, max_blocks=4, scale=0.1):
     return lib.mqa_decode_attention_paged(q, k, v, table, lens, out, B, Hq, Hkv, D, num_pages, page_size,
