@@ -17,7 +17,11 @@ Recipe (the same for every workload):
   * ragged lengths are iid uniform integers in ``[len_lo, len_hi]``, both ends
     included; the cache is allocated at ``Lmax`` regardless;
   * optionally the padding (positions >= the sequence's length) is poisoned
-    with the bfloat16 quiet-NaN pattern 0x7FC0 so that any read of it shows.
+    with the bfloat16 quiet-NaN pattern 0x7FC0 so that any read of it shows;
+  * an 8-bit cache (fp8 E4M3 or int8) is made from the bfloat16 one by
+    :func:`quantize_cache`: one fp32 scale per cached row (position, kv head)
+    = the row's largest magnitude over the format's largest code (448 or 127),
+    codes rounded to nearest-even; padding rows get NaN codes and scales.
 
 The same seed on a different device yields different (but equally valid)
 numbers; a test that compares two implementations always hands both the same
@@ -31,6 +35,9 @@ from dataclasses import dataclass, replace
 import torch
 
 BF16_QNAN_BITS = 0x7FC0
+FP8_E4M3_NAN_CODE = 0x7F
+INT8_UNUSED_CODE = 0x80   # -128: the symmetric int8 quantizer never produces it
+KV_FORMAT_MAX = {"fp8": 448.0, "int8": 127.0}
 
 
 @dataclass(frozen=True)
@@ -208,4 +215,43 @@ def page_contiguous_cache(inp: dict, page_size: int, seed: int, spare_pages: int
     out = dict(inp)
     out.update({"k_pages": k_pages, "v_pages": v_pages, "block_table": table.to(device),
                 "page_size": page_size, "num_pages": num_pages})
+    return out
+
+
+def quantize_cache(inp: dict, kv_format: str, pow2_scales: bool = False, poison_padding: bool = True) -> dict:
+    """8-bit copies of the bf16 caches of ``inp`` (from :func:`make_inputs`).
+
+    Returns ``k_codes`` / ``v_codes`` (uint8 bit patterns [B, Lmax, Hkv, D]:
+    E4M3 for "fp8", two's complement for "int8") and ``k_scale`` / ``v_scale``
+    (float32 [B, Hkv, Lmax], one per cached row), on the caches' device.  A
+    row's scale is its largest magnitude over the format's largest code (a
+    power of two at or above that when ``pow2_scales``), 1 for an all-zero
+    row; codes are the row divided by its scale, rounded to nearest-even.
+    Rows at or past a sequence's length get NaN scales and NaN (fp8) or -128
+    (int8) codes when ``poison_padding``.
+    """
+    qmax = KV_FORMAT_MAX[kv_format]
+    lens = inp["seq_lens"]
+    out = {}
+    for name in ("k", "v"):
+        x = inp[name].float()                                   # [B, Lmax, Hkv, D]
+        B, Lmax = x.shape[0], x.shape[1]
+        amax = x.abs().amax(dim=-1)                             # [B, Lmax, Hkv]
+        valid = torch.isfinite(amax) & (amax > 0)
+        sc = torch.where(valid, amax / qmax, torch.ones_like(amax))
+        if pow2_scales:
+            sc = torch.exp2(torch.ceil(torch.log2(sc)))
+        y = x / sc.unsqueeze(-1)
+        if kv_format == "fp8":
+            codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+        else:
+            codes = torch.round(y).clamp(-127, 127).to(torch.int8).view(torch.uint8)
+        pos = torch.arange(Lmax, device=x.device, dtype=torch.int32).view(1, Lmax)
+        pad = pos >= lens.to(x.device).view(B, 1)               # [B, Lmax]
+        if poison_padding:
+            fill = FP8_E4M3_NAN_CODE if kv_format == "fp8" else INT8_UNUSED_CODE
+            codes = codes.masked_fill(pad.view(B, Lmax, 1, 1), fill)
+            sc = sc.masked_fill(pad.view(B, Lmax, 1), float("nan"))
+        out[name + "_codes"] = codes.contiguous()
+        out[name + "_scale"] = sc.permute(0, 2, 1).contiguous().to(torch.float32)   # [B, Hkv, Lmax]
     return out

@@ -60,6 +60,12 @@ def _load():
             [ctypes.c_double, f64p]
         lib.oracle_local_prefill.argtypes = [u16p, u16p, u16p, i32p] + [ctypes.c_int] * 6 + \
             [ctypes.c_double, f64p]
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_decode_quant.argtypes = [u16p, u8p, u8p, f32p, f32p, i32p] + [ctypes.c_int] * 6 + \
+            [ctypes.c_double, f64p]
+        lib.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8_e4m3_value.restype = ctypes.c_double
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_set_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
@@ -203,4 +209,56 @@ def local_prefill(q_seq, k_cache, v_cache, seq_lens, window: int, scale: float):
                                       _ptr(out, ctypes.c_double))
     if rc != 0:
         raise ValueError("oracle_local_prefill rejected its arguments (code %d)" % rc)
+    return out
+
+
+KV_FORMATS = {"fp8": 1, "int8": 2}
+
+
+def fp8_e4m3_value(code: int) -> float:
+    """Value of one E4M3 code (0..255) as the oracle decodes it."""
+    return _load().oracle_fp8_e4m3_value(int(code))
+
+
+def _codes(x) -> np.ndarray:
+    """8-bit codes (uint8, int8 or float8 tensors, or arrays) as a C-contiguous uint8 array."""
+    import torch
+    if isinstance(x, torch.Tensor):
+        x = x.detach().to("cpu").contiguous()
+        if x.element_size() != 1:
+            raise TypeError("oracle expects 8-bit codes, got %s" % x.dtype)
+        return np.ascontiguousarray(x.view(torch.uint8).numpy())
+    a = np.ascontiguousarray(np.asarray(x))
+    if a.itemsize != 1:
+        raise TypeError("oracle expects 8-bit codes, got %s" % a.dtype)
+    return a.view(np.uint8)
+
+
+def _scales(x) -> np.ndarray:
+    import torch
+    if isinstance(x, torch.Tensor):
+        x = x.detach().to("cpu").numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def decode_quant(q, k_codes, v_codes, k_scale, v_scale, seq_lens, kv_format: str, scale: float):
+    """fp64 decode step against an 8-bit cache.  q [B,Hq,D] bf16; codes [B,Lmax,Hkv,D]
+    (uint8 bits; E4M3 for "fp8", two's complement for "int8"); scales [B,Hkv,Lmax] fp32.
+    Returns ``out`` [B,Hq,D] float64."""
+    qb, kc, vc = _bits(q), _codes(k_codes), _codes(v_codes)
+    ks, vs = _scales(k_scale), _scales(v_scale)
+    lens = _lens(seq_lens)
+    B, Hq, D = qb.shape
+    Bk, Lmax, Hkv, Dk = kc.shape
+    if vc.shape != kc.shape or Bk != B or Dk != D or lens.shape != (B,) or \
+            ks.shape != (B, Hkv, Lmax) or vs.shape != ks.shape:
+        raise ValueError("inconsistent shapes q%s codes%s scales%s lens%s" % (qb.shape, kc.shape, ks.shape,
+                                                                            lens.shape))
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    rc = _load().oracle_decode_quant(_ptr(qb, ctypes.c_uint16), _ptr(kc, ctypes.c_uint8), _ptr(vc, ctypes.c_uint8),
+                                     _ptr(ks, ctypes.c_float), _ptr(vs, ctypes.c_float), _ptr(lens, ctypes.c_int32),
+                                     B, Hq, Hkv, D, Lmax, KV_FORMATS[kv_format], float(scale),
+                                     _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_decode_quant rejected its arguments (code %d)" % rc)
     return out

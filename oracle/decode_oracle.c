@@ -401,6 +401,121 @@ int oracle_local_prefill(const uint16_t *q_seq, const uint16_t *k,
 }
 
 /*
+ * Value of one 8-bit E4M3 floating-point code, the 8-bit format the pages name
+ * for inference ("Machine Learning Engineering and AI Systems at Scale",
+ * section "Quantization": E4M3 for weights and activations), decoded from its
+ * fields: sign bit 7, a 4-bit exponent in bits 6..3 with bias 7, a 3-bit
+ * mantissa in bits 2..0.  Exponent 0 is subnormal (mantissa * 2^-9); the
+ * all-ones exponent with all-ones mantissa is NaN; there is no infinity (the
+ * largest finite magnitude is 448).
+ */
+double oracle_fp8_e4m3_value(uint8_t code)
+{
+    const int sign = code >> 7;
+    const int e = (code >> 3) & 15;
+    const int m = code & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* Value of one stored 8-bit code: E4M3 (format 1) or two's-complement int8
+ * (format 2). */
+static double code_value(uint8_t code, int format)
+{
+    if (format == 1) return oracle_fp8_e4m3_value(code);
+    return (double)(int8_t)code;
+}
+
+/*
+ * One decode step against a KV cache quantized to 8 bits per element ("How
+ * To Scale Your Model", Part 7 "Transformer Inference", passage on
+ * quantization: the KV cache can be stored in int8 or fp8 to save memory
+ * bandwidth; "Machine Learning Engineering and AI Systems at Scale", section
+ * "Quantization": E4M3 is the inference format, and the key/value cache is
+ * the second thing to quantize).  Each cached row (one position of one kv
+ * head) holds D codes and one fp32 scale per tensor; its values are
+ * code * scale:
+ *   kq, vq     [B, Lmax, Hkv, D]   8-bit codes (format 1: E4M3, 2: int8)
+ *   ks, vs     [B, Hkv, Lmax]      fp32 scales, one per cached row
+ *   K[b,j,g,d] = code(kq[b,j,g,d]) * ks[b,g,j]     (likewise V)
+ * and the attention is the one of oracle_decode on those values, step for
+ * step.  Returns 0, or a negative code on a bad shape, length or format.
+ */
+int oracle_decode_quant(const uint16_t *q, const uint8_t *kq, const uint8_t *vq,
+                        const float *ks, const float *vs, const int32_t *seq_lens,
+                        int B, int Hq, int Hkv, int D, int Lmax, int format,
+                        double scale, double *out)
+{
+    int rc = check_shape(B, Hq, Hkv, D, Lmax);
+    if (rc) return rc;
+    if (format != 1 && format != 2) return -7;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || seq_lens[b] > Lmax) return -3;
+
+    const int G = Hq / Hkv;
+    const long long pairs = (long long)B * Hq;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < pairs; ++bh) {
+        const int b = (int)(bh / Hq);
+        const int h = (int)(bh % Hq);
+        const int g = h / G;
+        const int n = seq_lens[b];
+        double *o = out + ((size_t)b * Hq + h) * D;
+
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (n == 0) continue;
+
+        double *s = (double *)malloc((size_t)n * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const uint16_t *qrow = q + ((size_t)b * Hq + h) * D;
+        const float *kscale = ks + ((size_t)b * Hkv + g) * Lmax;
+        const float *vscale = vs + ((size_t)b * Hkv + g) * Lmax;
+
+        /* logits against the dequantized keys */
+        for (int j = 0; j < n; ++j) {
+            const uint8_t *krow = kq + (((size_t)b * Lmax + j) * Hkv + g) * D;
+            const double sk = (double)kscale[j];
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += bf16_bits_to_double(qrow[d]) * (code_value(krow[d], format) * sk);
+            s[j] = scale * acc;
+        }
+
+        double m = s[0];
+        for (int j = 1; j < n; ++j)
+            if (s[j] > m) m = s[j];
+        double Z = 0.0;
+        for (int j = 0; j < n; ++j) {
+            s[j] = exp(s[j] - m);
+            Z += s[j];
+        }
+
+        /* weighted sum of the dequantized value rows */
+        for (int j = 0; j < n; ++j) {
+            const uint8_t *vrow = vq + (((size_t)b * Lmax + j) * Hkv + g) * D;
+            const double sv = (double)vscale[j];
+            for (int d = 0; d < D; ++d)
+                o[d] += s[j] * (code_value(vrow[d], format) * sv);
+        }
+        for (int d = 0; d < D; ++d) o[d] /= Z;
+        free(s);
+    }
+    return failed ? -4 : 0;
+}
+
+/*
  * Full causal self-attention over a whole sequence, recomputed with no cache
  * (the work the KV cache avoids).
  *   q_seq   [B, Lmax, Hq, D]   bf16 bits: one query per position
