@@ -81,6 +81,9 @@ def parse_args(argv=None):
     ap.add_argument("--window", type=int, default=0,
                     help="local (sliding-window) attention: each sequence attends its last WINDOW positions; "
                          "0 = every cached position")
+    ap.add_argument("--kv-format", default="bf16", choices=["bf16", "fp8", "int8"],
+                    help="cache element format: bf16, or 8-bit codes (E4M3 or int8) with one fp32 scale "
+                         "per cached row, made from the bf16 draw by the seeded per-row quantizer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -99,12 +102,16 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 5}))
 
 
-def cpu_baseline(w, inp, target_s: float, window: int = 0):
+def cpu_baseline(w, inp, target_s: float, window: int = 0, kv_format: str = "bf16"):
     """The oracle, as it stands, on whole decode steps of set 0 (or a prefix of the batch)."""
     import oracle
     q, k, v, lens = inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu()
     threads = oracle.max_threads()
-    if window:
+    if kv_format != "bf16":
+        ks, vs = inp["k_scale"].cpu(), inp["v_scale"].cpu()
+        run = lambda qq, kk, vv, ll: oracle.decode_quant(qq, kk, vv, ks[:len(ll)], vs[:len(ll)], ll, kv_format,
+                                                         inp["scale"])
+    elif window:
         run = lambda qq, kk, vv, ll: oracle.decode_window(qq, kk, vv, ll, window, inp["scale"])
     else:
         run = lambda qq, kk, vv, ll: oracle.decode(qq, kk, vv, ll, inp["scale"])
@@ -122,7 +129,8 @@ def cpu_baseline(w, inp, target_s: float, window: int = 0):
             run(q, k, v, lens)
         dt = time.perf_counter() - t0
         steps = reps
-        sample = "%d whole decode step(s) of the %s workload (B=%d)" % (reps, w.name, w.B)
+        sample = "%d whole decode step(s) of the %s workload (B=%d%s)" % (
+            reps, w.name, w.B, ", %s cache" % kv_format if kv_format != "bf16" else "")
     else:
         nseq = max(1, int(w.B * target_s / est_step))
         t0 = time.perf_counter()
@@ -147,8 +155,9 @@ def main(argv=None):
         return 0
 
     from gqa_decode_attention_mqa_amd import binding
-    from gqa_decode_attention_mqa_amd.traffic import decode_step_kv_bytes
-    from gqa_decode_attention_mqa_amd.workloads import WORKLOADS, make_inputs, page_contiguous_cache
+    from gqa_decode_attention_mqa_amd.traffic import decode_step_kv_bytes, decode_step_quant_bytes
+    from gqa_decode_attention_mqa_amd.workloads import (WORKLOADS, make_inputs, page_contiguous_cache,
+                                                        page_quant_cache, quantize_cache)
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -159,44 +168,66 @@ def main(argv=None):
     lens = base["seq_lens"]
     # positions attended: all of them, or the last `window` of each sequence
     attended = [min(n, args.window) if args.window else n for n in lens.cpu().tolist()]
-    set_bytes = decode_step_kv_bytes(attended, w.Hkv, w.D)  # bytes one step reads from a set
+    q8 = args.kv_format != "bf16"
+    step_bytes = (lambda n: decode_step_quant_bytes(n, w.Hkv, w.D)) if q8 else \
+        (lambda n: decode_step_kv_bytes(n, w.Hkv, w.D))
+    set_bytes = step_bytes(attended)  # bytes one step reads from a set
     nsets = min(MAX_SETS, max(1, math.ceil(MALL_DEFEAT_BYTES / max(set_bytes, 1))))
     sets = [base] + [make_inputs(w, device=dev, seed=w.seed + 1000 * i, seq_lens=lens) for i in range(1, nsets)]
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk, args.combine,
-                        window=args.window)
+                        window=args.window, kv_format=args.kv_format)
 
-    calls = []
+    # 8-bit caches: each set's bf16 draw is quantized per row (the codes and
+    # scales replace it); the scale pointers travel in each set's options
+    if q8:
+        for s in sets:
+            qc = quantize_cache(s, args.kv_format, poison_padding=False)
+            s["k"], s["v"] = qc["k_codes"], qc["v_codes"]
+            s["k_scale"], s["v_scale"] = qc["k_scale"], qc["v_scale"]
+    cpu_set = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in base.items()} \
+        if not args.no_cpu_baseline else None
+    calls, set_scales = [], []
     if args.page_size:
         # each set's caches move into a pool of pages in a seeded random order
         # (pages of one sequence are scattered over the pool)
-        cpu_set = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in base.items()} \
-            if not args.no_cpu_baseline else None
         for i, s in enumerate(sets):
-            pg = page_contiguous_cache(s, args.page_size, seed=w.seed + 7 * i, poison_spare=False)
-            del s["k"], s["v"], pg["k"], pg["v"]
-            s.update(pg)
+            if q8:
+                pg = page_quant_cache(s, {"k_codes": s["k"], "v_codes": s["v"], "k_scale": s["k_scale"],
+                                          "v_scale": s["v_scale"]}, args.page_size, seed=w.seed + 7 * i)
+                s["k_scale"], s["v_scale"] = pg["k_scale_pages"], pg["v_scale_pages"]
+            else:
+                pg = page_contiguous_cache(s, args.page_size, seed=w.seed + 7 * i, poison_spare=False)
+                del pg["k"], pg["v"]
+            del s["k"], s["v"]
+            s.update({k: pg[k] for k in ("k_pages", "v_pages", "block_table", "num_pages")})
             calls.append((s["q"].data_ptr(), s["k_pages"].data_ptr(), s["v_pages"].data_ptr(),
                           s["block_table"].data_ptr(), s["seq_lens"].data_ptr(), out.data_ptr(), w.B, w.Hq,
                           w.Hkv, w.D, s["num_pages"], args.page_size, s["block_table"].shape[1], w.scale, sptr))
         fn = lib.mqa_decode_attention_paged
     else:
-        cpu_set = None
         for s in sets:
             calls.append((s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(), s["seq_lens"].data_ptr(),
                           out.data_ptr(), w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, sptr))
         fn = lib.mqa_decode_attention_ex
+    for s in sets:
+        set_scales.append((s["k_scale"].data_ptr(), s["v_scale"].data_ptr()) if q8 else (None, None))
 
     def step(i, opts):
         st = fn(*calls[i % nsets], binding.ctypes.byref(opts))
         if st != 0:
             raise RuntimeError("decode failed: %s" % lib.mqa_last_error().decode())
 
-    plain = binding.make_opts(args.variant, args.chunk, args.combine, window=args.window)
+    def make(i, ev_b=None, ev_e=None):  # options of a step on set i % nsets
+        ks, vs = set_scales[i % nsets]
+        return binding.make_opts(args.variant, args.chunk, args.combine, ev_b, ev_e, args.window,
+                                 args.kv_format, ks, vs)
+
+    plain_sets = [make(i) for i in range(nsets)]
     for i in range(args.warmup):
-        step(i, plain)
+        step(i, plain_sets[i % nsets])
     torch.cuda.synchronize()
 
     # Start/stop events of the split-K kernel, recorded by its own dispatch on
@@ -209,9 +240,9 @@ def main(argv=None):
     for b, e in evs:  # torch creates the HIP event on first record; the library re-records it
         b.record(stream)
         e.record(stream)
-    opts = [plain] * args.steps
+    opts = [plain_sets[i % nsets] for i in range(args.steps)]
     for i, (b, e) in zip(sampled, evs):
-        opts[i] = binding.make_opts(args.variant, args.chunk, args.combine, b.cuda_event, e.cuda_event, args.window)
+        opts[i] = make(i, b.cuda_event, e.cuda_event)
     t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_begin.record(stream)
@@ -226,10 +257,11 @@ def main(argv=None):
     median_kern_ms = kern_ms[len(kern_ms) // 2]
 
     ms_per_step = total_ms / args.steps
-    kv_bytes = decode_step_kv_bytes(attended, w.Hkv, w.D)
+    kv_bytes = step_bytes(attended)
     achieved = kv_bytes / (mean_kern_ms * 1e-3) / 1e9
     traffic = read_traffic(w.name + ("_paged%d" % args.page_size if args.page_size else "")
-                           + ("_window%d" % args.window if args.window else ""))
+                           + ("_window%d" % args.window if args.window else "")
+                           + ("_" + args.kv_format if q8 else ""))
 
     result = {
         "metric": "decode-attention steps/sec and achieved HBM GB/s (% of MI355X peak)",
@@ -247,7 +279,9 @@ def main(argv=None):
         "config": {
             "workload": w.description + (" (paged cache, %d-position pages)" % args.page_size
                                          if args.page_size else "")
-                        + (" (sliding window of %d positions)" % args.window if args.window else ""),
+                        + (" (sliding window of %d positions)" % args.window if args.window else "")
+                        + (" (%s cache, one fp32 scale per row)" % args.kv_format if q8 else ""),
+            "kv_format": args.kv_format,
             "page_size": args.page_size or None,
             "window": args.window or None,
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "Lmax": w.Lmax,
@@ -272,8 +306,7 @@ def main(argv=None):
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, cpu_set if cpu_set is not None else base, args.cpu_seconds,
-                                              args.window)
+        result["cpu_baseline"] = cpu_baseline(w, cpu_set, args.cpu_seconds, args.window, args.kv_format)
     print(json.dumps(result), flush=True)
     return 0
 

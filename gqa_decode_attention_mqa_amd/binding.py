@@ -22,6 +22,7 @@ MQA_OK = 0
 VARIANTS = {"auto": 0, "valu": 1, "mfma": 2}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 COMBINE = {"auto": 0, "separate": 1, "fused": 2}
+KV_FORMATS = {"bf16": 0, "fp8": 1, "int8": 2}
 
 
 class MqaError(RuntimeError):
@@ -33,7 +34,8 @@ class MqaError(RuntimeError):
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("chunk", ctypes.c_int), ("combine", ctypes.c_int),
                 ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p),
-                ("window", ctypes.c_int)]
+                ("window", ctypes.c_int), ("kv_format", ctypes.c_int),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -64,6 +66,9 @@ def load_library():
     lib.mqa_decode_attention_paged.restype = ctypes.c_int
     lib.mqa_decode_attention_window.argtypes = [vp, vp, vp, i32p, f32p] + ints + [ctypes.c_int, ctypes.c_float, vp]
     lib.mqa_decode_attention_window.restype = ctypes.c_int
+    lib.mqa_decode_attention_quant.argtypes = [vp, vp, vp, vp, vp, i32p, f32p] + ints + \
+        [ctypes.c_int, ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
+    lib.mqa_decode_attention_quant.restype = ctypes.c_int
     lib.mqa_decode_attention_ex.argtypes = [vp, vp, vp, i32p, f32p] + ints + \
         [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
     lib.mqa_decode_attention_ex.restype = ctypes.c_int
@@ -96,9 +101,13 @@ def _check(status: int, where: str):
                                                    lib.mqa_last_error().decode()))
 
 
-def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None, window=None) -> DecodeOpts:
+def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None, window=None,
+              kv_format=None, k_scale=None, v_scale=None) -> DecodeOpts:
     o = DecodeOpts()
     o.window = int(window or 0)
+    o.kv_format = KV_FORMATS[kv_format] if isinstance(kv_format, str) else int(kv_format or 0)
+    o.k_scale = k_scale
+    o.v_scale = v_scale
     o.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant or 0)
     o.chunk = int(chunk or 0)
     o.combine = COMBINE[combine] if isinstance(combine, str) else int(combine or 0)
@@ -107,11 +116,12 @@ def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None
     return o
 
 
-def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None, window=None) -> dict:
+def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None, window=None,
+         kv_format=None) -> dict:
     """The library's launch plan for a decode call of this shape (host only)."""
     lib = load_library()
     info = PlanInfo()
-    opts = make_opts(variant, chunk, combine, window=window)
+    opts = make_opts(variant, chunk, combine, window=window, kv_format=kv_format)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.mqa_decode_plan(B, Hq, Hkv, D, Lmax, sc, ctypes.byref(opts), ctypes.byref(info)),
            "mqa_decode_plan")
@@ -179,15 +189,27 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
 
 def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
                  seq_lens: torch.Tensor, scale: float | None = None, out: torch.Tensor | None = None,
-                 variant=None, chunk=None, combine=None, events=None, window=None) -> torch.Tensor:
+                 variant=None, chunk=None, combine=None, events=None, window=None, kv_format=None,
+                 k_scale=None, v_scale=None) -> torch.Tensor:
     """One decode step over a paged cache.  q [B,Hq,D] bf16, pages [num_pages,page_size,Hkv,D] bf16,
-    block_table [B,max_blocks] int32, seq_lens [B] int32 -> fp32 [B,Hq,D]."""
+    block_table [B,max_blocks] int32, seq_lens [B] int32 -> fp32 [B,Hq,D].  With ``kv_format``
+    "fp8" or "int8" the pages hold 8-bit codes (uint8) and ``k_scale`` / ``v_scale`` are fp32
+    [num_pages, Hkv, page_size]."""
     if q.device.type != "cuda":
         raise ValueError("decode_paged runs on the GPU; q is on %s" % q.device)
     dev = q.device
     _require(q, "q", torch.bfloat16, 3, dev)
-    _require(k_pages, "k_pages", torch.bfloat16, 4, dev)
-    _require(v_pages, "v_pages", torch.bfloat16, 4, dev)
+    fmt = KV_FORMATS[kv_format] if isinstance(kv_format, str) else int(kv_format or 0)
+    _require(k_pages, "k_pages", torch.uint8 if fmt else torch.bfloat16, 4, dev)
+    _require(v_pages, "v_pages", torch.uint8 if fmt else torch.bfloat16, 4, dev)
+    sk = sv = None
+    if fmt:
+        _require(k_scale, "k_scale", torch.float32, 3, dev)
+        _require(v_scale, "v_scale", torch.float32, 3, dev)
+        if tuple(k_scale.shape) != (k_pages.shape[0], k_pages.shape[2], k_pages.shape[1]) or \
+                v_scale.shape != k_scale.shape:
+            raise ValueError("scales must have shape [num_pages, Hkv, page_size]")
+        sk, sv = k_scale.data_ptr(), v_scale.data_ptr()
     _require(block_table, "block_table", torch.int32, 2, dev)
     _require(seq_lens, "seq_lens", torch.int32, 1, dev)
     B, Hq, D = q.shape
@@ -202,13 +224,53 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
     ev_b = ev_e = None
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
-    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window)
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window, fmt, sk, sv)
     lib = load_library()
     st = lib.mqa_decode_attention_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                                         block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                                         B, Hq, Hkv, D, num_pages, page_size, block_table.shape[1],
                                         sc, _stream_ptr(dev), ctypes.byref(opts))
     _check(st, "mqa_decode_attention_paged")
+    return out
+
+
+def decode_quant(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor, k_scale: torch.Tensor,
+                 v_scale: torch.Tensor, seq_lens: torch.Tensor, kv_format: str, scale: float | None = None,
+                 out: torch.Tensor | None = None, variant=None, chunk=None, combine=None, events=None,
+                 window=None) -> torch.Tensor:
+    """One decode step against an 8-bit cache through ``mqa_decode_attention_quant``.
+    q [B,Hq,D] bf16; codes [B,Lmax,Hkv,D] uint8 (E4M3 for "fp8", two's complement for
+    "int8"); scales [B,Hkv,Lmax] fp32; seq_lens [B] int32 -> fp32 [B,Hq,D]."""
+    if q.device.type != "cuda":
+        raise ValueError("decode_quant runs on the GPU; q is on %s" % q.device)
+    dev = q.device
+    _require(q, "q", torch.bfloat16, 3, dev)
+    _require(k_codes, "k_codes", torch.uint8, 4, dev)
+    _require(v_codes, "v_codes", torch.uint8, 4, dev)
+    _require(k_scale, "k_scale", torch.float32, 3, dev)
+    _require(v_scale, "v_scale", torch.float32, 3, dev)
+    _require(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    Bk, Lmax, Hkv, Dk = k_codes.shape
+    if v_codes.shape != k_codes.shape or Bk != B or Dk != D or seq_lens.shape[0] != B or \
+            tuple(k_scale.shape) != (B, Hkv, Lmax) or v_scale.shape != k_scale.shape:
+        raise ValueError("shape mismatch: q %s, codes %s, scales %s, seq_lens %s" % (
+            tuple(q.shape), tuple(k_codes.shape), tuple(k_scale.shape), tuple(seq_lens.shape)))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, 3, dev)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must have shape %s" % ((B, Hq, D),))
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    ev_b = ev_e = None
+    if events is not None:
+        ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window)
+    lib = load_library()
+    st = lib.mqa_decode_attention_quant(q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(), k_scale.data_ptr(),
+                                        v_scale.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D,
+                                        Lmax, KV_FORMATS[kv_format], sc, _stream_ptr(dev), ctypes.byref(opts))
+    _check(st, "mqa_decode_attention_quant")
     return out
 
 

@@ -103,6 +103,18 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     if (st != MQA_OK) return st;
     st = mqa::check_pointers(B, Lmax, q, k, v, seq_lens, out);
     if (st != MQA_OK) return st;
+    const float* k_scale = opts ? opts->k_scale : nullptr;
+    const float* v_scale = opts ? opts->v_scale : nullptr;
+    if (plan.kv_format != MQA_KV_BF16 && B > 0 && Lmax > 0) {
+        if (!k_scale || !v_scale) {
+            mqa::set_error("k_scale and v_scale must be non-NULL for an 8-bit cache");
+            return MQA_ERR_NULL;
+        }
+        if (((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u) != 0) {
+            mqa::set_error("k_scale and v_scale must be 4-byte aligned");
+            return MQA_ERR_ALIGN;
+        }
+    }
     if (B == 0) return MQA_OK;
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
@@ -113,8 +125,12 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
 
     mqa::DecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
+    a.k = k;
+    a.v = v;
+    if (plan.kv_format != MQA_KV_BF16) {
+        a.k_scale = k_scale;
+        a.v_scale = v_scale;
+    }
     a.seq_lens = seq_lens;
     a.out = out;
     a.part_o = ws ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + plan.part_o_offset) : nullptr;
@@ -197,6 +213,22 @@ mqa_status mqa_decode_attention_window(const void* q, const void* k_cache, const
     return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, false);
 }
 
+mqa_status mqa_decode_attention_quant(const void* q, const void* k_codes, const void* v_codes,
+                                      const float* k_scale, const float* v_scale, const int32_t* seq_lens,
+                                      float* out, int B, int Hq, int Hkv, int D, int Lmax, int kv_format,
+                                      float scale, void* stream, const mqa_decode_opts* opts) {
+    if (kv_format != MQA_KV_FP8_E4M3 && kv_format != MQA_KV_INT8) {
+        mqa::set_error("kv_format must be MQA_KV_FP8_E4M3 or MQA_KV_INT8");
+        return MQA_ERR_ARG;
+    }
+    mqa_decode_opts o{};
+    if (opts) o = *opts;
+    o.kv_format = kv_format;
+    o.k_scale = k_scale;
+    o.v_scale = v_scale;
+    return run(q, k_codes, v_codes, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, false);
+}
+
 mqa_status mqa_decode_attention_paged(const void* q, const void* k_pages, const void* v_pages,
                                       const int32_t* block_table, const int32_t* seq_lens, float* out,
                                       int B, int Hq, int Hkv, int D, int num_pages, int page_size,
@@ -268,6 +300,6 @@ void mqa_release_workspaces(void) {
     g_ws.clear();
 }
 
-int mqa_version(void) { return 120; }
+int mqa_version(void) { return 130; }
 
 }  // extern "C"

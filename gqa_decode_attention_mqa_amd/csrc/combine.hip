@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const long long row = rh / a.Hq;
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
-    const int nsplit = chunk_span(a.window, a.chunk, len, 0).nsplit;
+    const int nsplit = chunk_span(a.window, a.chunk, a.max_splits, len, 0).nsplit;
     if (nsplit <= 1) return;  // written directly by the split kernel
 
     const int kvh = h / a.G, g = h % a.G;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
     const long long row = gh / a.Hq;
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
-    const int nsplit = chunk_span(a.window, a.chunk, len, 0).nsplit;
+    const int nsplit = chunk_span(a.window, a.chunk, a.max_splits, len, 0).nsplit;
     if (nsplit <= 1) return;  // written directly by the split kernel
 
     const int kvh = h / a.G, g = h % a.G;

@@ -32,7 +32,7 @@
 
 namespace mqa {
 
-template <int D, int NG>
+template <int D, int NG, int FMT>
 struct MfmaCfg {
     // NG compute waves (one per 16-head tile) and NL load-only waves.  The
     // loads of a tile all leave right after the ring barrier and queue in the
@@ -43,16 +43,27 @@ struct MfmaCfg {
     static constexpr int NW = NG + NL;
     static constexpr int THREADS = 64 * NW;
     static constexpr int STEP = 32;                  // positions per tile
-    static constexpr int STAGES = D == 256 ? 5 : 4;  // tiles in the LDS ring (D = 256: all 160 KB)
+    static constexpr bool Q8 = FMT != kKvBf16;       // 8-bit codes with a scale per row
+    static constexpr int EB = Q8 ? 1 : 2;            // bytes per cached element
+    // tiles in the LDS ring: bf16 D = 256 uses all 160 KB; D <= 128 leaves
+    // room for two workgroups per CU.  8-bit tiles are half as large; their
+    // kernel is bound by its own per-tile work rather than by loads in flight,
+    // and a 4-tile ring measured faster than deeper ones (MI355X, PaLM-shaped
+    // MQA: 24.8 us at 4 tiles against 29.0 us at 9; B=4, len 131072: 73.7
+    // against 82.1 us; B=32, Hkv=8, D=128: 51.6 against 53.3 us at 8 tiles)
+    static constexpr int STAGES = Q8 ? 4 : (D == 256 ? 5 : 4);
     static_assert(STAGES >= 4, "two tiles in use and at least one more in flight");
     static constexpr int KS = D / 32;                // k-steps over d in q.K
     static constexpr int MT = D / 16;                // 16-row tiles of O^T
-    static constexpr int CPR = D / 8;                // 16-byte chunks per row
-    static constexpr int TILE_BYTES = STEP * D * 2;  // K (or V) bytes of one tile
+    static constexpr int ROWB = D * EB;              // bytes of one cached row
+    static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+    static constexpr int TILE_BYTES = STEP * ROWB;   // K (or V) bytes of one tile
+    static constexpr int SCALE_BYTES = Q8 ? 2 * STEP * 4 : 0;  // the tile rows' K scales, then V scales
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES + SCALE_BYTES;
     static constexpr int LOADS = TILE_BYTES / 1024;  // wave-wide 16-byte loads per tile (K or V)
     static constexpr int KPW = LOADS / NL;           // K loads (and as many V loads) per loader per tile
-    static constexpr int PER_WAVE = 2 * KPW;         // loads a loader issues per tile
-    static constexpr int LDS_BYTES = STAGES * 2 * TILE_BYTES;
+    static constexpr int PER_WAVE = 2 * KPW + (Q8 ? 1 : 0);  // loads a loader issues per tile (+ a scale row)
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static_assert(D >= 64 && D % 64 == 0, "head size");
     static_assert(LOADS % NL == 0, "every loader issues the same number of loads");
     static_assert((STAGES - 2) * PER_WAVE <= 63, "loads in flight fit a wave's counter");
@@ -61,7 +72,7 @@ struct MfmaCfg {
     static_assert(LDS_BYTES >= (2 * kFusedMaxSplits + 2) * 16 * NG * 4 + 16, "fused-combine scratch fits");
 };
 
-// LDS layout of a tile: row t (D bf16) is D/8 chunks of 16 bytes, and chunk
+// LDS layout of a bf16 tile: row t (D bf16) is D/8 chunks of 16 bytes, and chunk
 // c of row t sits in slot c ^ swz_key(t).  The key takes all eight values over
 // any eight consecutive rows (the K reads of eight lanes hit eight different
 // 16-byte bank groups), and over rows 4i .. 4i+3 it takes four values that
@@ -69,10 +80,29 @@ struct MfmaCfg {
 // adjacent chunks of four rows, hit 128 distinct bytes of banks).
 __device__ __forceinline__ int swz_key(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
 
-// LDS byte offset of chunk c of row t inside a tile.
+// LDS byte offset of chunk c of row t inside a bf16 tile.
 template <int CPR>
 __device__ __forceinline__ int swz(int t, int c) {
     return (t * CPR + (c ^ swz_key(t))) * 16;
+}
+
+// 8-bit tiles: row t (D codes) is D/16 chunks of 16 bytes, chunk c in slot
+// c ^ swz8_key(t).  With R = 256/D rows per 256 bytes of banks, the key is
+// one-to-one over the rows of one bank offset among any 16 consecutive rows
+// (the q.K reads of a 16-lane group) and among rows 4i .. 4i+3 and
+// 16 + 4i .. 16 + 4i + 3 (the transposing V reads of a 16-lane group).
+template <int D>
+__device__ __forceinline__ int swz8_key(int t) {
+    constexpr int R = 256 / D;
+    return ((t / R) + (t >> 4) * (4 / R)) & (D / 16 - 1);
+}
+
+template <int FMT, int D>
+__device__ __forceinline__ int tile_key(int t) {
+    if constexpr (FMT == kKvBf16)
+        return swz_key(t);
+    else
+        return swz8_key<D>(t);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -97,6 +127,15 @@ template <int OFF>
 __device__ __forceinline__ u32x2_t ds_read_tr16_b64_asm(uint32_t addr) {
     u32x2_t r;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+// The same for 8-bit elements (ds_read_b64_tr_b8): in each group of 16
+// lanes, lane i receives as element k (k = 0..7) byte (i mod 8) of the 8-byte
+// row addressed by lane 2k + i/8 of its group (checked on MI355X).
+__device__ __forceinline__ u32x2_t ds_read_tr8_b64_asm(uint32_t addr) {
+    u32x2_t r;
+    asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(addr));
     return r;
 }
 
@@ -129,9 +168,16 @@ __device__ __forceinline__ void wait_vt_tile(u32x2_t (&lo)[MT], u32x2_t (&hi)[MT
     for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(lo[m]), "+v"(hi[m]));
 }
 
-template <int D, int NG>
+template <int MT>
+__device__ __forceinline__ void wait_v8_tile(u32x2_t (&v)[MT]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(v[m]));
+}
+
+template <int D, int NG, int FMT>
 __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
-    using C = MfmaCfg<D, NG>;
+    using C = MfmaCfg<D, NG, FMT>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int tid = threadIdx.x;
@@ -150,15 +196,14 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
     b = __builtin_amdgcn_readfirstlane(b);
     len = __builtin_amdgcn_readfirstlane(len);
-    const ChunkSpan span = chunk_span(a.window, a.chunk, len, s);
+    const ChunkSpan span = chunk_span(a.window, a.chunk, a.max_splits, len, s);
     if (s > 0 && span.p0 >= len) return;  // whole workgroup: this chunk is past the end
     // Sliding window: rows lo - 32 < t < lo of the first tile lie before it;
     // they are loaded as zeros and masked.
     const int lo = span.lo, p0 = span.p0, p1 = span.p1, nsplit = span.nsplit;
     const int ntiles = p1 > p0 ? (p1 - p0 + C::STEP - 1) / C::STEP : 0;
 
-    const size_t pos_stride = (size_t)a.Hkv * D;
-    const int rowbytes = (int)(pos_stride * 2);
+    const int rowbytes = a.Hkv * C::ROWB;  // bytes between consecutive positions of a cache
 
     // A compute wave's q^T operand (B of q.K): lane (li, kg), k-step ks holds
     // q[head 16w + li][32 ks + 8 kg .. +8]; heads past the group read as zero.
@@ -195,29 +240,39 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         // compiler that no load into it is pending inside the loop
         __builtin_amdgcn_s_waitcnt(kVmcntStages<0, 0>());
     }
-    auto tile_rows = [&](const uint16_t* cache, int t0) {
+    auto tile_loc = [&](int t0) {
         if (pages_in_lanes)
-            return page_rows(cache, a, __builtin_amdgcn_readlane(chunk_page, (t0 >> a.page_shift) - blk0), kvh, t0);
-        return kv_rows(cache, a, b, kvh, t0);
+            return page_loc(a, __builtin_amdgcn_readlane(chunk_page, (t0 >> a.page_shift) - blk0), kvh, t0);
+        return kv_loc(a, b, kvh, t0);
     };
     auto issue_tile = [&](int tile) {
         if (w < NG) return;
         const int t0 = p0 + tile * C::STEP;
         const int rows = max(0, min(C::STEP, p1 - t0));
         const int skip = lo - t0;  // rows before a sliding window (> 0 in the first tile only)
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows > 0 ? tile_rows(a.k, t0) : a.k, rows * rowbytes);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows > 0 ? tile_rows(a.v, t0) : a.v, rows * rowbytes);
-        unsigned char* slot = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
+        const RowLoc loc = rows > 0 ? tile_loc(t0) : RowLoc{0, 0};
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(row_ptr<C::EB>(a.k, a, loc.row), rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(row_ptr<C::EB>(a.v, a, loc.row), rows * rowbytes);
+        unsigned char* slot = smem + (tile % C::STAGES) * C::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::KPW; ++i) {
             const int jj = (w - NG) + C::NL * i;
             const int p = jj * 64 + lane;  // 16-byte LDS slot in the tile
             const int t = p / C::CPR, cs = p % C::CPR;
-            const int voff = t < skip ? kOutOfRange : t * rowbytes + ((cs ^ swz_key(t)) * 16);
+            const int voff = t < skip ? kOutOfRange : t * rowbytes + ((cs ^ tile_key<FMT, D>(t)) * 16);
             unsigned char* dst = slot + jj * 1024;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)dst, 16, voff, 0, 0, kCachePolicyNT);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dst + C::TILE_BYTES), 16, voff, 0, 0,
                                                      kCachePolicyNT);
+        }
+        if constexpr (C::Q8) {
+            // the tile rows' scales (contiguous per kv head): loader 0 the K
+            // scales, loader 1 the V scales, one dword per lane of the first 32
+            const float* sc = (w == NG ? a.k_scale : a.v_scale) + loc.scale;
+            const __amdgpu_buffer_rsrc_t srs = make_rsrc(sc, rows * 4);
+            if (lane < C::STEP)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_ptr_t)(slot + 2 * C::TILE_BYTES + (w - NG) * 128), 4,
+                                                         lane < skip ? kOutOfRange : lane * 4, 0, 0, kCachePolicyNT);
         }
     };
     // In a loader, the next tile and everything before it have landed once
@@ -242,8 +297,17 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     // Accumulator lane (li, kg), element r of tile mq: head li, position 16mq + 4kg + r.
     // Even and odd k-steps accumulate separately (four independent chains on
     // the matrix pipe), summed at the end.
+    // 8-bit tiles: lane (li, kg) of k-step ks reads the 8 codes of row t,
+    // columns 32 ks + 8 kg .. +7: half kg & 1 of chunk 2 ks + kg / 2.
+    int k8_row[2], k8_key[2];
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq) {
+        const int t = 16 * mq + li;
+        k8_row[mq] = t * C::ROWB + (kg & 1) * 8;
+        k8_key[mq] = (tile_key<FMT, D>(t) ^ (kg >> 1)) * 16;
+    }
     auto qk_tile = [&](int tile, f32x4_t (&sacc)[2]) {
-        const unsigned char* kt = smem + (tile % C::STAGES) * 2 * C::TILE_BYTES;
+        const unsigned char* kt = smem + (tile % C::STAGES) * C::STAGE_BYTES;
         f32x4_t part[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -253,8 +317,15 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq) {
-                const int t = 16 * mq + li;
-                const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kt + swz<C::CPR>(t, 4 * ks + kg));
+                u32x4_t ka;
+                if constexpr (C::Q8) {
+                    const u32x2_t k8 =
+                        *reinterpret_cast<const u32x2_t*>(kt + k8_row[mq] + (k8_key[mq] ^ (2 * ks * 16)));
+                    ka = widen8<FMT>(k8);
+                } else {
+                    const int t = 16 * mq + li;
+                    ka = *reinterpret_cast<const u32x4_t*>(kt + swz<C::CPR>(t, 4 * ks + kg));
+                }
                 part[ks & 1][mq] = mfma_16x16x32_bf16(ka, qb[ks], part[ks & 1][mq]);
             }
         }
@@ -263,12 +334,27 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     };
     // Scale, mask the tail, lazy online softmax; P^T of the tile in registers.
     // Returns whether the running maximum moved (then O must be rescaled by alpha).
+    // 8-bit caches: the logit of a position is scaled by its K row's scale,
+    // and its weight in P.V by its V row's scale (l sums the unscaled weights).
     auto softmax_tile = [&](int tile, f32x4_t (&sacc)[2], u32x4_t& pb, float& alpha) {
         const int st = p0 + tile * C::STEP;
+        f32x4_t vsc[2];
+        if constexpr (C::Q8) {
+            const float* scl = reinterpret_cast<const float*>(smem + (tile % C::STAGES) * C::STAGE_BYTES +
+                                                              2 * C::TILE_BYTES);
 #pragma unroll
-        for (int mq = 0; mq < 2; ++mq)
+            for (int mq = 0; mq < 2; ++mq) {
+                const f32x4_t ksc = *reinterpret_cast<const f32x4_t*>(scl + 16 * mq + 4 * kg);
+                vsc[mq] = *reinterpret_cast<const f32x4_t*>(scl + C::STEP + 16 * mq + 4 * kg);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[mq][r] *= qk;
+                for (int r = 0; r < 4; ++r) sacc[mq][r] *= qk * ksc[r];
+            }
+        } else {
+#pragma unroll
+            for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[mq][r] *= qk;
+        }
         if (st + C::STEP > p1 || st < lo) {
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq)
@@ -287,13 +373,24 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         float lsum = 0.f;
 #pragma unroll
         for (int mq = 0; mq < 2; ++mq) {
-            const uint32_t lo = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][0] - m_run),
-                                               __builtin_amdgcn_exp2f(sacc[mq][1] - m_run));
-            const uint32_t hi = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][2] - m_run),
-                                               __builtin_amdgcn_exp2f(sacc[mq][3] - m_run));
-            pb[2 * mq] = lo;
-            pb[2 * mq + 1] = hi;
-            lsum += (bf16_lo_f32(lo) + bf16_hi_f32(lo)) + (bf16_lo_f32(hi) + bf16_hi_f32(hi));
+            if constexpr (C::Q8) {
+                float pr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pr[r] = __builtin_amdgcn_exp2f(sacc[mq][r] - m_run);
+                    lsum += pr[r];
+                }
+                pb[2 * mq] = pack2_bf16_rne(pr[0] * vsc[mq][0], pr[1] * vsc[mq][1]);
+                pb[2 * mq + 1] = pack2_bf16_rne(pr[2] * vsc[mq][2], pr[3] * vsc[mq][3]);
+            } else {
+                const uint32_t lo = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][0] - m_run),
+                                                   __builtin_amdgcn_exp2f(sacc[mq][1] - m_run));
+                const uint32_t hi = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][2] - m_run),
+                                                   __builtin_amdgcn_exp2f(sacc[mq][3] - m_run));
+                pb[2 * mq] = lo;
+                pb[2 * mq + 1] = hi;
+                lsum += (bf16_lo_f32(lo) + bf16_hi_f32(lo)) + (bf16_lo_f32(hi) + bf16_hi_f32(hi));
+            }
         }
         l_run = l_run * alpha + lsum;
         return __any(moved);
@@ -316,15 +413,34 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         tr_lo[mm] = swz<C::CPR>(tr_tlo, c) + half;
         tr_hi[mm] = swz<C::CPR>(tr_thi, c) + half;
     }
+    // 8-bit tiles: one ds_read_b64_tr_b8 per 16-row tile m of d.  In lane
+    // group kg, lane 2k + x points at the 8 codes d = 16m + 8x .. +7 of
+    // position row 16 (k / 4) + 4 kg + k % 4, so lane li receives column
+    // 16m + li of the eight positions in the P^T order.
+    const int tr8_t = 16 * ((li >> 1) >> 2) + 4 * kg + ((li >> 1) & 3);
+    const int tr8_row = tr8_t * C::ROWB + (li & 1) * 8;
+    const int tr8_key = tile_key<FMT, D>(tr8_t) * 16;
     auto pv_issue = [&](int tile, u32x2_t (&lo)[C::MT], u32x2_t (&hi)[C::MT]) {
-        const uint32_t vbase = lds_addr(smem + (tile % C::STAGES) * 2 * C::TILE_BYTES + C::TILE_BYTES);
-        issue_vt_tile<C::MT>(vbase, tr_lo, tr_hi, lo, hi);
+        const uint32_t vbase = lds_addr(smem + (tile % C::STAGES) * C::STAGE_BYTES + C::TILE_BYTES);
+        if constexpr (C::Q8) {
+#pragma unroll
+            for (int m = 0; m < C::MT; ++m) lo[m] = ds_read_tr8_b64_asm(vbase + tr8_row + (tr8_key ^ (m * 16)));
+        } else {
+            issue_vt_tile<C::MT>(vbase, tr_lo, tr_hi, lo, hi);
+        }
     };
     auto pv_mma = [&](const u32x4_t& pb, u32x2_t (&lo)[C::MT], u32x2_t (&hi)[C::MT]) {
-        wait_vt_tile<C::MT>(lo, hi);
+        if constexpr (C::Q8)
+            wait_v8_tile<C::MT>(lo);
+        else
+            wait_vt_tile<C::MT>(lo, hi);
 #pragma unroll
         for (int m = 0; m < C::MT; ++m) {
-            const u32x4_t va = {lo[m].x, lo[m].y, hi[m].x, hi[m].y};
+            u32x4_t va;
+            if constexpr (C::Q8)
+                va = widen8<FMT>(lo[m]);
+            else
+                va = u32x4_t{lo[m].x, lo[m].y, hi[m].x, hi[m].y};
             oacc[m] = mfma_16x16x32_bf16(va, pb, oacc[m]);
         }
     };
@@ -445,10 +561,10 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
                   wts, 16 * NG);
 }
 
-template <int D, int NG>
+template <int D, int NG, int FMT>
 static hipError_t launch_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                             hipEvent_t ev1) {
-    using C = MfmaCfg<D, NG>;
+    using C = MfmaCfg<D, NG, FMT>;
     constexpr int lds = C::LDS_BYTES;
     if (lds > 64 * 1024) {
         static std::atomic<uint64_t> done_mask{0};
@@ -457,7 +573,7 @@ static hipError_t launch_mfma(const Plan& p, const DecodeArgs& a, hipStream_t st
         if (e != hipSuccess) return e;
         const uint64_t bit = 1ull << (dev & 63);
         if (!(done_mask.load() & bit)) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<D, NG>),
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<D, NG, FMT>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             if (e != hipSuccess) return e;
             done_mask.fetch_or(bit);
@@ -466,30 +582,41 @@ static hipError_t launch_mfma(const Plan& p, const DecodeArgs& a, hipStream_t st
     const dim3 grid((unsigned)p.grid_main, (unsigned)p.head_blocks);
     const dim3 block(C::THREADS);
     if (ev0 || ev1)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<D, NG>), grid, block, lds, stream, ev0, ev1, 0, a);
+        hipExtLaunchKernelGGL((decode_mfma_kernel<D, NG, FMT>), grid, block, lds, stream, ev0, ev1, 0, a);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<D, NG>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<D, NG, FMT>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int FMT>
 static hipError_t launch_mfma_d(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                               hipEvent_t ev1) {
     switch (p.heads_per_block / 16) {
-        case 1: return launch_mfma<D, 1>(p, a, stream, ev0, ev1);
-        case 2: return launch_mfma<D, 2>(p, a, stream, ev0, ev1);
-        case 3: return launch_mfma<D, 3>(p, a, stream, ev0, ev1);
-        case 4: return launch_mfma<D, 4>(p, a, stream, ev0, ev1);
+        case 1: return launch_mfma<D, 1, FMT>(p, a, stream, ev0, ev1);
+        case 2: return launch_mfma<D, 2, FMT>(p, a, stream, ev0, ev1);
+        case 3: return launch_mfma<D, 3, FMT>(p, a, stream, ev0, ev1);
+        case 4: return launch_mfma<D, 4, FMT>(p, a, stream, ev0, ev1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT>
+static hipError_t launch_mfma_f(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                              hipEvent_t ev1) {
+    switch (a.D) {
+        case 64: return launch_mfma_d<64, FMT>(p, a, stream, ev0, ev1);
+        case 128: return launch_mfma_d<128, FMT>(p, a, stream, ev0, ev1);
+        case 256: return launch_mfma_d<256, FMT>(p, a, stream, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                                     hipEvent_t ev1) {
-    switch (a.D) {
-        case 64: return launch_mfma_d<64>(p, a, stream, ev0, ev1);
-        case 128: return launch_mfma_d<128>(p, a, stream, ev0, ev1);
-        case 256: return launch_mfma_d<256>(p, a, stream, ev0, ev1);
+    switch (p.kv_format) {
+        case kKvBf16: return launch_mfma_f<kKvBf16>(p, a, stream, ev0, ev1);
+        case kKvFp8: return launch_mfma_f<kKvFp8>(p, a, stream, ev0, ev1);
+        case kKvInt8: return launch_mfma_f<kKvInt8>(p, a, stream, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }

@@ -25,7 +25,7 @@ template <int RL>
 __device__ __forceinline__ float row_sum(float x) {
     x += dpp_f32<kDppQuadXor1>(x);
     x += dpp_f32<kDppQuadXor2>(x);
-    x += dpp_f32<kDppRowHalfMirror>(x);
+    if constexpr (RL >= 8) x += dpp_f32<kDppRowHalfMirror>(x);
     if constexpr (RL >= 16) x += dpp_f32<kDppRowMirror>(x);
     if constexpr (RL >= 32) x = sum_xor16(x);
     return x;
@@ -36,6 +36,10 @@ __device__ __forceinline__ float row_sum(float x) {
 // swaps across rows.
 template <int RL, bool MAX>
 __device__ __forceinline__ float across_rows(float x) {
+    if constexpr (RL <= 4) {
+        const float y = dpp_f32<kDppRowRor4>(x);
+        x = MAX ? fmaxf(x, y) : x + y;
+    }
     if constexpr (RL <= 8) {
         const float y = dpp_f32<kDppRowRor8>(x);
         x = MAX ? fmaxf(x, y) : x + y;
@@ -45,13 +49,23 @@ __device__ __forceinline__ float across_rows(float x) {
     return x;
 }
 
-template <int D, int GB>
+// Value of lane `src` (0..63) of x, in every lane.  Must run with every lane
+// of the wave active: ds_bpermute reads zero from an inactive source lane.
+__device__ __forceinline__ float lane_value(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+template <int D, int GB, int FMT>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+    constexpr bool Q8 = FMT != kKvBf16;  // 8-bit codes with one scale per cached row
     constexpr int NW = 4;
-    constexpr int RL = D / 8;      // lanes per cache row
-    constexpr int RS = 64 / RL;    // rows per load instruction
-    constexpr int NB = 4;          // load instructions per block (even: P.V pairs them)
-    constexpr int WB = NB * RS;    // positions per wave block
+    constexpr int EPL = Q8 ? 16 : 8;     // cached elements per lane of one 16-byte load
+    constexpr int NP = EPL / 2;          // bf16 pairs per lane
+    constexpr int RL = D / EPL;          // lanes per cache row
+    constexpr int RS = 64 / RL;          // rows per load instruction
+    constexpr int NB = RS * 4 <= 32 ? 4 : 2;  // load instructions per block (even: P.V pairs them)
+    constexpr int WB = NB * RS;          // positions per wave block
+    static_assert(WB <= 32 && 32 % WB == 0, "a block never straddles a page");
     __shared__ float mrg_m[NW][GB];
     __shared__ float mrg_l[NW][GB];
     __shared__ __attribute__((aligned(16))) float mrg_o[NW][GB][D];
@@ -78,7 +92,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     // descriptors built from them) in scalar registers.
     b = __builtin_amdgcn_readfirstlane(b);
     len = __builtin_amdgcn_readfirstlane(len);
-    const ChunkSpan span = chunk_span(a.window, a.chunk, len, s);
+    const ChunkSpan span = chunk_span(a.window, a.chunk, a.max_splits, len, s);
     if (s > 0 && span.p0 >= len) return;
     // Blocks start at the block holding the first attended position (a
     // multiple of WB, which divides 32), so every block has a valid row.
@@ -87,68 +101,111 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const int p1 = span.p1;
     const int nsplit = span.nsplit;
 
-    // q for this lane's 8 columns of every head in the block, as bf16 pairs.
-    uint32_t qv[GB][4];
-    const uint16_t* qrow = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D + 8 * rl;
+    // q for this lane's EPL columns of every head in the block, as bf16 pairs.
+    uint32_t qv[GB][NP];
+    const uint16_t* qrow = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D + EPL * rl;
 #pragma unroll
     for (int gg = 0; gg < GB; ++gg) {
-        u32x4_t t = {0u, 0u, 0u, 0u};
-        if (gg < gcnt) t = load_u32x4(qrow + (size_t)gg * D);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) qv[gg][c] = t[c];
+        for (int h = 0; h < NP / 4; ++h) {
+            u32x4_t t = {0u, 0u, 0u, 0u};
+            if (gg < gcnt) t = load_u32x4(qrow + (size_t)gg * D + 8 * h);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qv[gg][4 * h + c] = t[c];
+        }
     }
 
-    const size_t pos_stride = (size_t)a.Hkv * D;
-    const int rowbytes = (int)(pos_stride * 2);
+    const int rowbytes = a.Hkv * D * (Q8 ? 1 : 2);  // bytes between consecutive positions of a cache
     const float qk = a.qk_log2;
-    // Byte offset of this lane's 8 columns in row st*RS + rr of a block.
+    // Byte offset of this lane's 16 bytes in row st*RS + rr of a block.
     int off[NB];
 #pragma unroll
     for (int st = 0; st < NB; ++st) off[st] = (st * RS + rr) * rowbytes + rl * 16;
 
-    float m[GB], l[GB], o[GB][8];
+    float m[GB], l[GB], o[GB][EPL];
 #pragma unroll
     for (int gg = 0; gg < GB; ++gg) {
         m[gg] = -INFINITY;
         l[gg] = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[gg][j] = 0.f;
+        for (int j = 0; j < EPL; ++j) o[gg][j] = 0.f;
     }
 
     const int nblk = p1 > p0 ? (p1 - p0 + WB - 1) / WB : 0;
     // Issue the loads of block `blk` (of this wave's blocks w, w + NW, ...).
     // The buffer range ends at the last valid row: rows past it, and whole
     // blocks past the chunk, read as zero without a memory access; so do rows
-    // before a sliding window's first position (out-of-range offsets).
-    auto load_block = [&](int blk, u32x4_t (&kr)[NB], u32x4_t (&vr)[NB]) {
+    // before a sliding window's first position (out-of-range offsets).  An
+    // 8-bit cache also loads the block rows' K and V scales, lane j holding
+    // those of row j % WB.
+    auto load_block = [&](int blk, u32x4_t (&kr)[NB], u32x4_t (&vr)[NB], float& ks, float& vs) {
         const int t0 = p0 + blk * WB;
         const int rows = max(0, min(WB, p1 - t0));
         const int skip = lo - t0;  // rows of the block before the window (> 0 in its first block only)
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(rows > 0 ? kv_rows(a.k, a, b, kvh, t0) : a.k, rows * rowbytes);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(rows > 0 ? kv_rows(a.v, a, b, kvh, t0) : a.v, rows * rowbytes);
+        const RowLoc loc = rows > 0 ? kv_loc(a, b, kvh, t0) : RowLoc{0, 0};
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(row_ptr<Q8 ? 1 : 2>(a.k, a, loc.row), rows * rowbytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(row_ptr<Q8 ? 1 : 2>(a.v, a, loc.row), rows * rowbytes);
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
             const int o = st * RS + rr < skip ? kOutOfRange : off[st];
             kr[st] = buffer_load_u32x4(krs, o);
             vr[st] = buffer_load_u32x4(vrs, o);
         }
+        if constexpr (Q8) {
+            const int j = lane % WB;
+            const int so = j < skip ? kOutOfRange : j * 4;
+            ks = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.k_scale + loc.scale, rows * 4), so, 0, kCachePolicyNT));
+            vs = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.v_scale + loc.scale, rows * 4), so, 0, kCachePolicyNT));
+        }
     };
-    auto compute_block = [&](int blk, const u32x4_t (&kr)[NB], const u32x4_t (&vr)[NB]) {
+    // The lane's EPL cached values of load st as bf16 pairs (exact widening of 8-bit codes).
+    auto widen_row = [&](const u32x4_t& r, uint32_t (&x)[NP]) {
+        if constexpr (Q8) {
+            const u32x4_t lo8 = widen8<FMT>(u32x2_t{r[0], r[1]});
+            const u32x4_t hi8 = widen8<FMT>(u32x2_t{r[2], r[3]});
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                x[c] = lo8[c];
+                x[4 + c] = hi8[c];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[c] = r[c];
+        }
+    };
+    auto compute_block = [&](int blk, const u32x4_t (&kr)[NB], const u32x4_t (&vr)[NB], float ks, float vs) {
         const int t0 = p0 + blk * WB;
         const int rows = min(WB, p1 - t0);
         const int skip = lo - t0;
-        // logits (base-2 units), masked outside [lo, p1)
+        // logits (base-2 units), masked outside [lo, p1); an 8-bit cache
+        // scales each logit by its K row's scale and each weight in P.V by
+        // its V row's scale (zero outside the range, where codes read as 0)
         const bool edge = rows < WB || skip > 0;
         float sc[NB][GB];
+        float vscale[NB];
 #pragma unroll
         for (int st = 0; st < NB; ++st) {
-            const bool ok = !edge || (st * RS + rr < rows && st * RS + rr >= skip);
+            const int r = st * RS + rr;
+            const bool ok = !edge || (r < rows && r >= skip);
+            float kscale = 1.f;
+            if constexpr (Q8) {
+                // every lane takes part in both permutes (a lane reading an
+                // inactive lane would get zero), then the V scale is masked
+                kscale = lane_value(ks, r);
+                const float vrow = lane_value(vs, r);
+                vscale[st] = ok ? vrow : 0.f;
+            }
+            uint32_t kk[NP];
+            widen_row(kr[st], kk);
 #pragma unroll
             for (int gg = 0; gg < GB; ++gg) {
                 float acc = 0.f;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc = dot2_bf16(qv[gg][c], kr[st][c], acc);
+                for (int c = 0; c < NP; ++c) acc = dot2_bf16(qv[gg][c], kk[c], acc);
                 acc = row_sum<RL>(acc) * qk;
+                if constexpr (Q8) acc *= kscale;
                 sc[st][gg] = ok ? acc : -INFINITY;
             }
         }
@@ -169,10 +226,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             float lsum = 0.f;
 #pragma unroll
             for (int st = 0; st < NB; st += 2) {
-                const uint32_t pair = pack2_bf16_rne(__builtin_amdgcn_exp2f(sc[st][gg] - m[gg]),
-                                                     __builtin_amdgcn_exp2f(sc[st + 1][gg] - m[gg]));
-                pp[st / 2][gg] = pair;
-                lsum += bf16_lo_f32(pair) + bf16_hi_f32(pair);
+                const float pa = __builtin_amdgcn_exp2f(sc[st][gg] - m[gg]);
+                const float pb = __builtin_amdgcn_exp2f(sc[st + 1][gg] - m[gg]);
+                if constexpr (Q8) {
+                    pp[st / 2][gg] = pack2_bf16_rne(pa * vscale[st], pb * vscale[st + 1]);
+                    lsum += pa + pb;
+                } else {
+                    const uint32_t pair = pack2_bf16_rne(pa, pb);
+                    pp[st / 2][gg] = pair;
+                    lsum += bf16_lo_f32(pair) + bf16_hi_f32(pair);
+                }
             }
             l[gg] = l[gg] * alpha[gg] + lsum;
         }
@@ -180,19 +243,22 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
             for (int gg = 0; gg < GB; ++gg)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) o[gg][j] *= alpha[gg];
+                for (int j = 0; j < EPL; ++j) o[gg][j] *= alpha[gg];
         }
         // P.V: two positions of one column per v_dot2
 #pragma unroll
         for (int st = 0; st < NB; st += 2) {
+            uint32_t va[NP], vb[NP];
+            widen_row(vr[st], va);
+            widen_row(vr[st + 1], vb);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t lo = perm_b32(vr[st + 1][c], vr[st][c], kPermLoHalves);
-                const uint32_t hi = perm_b32(vr[st + 1][c], vr[st][c], kPermHiHalves);
+            for (int c = 0; c < NP; ++c) {
+                const uint32_t lo2 = perm_b32(vb[c], va[c], kPermLoHalves);
+                const uint32_t hi2 = perm_b32(vb[c], va[c], kPermHiHalves);
 #pragma unroll
                 for (int gg = 0; gg < GB; ++gg) {
-                    o[gg][2 * c] = dot2_bf16(pp[st / 2][gg], lo, o[gg][2 * c]);
-                    o[gg][2 * c + 1] = dot2_bf16(pp[st / 2][gg], hi, o[gg][2 * c + 1]);
+                    o[gg][2 * c] = dot2_bf16(pp[st / 2][gg], lo2, o[gg][2 * c]);
+                    o[gg][2 * c + 1] = dot2_bf16(pp[st / 2][gg], hi2, o[gg][2 * c + 1]);
                 }
             }
         }
@@ -200,13 +266,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     // Double-buffered: the loads of a wave's next block are in flight while
     // it computes the current one (two register sets, alternating).
     u32x4_t ka[NB], va[NB], kb[NB], vb[NB];
-    if (w < nblk) load_block(w, ka, va);
+    float ksa = 0.f, vsa = 0.f, ksb = 0.f, vsb = 0.f;
+    if (w < nblk) load_block(w, ka, va, ksa, vsa);
     for (int blk = w; blk < nblk; blk += 2 * NW) {
-        load_block(blk + NW, kb, vb);
-        compute_block(blk, ka, va);
+        load_block(blk + NW, kb, vb, ksb, vsb);
+        compute_block(blk, ka, va, ksa, vsa);
         if (blk + NW >= nblk) break;
-        load_block(blk + 2 * NW, ka, va);
-        compute_block(blk + NW, kb, vb);
+        load_block(blk + 2 * NW, ka, va, ksa, vsa);
+        compute_block(blk + NW, kb, vb, ksb, vsb);
     }
 
     // Sum the rows of the wave (same softmax state in every row).
@@ -214,16 +281,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     for (int gg = 0; gg < GB; ++gg) {
         l[gg] = across_rows<RL, false>(l[gg]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[gg][j] = across_rows<RL, false>(o[gg][j]);
+        for (int j = 0; j < EPL; ++j) o[gg][j] = across_rows<RL, false>(o[gg][j]);
     }
     if (rr == 0) {
 #pragma unroll
-        for (int gg = 0; gg < GB; ++gg) {
-            f32x4_t lo4 = {o[gg][0], o[gg][1], o[gg][2], o[gg][3]};
-            f32x4_t hi4 = {o[gg][4], o[gg][5], o[gg][6], o[gg][7]};
-            *reinterpret_cast<f32x4_t*>(&mrg_o[w][gg][8 * rl]) = lo4;
-            *reinterpret_cast<f32x4_t*>(&mrg_o[w][gg][8 * rl + 4]) = hi4;
-        }
+        for (int gg = 0; gg < GB; ++gg)
+#pragma unroll
+            for (int j = 0; j < EPL; j += 4)
+                *reinterpret_cast<f32x4_t*>(&mrg_o[w][gg][EPL * rl + j]) =
+                    f32x4_t{o[gg][j], o[gg][j + 1], o[gg][j + 2], o[gg][j + 3]};
         if (rl == 0) {
 #pragma unroll
             for (int gg = 0; gg < GB; ++gg) {
@@ -302,36 +368,49 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                   &mrg_o[0][0][0], GB);
 }
 
-template <int D, int GB>
+template <int D, int GB, int FMT>
 static hipError_t launch_one(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                              hipEvent_t ev1) {
     const dim3 grid((unsigned)p.grid_main, (unsigned)p.head_blocks);
     const dim3 block(256);
     if (ev0 || ev1)
-        hipExtLaunchKernelGGL((decode_valu_kernel<D, GB>), grid, block, 0, stream, ev0, ev1, 0, a);
+        hipExtLaunchKernelGGL((decode_valu_kernel<D, GB, FMT>), grid, block, 0, stream, ev0, ev1, 0, a);
     else
-        hipLaunchKernelGGL((decode_valu_kernel<D, GB>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((decode_valu_kernel<D, GB, FMT>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int FMT>
 static hipError_t launch_valu_d(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                                 hipEvent_t ev1) {
     switch (p.heads_per_block) {
-        case 1: return launch_one<D, 1>(p, a, stream, ev0, ev1);
-        case 2: return launch_one<D, 2>(p, a, stream, ev0, ev1);
-        case 4: return launch_one<D, 4>(p, a, stream, ev0, ev1);
-        case 8: return launch_one<D, 8>(p, a, stream, ev0, ev1);
+        case 1: return launch_one<D, 1, FMT>(p, a, stream, ev0, ev1);
+        case 2: return launch_one<D, 2, FMT>(p, a, stream, ev0, ev1);
+        case 4: return launch_one<D, 4, FMT>(p, a, stream, ev0, ev1);
+        case 8:
+            if constexpr (FMT == kKvBf16) return launch_one<D, 8, FMT>(p, a, stream, ev0, ev1);
+            return hipErrorInvalidValue;  // the planner caps 8-bit caches at 4 heads per block
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT>
+static hipError_t launch_valu_f(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                                hipEvent_t ev1) {
+    switch (a.D) {
+        case 64: return launch_valu_d<64, FMT>(p, a, stream, ev0, ev1);
+        case 128: return launch_valu_d<128, FMT>(p, a, stream, ev0, ev1);
+        case 256: return launch_valu_d<256, FMT>(p, a, stream, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode_valu(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                               hipEvent_t ev1) {
-    switch (a.D) {
-        case 64: return launch_valu_d<64>(p, a, stream, ev0, ev1);
-        case 128: return launch_valu_d<128>(p, a, stream, ev0, ev1);
-        case 256: return launch_valu_d<256>(p, a, stream, ev0, ev1);
+    switch (p.kv_format) {
+        case kKvBf16: return launch_valu_f<kKvBf16>(p, a, stream, ev0, ev1);
+        case kKvFp8: return launch_valu_f<kKvFp8>(p, a, stream, ev0, ev1);
+        case kKvInt8: return launch_valu_f<kKvInt8>(p, a, stream, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }

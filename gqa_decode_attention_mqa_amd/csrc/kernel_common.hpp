@@ -24,8 +24,10 @@ typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 // (unit, chunk, head block).
 struct DecodeArgs {
     const uint16_t* q;         // bf16 [rows, Hq, D]
-    const uint16_t* k;         // bf16 [B, Lmax, Hkv, D]
-    const uint16_t* v;         // bf16 [B, Lmax, Hkv, D]
+    const void* k;             // [B, Lmax, Hkv, D] (or pages): bf16, or 8-bit codes
+    const void* v;             // likewise
+    const float* k_scale;      // 8-bit caches: fp32 [B, Hkv, Lmax] (pages: [num_pages, Hkv, page_size]),
+    const float* v_scale;      // one per cached row; NULL for bf16
     const int32_t* seq_lens;   // [B]
     float* out;                // fp32 [rows, Hq, D]
     uint16_t* part_o;          // fp16 [rows * Hkv * max_splits, G, D]: O / l / 2^e per chunk
@@ -60,43 +62,54 @@ struct CombineArgs {
 // touches no memory.
 constexpr int kOutOfRange = 0x40000000;
 
-// Positions covered by chunk s of a row that attends `len` positions.  Without
-// a window, chunk s is [s * chunk, (s + 1) * chunk) cut at len.  With a window
-// of W positions (local attention: the row sees only its last W positions) the
-// first attended position is lo = len - W; the chunks then start at lo rounded
-// down to a multiple of 32, so tiles and pages keep their alignment, and the
-// kernels read positions below lo as zero and mask them.  nsplit is the number
-// of chunks that hold positions (1 for an empty row).
+// Positions covered by chunk s (of max_splits) of a row that attends `len`
+// positions.  Without a window, chunk s is [s * chunk, (s + 1) * chunk) cut at
+// len.  With a window of W positions (local attention: the row sees only its
+// last W positions) the first attended position is lo = len - W; the chunks
+// then start at base = lo rounded down to a multiple of 32, so tiles and pages
+// keep their alignment, and the kernels read positions below lo as zero and
+// mask them.  The last chunk runs to len, so it may hold up to 31 positions
+// more than `chunk` (the planner sizes max_splits for W positions, not W + 31).
+// nsplit is the number of chunks that hold positions (1 for an empty row).
 struct ChunkSpan {
     int lo, p0, p1, nsplit;
 };
-__device__ __forceinline__ ChunkSpan chunk_span(int window, int chunk, int len, int s) {
+__device__ __forceinline__ ChunkSpan chunk_span(int window, int chunk, int max_splits, int len, int s) {
     ChunkSpan c;
     c.lo = (window > 0 && len > window) ? len - window : 0;
     const int base = c.lo & ~31;
     c.p0 = base + s * chunk;
-    c.p1 = min(c.p0 + chunk, len);
-    c.nsplit = len > base ? (len - base + chunk - 1) / chunk : 1;
+    c.p1 = s == max_splits - 1 ? len : min(c.p0 + chunk, len);
+    const int n = len > base ? (len - base + chunk - 1) / chunk : 1;
+    c.nsplit = n < max_splits ? n : max_splits;
     return c;
 }
 
-// Base of the cache rows t0, t0 + 1, ... of kv head kvh of sequence b; the
-// rows a caller reads from it never straddle a page (pages hold a power of two
-// >= 32 positions, and every tile or block starts at a multiple of its own
-// size <= 32).  Only called for rows below the sequence length, so the block
-// table entry read is one of the sequence's own; page indices outside the pool
-// are clamped into it, so a bad table gives wrong data, never a stray read.
-__device__ __forceinline__ const uint16_t* page_rows(const uint16_t* cache, const DecodeArgs& a, int page, int kvh,
-                                                     int t0) {
+// Where position t0 of kv head kvh of sequence b lives: `row` is the index of
+// its D-element cache row (the rows of one position's kv heads are adjacent)
+// and `scale` the index of its scale in an 8-bit cache's scale array.  The
+// rows t0, t0 + 1, ... a caller reads from there never straddle a page (pages
+// hold a power of two >= 32 positions, and every tile or block starts at a
+// multiple of its own size <= 32), and neither do their scales.  Only called
+// for rows below the sequence length, so the block table entry read is one of
+// the sequence's own; page indices outside the pool are clamped into it, so a
+// bad table gives wrong data, never a stray read.
+struct RowLoc {
+    size_t row, scale;
+};
+__device__ __forceinline__ RowLoc page_loc(const DecodeArgs& a, int page, int kvh, int t0) {
     page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-    const size_t row = ((size_t)page << a.page_shift) + (size_t)(t0 & ((1 << a.page_shift) - 1));
-    return cache + (row * a.Hkv + kvh) * a.D;
+    const size_t off = (size_t)(t0 & ((1 << a.page_shift) - 1));
+    return {(((size_t)page << a.page_shift) + off) * a.Hkv + kvh, (((size_t)page * a.Hkv + kvh) << a.page_shift) + off};
 }
-__device__ __forceinline__ const uint16_t* kv_rows(const uint16_t* cache, const DecodeArgs& a, int b, int kvh,
-                                                   int t0) {
-    if (a.block_table)
-        return page_rows(cache, a, a.block_table[(size_t)b * a.max_blocks + (t0 >> a.page_shift)], kvh, t0);
-    return cache + (((size_t)b * a.Lmax + t0) * a.Hkv + kvh) * a.D;
+__device__ __forceinline__ RowLoc kv_loc(const DecodeArgs& a, int b, int kvh, int t0) {
+    if (a.block_table) return page_loc(a, a.block_table[(size_t)b * a.max_blocks + (t0 >> a.page_shift)], kvh, t0);
+    return {((size_t)b * a.Lmax + t0) * a.Hkv + kvh, ((size_t)b * a.Hkv + kvh) * a.Lmax + t0};
+}
+// Byte address of cache row `row` of a cache with EB-byte elements.
+template <int EB>
+__device__ __forceinline__ const unsigned char* row_ptr(const void* cache, const DecodeArgs& a, size_t row) {
+    return static_cast<const unsigned char*>(cache) + row * (size_t)a.D * EB;
 }
 
 // Attended length of a row, with seq_lens clamped to [0, Lmax].
@@ -226,6 +239,7 @@ constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within each 8-lane half row
 constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within each 16-lane row
 constexpr int kDppRowRor8 = 0x128;       // lane i <- lane (i+8) mod 16 within the row
+constexpr int kDppRowRor4 = 0x124;       // lane i <- lane (i+4) mod 16 within the row
 
 // Maximum over the 64 lanes of a wave, in every lane.
 __device__ __forceinline__ float wave_max(float x) {
@@ -252,6 +266,33 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
 }
 constexpr uint32_t kPermLoHalves = 0x05040100u;  // (lo.lo16) | (hi.lo16 << 16)
 constexpr uint32_t kPermHiHalves = 0x07060302u;  // (lo.hi16) | (hi.hi16 << 16)
+
+// Cache element formats (the values of mqa_kv_format).
+constexpr int kKvBf16 = 0;
+constexpr int kKvFp8 = 1;   // E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; 0x7F/0xFF NaN
+constexpr int kKvInt8 = 2;  // two's complement
+
+// Eight 8-bit codes (two dwords, code i in byte i % 4 of dword i / 4) widened
+// to eight bf16 values, element i in the low half of dword i / 2 for even i.
+// Exact: every E4M3 value and every int8 is a bf16 number.
+template <int FMT>
+__device__ __forceinline__ u32x4_t widen8(u32x2_t c) {
+    if constexpr (FMT == kKvFp8) {
+        // v_cvt_scalef32_pk_bf16_fp8 with scale 1: codes of bytes 0,1 (or 2,3) -> two bf16
+        return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false)),
+                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true))};
+    } else {
+        // sign-extend each byte, convert to f32 (exact), keep the upper half of the bits
+        auto pair = [](uint32_t w, int sh) {
+            const float lo = (float)(int)(int8_t)(w >> sh);
+            const float hi = (float)(int)(int8_t)(w >> (sh + 8));
+            return perm_b32(__float_as_uint(hi), __float_as_uint(lo), kPermHiHalves);
+        };
+        return u32x4_t{pair(c.x, 0), pair(c.x, 16), pair(c.y, 0), pair(c.y, 16)};
+    }
+}
 
 // Fused log-sum-exp combine, run by the last chunk of a unit to arrive.  The
 // caller has already written its own partial.  Returns after every thread of

@@ -99,6 +99,8 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         return fail(MQA_ERR_ARG, "combine must be 0, 1 or 2");
     if (o.window < 0)
         return fail(MQA_ERR_ARG, "window must be >= 0 (0 = no window)");
+    if (o.kv_format < MQA_KV_BF16 || o.kv_format > MQA_KV_INT8)
+        return fail(MQA_ERR_ARG, "unknown kv_format");
     // Chunk starts sit up to 31 positions before a window's first position.
     if (o.window > 0 && Lmax > 0x7FFFFFFF - 64)
         return fail(MQA_ERR_UNSUPPORTED, "Lmax too large for a sliding window");
@@ -113,8 +115,10 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         const int heads = p.G < kMfmaMaxHeads ? p.G : kMfmaMaxHeads;
         p.heads_per_block = (int)round_up(heads, kMfmaHeadsPerTile);
     } else {
+        // 8-bit caches: each lane holds twice the columns, so fewer heads per block
+        const int cap = o.kv_format == MQA_KV_BF16 ? kValuMaxHeads : kValuMaxHeads8;
         int gb = 1;
-        while (gb < p.G && gb < kValuMaxHeads) gb *= 2;
+        while (gb < p.G && gb < cap) gb *= 2;
         p.heads_per_block = gb;
     }
     p.head_blocks = (int)ceil_div(p.G, p.heads_per_block);
@@ -122,26 +126,25 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     p.rows = causal ? (long long)B * Lmax : (long long)B;
     const long long units = p.rows * Hkv * p.head_blocks;
 
-    // Positions one row's chunks can span: Lmax, or with a sliding window of W
-    // positions at most W + 31 (chunks start at the window's first position
-    // rounded down to a multiple of 32).
+    // Positions one row attends: Lmax, or W with a sliding window of W
+    // positions.  Windowed chunks start at the window's first position rounded
+    // down to a multiple of 32; the last chunk of a row absorbs those up to 31
+    // extra positions, so `span` chunks still cover every row.
     long long span = Lmax;
-    if (o.window > 0 && (long long)o.window + 31 < span) span = (long long)o.window + 31;
+    if (o.window > 0 && o.window < span) span = o.window;
     p.window = o.window;
+    p.kv_format = o.kv_format;
 
     if (o.chunk > 0) {
         p.chunk = o.chunk;
     } else if (units == 0 || span == 0) {
         p.chunk = kChunkQuantum;
     } else {
-        // Sized for the positions a row attends (the window, when there is
-        // one: its alignment slack only adds a chunk that exits at once for
-        // most rows).  A windowed step is small, so its chunks may go down to
-        // 128 positions (measured on MI355X, B=4, Hq=48, D=256, W=8192:
-        // 14.6 us at 128 against 16.0 us at 256).
+        // A windowed step is small, so its chunks may go down to 128
+        // positions (measured on MI355X, B=4, Hq=48, D=256, W=8192: 14.6 us at
+        // 128 against 16.0 us at 256).
         const bool windowed = o.window > 0 && o.window < Lmax;
-        const long long attended = windowed ? o.window : Lmax;
-        long long c = round_up(ceil_div(attended * units, kTargetWorkgroups), kChunkQuantum);
+        long long c = round_up(ceil_div(span * units, kTargetWorkgroups), kChunkQuantum);
         const long long cmax = p.variant == MQA_VARIANT_MFMA ? kMaxChunkMfma : kMaxChunkValu;
         const long long cmin = windowed ? kChunkQuantum : kMinChunk;
         if (c < cmin) c = cmin;

@@ -26,8 +26,9 @@ constexpr int kMfmaHeadsPerTile = 16;
 constexpr int kMfmaMinGroup = 5;
 // Most query heads one MFMA workgroup serves (four 16-head tiles).
 constexpr int kMfmaMaxHeads = 64;
-// Most query heads one VALU workgroup serves.
+// Most query heads one VALU workgroup serves (bf16 cache; 8-bit caches).
 constexpr int kValuMaxHeads = 8;
+constexpr int kValuMaxHeads8 = 4;
 // Most chunks per unit the fused combine handles (its weights live in LDS).
 constexpr int kFusedMaxSplits = 16;
 // Up to this many chunks per sequence the combine kernel keeps every chunk of
@@ -44,8 +45,9 @@ struct Plan {
     int head_blocks = 1;             // workgroups per (row, kv head, chunk) along heads
     int chunk = 0;                   // positions per split
     int max_splits = 1;              // ceil(span / chunk), >= 1 (span: Lmax, or
-                                     // min(Lmax, window + 31) with a sliding window)
+                                     // min(Lmax, window) with a sliding window)
     int window = 0;                  // sliding window (0 = none)
+    int kv_format = 0;               // mqa_kv_format of the cache
     int combine = 0;                 // 0 none, 1 separate kernel, 2 fused
     long long rows = 0;              // query rows: B (decode) or B * Lmax (prefill)
     long long grid_main = 0;         // workgroups along x of the split kernel

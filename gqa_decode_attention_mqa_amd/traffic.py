@@ -39,6 +39,14 @@ def decode_step_kv_bytes(seq_lens: Iterable[int], Hkv: int, D: int, bytes_per_el
     return kv_cache_bytes(1, Hkv, D, bytes_per_elem, total_tokens, 1)
 
 
+def decode_step_quant_bytes(seq_lens: Iterable[int], Hkv: int, D: int) -> int:
+    """Algorithmic bytes one decode step must read from an 8-bit cache: per
+    attended position and kv head, D one-byte codes of K and of V plus one fp32
+    scale for each."""
+    total_tokens = sum(int(n) for n in seq_lens)
+    return total_tokens * Hkv * (2 * D + 2 * 4)
+
+
 def decode_step_flops(seq_lens: Iterable[int], Hq: int, D: int) -> int:
     """Multiply-adds of q.K^T and P.V counted as 2 flops each: 4 * Hq * D per position."""
     return 4 * Hq * D * sum(int(n) for n in seq_lens)

@@ -164,6 +164,31 @@ def make_prefill_inputs(w: Workload, device="cpu", seed: int | None = None,
     return {"q_seq": q, "k": k, "v": v, "seq_lens": lens, "scale": w.scale}
 
 
+def _page_assignment(lens: torch.Tensor, Lmax: int, page_size: int, seed: int, spare_pages: int):
+    """Seeded placement of each sequence's ceil(len / page_size) blocks on physical pages.
+
+    Returns (block_table [B, max_blocks] int32 on the CPU, -1 past a sequence's
+    last block; [(b, blk, page)] in placement order; num_pages; max_blocks).
+    """
+    B = lens.shape[0]
+    max_blocks = max(1, -(-Lmax // page_size))
+    lens_cpu = lens.to("cpu").tolist()
+    nblocks = [-(-n // page_size) for n in lens_cpu]
+    num_pages = sum(nblocks) + spare_pages
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    perm = torch.randperm(max(num_pages, 1), generator=gen)[:num_pages].tolist()
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    placed = []
+    i = 0
+    for b in range(B):
+        for blk in range(nblocks[b]):
+            table[b, blk] = perm[i]
+            placed.append((b, blk, perm[i]))
+            i += 1
+    return table, placed, num_pages, max_blocks
+
+
 def page_contiguous_cache(inp: dict, page_size: int, seed: int, spare_pages: int = 0,
                           poison_spare: bool = True) -> dict:
     """Move the contiguous caches of ``inp`` (from :func:`make_inputs`) into a paged pool.
@@ -179,15 +204,7 @@ def page_contiguous_cache(inp: dict, page_size: int, seed: int, spare_pages: int
     k, v, lens = inp["k"], inp["v"], inp["seq_lens"]
     B, Lmax, Hkv, D = k.shape
     device = k.device
-    max_blocks = max(1, -(-Lmax // page_size))
-    lens_cpu = lens.to("cpu").tolist()
-    nblocks = [-(-n // page_size) for n in lens_cpu]
-    used = sum(nblocks)
-    num_pages = used + spare_pages
-    gen = torch.Generator(device="cpu")
-    gen.manual_seed(int(seed))
-    perm = torch.randperm(max(num_pages, 1), generator=gen)[:num_pages].tolist()
-    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    table, placed, num_pages, max_blocks = _page_assignment(lens, Lmax, page_size, seed, spare_pages)
     # padded contiguous caches so every block of page_size rows exists
     padded_len = max_blocks * page_size
     if padded_len > Lmax:
@@ -204,17 +221,44 @@ def page_contiguous_cache(inp: dict, page_size: int, seed: int, spare_pages: int
     else:
         k_pages.zero_()
         v_pages.zero_()
-    i = 0
-    for b in range(B):
-        for blk in range(nblocks[b]):
-            page = perm[i]
-            i += 1
-            table[b, blk] = page
-            k_pages[page] = kc[b, blk * page_size:(blk + 1) * page_size]
-            v_pages[page] = vc[b, blk * page_size:(blk + 1) * page_size]
+    for b, blk, page in placed:
+        k_pages[page] = kc[b, blk * page_size:(blk + 1) * page_size]
+        v_pages[page] = vc[b, blk * page_size:(blk + 1) * page_size]
     out = dict(inp)
     out.update({"k_pages": k_pages, "v_pages": v_pages, "block_table": table.to(device),
                 "page_size": page_size, "num_pages": num_pages})
+    return out
+
+
+def page_quant_cache(inp: dict, qc: dict, page_size: int, seed: int, spare_pages: int = 0) -> dict:
+    """Move an 8-bit cache (``qc`` from :func:`quantize_cache` of ``inp``) into a paged pool,
+    with the same seeded placement as :func:`page_contiguous_cache`.
+
+    Returns ``k_pages`` / ``v_pages`` (uint8 [num_pages, page_size, Hkv, D]),
+    ``k_scale_pages`` / ``v_scale_pages`` (fp32 [num_pages, Hkv, page_size]),
+    ``block_table``, ``page_size`` and ``num_pages``.  Spare pages and rows
+    past Lmax hold 0xFF codes (NaN in E4M3) and NaN scales.
+    """
+    lens = inp["seq_lens"]
+    kq = qc["k_codes"]
+    B, Lmax, Hkv, D = kq.shape
+    device = kq.device
+    table, placed, num_pages, max_blocks = _page_assignment(lens, Lmax, page_size, seed, spare_pages)
+    padded_len = max_blocks * page_size
+    out = {"block_table": table.to(device), "page_size": page_size, "num_pages": num_pages}
+    for name in ("k", "v"):
+        codes, sc = qc[name + "_codes"], qc[name + "_scale"]          # [B,L,Hkv,D], [B,Hkv,L]
+        if padded_len > Lmax:
+            codes = torch.cat([codes, torch.full((B, padded_len - Lmax, Hkv, D), 0xFF, dtype=torch.uint8,
+                                                 device=device)], 1)
+            sc = torch.cat([sc, torch.full((B, Hkv, padded_len - Lmax), float("nan"), device=device)], 2)
+        pages = torch.full((max(num_pages, 1), page_size, Hkv, D), 0xFF, dtype=torch.uint8, device=device)
+        spages = torch.full((max(num_pages, 1), Hkv, page_size), float("nan"), dtype=torch.float32, device=device)
+        for b, blk, page in placed:
+            pages[page] = codes[b, blk * page_size:(blk + 1) * page_size]
+            spages[page] = sc[b, :, blk * page_size:(blk + 1) * page_size]
+        out[name + "_pages"] = pages
+        out[name + "_scale_pages"] = spages
     return out
 
 

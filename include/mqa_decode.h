@@ -76,6 +76,14 @@ typedef enum mqa_variant {
     MQA_VARIANT_MFMA = 2  /* bf16 matrix-core tiles, 16 query heads per tile (large groups) */
 } mqa_variant;
 
+/* Element format of the key/value cache. */
+typedef enum mqa_kv_format {
+    MQA_KV_BF16 = 0,     /* bfloat16 values                                                */
+    MQA_KV_FP8_E4M3 = 1, /* 8-bit E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa
+                            bits; 0x7F and 0xFF are NaN) times one fp32 scale per cached row */
+    MQA_KV_INT8 = 2      /* two's-complement int8 codes times one fp32 scale per cached row  */
+} mqa_kv_format;
+
 /* Optional knobs for mqa_decode_attention_ex; zero-initialise for defaults. */
 typedef struct mqa_decode_opts {
     int variant;          /* mqa_variant                                                */
@@ -93,6 +101,9 @@ typedef struct mqa_decode_opts {
                              window) attention: a sequence of length n attends positions
                              max(0, n - W) .. n-1 only, and earlier positions are never
                              read (see mqa_decode_attention_window); < 0 is MQA_ERR_ARG  */
+    int kv_format;        /* mqa_kv_format of k/v (see mqa_decode_attention_quant)         */
+    const float *k_scale; /* 8-bit formats: the caches' per-row scales (device memory,     */
+    const float *v_scale; /* 4-byte aligned); ignored for MQA_KV_BF16                      */
 } mqa_decode_opts;
 
 /* What the planner decided for a shape (host-only query, no HIP call). */
@@ -100,7 +111,7 @@ typedef struct mqa_plan_info {
     int variant;              /* MQA_VARIANT_VALU or MQA_VARIANT_MFMA                  */
     int chunk;                /* positions per split-K chunk                           */
     int max_splits;           /* chunks per sequence: ceil(span / chunk), at least 1, where
-                                 span = Lmax, or min(Lmax, window + 31) with a window  */
+                                 span = Lmax, or min(Lmax, window) with a window      */
     int combine;              /* 1 = separate kernel, 2 = fused, 0 = none needed       */
     int head_blocks;          /* query-head blocks per kv head (VALU path: ceil(G/8))  */
     long long grid_main;      /* workgroups of the split-K kernel                      */
@@ -150,6 +161,35 @@ mqa_status mqa_decode_attention_ex(const void *q, const void *k_cache, const voi
 mqa_status mqa_decode_attention_window(const void *q, const void *k_cache, const void *v_cache,
                                        const int32_t *seq_lens, float *out, int B, int Hq, int Hkv,
                                        int D, int Lmax, int window, float scale, void *stream);
+
+/*
+ * One decode step against a KV cache stored as 8-bit codes ("How To Scale
+ * Your Model", Part 7 "Transformer Inference", passage on quantization: the
+ * KV cache can be kept in int8 or fp8 to save memory bandwidth; "Machine
+ * Learning Engineering and AI Systems at Scale", section "Quantization": E4M3
+ * is the 8-bit inference format and the key/value cache the second thing to
+ * quantize).  Each cached row (one position of one kv head) holds D codes
+ * and one fp32 scale per tensor, and stands for the values code * scale:
+ *   k_codes, v_codes  [B, Lmax, Hkv, D] bytes (kv_format MQA_KV_FP8_E4M3 or
+ *                     MQA_KV_INT8), 16-byte aligned
+ *   k_scale, v_scale  fp32 [B, Hkv, Lmax] (positions contiguous per kv head),
+ *                     4-byte aligned
+ *   q, seq_lens, out, scale as for mqa_decode_attention
+ *   opts              optional (may be NULL); its kv_format and scale
+ *                     pointers are replaced by the explicit arguments
+ * The result is the decode step on the dequantized cache.  Codes and scales
+ * of positions >= seq_lens[b] are never read.  The bytes read per cached row
+ * are 2 * D codes plus two scales, about half of a bf16 cache's.  A
+ * kv_format other than the two 8-bit ones is MQA_ERR_ARG; NULL scale
+ * pointers (when B > 0 and Lmax > 0) are MQA_ERR_NULL.  A paged 8-bit cache
+ * goes through mqa_decode_attention_paged with opts->kv_format and the scale
+ * pointers set, the scales then laid out [num_pages, Hkv, page_size].
+ */
+mqa_status mqa_decode_attention_quant(const void *q, const void *k_codes, const void *v_codes,
+                                      const float *k_scale, const float *v_scale,
+                                      const int32_t *seq_lens, float *out, int B, int Hq, int Hkv,
+                                      int D, int Lmax, int kv_format, float scale, void *stream,
+                                      const mqa_decode_opts *opts);
 
 /*
  * One decode step over a paged KV cache.  Instead of one contiguous

@@ -21,7 +21,8 @@ import torch
 import oracle
 from gqa_decode_attention_mqa_amd import binding
 from gqa_decode_attention_mqa_amd.workloads import (WORKLOADS, Workload, make_inputs, make_prefill_inputs,
-                                                    page_contiguous_cache, poison_positions_below_)
+                                                    page_contiguous_cache, page_quant_cache, poison_positions_below_,
+                                                    quantize_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -381,6 +382,103 @@ def test_window_full_size_sampled(name, window):
                                window, inp["scale"])
     err = check_close(out.index_select(0, sel), ref, "%s window %d" % (name, window))
     print("full %s window %d: %d sequences checked, max abs err %.3g" % (name, window, len(idx), err), flush=True)
+
+
+# ------------------------------------------------------ 8-bit KV cache
+
+def quant_case(w: Workload, kv_format: str):
+    """Seeded bf16 inputs, their 8-bit cache (NaN codes and scales past each length) and the oracle."""
+    inp = make_inputs(w, poison_padding=True)
+    qc = quantize_cache(inp, kv_format)
+    ref = oracle.decode_quant(inp["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
+                              inp["seq_lens"], kv_format, inp["scale"])
+    return to_dev(inp), to_dev(qc), ref
+
+
+@pytest.mark.parametrize("kv_format", ["fp8", "int8"])
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G,Hkv,B", [(1, 2, 3), (4, 2, 4), (8, 1, 3), (48, 1, 3), (20, 2, 3)])
+def test_quant_small_shapes(kv_format, variant, D, G, Hkv, B):
+    w = Workload("q8", B=B, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=700, seed=700 + D + 7 * G + Hkv,
+                 len_lo=0, len_hi=700)
+    dev, qc, ref = quant_case(w, kv_format)
+    for chunk, combine in ((None, None), (128, "separate"), (128, "fused")):
+        print("case quant", kv_format, variant, D, G, Hkv, B, chunk, combine, flush=True)
+        out = binding.decode_quant(dev["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
+                                   dev["seq_lens"], kv_format, dev["scale"], variant=variant, chunk=chunk,
+                                   combine=combine)
+        torch.cuda.synchronize()
+        check_close(out, ref, "quant %s %s D %d G %d chunk %s %s" % (kv_format, variant, D, G, chunk, combine))
+
+
+@pytest.mark.parametrize("kv_format", ["fp8", "int8"])
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("page_size", [32, 128])
+def test_quant_paged(kv_format, variant, page_size):
+    w = Workload("q8pg", B=5, Hq=16, Hkv=2, D=128, Lmax=1000, seed=760 + page_size, len_lo=0, len_hi=1000)
+    inp = make_inputs(w, poison_padding=True)
+    qc = quantize_cache(inp, kv_format)
+    ref = oracle.decode_quant(inp["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
+                              inp["seq_lens"], kv_format, inp["scale"])
+    pg = to_dev(page_quant_cache(inp, qc, page_size, seed=page_size, spare_pages=2))
+    dev = to_dev(inp)
+    for chunk in (None, 128):
+        print("case quant paged", kv_format, variant, page_size, chunk, flush=True)
+        out = binding.decode_paged(dev["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], dev["seq_lens"],
+                                   dev["scale"], variant=variant, chunk=chunk, kv_format=kv_format,
+                                   k_scale=pg["k_scale_pages"], v_scale=pg["v_scale_pages"])
+        torch.cuda.synchronize()
+        check_close(out, ref, "quant paged %s %s page %d chunk %s" % (kv_format, variant, page_size, chunk))
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("window", [1, 45, 300])
+def test_quant_window(variant, window):
+    """fp8 cache with a sliding window, against the oracle run on the window's rows moved to the front."""
+    w = Workload("q8win", B=5, Hq=16, Hkv=2, D=128, Lmax=900, seed=780 + window, len_lo=0, len_hi=900)
+    inp = make_inputs(w, poison_padding=True)
+    qc = quantize_cache(inp, "fp8")
+    lens = inp["seq_lens"]
+    lo = torch.clamp(lens.to(torch.int64) - window, min=0)
+    shifted = {key: torch.full_like(qc[key], 0x7F) for key in ("k_codes", "v_codes")}
+    shifted.update({key: torch.full_like(qc[key], float("nan")) for key in ("k_scale", "v_scale")})
+    for b in range(w.B):
+        n, a0 = int(lens[b]), int(lo[b])
+        for key in ("k_codes", "v_codes"):
+            shifted[key][b, :n - a0] = qc[key][b, a0:n]
+            qc[key][b, :a0] = 0x7F                       # positions before the window: NaN codes
+        for key in ("k_scale", "v_scale"):
+            shifted[key][b, :, :n - a0] = qc[key][b, :, a0:n]
+            qc[key][b, :, :a0] = float("nan")
+    ref = oracle.decode_quant(inp["q"], shifted["k_codes"], shifted["v_codes"], shifted["k_scale"],
+                              shifted["v_scale"], (lens - lo).to(torch.int32), "fp8", inp["scale"])
+    dev, dq = to_dev(inp), to_dev(qc)
+    print("case quant window", variant, window, flush=True)
+    out = binding.decode_quant(dev["q"], dq["k_codes"], dq["v_codes"], dq["k_scale"], dq["v_scale"],
+                               dev["seq_lens"], "fp8", dev["scale"], variant=variant, window=window)
+    torch.cuda.synchronize()
+    check_close(out, ref, "quant window %s W %d" % (variant, window))
+
+
+@pytest.mark.parametrize("name,kv_format", [("palm", "fp8"), ("gqa70b", "fp8"), ("ragged", "fp8"), ("long", "fp8"),
+                                            ("ragged", "int8"), ("palm", "int8")])
+def test_quant_full_size_sampled(name, kv_format):
+    w = WORKLOADS[name]
+    print("case full quant", name, kv_format, flush=True)
+    inp = make_inputs(w, device=DEV, poison_padding=w.ragged)
+    qc = quantize_cache(inp, kv_format)
+    del inp["k"], inp["v"]
+    out = binding.decode_quant(inp["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
+                               inp["seq_lens"], kv_format, inp["scale"])
+    torch.cuda.synchronize()
+    idx = sample_indices(inp["seq_lens"], SAMPLES[name])
+    sel = torch.tensor(idx, device=DEV)
+    pick = lambda t: t.index_select(0, sel).cpu()
+    ref = oracle.decode_quant(pick(inp["q"]), pick(qc["k_codes"]), pick(qc["v_codes"]), pick(qc["k_scale"]),
+                              pick(qc["v_scale"]), pick(inp["seq_lens"]), kv_format, inp["scale"])
+    err = check_close(out.index_select(0, sel), ref, "%s %s" % (name, kv_format))
+    print("full %s %s: %d sequences checked, max abs err %.3g" % (name, kv_format, len(idx), err), flush=True)
 
 
 # ------------------------------------------------------ full-size workloads

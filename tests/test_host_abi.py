@@ -144,27 +144,29 @@ def test_chunk_schedule_covers_every_valid_position_once():
 def test_window_schedule_covers_the_window_once(window):
     """With a window W the split kernels start chunk s at base + s*chunk, where
     base is the first attended position lo = max(0, n - W) rounded down to a
-    multiple of 32, and mask positions below lo.  Every position of [lo, n)
-    must fall in exactly one chunk s < max_splits, chunk starts must stay
-    32-aligned (tiles and pages), and the plan's splits must bound the span."""
+    multiple of 32, mask positions below lo, and let the last of the plan's
+    chunks run to n.  Every position of [lo, n) must fall in exactly one chunk,
+    chunk starts must stay 32-aligned (tiles and pages), and no chunk may hold
+    more than chunk + 31 positions."""
     Lmax = 8192
     p = binding.plan(256, 32, 8, 128, Lmax, window=window)
     C, S = p["chunk"], p["max_splits"]
-    assert S == -(-min(Lmax, window + 31) // C)
+    assert S == -(-min(Lmax, window) // C)
     for n in sorted({0, 1, 31, 32, 33, window - 1, window, window + 1, window + 31, window + 32,
                      Lmax - 33, Lmax - 1, Lmax} & set(range(0, Lmax + 1))):
         lo = max(0, n - window)
         base = lo & ~31
-        nsplit = -(-(n - base) // C) if n > base else 1
-        assert nsplit <= S
+        nsplit = min(-(-(n - base) // C) if n > base else 1, S)
         seen = []
         for s in range(S):
             p0 = base + s * C
             assert p0 % 32 == 0
             if s > 0 and p0 >= n:
                 continue
+            p1 = n if s == S - 1 else min(p0 + C, n)
             assert s < nsplit or n == 0
-            seen.extend(t for t in range(p0, min(p0 + C, n)) if t >= lo)
+            assert p1 - p0 <= C + 31
+            seen.extend(t for t in range(p0, p1) if t >= lo)
         assert seen == list(range(lo, n))
 
 
@@ -178,13 +180,47 @@ def test_window_arguments():
     assert binding.plan(8, 32, 8, 128, 4096, window=4096) == binding.plan(8, 32, 8, 128, 4096)
     assert binding.plan(8, 32, 8, 128, 4096, window=1 << 30) == binding.plan(8, 32, 8, 128, 4096)
     assert binding.plan(2, 8, 1, 64, 600, window=600) == binding.plan(2, 8, 1, 64, 600)
-    # chunks sized for the window itself: PaLM-shaped batch, W = 1024 -> 256-position chunks
-    # (four per window, plus one for the alignment slack)
+    # chunks sized for the window itself: PaLM-shaped batch, W = 1024 -> four 256-position chunks
     p = binding.plan(64, 48, 1, 256, 2048, window=1024)
-    assert p["chunk"] == 256 and p["max_splits"] == 5
-    # the window bounds the grid: 8 chunks of 512 without it, at most 2 with W = 512
+    assert p["chunk"] == 256 and p["max_splits"] == 4
+    # the window bounds the grid: 8 chunks of 512 without it, 1 with W = 512 (the
+    # last chunk absorbs the window start's alignment to 32)
     assert binding.plan(64, 48, 1, 256, 4096, chunk=512)["max_splits"] == 8
-    assert binding.plan(64, 48, 1, 256, 4096, chunk=512, window=512)["max_splits"] == 2
+    assert binding.plan(64, 48, 1, 256, 4096, chunk=512, window=512)["max_splits"] == 1
+
+
+def quant_call(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, lens=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, D=128, Lmax=64,
+               fmt=1, scale=0.1, opts=None):
+    return lib.mqa_decode_attention_quant(q, k, v, ks, vs, lens, out, B, Hq, Hkv, D, Lmax, fmt, scale, None, opts)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(fmt=0), ERR_ARG), (dict(fmt=3), ERR_ARG), (dict(fmt=-1), ERR_ARG),
+    (dict(ks=0), ERR_NULL), (dict(vs=0), ERR_NULL), (dict(ks=FAKE + 2), ERR_ALIGN), (dict(vs=FAKE + 1), ERR_ALIGN),
+    (dict(k=0), ERR_NULL), (dict(k=FAKE + 8), ERR_ALIGN), (dict(Hq=7), ERR_SHAPE), (dict(D=96), ERR_UNSUPPORTED),
+    (dict(fmt=2, ks=0), ERR_NULL),
+])
+def test_quant_arguments_are_rejected_before_any_hip_call(kw, expect):
+    # every other argument is valid, and B = 2, so the call would launch if the checks passed
+    assert quant_call(**kw) == expect
+    assert lib.mqa_last_error()
+
+
+def test_quant_empty_batch_and_cache_need_no_scales():
+    assert quant_call(q=0, k=0, v=0, ks=0, vs=0, lens=0, out=0, B=0) == OK
+
+
+def test_quant_plan():
+    with pytest.raises(binding.MqaError):
+        binding.plan(2, 8, 2, 128, 64, kv_format=3)
+    # 8-bit caches hold twice the columns per lane in the vector kernel: at most 4 heads per block
+    p = binding.plan(4, 16, 2, 128, 512, variant="valu", kv_format="fp8")
+    assert p["head_blocks"] == 2 and p["block_main"] == 256
+    assert binding.plan(4, 16, 2, 128, 512, variant="valu")["head_blocks"] == 1
+    # the matrix-core plan does not depend on the format
+    a = binding.plan(64, 48, 1, 256, 2048, kv_format="fp8")
+    b = binding.plan(64, 48, 1, 256, 2048)
+    assert a == b
 
 
 def paged_call(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, D=128,

@@ -4,7 +4,7 @@ import os
 
 import pytest
 
-from gqa_decode_attention_mqa_amd.traffic import (decode_step_flops, decode_step_kv_bytes,
+from gqa_decode_attention_mqa_amd.traffic import (decode_step_flops, decode_step_kv_bytes, decode_step_quant_bytes,
                                                   kv_cache_bytes, max_context_tokens)
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kv_cache_worked_examples.json")))
@@ -37,3 +37,11 @@ def test_decode_step_bytes_for_the_five_workloads():
     assert decode_step_kv_bytes([131072] * 4, 1, 256) == 512 * 2 ** 20
     assert decode_step_kv_bytes([1, 8192], 8, 128) == 8193 * 4096
     assert decode_step_flops([2048] * 64, 48, 256) == 4 * 48 * 256 * 2048 * 64
+
+
+def test_decode_step_bytes_of_an_8bit_cache():
+    # per position and kv head: D codes of K and of V (one byte each) plus one fp32 scale each
+    assert decode_step_quant_bytes([2048] * 64, 1, 256) == 64 * 2048 * (512 + 8)
+    assert decode_step_quant_bytes([4096] * 32, 8, 128) == 32 * 4096 * 8 * 264
+    # half of the bf16 bytes plus the scales
+    assert decode_step_quant_bytes([100], 2, 64) == decode_step_kv_bytes([100], 2, 64) // 2 + 100 * 2 * 8
