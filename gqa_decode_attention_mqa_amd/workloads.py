@@ -146,6 +146,25 @@ def make_inputs(w: Workload, device="cpu", seed: int | None = None,
     return {"q": q, "k": k, "v": v, "seq_lens": lens, "scale": w.scale}
 
 
+def make_multi_inputs(w: Workload, tokens: int, device="cpu", seed: int | None = None,
+                      poison_padding: bool = False) -> dict:
+    """Like :func:`make_inputs` but with ``tokens`` new query tokens per sequence:
+    q [B, tokens, Hq, D] (their keys and values sit at the last ``tokens`` cached positions)."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(w.seed if seed is None else seed))
+    lens = draw_lengths(w, gen, device)
+    q = _randn_bf16((w.B, tokens, w.Hq, w.D), gen, device)
+    if w.q_mult != 1.0:
+        q = q * w.q_mult
+    k = _randn_bf16((w.B, w.Lmax, w.Hkv, w.D), gen, device)
+    v = _randn_bf16((w.B, w.Lmax, w.Hkv, w.D), gen, device)
+    if poison_padding:
+        poison_padding_(k, lens)
+        poison_padding_(v, lens)
+    return {"q": q, "k": k, "v": v, "seq_lens": lens, "scale": w.scale}
+
+
 def make_prefill_inputs(w: Workload, device="cpu", seed: int | None = None,
                         poison_padding: bool = False) -> dict:
     """Like :func:`make_inputs` but with one query per position: q_seq [B, Lmax, Hq, D]."""

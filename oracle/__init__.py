@@ -66,6 +66,8 @@ def _load():
             [ctypes.c_double, f64p]
         lib.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
         lib.oracle_fp8_e4m3_value.restype = ctypes.c_double
+        lib.oracle_decode_multi.argtypes = [u16p, u16p, u16p, i32p] + [ctypes.c_int] * 6 + \
+            [ctypes.c_double, f64p]
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_set_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
@@ -261,4 +263,23 @@ def decode_quant(q, k_codes, v_codes, k_scale, v_scale, seq_lens, kv_format: str
                                      _ptr(out, ctypes.c_double))
     if rc != 0:
         raise ValueError("oracle_decode_quant rejected its arguments (code %d)" % rc)
+    return out
+
+
+def decode_multi(q, k_cache, v_cache, seq_lens, scale: float):
+    """fp64 decode of T tokens per sequence, causal among themselves: token i of
+    sequence b attends positions 0 .. seq_lens[b] - T + i.  q [B,T,Hq,D] ->
+    ``out`` [B,T,Hq,D] float64."""
+    qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+    lens = _lens(seq_lens)
+    B, T, Hq, D = qb.shape
+    Bk, Lmax, Hkv, Dk = kb.shape
+    if vb.shape != kb.shape or Bk != B or Dk != D or lens.shape != (B,):
+        raise ValueError("inconsistent shapes q%s k%s v%s lens%s" % (qb.shape, kb.shape, vb.shape, lens.shape))
+    out = np.empty((B, T, Hq, D), dtype=np.float64)
+    rc = _load().oracle_decode_multi(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+                                     _ptr(vb, ctypes.c_uint16), _ptr(lens, ctypes.c_int32),
+                                     B, T, Hq, Hkv, D, Lmax, float(scale), _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_decode_multi rejected its arguments (code %d)" % rc)
     return out

@@ -516,6 +516,80 @@ int oracle_decode_quant(const uint16_t *q, const uint8_t *kq, const uint8_t *vq,
 }
 
 /*
+ * Decode of T new tokens per sequence at once (speculative verification,
+ * chunked prefill: "How To Scale Your Model", Part 7 "Transformer Inference",
+ * passages on prefill and on speculative sampling, where several new tokens
+ * are scored against the cache in one step).  The T tokens' own keys and
+ * values are already in the cache at positions n-T .. n-1 (n = seq_lens[b]),
+ * and they are causal among themselves: token i (0 .. T-1) sits at position
+ * n-T+i and attends positions 0 .. n-T+i.  A token whose position would be
+ * negative (n < T) attends nothing and gets a zero row.
+ *   q    [B, T, Hq, D]   bf16 bits
+ *   k, v [B, Lmax, Hkv, D]
+ *   out  [B, T, Hq, D]   double
+ * Each (b, i, h) is the attention of oracle_decode with length n-T+i+1.
+ * Returns 0, or a negative code on a bad shape, length or token count.
+ */
+int oracle_decode_multi(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const int32_t *seq_lens, int B, int T, int Hq, int Hkv, int D,
+                        int Lmax, double scale, double *out)
+{
+    int rc = check_shape(B, Hq, Hkv, D, Lmax);
+    if (rc) return rc;
+    if (T < 1) return -8;
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || seq_lens[b] > Lmax) return -3;
+
+    const int G = Hq / Hkv;
+    const long long rows = (long long)B * T * Hq;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long r = 0; r < rows; ++r) {
+        const int h = (int)(r % Hq);
+        const int i = (int)((r / Hq) % T);
+        const int b = (int)(r / ((long long)Hq * T));
+        const int g = h / G;
+        const int n = seq_lens[b] - T + 1 + i; /* positions token i attends */
+        double *o = out + (size_t)r * D;
+
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (n <= 0) continue;
+
+        double *s = (double *)malloc((size_t)n * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        const uint16_t *qrow = q + (size_t)r * D;
+        for (int j = 0; j < n; ++j) {
+            const uint16_t *krow = k + (((size_t)b * Lmax + j) * Hkv + g) * D;
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += bf16_bits_to_double(qrow[d]) * bf16_bits_to_double(krow[d]);
+            s[j] = scale * acc;
+        }
+        double m = s[0];
+        for (int j = 1; j < n; ++j)
+            if (s[j] > m) m = s[j];
+        double Z = 0.0;
+        for (int j = 0; j < n; ++j) {
+            s[j] = exp(s[j] - m);
+            Z += s[j];
+        }
+        for (int j = 0; j < n; ++j) {
+            const uint16_t *vrow = v + (((size_t)b * Lmax + j) * Hkv + g) * D;
+            for (int d = 0; d < D; ++d)
+                o[d] += s[j] * bf16_bits_to_double(vrow[d]);
+        }
+        for (int d = 0; d < D; ++d) o[d] /= Z;
+        free(s);
+    }
+    return failed ? -4 : 0;
+}
+
+/*
  * Full causal self-attention over a whole sequence, recomputed with no cache
  * (the work the KV cache avoids).
  *   q_seq   [B, Lmax, Hq, D]   bf16 bits: one query per position

@@ -28,7 +28,7 @@ import torch.nn.functional as F
 
 import oracle
 from gqa_decode_attention_mqa_amd.workloads import (Workload, make_inputs, make_prefill_inputs, page_contiguous_cache,
-                                                    poison_positions_below_, quantize_cache)
+                                                    make_multi_inputs, poison_positions_below_, quantize_cache)
 
 TIGHT = 1e-12
 
@@ -619,3 +619,67 @@ def test_quant_oracle_rejects_an_unknown_format():
     with pytest.raises(KeyError):
         oracle.decode_quant(inp["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
                             inp["seq_lens"], "fp4", inp["scale"])
+
+
+# ------------------------------------------------------------ multi-token decode
+#
+# T new tokens per sequence scored against the cache in one step, causal among
+# themselves ("How To Scale Your Model", Part 7, passages on prefill and on
+# speculative sampling): token i attends positions 0 .. n - T + i.
+
+@pytest.mark.parametrize("T", [1, 2, 3, 8])
+def test_multi_token_rows_are_the_causal_prefill_rows(T):
+    """Token i of sequence b is row n - T + i of causal attention with no cache
+    (the already pinned oracle_causal_prefill), fed the same query."""
+    w = Workload("multi", B=4, Hq=12, Hkv=3, D=16, Lmax=30, seed=801 + T, len_lo=T, len_hi=30)
+    inp = make_multi_inputs(w, T, poison_padding=True)
+    out = oracle.decode_multi(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    lens = inp["seq_lens"]
+    q_seq = torch.zeros((w.B, w.Lmax, w.Hq, w.D), dtype=torch.bfloat16)
+    for b in range(w.B):
+        n = int(lens[b])
+        q_seq[b, n - T:n] = inp["q"][b]
+    full = oracle.causal_prefill(q_seq, inp["k"], inp["v"], lens, inp["scale"])
+    for b in range(w.B):
+        n = int(lens[b])
+        np.testing.assert_allclose(out[b], full[b, n - T:n], rtol=0, atol=TIGHT)
+
+
+def test_multi_token_with_one_token_is_decode():
+    w = Workload("multi1", B=3, Hq=8, Hkv=2, D=32, Lmax=40, seed=811, len_lo=0, len_hi=40)
+    inp = make_inputs(w, poison_padding=True)
+    a = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    b = oracle.decode_multi(inp["q"].unsqueeze(1), inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    assert np.array_equal(a, b[:, 0])
+
+
+def test_multi_token_matches_library_attention_with_an_offset_causal_mask():
+    T = 4
+    w = Workload("multi-lib", B=3, Hq=8, Hkv=2, D=16, Lmax=25, seed=812, len_lo=T, len_hi=25)
+    inp = make_multi_inputs(w, T, poison_padding=True)
+    out = oracle.decode_multi(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    for b in range(w.B):
+        n = int(inp["seq_lens"][b])
+        i = torch.arange(T).view(T, 1)
+        j = torch.arange(n).view(1, n)
+        mask = j <= n - T + i                                  # True = attend
+        qb = f64(inp["q"][b]).permute(1, 0, 2).unsqueeze(0)    # [1, Hq, T, D]
+        kb = f64(inp["k"][b, :n]).permute(1, 0, 2).unsqueeze(0)
+        vb = f64(inp["v"][b, :n]).permute(1, 0, 2).unsqueeze(0)
+        ref = F.scaled_dot_product_attention(qb, kb, vb, attn_mask=mask, scale=inp["scale"], enable_gqa=True)
+        np.testing.assert_allclose(out[b], ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=TIGHT)
+
+
+def test_multi_token_short_sequences_give_zero_rows_for_tokens_before_the_start():
+    """n < T: tokens at negative positions attend nothing; the others see 0 .. n - T + i."""
+    T = 5
+    w = Workload("multi-short", B=1, Hq=4, Hkv=1, D=8, Lmax=8, seed=813)
+    inp = make_multi_inputs(w, T)
+    lens = torch.tensor([3], dtype=torch.int32)
+    out = oracle.decode_multi(inp["q"], inp["k"], inp["v"], lens, inp["scale"])
+    assert np.array_equal(out[0, :2], np.zeros_like(out[0, :2]))       # positions -2, -1
+    vv = f64(inp["v"][0, 0, 0]).numpy()
+    for h in range(4):                                                  # token 2 sees position 0 only
+        assert np.array_equal(out[0, 2, h], vv)
+    one = oracle.decode(inp["q"][:, 4], inp["k"], inp["v"], lens, inp["scale"])
+    np.testing.assert_allclose(out[:, 4], one, rtol=0, atol=TIGHT)     # the last token sees all three
