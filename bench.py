@@ -84,6 +84,9 @@ def parse_args(argv=None):
     ap.add_argument("--kv-format", default="bf16", choices=["bf16", "fp8", "int8"],
                     help="cache element format: bf16, or 8-bit codes (E4M3 or int8) with one fp32 scale "
                          "per cached row, made from the bf16 draw by the seeded per-row quantizer")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="query tokens per sequence decoded at once (causal among themselves; the cache is "
+                         "read once for all of them); 1 = the decode step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -102,12 +105,14 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 5}))
 
 
-def cpu_baseline(w, inp, target_s: float, window: int = 0, kv_format: str = "bf16"):
+def cpu_baseline(w, inp, target_s: float, window: int = 0, kv_format: str = "bf16", tokens: int = 1):
     """The oracle, as it stands, on whole decode steps of set 0 (or a prefix of the batch)."""
     import oracle
     q, k, v, lens = inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu()
     threads = oracle.max_threads()
-    if kv_format != "bf16":
+    if tokens > 1:
+        run = lambda qq, kk, vv, ll: oracle.decode_multi(qq, kk, vv, ll, inp["scale"])
+    elif kv_format != "bf16":
         ks, vs = inp["k_scale"].cpu(), inp["v_scale"].cpu()
         run = lambda qq, kk, vv, ll: oracle.decode_quant(qq, kk, vv, ks[:len(ll)], vs[:len(ll)], ll, kv_format,
                                                          inp["scale"])
@@ -156,15 +161,22 @@ def main(argv=None):
 
     from gqa_decode_attention_mqa_amd import binding
     from gqa_decode_attention_mqa_amd.traffic import decode_step_kv_bytes, decode_step_quant_bytes
-    from gqa_decode_attention_mqa_amd.workloads import (WORKLOADS, make_inputs, page_contiguous_cache,
-                                                        page_quant_cache, quantize_cache)
+    from gqa_decode_attention_mqa_amd.workloads import (WORKLOADS, make_inputs, make_multi_inputs,
+                                                        page_contiguous_cache, page_quant_cache, quantize_cache)
 
     w = WORKLOADS[args.workload]
+    if args.tokens > 1 and (args.page_size or args.window or args.kv_format != "bf16"):
+        print("bench.py: --tokens > 1 is timed on the contiguous bf16 cache only", file=sys.stderr)
+        return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = binding.load_library()
 
-    base = make_inputs(w, device=dev)
+    if args.tokens > 1:
+        make = lambda seed=None, seq_lens=None: make_multi_inputs(w, args.tokens, device=dev, seed=seed)
+    else:
+        make = lambda seed=None, seq_lens=None: make_inputs(w, device=dev, seed=seed, seq_lens=seq_lens)
+    base = make()
     lens = base["seq_lens"]
     # positions attended: all of them, or the last `window` of each sequence
     attended = [min(n, args.window) if args.window else n for n in lens.cpu().tolist()]
@@ -173,12 +185,16 @@ def main(argv=None):
         (lambda n: decode_step_kv_bytes(n, w.Hkv, w.D))
     set_bytes = step_bytes(attended)  # bytes one step reads from a set
     nsets = min(MAX_SETS, max(1, math.ceil(MALL_DEFEAT_BYTES / max(set_bytes, 1))))
-    sets = [base] + [make_inputs(w, device=dev, seed=w.seed + 1000 * i, seq_lens=lens) for i in range(1, nsets)]
-    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    sets = [base] + [make(seed=w.seed + 1000 * i, seq_lens=lens) for i in range(1, nsets)]
+    if args.tokens > 1:
+        for s in sets[1:]:
+            s["seq_lens"] = lens  # every set runs the same lengths
+    out = torch.empty((w.B, args.tokens, w.Hq, w.D) if args.tokens > 1 else (w.B, w.Hq, w.D),
+                      dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk, args.combine,
-                        window=args.window, kv_format=args.kv_format)
+                        window=args.window, kv_format=args.kv_format, tokens=args.tokens)
 
     # 8-bit caches: each set's bf16 draw is quantized per row (the codes and
     # scales replace it); the scale pointers travel in each set's options
@@ -207,6 +223,11 @@ def main(argv=None):
                           s["block_table"].data_ptr(), s["seq_lens"].data_ptr(), out.data_ptr(), w.B, w.Hq,
                           w.Hkv, w.D, s["num_pages"], args.page_size, s["block_table"].shape[1], w.scale, sptr))
         fn = lib.mqa_decode_attention_paged
+    elif args.tokens > 1:
+        for s in sets:
+            calls.append((s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(), s["seq_lens"].data_ptr(),
+                          out.data_ptr(), w.B, args.tokens, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, sptr))
+        fn = lib.mqa_decode_attention_multi
     else:
         for s in sets:
             calls.append((s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(), s["seq_lens"].data_ptr(),
@@ -261,7 +282,8 @@ def main(argv=None):
     achieved = kv_bytes / (mean_kern_ms * 1e-3) / 1e9
     traffic = read_traffic(w.name + ("_paged%d" % args.page_size if args.page_size else "")
                            + ("_window%d" % args.window if args.window else "")
-                           + ("_" + args.kv_format if q8 else ""))
+                           + ("_" + args.kv_format if q8 else "")
+                           + ("_tokens%d" % args.tokens if args.tokens > 1 else ""))
 
     result = {
         "metric": "decode-attention steps/sec and achieved HBM GB/s (% of MI355X peak)",
@@ -280,7 +302,9 @@ def main(argv=None):
             "workload": w.description + (" (paged cache, %d-position pages)" % args.page_size
                                          if args.page_size else "")
                         + (" (sliding window of %d positions)" % args.window if args.window else "")
-                        + (" (%s cache, one fp32 scale per row)" % args.kv_format if q8 else ""),
+                        + (" (%s cache, one fp32 scale per row)" % args.kv_format if q8 else "")
+                        + (" (%d query tokens per sequence)" % args.tokens if args.tokens > 1 else ""),
+            "tokens": args.tokens,
             "kv_format": args.kv_format,
             "page_size": args.page_size or None,
             "window": args.window or None,
@@ -306,7 +330,8 @@ def main(argv=None):
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, cpu_set, args.cpu_seconds, args.window, args.kv_format)
+        result["cpu_baseline"] = cpu_baseline(w, cpu_set, args.cpu_seconds, args.window, args.kv_format,
+                                              args.tokens)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -69,6 +69,9 @@ def load_library():
     lib.mqa_decode_attention_quant.argtypes = [vp, vp, vp, vp, vp, i32p, f32p] + ints + \
         [ctypes.c_int, ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
     lib.mqa_decode_attention_quant.restype = ctypes.c_int
+    lib.mqa_decode_attention_multi.argtypes = [vp, vp, vp, i32p, f32p] + [ctypes.c_int] * 6 + \
+        [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
+    lib.mqa_decode_attention_multi.restype = ctypes.c_int
     lib.mqa_decode_attention_ex.argtypes = [vp, vp, vp, i32p, f32p] + ints + \
         [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
     lib.mqa_decode_attention_ex.restype = ctypes.c_int
@@ -76,6 +79,9 @@ def load_library():
     lib.mqa_prefill_attention.restype = ctypes.c_int
     lib.mqa_decode_plan.argtypes = ints + [ctypes.c_float, ctypes.POINTER(DecodeOpts), ctypes.POINTER(PlanInfo)]
     lib.mqa_decode_plan.restype = ctypes.c_int
+    lib.mqa_decode_plan_multi.argtypes = [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.POINTER(DecodeOpts),
+                                                              ctypes.POINTER(PlanInfo)]
+    lib.mqa_decode_plan_multi.restype = ctypes.c_int
     lib.mqa_status_string.argtypes = [ctypes.c_int]
     lib.mqa_status_string.restype = ctypes.c_char_p
     lib.mqa_last_error.argtypes = []
@@ -117,13 +123,14 @@ def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None
 
 
 def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None, window=None,
-         kv_format=None) -> dict:
-    """The library's launch plan for a decode call of this shape (host only)."""
+         kv_format=None, tokens=1) -> dict:
+    """The library's launch plan for a decode call of this shape (host only);
+    ``tokens`` > 1 plans a multi-token call."""
     lib = load_library()
     info = PlanInfo()
     opts = make_opts(variant, chunk, combine, window=window, kv_format=kv_format)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib.mqa_decode_plan(B, Hq, Hkv, D, Lmax, sc, ctypes.byref(opts), ctypes.byref(info)),
+    _check(lib.mqa_decode_plan_multi(B, int(tokens), Hq, Hkv, D, Lmax, sc, ctypes.byref(opts), ctypes.byref(info)),
            "mqa_decode_plan")
     return {"variant": VARIANT_NAMES.get(info.variant, info.variant), "chunk": info.chunk,
             "max_splits": info.max_splits, "combine": info.combine, "head_blocks": info.head_blocks,
@@ -271,6 +278,50 @@ def decode_quant(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor, 
                                         v_scale.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D,
                                         Lmax, KV_FORMATS[kv_format], sc, _stream_ptr(dev), ctypes.byref(opts))
     _check(st, "mqa_decode_attention_quant")
+    return out
+
+
+def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                 scale: float | None = None, out: torch.Tensor | None = None, variant=None, chunk=None,
+                 combine=None, events=None, kv_format=None, k_scale=None, v_scale=None) -> torch.Tensor:
+    """T new tokens per sequence through ``mqa_decode_attention_multi``: q [B,T,Hq,D] bf16
+    -> fp32 [B,T,Hq,D]; token i attends positions 0 .. seq_lens[b] - T + i.  Caches as for
+    :func:`decode` (bf16), or 8-bit codes with ``kv_format`` and scales as for :func:`decode_quant`."""
+    if q.device.type != "cuda":
+        raise ValueError("decode_multi runs on the GPU; q is on %s" % q.device)
+    dev = q.device
+    _require(q, "q", torch.bfloat16, 4, dev)
+    fmt = KV_FORMATS[kv_format] if isinstance(kv_format, str) else int(kv_format or 0)
+    _require(k_cache, "k_cache", torch.uint8 if fmt else torch.bfloat16, 4, dev)
+    _require(v_cache, "v_cache", torch.uint8 if fmt else torch.bfloat16, 4, dev)
+    _require(seq_lens, "seq_lens", torch.int32, 1, dev)
+    B, T, Hq, D = q.shape
+    Bk, Lmax, Hkv, Dk = k_cache.shape
+    if v_cache.shape != k_cache.shape or Bk != B or Dk != D or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch: q %s, k %s, v %s, seq_lens %s" % (
+            tuple(q.shape), tuple(k_cache.shape), tuple(v_cache.shape), tuple(seq_lens.shape)))
+    sk = sv = None
+    if fmt:
+        _require(k_scale, "k_scale", torch.float32, 3, dev)
+        _require(v_scale, "v_scale", torch.float32, 3, dev)
+        if tuple(k_scale.shape) != (B, Hkv, Lmax) or v_scale.shape != k_scale.shape:
+            raise ValueError("scales must have shape [B, Hkv, Lmax]")
+        sk, sv = k_scale.data_ptr(), v_scale.data_ptr()
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, 4, dev)
+    if tuple(out.shape) != (B, T, Hq, D):
+        raise ValueError("out must have shape %s" % ((B, T, Hq, D),))
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    ev_b = ev_e = None
+    if events is not None:
+        ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e, None, fmt, sk, sv)
+    lib = load_library()
+    st = lib.mqa_decode_attention_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                        out.data_ptr(), B, T, Hq, Hkv, D, Lmax, sc, _stream_ptr(dev),
+                                        ctypes.byref(opts))
+    _check(st, "mqa_decode_attention_multi")
     return out
 
 

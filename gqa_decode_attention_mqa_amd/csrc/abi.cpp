@@ -96,10 +96,10 @@ mqa_status get_workspace(hipStream_t stream, size_t bytes, size_t ncounters, voi
 
 mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_lens, float* out,
                int B, int Hq, int Hkv, int D, int Lmax, float scale, void* stream_ptr,
-               const mqa_decode_opts* opts, bool causal, const mqa::PagedCache* paged = nullptr) {
+               const mqa_decode_opts* opts, bool causal, const mqa::PagedCache* paged = nullptr, int T = 1) {
     mqa::set_error("");
     Plan plan;
-    mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, causal, &plan);
+    mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, causal, &plan, T);
     if (st != MQA_OK) return st;
     st = mqa::check_pointers(B, Lmax, q, k, v, seq_lens, out);
     if (st != MQA_OK) return st;
@@ -149,6 +149,8 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.D = D;
     a.Lmax = Lmax;
     a.G = plan.G;
+    a.T = plan.T;
+    a.GT = plan.GT;
     a.chunk = plan.chunk;
     a.max_splits = plan.max_splits;
     a.causal = causal ? 1 : 0;
@@ -174,6 +176,8 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
         c.D = D;
         c.Lmax = Lmax;
         c.G = plan.G;
+        c.T = plan.T;
+        c.GT = plan.GT;
         c.chunk = plan.chunk;
         c.max_splits = plan.max_splits;
         c.causal = a.causal;
@@ -229,6 +233,12 @@ mqa_status mqa_decode_attention_quant(const void* q, const void* k_codes, const 
     return run(q, k_codes, v_codes, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, false);
 }
 
+mqa_status mqa_decode_attention_multi(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* seq_lens, float* out, int B, int T, int Hq, int Hkv,
+                                      int D, int Lmax, float scale, void* stream, const mqa_decode_opts* opts) {
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false, nullptr, T);
+}
+
 mqa_status mqa_decode_attention_paged(const void* q, const void* k_pages, const void* v_pages,
                                       const int32_t* block_table, const int32_t* seq_lens, float* out,
                                       int B, int Hq, int Hkv, int D, int num_pages, int page_size,
@@ -251,9 +261,14 @@ mqa_status mqa_prefill_attention(const void* q_seq, const void* k_cache, const v
 
 mqa_status mqa_decode_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                            const mqa_decode_opts* opts, mqa_plan_info* info) {
+    return mqa_decode_plan_multi(B, 1, Hq, Hkv, D, Lmax, scale, opts, info);
+}
+
+mqa_status mqa_decode_plan_multi(int B, int T, int Hq, int Hkv, int D, int Lmax, float scale,
+                                 const mqa_decode_opts* opts, mqa_plan_info* info) {
     mqa::set_error("");
     Plan p;
-    const mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, false, &p);
+    const mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, false, &p, T);
     if (st != MQA_OK) return st;
     if (info) {
         info->variant = p.variant;
@@ -300,6 +315,6 @@ void mqa_release_workspaces(void) {
     g_ws.clear();
 }
 
-int mqa_version(void) { return 130; }
+int mqa_version(void) { return 140; }
 
 }  // extern "C"

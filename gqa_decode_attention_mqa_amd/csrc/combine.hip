@@ -7,7 +7,10 @@
 //     out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M),
 // an exact identity of softmax over a partition of the positions.
 //
-// Many chunks: one workgroup per (row, query head), 256 threads.  Thread t owns
+// A row with T query tokens has T * Hq query rows (token i, head h); their
+// partials sit at query row i * G + h % G of unit (row, h / G).
+//
+// Many chunks: one workgroup per (row, token, query head), 256 threads.  Thread t owns
 // a slot of four columns (t mod D/4) and the chunks s = t div (D/4), step 256/(D/4), so
 // several chunks are read in parallel; the per-thread sums are then added in a
 // fixed order through LDS, so the result is bitwise reproducible for a plan.
@@ -28,19 +31,21 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     __shared__ float s_w[256];
 
     const int tid = threadIdx.x;
-    const long long rh = blockIdx.x;
+    const long long rh = blockIdx.x;  // (row * T + token) * Hq + h
     const int h = (int)(rh % a.Hq);
-    const long long row = rh / a.Hq;
+    const long long rt = rh / a.Hq;
+    const long long row = rt / a.T;
+    const int tok = (int)(rt % a.T);
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
     const int nsplit = chunk_span(a.window, a.chunk, a.max_splits, len, 0).nsplit;
     if (nsplit <= 1) return;  // written directly by the split kernel
 
-    const int kvh = h / a.G, g = h % a.G;
-    const size_t first = ((size_t)(row * a.Hkv + kvh) * a.max_splits) * a.G + g;  // split 0
+    const int kvh = h / a.G, g = tok * a.G + h % a.G;
+    const size_t first = ((size_t)(row * a.Hkv + kvh) * a.max_splits) * a.GT + g;  // split 0
     const f32x2_t* ml = a.part_ml + first;
     const uint16_t* po = a.part_o + first * a.D;
-    const size_t step = (size_t)a.G;  // partials of consecutive splits are G heads apart
+    const size_t step = (size_t)a.GT;  // partials of consecutive splits are T * G query rows apart
 
     // M = max over chunks (threads stride over the chunks, then a block max)
     float m = -INFINITY;
@@ -71,7 +76,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
             acc += s_acc[j * slots + slot];
             wsum += s_w[j * slots + slot];
         }
-        float* dst = a.out + ((size_t)row * a.Hq + h) * a.D;
+        float* dst = a.out + (size_t)rh * a.D;
         *reinterpret_cast<f32x4_t*>(dst + 4 * slot) = acc * (1.f / wsum);
     }
 }
@@ -88,19 +93,21 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
     constexpr int HPB = 256 / SLOTS;
     constexpr int S = kCombineFewMaxSplits;
     const int tid = threadIdx.x;
-    const long long gh = (long long)blockIdx.x * HPB + tid / SLOTS;  // row * Hq + h
+    const long long gh = (long long)blockIdx.x * HPB + tid / SLOTS;  // (row * T + token) * Hq + h
     if (gh >= nheads) return;
     const int slot = tid % SLOTS;
     const int h = (int)(gh % a.Hq);
-    const long long row = gh / a.Hq;
+    const long long rt = gh / a.Hq;
+    const long long row = rt / a.T;
+    const int tok = (int)(rt % a.T);
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
     const int nsplit = chunk_span(a.window, a.chunk, a.max_splits, len, 0).nsplit;
     if (nsplit <= 1) return;  // written directly by the split kernel
 
-    const int kvh = h / a.G, g = h % a.G;
-    const size_t first = ((size_t)(row * a.Hkv + kvh) * a.max_splits) * a.G + g;  // split 0
-    const size_t step = (size_t)a.G;  // partials of consecutive splits are G heads apart
+    const int kvh = h / a.G, g = tok * a.G + h % a.G;
+    const size_t first = ((size_t)(row * a.Hkv + kvh) * a.max_splits) * a.GT + g;  // split 0
+    const size_t step = (size_t)a.GT;  // partials of consecutive splits are T * G query rows apart
     f32x2_t ml[S];
     u32x4_t o[S];
 #pragma unroll
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
         acc1 += wgt * unpack_partial4(u32x2_t{o[s].z, o[s].w}, e);
         wsum += wgt;
     }
-    float* dst = a.out + ((size_t)row * a.Hq + h) * D + 8 * slot;
+    float* dst = a.out + (size_t)gh * D + 8 * slot;
     const float inv = 1.f / wsum;
     *reinterpret_cast<f32x4_t*>(dst) = acc0 * inv;
     *reinterpret_cast<f32x4_t*>(dst + 4) = acc1 * inv;
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
 hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream) {
     if (p.grid_combine <= 0) return hipSuccess;
     if (p.max_splits <= kCombineFewMaxSplits) {
-        const long long nheads = p.rows * a.Hq;
+        const long long nheads = p.rows * a.T * a.Hq;
         switch (a.D) {
             case 64:
                 hipLaunchKernelGGL(combine_few_kernel<64>, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a,

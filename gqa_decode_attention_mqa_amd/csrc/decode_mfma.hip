@@ -190,7 +190,7 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     const int kvh = (int)(unit % a.Hkv);
     const long long row = unit / a.Hkv;
     const int g0 = blockIdx.y * 16 * NG;
-    const int gcnt = min(16 * NG, a.G - g0);
+    const int gcnt = min(16 * NG, a.GT - g0);  // query rows (token, head) of this block
 
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
@@ -212,12 +212,15 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
     } else {
-        const uint16_t* qblk = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D;
-        const __amdgpu_buffer_rsrc_t qr = make_rsrc(qblk, gcnt * D * 2);
+        // the unit's query rows span T tokens, Hq * D elements apart
+        const size_t q0 = qrow_offset(row, a.T, a.Hq, a.G, D, kvh, 0);
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, a.GT - 1) - q0 + D) * 2);
+        const int r = g0 + 16 * w + li;
+        const int qoff = r < a.GT ? (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, r) - q0) * 2 : kOutOfRange;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
             qb[ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      qr, (16 * w + li) * D * 2 + ks * 64 + kg * 16, 0, 0));
+                                                      qr, qoff + ks * 64 + kg * 16, 0, 0));
         // A compute wave can do nothing before q; waiting here also tells the
         // compiler that no load is pending into registers the loop reads.
         __builtin_amdgcn_s_waitcnt(kVmcntStages<0, 0>());
@@ -334,6 +337,11 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     };
     // Scale, mask the tail, lazy online softmax; P^T of the tile in registers.
     // Returns whether the running maximum moved (then O must be rescaled by alpha).
+    // Query row of this lane's column: token (g0 + 16w + li) / G may attend
+    // positions below lim (len - T + 1 + token); tiles reaching past tmask
+    // hold a position some column must not see.
+    const int lim = min(p1, len - a.T + 1 + (g0 + 16 * w + li) / a.G);
+    const int tmask = p1 - a.T + 1;
     // 8-bit caches: the logit of a position is scaled by its K row's scale,
     // and its weight in P.V by its V row's scale (l sums the unscaled weights).
     auto softmax_tile = [&](int tile, f32x4_t (&sacc)[2], u32x4_t& pb, float& alpha) {
@@ -355,13 +363,13 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sacc[mq][r] *= qk;
         }
-        if (st + C::STEP > p1 || st < lo) {
+        if (st + C::STEP > tmask || st < lo) {
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = st + 16 * mq + 4 * kg + r;
-                    sacc[mq][r] = (t < p1 && t >= lo) ? sacc[mq][r] : -INFINITY;
+                    sacc[mq][r] = (t < lim && t >= lo) ? sacc[mq][r] : -INFINITY;
                 }
         }
         float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
@@ -370,6 +378,9 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
         const bool moved = mx > m_run + kRescaleSlack;
         alpha = moved ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
         m_run = moved ? mx : m_run;
+        // a column with no visible position yet (a later query token's limit
+        // can lie past a whole tile) keeps m = -inf; its weights are zero
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float lsum = 0.f;
 #pragma unroll
         for (int mq = 0; mq < 2; ++mq) {
@@ -377,16 +388,16 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
                 float pr[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    pr[r] = __builtin_amdgcn_exp2f(sacc[mq][r] - m_run);
+                    pr[r] = __builtin_amdgcn_exp2f(sacc[mq][r] - m_use);
                     lsum += pr[r];
                 }
                 pb[2 * mq] = pack2_bf16_rne(pr[0] * vsc[mq][0], pr[1] * vsc[mq][1]);
                 pb[2 * mq + 1] = pack2_bf16_rne(pr[2] * vsc[mq][2], pr[3] * vsc[mq][3]);
             } else {
-                const uint32_t lo = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][0] - m_run),
-                                                   __builtin_amdgcn_exp2f(sacc[mq][1] - m_run));
-                const uint32_t hi = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][2] - m_run),
-                                                   __builtin_amdgcn_exp2f(sacc[mq][3] - m_run));
+                const uint32_t lo = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][0] - m_use),
+                                                   __builtin_amdgcn_exp2f(sacc[mq][1] - m_use));
+                const uint32_t hi = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][2] - m_use),
+                                                   __builtin_amdgcn_exp2f(sacc[mq][3] - m_use));
                 pb[2 * mq] = lo;
                 pb[2 * mq + 1] = hi;
                 lsum += (bf16_lo_f32(lo) + bf16_hi_f32(lo)) + (bf16_lo_f32(hi) + bf16_hi_f32(hi));
@@ -509,7 +520,6 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int m = 0; m < C::MT; ++m)
                 *reinterpret_cast<f32x4_t*>(ot + li * ROWF + 16 * m + 4 * kg) = oacc[m] * inv_l;
-            float* dst = a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0 + 16 * w) * D;
             constexpr int LPR = D / 4;     // lanes per row, 16 bytes each
             constexpr int RPI = 64 / LPR;  // rows per store instruction
             const int hr = lane / LPR, c = lane % LPR;
@@ -517,8 +527,8 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
             for (int h0 = 0; h0 < 16; h0 += RPI) {
                 const int h = h0 + hr;
                 if (16 * w + h < gcnt)
-                    *reinterpret_cast<f32x4_t*>(dst + (size_t)h * D + 4 * c) =
-                        *reinterpret_cast<const f32x4_t*>(ot + h * ROWF + 4 * c);
+                    *reinterpret_cast<f32x4_t*>(a.out + qrow_offset(row, a.T, a.Hq, a.G, D, kvh, g0 + 16 * w + h) +
+                                                4 * c) = *reinterpret_cast<const f32x4_t*>(ot + h * ROWF + 4 * c);
             }
         } else {
             float mx = 0.f;
@@ -536,7 +546,7 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
                                     pack2_f16_rne(__builtin_amdgcn_ldexpf(x[2], -e), __builtin_amdgcn_ldexpf(x[3], -e))};
                 *reinterpret_cast<u32x2_t*>(ot + li * ROWH + 16 * m + 4 * kg) = pk;
             }
-            const size_t part0 = ((size_t)unit * a.max_splits + s) * a.G + g0 + 16 * w;  // this wave's first head
+            const size_t part0 = ((size_t)unit * a.max_splits + s) * a.GT + g0 + 16 * w;  // this wave's first row
             uint16_t* dst = a.part_o + part0 * D;
             constexpr int LPR = D / 8;     // lanes per row, 16 bytes (8 halves) each
             constexpr int RPI = 64 / LPR;  // rows per store instruction
@@ -557,8 +567,7 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     int* flag = reinterpret_cast<int*>(smem);
     if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, flag)) return;
     float* wts = reinterpret_cast<float*>(smem + 16);
-    fused_combine(a, unit, nsplit, g0, gcnt, a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D,
-                  wts, 16 * NG);
+    fused_combine(a, unit, row, kvh, nsplit, g0, gcnt, wts, 16 * NG);
 }
 
 template <int D, int NG, int FMT>

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const int kvh = (int)(unit % a.Hkv);
     const long long row = unit / a.Hkv;
     const int g0 = blockIdx.y * GB;
-    const int gcnt = min(GB, a.G - g0);
+    const int gcnt = min(GB, a.GT - g0);  // query rows (token, head) of this block
 
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
@@ -101,19 +101,24 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const int p1 = span.p1;
     const int nsplit = span.nsplit;
 
-    // q for this lane's EPL columns of every head in the block, as bf16 pairs.
+    // q for this lane's EPL columns of every query row in the block, as bf16
+    // pairs; and the positions each row may attend (token i of the row's T:
+    // len - T + 1 + i).
     uint32_t qv[GB][NP];
-    const uint16_t* qrow = a.q + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D + EPL * rl;
+    int lim[GB];
 #pragma unroll
     for (int gg = 0; gg < GB; ++gg) {
+        const uint16_t* qrow = a.q + qrow_offset(row, a.T, a.Hq, a.G, D, kvh, min(g0 + gg, a.GT - 1)) + EPL * rl;
+        lim[gg] = len - a.T + 1 + (g0 + gg) / a.G;
 #pragma unroll
         for (int h = 0; h < NP / 4; ++h) {
             u32x4_t t = {0u, 0u, 0u, 0u};
-            if (gg < gcnt) t = load_u32x4(qrow + (size_t)gg * D + 8 * h);
+            if (gg < gcnt) t = load_u32x4(qrow + 8 * h);
 #pragma unroll
             for (int c = 0; c < 4; ++c) qv[gg][4 * h + c] = t[c];
         }
     }
+    const int tmask = p1 - a.T + 1;  // blocks reaching past it hold a position some row must not see
 
     const int rowbytes = a.Hkv * D * (Q8 ? 1 : 2);  // bytes between consecutive positions of a cache
     const float qk = a.qk_log2;
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         // logits (base-2 units), masked outside [lo, p1); an 8-bit cache
         // scales each logit by its K row's scale and each weight in P.V by
         // its V row's scale (zero outside the range, where codes read as 0)
-        const bool edge = rows < WB || skip > 0;
+        const bool edge = rows < WB || skip > 0 || t0 + WB > tmask;
         float sc[NB][GB];
         float vscale[NB];
 #pragma unroll
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                 for (int c = 0; c < NP; ++c) acc = dot2_bf16(qv[gg][c], kk[c], acc);
                 acc = row_sum<RL>(acc) * qk;
                 if constexpr (Q8) acc *= kscale;
-                sc[st][gg] = ok ? acc : -INFINITY;
+                sc[st][gg] = (ok && (!edge || t0 + r < lim[gg])) ? acc : -INFINITY;
             }
         }
         // online softmax update for the block, with lazy rescaling
@@ -223,11 +228,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             alpha[gg] = moved ? __builtin_amdgcn_exp2f(m[gg] - mx) : 1.f;
             m[gg] = moved ? mx : m[gg];
             any_rescale |= moved;
+            // a row with no visible position yet keeps m = -inf; its weights are zero
+            const float m_use = m[gg] == -INFINITY ? 0.f : m[gg];
             float lsum = 0.f;
 #pragma unroll
             for (int st = 0; st < NB; st += 2) {
-                const float pa = __builtin_amdgcn_exp2f(sc[st][gg] - m[gg]);
-                const float pb = __builtin_amdgcn_exp2f(sc[st + 1][gg] - m[gg]);
+                const float pa = __builtin_amdgcn_exp2f(sc[st][gg] - m_use);
+                const float pb = __builtin_amdgcn_exp2f(sc[st + 1][gg] - m_use);
                 if constexpr (Q8) {
                     pp[st / 2][gg] = pack2_bf16_rne(pa * vscale[st], pb * vscale[st + 1]);
                     lsum += pa + pb;
@@ -337,8 +344,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         for (int k = 0; k < VPT; ++k) {
             const int idx = tid + 256 * k;
             if (idx < gcnt * D) {
-                const int gh = g0 + idx / D;
-                a.out[((size_t)row * a.Hq + (size_t)kvh * a.G + gh) * D + idx % D] = val[k];
+                a.out[qrow_offset(row, a.T, a.Hq, a.G, D, kvh, g0 + idx / D) + idx % D] = val[k];
             }
         }
     } else {
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             if (idx < gcnt * D) {
                 const int gg = idx / D, d = idx % D;
                 const int e = scale_exponent(__uint_as_float(s_amax[gg]));
-                const size_t part = ((size_t)unit * a.max_splits + s) * a.G + g0 + gg;
+                const size_t part = ((size_t)unit * a.max_splits + s) * a.GT + g0 + gg;
                 a.part_o[part * D + d] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(val[k], -e));
                 if (d == 0) a.part_ml[part] = f32x2_t{lse[k], (float)e};
             }
@@ -364,8 +370,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     if (direct || !a.fused) return;
     // Fused combine: the last chunk of this (row, kv head, head block) merges all partials.
     if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, &s_flag)) return;
-    fused_combine(a, unit, nsplit, g0, gcnt, a.out + ((size_t)row * a.Hq + (size_t)kvh * a.G + g0) * D,
-                  &mrg_o[0][0][0], GB);
+    fused_combine(a, unit, row, kvh, nsplit, g0, gcnt, &mrg_o[0][0][0], GB);
 }
 
 template <int D, int GB, int FMT>

@@ -17,21 +17,23 @@ typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 
 // Arguments of the split-K decode kernels, passed by value.
 //
-// A "row" is one query token: row r of a decode call is sequence r; in the
-// causal (prefill) form row r is position t = r % Lmax of sequence
-// b = r / Lmax and attends positions 0..t.  A "unit" is (row, kv head); a
-// unit's positions are cut into chunks of `chunk` positions, one workgroup per
-// (unit, chunk, head block).
+// A "row" is one sequence of a decode call (sequence r), or in the causal
+// (prefill) form position t = r % Lmax of sequence b = r / Lmax, attending
+// positions 0..t.  A row brings T query tokens (T > 1: several new tokens
+// decoded at once, causal among themselves).  A "unit" is (row, kv head); its
+// T * G query rows (token, head in the group) share the unit's keys and
+// values.  A unit's positions are cut into chunks of `chunk` positions, one
+// workgroup per (unit, chunk, head block).
 struct DecodeArgs {
-    const uint16_t* q;         // bf16 [rows, Hq, D]
+    const uint16_t* q;         // bf16 [rows, T, Hq, D]
     const void* k;             // [B, Lmax, Hkv, D] (or pages): bf16, or 8-bit codes
     const void* v;             // likewise
     const float* k_scale;      // 8-bit caches: fp32 [B, Hkv, Lmax] (pages: [num_pages, Hkv, page_size]),
     const float* v_scale;      // one per cached row; NULL for bf16
     const int32_t* seq_lens;   // [B]
-    float* out;                // fp32 [rows, Hq, D]
-    uint16_t* part_o;          // fp16 [rows * Hkv * max_splits, G, D]: O / l / 2^e per chunk
-    f32x2_t* part_ml;          // [rows * Hkv * max_splits, G]: {m + log2(l) (base 2), e}
+    float* out;                // fp32 [rows, T, Hq, D]
+    uint16_t* part_o;          // fp16 [rows * Hkv * max_splits, T * G, D]: O / l / 2^e per chunk
+    f32x2_t* part_ml;          // [rows * Hkv * max_splits, T * G]: {m + log2(l) (base 2), e}
     const int32_t* block_table;  // paged cache: [B, max_blocks] physical page per block of
                                  // 2^page_shift positions; NULL for the contiguous layout
     int page_shift, max_blocks, num_pages;
@@ -39,6 +41,7 @@ struct DecodeArgs {
                                // zero between calls: the last arriving chunk resets its counter
     long long units;           // rows * Hkv
     int Hq, Hkv, D, Lmax, G;
+    int T, GT;                 // query tokens per row; query rows per unit (T * G)
     int chunk, max_splits;
     int causal;                // 0 decode, 1 causal rows
     int window;                // > 0: sliding window, a row of length n attends n-window .. n-1
@@ -52,10 +55,19 @@ struct CombineArgs {
     const int32_t* seq_lens;
     float* out;
     int Hq, Hkv, D, Lmax, G;
+    int T, GT;
     int chunk, max_splits;
     int causal;
     int window;
 };
+
+// Query row r (0 .. T*G - 1) of unit (row, kv head kvh) is token r / G of the
+// row's T query tokens and query head kvh * G + r % G.  Element offset of its
+// q (and output) row in [rows, T, Hq, D].
+__device__ __forceinline__ size_t qrow_offset(long long row, int T, int Hq, int G, int D, int kvh, int r) {
+    const int i = r / G;
+    return (((size_t)row * T + i) * Hq + (size_t)kvh * G + (r - i * G)) * (size_t)D;
+}
 
 // Buffer offset that lies past the range of every tile descriptor (a tile spans
 // at most 32 rows of at most 2^24 bytes): a load from it returns zero and
@@ -298,20 +310,20 @@ __device__ __forceinline__ u32x4_t widen8(u32x2_t c) {
 // caller has already written its own partial.  Returns after every thread of
 // the workgroup has finished (it contains barriers: call it from all threads).
 //   wts: LDS scratch of 2 * kFusedMaxSplits * gp + 2 * gp floats, gp >= gcnt.
-__device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long unit, int nsplit,
-                                              int g0, int gcnt, float* out_row, float* wts, int gp) {
+__device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long unit, long long row, int kvh,
+                                              int nsplit, int g0, int gcnt, float* wts, int gp) {
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
     float* Mg = wts + kFusedMaxSplits * gp;
     float* Wg = Mg + gp;
-    const size_t base = (size_t)unit * a.max_splits * a.G;  // partial (unit, split 0, head 0)
+    const size_t base = (size_t)unit * a.max_splits * a.GT;  // partial (unit, split 0, query row 0)
     int* ex = reinterpret_cast<int*>(Wg + gp);  // kFusedMaxSplits * gp scale exponents
     if (tid < gcnt) {
         float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_ml[base + (size_t)s * a.G + g0 + tid].x);
+        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_ml[base + (size_t)s * a.GT + g0 + tid].x);
         float W = 0.f;
         for (int s = 0; s < nsplit; ++s) {
-            const f32x2_t ml = a.part_ml[base + (size_t)s * a.G + g0 + tid];
+            const f32x2_t ml = a.part_ml[base + (size_t)s * a.GT + g0 + tid];
             const float w = __builtin_amdgcn_exp2f(ml.x - M);
             wts[s * gp + tid] = w;
             ex[s * gp + tid] = (int)ml.y;
@@ -327,13 +339,13 @@ __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long uni
         const int g = idx / (D / 4), d4 = idx % (D / 4);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < nsplit; ++s) {
-            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(a.part_o + (base + (size_t)s * a.G + g0 + g) * D + 4 * d4);
+            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(a.part_o + (base + (size_t)s * a.GT + g0 + g) * D + 4 * d4);
             const int e = ex[s * gp + g];
             const f32x4_t o = {__builtin_amdgcn_ldexpf(f16_lo_f32(h.x), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.x), e),
                                __builtin_amdgcn_ldexpf(f16_lo_f32(h.y), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.y), e)};
             acc += wts[s * gp + g] * o;
         }
-        *reinterpret_cast<f32x4_t*>(out_row + (size_t)g * D + 4 * d4) = acc * Wg[g];
+        *reinterpret_cast<f32x4_t*>(a.out + qrow_offset(row, a.T, a.Hq, a.G, D, kvh, g0 + g) + 4 * d4) = acc * Wg[g];
     }
 }
 

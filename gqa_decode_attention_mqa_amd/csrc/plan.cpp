@@ -74,7 +74,7 @@ mqa_status check_paged(int B, const int32_t* block_table, int num_pages, int pag
 }
 
 mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
-                     const mqa_decode_opts* opts, bool causal, Plan* plan) {
+                     const mqa_decode_opts* opts, bool causal, Plan* plan, int T) {
     if (B < 0 || Lmax < 0)
         return fail(MQA_ERR_SHAPE, "B and Lmax must be >= 0");
     if (Hq <= 0 || Hkv <= 0 || D <= 0)
@@ -101,27 +101,36 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         return fail(MQA_ERR_ARG, "window must be >= 0 (0 = no window)");
     if (o.kv_format < MQA_KV_BF16 || o.kv_format > MQA_KV_INT8)
         return fail(MQA_ERR_ARG, "unknown kv_format");
+    if (T < 1)
+        return fail(MQA_ERR_SHAPE, "the number of query tokens must be >= 1");
+    if (T > 1 && o.window > 0)
+        return fail(MQA_ERR_ARG, "a sliding window is not supported with several query tokens");
+    // a unit's query rows are addressed through one 32-bit buffer range
+    if ((long long)T * Hq * D * 2 >= (1LL << 30))
+        return fail(MQA_ERR_UNSUPPORTED, "T * Hq * D too large");
     // Chunk starts sit up to 31 positions before a window's first position.
     if (o.window > 0 && Lmax > 0x7FFFFFFF - 64)
         return fail(MQA_ERR_UNSUPPORTED, "Lmax too large for a sliding window");
 
     Plan p;
     p.G = Hq / Hkv;
+    p.T = T;
+    p.GT = T * p.G;  // query rows sharing one kv head: what the head tiles hold
     p.variant = o.variant;
     if (p.variant == MQA_VARIANT_AUTO)
-        p.variant = (p.G >= kMfmaMinGroup) ? MQA_VARIANT_MFMA : MQA_VARIANT_VALU;
+        p.variant = (p.GT >= kMfmaMinGroup) ? MQA_VARIANT_MFMA : MQA_VARIANT_VALU;
 
     if (p.variant == MQA_VARIANT_MFMA) {
-        const int heads = p.G < kMfmaMaxHeads ? p.G : kMfmaMaxHeads;
+        const int heads = p.GT < kMfmaMaxHeads ? p.GT : kMfmaMaxHeads;
         p.heads_per_block = (int)round_up(heads, kMfmaHeadsPerTile);
     } else {
         // 8-bit caches: each lane holds twice the columns, so fewer heads per block
         const int cap = o.kv_format == MQA_KV_BF16 ? kValuMaxHeads : kValuMaxHeads8;
         int gb = 1;
-        while (gb < p.G && gb < cap) gb *= 2;
+        while (gb < p.GT && gb < cap) gb *= 2;
         p.heads_per_block = gb;
     }
-    p.head_blocks = (int)ceil_div(p.G, p.heads_per_block);
+    p.head_blocks = (int)ceil_div(p.GT, p.heads_per_block);
 
     p.rows = causal ? (long long)B * Lmax : (long long)B;
     const long long units = p.rows * Hkv * p.head_blocks;
@@ -172,12 +181,12 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         if (p.combine != 1)
             p.grid_combine = 0;
         else if (p.max_splits <= kCombineFewMaxSplits)
-            p.grid_combine = ceil_div(p.rows * Hq, combine_heads_per_block(D));
+            p.grid_combine = ceil_div(p.rows * T * Hq, combine_heads_per_block(D));
         else
-            p.grid_combine = p.rows * Hq;
+            p.grid_combine = p.rows * T * Hq;
         if (p.grid_combine > kMaxGrid)
             return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (combine grid limit)");
-        const size_t parts = (size_t)p.rows * Hkv * p.max_splits * p.G;
+        const size_t parts = (size_t)p.rows * Hkv * p.max_splits * p.GT;
         p.part_o_offset = 0;  // fp16 partial rows, then {lse, e} pairs
         p.part_ml_offset = round_up((long long)(parts * D * sizeof(uint16_t)), 256);
         p.workspace_bytes = p.part_ml_offset + round_up((long long)(parts * 2 * sizeof(float)), 256);

@@ -41,6 +41,8 @@ constexpr int combine_heads_per_block(int D) { return 2048 / D; }
 struct Plan {
     int variant = MQA_VARIANT_VALU;  // resolved, never AUTO
     int G = 0;                       // query heads per kv head
+    int T = 1;                       // query tokens per row
+    int GT = 0;                      // query rows per (row, kv head): T * G
     int heads_per_block = 0;         // padded heads a workgroup serves
     int head_blocks = 1;             // workgroups per (row, kv head, chunk) along heads
     int chunk = 0;                   // positions per split
@@ -66,9 +68,10 @@ void set_error(const std::string& msg);
 const char* last_error();
 
 // Checks sizes, scale and options; on success fills `plan`.  `rows` is B for
-// a decode call and B * Lmax for the causal (prefill) form.
+// a decode call and B * Lmax for the causal (prefill) form; T is the number
+// of query tokens per row (1 for a decode step).
 mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
-                     const mqa_decode_opts* opts, bool causal, Plan* plan);
+                     const mqa_decode_opts* opts, bool causal, Plan* plan, int T = 1);
 
 // A paged cache as the kernels see it (see check_paged).
 struct PagedCache {

@@ -142,6 +142,31 @@ mqa_status mqa_decode_attention_ex(const void *q, const void *k_cache, const voi
                                    const mqa_decode_opts *opts);
 
 /*
+ * Several new tokens per sequence decoded in one call (speculative
+ * verification, chunked prefill: "How To Scale Your Model", Part 7
+ * "Transformer Inference", passages on prefill and on speculative sampling,
+ * where several new tokens are scored against the cache at once).  The T new
+ * tokens' keys and values are already in the cache at positions n-T .. n-1
+ * (n = seq_lens[b]) and the tokens are causal among themselves: token i
+ * (0 .. T-1) attends positions 0 .. n-T+i.  A token whose position would be
+ * negative (n < T) gets an all-zero row.  The cache is read once for all T
+ * tokens: the T * Hq/Hkv query rows of a key/value head share its tiles.
+ *   q        bf16 [B, T, Hq, D]
+ *   out      fp32 [B, T, Hq, D], fully overwritten
+ *   k_cache, v_cache, seq_lens, scale as for mqa_decode_attention
+ *   opts     optional (may be NULL): kernel options and an 8-bit cache format
+ *            as for the other calls; a window (opts->window > 0) with T > 1 is
+ *            MQA_ERR_ARG
+ * T >= 1 (T == 1 is mqa_decode_attention_ex); T * Hq * D * 2 must stay below
+ * 2^30 (MQA_ERR_UNSUPPORTED).  Errors and ownership as for
+ * mqa_decode_attention.
+ */
+mqa_status mqa_decode_attention_multi(const void *q, const void *k_cache, const void *v_cache,
+                                      const int32_t *seq_lens, float *out, int B, int T, int Hq, int Hkv,
+                                      int D, int Lmax, float scale, void *stream,
+                                      const mqa_decode_opts *opts);
+
+/*
  * One decode step with local (sliding-window) attention ("How To Scale Your
  * Model", Part 7 "Transformer Inference", passage on mixing in local attention
  * layers: a local layer caps the context a token sees, its attention mask
@@ -242,6 +267,11 @@ mqa_status mqa_prefill_attention(const void *q_seq, const void *k_cache, const v
  */
 mqa_status mqa_decode_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                            const mqa_decode_opts *opts, mqa_plan_info *info);
+
+/* mqa_decode_plan for a mqa_decode_attention_multi call with T tokens per
+ * sequence (host only, no HIP call). */
+mqa_status mqa_decode_plan_multi(int B, int T, int Hq, int Hkv, int D, int Lmax, float scale,
+                                 const mqa_decode_opts *opts, mqa_plan_info *info);
 
 /* Static description of a status code (never NULL). */
 const char *mqa_status_string(mqa_status status);

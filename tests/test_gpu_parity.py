@@ -21,8 +21,8 @@ import torch
 import oracle
 from gqa_decode_attention_mqa_amd import binding
 from gqa_decode_attention_mqa_amd.workloads import (WORKLOADS, Workload, make_inputs, make_prefill_inputs,
-                                                    page_contiguous_cache, page_quant_cache, poison_positions_below_,
-                                                    quantize_cache)
+                                                    make_multi_inputs, page_contiguous_cache, page_quant_cache,
+                                                    poison_positions_below_, quantize_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -479,6 +479,81 @@ def test_quant_full_size_sampled(name, kv_format):
                               pick(qc["v_scale"]), pick(inp["seq_lens"]), kv_format, inp["scale"])
     err = check_close(out.index_select(0, sel), ref, "%s %s" % (name, kv_format))
     print("full %s %s: %d sequences checked, max abs err %.3g" % (name, kv_format, len(idx), err), flush=True)
+
+
+# ------------------------------------------------------ multi-token decode
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("T,G,Hkv", [(2, 1, 2), (4, 4, 2), (8, 1, 1), (3, 8, 1), (2, 48, 1), (4, 20, 1)])
+def test_multi_matches_multi_oracle(variant, D, T, G, Hkv):
+    w = Workload("multi", B=4, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=600, seed=900 + D + 7 * G + T, len_lo=0, len_hi=600)
+    inp = make_multi_inputs(w, T, poison_padding=True)
+    ref = oracle.decode_multi(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    dev = to_dev(inp)
+    for chunk, combine in ((None, None), (128, "separate"), (128, "fused")):
+        print("case multi", variant, D, T, G, Hkv, chunk, combine, flush=True)
+        out = binding.decode_multi(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant,
+                                   chunk=chunk, combine=combine)
+        torch.cuda.synchronize()
+        check_close(out, ref, "multi %s D %d T %d G %d chunk %s %s" % (variant, D, T, G, chunk, combine))
+
+
+def test_multi_short_sequences_and_one_token():
+    """Lengths below T (tokens before the start get zero rows), and T = 1 = the decode step bit for bit."""
+    w = Workload("multi-short", B=6, Hq=16, Hkv=2, D=128, Lmax=300, seed=950)
+    T = 6
+    inp = make_multi_inputs(w, T)
+    lens = torch.tensor([0, 1, 3, 5, 6, 300], dtype=torch.int32)
+    from gqa_decode_attention_mqa_amd.workloads import poison_padding_
+    poison_padding_(inp["k"], lens)
+    poison_padding_(inp["v"], lens)
+    ref = oracle.decode_multi(inp["q"], inp["k"], inp["v"], lens, inp["scale"])
+    dev = to_dev(inp)
+    dl = lens.to(DEV)
+    for variant in ("mfma", "valu"):
+        print("case multi short", variant, flush=True)
+        out = binding.decode_multi(dev["q"], dev["k"], dev["v"], dl, dev["scale"], variant=variant, chunk=128)
+        torch.cuda.synchronize()
+        check_close(out, ref, "multi short %s" % variant)
+        one = binding.decode_multi(dev["q"][:, :1].contiguous(), dev["k"], dev["v"], dl, dev["scale"], variant=variant)
+        dec = binding.decode(dev["q"][:, 0].contiguous(), dev["k"], dev["v"], dl, dev["scale"], variant=variant)
+        torch.cuda.synchronize()
+        assert torch.equal(one[:, 0], dec)
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+def test_multi_on_an_fp8_cache(variant):
+    T = 4
+    w = Workload("multi-q8", B=4, Hq=16, Hkv=4, D=128, Lmax=700, seed=960, len_lo=0, len_hi=700)
+    inp = make_multi_inputs(w, T, poison_padding=True)
+    qc = quantize_cache(inp, "fp8")
+    # the oracle of several tokens on an 8-bit cache: each token is an 8-bit
+    # decode with its own length (the pinned quantized decode)
+    lens = inp["seq_lens"]
+    ref = np.stack([oracle.decode_quant(inp["q"][:, i], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
+                                        torch.clamp(lens - T + 1 + i, min=0), "fp8", inp["scale"]) for i in range(T)], 1)
+    dev, dq = to_dev(inp), to_dev(qc)
+    print("case multi fp8", variant, flush=True)
+    out = binding.decode_multi(dev["q"], dq["k_codes"], dq["v_codes"], dev["seq_lens"], dev["scale"], variant=variant,
+                               kv_format="fp8", k_scale=dq["k_scale"], v_scale=dq["v_scale"])
+    torch.cuda.synchronize()
+    check_close(out, ref, "multi fp8 %s" % variant)
+
+
+@pytest.mark.parametrize("name,T", [("ragged", 4), ("gqa70b", 4), ("palm", 2)])
+def test_multi_full_size_sampled(name, T):
+    w = WORKLOADS[name]
+    print("case full multi", name, T, flush=True)
+    inp = make_multi_inputs(w, T, device=DEV, poison_padding=w.ragged)
+    out = binding.decode_multi(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    torch.cuda.synchronize()
+    idx = sample_indices(inp["seq_lens"], SAMPLES[name])
+    sel = torch.tensor(idx, device=DEV)
+    pick = lambda t: t.index_select(0, sel).cpu()
+    ref = oracle.decode_multi(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), pick(inp["seq_lens"]), inp["scale"])
+    err = check_close(out.index_select(0, sel), ref, "%s T=%d" % (name, T))
+    print("full %s T=%d: %d sequences checked, max abs err %.3g" % (name, T, len(idx), err), flush=True)
 
 
 # ------------------------------------------------------ full-size workloads

@@ -223,6 +223,41 @@ def test_quant_plan():
     assert a == b
 
 
+def multi_call(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, B=2, T=4, Hq=8, Hkv=2, D=128, Lmax=64, scale=0.1,
+               opts=None):
+    return lib.mqa_decode_attention_multi(q, k, v, lens, out, B, T, Hq, Hkv, D, Lmax, scale, None, opts)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(T=0), ERR_SHAPE), (dict(T=-2), ERR_SHAPE), (dict(T=1 << 15, Hq=64, D=256), ERR_UNSUPPORTED),
+    (dict(opts=binding.make_opts(window=16)), ERR_ARG), (dict(q=0), ERR_NULL), (dict(Hq=7), ERR_SHAPE),
+    (dict(opts=binding.make_opts(kv_format="fp8")), ERR_NULL),
+])
+def test_multi_arguments_are_rejected_before_any_hip_call(kw, expect):
+    if "opts" in kw:
+        kw["opts"] = binding.ctypes.byref(kw["opts"])
+    assert multi_call(**kw) == expect
+    assert lib.mqa_last_error()
+
+
+def test_multi_plan_fills_tiles_with_tokens():
+    # four tokens of a 4-head group make a full 16-row tile: the matrix-core kernel
+    p = binding.plan(256, 32, 8, 128, 8192, tokens=4)
+    assert p["variant"] == "mfma" and p["head_blocks"] == 1 and p["block_main"] == 64 * 3
+    assert binding.plan(256, 32, 8, 128, 8192)["variant"] == "valu"
+    # 2 tokens x 48 heads = 96 query rows: two blocks of up to 64
+    p = binding.plan(64, 48, 1, 256, 2048, tokens=2)
+    assert p["head_blocks"] == 2
+    # the combine covers every (row, token, head)
+    p = binding.plan(8, 16, 2, 128, 4096, tokens=3, chunk=512)
+    assert p["grid_combine"] == -(-8 * 3 * 16 // (2048 // 128))
+    assert p["workspace_bytes"] >= 8 * 2 * p["max_splits"] * 24 * (2 * 128 + 8)
+
+
+def test_multi_empty_batch_is_a_no_op():
+    assert multi_call(q=0, k=0, v=0, lens=0, out=0, B=0) == OK
+
+
 def paged_call(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, D=128,
                num_pages=16, page_size=64, max_blocks=4, scale=0.1):
     return lib.mqa_decode_attention_paged(q, k, v, table, lens, out, B, Hq, Hkv, D, num_pages, page_size,
