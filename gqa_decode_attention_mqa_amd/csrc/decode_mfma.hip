@@ -72,35 +72,53 @@ struct MfmaCfg {
     static_assert(LDS_BYTES >= (2 * kFusedMaxSplits + 2) * 16 * NG * 4 + 16, "fused-combine scratch fits");
 };
 
-// LDS layout of a bf16 tile: row t (D bf16) is D/8 chunks of 16 bytes, and chunk
-// c of row t sits in slot c ^ swz_key(t).  The key takes all eight values over
-// any eight consecutive rows (the K reads of eight lanes hit eight different
-// 16-byte bank groups), and over rows 4i .. 4i+3 it takes four values that
-// differ above bit 0 (the transposing V reads of a 16-lane group, two
-// adjacent chunks of four rows, hit 128 distinct bytes of banks).
-__device__ __forceinline__ int swz_key(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// LDS bank model used below: an LDS access is served 256 bytes (all 64
+// banks of 4 bytes) at a time, i.e. 16 lanes of a 16-byte read or 32 lanes
+// of an 8-byte read per pass; rows of a tile that are a multiple of 256 bytes
+// apart hit the same banks.
+//
+// LDS layout of a bf16 tile: row t (D bf16) is D/8 chunks of 16 bytes, and
+// chunk c of row t sits in slot c ^ swz_key<D>(t).  For D >= 128 (every row
+// starts on bank 0) the key takes sixteen values over any sixteen consecutive
+// rows (the q.K reads of a pass: sixteen rows, one chunk column) and eight
+// values differing above bit 0 over rows 8i .. 8i+7 (the transposing V reads
+// of a pass: eight rows, two adjacent chunks each).  For D = 64 (two rows per
+// 256 bytes) the same holds among the rows of one parity.
+template <int D>
+__device__ __forceinline__ int swz_key(int t) {
+    if constexpr (D >= 128)
+        return ((t & 7) << 1) | ((t >> 3) & 1);
+    else
+        return (((t >> 1) & 3) << 1) | ((t >> 3) & 1);
+}
+// Address registers per row the V^T reads need: the key is below 2 * SWZ_NR,
+// so chunk 2m + x of row t sits in slot (2 (m mod NR) + x) ^ key, plus 2 NR
+// (m div NR).
+template <int D>
+constexpr int kSwzRegs = D >= 128 ? 8 : 4;
 
 // LDS byte offset of chunk c of row t inside a bf16 tile.
-template <int CPR>
+template <int D>
 __device__ __forceinline__ int swz(int t, int c) {
-    return (t * CPR + (c ^ swz_key(t))) * 16;
+    return (t * (D / 8) + (c ^ swz_key<D>(t))) * 16;
 }
 
 // 8-bit tiles: row t (D codes) is D/16 chunks of 16 bytes, chunk c in slot
-// c ^ swz8_key(t).  With R = 256/D rows per 256 bytes of banks, the key is
-// one-to-one over the rows of one bank offset among any 16 consecutive rows
-// (the q.K reads of a 16-lane group) and among rows 4i .. 4i+3 and
-// 16 + 4i .. 16 + 4i + 3 (the transposing V reads of a 16-lane group).
+// c ^ swz8_key<D>(t).  With R = 256/D rows per 256 bytes of banks and S = D/16
+// slots per row, the key is one-to-one over the rows of one bank offset among
+// any 16 consecutive rows (the q.K reads of a pass) and among rows 8i .. 8i+7
+// together with rows 16 + 8i .. 16 + 8i + 7 (the transposing V reads of a
+// pass, two 16-lane groups).
 template <int D>
 __device__ __forceinline__ int swz8_key(int t) {
-    constexpr int R = 256 / D;
-    return ((t / R) + (t >> 4) * (4 / R)) & (D / 16 - 1);
+    constexpr int R = 256 / D, S = D / 16;
+    return ((t / R) + (S / 2) * ((t >> 4) & 1)) & (S - 1);
 }
 
 template <int FMT, int D>
 __device__ __forceinline__ int tile_key(int t) {
     if constexpr (FMT == kKvBf16)
-        return swz_key(t);
+        return swz_key<D>(t);
     else
         return swz8_key<D>(t);
 }
@@ -150,13 +168,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Issue the V^T operand reads of one tile: for 16-row tile m of d, the
 // transposing reads at rows `lo` and `hi` (the lane's two groups of four
 // positions).  The results are valid only after wait_vt_tile.
-template <int MT>
-__device__ __forceinline__ void issue_vt_tile(uint32_t vbase, const int (&alo)[4], const int (&ahi)[4],
+template <int MT, int NR>
+__device__ __forceinline__ void issue_vt_tile(uint32_t vbase, const int (&alo)[NR], const int (&ahi)[NR],
                                               u32x2_t (&lo)[MT], u32x2_t (&hi)[MT]) {
     static_for<0, MT>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
-        lo[m] = ds_read_tr16_b64_asm<128 * (m >> 2)>(vbase + alo[m & 3]);
-        hi[m] = ds_read_tr16_b64_asm<128 * (m >> 2)>(vbase + ahi[m & 3]);
+        lo[m] = ds_read_tr16_b64_asm<32 * NR * (m / NR)>(vbase + alo[m % NR]);
+        hi[m] = ds_read_tr16_b64_asm<32 * NR * (m / NR)>(vbase + ahi[m % NR]);
     });
 }
 // Wait until every LDS read of this wave has landed and tie the V^T operands
@@ -327,7 +345,7 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
                     ka = widen8<FMT>(k8);
                 } else {
                     const int t = 16 * mq + li;
-                    ka = *reinterpret_cast<const u32x4_t*>(kt + swz<C::CPR>(t, 4 * ks + kg));
+                    ka = *reinterpret_cast<const u32x4_t*>(kt + swz<D>(t, 4 * ks + kg));
                 }
                 part[ks & 1][mq] = mfma_16x16x32_bf16(ka, qb[ks], part[ks & 1][mq]);
             }
@@ -413,16 +431,17 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
     // 16m + li of the four rows.  Element e of lane group kg is position
     // 16*(e/4) + 4*kg + e%4, the order of the P^T operand.
     //   Chunk 2m + x (x = 0, 1) of row t sits at the slot of chunk
-    // 2(m mod 4) + x plus 8 (m div 4), since the swizzle key is below 8, so
-    // four address registers per row and constant offsets cover all m.
+    // 2(m mod NR) + x plus 2 NR (m div NR) (see kSwzRegs), so NR address
+    // registers per row and constant offsets cover all m.
+    constexpr int NR = kSwzRegs<D>;
     const int tr_j = li >> 2, tr_b = li & 3;
     const int tr_tlo = 4 * kg + tr_j, tr_thi = 16 + 4 * kg + tr_j;
-    int tr_lo[4], tr_hi[4];
+    int tr_lo[NR], tr_hi[NR];
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
+    for (int mm = 0; mm < NR; ++mm) {
         const int c = 2 * mm + (tr_b >> 1), half = (tr_b & 1) * 8;
-        tr_lo[mm] = swz<C::CPR>(tr_tlo, c) + half;
-        tr_hi[mm] = swz<C::CPR>(tr_thi, c) + half;
+        tr_lo[mm] = swz<D>(tr_tlo, c) + half;
+        tr_hi[mm] = swz<D>(tr_thi, c) + half;
     }
     // 8-bit tiles: one ds_read_b64_tr_b8 per 16-row tile m of d.  In lane
     // group kg, lane 2k + x points at the 8 codes d = 16m + 8x .. +7 of
@@ -437,7 +456,7 @@ __global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int m = 0; m < C::MT; ++m) lo[m] = ds_read_tr8_b64_asm(vbase + tr8_row + (tr8_key ^ (m * 16)));
         } else {
-            issue_vt_tile<C::MT>(vbase, tr_lo, tr_hi, lo, hi);
+            issue_vt_tile<C::MT, NR>(vbase, tr_lo, tr_hi, lo, hi);
         }
     };
     auto pv_mma = [&](const u32x4_t& pb, u32x2_t (&lo)[C::MT], u32x2_t (&hi)[C::MT]) {

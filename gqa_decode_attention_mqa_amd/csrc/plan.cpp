@@ -154,7 +154,8 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         // 128 against 16.0 us at 256).
         const bool windowed = o.window > 0 && o.window < Lmax;
         long long c = round_up(ceil_div(span * units, kTargetWorkgroups), kChunkQuantum);
-        const long long cmax = p.variant == MQA_VARIANT_MFMA ? kMaxChunkMfma : kMaxChunkValu;
+        const long long cmax = p.variant != MQA_VARIANT_MFMA ? kMaxChunkValu
+                               : (units >= kManyUnits ? kMaxChunkMfmaMany : kMaxChunkMfma);
         const long long cmin = windowed ? kChunkQuantum : kMinChunk;
         if (c < cmin) c = cmin;
         if (c > cmax) c = cmax;

@@ -19,11 +19,20 @@ constexpr int kComputeUnits = 256;
 constexpr int kChunkQuantum = 128;
 // Query heads per MFMA tile along the N dimension.
 constexpr int kMfmaHeadsPerTile = 16;
-// Smallest group (query heads per kv head) sent to the matrix-core kernel by
-// default.  Measured on MI355X: at G = 8 the 16-row tile (half filled) beats
-// the vector kernel (95.5 us vs 128 us for B=32, Hkv=8, D=128, len 4096); at
-// G = 4 the vector kernel wins (790 us vs 944 us on the ragged batch).
-constexpr int kMfmaMinGroup = 5;
+// Smallest number of query rows per kv head (G times the query tokens) sent
+// to the matrix-core kernel by default: every group.  Measured on MI355X on
+// the ragged batch (B=256, Hkv=8, D=128, lengths U[1, 8192]) with 512-position
+// chunks against the vector kernel: G = 4: 753 vs 776 us (bf16), 456 vs 676 us
+// (fp8); G = 2: 723 vs 736 us, 429 vs 452 us; G = 1: 706 vs 730 us, 416 vs
+// 447 us.  The vector kernel stays available as an explicit variant.
+constexpr int kMfmaMinGroup = 1;
+// With at least this many (row, kv head) units the matrix-core chunks are
+// capped at kMaxChunkMfmaMany positions: there are workgroups enough without
+// long chunks, and short ones balance ragged lengths (ragged batch above:
+// 753 us at 512 or 1024 positions against 826 us at 2048; 1024 keeps a
+// sequence within the few-chunk combine, 5 us against 17 us for 16 chunks).
+constexpr long long kManyUnits = 4 * kComputeUnits;
+constexpr long long kMaxChunkMfmaMany = 1024;
 // Most query heads one MFMA workgroup serves (four 16-head tiles).
 constexpr int kMfmaMaxHeads = 64;
 // Most query heads one VALU workgroup serves (bf16 cache; 8-bit caches).
