@@ -63,11 +63,13 @@ struct MfmaCfg {
     static constexpr int LOADS = TILE_BYTES / 1024;  // wave-wide 16-byte loads per tile (K or V)
     static constexpr int KPW = LOADS / NL;           // K loads (and as many V loads) per loader per tile
     static constexpr int PER_WAVE = 2 * KPW + (Q8 ? 1 : 0);  // loads a loader issues per tile (+ a scale row)
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int EPI_BYTES = NG * 16 * (D + 4) * 4;  // the output transpose, after the ring is drained
+    static constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
     static_assert(D >= 64 && D % 64 == 0, "head size");
     static_assert(LOADS % NL == 0, "every loader issues the same number of loads");
     static_assert((STAGES - 2) * PER_WAVE <= 63, "loads in flight fit a wave's counter");
-    static_assert(NG * 16 * (D + 4) * 4 <= LDS_BYTES, "the output transpose fits in the ring");
+    static_assert(NG >= 1 && NG <= 6, "one to six 16-row tiles of query rows");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
     static_assert(LDS_BYTES >= (2 * kFusedMaxSplits + 2) * 16 * NG * 4 + 16, "fused-combine scratch fits");
 };
@@ -194,7 +196,7 @@ __device__ __forceinline__ void wait_v8_tile(u32x2_t (&v)[MT]) {
 }
 
 template <int D, int NG, int FMT>
-__global__ __launch_bounds__(384) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     using C = MfmaCfg<D, NG, FMT>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -624,6 +626,8 @@ static hipError_t launch_mfma_d(const Plan& p, const DecodeArgs& a, hipStream_t 
         case 2: return launch_mfma<D, 2, FMT>(p, a, stream, ev0, ev1);
         case 3: return launch_mfma<D, 3, FMT>(p, a, stream, ev0, ev1);
         case 4: return launch_mfma<D, 4, FMT>(p, a, stream, ev0, ev1);
+        case 5: return launch_mfma<D, 5, FMT>(p, a, stream, ev0, ev1);
+        case 6: return launch_mfma<D, 6, FMT>(p, a, stream, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }

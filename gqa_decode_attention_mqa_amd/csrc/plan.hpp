@@ -33,8 +33,9 @@ constexpr int kMfmaMinGroup = 1;
 // sequence within the few-chunk combine, 5 us against 17 us for 16 chunks).
 constexpr long long kManyUnits = 4 * kComputeUnits;
 constexpr long long kMaxChunkMfmaMany = 1024;
-// Most query heads one MFMA workgroup serves (four 16-head tiles).
-constexpr int kMfmaMaxHeads = 64;
+// Most query rows one MFMA workgroup serves (six 16-row tiles, one compute
+// wave each): 2 tokens of a 48-head group still read the cache once.
+constexpr int kMfmaMaxHeads = 96;
 // Most query heads one VALU workgroup serves (bf16 cache; 8-bit caches).
 constexpr int kValuMaxHeads = 8;
 constexpr int kValuMaxHeads8 = 4;

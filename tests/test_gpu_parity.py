@@ -71,7 +71,7 @@ def test_tiny_workload_full():
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("G,Hkv,B", [(1, 2, 3), (2, 3, 5), (3, 1, 3), (4, 2, 4), (8, 1, 3), (16, 1, 8), (48, 1, 3),
-                                     (20, 2, 3), (64, 1, 3), (80, 1, 3)])
+                                     (20, 2, 3), (64, 1, 3), (80, 1, 3), (96, 1, 2), (112, 1, 2)])
 def test_small_shapes(variant, D, G, Hkv, B):
     seed = 1000 + D + 7 * G + Hkv + (0 if variant == "mfma" else 1)
     w = Workload("small", B=B, Hq=G * Hkv, Hkv=Hkv, D=D, Lmax=700, seed=seed, len_lo=1, len_hi=700)

@@ -90,7 +90,7 @@ def test_plan_invariants(B, Hq, Hkv, D, Lmax):
     assert p["max_splits"] >= 1 and p["chunk"] * p["max_splits"] >= Lmax
     assert (p["max_splits"] - 1) * p["chunk"] < max(Lmax, 1)
     assert p["variant"] == "mfma"  # the matrix-core kernel serves every group by default
-    per_block = min(G, 64) if p["variant"] == "mfma" else min(G, 8)
+    per_block = min(G, 96) if p["variant"] == "mfma" else min(G, 8)
     assert p["head_blocks"] * per_block >= G
     assert p["grid_main"] == B * Hkv * p["max_splits"] * p["head_blocks"]
     # matrix cores: a compute wave per 16 heads and two load-only waves; vector ALU: four waves
@@ -245,9 +245,11 @@ def test_multi_plan_fills_tiles_with_tokens():
     # four tokens of a 4-head group make a full 16-row tile
     p = binding.plan(256, 32, 8, 128, 8192, tokens=4)
     assert p["variant"] == "mfma" and p["head_blocks"] == 1 and p["block_main"] == 64 * 3
-    # 2 tokens x 48 heads = 96 query rows: two blocks of up to 64
+    # 2 tokens x 48 heads = 96 query rows: one block of six 16-row tiles (six compute waves)
     p = binding.plan(64, 48, 1, 256, 2048, tokens=2)
-    assert p["head_blocks"] == 2
+    assert p["head_blocks"] == 1 and p["block_main"] == 64 * (6 + 2)
+    # 3 tokens x 48 heads = 144 rows: two blocks of up to 96
+    assert binding.plan(64, 48, 1, 256, 2048, tokens=3)["head_blocks"] == 2
     # the combine covers every (row, token, head)
     p = binding.plan(8, 16, 2, 128, 4096, tokens=3, chunk=512)
     assert p["grid_combine"] == -(-8 * 3 * 16 // (2048 // 128))
