@@ -4,7 +4,7 @@
 // 48-head multiquery attention of PaLM 540B in "Efficiently Scaling
 // Transformer Inference", section 3.4, "Attention Layer Partitioning", or the
 // 8-head groups of grouped-query attention) a workgroup owns (query row, kv
-// head, chunk of positions, block of 16*NG heads, NG = 1..4).  Compute wave
+// head, chunk of positions, block of 16*NG query rows, NG = 1..6).  Compute wave
 // w < NG owns heads 16w .. 16w+15 for every position of the chunk, so no two
 // waves ever merge softmax state; groups below 16 pad the head tile.  The
 // chunk's K and V rows are read from HBM exactly once per workgroup into an

@@ -71,8 +71,8 @@ typedef enum mqa_status {
 
 /* Kernel family for the q.K^T and P.V products. */
 typedef enum mqa_variant {
-    MQA_VARIANT_AUTO = 0, /* planner's choice by group size G = Hq / Hkv: VALU for G <= 4  */
-    MQA_VARIANT_VALU = 1, /* vector-ALU dot products (small groups)                        */
+    MQA_VARIANT_AUTO = 0, /* planner's choice (the matrix-core kernel, measured fastest)    */
+    MQA_VARIANT_VALU = 1, /* vector-ALU dot products                                       */
     MQA_VARIANT_MFMA = 2  /* bf16 matrix-core tiles, 16 query heads per tile (large groups) */
 } mqa_variant;
 
