@@ -106,15 +106,17 @@ __device__ __forceinline__ int swz(int t, int c) {
 }
 
 // 8-bit tiles: row t (D codes) is D/16 chunks of 16 bytes, chunk c in slot
-// c ^ swz8_key<D>(t).  With R = 256/D rows per 256 bytes of banks and S = D/16
-// slots per row, the key is one-to-one over the rows of one bank offset among
-// any 16 consecutive rows (the q.K reads of a pass) and among rows 8i .. 8i+7
-// together with rows 16 + 8i .. 16 + 8i + 7 (the transposing V reads of a
-// pass, two 16-lane groups).
+// c ^ swz8_key<D>(t).  With R = 256/D rows per 256 bytes of banks, the key is
+// one-to-one over the rows of one bank offset among any 16 consecutive rows
+// (the q.K reads of a 16-lane group) and among rows 4i .. 4i+3 and
+// 16 + 4i .. 16 + 4i + 3 (the transposing V reads of a 16-lane group).  A key
+// also separating two such groups (for 32-lane passes) measured slower on
+// MI355X (int8 PaLM MQA 35.0 against 32.5 us, B=4 len 131072 116 against
+// 105 us), so the 16-lane form is kept for 8-bit tiles.
 template <int D>
 __device__ __forceinline__ int swz8_key(int t) {
-    constexpr int R = 256 / D, S = D / 16;
-    return ((t / R) + (S / 2) * ((t >> 4) & 1)) & (S - 1);
+    constexpr int R = 256 / D;
+    return ((t / R) + (t >> 4) * (4 / R)) & (D / 16 - 1);
 }
 
 template <int FMT, int D>
