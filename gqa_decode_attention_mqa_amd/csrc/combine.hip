@@ -81,17 +81,17 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
 }
 
-// Few chunks per sequence (at most kCombineFewMaxSplits): one thread per
-// (query head, 8-value column slot), 2048/D heads per workgroup.  Each thread
-// issues the loads of every chunk's {lse, e} and slot at once (indices
-// clamped to the sequence's chunks, so every load is in bounds) and merges
-// them in ascending chunk order, so the result is bitwise reproducible for a
-// plan.
-template <int D>
+// Few chunks per sequence (at most S, the plan's chunk bound rounded up to
+// 2, 4 or 8): one thread per (query head, 8-value column slot), 2048/D heads
+// per workgroup.  Each thread issues the loads of all S chunks' {lse, e} and
+// slot at once (indices clamped to the sequence's chunks, so every load is in
+// bounds) and merges them in ascending chunk order, so the result is bitwise
+// reproducible for a plan.
+template <int D, int S>
 __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long long nheads) {
     constexpr int SLOTS = D / 8;
     constexpr int HPB = 256 / SLOTS;
-    constexpr int S = kCombineFewMaxSplits;
+    static_assert(S >= 2 && S <= kCombineFewMaxSplits, "chunk bound of the few-chunk combine");
     const int tid = threadIdx.x;
     const long long gh = (long long)blockIdx.x * HPB + tid / SLOTS;  // (row * T + token) * Hq + h
     if (gh >= nheads) return;
@@ -135,23 +135,26 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
     *reinterpret_cast<f32x4_t*>(dst + 4) = acc1 * inv;
 }
 
+template <int D>
+static void launch_few(int max_splits, unsigned grid, const CombineArgs& a, long long nheads, hipStream_t stream) {
+    if (max_splits <= 2)
+        hipLaunchKernelGGL((combine_few_kernel<D, 2>), dim3(grid), dim3(256), 0, stream, a, nheads);
+    else if (max_splits <= 4)
+        hipLaunchKernelGGL((combine_few_kernel<D, 4>), dim3(grid), dim3(256), 0, stream, a, nheads);
+    else
+        hipLaunchKernelGGL((combine_few_kernel<D, kCombineFewMaxSplits>), dim3(grid), dim3(256), 0, stream, a,
+                           nheads);
+}
+
 hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream) {
     if (p.grid_combine <= 0) return hipSuccess;
     if (p.max_splits <= kCombineFewMaxSplits) {
         const long long nheads = p.rows * a.T * a.Hq;
+        const unsigned grid = (unsigned)p.grid_combine;
         switch (a.D) {
-            case 64:
-                hipLaunchKernelGGL(combine_few_kernel<64>, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a,
-                                   nheads);
-                break;
-            case 128:
-                hipLaunchKernelGGL(combine_few_kernel<128>, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a,
-                                   nheads);
-                break;
-            case 256:
-                hipLaunchKernelGGL(combine_few_kernel<256>, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a,
-                                   nheads);
-                break;
+            case 64: launch_few<64>(p.max_splits, grid, a, nheads, stream); break;
+            case 128: launch_few<128>(p.max_splits, grid, a, nheads, stream); break;
+            case 256: launch_few<256>(p.max_splits, grid, a, nheads, stream); break;
             default: return hipErrorInvalidValue;
         }
     } else {

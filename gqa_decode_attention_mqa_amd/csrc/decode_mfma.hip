@@ -93,9 +93,13 @@ __device__ __forceinline__ int swz_key(int t) {
     else
         return (((t >> 1) & 3) << 1) | ((t >> 3) & 1);
 }
-// Address registers per row the V^T reads need: the key is below 2 * SWZ_NR,
-// so chunk 2m + x of row t sits in slot (2 (m mod NR) + x) ^ key, plus 2 NR
-// (m div NR).
+// The key is below 2 * kSwzRegs, so chunk 2m + x of row t sits in slot
+// (2 (m mod NR) + x) ^ key, plus 2 NR (m div NR), with NR = kSwzRegs: at byte
+// 32 ((m mod NR) ^ (key >> 1)) + 16 (x ^ (key & 1)) + 32 NR (m div NR) of
+// the row.  The address for m is therefore the one for m = 0 XOR 32 (m mod
+// NR), plus a constant; rows, tiles and ring slots all start on multiples of
+// 32 NR bytes (the LDS block itself at address 0), so the XOR never reaches
+// above the row.
 template <int D>
 constexpr int kSwzRegs = D >= 128 ? 8 : 4;
 
@@ -169,16 +173,18 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// Issue the V^T operand reads of one tile: for 16-row tile m of d, the
-// transposing reads at rows `lo` and `hi` (the lane's two groups of four
-// positions).  The results are valid only after wait_vt_tile.
-template <int MT, int NR>
-__device__ __forceinline__ void issue_vt_tile(uint32_t vbase, const int (&alo)[NR], const int (&ahi)[NR],
-                                              u32x2_t (&lo)[MT], u32x2_t (&hi)[MT]) {
-    static_for<0, MT>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        lo[m] = ds_read_tr16_b64_asm<32 * NR * (m / NR)>(vbase + alo[m % NR]);
-        hi[m] = ds_read_tr16_b64_asm<32 * NR * (m / NR)>(vbase + ahi[m % NR]);
+// Issue the V^T operand reads of 16-row tiles m = M0 .. M0+MH-1 of d of one
+// tile: the transposing reads at rows `lo` and `hi` (the lane's two groups of
+// four positions).  alo / ahi are the LDS addresses for m = 0; tile m reads
+// at that address XOR 32 (m mod NR), plus 32 NR (m div NR) (see kSwzRegs).
+// The results are valid only after wait_vt_tile.
+template <int M0, int MH, int NR>
+__device__ __forceinline__ void issue_vt_tile(uint32_t alo, uint32_t ahi, u32x2_t (&lo)[MH], u32x2_t (&hi)[MH]) {
+    static_for<0, MH>([&](auto jc) {
+        constexpr int j = decltype(jc)::value, m = M0 + j;
+        constexpr int off = 32 * NR * (m / NR);
+        lo[j] = ds_read_tr16_b64_asm<off>(alo ^ (32 * (m % NR)));
+        hi[j] = ds_read_tr16_b64_asm<off>(ahi ^ (32 * (m % NR)));
     });
 }
 // Wait until every LDS read of this wave has landed and tie the V^T operands
@@ -200,7 +206,7 @@ __device__ __forceinline__ void wait_v8_tile(u32x2_t (&v)[MT]) {
 template <int D, int NG, int FMT>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     using C = MfmaCfg<D, NG, FMT>;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -331,8 +337,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         k8_row[mq] = t * C::ROWB + (kg & 1) * 8;
         k8_key[mq] = (tile_key<FMT, D>(t) ^ (kg >> 1)) * 16;
     }
-    auto qk_tile = [&](int tile, f32x4_t (&sacc)[2]) {
-        const unsigned char* kt = smem + (tile % C::STAGES) * C::STAGE_BYTES;
+    auto qk_tile = [&](int soff, f32x4_t (&sacc)[2]) {
+        const unsigned char* kt = smem + soff;
         f32x4_t part[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -354,6 +360,21 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
                 part[ks & 1][mq] = mfma_16x16x32_bf16(ka, qb[ks], part[ks & 1][mq]);
             }
         }
+        // Keep eight K reads ahead of the matrix products (the LDS latency of
+        // a read spans several products): eight reads, then one product and
+        // one read alternately, then the last eight products.
+        // (bf16 tiles only: the widening of 8-bit codes sits between a read
+        // and its product, and pinning the order there measured slower)
+        if constexpr (!C::Q8) {
+            constexpr int NQ = 2 * C::KS;  // reads = products of this tile
+            constexpr int AHEAD = NQ / 2 < 8 ? NQ / 2 : 8;
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+            static_for<0, NQ - AHEAD>([&](auto) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            });
+            __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+        }
         sacc[0] = part[0][0] + part[1][0];
         sacc[1] = part[0][1] + part[1][1];
     };
@@ -366,12 +387,12 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     const int tmask = p1 - a.T + 1;
     // 8-bit caches: the logit of a position is scaled by its K row's scale,
     // and its weight in P.V by its V row's scale (l sums the unscaled weights).
-    auto softmax_tile = [&](int tile, f32x4_t (&sacc)[2], u32x4_t& pb, float& alpha) {
+    // First part: scale the logits and mask the positions a column must not
+    // see (a rare, uniform branch); vsc gets the V scales of 8-bit tiles.
+    auto softmax_prep = [&](int tile, int soff, f32x4_t (&sacc)[2], f32x4_t (&vsc)[2]) {
         const int st = p0 + tile * C::STEP;
-        f32x4_t vsc[2];
         if constexpr (C::Q8) {
-            const float* scl = reinterpret_cast<const float*>(smem + (tile % C::STAGES) * C::STAGE_BYTES +
-                                                              2 * C::TILE_BYTES);
+            const float* scl = reinterpret_cast<const float*>(smem + soff + 2 * C::TILE_BYTES);
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq) {
                 const f32x4_t ksc = *reinterpret_cast<const f32x4_t*>(scl + 16 * mq + 4 * kg);
@@ -394,6 +415,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
                     sacc[mq][r] = (t < lim && t >= lo) ? sacc[mq][r] : -INFINITY;
                 }
         }
+    };
+    // Second part: the online softmax proper, free of branches so that it can
+    // share a basic block (and the issue slots) with the matrix products.
+    auto softmax_finish = [&](f32x4_t (&sacc)[2], const f32x4_t (&vsc)[2], u32x4_t& pb, float& alpha) {
         float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                          fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
         mx = max_xor32(max_xor16(mx));
@@ -428,6 +453,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         l_run = l_run * alpha + lsum;
         return __any(moved);
     };
+    auto softmax_tile = [&](int tile, int soff, f32x4_t (&sacc)[2], u32x4_t& pb, float& alpha) {
+        f32x4_t vsc[2];
+        softmax_prep(tile, soff, sacc, vsc);
+        return softmax_finish(sacc, vsc, pb, alpha);
+    };
     // O^T += V^T P^T for one tile.  The A operand (row d = 16m + li, eight
     // positions per lane group) comes straight from LDS with transposing
     // reads: in each 16-lane group, lane 4j + b points at the 8 bytes
@@ -440,13 +470,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int NR = kSwzRegs<D>;
     const int tr_j = li >> 2, tr_b = li & 3;
     const int tr_tlo = 4 * kg + tr_j, tr_thi = 16 + 4 * kg + tr_j;
-    int tr_lo[NR], tr_hi[NR];
-#pragma unroll
-    for (int mm = 0; mm < NR; ++mm) {
-        const int c = 2 * mm + (tr_b >> 1), half = (tr_b & 1) * 8;
-        tr_lo[mm] = swz<D>(tr_tlo, c) + half;
-        tr_hi[mm] = swz<D>(tr_thi, c) + half;
-    }
+    const int tr_lo = swz<D>(tr_tlo, tr_b >> 1) + (tr_b & 1) * 8;  // m = 0
+    const int tr_hi = swz<D>(tr_thi, tr_b >> 1) + (tr_b & 1) * 8;
     // 8-bit tiles: one ds_read_b64_tr_b8 per 16-row tile m of d.  In lane
     // group kg, lane 2k + x points at the 8 codes d = 16m + 8x .. +7 of
     // position row 16 (k / 4) + 4 kg + k % 4, so lane li receives column
@@ -454,28 +479,34 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     const int tr8_t = 16 * ((li >> 1) >> 2) + 4 * kg + ((li >> 1) & 3);
     const int tr8_row = tr8_t * C::ROWB + (li & 1) * 8;
     const int tr8_key = tile_key<FMT, D>(tr8_t) * 16;
-    auto pv_issue = [&](int tile, u32x2_t (&lo)[C::MT], u32x2_t (&hi)[C::MT]) {
-        const uint32_t vbase = lds_addr(smem + (tile % C::STAGES) * C::STAGE_BYTES + C::TILE_BYTES);
+    // P.V runs in two halves of d (tiles m < MT/2, then the rest), so the
+    // V^T operands of only one half occupy registers at a time.
+    constexpr int MH = C::MT / 2;
+    auto pv_issue = [&](int soff, auto half, u32x2_t (&lo)[MH], u32x2_t (&hi)[MH]) {
+        constexpr int M0 = decltype(half)::value * MH;
+        const uint32_t vbase = lds_addr(smem + soff + C::TILE_BYTES);
         if constexpr (C::Q8) {
 #pragma unroll
-            for (int m = 0; m < C::MT; ++m) lo[m] = ds_read_tr8_b64_asm(vbase + tr8_row + (tr8_key ^ (m * 16)));
+            for (int j = 0; j < MH; ++j)
+                lo[j] = ds_read_tr8_b64_asm(vbase + tr8_row + (tr8_key ^ ((M0 + j) * 16)));
         } else {
-            issue_vt_tile<C::MT, NR>(vbase, tr_lo, tr_hi, lo, hi);
+            issue_vt_tile<M0, MH, NR>(vbase + tr_lo, vbase + tr_hi, lo, hi);
         }
     };
-    auto pv_mma = [&](const u32x4_t& pb, u32x2_t (&lo)[C::MT], u32x2_t (&hi)[C::MT]) {
+    auto pv_mma = [&](const u32x4_t& pb, auto half, u32x2_t (&lo)[MH], u32x2_t (&hi)[MH]) {
+        constexpr int M0 = decltype(half)::value * MH;
         if constexpr (C::Q8)
-            wait_v8_tile<C::MT>(lo);
+            wait_v8_tile<MH>(lo);
         else
-            wait_vt_tile<C::MT>(lo, hi);
+            wait_vt_tile<MH>(lo, hi);
 #pragma unroll
-        for (int m = 0; m < C::MT; ++m) {
+        for (int j = 0; j < MH; ++j) {
             u32x4_t va;
             if constexpr (C::Q8)
-                va = widen8<FMT>(lo[m]);
+                va = widen8<FMT>(lo[j]);
             else
-                va = u32x4_t{lo[m].x, lo[m].y, hi[m].x, hi[m].y};
-            oacc[m] = mfma_16x16x32_bf16(va, pb, oacc[m]);
+                va = u32x4_t{lo[j].x, lo[j].y, hi[j].x, hi[j].y};
+            oacc[M0 + j] = mfma_16x16x32_bf16(va, pb, oacc[M0 + j]);
         }
     };
 
@@ -483,11 +514,18 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < C::STAGES - 2; ++t) issue_tile(t);
 
-    // Software pipeline: step `tile` reads V of `tile` (P.V with the P^T made
-    // in the previous step) and K of `tile` + 1 (q.K and its softmax), so the
-    // matrix cores and the vector ALU overlap inside each wave.  Ring slots
-    // in use during a step: `tile` and `tile` + 1; the step refills the slot
-    // of `tile` - 1 with `tile` + STAGES - 1, so STAGES - 2 tiles stay in flight.
+    // Software pipeline: step `tile` computes q.K of `tile` + 1 with its
+    // softmax and P.V of `tile` (P^T made in the previous step), so the matrix
+    // pipe and the vector ALU overlap inside each wave.  Order inside a step:
+    // q.K of the next tile (its K reads kept eight ahead), the V^T reads of
+    // the first half of d and the logit scaling while they land; then, in one
+    // basic block, P.V of the first half with the second half's V^T reads in
+    // its shadow, the rest of the softmax while those land, P.V of the second
+    // half.  A wave issues in order, and one 16x16x32 product takes about 17
+    // cycles to issue but about 50 before a dependent one may start (MI355X),
+    // so the order decides how much of the step is waiting.  Ring slots in use
+    // during a step: `tile` and `tile` + 1; the step refills the slot of
+    // `tile` - 1 with `tile` + STAGES - 1, so STAGES - 2 tiles stay in flight.
     u32x4_t pb = {0u, 0u, 0u, 0u};
     if (ntiles > 0) {
         ring_sync();  // tile 0 landed
@@ -496,26 +534,57 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
             f32x4_t sacc[2];
             qk_tile(0, sacc);
             float alpha;
-            softmax_tile(0, sacc, pb, alpha);  // O is still zero: no rescale
+            softmax_tile(0, 0, sacc, pb, alpha);  // O is still zero: no rescale
         }
     }
     for (int tile = 0; tile < ntiles; ++tile) {
+        const int soff = (tile % C::STAGES) * C::STAGE_BYTES, soff_next = ((tile + 1) % C::STAGES) * C::STAGE_BYTES;
         ring_sync();  // tile + 1 landed (a no-op read past the end)
         issue_tile(tile + C::STAGES - 1);
         if (w >= NG) continue;  // the load-only wave
-        const bool next = tile + 1 < ntiles;
-        // V of this tile is read first so it lands while q.K of the next runs
-        u32x2_t vlo[C::MT], vhi[C::MT];
-        pv_issue(tile, vlo, vhi);
-        f32x4_t sacc[2];
-        if (next) qk_tile(tile + 1, sacc);
-        pv_mma(pb, vlo, vhi);
-        if (next) {
-            float alpha;
-            if (softmax_tile(tile + 1, sacc, pb, alpha)) {
+        constexpr std::integral_constant<int, 0> first_half{};
+        constexpr std::integral_constant<int, 1> second_half{};
+        u32x2_t vlo[MH], vhi[MH];
+        f32x4_t sacc[2], vsc[2];
+        if (tile + 1 < ntiles) {
+            // q.K of the next tile first: the V^T reads issued after its
+            // K reads land while its products and the logit scaling run
+            qk_tile(soff_next, sacc);
+            pv_issue(soff, first_half, vlo, vhi);
+            softmax_prep(tile + 1, soff_next, sacc, vsc);
+        } else {
+            pv_issue(soff, first_half, vlo, vhi);
+            // past the last tile: all logits -inf, so the softmax step below
+            // leaves m and l unchanged (the max does not move, every weight is 0)
 #pragma unroll
-                for (int m = 0; m < C::MT; ++m) oacc[m] = oacc[m] * alpha;
+            for (int mq = 0; mq < 2; ++mq) {
+                sacc[mq] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                vsc[mq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
+        }
+        // One basic block from here (the softmax finish is branch-free): P.V of
+        // this tile and the softmax of the next, whose vector instructions
+        // issue while the products run.
+        pv_mma(pb, first_half, vlo, vhi);
+        pv_issue(soff, second_half, vlo, vhi);
+        u32x4_t pb_next;
+        float alpha;
+        const bool moved = softmax_finish(sacc, vsc, pb_next, alpha);
+        // tie the softmax results here so the compiler cannot sink their
+        // computation below the products (or past the rescale branch)
+        asm volatile("" : "+v"(pb_next), "+v"(l_run), "+v"(alpha));
+        pv_mma(pb, second_half, vlo, vhi);
+        if constexpr (!C::Q8) {
+            // products and vector instructions alternate
+            static_for<0, 2 * MH>([&](auto) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
+            });
+        }
+        pb = pb_next;
+        if (moved) {
+#pragma unroll
+            for (int m = 0; m < C::MT; ++m) oacc[m] = oacc[m] * alpha;
         }
     }
 
