@@ -461,6 +461,43 @@ def test_quant_window(variant, window):
     check_close(out, ref, "quant window %s W %d" % (variant, window))
 
 
+@pytest.mark.parametrize("kv_format", ["fp8", "int8"])
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("page_size,window", [(32, 45), (64, 300)])
+def test_quant_paged_window(kv_format, variant, page_size, window):
+    """8-bit codes in a paged pool with a sliding window: the oracle sees the window's rows moved to
+    the front of a contiguous 8-bit cache; the pool holds the unshifted cache, whose positions before
+    the window carry NaN codes and scales."""
+    w = Workload("q8pgwin", B=5, Hq=16, Hkv=2, D=128, Lmax=900, seed=1100 + window + page_size, len_lo=0, len_hi=900)
+    inp = make_inputs(w, poison_padding=True)
+    qc = quantize_cache(inp, kv_format)
+    lens = inp["seq_lens"]
+    lo = torch.clamp(lens.to(torch.int64) - window, min=0)
+    bad_code = 0x7F if kv_format == "fp8" else 0
+    shifted = {key: torch.full_like(qc[key], bad_code) for key in ("k_codes", "v_codes")}
+    shifted.update({key: torch.full_like(qc[key], float("nan")) for key in ("k_scale", "v_scale")})
+    for b in range(w.B):
+        n, a0 = int(lens[b]), int(lo[b])
+        for key in ("k_codes", "v_codes"):
+            shifted[key][b, :n - a0] = qc[key][b, a0:n]
+            qc[key][b, :a0] = bad_code
+        for key in ("k_scale", "v_scale"):
+            shifted[key][b, :, :n - a0] = qc[key][b, :, a0:n]
+            qc[key][b, :, :a0] = float("nan")       # positions before the window: NaN scales
+    ref = oracle.decode_quant(inp["q"], shifted["k_codes"], shifted["v_codes"], shifted["k_scale"],
+                              shifted["v_scale"], (lens - lo).to(torch.int32), kv_format, inp["scale"])
+    pg = to_dev(page_quant_cache(inp, qc, page_size, seed=page_size + window, spare_pages=2))
+    dev = to_dev(inp)
+    for chunk, combine in ((None, None), (128, "separate"), (128, "fused")):
+        print("case quant paged window", kv_format, variant, page_size, window, chunk, combine, flush=True)
+        out = binding.decode_paged(dev["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], dev["seq_lens"],
+                                   dev["scale"], variant=variant, chunk=chunk, combine=combine, window=window,
+                                   kv_format=kv_format, k_scale=pg["k_scale_pages"], v_scale=pg["v_scale_pages"])
+        torch.cuda.synchronize()
+        check_close(out, ref, "quant paged window %s %s page %d W %d chunk %s %s"
+                    % (kv_format, variant, page_size, window, chunk, combine))
+
+
 @pytest.mark.parametrize("name,kv_format", [("palm", "fp8"), ("gqa70b", "fp8"), ("ragged", "fp8"), ("long", "fp8"),
                                             ("ragged", "int8"), ("palm", "int8")])
 def test_quant_full_size_sampled(name, kv_format):
