@@ -646,11 +646,21 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int h0 = 0; h0 < 16; h0 += RPI) {
                 const int h = h0 + hr;
-                if (16 * w + h < gcnt)
-                    *reinterpret_cast<u32x4_t*>(dst + (size_t)h * D + 8 * c) =
-                        *reinterpret_cast<const u32x4_t*>(ot + h * ROWH + 8 * c);
+                if (16 * w + h < gcnt) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ot + h * ROWH + 8 * c);
+                    if (a.fused)
+                        store_coherent16(dst + (size_t)h * D + 8 * c, v);
+                    else
+                        *reinterpret_cast<u32x4_t*>(dst + (size_t)h * D + 8 * c) = v;
+                }
             }
-            if (kg == 0 && g < gcnt) a.part_ml[part0 + li] = f32x2_t{m_run + __log2f(l_run), (float)e};
+            if (kg == 0 && g < gcnt) {
+                const f32x2_t ml = f32x2_t{m_run + __log2f(l_run), (float)e};
+                if (a.fused)
+                    store_coherent8(a.part_ml + part0 + li, ml);
+                else
+                    a.part_ml[part0 + li] = ml;
+            }
         }
     }
     if (direct || !a.fused) return;

@@ -362,8 +362,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                 const int gg = idx / D, d = idx % D;
                 const int e = scale_exponent(__uint_as_float(s_amax[gg]));
                 const size_t part = ((size_t)unit * a.max_splits + s) * a.GT + g0 + gg;
-                a.part_o[part * D + d] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(val[k], -e));
-                if (d == 0) a.part_ml[part] = f32x2_t{lse[k], (float)e};
+                const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(val[k], -e));
+                if (a.fused) {
+                    store_coherent(a.part_o + part * D + d, h);
+                    if (d == 0) store_coherent8(a.part_ml + part, f32x2_t{lse[k], (float)e});
+                } else {
+                    a.part_o[part * D + d] = h;
+                    if (d == 0) a.part_ml[part] = f32x2_t{lse[k], (float)e};
+                }
             }
         }
     }

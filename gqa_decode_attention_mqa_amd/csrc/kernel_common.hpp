@@ -306,6 +306,27 @@ __device__ __forceinline__ u32x4_t widen8(u32x2_t c) {
     }
 }
 
+// Device-coherent stores and loads for the fused combine's partials: relaxed
+// atomics at agent scope, which gfx950 issues with the device-scope cache bit,
+// so a store writes through the XCD's L2 and a load reads past it.  With them
+// the partials need no L2 write-back or invalidate around the arrival counter
+// (both of which act on a whole XCD's L2).
+template <typename T>
+__device__ __forceinline__ void store_coherent(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent16(void* p, const u32x4_t& v) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    store_coherent(q, (uint64_t)v.x | ((uint64_t)v.y << 32));
+    store_coherent(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32));
+}
+__device__ __forceinline__ void store_coherent8(void* p, const f32x2_t& v) {
+    store_coherent(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v));
+}
+__device__ __forceinline__ uint64_t load_coherent8(const void* p) {
+    return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Fused log-sum-exp combine, run by the last chunk of a unit to arrive.  The
 // caller has already written its own partial.  Returns after every thread of
 // the workgroup has finished (it contains barriers: call it from all threads).
@@ -320,10 +341,11 @@ __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long uni
     int* ex = reinterpret_cast<int*>(Wg + gp);  // kFusedMaxSplits * gp scale exponents
     if (tid < gcnt) {
         float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_ml[base + (size_t)s * a.GT + g0 + tid].x);
+        for (int s = 0; s < nsplit; ++s)
+            M = fmaxf(M, __builtin_bit_cast(f32x2_t, load_coherent8(a.part_ml + base + (size_t)s * a.GT + g0 + tid)).x);
         float W = 0.f;
         for (int s = 0; s < nsplit; ++s) {
-            const f32x2_t ml = a.part_ml[base + (size_t)s * a.GT + g0 + tid];
+            const f32x2_t ml = __builtin_bit_cast(f32x2_t, load_coherent8(a.part_ml + base + (size_t)s * a.GT + g0 + tid));
             const float w = __builtin_amdgcn_exp2f(ml.x - M);
             wts[s * gp + tid] = w;
             ex[s * gp + tid] = (int)ml.y;
@@ -339,7 +361,7 @@ __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long uni
         const int g = idx / (D / 4), d4 = idx % (D / 4);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < nsplit; ++s) {
-            const u32x2_t h = *reinterpret_cast<const u32x2_t*>(a.part_o + (base + (size_t)s * a.GT + g0 + g) * D + 4 * d4);
+            const u32x2_t h = __builtin_bit_cast(u32x2_t, load_coherent8(a.part_o + (base + (size_t)s * a.GT + g0 + g) * D + 4 * d4));
             const int e = ex[s * gp + g];
             const f32x4_t o = {__builtin_amdgcn_ldexpf(f16_lo_f32(h.x), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.x), e),
                                __builtin_amdgcn_ldexpf(f16_lo_f32(h.y), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.y), e)};
@@ -351,11 +373,14 @@ __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long uni
 
 // Arrival bookkeeping of the fused combine: returns true in every thread of
 // the last workgroup to finish a chunk of this unit (and resets the counter).
-// The caller must have written its partial before calling.
+// The caller must have written its partial with the coherent stores above.
+// Each wave first waits until its stores are complete (acknowledged at the
+// device's coherence point), so by the time the counter shows the last
+// arrival every partial is readable with coherent loads.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, int nsplit, int* flag_lds) {
-    // Release only (write back, no invalidate): an acquire here would drop the
-    // XCD's whole L2 under every other workgroup still streaming K/V.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t old = atomicAdd(counter, 1u);
@@ -365,7 +390,7 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int nsplit, int* 
     }
     __syncthreads();
     const bool last = *flag_lds != 0;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other chunks' partials
+    asm volatile("" ::: "memory");
     return last;
 }
 
