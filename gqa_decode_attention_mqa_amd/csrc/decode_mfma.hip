@@ -1,9 +1,9 @@
 // Split-K decode attention on bf16 matrix cores, one wave per 16 query heads.
 //
-// For groups of more than four query heads per key/value head (e.g. the
-// 48-head multiquery attention of PaLM 540B in "Efficiently Scaling
-// Transformer Inference", section 3.4, "Attention Layer Partitioning", or the
-// 8-head groups of grouped-query attention) a workgroup owns (query row, kv
+// For every group size (e.g. the 48-head multiquery attention of PaLM 540B
+// in "Efficiently Scaling Transformer Inference", section 3.4, "Attention
+// Layer Partitioning", the 8-head groups of grouped-query attention, or
+// 8-bit caches widened to bf16 in registers) a workgroup owns (query row, kv
 // head, chunk of positions, block of 16*NG query rows, NG = 1..6).  Compute wave
 // w < NG owns heads 16w .. 16w+15 for every position of the chunk, so no two
 // waves ever merge softmax state; groups below 16 pad the head tile.  The
@@ -46,7 +46,10 @@ struct MfmaCfg {
     static constexpr bool Q8 = FMT != kKvBf16;       // 8-bit codes with a scale per row
     static constexpr int EB = Q8 ? 1 : 2;            // bytes per cached element
     // tiles in the LDS ring: bf16 D = 256 uses all 160 KB; D <= 128 leaves
-    // room for two workgroups per CU.  8-bit tiles are half as large; their
+    // room for two workgroups per CU (bf16 D = 128, B=32, Hkv=8, len 4096:
+    // 89.0 us at 4 tiles against 92.1 at 5 and 88.3 at 6, where one
+    // workgroup per CU fits; the ragged batch: 751 us at 4 and 5 tiles
+    // against 943 at 6).  8-bit tiles are half as large; their
     // kernel is bound by its own per-tile work rather than by loads in flight,
     // and a 4-tile ring measured faster than deeper ones (MI355X, PaLM-shaped
     // MQA: 24.8 us at 4 tiles against 29.0 us at 9; B=4, len 131072: 73.7
