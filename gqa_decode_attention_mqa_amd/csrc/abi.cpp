@@ -3,6 +3,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
@@ -285,7 +286,11 @@ mqa_status mqa_decode_plan_multi(int B, int T, int Hq, int Hkv, int D, int Lmax,
 }
 
 const char* mqa_status_string(mqa_status s) {
-    switch (s) {
+    // A C caller may pass any int; read it as one, since a C++ load of an
+    // enum outside its enumerators' range is undefined.
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
         case MQA_OK: return "ok";
         case MQA_ERR_NULL: return "null pointer argument";
         case MQA_ERR_SHAPE: return "invalid shape";
