@@ -151,8 +151,9 @@ def cpu_baseline(w, inp, target_s: float, window: int = 0, kv_format: str = "bf1
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (requested --gpus %d); the multi-GPU sharding "
-              "of the decode step is described in DESIGN.md but not built." % args.gpus, file=sys.stderr)
+        print("bench.py: the decode step runs on one GPU only (requested --gpus %d); sharding it over "
+              "several GPUs (by sequence, or by positions with an all-gather of the partials) is not "
+              "implemented." % args.gpus, file=sys.stderr)
         return 2
     import torch
     if args.copy_probe:
