@@ -128,6 +128,27 @@ def test_many_chunks_and_shape_changes_reuse_the_workspace(combine):
 
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
+def test_fused_combine_reads_this_calls_partials(variant):
+    """The fused combine's last workgroup reads the other chunks' partials through device-coherent
+    loads: two different input sets alternate through the same cached workspace, so a stale read
+    (the previous call's partials) would show as a wrong result."""
+    ws = [Workload("fz%d" % i, B=8, Hq=48, Hkv=1, D=256, Lmax=1536, seed=1200 + i, len_lo=700, len_hi=1536)
+          for i in range(2)]
+    cases = []
+    for w in ws:
+        inp = make_inputs(w, poison_padding=True)
+        ref = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+        cases.append((to_dev(inp), ref))
+    for it in range(12):
+        dev, ref = cases[it % 2]
+        print("case fused alternate", variant, it, flush=True)
+        out = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant, chunk=128,
+                             combine="fused")
+        torch.cuda.synchronize()
+        check_close(out, ref, "fused alternate %s iteration %d" % (variant, it))
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
 @pytest.mark.parametrize("vscale", [2.0 ** 20, 2.0 ** -20])
 def test_split_partials_keep_range_and_precision(variant, vscale):
     """Split chunks store fp16 partials scaled per (chunk, head); V far outside the fp16 range
