@@ -208,6 +208,12 @@ def _page_assignment(lens: torch.Tensor, Lmax: int, page_size: int, seed: int, s
     return table, placed, num_pages, max_blocks
 
 
+def _placement_indices(placed, device):
+    """(sequence, logical block, physical page) triples as three index tensors."""
+    t = torch.tensor(placed, dtype=torch.int64).reshape(-1, 3).to(device)
+    return t[:, 0], t[:, 1], t[:, 2]
+
+
 def page_contiguous_cache(inp: dict, page_size: int, seed: int, spare_pages: int = 0,
                           poison_spare: bool = True) -> dict:
     """Move the contiguous caches of ``inp`` (from :func:`make_inputs`) into a paged pool.
@@ -240,9 +246,11 @@ def page_contiguous_cache(inp: dict, page_size: int, seed: int, spare_pages: int
     else:
         k_pages.zero_()
         v_pages.zero_()
-    for b, blk, page in placed:
-        k_pages[page] = kc[b, blk * page_size:(blk + 1) * page_size]
-        v_pages[page] = vc[b, blk * page_size:(blk + 1) * page_size]
+    if placed:
+        # one gather per cache (a copy per page would be thousands of launches)
+        bs, blks, pages = _placement_indices(placed, device)
+        k_pages[pages] = kc.reshape(B, max_blocks, page_size, Hkv, D)[bs, blks]
+        v_pages[pages] = vc.reshape(B, max_blocks, page_size, Hkv, D)[bs, blks]
     out = dict(inp)
     out.update({"k_pages": k_pages, "v_pages": v_pages, "block_table": table.to(device),
                 "page_size": page_size, "num_pages": num_pages})
@@ -273,9 +281,11 @@ def page_quant_cache(inp: dict, qc: dict, page_size: int, seed: int, spare_pages
             sc = torch.cat([sc, torch.full((B, Hkv, padded_len - Lmax), float("nan"), device=device)], 2)
         pages = torch.full((max(num_pages, 1), page_size, Hkv, D), 0xFF, dtype=torch.uint8, device=device)
         spages = torch.full((max(num_pages, 1), Hkv, page_size), float("nan"), dtype=torch.float32, device=device)
-        for b, blk, page in placed:
-            pages[page] = codes[b, blk * page_size:(blk + 1) * page_size]
-            spages[page] = sc[b, :, blk * page_size:(blk + 1) * page_size]
+        if placed:
+            bs, blks, idx = _placement_indices(placed, device)
+            pages[idx] = codes.reshape(B, max_blocks, page_size, Hkv, D)[bs, blks]
+            # a slice between the two index tensors: the result is [pages, Hkv, page_size]
+            spages[idx] = sc.reshape(B, Hkv, max_blocks, page_size)[bs, :, blks]
         out[name + "_pages"] = pages
         out[name + "_scale_pages"] = spages
     return out
