@@ -19,13 +19,14 @@ mqa_status fail(mqa_status s, const std::string& msg) {
 }
 
 // Workgroups the planner aims for when it picks the chunk size: one per CU.
-// Measured on MI355X, more, shorter chunks lose to the extra partial traffic
-// (PaLM-shaped MQA: chunk 512 -> 39.6 us, 256 -> 48.8 us, 1024 -> 55.9 us;
-// long-context MQA: 2048 -> 110 us, 1024 -> 122 us, 4096 -> 186 us).
+// Measured on MI355X (split kernel), more, shorter chunks lose to their extra
+// fixed costs and partial traffic, fewer leave CUs idle (PaLM-shaped MQA:
+// chunk 512 -> 28.5 us, 256 -> 34.8 us, 1024 -> 33.6 us; long-context MQA:
+// 2048 -> 84.2 us, 1024 -> 92.9 us, 4096 -> 111.3 us).
 constexpr long long kTargetWorkgroups = kComputeUnits;
 // Chunk bounds: below 256 positions the partial outputs cost more traffic than
 // the split saves; longer chunks balance a ragged batch poorly (the vector
-// kernel, used for ragged small-group batches, gets the tighter bound).
+// kernel, an explicit variant, gets the tighter bound).
 constexpr long long kMinChunk = 256;
 constexpr long long kMaxChunkMfma = 2048;
 constexpr long long kMaxChunkValu = 1024;
@@ -175,9 +176,10 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     if (p.max_splits > 1 && p.rows > 0) {
         if (o.combine == 2 && p.max_splits > kFusedMaxSplits)
             return fail(MQA_ERR_ARG, "the fused combine handles at most 16 chunks per sequence");
-        // Default: the separate combine kernel.  The fused form needs an
-        // agent-scope release (an L2 write-back) in every workgroup, which
-        // measured 2-3x slower on MI355X.
+        // Default: the separate combine kernel.  In the fused form the last
+        // workgroup of each unit merges the partials at the tail of the split
+        // kernel, which measured slower on MI355X (PaLM-shaped MQA step
+        // 39.7 us against 32.4 us with the separate kernel).
         p.combine = (o.combine == 0) ? 1 : o.combine;
         if (p.combine != 1)
             p.grid_combine = 0;
