@@ -45,6 +45,10 @@ struct MfmaCfg {
     static constexpr int STEP = 32;                  // positions per tile
     static constexpr bool Q8 = FMT != kKvBf16;       // 8-bit codes with a scale per row
     static constexpr int EB = Q8 ? 1 : 2;            // bytes per cached element
+    // E4M3 caches with D a multiple of 128: q.K runs on fp8 matrix cores
+    // (16x16x128) straight from the codes, with q split into two E4M3 parts
+    static constexpr bool F8MMA = FMT == kKvFp8 && D % 128 == 0;
+    static constexpr int NH8 = F8MMA ? D / 128 : 1;  // 128-wide halves of d
     // tiles in the LDS ring: bf16 D = 256 uses all 160 KB; D <= 128 leaves
     // room for two workgroups per CU (bf16 D = 128, B=32, Hkv=8, len 4096:
     // 89.0 us at 4 tiles against 92.1 at 5 and 88.3 at 6, where one
@@ -239,7 +243,65 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // A compute wave's q^T operand (B of q.K): lane (li, kg), k-step ks holds
     // q[head 16w + li][32 ks + 8 kg .. +8]; heads past the group read as zero.
     u32x4_t qb[C::KS];
+    // fp8 matrix cores: lane (li, kg) holds, for each 128-wide half h of d,
+    // q[head][128h + 32kg .. +31] * 2^qe as the sum of two E4M3 codes (qh +
+    // ql), qe per head putting its largest |q| in [128, 256).  A bf16 value
+    // has 8 significant bits: the high code keeps 4, and the remainder (at
+    // most 8 units of the value's last place) fits the low code exactly, so
+    // only parts below E4M3's smallest subnormal (2^-9 of a 2^7..2^8 range)
+    // are rounded.  qk8 = 2^-qe undoes the scaling in the logit.
+    i32x8_t qh[C::NH8], ql[C::NH8];
+    float qk8 = 1.f;
     if (w >= NG) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    } else if constexpr (C::F8MMA) {
+        const size_t q0 = qrow_offset(row, a.T, a.Hq, a.G, D, kvh, 0);
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, a.GT - 1) - q0 + D) * 2);
+        const int r = g0 + 16 * w + li;
+        const int qoff = r < a.GT ? (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, r) - q0) * 2 : kOutOfRange;
+        u32x4_t raw[C::NH8][4];
+#pragma unroll
+        for (int h = 0; h < C::NH8; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                raw[h][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            qr, qoff + (128 * h + 32 * kg) * 2 + 16 * j, 0, 0));
+        __builtin_amdgcn_s_waitcnt(kVmcntStages<0, 0>());
+        float mx = 0.f;
+#pragma unroll
+        for (int h = 0; h < C::NH8; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    mx = fmaxf(mx, fmaxf(fabsf(bf16_lo_f32(raw[h][j][d])), fabsf(bf16_hi_f32(raw[h][j][d]))));
+        mx = max_xor32(max_xor16(mx));  // over the head's lanes li, li + 16, li + 32, li + 48
+        int qe = 0;
+        if (mx > 0.f) {
+            int e2;
+            (void)frexpf(mx, &e2);  // mx = f 2^e2, f in [0.5, 1)
+            qe = 8 - e2;
+        }
+        qk8 = __builtin_amdgcn_ldexpf(1.f, -qe);
+#pragma unroll
+        for (int h = 0; h < C::NH8; ++h)
+#pragma unroll
+            for (int dw = 0; dw < 8; ++dw) {
+                const uint32_t w0 = raw[h][dw >> 1][2 * (dw & 1)], w1 = raw[h][dw >> 1][2 * (dw & 1) + 1];
+                const float x0 = __builtin_amdgcn_ldexpf(bf16_lo_f32(w0), qe);
+                const float x1 = __builtin_amdgcn_ldexpf(bf16_hi_f32(w0), qe);
+                const float x2 = __builtin_amdgcn_ldexpf(bf16_lo_f32(w1), qe);
+                const float x3 = __builtin_amdgcn_ldexpf(bf16_hi_f32(w1), qe);
+                int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
+                int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - __builtin_amdgcn_cvt_f32_fp8(hi, 0),
+                                                         x1 - __builtin_amdgcn_cvt_f32_fp8(hi, 1), 0, false);
+                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - __builtin_amdgcn_cvt_f32_fp8(hi, 2),
+                                                     x3 - __builtin_amdgcn_cvt_f32_fp8(hi, 3), lo, true);
+                qh[h][dw] = hi;
+                ql[h][dw] = lo;
+            }
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
     } else {
@@ -326,6 +388,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < C::MT; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const float qk = a.qk_log2;
+    const float qkq = C::F8MMA ? qk * qk8 : qk;  // 8-bit logits: undo q's power-of-two scaling
 
     // S^T = K q^T for one tile: A = two 16-row K tiles read from LDS, B = q^T.
     // Accumulator lane (li, kg), element r of tile mq: head li, position 16mq + 4kg + r.
@@ -340,8 +403,42 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         k8_row[mq] = t * C::ROWB + (kg & 1) * 8;
         k8_key[mq] = (tile_key<FMT, D>(t) ^ (kg >> 1)) * 16;
     }
+    // fp8 matrix cores: lane (li, kg) reads, for row 16mq + li and half h,
+    // the 32 codes 128h + 32kg .. +31 (chunks 8h + 2kg and 8h + 2kg + 1)
+    int f8_off[2][C::NH8][2];
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+        for (int h = 0; h < C::NH8; ++h)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int t = 16 * mq + li;
+                f8_off[mq][h][x] = t * C::ROWB + (((8 * h + 2 * kg + x) ^ tile_key<FMT, D>(t)) * 16);
+            }
     auto qk_tile = [&](int soff, f32x4_t (&sacc)[2]) {
         const unsigned char* kt = smem + soff;
+        if constexpr (C::F8MMA) {
+            f32x4_t part[2][2];  // [mq][high or low part of q]
+#pragma unroll
+            for (int mq = 0; mq < 2; ++mq) part[mq][0] = part[mq][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int h = 0; h < C::NH8; ++h)
+#pragma unroll
+                for (int mq = 0; mq < 2; ++mq) {
+                    const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kt + f8_off[mq][h][0]);
+                    const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(kt + f8_off[mq][h][1]);
+                    const i32x8_t ka = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
+                                        (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+                    part[mq][0] = mfma_16x16x128_fp8(ka, qh[h], part[mq][0]);
+                    part[mq][1] = mfma_16x16x128_fp8(ka, ql[h], part[mq][1]);
+                }
+            // every K read of the tile first, then the products
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * C::NH8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * C::NH8, 0);
+            sacc[0] = part[0][0] + part[0][1];
+            sacc[1] = part[1][0] + part[1][1];
+            return;
+        }
         f32x4_t part[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -401,7 +498,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
                 const f32x4_t ksc = *reinterpret_cast<const f32x4_t*>(scl + 16 * mq + 4 * kg);
                 vsc[mq] = *reinterpret_cast<const f32x4_t*>(scl + C::STEP + 16 * mq + 4 * kg);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sacc[mq][r] *= qk * ksc[r];
+                for (int r = 0; r < 4; ++r) sacc[mq][r] *= qkq * ksc[r];
             }
         } else {
 #pragma unroll

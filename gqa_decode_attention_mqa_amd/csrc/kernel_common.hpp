@@ -14,6 +14,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 
 // Arguments of the split-K decode kernels, passed by value.
 //
@@ -265,6 +266,14 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 16x16x128 product of E4M3 codes (gfx950), unscaled (E8M0 scale 127 = 2^0).
+// Lane (i, g) of A holds 32 codes of row i and lane (i, g) of B 32 codes of
+// column i, for the same 32 values of k: the sum over k does not depend on
+// which k the hardware gives each byte, as long as A and B agree.
+__device__ __forceinline__ f32x4_t mfma_16x16x128_fp8(const i32x8_t& a, const i32x8_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
