@@ -49,6 +49,9 @@ struct MfmaCfg {
     // (16x16x128) straight from the codes, with q split into two E4M3 parts
     static constexpr bool F8MMA = FMT == kKvFp8 && D % 128 == 0;
     static constexpr int NH8 = F8MMA ? D / 128 : 1;  // 128-wide halves of d
+    // int8 caches: q.K on int8 matrix cores (16x16x64), q as 128 hi + lo
+    static constexpr bool I8MMA = FMT == kKvInt8;
+    static constexpr int NB8 = I8MMA ? D / 64 : 1;   // 64-wide blocks of d
     // tiles in the LDS ring: bf16 D = 256 uses all 160 KB; D <= 128 leaves
     // room for two workgroups per CU (bf16 D = 128, B=32, Hkv=8, len 4096:
     // 89.0 us at 4 tiles against 92.1 at 5 and 88.3 at 6, where one
@@ -251,6 +254,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // only parts below E4M3's smallest subnormal (2^-9 of a 2^7..2^8 range)
     // are rounded.  qk8 = 2^-qe undoes the scaling in the logit.
     i32x8_t qh[C::NH8], ql[C::NH8];
+    // int8 matrix cores: lane (li, kg) holds, for each 64-wide block b of d,
+    // Q = rint(q[head][64b + 16kg .. +15] * 2^qe) as 128 hi + lo (int8
+    // each, |hi| <= 64, -64 <= lo < 64), qe per head putting its largest |q|
+    // in [2^12, 2^13): each q is rounded to 2^-13 of the head's largest |q|.
+    i32x4_t qih[C::NB8], qil[C::NB8];
     float qk8 = 1.f;
     if (w >= NG) {
 #pragma unroll
@@ -301,6 +309,56 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
                                                      x3 - __builtin_amdgcn_cvt_f32_fp8(hi, 3), lo, true);
                 qh[h][dw] = hi;
                 ql[h][dw] = lo;
+            }
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    } else if constexpr (C::I8MMA) {
+        const size_t q0 = qrow_offset(row, a.T, a.Hq, a.G, D, kvh, 0);
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, a.GT - 1) - q0 + D) * 2);
+        const int r = g0 + 16 * w + li;
+        const int qoff = r < a.GT ? (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, r) - q0) * 2 : kOutOfRange;
+        u32x4_t raw[C::NB8][2];
+#pragma unroll
+        for (int b = 0; b < C::NB8; ++b)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                raw[b][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            qr, qoff + (64 * b + 16 * kg) * 2 + 16 * j, 0, 0));
+        __builtin_amdgcn_s_waitcnt(kVmcntStages<0, 0>());
+        float mx = 0.f;
+#pragma unroll
+        for (int b = 0; b < C::NB8; ++b)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    mx = fmaxf(mx, fmaxf(fabsf(bf16_lo_f32(raw[b][j][d])), fabsf(bf16_hi_f32(raw[b][j][d]))));
+        mx = max_xor32(max_xor16(mx));
+        int qe = 0;
+        if (mx > 0.f) {
+            int e2;
+            (void)frexpf(mx, &e2);  // mx = f 2^e2, f in [0.5, 1)
+            qe = 13 - e2;
+        }
+        qk8 = __builtin_amdgcn_ldexpf(1.f, -qe);
+#pragma unroll
+        for (int b = 0; b < C::NB8; ++b)
+#pragma unroll
+            for (int dw = 0; dw < 4; ++dw) {
+                // codes 4dw .. 4dw + 3 of the lane's 16: bf16 elements of raw[b][dw / 2]
+                const uint32_t w0 = raw[b][dw >> 1][2 * (dw & 1)], w1 = raw[b][dw >> 1][2 * (dw & 1) + 1];
+                const float xs[4] = {bf16_lo_f32(w0), bf16_hi_f32(w0), bf16_lo_f32(w1), bf16_hi_f32(w1)};
+                uint32_t hi = 0u, lo = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int Q = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(xs[e], qe));
+                    const int qh8 = (Q + 64) >> 7;  // round(Q / 128), |qh8| <= 64
+                    const int ql8 = Q - 128 * qh8;  // in [-64, 64)
+                    hi |= (uint32_t)(qh8 & 0xFF) << (8 * e);
+                    lo |= (uint32_t)(ql8 & 0xFF) << (8 * e);
+                }
+                qih[b][dw] = (int)hi;
+                qil[b][dw] = (int)lo;
             }
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
@@ -388,7 +446,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < C::MT; ++j) oacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const float qk = a.qk_log2;
-    const float qkq = C::F8MMA ? qk * qk8 : qk;  // 8-bit logits: undo q's power-of-two scaling
+    const float qkq = (C::F8MMA || C::I8MMA) ? qk * qk8 : qk;  // 8-bit logits: undo q's power-of-two scaling
 
     // S^T = K q^T for one tile: A = two 16-row K tiles read from LDS, B = q^T.
     // Accumulator lane (li, kg), element r of tile mq: head li, position 16mq + 4kg + r.
@@ -415,8 +473,40 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
                 const int t = 16 * mq + li;
                 f8_off[mq][h][x] = t * C::ROWB + (((8 * h + 2 * kg + x) ^ tile_key<FMT, D>(t)) * 16);
             }
+    // int8 matrix cores: lane (li, kg) reads, for row 16mq + li and block b,
+    // the 16 codes 64b + 16kg .. +15 (chunk 4b + kg)
+    int i8_off[2][C::NB8];
+#pragma unroll
+    for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+        for (int b = 0; b < C::NB8; ++b) {
+            const int t = 16 * mq + li;
+            i8_off[mq][b] = t * C::ROWB + (((4 * b + kg) ^ tile_key<FMT, D>(t)) * 16);
+        }
     auto qk_tile = [&](int soff, f32x4_t (&sacc)[2]) {
         const unsigned char* kt = smem + soff;
+        if constexpr (C::I8MMA) {
+            i32x4_t part[2][2];  // [mq][hi or lo part of q]
+#pragma unroll
+            for (int mq = 0; mq < 2; ++mq) part[mq][0] = part[mq][1] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int b = 0; b < C::NB8; ++b)
+#pragma unroll
+                for (int mq = 0; mq < 2; ++mq) {
+                    const i32x4_t ka = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(kt + i8_off[mq][b]));
+                    part[mq][0] = mfma_16x16x64_i8(ka, qih[b], part[mq][0]);
+                    part[mq][1] = mfma_16x16x64_i8(ka, qil[b], part[mq][1]);
+                }
+            // every K read of the tile first, then the products
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NB8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * C::NB8, 0);
+#pragma unroll
+            for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)  // |128 hi + lo| sums stay below 2^24: exact in fp32
+                    sacc[mq][r] = (float)(128 * part[mq][0][r] + part[mq][1][r]);
+            return;
+        }
         if constexpr (C::F8MMA) {
             f32x4_t part[2][2];  // [mq][high or low part of q]
 #pragma unroll

@@ -15,6 +15,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
 
 // Arguments of the split-K decode kernels, passed by value.
 //
@@ -274,6 +275,12 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const u32x4_t& a, const u3
 // which k the hardware gives each byte, as long as A and B agree.
 __device__ __forceinline__ f32x4_t mfma_16x16x128_fp8(const i32x8_t& a, const i32x8_t& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// 16x16x64 product of int8 values with int32 accumulation (gfx950); the
+// same agreement of A and B on each byte's k as above.
+__device__ __forceinline__ i32x4_t mfma_16x16x64_i8(const i32x4_t& a, const i32x4_t& b, const i32x4_t& c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
