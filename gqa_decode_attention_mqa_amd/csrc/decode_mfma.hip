@@ -1,9 +1,9 @@
-// Split-K decode attention on bf16 matrix cores, one wave per 16 query heads.
+// Split-K decode attention on matrix cores, one wave per 16 query heads.
 //
 // For every group size (e.g. the 48-head multiquery attention of PaLM 540B
 // in "Efficiently Scaling Transformer Inference", section 3.4, "Attention
-// Layer Partitioning", the 8-head groups of grouped-query attention, or
-// 8-bit caches widened to bf16 in registers) a workgroup owns (query row, kv
+// Layer Partitioning", the 8-head groups of grouped-query attention) and
+// every cache format (bf16, E4M3 or int8 codes) a workgroup owns (query row, kv
 // head, chunk of positions, block of 16*NG query rows, NG = 1..6).  Compute wave
 // w < NG owns heads 16w .. 16w+15 for every position of the chunk, so no two
 // waves ever merge softmax state; groups below 16 pad the head tile.  The
@@ -15,11 +15,14 @@
 //
 // Per tile, in each compute wave:
 //   * S^T = K q^T on 16x16x32 bf16 tiles: A = two 16-row K tiles (read from
-//     LDS), B = this wave's q^T (registers).  Head g = lane mod 16.
+//     LDS), B = this wave's q^T (registers).  Head g = lane mod 16.  8-bit
+//     caches feed their codes to the fp8 (16x16x128) or int8 (16x16x64)
+//     matrix cores directly, with q split into two 8-bit parts.
 //   * base-2 online softmax with lazy rescaling; the two S^T accumulators are
 //     exactly the 8 k-slots per lane of the P^T operand of P.V.
 //   * O^T += V^T P^T on 16x16x32 tiles: the V^T operand is read from LDS with
-//     gfx950's transposing LDS reads (ds_read_b64_tr_b16), so no lane shuffles.
+//     gfx950's transposing LDS reads (ds_read_b64_tr_b16), so no lane shuffles
+//     (8-bit caches: ds_read_b64_tr_b8, codes widened to bf16 in registers).
 // The loop is software-pipelined by one tile: q.K of the next tile is issued
 // together with P.V of the current one.
 // Rows at or past the end of the chunk are out of the buffer range and arrive
