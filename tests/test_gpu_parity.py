@@ -520,7 +520,7 @@ def test_quant_paged_window(kv_format, variant, page_size, window):
 
 
 @pytest.mark.parametrize("name,kv_format", [("palm", "fp8"), ("gqa70b", "fp8"), ("ragged", "fp8"), ("long", "fp8"),
-                                            ("ragged", "int8"), ("palm", "int8")])
+                                            ("ragged", "int8"), ("palm", "int8"), ("long", "int8"), ("gqa70b", "int8")])
 def test_quant_full_size_sampled(name, kv_format):
     w = WORKLOADS[name]
     print("case full quant", name, kv_format, flush=True)
