@@ -53,7 +53,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     if ((tid & 63) == 0) s_max[tid >> 6] = m;
     __syncthreads();
-    const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    // A query row that sees no position in any chunk (a later token of a
+    // multi-token call whose limit lies before the sequence start) has lse =
+    // -inf everywhere: every weight is then 0 and the row is written as zeros.
+    float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    M = M == -INFINITY ? 0.f : M;
 
     const int slots = a.D / 4;          // 16, 32 or 64
     const int lanes_per_slot = 256 / slots;
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
             wsum += s_w[j * slots + slot];
         }
         float* dst = a.out + (size_t)rh * a.D;
-        *reinterpret_cast<f32x4_t*>(dst + 4 * slot) = acc * (1.f / wsum);
+        *reinterpret_cast<f32x4_t*>(dst + 4 * slot) = acc * (wsum > 0.f ? 1.f / wsum : 0.f);
     }
 }
 
@@ -119,6 +123,7 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
     float M = ml[0].x;
 #pragma unroll
     for (int s = 1; s < S; ++s) M = fmaxf(M, ml[s].x);
+    M = M == -INFINITY ? 0.f : M;  // no visible position in any chunk: all weights 0, zero row
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
 #pragma unroll
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
         wsum += wgt;
     }
     float* dst = a.out + (size_t)gh * D + 8 * slot;
-    const float inv = 1.f / wsum;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     *reinterpret_cast<f32x4_t*>(dst) = acc0 * inv;
     *reinterpret_cast<f32x4_t*>(dst + 4) = acc1 * inv;
 }

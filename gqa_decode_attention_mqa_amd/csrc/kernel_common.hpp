@@ -359,6 +359,7 @@ __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long uni
         float M = -INFINITY;
         for (int s = 0; s < nsplit; ++s)
             M = fmaxf(M, __builtin_bit_cast(f32x2_t, load_coherent8(a.part_ml + base + (size_t)s * a.GT + g0 + tid)).x);
+        M = M == -INFINITY ? 0.f : M;  // a query row that sees no position: zero row
         float W = 0.f;
         for (int s = 0; s < nsplit; ++s) {
             const f32x2_t ml = __builtin_bit_cast(f32x2_t, load_coherent8(a.part_ml + base + (size_t)s * a.GT + g0 + tid));
@@ -368,7 +369,7 @@ __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long uni
             W += w;
         }
         Mg[tid] = M;
-        Wg[tid] = 1.f / W;
+        Wg[tid] = W > 0.f ? 1.f / W : 0.f;
     }
     __syncthreads();
     const int D = a.D;

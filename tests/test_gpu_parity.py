@@ -9,8 +9,8 @@ NaN so a read of it shows.
 
 Small cases cover several tiles, ragged tails, every head size, both kernel
 families, forced split sizes (so the combine kernel runs) and edge cases.  The
-five full-size workloads run in the launch configuration the benchmark uses;
-there the oracle checks a sample of sequences.
+five full-size workloads run in the launch configuration the benchmark uses,
+every sequence against the oracle.
 """
 import math
 
@@ -308,8 +308,9 @@ def test_paged_shared_prefix():
     check_close(out, ref, "shared prefix")
 
 
-def test_paged_full_size_ragged_sampled():
-    """The ragged workload on a page pool of 64-position pages (pool = the used pages only)."""
+def test_paged_full_size_ragged():
+    """The ragged workload on a page pool of 64-position pages (pool = the used pages only),
+    every sequence against the paged oracle."""
     w = WORKLOADS["ragged"]
     print("case full paged ragged", flush=True)
     inp = make_inputs(w, device=DEV)
@@ -317,13 +318,10 @@ def test_paged_full_size_ragged_sampled():
     del inp["k"], inp["v"]
     out = binding.decode_paged(pg["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], pg["seq_lens"], pg["scale"])
     torch.cuda.synchronize()
-    idx = sample_indices(pg["seq_lens"], 8)
-    sel = torch.tensor(idx, device=DEV)
-    ref = oracle.decode_paged(pg["q"].index_select(0, sel).cpu(), pg["k_pages"].cpu(), pg["v_pages"].cpu(),
-                              pg["block_table"].index_select(0, sel).cpu(), pg["seq_lens"].index_select(0, sel).cpu(),
-                              pg["scale"])
-    err = check_close(out.index_select(0, sel), ref, "paged ragged")
-    print("full paged ragged: %d sequences checked, max abs err %.3g" % (len(idx), err), flush=True)
+    ref = oracle.decode_paged(pg["q"].cpu(), pg["k_pages"].cpu(), pg["v_pages"].cpu(), pg["block_table"].cpu(),
+                              pg["seq_lens"].cpu(), pg["scale"])
+    err = check_close(out, ref, "paged ragged")
+    print("full paged ragged: all %d sequences checked, max abs err %.3g" % (w.B, err), flush=True)
 
 
 # ------------------------------------------------------ sliding window (local attention)
@@ -386,8 +384,8 @@ def test_window_on_a_paged_cache(variant, page_size, window):
         check_close(out, ref, "window paged %s page %d W %d chunk %s" % (variant, page_size, window, chunk))
 
 
-@pytest.mark.parametrize("name,window", [("ragged", 4096), ("palm", 1024)])
-def test_window_full_size_sampled(name, window):
+@pytest.mark.parametrize("name,window", [("ragged", 4096), ("palm", 1024), ("long", 8192)])
+def test_window_full_size(name, window):
     w = WORKLOADS[name]
     print("case full window", name, window, flush=True)
     inp = make_inputs(w, device=DEV, poison_padding=w.ragged)
@@ -396,13 +394,10 @@ def test_window_full_size_sampled(name, window):
     poison_positions_below_(inp["v"], lo)
     out = binding.decode_window(inp["q"], inp["k"], inp["v"], inp["seq_lens"], window, inp["scale"])
     torch.cuda.synchronize()
-    idx = sample_indices(inp["seq_lens"], SAMPLES[name])
-    sel = torch.tensor(idx, device=DEV)
-    ref = oracle.decode_window(inp["q"].index_select(0, sel).cpu(), inp["k"].index_select(0, sel).cpu(),
-                               inp["v"].index_select(0, sel).cpu(), inp["seq_lens"].index_select(0, sel).cpu(),
-                               window, inp["scale"])
-    err = check_close(out.index_select(0, sel), ref, "%s window %d" % (name, window))
-    print("full %s window %d: %d sequences checked, max abs err %.3g" % (name, window, len(idx), err), flush=True)
+    ref = oracle.decode_window(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), window,
+                               inp["scale"])
+    err = check_close(out, ref, "%s window %d" % (name, window))
+    print("full %s window %d: all %d sequences checked, max abs err %.3g" % (name, window, w.B, err), flush=True)
 
 
 # ------------------------------------------------------ 8-bit KV cache
@@ -521,7 +516,7 @@ def test_quant_paged_window(kv_format, variant, page_size, window):
 
 @pytest.mark.parametrize("name,kv_format", [("palm", "fp8"), ("gqa70b", "fp8"), ("ragged", "fp8"), ("long", "fp8"),
                                             ("ragged", "int8"), ("palm", "int8"), ("long", "int8"), ("gqa70b", "int8")])
-def test_quant_full_size_sampled(name, kv_format):
+def test_quant_full_size(name, kv_format):
     w = WORKLOADS[name]
     print("case full quant", name, kv_format, flush=True)
     inp = make_inputs(w, device=DEV, poison_padding=w.ragged)
@@ -530,13 +525,10 @@ def test_quant_full_size_sampled(name, kv_format):
     out = binding.decode_quant(inp["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
                                inp["seq_lens"], kv_format, inp["scale"])
     torch.cuda.synchronize()
-    idx = sample_indices(inp["seq_lens"], SAMPLES[name])
-    sel = torch.tensor(idx, device=DEV)
-    pick = lambda t: t.index_select(0, sel).cpu()
-    ref = oracle.decode_quant(pick(inp["q"]), pick(qc["k_codes"]), pick(qc["v_codes"]), pick(qc["k_scale"]),
-                              pick(qc["v_scale"]), pick(inp["seq_lens"]), kv_format, inp["scale"])
-    err = check_close(out.index_select(0, sel), ref, "%s %s" % (name, kv_format))
-    print("full %s %s: %d sequences checked, max abs err %.3g" % (name, kv_format, len(idx), err), flush=True)
+    ref = oracle.decode_quant(inp["q"].cpu(), qc["k_codes"].cpu(), qc["v_codes"].cpu(), qc["k_scale"].cpu(),
+                              qc["v_scale"].cpu(), inp["seq_lens"].cpu(), kv_format, inp["scale"])
+    err = check_close(out, ref, "%s %s" % (name, kv_format))
+    print("full %s %s: all %d sequences checked, max abs err %.3g" % (name, kv_format, w.B, err), flush=True)
 
 
 # ------------------------------------------------------ multi-token decode
@@ -581,6 +573,52 @@ def test_multi_short_sequences_and_one_token():
 
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("combine", ["separate", "fused"])
+def test_multi_tokens_before_the_start_of_a_split_sequence(variant, combine):
+    """chunk < n < T: tokens i < T - n see no position in any of the sequence's chunks, so every chunk
+    reports lse = -inf for them; the merge must write their rows as zeros (the oracle's and the
+    header's contract), not NaN."""
+    T = 600
+    w = Workload("multi-split-short", B=3, Hq=8, Hkv=1, D=128, Lmax=1024, seed=970)
+    inp = make_multi_inputs(w, T)
+    lens = torch.tensor([500, 300, 1024], dtype=torch.int32)
+    from gqa_decode_attention_mqa_amd.workloads import poison_padding_
+    poison_padding_(inp["k"], lens)
+    poison_padding_(inp["v"], lens)
+    ref = oracle.decode_multi(inp["q"], inp["k"], inp["v"], lens, inp["scale"])
+    assert (ref[0, :T - 500] == 0).all() and (ref[1, :T - 300] == 0).all()
+    dev = to_dev(inp)
+    print("case multi split short", variant, combine, flush=True)
+    out = binding.decode_multi(dev["q"], dev["k"], dev["v"], lens.to(DEV), dev["scale"], variant=variant,
+                               chunk=128, combine=combine)
+    torch.cuda.synchronize()
+    check_close(out, ref, "multi split short %s %s" % (variant, combine))
+    assert torch.equal(out[0, :T - 500].cpu(), torch.zeros_like(out[0, :T - 500].cpu()))
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+def test_multi_default_plan_with_tokens_before_the_start(variant):
+    """The planner's own chunking (B=1, Hq=8, D=64, Lmax=2048, T=1500, n=1200 splits the sequence):
+    tokens 0..299 have no visible position and must come back as zero rows."""
+    T = 1500
+    w = Workload("multi-plan-short", B=1, Hq=8, Hkv=1, D=64, Lmax=2048, seed=971)
+    inp = make_multi_inputs(w, T)
+    lens = torch.tensor([1200], dtype=torch.int32)
+    from gqa_decode_attention_mqa_amd.workloads import poison_padding_
+    poison_padding_(inp["k"], lens)
+    poison_padding_(inp["v"], lens)
+    plan = binding.plan(1, 8, 1, 64, 2048, inp["scale"], variant=variant, tokens=T)
+    assert plan["max_splits"] > 1, plan
+    ref = oracle.decode_multi(inp["q"], inp["k"], inp["v"], lens, inp["scale"])
+    dev = to_dev(inp)
+    print("case multi default plan short", variant, plan, flush=True)
+    out = binding.decode_multi(dev["q"], dev["k"], dev["v"], lens.to(DEV), dev["scale"], variant=variant)
+    torch.cuda.synchronize()
+    check_close(out, ref, "multi default plan short %s" % variant)
+    assert torch.equal(out[0, :300].cpu(), torch.zeros((300, 8, 64)))
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
 def test_multi_on_an_fp8_cache(variant):
     T = 4
     w = Workload("multi-q8", B=4, Hq=16, Hkv=4, D=128, Lmax=700, seed=960, len_lo=0, len_hi=700)
@@ -599,54 +637,54 @@ def test_multi_on_an_fp8_cache(variant):
     check_close(out, ref, "multi fp8 %s" % variant)
 
 
-@pytest.mark.parametrize("name,T", [("ragged", 4), ("gqa70b", 4), ("palm", 2)])
-def test_multi_full_size_sampled(name, T):
+@pytest.mark.parametrize("name,T", [("ragged", 4), ("gqa70b", 4), ("palm", 2), ("long", 2)])
+def test_multi_full_size(name, T):
     w = WORKLOADS[name]
     print("case full multi", name, T, flush=True)
     inp = make_multi_inputs(w, T, device=DEV, poison_padding=w.ragged)
     out = binding.decode_multi(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
     torch.cuda.synchronize()
-    idx = sample_indices(inp["seq_lens"], SAMPLES[name])
-    sel = torch.tensor(idx, device=DEV)
-    pick = lambda t: t.index_select(0, sel).cpu()
-    ref = oracle.decode_multi(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), pick(inp["seq_lens"]), inp["scale"])
-    err = check_close(out.index_select(0, sel), ref, "%s T=%d" % (name, T))
-    print("full %s T=%d: %d sequences checked, max abs err %.3g" % (name, T, len(idx), err), flush=True)
+    ref = oracle.decode_multi(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
+    err = check_close(out, ref, "%s T=%d" % (name, T))
+    print("full %s T=%d: all %d sequences checked, max abs err %.3g" % (name, T, w.B, err), flush=True)
 
 
 # ------------------------------------------------------ full-size workloads
 
-SAMPLES = {"tiny": None, "palm": 8, "gqa70b": 6, "ragged": 12, "long": 1}
-
-
-def sample_indices(lens: torch.Tensor, count):
-    B = lens.numel()
-    if count is None or count >= B:
-        return list(range(B))
-    order = torch.argsort(lens.cpu())
-    picks = {int(order[0]), int(order[-1]), 0, B - 1}
-    g = torch.Generator().manual_seed(1234)
-    for i in torch.randperm(B, generator=g).tolist():
-        if len(picks) >= count:
-            break
-        picks.add(i)
-    return sorted(picks)
-
-
-@pytest.mark.parametrize("name", ["tiny", "palm", "gqa70b", "ragged", "long"])
-def test_full_size_workload_sampled(name):
+@pytest.mark.parametrize("name,variant", [("tiny", None), ("palm", None), ("gqa70b", None), ("ragged", None),
+                                          ("long", None), ("tiny", "valu"), ("gqa70b", "valu"), ("ragged", "valu")])
+def test_full_size_workload(name, variant):
+    """The five workloads at their full sizes, in the launch configuration the benchmark times
+    (the planner's choice), every sequence against the oracle; the vector-ALU kernel also runs the
+    small-group workloads (G = 8 and 4) at full size."""
     w = WORKLOADS[name]
-    print("case full", name, flush=True)
+    print("case full", name, variant, flush=True)
     inp = make_inputs(w, device=DEV, poison_padding=w.ragged)
-    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], variant=variant)
     torch.cuda.synchronize()
-    idx = sample_indices(inp["seq_lens"], SAMPLES[name])
-    sel = torch.tensor(idx, device=DEV)
-    q = inp["q"].index_select(0, sel).cpu()
-    k = inp["k"].index_select(0, sel).cpu()
-    v = inp["v"].index_select(0, sel).cpu()
-    lens = inp["seq_lens"].index_select(0, sel).cpu()
-    ref = oracle.decode(q, k, v, lens, inp["scale"])
-    err = check_close(out.index_select(0, sel), ref, name)
-    print("full %s: %d sequences checked, max abs err %.3g" % (name, len(idx), err), flush=True)
-    assert torch.isfinite(out).all()
+    ref = oracle.decode(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
+    err = check_close(out, ref, "%s %s" % (name, variant))
+    print("full %s %s: all %d sequences checked, max abs err %.3g" % (name, variant, w.B, err), flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "palm", "ragged"])
+def test_plain_entry_point(name):
+    """mqa_decode_attention itself (no options): bit for bit the options form with NULL options,
+    and within the bar of the oracle on every sequence."""
+    w = WORKLOADS[name]
+    print("case plain entry point", name, flush=True)
+    inp = make_inputs(w, device=DEV, poison_padding=w.ragged)
+    lib = binding.load_library()
+    B, Hq, Hkv, D, Lmax = w.B, w.Hq, w.Hkv, w.D, w.Lmax
+    plain = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    ex = torch.empty_like(plain)
+    sp = torch.cuda.current_stream(DEV).cuda_stream
+    args = (inp["q"].data_ptr(), inp["k"].data_ptr(), inp["v"].data_ptr(), inp["seq_lens"].data_ptr())
+    st = lib.mqa_decode_attention(*args, plain.data_ptr(), B, Hq, Hkv, D, Lmax, inp["scale"], sp)
+    assert st == 0, lib.mqa_last_error()
+    st = lib.mqa_decode_attention_ex(*args, ex.data_ptr(), B, Hq, Hkv, D, Lmax, inp["scale"], sp, None)
+    assert st == 0, lib.mqa_last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(plain, ex)
+    ref = oracle.decode(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
+    check_close(plain, ref, "plain entry point %s" % name)
