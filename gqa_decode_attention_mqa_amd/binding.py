@@ -75,6 +75,9 @@ def load_library():
     lib.mqa_decode_attention_ex.argtypes = [vp, vp, vp, i32p, f32p] + ints + \
         [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
     lib.mqa_decode_attention_ex.restype = ctypes.c_int
+    lib.mqa_decode_attention_noalloc.argtypes = [vp, vp, vp, i32p, f32p] + ints + \
+        [ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
+    lib.mqa_decode_attention_noalloc.restype = ctypes.c_int
     lib.mqa_prefill_attention.argtypes = [vp, vp, vp, i32p, f32p] + ints + [ctypes.c_float, vp]
     lib.mqa_prefill_attention.restype = ctypes.c_int
     lib.mqa_decode_plan.argtypes = ints + [ctypes.c_float, ctypes.POINTER(DecodeOpts), ctypes.POINTER(PlanInfo)]

@@ -31,6 +31,19 @@ struct Workspace {
 std::mutex g_ws_mutex;
 std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
 
+// Scratch of the no-allocation entry point (mqa_decode_attention_noalloc):
+// the split partials live in this file-scope device array instead of a
+// hipMalloc'd workspace.  Each device holds its own copy at its own address.
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// the device address comes from hipGetSymbolAddress (scratch_address), and
+// only that address is handed to kernels.
+constexpr size_t kScratchBytes = (size_t)MQA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 mqa_status hip_fail(hipError_t e, const char* what) {
     mqa::set_error(std::string(what) + ": " + hipGetErrorString(e));
     return MQA_ERR_HIP;
@@ -95,9 +108,54 @@ mqa_status get_workspace(hipStream_t stream, size_t bytes, size_t ncounters, voi
     return MQA_OK;
 }
 
+// Device address of this device's `scratch`, looked up once per device with
+// that device current (the first no-allocation call on it).
+mqa_status scratch_address(void** out) {
+    *out = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) {
+        mqa::set_error("device index beyond the scratch table");
+        return MQA_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) {
+            mqa::set_error("hipGetSymbolAddress(scratch) returned NULL");
+            return MQA_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MQA_OK;
+}
+
+// Checks the no-allocation entry point adds to the plan: the separate combine
+// only (nothing in the scratch then has to start at zero) and a workspace that
+// fits the scratch.  Host only, before any HIP call.
+mqa_status check_noalloc(const Plan& plan) {
+    if (plan.combine == 2) {
+        mqa::set_error("the no-allocation entry point merges split sequences with the separate combine kernel "
+                       "only (combine = 2 is not available)");
+        return MQA_ERR_ARG;
+    }
+    if (plan.workspace_bytes > kScratchBytes) {
+        mqa::set_error("this call needs " + std::to_string(plan.workspace_bytes) +
+                       " bytes of split scratch; the no-allocation entry point holds " +
+                       std::to_string(kScratchBytes) + " (use mqa_decode_attention_ex, or larger chunks)");
+        return MQA_ERR_WORKSPACE;
+    }
+    return MQA_OK;
+}
+
 mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_lens, float* out,
                int B, int Hq, int Hkv, int D, int Lmax, float scale, void* stream_ptr,
-               const mqa_decode_opts* opts, bool causal, const mqa::PagedCache* paged = nullptr, int T = 1) {
+               const mqa_decode_opts* opts, bool causal, const mqa::PagedCache* paged = nullptr, int T = 1,
+               bool noalloc = false) {
     mqa::set_error("");
     Plan plan;
     mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, causal, &plan, T);
@@ -116,13 +174,24 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
             return MQA_ERR_ALIGN;
         }
     }
+    if (noalloc) {
+        st = check_noalloc(plan);
+        if (st != MQA_OK) return st;
+    }
     if (B == 0) return MQA_OK;
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
     void* ws = nullptr;
     uint32_t* counters = nullptr;
-    st = get_workspace(stream, plan.workspace_bytes, plan.counters, &ws, &counters);
-    if (st != MQA_OK) return st;
+    if (noalloc) {
+        if (plan.workspace_bytes > 0) {
+            st = scratch_address(&ws);
+            if (st != MQA_OK) return st;
+        }
+    } else {
+        st = get_workspace(stream, plan.workspace_bytes, plan.counters, &ws, &counters);
+        if (st != MQA_OK) return st;
+    }
 
     mqa::DecodeArgs a{};
     a.q = static_cast<const uint16_t*>(q);
@@ -204,6 +273,14 @@ mqa_status mqa_decode_attention_ex(const void* q, const void* k_cache, const voi
                                    int D, int Lmax, float scale, void* stream,
                                    const mqa_decode_opts* opts) {
     return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false);
+}
+
+mqa_status mqa_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
+                                        int D, int Lmax, float scale, void* stream,
+                                        const mqa_decode_opts* opts) {
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false, nullptr, 1,
+               true);
 }
 
 mqa_status mqa_decode_attention_window(const void* q, const void* k_cache, const void* v_cache,

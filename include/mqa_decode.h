@@ -142,6 +142,31 @@ mqa_status mqa_decode_attention_ex(const void *q, const void *k_cache, const voi
                                    const mqa_decode_opts *opts);
 
 /*
+ * mqa_decode_attention_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It never calls hipMalloc, hipFree or any allocating routine:
+ * the split-K partials live in a static device array of the library,
+ * MQA_NOALLOC_SCRATCH_BYTES bytes on each device it runs on, held until the
+ * process ends.  Arguments, semantics and results are those of
+ * mqa_decode_attention_ex (the same kernels and plan, so the same bits), with
+ * two extra checks made on the host before any HIP call:
+ *   - a call whose split workspace (mqa_plan_info.workspace_bytes) exceeds
+ *     MQA_NOALLOC_SCRATCH_BYTES is MQA_ERR_WORKSPACE (choose longer chunks, or
+ *     use mqa_decode_attention_ex);
+ *   - opts->combine == 2 (the fused merge, whose counters would have to
+ *     start at zero) is MQA_ERR_ARG; the separate merge kernel is used.
+ * Every call on a device shares that device's scratch and leaves its contents
+ * behind (nothing in it needs clearing: each call writes every partial it
+ * reads).  Calls that overlap on one device (several streams, or several host
+ * threads) race on the scratch: serialise them.
+ */
+#define MQA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+mqa_status mqa_decode_attention_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                        const int32_t *seq_lens, float *out, int B, int Hq,
+                                        int Hkv, int D, int Lmax, float scale, void *stream,
+                                        const mqa_decode_opts *opts);
+
+/*
  * Several new tokens per sequence decoded in one call (speculative
  * verification, chunked prefill: "How To Scale Your Model", Part 7
  * "Transformer Inference", passages on prefill and on speculative sampling,

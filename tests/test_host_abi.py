@@ -281,3 +281,48 @@ def test_paged_arguments_are_rejected_before_any_hip_call(kw, expect):
 
 def test_paged_empty_batch_is_a_no_op():
     assert paged_call(q=0, k=0, v=0, table=0, lens=0, out=0, B=0) == OK
+
+
+# ------------------------------------------------ the no-allocation entry point
+
+NOALLOC_SCRATCH = 32 * 1024 * 1024
+
+
+def call_noalloc(B=2, Hq=8, Hkv=2, D=128, Lmax=64, opts=None, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE)
+    p.update(ptrs)
+    return lib.mqa_decode_attention_noalloc(p["q"], p["k"], p["v"], p["lens"], p["out"], B, Hq, Hkv, D, Lmax, 0.1,
+                                            None, ctypes.byref(opts) if opts is not None else None)
+
+
+def test_noalloc_scratch_limit_matches_the_header():
+    text = binding.HEADER_PATH.read_text()
+    assert "#define MQA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)" in text
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_scratch():
+    # B=256, Hkv=8, 32 heads, D=256, 131072 positions in 128-position chunks:
+    # 256 * 8 * 1024 chunks * 4 heads * 256 * 2 bytes of partials, far beyond 32 MiB
+    opts = binding.make_opts(chunk=128)
+    need = binding.plan(256, 32, 8, 256, 131072, chunk=128)["workspace_bytes"]
+    assert need > NOALLOC_SCRATCH
+    assert call_noalloc(B=256, Hq=32, Hkv=8, D=256, Lmax=131072, opts=opts) == ERR_WORKSPACE
+    assert b"no-allocation" in lib.mqa_last_error()
+
+
+def test_noalloc_accepts_what_fits_and_checks_like_the_options_form():
+    # the five workloads' plans all fit the scratch
+    for B, Hq, Hkv, D, Lmax in ((1, 8, 1, 64, 128), (64, 48, 1, 256, 2048), (32, 64, 8, 128, 4096),
+                                (256, 32, 8, 128, 8192), (4, 48, 1, 256, 131072)):
+        assert binding.plan(B, Hq, Hkv, D, Lmax)["workspace_bytes"] <= NOALLOC_SCRATCH
+    # the same argument errors as mqa_decode_attention_ex, before any HIP call
+    assert call_noalloc(q=0) == ERR_NULL
+    assert call_noalloc(Hq=7) == ERR_SHAPE
+    assert call_noalloc(D=96) == ERR_UNSUPPORTED
+    assert call_noalloc(out=FAKE + 4) == ERR_ALIGN
+    assert call_noalloc(B=0, q=0, k=0, v=0, lens=0, out=0) == OK
+
+
+def test_noalloc_refuses_the_fused_merge():
+    assert call_noalloc(Lmax=2048, opts=binding.make_opts(chunk=128, combine=2)) == ERR_ARG
+    assert b"separate combine" in lib.mqa_last_error()
