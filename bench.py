@@ -2,23 +2,36 @@
 """Decode-attention benchmark: steps/s and achieved HBM bandwidth on one MI355X.
 
 One step = one decode step of the whole batch (split-K kernel, plus the
-combine kernel when sequences are split), inputs resident in HBM.  Default
-workload: PaLM-540B-shaped MQA decode (B=64, Hq=48, Hkv=1, D=256, len 2048).
+log-sum-exp merge kernel when sequences are split), inputs resident in HBM.
+Default workload: PaLM-540B-shaped MQA decode (B=64, Hq=48, Hkv=1, D=256,
+len 2048).
 
 To keep the memory-side Infinity Cache (256 MB) from serving repeated reads,
-the timed loop rotates through enough distinct q/K/V sets that the K/V bytes
-the steps read cover at least 768 MiB, so every step reads its K/V from HBM.
+every loop rotates through enough distinct q/K/V sets that the K/V bytes the
+steps read cover at least 768 MiB, so every step reads its K/V from HBM.
+
+Three passes, each on the library's stream:
+  1. wall clock: W warmup steps, then K timed steps launched plainly (no
+     per-kernel events), bracketed by HIP events in about 20 blocks;
+  2. kernel pass (separate, after the timed loop): start/stop events recorded
+     by the split kernel's own dispatch and by the merge kernel's own dispatch
+     on every step of a further pass, so that each step's summed kernel
+     duration is known;
+  3. ceiling: the library's streaming-read probe over 2 GiB (8192 workgroups)
+     and over the workload's own bytes and split grid.
 
 Prints ONE JSON line (rank 0, N=1):
-  value        decode steps per second over the timed steps
-  roofline     the split-K kernel's algorithmic K+V bytes per launch divided by
-               its mean duration (start/stop HIP events recorded by that
-               launch's own dispatch, on the stream it runs on, on about 100
-               evenly spaced steps of the timed region) against the 8 TB/s HBM peak;
-               `traffic` is the HBM bytes per launch measured by rocprofv3 PMC
-               counters (profiles/split_kernel_traffic_<workload>.txt) when those counters
-               were taken on the current kernel sources, else null
-  cpu_baseline the CPU fp64 oracle on the host's cores on a bounded sample
+  value        decode steps per second over the K timed steps (pass 1)
+  roofline     algorithmic K+V bytes per step divided by the mean summed
+               duration of the step's kernels (split + merge, pass 2), against
+               the 8 TB/s HBM peak; `split_only` gives the split kernel alone;
+               `traffic` is the HBM bytes per split launch measured by
+               rocprofv3 PMC counters (profiles/split_kernel_traffic_<workload>.txt)
+               when those counters were taken on the current kernel sources,
+               else null; `ceiling` the probe's rates
+  step_kernel_us  mean, p10, p50, p90 of the per-step summed kernel durations
+  cpu_baseline the CPU fp64 oracle on the host's cores on a bounded sample,
+               with the CPU model and single-thread times for tiny and palm
 """
 from __future__ import annotations
 
@@ -39,6 +52,10 @@ MALL_DEFEAT_BYTES = 768 * 2 ** 20
 MAX_SETS = 64  # tiny problems live in cache whatever the rotation
 KERNEL_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "combine.hip", "kernel_common.hpp",
                   "abi.cpp", "plan.cpp"]
+WALL_BLOCKS = 20          # event-bracketed blocks of the timed loop (p10/p90 of block means)
+CEILING_BYTES = 2 * 2 ** 30
+CEILING_WORKGROUPS = 8192
+CEILING_REPS = 20
 
 
 def kernel_sources_sha() -> str:
@@ -87,6 +104,9 @@ def parse_args(argv=None):
     ap.add_argument("--tokens", type=int, default=1,
                     help="query tokens per sequence decoded at once (causal among themselves; the cache is "
                          "read once for all of them); 1 = the decode step")
+    ap.add_argument("--kernel-steps", type=int, default=None,
+                    help="steps of the evented kernel pass (default: max(200, min(steps, 2000)))")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -103,6 +123,47 @@ def copy_probe(nbytes: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 5}))
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def single_thread_baseline(target_s: float = 4.0) -> dict:
+    """The oracle on one thread: the tiny workload's whole step, and the PaLM-shaped step
+    (whole when it fits ``target_s``, else a prefix of its sequences, scaled)."""
+    import oracle
+    from gqa_decode_attention_mqa_amd.workloads import WORKLOADS, make_inputs
+    prev = oracle.max_threads()
+    oracle.set_threads(1)
+    try:
+        res = {}
+        for name in ("tiny", "palm"):
+            w = WORKLOADS[name]
+            inp = make_inputs(w)
+            q, k, v, lens = inp["q"], inp["k"], inp["v"], inp["seq_lens"]
+            t0 = time.perf_counter()
+            oracle.decode(q[:1], k[:1], v[:1], lens[:1], inp["scale"])
+            one = max(time.perf_counter() - t0, 1e-6)
+            nseq = w.B if one * w.B <= target_s else max(1, int(target_s / one))
+            reps = max(1, int(target_s / (one * nseq))) if nseq == w.B else 1
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                oracle.decode(q[:nseq], k[:nseq], v[:nseq], lens[:nseq], inp["scale"])
+            dt = time.perf_counter() - t0
+            steps = reps * float(lens[:nseq].double().sum() / lens.double().sum())
+            res[name] = {"steps_per_s": round(steps / dt, 4), "seconds": round(dt, 3),
+                         "sample": ("%d whole step(s)" % reps) if nseq == w.B else
+                         ("first %d of %d sequences of one step, scaled by their share of positions" % (nseq, w.B))}
+        return res
+    finally:
+        oracle.set_threads(prev)
 
 
 def cpu_baseline(w, inp, target_s: float, window: int = 0, kv_format: str = "bf16", tokens: int = 1):
@@ -145,7 +206,50 @@ def cpu_baseline(w, inp, target_s: float, window: int = 0, kv_format: str = "bf1
         sample = "first %d of %d sequences of one %s decode step, scaled by their share of positions" % (
             nseq, w.B, w.name)
     return {"value": steps / dt, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": sample + "; fp64 C oracle, OpenMP over (sequence, head)", "seconds": round(dt, 3)}
+            "sample": sample + "; fp64 C oracle, OpenMP over (sequence, head)", "seconds": round(dt, 3),
+            "cpu_model": cpu_model(), "single_thread": single_thread_baseline()}
+
+
+def pct(sorted_vals, p):
+    """Nearest-rank percentile of an ascending list."""
+    if not sorted_vals:
+        return None
+    i = min(len(sorted_vals) - 1, max(0, int(math.ceil(p / 100.0 * len(sorted_vals))) - 1))
+    return sorted_vals[i]
+
+
+def stream_ceiling(binding, torch, dev, pattern_bytes: int, pattern_wgs: int) -> dict:
+    """Streaming-read rates of the library's probe: 2 GiB with 8192 workgroups, and the
+    workload's own bytes with its split grid (rotating over 128 MiB-aligned slices of the
+    2 GiB buffer so the Infinity Cache never serves a repeated read).  Medians of 20."""
+    buf = torch.empty(CEILING_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.empty(max(CEILING_WORKGROUPS, pattern_wgs), dtype=torch.int32, device=dev)
+    res = {}
+    cases = [("stream_2gib", CEILING_BYTES, CEILING_WORKGROUPS)]
+    nb = (pattern_bytes + 15) // 16 * 16
+    if 0 < nb <= CEILING_BYTES // 4:
+        cases.append(("workload_pattern", nb, pattern_wgs))
+    for name, nbytes, wgs in cases:
+        span = (nbytes + 2 ** 27 - 1) // 2 ** 27 * 2 ** 27
+        nslices = max(1, CEILING_BYTES // span)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(CEILING_REPS)]
+        for b, e in evs:
+            b.record()
+            e.record()
+        for i in range(3):
+            binding.stream_read_probe(buf[(i % nslices) * span:(i % nslices) * span + nbytes], wgs, sink)
+        torch.cuda.synchronize()
+        for i, ev in enumerate(evs):
+            off = (i % nslices) * span
+            binding.stream_read_probe(buf[off:off + nbytes], wgs, sink, events=ev)
+        torch.cuda.synchronize()
+        us = sorted(b.elapsed_time(e) * 1e3 for b, e in evs)
+        med = us[len(us) // 2]
+        res[name] = {"bytes": nbytes, "workgroups": wgs, "median_us": round(med, 3),
+                     "gbs": round(nbytes / (med * 1e-6) / 1e9, 1)}
+    del buf
+    return res
 
 
 def main(argv=None):
@@ -252,39 +356,62 @@ def main(argv=None):
         step(i, plain_sets[i % nsets])
     torch.cuda.synchronize()
 
-    # Start/stop events of the split-K kernel, recorded by its own dispatch on
-    # the library's stream, on every `stride`-th timed step (about 100 of
-    # them): an evented dispatch lengthens the gap to the next kernel by a few
-    # microseconds, so the other steps launch plainly, as a caller would.
-    stride = max(1, args.steps // 100)
-    sampled = list(range(0, args.steps, stride))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sampled]
-    for b, e in evs:  # torch creates the HIP event on first record; the library re-records it
-        b.record(stream)
-        e.record(stream)
-    opts = [plain_sets[i % nsets] for i in range(args.steps)]
-    for i, (b, e) in zip(sampled, evs):
-        opts[i] = make(i, b.cuda_event, e.cuda_event)
-    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Pass 1, wall clock: plain launches only, as a caller makes them; HIP
+    # events between blocks of steps give the loop's time and its spread.
+    nblocks = max(1, min(WALL_BLOCKS, args.steps // 10))
+    bounds = [round(j * args.steps / nblocks) for j in range(nblocks + 1)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(nblocks + 1)]
     torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        step(i, opts[i])
-    t_end.record(stream)
+    marks[0].record(stream)
+    for j in range(nblocks):
+        for i in range(bounds[j], bounds[j + 1]):
+            step(i, plain_sets[i % nsets])
+        marks[j + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    kern_ms = [b.elapsed_time(e) for b, e in evs]
-    kern_ms.sort()
-    mean_kern_ms = sum(kern_ms) / len(kern_ms)
-    median_kern_ms = kern_ms[len(kern_ms) // 2]
+    total_ms = marks[0].elapsed_time(marks[-1])
+    block_us = sorted(marks[j].elapsed_time(marks[j + 1]) * 1e3 / max(1, bounds[j + 1] - bounds[j])
+                      for j in range(nblocks))
+
+    # Pass 2, kernel durations: every step records start/stop events from the
+    # split kernel's own dispatch and from the merge kernel's own dispatch.
+    ksteps = args.kernel_steps or max(200, min(args.steps, 2000))
+    has_combine = plan["grid_combine"] > 0 and plan["combine"] == 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ksteps)]
+    for e4 in ev:  # torch creates the HIP event on first record; the library re-records it
+        for e in e4:
+            e.record(stream)
+    kopts = []
+    for i in range(ksteps):
+        o = make(i, ev[i][0].cuda_event, ev[i][1].cuda_event)
+        if has_combine:
+            o.ev_combine_begin, o.ev_combine_end = ev[i][2].cuda_event, ev[i][3].cuda_event
+        kopts.append(o)
+    torch.cuda.synchronize()
+    for i in range(ksteps):
+        step(i, kopts[i])
+    torch.cuda.synchronize()
+    split_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(ksteps)]
+    comb_us = [ev[i][2].elapsed_time(ev[i][3]) * 1e3 if has_combine else 0.0 for i in range(ksteps)]
+    step_us = sorted(a + b for a, b in zip(split_us, comb_us))
+    mean_split = sum(split_us) / ksteps
+    mean_comb = sum(comb_us) / ksteps
+    mean_step = mean_split + mean_comb
 
     ms_per_step = total_ms / args.steps
     kv_bytes = step_bytes(attended)
-    achieved = kv_bytes / (mean_kern_ms * 1e-3) / 1e9
+    achieved = kv_bytes / (mean_step * 1e-6) / 1e9
+    achieved_split = kv_bytes / (mean_split * 1e-6) / 1e9
     traffic = read_traffic(w.name + ("_paged%d" % args.page_size if args.page_size else "")
                            + ("_window%d" % args.window if args.window else "")
                            + ("_" + args.kv_format if q8 else "")
                            + ("_tokens%d" % args.tokens if args.tokens > 1 else ""))
+    ceiling = None
+    if not args.no_ceiling:
+        for s_ in sets[1:]:
+            s_.clear()
+        del sets[1:]
+        torch.cuda.empty_cache()
+        ceiling = stream_ceiling(binding, torch, dev, kv_bytes, int(plan["grid_main"]))
 
     result = {
         "metric": "decode-attention steps/sec and achieved HBM GB/s (% of MI355X peak)",
@@ -323,12 +450,20 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "split-K decode (%s)" % plan["variant"],
-            "kernel_mean_us": round(mean_kern_ms * 1e3, 3),
-            "kernel_median_us": round(median_kern_ms * 1e3, 3),
-            "kernel_samples": len(kern_ms),
-            "step_kv_gbs": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+            "kernel": "split-K decode (%s)%s" % (plan["variant"], " + log-sum-exp merge" if has_combine else ""),
+            "step_kernel_mean_us": round(mean_step, 3),
+            "split_only": {"achieved": round(achieved_split, 1), "frac": round(achieved_split / HBM_PEAK_GBS, 4),
+                           "kernel_mean_us": round(mean_split, 3)},
+            "combine_mean_us": round(mean_comb, 3) if has_combine else None,
+            "kernel_steps": ksteps,
+            "ceiling": ceiling,
+            "step_kv_gbs_wall": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         },
+        "step_kernel_us": {"mean": round(mean_step, 3), "p10": round(pct(step_us, 10), 3),
+                           "p50": round(pct(step_us, 50), 3), "p90": round(pct(step_us, 90), 3)},
+        "wall_us_per_step": {"mean": round(ms_per_step * 1e3, 3), "p10": round(pct(block_us, 10), 3),
+                             "p50": round(pct(block_us, 50), 3), "p90": round(pct(block_us, 90), 3),
+                             "blocks": nblocks},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, cpu_set, args.cpu_seconds, args.window, args.kv_format,

@@ -35,7 +35,8 @@ class DecodeOpts(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("chunk", ctypes.c_int), ("combine", ctypes.c_int),
                 ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p),
                 ("window", ctypes.c_int), ("kv_format", ctypes.c_int),
-                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("ev_combine_begin", ctypes.c_void_p), ("ev_combine_end", ctypes.c_void_p)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -91,6 +92,8 @@ def load_library():
     lib.mqa_last_error.restype = ctypes.c_char_p
     lib.mqa_release_workspaces.argtypes = []
     lib.mqa_release_workspaces.restype = None
+    lib.mqa_stream_read_probe.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp, vp, vp]
+    lib.mqa_stream_read_probe.restype = ctypes.c_int
     lib.mqa_version.argtypes = []
     lib.mqa_version.restype = ctypes.c_int
     _lib = lib
@@ -111,8 +114,10 @@ def _check(status: int, where: str):
 
 
 def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None, window=None,
-              kv_format=None, k_scale=None, v_scale=None) -> DecodeOpts:
+              kv_format=None, k_scale=None, v_scale=None, ev_combine_begin=None, ev_combine_end=None) -> DecodeOpts:
     o = DecodeOpts()
+    o.ev_combine_begin = ev_combine_begin
+    o.ev_combine_end = ev_combine_end
     o.window = int(window or 0)
     o.kv_format = KV_FORMATS[kv_format] if isinstance(kv_format, str) else int(kv_format or 0)
     o.k_scale = k_scale
@@ -386,3 +391,20 @@ def prefill(q_seq: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, s
 
 def release_workspaces():
     load_library().mqa_release_workspaces()
+
+
+def stream_read_probe(buf: torch.Tensor, workgroups: int, sink: torch.Tensor, events=None):
+    """Streaming-read calibration over all of ``buf`` (contiguous device memory) with
+    ``workgroups`` workgroups; ``sink`` int32 or uint32 [>= workgroups]; ``events`` =
+    (begin, end) torch.cuda.Event pair recorded by the kernel's own dispatch."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be contiguous device memory")
+    if sink.device != buf.device or sink.numel() < workgroups or sink.element_size() != 4:
+        raise ValueError("sink must hold at least `workgroups` 4-byte words on buf's device")
+    ev_b = ev_e = None
+    if events is not None:
+        ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
+    lib = load_library()
+    st = lib.mqa_stream_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), int(workgroups),
+                                   sink.data_ptr(), _stream_ptr(buf.device), ev_b, ev_e)
+    _check(st, "mqa_stream_read_probe")

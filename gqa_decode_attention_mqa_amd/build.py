@@ -20,7 +20,7 @@ LIB = PKG / "libmqa_decode.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "plan.cpp", "decode_mfma.hip", "decode_valu.hip", "combine.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "decode_mfma.hip", "decode_valu.hip", "combine.hip", "probe.hip"]
 COMMON = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -252,7 +252,8 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
         c.max_splits = plan.max_splits;
         c.causal = a.causal;
         c.window = a.window;
-        e = mqa::launch_combine(plan, c, stream);
+        e = mqa::launch_combine(plan, c, stream, opts ? static_cast<hipEvent_t>(opts->ev_combine_begin) : nullptr,
+                                opts ? static_cast<hipEvent_t>(opts->ev_combine_end) : nullptr);
         if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
     }
     return MQA_OK;
@@ -397,6 +398,34 @@ void mqa_release_workspaces(void) {
     g_ws.clear();
 }
 
-int mqa_version(void) { return 140; }
+mqa_status mqa_stream_read_probe(const void* buf, size_t bytes, int workgroups, uint32_t* sink, void* stream,
+                                 void* ev_begin, void* ev_end) {
+    mqa::set_error("");
+    if (bytes == 0) return MQA_OK;
+    if (!buf || !sink) {
+        mqa::set_error("buf and sink must be non-NULL");
+        return MQA_ERR_NULL;
+    }
+    if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0 || (bytes & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) {
+        mqa::set_error("buf must be 16-byte aligned, bytes a multiple of 16 and sink 4-byte aligned");
+        return MQA_ERR_ALIGN;
+    }
+    if (workgroups < 1 || workgroups > (1 << 24)) {
+        mqa::set_error("workgroups must be in [1, 2^24]");
+        return MQA_ERR_ARG;
+    }
+    if ((bytes + (size_t)workgroups - 1) / (size_t)workgroups > ((size_t)1 << 30)) {
+        mqa::set_error("each workgroup's slice must be at most 1 GiB");
+        return MQA_ERR_UNSUPPORTED;
+    }
+    const hipError_t e = mqa::launch_stream_read(buf, (long long)bytes, workgroups, sink,
+                                                 reinterpret_cast<hipStream_t>(stream),
+                                                 static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end));
+    if (e != hipSuccess) return hip_fail(e, "stream-read kernel launch");
+    return MQA_OK;
+}
+
+int mqa_version(void) { return 150; }
 
 }  // extern "C"

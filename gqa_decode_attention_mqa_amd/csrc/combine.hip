@@ -19,12 +19,6 @@
 
 namespace mqa {
 
-// Stored partial slot -> fp32: four fp16 values scaled back by 2^e.
-__device__ __forceinline__ f32x4_t unpack_partial4(u32x2_t h, int e) {
-    return f32x4_t{__builtin_amdgcn_ldexpf(f16_lo_f32(h.x), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.x), e),
-                   __builtin_amdgcn_ldexpf(f16_lo_f32(h.y), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.y), e)};
-}
-
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     __shared__ float s_max[4];
     __shared__ __attribute__((aligned(16))) f32x4_t s_acc[256];
@@ -86,31 +80,45 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 // Few chunks per sequence (at most S, the plan's chunk bound rounded up to
-// 2, 4 or 8): one thread per (query head, 8-value column slot), 2048/D heads
-// per workgroup.  Each thread issues the loads of all S chunks' {lse, e} and
-// slot at once (indices clamped to the sequence's chunks, so every load is in
-// bounds) and merges them in ascending chunk order, so the result is bitwise
+// 2, 4 or 8): one thread per (query row, 8-value column slot), 2048/D query
+// rows per workgroup, all of one unit (row, kv head).  Workgroup b runs on XCD
+// b mod 8; when the number of units is a multiple of 8 it takes a unit of the
+// same residue, the XCD on which the split kernel ran that unit's chunks
+// (map_block), so the partials it reads were written through that XCD's L2.
+// Each thread issues the loads of all S chunks' {lse, e} and slot at once
+// (indices clamped to the sequence's chunks, so every load is in bounds) and
+// merges them in ascending chunk order, so the result is bitwise
 // reproducible for a plan.
 template <int D, int S>
-__global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long long nheads) {
+__global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long long units, int blocks_per_unit) {
     constexpr int SLOTS = D / 8;
     constexpr int HPB = 256 / SLOTS;
     static_assert(S >= 2 && S <= kCombineFewMaxSplits, "chunk bound of the few-chunk combine");
     const int tid = threadIdx.x;
-    const long long gh = (long long)blockIdx.x * HPB + tid / SLOTS;  // (row * T + token) * Hq + h
-    if (gh >= nheads) return;
+    const long long bx = blockIdx.x;
+    long long unit;
+    int j;
+    if ((units & 7) == 0) {
+        const long long y = bx >> 3;
+        unit = (y / blocks_per_unit) * 8 + (bx & 7);
+        j = (int)(y % blocks_per_unit);
+    } else {
+        unit = bx / blocks_per_unit;
+        j = (int)(bx % blocks_per_unit);
+    }
+    const int g = j * HPB + tid / SLOTS;  // query row of the unit: token g / G, head kvh * G + g % G
+    if (unit >= units || g >= a.GT) return;
     const int slot = tid % SLOTS;
-    const int h = (int)(gh % a.Hq);
-    const long long rt = gh / a.Hq;
-    const long long row = rt / a.T;
-    const int tok = (int)(rt % a.T);
+    const long long row = unit / a.Hkv;
+    const int kvh = (int)(unit % a.Hkv);
+    const int tok = g / a.G;
+    const long long gh = (row * a.T + tok) * a.Hq + (long long)kvh * a.G + (g - tok * a.G);  // output row
     int b, len;
     row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
     const int nsplit = chunk_span(a.window, a.chunk, a.max_splits, len, 0).nsplit;
     if (nsplit <= 1) return;  // written directly by the split kernel
 
-    const int kvh = h / a.G, g = tok * a.G + h % a.G;
-    const size_t first = ((size_t)(row * a.Hkv + kvh) * a.max_splits) * a.GT + g;  // split 0
+    const size_t first = ((size_t)unit * a.max_splits) * a.GT + g;  // split 0
     const size_t step = (size_t)a.GT;  // partials of consecutive splits are T * G query rows apart
     f32x2_t ml[S];
     u32x4_t o[S];
@@ -120,52 +128,51 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
         ml[s] = a.part_ml[first + sc * step];
         o[s] = *reinterpret_cast<const u32x4_t*>(a.part_o + (first + sc * step) * D + 8 * slot);
     }
-    float M = ml[0].x;
-#pragma unroll
-    for (int s = 1; s < S; ++s) M = fmaxf(M, ml[s].x);
-    M = M == -INFINITY ? 0.f : M;  // no visible position in any chunk: all weights 0, zero row
-    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const float wgt = s < nsplit ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
-        const int e = (int)ml[s].y;
-        acc0 += wgt * unpack_partial4(u32x2_t{o[s].x, o[s].y}, e);
-        acc1 += wgt * unpack_partial4(u32x2_t{o[s].z, o[s].w}, e);
-        wsum += wgt;
-    }
+    f32x4_t r0, r1;
+    merge_slot<S>(ml, o, nsplit, r0, r1);
     float* dst = a.out + (size_t)gh * D + 8 * slot;
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    *reinterpret_cast<f32x4_t*>(dst) = acc0 * inv;
-    *reinterpret_cast<f32x4_t*>(dst + 4) = acc1 * inv;
+    *reinterpret_cast<f32x4_t*>(dst) = r0;
+    *reinterpret_cast<f32x4_t*>(dst + 4) = r1;
 }
+
+// Launch through hipExtLaunchKernelGGL when the caller asked for events
+// recorded by the merge's own dispatch.
+#define MQA_LAUNCH(kernel, grid, ...)                                                               \
+    do {                                                                                            \
+        if (ev0 || ev1)                                                                             \
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream, ev0, ev1, 0, __VA_ARGS__); \
+        else                                                                                        \
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, stream, __VA_ARGS__);                \
+    } while (0)
 
 template <int D>
-static void launch_few(int max_splits, unsigned grid, const CombineArgs& a, long long nheads, hipStream_t stream) {
+static void launch_few(int max_splits, const CombineArgs& a, long long units, hipStream_t stream, hipEvent_t ev0,
+                       hipEvent_t ev1) {
+    const int bpu = (a.GT + combine_heads_per_block(D) - 1) / combine_heads_per_block(D);
+    const unsigned grid = (unsigned)(units * bpu);
     if (max_splits <= 2)
-        hipLaunchKernelGGL((combine_few_kernel<D, 2>), dim3(grid), dim3(256), 0, stream, a, nheads);
+        MQA_LAUNCH((combine_few_kernel<D, 2>), grid, a, units, bpu);
     else if (max_splits <= 4)
-        hipLaunchKernelGGL((combine_few_kernel<D, 4>), dim3(grid), dim3(256), 0, stream, a, nheads);
+        MQA_LAUNCH((combine_few_kernel<D, 4>), grid, a, units, bpu);
     else
-        hipLaunchKernelGGL((combine_few_kernel<D, kCombineFewMaxSplits>), dim3(grid), dim3(256), 0, stream, a,
-                           nheads);
+        MQA_LAUNCH((combine_few_kernel<D, kCombineFewMaxSplits>), grid, a, units, bpu);
 }
 
-hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream) {
+hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (p.grid_combine <= 0) return hipSuccess;
     if (p.max_splits <= kCombineFewMaxSplits) {
-        const long long nheads = p.rows * a.T * a.Hq;
-        const unsigned grid = (unsigned)p.grid_combine;
+        const long long units = p.rows * a.Hkv;
         switch (a.D) {
-            case 64: launch_few<64>(p.max_splits, grid, a, nheads, stream); break;
-            case 128: launch_few<128>(p.max_splits, grid, a, nheads, stream); break;
-            case 256: launch_few<256>(p.max_splits, grid, a, nheads, stream); break;
+            case 64: launch_few<64>(p.max_splits, a, units, stream, ev0, ev1); break;
+            case 128: launch_few<128>(p.max_splits, a, units, stream, ev0, ev1); break;
+            case 256: launch_few<256>(p.max_splits, a, units, stream, ev0, ev1); break;
             default: return hipErrorInvalidValue;
         }
     } else {
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.grid_combine), dim3(256), 0, stream, a);
+        MQA_LAUNCH(combine_kernel, (unsigned)p.grid_combine, a);
     }
     return hipGetLastError();
 }
+#undef MQA_LAUNCH
 
 }  // namespace mqa

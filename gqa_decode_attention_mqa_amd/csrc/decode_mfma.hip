@@ -84,7 +84,6 @@ struct MfmaCfg {
     static_assert((STAGES - 2) * PER_WAVE <= 63, "loads in flight fit a wave's counter");
     static_assert(NG >= 1 && NG <= 6, "one to six 16-row tiles of query rows");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
-    static_assert(LDS_BYTES >= (2 * kFusedMaxSplits + 2) * 16 * NG * 4 + 16, "fused-combine scratch fits");
 };
 
 // LDS bank model used below: an LDS access is served 256 bytes (all 64
@@ -833,6 +832,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
             }
             const size_t part0 = ((size_t)unit * a.max_splits + s) * a.GT + g0 + 16 * w;  // this wave's first row
             uint16_t* dst = a.part_o + part0 * D;
+            // the fused merge reads these rows from another workgroup: 16-byte
+            // coherent stores (sc1) through a descriptor over the wave's rows
+            const __amdgpu_buffer_rsrc_t prs = make_rsrc(dst, 16 * D * 2);
             constexpr int LPR = D / 8;     // lanes per row, 16 bytes (8 halves) each
             constexpr int RPI = 64 / LPR;  // rows per store instruction
             const int hr = lane / LPR, c = lane % LPR;
@@ -842,7 +844,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
                 if (16 * w + h < gcnt) {
                     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ot + h * ROWH + 8 * c);
                     if (a.fused)
-                        store_coherent16(dst + (size_t)h * D + 8 * c, v);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, prs, (h * D + 8 * c) * 2, 0, kCachePolicyCoherent);
                     else
                         *reinterpret_cast<u32x4_t*>(dst + (size_t)h * D + 8 * c) = v;
                 }
@@ -861,8 +863,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     __syncthreads();
     int* flag = reinterpret_cast<int*>(smem);
     if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, flag)) return;
-    float* wts = reinterpret_cast<float*>(smem + 16);
-    fused_combine(a, unit, row, kvh, nsplit, g0, gcnt, wts, 16 * NG);
+    fused_combine(a, unit, row, kvh, nsplit, g0, gcnt);
 }
 
 template <int D, int NG, int FMT>

@@ -71,7 +71,6 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float mrg_o[NW][GB][D];
     __shared__ int s_flag;
     __shared__ unsigned s_amax[GB];  // per head: largest |output| (fp32 bits) of a partial row
-    static_assert(NW * D >= 2 * kFusedMaxSplits + 2, "fused-combine scratch fits in mrg_o");
     static_assert(D % 64 == 0, "a wave of the merge covers one head row");
 
     const int tid = threadIdx.x;
@@ -376,7 +375,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     if (direct || !a.fused) return;
     // Fused combine: the last chunk of this (row, kv head, head block) merges all partials.
     if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, &s_flag)) return;
-    fused_combine(a, unit, row, kvh, nsplit, g0, gcnt, &mrg_o[0][0][0], GB);
+    fused_combine(a, unit, row, kvh, nsplit, g0, gcnt);
 }
 
 template <int D, int GB, int FMT>

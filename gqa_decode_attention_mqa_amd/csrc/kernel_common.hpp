@@ -322,70 +322,127 @@ __device__ __forceinline__ u32x4_t widen8(u32x2_t c) {
     }
 }
 
-// Device-coherent stores and loads for the fused combine's partials: relaxed
-// atomics at agent scope, which gfx950 issues with the device-scope cache bit,
-// so a store writes through the XCD's L2 and a load reads past it.  With them
-// the partials need no L2 write-back or invalidate around the arrival counter
-// (both of which act on a whole XCD's L2).
+// Device-coherent stores and loads for the fused combine's partials: the
+// sc1 cache bit, the one gfx950 puts on relaxed agent-scope atomic accesses
+// (a store writes through the XCD's L2, a load reads past it).  With it the
+// partials need no L2 write-back or invalidate around the arrival counter
+// (both of which act on a whole XCD's L2), and 16-byte accesses stay whole.
+constexpr int kCachePolicyCoherent = 16;  // sc1
 template <typename T>
 __device__ __forceinline__ void store_coherent(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_coherent16(void* p, const u32x4_t& v) {
-    uint64_t* q = reinterpret_cast<uint64_t*>(p);
-    store_coherent(q, (uint64_t)v.x | ((uint64_t)v.y << 32));
-    store_coherent(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32));
-}
 __device__ __forceinline__ void store_coherent8(void* p, const f32x2_t& v) {
     store_coherent(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v));
 }
-__device__ __forceinline__ uint64_t load_coherent8(const void* p) {
-    return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// Stored partial slot -> fp32: four fp16 values scaled back by 2^e.
+__device__ __forceinline__ f32x4_t unpack_partial4(u32x2_t h, int e) {
+    return f32x4_t{__builtin_amdgcn_ldexpf(f16_lo_f32(h.x), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.x), e),
+                   __builtin_amdgcn_ldexpf(f16_lo_f32(h.y), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.y), e)};
 }
 
-// Fused log-sum-exp combine, run by the last chunk of a unit to arrive.  The
-// caller has already written its own partial.  Returns after every thread of
-// the workgroup has finished (it contains barriers: call it from all threads).
-//   wts: LDS scratch of 2 * kFusedMaxSplits * gp + 2 * gp floats, gp >= gcnt.
+// Log-sum-exp merge of one 8-value column slot of one query row over S chunk
+// partials: ml[s] = {lse_s (base 2), e_s}, o[s] = eight fp16 values of O_s
+// scaled by 2^-e_s.  Chunks s >= nsplit carry weight 0 (callers fill them with
+// copies of a real chunk, so the maximum is unchanged and every term stays
+// finite).  With M = max_s lse_s:
+//     out = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M),
+// summed in ascending s.  A query row with no visible position in any chunk
+// (every lse = -inf) gets weight 0 everywhere and a zero row.  Both merge forms
+// (the separate kernel and the fused one) call this, so they give the same bits.
+template <int S>
+__device__ __forceinline__ void merge_slot(const f32x2_t (&ml)[S], const u32x4_t (&o)[S], int nsplit, f32x4_t& r0,
+                                           f32x4_t& r1) {
+    float M = ml[0].x;
+#pragma unroll
+    for (int s = 1; s < S; ++s) M = fmaxf(M, ml[s].x);
+    M = M == -INFINITY ? 0.f : M;
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const float wgt = s < nsplit ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
+        const int e = (int)ml[s].y;
+        acc0 += wgt * unpack_partial4(u32x2_t{o[s].x, o[s].y}, e);
+        acc1 += wgt * unpack_partial4(u32x2_t{o[s].z, o[s].w}, e);
+        wsum += wgt;
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    r0 = acc0 * inv;
+    r1 = acc1 * inv;
+}
+
+// A batch of the fused merge: this thread's items idx0, idx0 + stride, ...
+// (IT of them; an item is one (query row, 8-value slot) of the unit's query
+// rows g0 ..), with the S chunks' {lse, e} and 16-byte slots of every item
+// loaded coherently before any is merged, so the batch costs one round trip.
+// Loads of chunks past nsplit repeat the last chunk and loads of items past
+// the end repeat the last item (both stay in range); merge_slot then gives
+// those chunks weight 0, and items past the end are not stored.  ro / rm cover
+// the unit's partial rows and {lse, e} pairs (split-major, GT rows per split).
+template <int S, int IT>
+__device__ __forceinline__ void fused_merge_batch(const DecodeArgs& a, __amdgpu_buffer_rsrc_t ro,
+                                                  __amdgpu_buffer_rsrc_t rm, long long row, int kvh, int g0,
+                                                  int items, int idx0, int stride, int nsplit) {
+    const int D = a.D, slots = D / 8;
+    f32x2_t ml[IT][S];
+    u32x4_t o[IT][S];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = min(idx0 + it * stride, items - 1);
+        const int g = g0 + idx / slots, slot = idx % slots;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int sc = s < nsplit ? s : nsplit - 1;
+            ml[it][s] = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rm, (sc * a.GT + g) * 8, 0,
+                                                                                          kCachePolicyCoherent));
+            o[it][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        ro, ((sc * a.GT + g) * D + 8 * slot) * 2, 0, kCachePolicyCoherent));
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = idx0 + it * stride;
+        if (idx < items) {
+            const int g = g0 + idx / slots, slot = idx % slots;
+            f32x4_t r0, r1;
+            merge_slot<S>(ml[it], o[it], nsplit, r0, r1);
+            float* dst = a.out + qrow_offset(row, a.T, a.Hq, a.G, D, kvh, g) + 8 * slot;
+            *reinterpret_cast<f32x4_t*>(dst) = r0;
+            *reinterpret_cast<f32x4_t*>(dst + 4) = r1;
+        }
+    }
+}
+
+template <int S, int IT>
+__device__ __forceinline__ void fused_merge_all(const DecodeArgs& a, __amdgpu_buffer_rsrc_t ro,
+                                                __amdgpu_buffer_rsrc_t rm, long long row, int kvh, int g0, int items,
+                                                int nsplit) {
+    const int stride = blockDim.x;
+    for (int idx0 = threadIdx.x; idx0 < items; idx0 += IT * stride)
+        fused_merge_batch<S, IT>(a, ro, rm, row, kvh, g0, items, idx0, stride, nsplit);
+}
+
+// Fused log-sum-exp merge, run by the last chunk of a unit to arrive, over the
+// query rows g0 .. g0 + gcnt - 1 of the unit: every thread of the workgroup
+// takes (query row, 8-value slot) items, a batch of them at a time (about 144
+// registers of loads in flight per thread).  The caller has written its own
+// partial with coherent stores; the planner keeps nsplit <= 8 and the unit's
+// partials within a 2 GiB buffer range for this form.
 __device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long unit, long long row, int kvh,
-                                              int nsplit, int g0, int gcnt, float* wts, int gp) {
-    const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
-    float* Mg = wts + kFusedMaxSplits * gp;
-    float* Wg = Mg + gp;
-    const size_t base = (size_t)unit * a.max_splits * a.GT;  // partial (unit, split 0, query row 0)
-    int* ex = reinterpret_cast<int*>(Wg + gp);  // kFusedMaxSplits * gp scale exponents
-    if (tid < gcnt) {
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s)
-            M = fmaxf(M, __builtin_bit_cast(f32x2_t, load_coherent8(a.part_ml + base + (size_t)s * a.GT + g0 + tid)).x);
-        M = M == -INFINITY ? 0.f : M;  // a query row that sees no position: zero row
-        float W = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const f32x2_t ml = __builtin_bit_cast(f32x2_t, load_coherent8(a.part_ml + base + (size_t)s * a.GT + g0 + tid));
-            const float w = __builtin_amdgcn_exp2f(ml.x - M);
-            wts[s * gp + tid] = w;
-            ex[s * gp + tid] = (int)ml.y;
-            W += w;
-        }
-        Mg[tid] = M;
-        Wg[tid] = W > 0.f ? 1.f / W : 0.f;
-    }
-    __syncthreads();
+                                              int nsplit, int g0, int gcnt) {
     const int D = a.D;
-    const int slots = gcnt * (D / 4);
-    for (int idx = tid; idx < slots; idx += nthreads) {
-        const int g = idx / (D / 4), d4 = idx % (D / 4);
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < nsplit; ++s) {
-            const u32x2_t h = __builtin_bit_cast(u32x2_t, load_coherent8(a.part_o + (base + (size_t)s * a.GT + g0 + g) * D + 4 * d4));
-            const int e = ex[s * gp + g];
-            const f32x4_t o = {__builtin_amdgcn_ldexpf(f16_lo_f32(h.x), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.x), e),
-                               __builtin_amdgcn_ldexpf(f16_lo_f32(h.y), e), __builtin_amdgcn_ldexpf(f16_hi_f32(h.y), e)};
-            acc += wts[s * gp + g] * o;
-        }
-        *reinterpret_cast<f32x4_t*>(a.out + qrow_offset(row, a.T, a.Hq, a.G, D, kvh, g0 + g) + 4 * d4) = acc * Wg[g];
-    }
+    const size_t first = (size_t)unit * a.max_splits * a.GT;  // (unit, split 0, query row 0)
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o + first * D, a.max_splits * a.GT * D * 2);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.part_ml + first, a.max_splits * a.GT * 8);
+    const int items = gcnt * (D / 8);
+    if (nsplit <= 2)
+        fused_merge_all<2, 8>(a, ro, rm, row, kvh, g0, items, nsplit);
+    else if (nsplit <= 4)
+        fused_merge_all<4, 6>(a, ro, rm, row, kvh, g0, items, nsplit);
+    else
+        fused_merge_all<kFusedMaxSplits, 3>(a, ro, rm, row, kvh, g0, items, nsplit);
 }
 
 // Arrival bookkeeping of the fused combine: returns true in every thread of

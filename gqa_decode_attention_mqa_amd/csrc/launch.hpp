@@ -17,7 +17,14 @@ hipError_t launch_decode_mfma(const Plan& p, const DecodeArgs& a, hipStream_t st
 // Split-K kernel on the vector ALU (groups of up to 8 heads per workgroup).
 hipError_t launch_decode_valu(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                               hipEvent_t ev1);
-// Log-sum-exp merge of the per-chunk partials of split sequences.
-hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream);
+// Log-sum-exp merge of the per-chunk partials of split sequences; ev0/ev1 as
+// above, recorded around the merge kernel.
+hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream, hipEvent_t ev0 = nullptr,
+                          hipEvent_t ev1 = nullptr);
+// Streaming-read calibration: `workgroups` workgroups each read one
+// contiguous slice of `bytes` bytes (a multiple of 16) and write one word to
+// sink[workgroup].
+hipError_t launch_stream_read(const void* buf, long long bytes, int workgroups, uint32_t* sink, hipStream_t stream,
+                              hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace mqa

@@ -174,8 +174,12 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (grid limit)");
 
     if (p.max_splits > 1 && p.rows > 0) {
-        if (o.combine == 2 && p.max_splits > kFusedMaxSplits)
-            return fail(MQA_ERR_ARG, "the fused combine handles at most 16 chunks per sequence");
+        // the fused merge addresses a unit's partials through one 32-bit buffer range
+        const bool fusable = p.max_splits <= kFusedMaxSplits &&
+                             (long long)p.max_splits * p.GT * D * 2 <= 0x7FFFFFFFLL;
+        if (o.combine == 2 && !fusable)
+            return fail(MQA_ERR_ARG, "the fused combine handles at most 8 chunks per sequence "
+                                     "(and max_splits * T * G * D * 2 < 2^31)");
         // Default: the separate combine kernel.  In the fused form the last
         // workgroup of each unit merges the partials at the tail of the split
         // kernel, which measured slower on MI355X (PaLM-shaped MQA step
@@ -183,8 +187,8 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         p.combine = (o.combine == 0) ? 1 : o.combine;
         if (p.combine != 1)
             p.grid_combine = 0;
-        else if (p.max_splits <= kCombineFewMaxSplits)
-            p.grid_combine = ceil_div(p.rows * T * Hq, combine_heads_per_block(D));
+        else if (p.max_splits <= kCombineFewMaxSplits)  // whole head blocks of each unit
+            p.grid_combine = p.rows * Hkv * ceil_div(p.GT, combine_heads_per_block(D));
         else
             p.grid_combine = p.rows * T * Hq;
         if (p.grid_combine > kMaxGrid)

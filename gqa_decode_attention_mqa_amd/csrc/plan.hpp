@@ -39,12 +39,13 @@ constexpr int kMfmaMaxHeads = 96;
 // Most query heads one VALU workgroup serves (bf16 cache; 8-bit caches).
 constexpr int kValuMaxHeads = 8;
 constexpr int kValuMaxHeads8 = 4;
-// Most chunks per unit the fused combine handles (its weights live in LDS).
-constexpr int kFusedMaxSplits = 16;
 // Up to this many chunks per sequence the combine kernel keeps every chunk of
 // a column slot in registers (one thread per (query head, 16-byte slot));
 // beyond it, threads of a workgroup split the chunks of one head.
 constexpr int kCombineFewMaxSplits = 8;
+// Most chunks per unit the fused combine handles: the same register-resident
+// merge of every chunk's slot as the few-chunk kernel.
+constexpr int kFusedMaxSplits = kCombineFewMaxSplits;
 // Query heads per workgroup of the few-chunk combine (256 threads, D/8 each).
 constexpr int combine_heads_per_block(int D) { return 2048 / D; }
 

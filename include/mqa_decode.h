@@ -93,7 +93,8 @@ typedef struct mqa_decode_opts {
                              1 = separate combine kernel,
                              2 = combine fused into the split kernel: the last chunk of
                              each (sequence, kv head) to finish merges the partials
-                             (at most 16 chunks per sequence, else MQA_ERR_ARG)          */
+                             (at most 8 chunks per sequence, else MQA_ERR_ARG); both
+                             merges give the same bits                                   */
     void *ev_main_begin;  /* optional hipEvent_t pair recorded by the split-K kernel's own
                              dispatch (hipExtLaunchKernelGGL) at its start and end, so  */
     void *ev_main_end;    /* their interval is that kernel's execution time alone      */
@@ -104,6 +105,8 @@ typedef struct mqa_decode_opts {
     int kv_format;        /* mqa_kv_format of k/v (see mqa_decode_attention_quant)         */
     const float *k_scale; /* 8-bit formats: the caches' per-row scales (device memory,     */
     const float *v_scale; /* 4-byte aligned); ignored for MQA_KV_BF16                      */
+    void *ev_combine_begin; /* optional hipEvent_t pair recorded by the log-sum-exp merge   */
+    void *ev_combine_end;   /* kernel's own dispatch (only when a merge kernel runs)      */
 } mqa_decode_opts;
 
 /* What the planner decided for a shape (host-only query, no HIP call). */
@@ -307,6 +310,26 @@ const char *mqa_last_error(void);
 /* Frees every cached split-K workspace.  Must not race with calls in flight:
  * synchronise the streams that used the library first. */
 void mqa_release_workspaces(void);
+
+/*
+ * Calibration: the read rate of a pure streaming read on this device, the
+ * ceiling the decode kernels are read against (decode attention is bound by
+ * streaming the cache from HBM: "How To Scale Your Model", Part 7 "Transformer
+ * Inference", the passage on the arithmetic intensity of attention).
+ * `workgroups` workgroups of 256 threads each read one contiguous slice of
+ * ceil(bytes / workgroups) bytes (rounded up to 16) of `buf` with 16-byte
+ * non-temporal loads (the cache policy of the K/V tiles) and write one
+ * word to sink[w]; no other memory is written.
+ *   buf        device memory, 16-byte aligned; bytes a multiple of 16
+ *   sink       uint32 [number of slices] (at most `workgroups`), device memory
+ *   ev_begin, ev_end  optional hipEvent_t pair recorded by the kernel's own
+ *              dispatch, so their interval is its execution time alone
+ * bytes == 0 is a no-op.  NULL pointers are MQA_ERR_NULL, misalignment
+ * MQA_ERR_ALIGN, workgroups outside [1, 2^24] MQA_ERR_ARG, a slice above
+ * 1 GiB MQA_ERR_UNSUPPORTED, all checked before any HIP call.
+ */
+mqa_status mqa_stream_read_probe(const void *buf, size_t bytes, int workgroups, uint32_t *sink, void *stream,
+                                 void *ev_begin, void *ev_end);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int mqa_version(void);

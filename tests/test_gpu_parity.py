@@ -124,7 +124,8 @@ def test_many_chunks_and_shape_changes_reuse_the_workspace(combine):
     for w in cases:
         for variant in ("mfma", "valu"):
             print("case ws", w.name, combine, variant, flush=True)
-            run_case(w, variant=variant, chunk=128, combine=combine)
+            # the fused merge takes at most 8 chunks per sequence
+            run_case(w, variant=variant, chunk=128 if combine == "separate" else 256, combine=combine)
 
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
@@ -142,10 +143,25 @@ def test_fused_combine_reads_this_calls_partials(variant):
     for it in range(12):
         dev, ref = cases[it % 2]
         print("case fused alternate", variant, it, flush=True)
-        out = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant, chunk=128,
+        out = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant, chunk=256,
                              combine="fused")
         torch.cuda.synchronize()
         check_close(out, ref, "fused alternate %s iteration %d" % (variant, it))
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+@pytest.mark.parametrize("chunk", [None, 128, 256])
+def test_fused_and_separate_merges_give_the_same_bits(variant, chunk):
+    """Both merge forms run the same arithmetic over the same partials in the same order."""
+    w = Workload("fz-eq", B=6, Hq=48, Hkv=1, D=256, Lmax=1000, seed=1210, len_lo=0, len_hi=1000)
+    dev = to_dev(make_inputs(w, poison_padding=True))
+    print("case fused == separate", variant, chunk, flush=True)
+    a = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant, chunk=chunk,
+                       combine="separate")
+    b = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant, chunk=chunk,
+                       combine="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])

@@ -63,10 +63,11 @@ def test_invalid_options_are_rejected(opts, expect):
 
 
 def test_fused_combine_is_refused_beyond_its_split_limit():
-    # 100000 positions in chunks of 128 -> 782 chunks > 16
+    # 100000 positions in chunks of 128 -> 782 chunks > 8
     assert call(Lmax=100000, opts=binding.make_opts(chunk=128, combine=2)) == ERR_ARG
+    assert call(Lmax=1025, opts=binding.make_opts(chunk=128, combine=2)) == ERR_ARG  # 9 chunks
     assert binding.plan(2, 8, 2, 128, 100000, chunk=128)["combine"] == 1
-    assert binding.plan(2, 8, 2, 128, 2048, chunk=128, combine="fused")["combine"] == 2
+    assert binding.plan(2, 8, 2, 128, 1024, chunk=128, combine="fused")["combine"] == 2
 
 
 def test_empty_batch_is_a_no_op_even_with_null_pointers():
@@ -98,7 +99,7 @@ def test_plan_invariants(B, Hq, Hkv, D, Lmax):
     if p["max_splits"] > 1:
         assert p["combine"] == 1
         if p["max_splits"] <= 8:   # few chunks: one thread per (head, 8 columns), 2048/D heads per block
-            assert p["grid_combine"] == -(-B * Hq // (2048 // D))
+            assert p["grid_combine"] == B * Hkv * -(-G // (2048 // D))  # whole head blocks per unit
         else:                      # many chunks: one workgroup per (row, head)
             assert p["grid_combine"] == B * Hq
         # fp16 partial rows plus an {lse, exponent} float pair per (chunk, head)
@@ -252,7 +253,7 @@ def test_multi_plan_fills_tiles_with_tokens():
     assert binding.plan(64, 48, 1, 256, 2048, tokens=3)["head_blocks"] == 2
     # the combine covers every (row, token, head)
     p = binding.plan(8, 16, 2, 128, 4096, tokens=3, chunk=512)
-    assert p["grid_combine"] == -(-8 * 3 * 16 // (2048 // 128))
+    assert p["grid_combine"] == 8 * 2 * -(-3 * 8 // (2048 // 128))  # per unit: T * G = 24 query rows
     assert p["workspace_bytes"] >= 8 * 2 * p["max_splits"] * 24 * (2 * 128 + 8)
 
 
@@ -324,5 +325,24 @@ def test_noalloc_accepts_what_fits_and_checks_like_the_options_form():
 
 
 def test_noalloc_refuses_the_fused_merge():
-    assert call_noalloc(Lmax=2048, opts=binding.make_opts(chunk=128, combine=2)) == ERR_ARG
+    assert call_noalloc(Lmax=1024, opts=binding.make_opts(chunk=128, combine=2)) == ERR_ARG
     assert b"separate combine" in lib.mqa_last_error()
+
+
+# ------------------------------------------------ the streaming-read probe (calibration)
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, 1 << 20, 256, FAKE), ERR_NULL), ((FAKE, 1 << 20, 256, 0), ERR_NULL),
+    ((FAKE + 8, 1 << 20, 256, FAKE), ERR_ALIGN), ((FAKE, (1 << 20) + 4, 256, FAKE), ERR_ALIGN),
+    ((FAKE, 1 << 20, 256, FAKE + 2), ERR_ALIGN),
+    ((FAKE, 1 << 20, 0, FAKE), ERR_ARG), ((FAKE, 1 << 20, (1 << 24) + 1, FAKE), ERR_ARG),
+    ((FAKE, 4 << 30, 2, FAKE), ERR_UNSUPPORTED),
+])
+def test_stream_read_probe_checks_its_arguments(args, expect):
+    buf, nbytes, wgs, sink = args
+    assert lib.mqa_stream_read_probe(buf, nbytes, wgs, sink, None, None, None) == expect
+    assert lib.mqa_last_error()
+
+
+def test_stream_read_probe_of_nothing_is_a_no_op():
+    assert lib.mqa_stream_read_probe(0, 0, 1, 0, None, None, None) == OK
