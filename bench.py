@@ -104,6 +104,11 @@ def parse_args(argv=None):
     ap.add_argument("--tokens", type=int, default=1,
                     help="query tokens per sequence decoded at once (causal among themselves; the cache is "
                          "read once for all of them); 1 = the decode step")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time causal prefill (mqa_prefill_attention: every position of every sequence, no cache) "
+                         "of the workload's shapes instead of the decode step; roofline against the bf16 "
+                         "matrix-core peak")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch size B")
     ap.add_argument("--kernel-steps", type=int, default=None,
                     help="steps of the evented kernel pass (default: max(200, min(steps, 2000)))")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
@@ -252,6 +257,77 @@ def stream_ceiling(binding, torch, dev, pattern_bytes: int, pattern_wgs: int) ->
     return res
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(lens, Hq, D) -> float:
+    """Algorithmic flops of causal attention: position t of a sequence takes 2 * Hq * D flops for
+    q.k and as many for p.v at each of its t + 1 attended positions."""
+    return float(sum(4.0 * Hq * D * n * (n + 1) / 2 for n in lens))
+
+
+def run_prefill(args, w, torch, binding):
+    """Causal prefill of the workload's batch: one step = one mqa_prefill_attention call."""
+    from gqa_decode_attention_mqa_amd.workloads import make_prefill_inputs
+    dev = torch.device("cuda:0")
+    inp = make_prefill_inputs(w, device=dev)
+    plan = binding.prefill_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale)
+    out = torch.empty((w.B, w.Lmax, w.Hq, w.D), dtype=torch.float32, device=dev)
+    lens = inp["seq_lens"].cpu().tolist()
+    flops = prefill_flops(lens, w.Hq, w.D)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.prefill(inp["q_seq"], inp["k"], inp["v"], inp["seq_lens"], w.scale, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record(stream)
+    for i in range(args.steps):
+        step()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(marks[i].elapsed_time(marks[i + 1]) * 1e3 for i in range(args.steps))
+    total_ms = marks[0].elapsed_time(marks[-1])
+    ms_per_step = total_ms / args.steps
+    achieved = flops / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": "causal prefill steps/sec and achieved TFLOP/s (% of MI355X bf16 matrix-core peak)",
+        "value": round(1000.0 / ms_per_step, 3), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "causal prefill of " + w.description + (" (B=%d)" % w.B),
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "Lmax": w.Lmax, "tokens": int(sum(lens)),
+                   "flops_per_step": flops, "plan": plan},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "blocked causal prefill (mfma, %d positions per block)" % plan["tokens"],
+                     "step_us_p10_p50_p90": [round(pct(per, p), 2) for p in (10, 50, 90)]},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        # the oracle's causal attention on a prefix of sequence 0, sized to about cpu_seconds,
+        # scaled by the flops of the prefix against the whole step
+        L = min(w.Lmax, 64)
+        while True:
+            q, k, v = inp["q_seq"][:1, :L].cpu(), inp["k"][:1, :L].cpu(), inp["v"][:1, :L].cpu()
+            t0 = time.perf_counter()
+            oracle.causal_prefill(q, k, v, [L], w.scale)
+            dt = time.perf_counter() - t0
+            if dt * 4 > args.cpu_seconds or L >= min(w.Lmax, lens[0]):
+                break
+            L = min(w.Lmax, lens[0], 2 * L)
+        sub = prefill_flops([L], w.Hq, w.D)
+        result["cpu_baseline"] = {"value": (sub / flops) / dt, "unit": "steps/s", "cores": oracle.max_threads(),
+                                  "kind": "oracle", "seconds": round(dt, 3), "cpu_model": cpu_model(),
+                                  "sample": "positions 0..%d of sequence 0 (causal prefill, fp64 C oracle), scaled "
+                                            "by its share of the step's flops" % (L - 1)}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -270,6 +346,10 @@ def main(argv=None):
                                                         page_contiguous_cache, page_quant_cache, quantize_cache)
 
     w = WORKLOADS[args.workload]
+    if args.batch:
+        w = w.with_(B=args.batch)
+    if args.prefill:
+        return run_prefill(args, w, torch, binding)
     if args.tokens > 1 and (args.page_size or args.window or args.kv_format != "bf16"):
         print("bench.py: --tokens > 1 is timed on the contiguous bf16 cache only", file=sys.stderr)
         return 2

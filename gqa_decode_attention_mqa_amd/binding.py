@@ -86,6 +86,9 @@ def load_library():
     lib.mqa_decode_plan_multi.argtypes = [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.POINTER(DecodeOpts),
                                                               ctypes.POINTER(PlanInfo)]
     lib.mqa_decode_plan_multi.restype = ctypes.c_int
+    lib.mqa_prefill_plan.argtypes = [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.POINTER(PlanInfo),
+                                                          ctypes.POINTER(ctypes.c_int)]
+    lib.mqa_prefill_plan.restype = ctypes.c_int
     lib.mqa_status_string.argtypes = [ctypes.c_int]
     lib.mqa_status_string.restype = ctypes.c_char_p
     lib.mqa_last_error.argtypes = []
@@ -144,6 +147,21 @@ def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None
             "max_splits": info.max_splits, "combine": info.combine, "head_blocks": info.head_blocks,
             "grid_main": info.grid_main, "block_main": info.block_main,
             "grid_combine": info.grid_combine, "workspace_bytes": info.workspace_bytes}
+
+
+def prefill_plan(B, Hq, Hkv, D, Lmax, scale=None) -> dict:
+    """The library's launch plan for a mqa_prefill_attention call (host only); ``tokens``
+    is the number of query positions per block."""
+    lib = load_library()
+    info = PlanInfo()
+    tokens = ctypes.c_int(0)
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.mqa_prefill_plan(B, Hq, Hkv, D, Lmax, sc, ctypes.byref(info), ctypes.byref(tokens)),
+           "mqa_prefill_plan")
+    return {"variant": VARIANT_NAMES.get(info.variant, info.variant), "chunk": info.chunk,
+            "max_splits": info.max_splits, "combine": info.combine, "head_blocks": info.head_blocks,
+            "grid_main": info.grid_main, "block_main": info.block_main,
+            "grid_combine": info.grid_combine, "workspace_bytes": info.workspace_bytes, "tokens": tokens.value}
 
 
 def _stream_ptr(device) -> int:

@@ -154,7 +154,7 @@ mqa_status check_noalloc(const Plan& plan) {
 
 mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_lens, float* out,
                int B, int Hq, int Hkv, int D, int Lmax, float scale, void* stream_ptr,
-               const mqa_decode_opts* opts, bool causal, const mqa::PagedCache* paged = nullptr, int T = 1,
+               const mqa_decode_opts* opts, int causal, const mqa::PagedCache* paged = nullptr, int T = 1,
                bool noalloc = false) {
     mqa::set_error("");
     Plan plan;
@@ -223,7 +223,9 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.GT = plan.GT;
     a.chunk = plan.chunk;
     a.max_splits = plan.max_splits;
-    a.causal = causal ? 1 : 0;
+    a.causal = causal;
+    a.B = B;
+    a.nblk = plan.nblk;
     a.window = plan.window;
     a.qk_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
@@ -266,21 +268,21 @@ extern "C" {
 mqa_status mqa_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
                                 int D, int Lmax, float scale, void* stream) {
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, nullptr, false);
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, nullptr, 0);
 }
 
 mqa_status mqa_decode_attention_ex(const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
                                    int D, int Lmax, float scale, void* stream,
                                    const mqa_decode_opts* opts) {
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false);
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, 0);
 }
 
 mqa_status mqa_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
                                         const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
                                         int D, int Lmax, float scale, void* stream,
                                         const mqa_decode_opts* opts) {
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false, nullptr, 1,
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, 0, nullptr, 1,
                true);
 }
 
@@ -293,7 +295,7 @@ mqa_status mqa_decode_attention_window(const void* q, const void* k_cache, const
     }
     mqa_decode_opts o{};
     o.window = window;
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, false);
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, 0);
 }
 
 mqa_status mqa_decode_attention_quant(const void* q, const void* k_codes, const void* v_codes,
@@ -309,13 +311,13 @@ mqa_status mqa_decode_attention_quant(const void* q, const void* k_codes, const 
     o.kv_format = kv_format;
     o.k_scale = k_scale;
     o.v_scale = v_scale;
-    return run(q, k_codes, v_codes, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, false);
+    return run(q, k_codes, v_codes, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, 0);
 }
 
 mqa_status mqa_decode_attention_multi(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* seq_lens, float* out, int B, int T, int Hq, int Hkv,
                                       int D, int Lmax, float scale, void* stream, const mqa_decode_opts* opts) {
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false, nullptr, T);
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, 0, nullptr, T);
 }
 
 mqa_status mqa_decode_attention_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -328,14 +330,35 @@ mqa_status mqa_decode_attention_paged(const void* q, const void* k_pages, const 
     int Lmax = 0;
     const mqa_status st = mqa::check_paged(B, block_table, num_pages, page_size, max_blocks, &pc, &Lmax);
     if (st != MQA_OK) return st;
-    return run(q, k_pages, v_pages, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, false, &pc);
+    return run(q, k_pages, v_pages, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, 0, &pc);
 }
 
 mqa_status mqa_prefill_attention(const void* q_seq, const void* k_cache, const void* v_cache,
                                  const int32_t* seq_lens, float* out_seq, int B, int Hq, int Hkv,
                                  int D, int Lmax, float scale, void* stream) {
     return run(q_seq, k_cache, v_cache, seq_lens, out_seq, B, Hq, Hkv, D, Lmax, scale, stream,
-               nullptr, true);
+               nullptr, mqa::kCausalBlocked);
+}
+
+mqa_status mqa_prefill_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale, mqa_plan_info* info,
+                            int* tokens_per_block) {
+    mqa::set_error("");
+    Plan p;
+    const mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, nullptr, mqa::kCausalBlocked, &p);
+    if (st != MQA_OK) return st;
+    if (info) {
+        info->variant = p.variant;
+        info->chunk = p.chunk;
+        info->max_splits = p.max_splits;
+        info->combine = p.combine;
+        info->head_blocks = p.head_blocks;
+        info->grid_main = p.grid_main * p.head_blocks;
+        info->block_main = p.block_main;
+        info->grid_combine = p.grid_combine;
+        info->workspace_bytes = p.workspace_bytes;
+    }
+    if (tokens_per_block) *tokens_per_block = p.T;
+    return MQA_OK;
 }
 
 mqa_status mqa_decode_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
@@ -347,7 +370,7 @@ mqa_status mqa_decode_plan_multi(int B, int T, int Hq, int Hkv, int D, int Lmax,
                                  const mqa_decode_opts* opts, mqa_plan_info* info) {
     mqa::set_error("");
     Plan p;
-    const mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, false, &p, T);
+    const mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, 0, &p, T);
     if (st != MQA_OK) return st;
     if (info) {
         info->variant = p.variant;

@@ -232,10 +232,14 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     const int g0 = blockIdx.y * 16 * NG;
     const int gcnt = min(16 * NG, a.GT - g0);  // query rows (token, head) of this block
 
-    int b, len;
-    row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
+    int b, len, qbase;
+    row_extent(a, row, &b, &len, &qbase);
     b = __builtin_amdgcn_readfirstlane(b);
     len = __builtin_amdgcn_readfirstlane(len);
+    qbase = __builtin_amdgcn_readfirstlane(qbase);
+    // query rows of the unit that exist in q and out (all T * G but in the
+    // last block of a blocked causal row)
+    const int gq = row_tokens(a, row) * a.G;
     const ChunkSpan span = chunk_span(a.window, a.chunk, a.max_splits, len, s);
     if (s > 0 && span.p0 >= len) return;  // whole workgroup: this chunk is past the end
     // Sliding window: rows lo - 32 < t < lo of the first tile lie before it;
@@ -266,10 +270,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
     } else if constexpr (C::F8MMA) {
-        const size_t q0 = qrow_offset(row, a.T, a.Hq, a.G, D, kvh, 0);
-        const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, a.GT - 1) - q0 + D) * 2);
+        const size_t q0 = qrow_offset(a, row, kvh, 0);
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(a, row, kvh, gq - 1) - q0 + D) * 2);
         const int r = g0 + 16 * w + li;
-        const int qoff = r < a.GT ? (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, r) - q0) * 2 : kOutOfRange;
+        const int qoff = r < gq ? (int)(qrow_offset(a, row, kvh, r) - q0) * 2 : kOutOfRange;
         u32x4_t raw[C::NH8][4];
 #pragma unroll
         for (int h = 0; h < C::NH8; ++h)
@@ -315,10 +319,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
     } else if constexpr (C::I8MMA) {
-        const size_t q0 = qrow_offset(row, a.T, a.Hq, a.G, D, kvh, 0);
-        const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, a.GT - 1) - q0 + D) * 2);
+        const size_t q0 = qrow_offset(a, row, kvh, 0);
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(a, row, kvh, gq - 1) - q0 + D) * 2);
         const int r = g0 + 16 * w + li;
-        const int qoff = r < a.GT ? (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, r) - q0) * 2 : kOutOfRange;
+        const int qoff = r < gq ? (int)(qrow_offset(a, row, kvh, r) - q0) * 2 : kOutOfRange;
         u32x4_t raw[C::NB8][2];
 #pragma unroll
         for (int b = 0; b < C::NB8; ++b)
@@ -366,10 +370,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
     } else {
         // the unit's query rows span T tokens, Hq * D elements apart
-        const size_t q0 = qrow_offset(row, a.T, a.Hq, a.G, D, kvh, 0);
-        const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, a.GT - 1) - q0 + D) * 2);
+        const size_t q0 = qrow_offset(a, row, kvh, 0);
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(a, row, kvh, gq - 1) - q0 + D) * 2);
         const int r = g0 + 16 * w + li;
-        const int qoff = r < a.GT ? (int)(qrow_offset(row, a.T, a.Hq, a.G, D, kvh, r) - q0) * 2 : kOutOfRange;
+        const int qoff = r < gq ? (int)(qrow_offset(a, row, kvh, r) - q0) * 2 : kOutOfRange;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
             qb[ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
@@ -572,11 +576,14 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     };
     // Scale, mask the tail, lazy online softmax; P^T of the tile in registers.
     // Returns whether the running maximum moved (then O must be rescaled by alpha).
-    // Query row of this lane's column: token (g0 + 16w + li) / G may attend
-    // positions below lim (len - T + 1 + token); tiles reaching past tmask
-    // hold a position some column must not see.
-    const int lim = min(p1, len - a.T + 1 + (g0 + 16 * w + li) / a.G);
-    const int tmask = p1 - a.T + 1;
+    // Query row of this lane's column: token i = (g0 + 16w + li) / G may
+    // attend positions below lim = qbase + i + 1, none if that position is at
+    // or past len (a blocked causal row's tokens past the sequence end); tiles
+    // reaching past tmask hold a position some column must not see, and a row
+    // with such a token masks every tile.
+    const int qpos = qbase + (g0 + 16 * w + li) / a.G;
+    const int lim = qpos < len ? min(p1, qpos + 1) : 0;
+    const int tmask = qbase + a.T > len ? -0x40000000 : p1 - a.T + 1;
     // 8-bit caches: the logit of a position is scaled by its K row's scale,
     // and its weight in P.V by its V row's scale (l sums the unscaled weights).
     // First part: scale the logits and mask the positions a column must not
@@ -810,8 +817,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int h0 = 0; h0 < 16; h0 += RPI) {
                 const int h = h0 + hr;
-                if (16 * w + h < gcnt)
-                    *reinterpret_cast<f32x4_t*>(a.out + qrow_offset(row, a.T, a.Hq, a.G, D, kvh, g0 + 16 * w + h) +
+                if (16 * w + h < gcnt && g0 + 16 * w + h < gq)
+                    *reinterpret_cast<f32x4_t*>(a.out + qrow_offset(a, row, kvh, g0 + 16 * w + h) +
                                                 4 * c) = *reinterpret_cast<const f32x4_t*>(ot + h * ROWF + 4 * c);
             }
         } else {

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     int lim[GB];
 #pragma unroll
     for (int gg = 0; gg < GB; ++gg) {
-        const uint16_t* qrow = a.q + qrow_offset(row, a.T, a.Hq, a.G, D, kvh, min(g0 + gg, a.GT - 1)) + EPL * rl;
+        const uint16_t* qrow = a.q + qrow_offset(a, row, kvh, min(g0 + gg, a.GT - 1)) + EPL * rl;
         lim[gg] = len - a.T + 1 + (g0 + gg) / a.G;
 #pragma unroll
         for (int h = 0; h < NP / 4; ++h) {
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         for (int k = 0; k < VPT; ++k) {
             const int idx = tid + 256 * k;
             if (idx < gcnt * D) {
-                a.out[qrow_offset(row, a.T, a.Hq, a.G, D, kvh, g0 + idx / D) + idx % D] = val[k];
+                a.out[qrow_offset(a, row, kvh, g0 + idx / D) + idx % D] = val[k];
             }
         }
     } else {

@@ -75,7 +75,7 @@ mqa_status check_paged(int B, const int32_t* block_table, int num_pages, int pag
 }
 
 mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
-                     const mqa_decode_opts* opts, bool causal, Plan* plan, int T) {
+                     const mqa_decode_opts* opts, int causal, Plan* plan, int T) {
     if (B < 0 || Lmax < 0)
         return fail(MQA_ERR_SHAPE, "B and Lmax must be >= 0");
     if (Hq <= 0 || Hkv <= 0 || D <= 0)
@@ -115,6 +115,15 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
 
     Plan p;
     p.G = Hq / Hkv;
+    if (causal) {
+        // blocked causal prefill: T consecutive positions of one sequence per
+        // row, so T * G query rows (up to six 16-row tiles) share each read
+        // of the block's causal prefix
+        if (o.variant == MQA_VARIANT_VALU || o.window > 0 || o.kv_format != MQA_KV_BF16 || o.chunk || o.combine)
+            return fail(MQA_ERR_ARG, "the prefill form takes no variant, window, cache format, chunk or combine option");
+        T = p.G >= kMfmaMaxHeads ? 1 : kMfmaMaxHeads / p.G;
+        o.variant = MQA_VARIANT_MFMA;
+    }
     p.T = T;
     p.GT = T * p.G;  // query rows sharing one kv head: what the head tiles hold
     p.variant = o.variant;
@@ -133,7 +142,8 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     }
     p.head_blocks = (int)ceil_div(p.GT, p.heads_per_block);
 
-    p.rows = causal ? (long long)B * Lmax : (long long)B;
+    p.nblk = causal ? (int)ceil_div(Lmax, T) : 0;
+    p.rows = causal ? (long long)B * p.nblk : (long long)B;
     const long long units = p.rows * Hkv * p.head_blocks;
 
     // Positions one row attends: Lmax, or W with a sliding window of W
@@ -145,7 +155,11 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     p.window = o.window;
     p.kv_format = o.kv_format;
 
-    if (o.chunk > 0) {
+    if (causal) {
+        // one chunk per row: a block's prefix is read once, and the longest
+        // prefixes are dispatched first (row order) to balance the grid
+        p.chunk = (int)round_up(span > 0 ? span : 1, kChunkQuantum);
+    } else if (o.chunk > 0) {
         p.chunk = o.chunk;
     } else if (units == 0 || span == 0) {
         p.chunk = kChunkQuantum;

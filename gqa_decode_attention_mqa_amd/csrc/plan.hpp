@@ -62,7 +62,8 @@ struct Plan {
     int window = 0;                  // sliding window (0 = none)
     int kv_format = 0;               // mqa_kv_format of the cache
     int combine = 0;                 // 0 none, 1 separate kernel, 2 fused
-    long long rows = 0;              // query rows: B (decode) or B * Lmax (prefill)
+    long long rows = 0;              // rows: B (decode) or B * nblk (blocked causal prefill)
+    int nblk = 0;                    // blocked causal prefill: blocks of T positions per sequence
     long long grid_main = 0;         // workgroups along x of the split kernel
     int block_main = 256;
     long long grid_combine = 0;
@@ -78,11 +79,13 @@ struct Plan {
 void set_error(const std::string& msg);
 const char* last_error();
 
-// Checks sizes, scale and options; on success fills `plan`.  `rows` is B for
-// a decode call and B * Lmax for the causal (prefill) form; T is the number
-// of query tokens per row (1 for a decode step).
+// Checks sizes, scale and options; on success fills `plan`.  causal = 0 plans
+// a decode call (B rows of T query tokens, T = 1 for a decode step); causal =
+// 2 plans the blocked causal (prefill) form: each sequence's positions in
+// blocks of T = floor(kMfmaMaxHeads / G) (at least 1) query tokens, B * nblk
+// rows, one chunk per row (no split, no merge), the matrix-core kernel.
 mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
-                     const mqa_decode_opts* opts, bool causal, Plan* plan, int T = 1);
+                     const mqa_decode_opts* opts, int causal, Plan* plan, int T = 1);
 
 // A paged cache as the kernels see it (see check_paged).
 struct PagedCache {

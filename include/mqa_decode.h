@@ -273,15 +273,20 @@ mqa_status mqa_decode_attention_paged(const void *q, const void *k_pages, const 
 /*
  * Causal attention over whole sequences with no cache, the computation a KV
  * cache replaces ("How To Scale Your Model", Part 7, passage introducing the
- * KV cache: a token attends only to itself and earlier tokens).  Row t of
- * sequence b (t < seq_lens[b]) attends positions 0..t; its result equals a
- * decode step at length t+1 with query q_seq[b,t].  Rows t >= seq_lens[b] are
- * written as zeros.  Correctness-grade: it runs the decode kernels once per
- * row, so it is not a fast prefill.
+ * KV cache: a token attends only to itself and earlier tokens; prefill is the
+ * compute-bound pass over a whole prompt, passage on prefill versus
+ * generation).  Row t of sequence b (t < seq_lens[b]) attends positions
+ * 0..t; its result equals a decode step at length t+1 with query q_seq[b,t].
+ * Rows t >= seq_lens[b] are written as zeros.
+ * It runs on the matrix cores: each sequence's positions are taken in blocks
+ * of T = floor(96 / (Hq/Hkv)) consecutive query tokens (at least 1), and the
+ * T * Hq/Hkv query rows of a block and kv head share one read of the block's
+ * causal prefix (mqa_prefill_plan reports T and the grid).  No scratch memory.
  *   q_seq    bf16 [B, Lmax, Hq, D]
  *   k_cache  bf16 [B, Lmax, Hkv, D];  v_cache likewise
  *   seq_lens int32 [B] (device)
- *   out_seq  fp32 [B, Lmax, Hq, D]
+ *   out_seq  fp32 [B, Lmax, Hq, D], fully overwritten
+ * Errors and ownership as for mqa_decode_attention.
  */
 mqa_status mqa_prefill_attention(const void *q_seq, const void *k_cache, const void *v_cache,
                                  const int32_t *seq_lens, float *out_seq, int B, int Hq,
@@ -295,6 +300,12 @@ mqa_status mqa_prefill_attention(const void *q_seq, const void *k_cache, const v
  */
 mqa_status mqa_decode_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                            const mqa_decode_opts *opts, mqa_plan_info *info);
+
+/* The plan of a mqa_prefill_attention call (host only, no HIP call): fills
+ * *info when non-NULL and the query tokens per block (T) when tokens_per_block
+ * is non-NULL. */
+mqa_status mqa_prefill_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale, mqa_plan_info *info,
+                            int *tokens_per_block);
 
 /* mqa_decode_plan for a mqa_decode_attention_multi call with T tokens per
  * sequence (host only, no HIP call). */

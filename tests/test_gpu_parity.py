@@ -269,6 +269,57 @@ def test_prefill_matches_oracle_causal_attention(B, Hq, Hkv, D, Lmax):
     assert (dec - last).abs().max().item() <= ATOL
 
 
+@pytest.mark.parametrize("G,Hkv,D,Lmax,B", [(1, 2, 64, 700, 2), (2, 3, 128, 333, 3), (4, 2, 128, 500, 2),
+                                           (8, 1, 256, 420, 2), (48, 1, 256, 300, 2), (64, 1, 128, 200, 2),
+                                           (80, 1, 64, 150, 2), (96, 1, 128, 130, 1), (112, 1, 64, 100, 2),
+                                           (3, 2, 256, 257, 2), (20, 2, 128, 97, 3)])
+def test_blocked_prefill_shapes(G, Hkv, D, Lmax, B):
+    """The blocked causal form at several tiles per prefix, block sizes T = 96 // G that do not
+    divide Lmax, ragged lengths (0, 1 and Lmax among them), NaN padding, more than 96 query rows
+    per kv head (two head blocks), every head size."""
+    Hq = G * Hkv
+    w = Workload("pf-blk", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, seed=1400 + G + D + Lmax)
+    inp = make_prefill_inputs(w)
+    lens = torch.tensor(([0, Lmax, 1] + [Lmax // 2 + 7])[:B] if B > 1 else [Lmax - 3], dtype=torch.int32)
+    from gqa_decode_attention_mqa_amd.workloads import poison_padding_
+    poison_padding_(inp["k"], lens)
+    poison_padding_(inp["v"], lens)
+    plan = binding.prefill_plan(B, Hq, Hkv, D, Lmax, inp["scale"])
+    assert plan["tokens"] == max(1, 96 // G) and plan["combine"] == 0 and plan["workspace_bytes"] == 0
+    ref = oracle.causal_prefill(inp["q_seq"], inp["k"], inp["v"], lens, inp["scale"])
+    dev = to_dev(inp)
+    print("case blocked prefill", G, Hkv, D, Lmax, B, plan["tokens"], flush=True)
+    out = torch.full((B, Lmax, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
+    binding.prefill(dev["q_seq"], dev["k"], dev["v"], lens.to(DEV), dev["scale"], out=out)
+    torch.cuda.synchronize()
+    check_close(out, ref, "blocked prefill G %d D %d Lmax %d" % (G, D, Lmax))
+    for b in range(B):  # rows at or past the length are zeros
+        assert torch.equal(out[b, int(lens[b]):].cpu(), torch.zeros_like(out[b, int(lens[b]):].cpu()))
+
+
+@pytest.mark.parametrize("name", ["palm", "gqa70b"])
+def test_blocked_prefill_full_size_rows(name):
+    """Prefill of a full-size batch's sequences (the first four of the workload's B, every
+    position of their Lmax), checked on sampled rows against the oracle's decode at length t + 1
+    (a causal row t is the decode step at that length, pinned in the oracle's tests)."""
+    w = WORKLOADS[name].with_(B=4)
+    inp = make_prefill_inputs(w, device=DEV)
+    print("case full prefill", name, binding.prefill_plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax), flush=True)
+    out = binding.prefill(inp["q_seq"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(77)
+    worst = 0.0
+    for b in range(w.B):
+        n = int(inp["seq_lens"][b])
+        rows = sorted(set([0, 1, n - 1] + torch.randint(0, n, (13,), generator=g).tolist()))
+        q = torch.stack([inp["q_seq"][b, t] for t in rows]).contiguous().cpu()
+        kk = inp["k"][b:b + 1].cpu().expand(len(rows), -1, -1, -1).contiguous()
+        vv = inp["v"][b:b + 1].cpu().expand(len(rows), -1, -1, -1).contiguous()
+        ref = oracle.decode(q, kk, vv, torch.tensor([t + 1 for t in rows], dtype=torch.int32), inp["scale"])
+        worst = max(worst, check_close(out[b, rows], ref, "%s prefill rows of sequence %d" % (name, b)))
+    print("full prefill %s: %d sampled rows per sequence, max abs err %.3g" % (name, 16, worst), flush=True)
+
+
 # ------------------------------------------------------------ paged cache
 
 
