@@ -55,16 +55,20 @@ struct MfmaCfg {
     // int8 caches: q.K on int8 matrix cores (16x16x64), q as 128 hi + lo
     static constexpr bool I8MMA = FMT == kKvInt8;
     static constexpr int NB8 = I8MMA ? D / 64 : 1;   // 64-wide blocks of d
-    // tiles in the LDS ring: bf16 D = 256 uses all 160 KB; D <= 128 leaves
-    // room for two workgroups per CU (bf16 D = 128, B=32, Hkv=8, len 4096:
-    // 89.0 us at 4 tiles against 92.1 at 5 and 88.3 at 6, where one
-    // workgroup per CU fits; the ragged batch: 751 us at 4 and 5 tiles
-    // against 943 at 6).  8-bit tiles are half as large; their
-    // kernel is bound by its own per-tile work rather than by loads in flight,
-    // and a 4-tile ring measured faster than deeper ones (MI355X, PaLM-shaped
-    // MQA: 24.8 us at 4 tiles against 29.0 us at 9; B=4, len 131072: 73.7
-    // against 82.1 us; B=32, Hkv=8, D=128: 51.6 against 53.3 us at 8 tiles)
-    static constexpr int STAGES = Q8 ? 4 : (D == 256 ? 5 : 4);
+    // tiles in the LDS ring: four, i.e. two tiles in flight beyond the two
+    // in use.  bf16 D = 256 (128 KB): a fifth tile measured slower on MI355X
+    // (PaLM-shaped MQA 29.5 against 30.4 us per step, B=4 len 131072 87.4
+    // against 88.2 us); per-workgroup timestamps show the later loop end
+    // comes from the compute waves holding the ring barrier, not from loads
+    // in flight.  D <= 128 leaves room for two workgroups per CU (B=32,
+    // Hkv=8, len 4096: 89.0 us at 4 tiles against 92.1 at 5 and 88.3 at 6,
+    // where one workgroup per CU fits; the ragged batch: 751 us at 4 and 5
+    // tiles against 943 at 6).  8-bit tiles are half as large; their kernel is
+    // bound by its own per-tile work rather than by loads in flight, and a
+    // 4-tile ring measured faster than deeper ones (PaLM-shaped MQA: 24.8 us
+    // at 4 tiles against 29.0 us at 9; B=4, len 131072: 73.7 against 82.1 us;
+    // B=32, Hkv=8, D=128: 51.6 against 53.3 us at 8 tiles)
+    static constexpr int STAGES = 4;
     static_assert(STAGES >= 4, "two tiles in use and at least one more in flight");
     static constexpr int KS = D / 32;                // k-steps over d in q.K
     static constexpr int MT = D / 16;                // 16-row tiles of O^T
