@@ -14,8 +14,12 @@ from pathlib import Path
 
 import torch
 
+import os
+
 _PKG = Path(__file__).resolve().parent
-LIB_PATH = _PKG / "libmqa_decode.so"
+# MQA_DECODE_LIB names another build of the library (e.g. the host-sanitizer
+# build, _build/libmqa_decode_asan.so); by default the in-tree build is loaded.
+LIB_PATH = Path(os.environ["MQA_DECODE_LIB"]) if os.environ.get("MQA_DECODE_LIB") else _PKG / "libmqa_decode.so"
 HEADER_PATH = _PKG.parent / "include" / "mqa_decode.h"
 
 MQA_OK = 0

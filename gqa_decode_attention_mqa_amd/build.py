@@ -3,6 +3,8 @@
 hipcc cross-compiles for gfx950 without a GPU.  Every HIP source is compiled
 with packed-fp32 instructions disabled; objects go to ``_build/`` and the
 shared object next to this file, where :mod:`.binding` loads it.
+``python -m gqa_decode_attention_mqa_amd.build --sanitize`` builds the host
+sanitizer variant (see build_sanitized).
 """
 from __future__ import annotations
 
@@ -58,5 +60,56 @@ def build(verbose: bool = False) -> Path:
     return LIB
 
 
+# Host-only sanitizer build: abi.cpp and plan.cpp (the argument checks,
+# planner and workspace cache) are recompiled with AddressSanitizer and
+# UndefinedBehaviorSanitizer on their host side only; the device objects are
+# the regular ones.  The result, _build/libmqa_decode_asan.so, is loaded by a
+# process that preloads the ASan runtime (asan_runtime()); the CPU test
+# tests/test_host_sanitized.py runs the host ABI tests that way.
+HOST_SOURCES = ["abi.cpp", "plan.cpp"]
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+ASAN_LIB = BUILD / "libmqa_decode_asan.so"
+
+
+def asan_runtime() -> str:
+    """Path of the shared ASan runtime of the HIP toolchain's clang."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_sanitized(verbose: bool = False) -> Path:
+    BUILD.mkdir(exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src in HOST_SOURCES:
+            obj = BUILD / (src + ".asan.o")
+            cmd = [HIPCC] + COMMON + SAN_FLAGS + ["-c", str(CSRC / src), "-o", str(obj)]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                sys.stderr.write(r.stdout + r.stderr)
+                raise RuntimeError("hipcc (sanitized host) failed on %s" % src)
+        else:
+            obj = BUILD / (src + ".o")
+            if not obj.exists() or obj.stat().st_mtime < (CSRC / src).stat().st_mtime:
+                obj = _compile(src)
+        objs.append(obj)
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", str(ASAN_LIB)] + [str(o) for o in objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link of libmqa_decode_asan.so failed")
+    if verbose:
+        print("built", ASAN_LIB)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)

@@ -3,6 +3,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -54,6 +55,14 @@ mqa_status get_workspace(hipStream_t stream, size_t bytes, size_t ncounters, voi
     *out = nullptr;
     *counters_out = nullptr;
     if (bytes == 0 && ncounters == 0) return MQA_OK;
+    // Fault injection for tests: MQA_FAIL_WORKSPACE_ALLOC=1 makes every
+    // workspace allocation fail, before any HIP call.
+    if (const char* f = std::getenv("MQA_FAIL_WORKSPACE_ALLOC")) {
+        if (f[0] == '1') {
+            mqa::set_error("split-K workspace allocation failed (MQA_FAIL_WORKSPACE_ALLOC is set)");
+            return MQA_ERR_WORKSPACE;
+        }
+    }
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");

@@ -43,6 +43,9 @@
  * Errors: every argument check happens on the host before any HIP call, so
  * the checks can run on a machine with no GPU.  No call aborts or throws; a
  * failure returns a status and mqa_last_error() holds a thread-local message.
+ * For tests, the environment variable MQA_FAIL_WORKSPACE_ALLOC=1 makes every
+ * split-K workspace allocation fail with MQA_ERR_WORKSPACE (before any HIP
+ * call).
  *
  * All calls are asynchronous with respect to the host: results are valid once
  * `stream` has been synchronised.  `stream` is a hipStream_t passed as void*

@@ -346,3 +346,19 @@ def test_stream_read_probe_checks_its_arguments(args, expect):
 
 def test_stream_read_probe_of_nothing_is_a_no_op():
     assert lib.mqa_stream_read_probe(0, 0, 1, 0, None, None, None) == OK
+
+
+# ------------------------------------------------ workspace allocation failure
+
+def test_workspace_allocation_failure_is_reported(monkeypatch):
+    """MQA_FAIL_WORKSPACE_ALLOC=1 makes the split workspace allocation fail (before any HIP call):
+    a split call reports MQA_ERR_WORKSPACE with a message; calls that need no workspace are unaffected."""
+    monkeypatch.setenv("MQA_FAIL_WORKSPACE_ALLOC", "1")
+    opts = binding.make_opts(chunk=128)
+    assert binding.plan(2, 8, 2, 128, 4096, chunk=128)["workspace_bytes"] > 0
+    assert call(Lmax=4096, opts=opts) == ERR_WORKSPACE
+    assert b"workspace" in lib.mqa_last_error()
+    assert lib.mqa_decode_attention_multi(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3, 8, 2, 128, 4096, 0.1, None,
+                                          ctypes.byref(opts)) == ERR_WORKSPACE
+    # B == 0 never allocates
+    assert call(q=0, k=0, v=0, lens=0, out=0, B=0, Lmax=4096, opts=opts) == OK
