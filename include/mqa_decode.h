@@ -278,7 +278,9 @@ mqa_status mqa_decode_attention_paged(const void *q, const void *k_pages, const 
  * cache replaces ("How To Scale Your Model", Part 7, passage introducing the
  * KV cache: a token attends only to itself and earlier tokens; prefill is the
  * compute-bound pass over a whole prompt, passage on prefill versus
- * generation).  Row t of sequence b (t < seq_lens[b]) attends positions
+ * generation; "Efficiently Scaling Transformer Inference", section 3.4,
+ * "Attention Layer Partitioning": in prefill the K/V read is amortised over
+ * the query tokens).  Row t of sequence b (t < seq_lens[b]) attends positions
  * 0..t; its result equals a decode step at length t+1 with query q_seq[b,t].
  * Rows t >= seq_lens[b] are written as zeros.
  * It runs on the matrix cores: each sequence's positions are taken in blocks
