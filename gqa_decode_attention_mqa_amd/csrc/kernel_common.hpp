@@ -429,10 +429,10 @@ __device__ __forceinline__ void merge_slot(const f32x2_t (&ml)[S], const u32x4_t
 // (IT of them; an item is one (query row, 8-value slot) of the unit's query
 // rows g0 ..), with the S chunks' {lse, e} and 16-byte slots of every item
 // loaded coherently before any is merged, so the batch costs one round trip.
-// Loads of chunks past nsplit repeat the last chunk and loads of items past
-// the end repeat the last item (both stay in range); merge_slot then gives
-// those chunks weight 0, and items past the end are not stored.  ro / rm cover
-// the unit's partial rows and {lse, e} pairs (split-major, GT rows per split).
+// Loads of chunks past nsplit repeat the last chunk (in range; merge_slot
+// gives them weight 0); items past the end load and store nothing.  ro / rm
+// cover the unit's partial rows and {lse, e} pairs (split-major, GT rows per
+// split).
 template <int S, int IT>
 __device__ __forceinline__ void fused_merge_batch(const DecodeArgs& a, __amdgpu_buffer_rsrc_t ro,
                                                   __amdgpu_buffer_rsrc_t rm, long long row, int kvh, int g0,
@@ -442,7 +442,8 @@ __device__ __forceinline__ void fused_merge_batch(const DecodeArgs& a, __amdgpu_
     u32x4_t o[IT][S];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int idx = min(idx0 + it * stride, items - 1);
+        const int idx = idx0 + it * stride;
+        if (idx >= items) continue;
         const int g = g0 + idx / slots, slot = idx % slots;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
