@@ -146,13 +146,15 @@ def single_thread_baseline(target_s: float = 4.0) -> dict:
     import oracle
     from gqa_decode_attention_mqa_amd.workloads import WORKLOADS, make_inputs
     prev = oracle.max_threads()
-    oracle.set_threads(1)
     try:
         res = {}
         for name in ("tiny", "palm"):
             w = WORKLOADS[name]
             inp = make_inputs(w)
             q, k, v, lens = inp["q"], inp["k"], inp["v"], inp["seq_lens"]
+            # set after the inputs are drawn: torch's own OpenMP use can reset the count
+            if oracle.set_threads(1) != 1:
+                raise RuntimeError("could not restrict the oracle to one thread")
             t0 = time.perf_counter()
             oracle.decode(q[:1], k[:1], v[:1], lens[:1], inp["scale"])
             one = max(time.perf_counter() - t0, 1e-6)
@@ -163,7 +165,7 @@ def single_thread_baseline(target_s: float = 4.0) -> dict:
                 oracle.decode(q[:nseq], k[:nseq], v[:nseq], lens[:nseq], inp["scale"])
             dt = time.perf_counter() - t0
             steps = reps * float(lens[:nseq].double().sum() / lens.double().sum())
-            res[name] = {"steps_per_s": round(steps / dt, 4), "seconds": round(dt, 3),
+            res[name] = {"steps_per_s": round(steps / dt, 4), "seconds": round(dt, 3), "threads": oracle.max_threads(),
                          "sample": ("%d whole step(s)" % reps) if nseq == w.B else
                          ("first %d of %d sequences of one step, scaled by their share of positions" % (nseq, w.B))}
         return res
@@ -175,7 +177,9 @@ def cpu_baseline(w, inp, target_s: float, window: int = 0, kv_format: str = "bf1
     """The oracle, as it stands, on whole decode steps of set 0 (or a prefix of the batch)."""
     import oracle
     q, k, v, lens = inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu()
-    threads = oracle.max_threads()
+    # every core this process may run on, set right before timing (torch's own
+    # OpenMP use can change the count)
+    threads = oracle.set_threads(len(os.sched_getaffinity(0)))
     if tokens > 1:
         run = lambda qq, kk, vv, ll: oracle.decode_multi(qq, kk, vv, ll, inp["scale"])
     elif kv_format != "bf16":
@@ -313,6 +317,7 @@ def run_prefill(args, w, torch, binding):
         L = min(w.Lmax, 64)
         while True:
             q, k, v = inp["q_seq"][:1, :L].cpu(), inp["k"][:1, :L].cpu(), inp["v"][:1, :L].cpu()
+            oracle.set_threads(len(os.sched_getaffinity(0)))
             t0 = time.perf_counter()
             oracle.causal_prefill(q, k, v, [L], w.scale)
             dt = time.perf_counter() - t0
