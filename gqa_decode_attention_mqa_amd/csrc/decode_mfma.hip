@@ -843,8 +843,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
             }
             const size_t part0 = ((size_t)unit * a.max_splits + s) * a.GT + g0 + 16 * w;  // this wave's first row
             uint16_t* dst = a.part_o + part0 * D;
-            // the fused merge reads these rows from another workgroup: 16-byte
-            // coherent stores (sc1) through a descriptor over the wave's rows
+            // 16-byte device-scope stores (sc1) through a descriptor over the
+            // wave's rows: the fused merge reads them from another workgroup,
+            // and for the separate merge they measured faster than plain
+            // stores (PaLM-shaped MQA, split kernel 25.6 against 26.2 us)
             const __amdgpu_buffer_rsrc_t prs = make_rsrc(dst, 16 * D * 2);
             constexpr int LPR = D / 8;     // lanes per row, 16 bytes (8 halves) each
             constexpr int RPI = 64 / LPR;  // rows per store instruction
@@ -854,18 +856,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
                 const int h = h0 + hr;
                 if (16 * w + h < gcnt) {
                     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ot + h * ROWH + 8 * c);
-                    if (a.fused)
-                        __builtin_amdgcn_raw_buffer_store_b128(v, prs, (h * D + 8 * c) * 2, 0, kCachePolicyCoherent);
-                    else
-                        *reinterpret_cast<u32x4_t*>(dst + (size_t)h * D + 8 * c) = v;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, prs, (h * D + 8 * c) * 2, 0, kCachePolicyCoherent);
                 }
             }
             if (kg == 0 && g < gcnt) {
-                const f32x2_t ml = f32x2_t{m_run + __log2f(l_run), (float)e};
-                if (a.fused)
-                    store_coherent8(a.part_ml + part0 + li, ml);
-                else
-                    a.part_ml[part0 + li] = ml;
+                store_coherent8(a.part_ml + part0 + li, f32x2_t{m_run + __log2f(l_run), (float)e});
             }
         }
     }
