@@ -307,7 +307,7 @@ def run_prefill(args, w, torch, binding):
                    "flops_per_step": flops, "plan": plan},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "blocked causal prefill (mfma, %d positions per block)" % plan["tokens"],
+                     "kernel": "causal prefill (mfma, %d query rows per workgroup)" % plan["rows_per_block"],
                      "step_us_p10_p50_p90": [round(pct(per, p), 2) for p in (10, 50, 90)]},
     }
     if not args.no_cpu_baseline:

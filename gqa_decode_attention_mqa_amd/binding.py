@@ -154,18 +154,20 @@ def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None
 
 
 def prefill_plan(B, Hq, Hkv, D, Lmax, scale=None) -> dict:
-    """The library's launch plan for a mqa_prefill_attention call (host only); ``tokens``
-    is the number of query positions per block."""
+    """The library's launch plan for a mqa_prefill_attention call (host only);
+    ``rows_per_block`` is the number of query rows (position, head of the group)
+    one workgroup serves."""
     lib = load_library()
     info = PlanInfo()
-    tokens = ctypes.c_int(0)
+    rows = ctypes.c_int(0)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib.mqa_prefill_plan(B, Hq, Hkv, D, Lmax, sc, ctypes.byref(info), ctypes.byref(tokens)),
+    _check(lib.mqa_prefill_plan(B, Hq, Hkv, D, Lmax, sc, ctypes.byref(info), ctypes.byref(rows)),
            "mqa_prefill_plan")
     return {"variant": VARIANT_NAMES.get(info.variant, info.variant), "chunk": info.chunk,
             "max_splits": info.max_splits, "combine": info.combine, "head_blocks": info.head_blocks,
             "grid_main": info.grid_main, "block_main": info.block_main,
-            "grid_combine": info.grid_combine, "workspace_bytes": info.workspace_bytes, "tokens": tokens.value}
+            "grid_combine": info.grid_combine, "workspace_bytes": info.workspace_bytes,
+            "rows_per_block": rows.value}
 
 
 def _stream_ptr(device) -> int:

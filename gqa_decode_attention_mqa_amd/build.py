@@ -22,20 +22,26 @@ LIB = PKG / "libmqa_decode.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "plan.cpp", "decode_mfma.hip", "decode_valu.hip", "combine.hip", "probe.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "decode_mfma.hip", "decode_valu.hip", "combine.hip", "probe.hip", "prefill_mfma.hip"]
 COMMON = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          # matrix-core accumulators in ordinary VGPRs: the online-softmax
-          # rescale touches them with vector ALU ops, and AGPR accumulators
-          # cost a copy in and out around every product
-          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", str(ROOT / "include")]
+# Matrix-core accumulators in ordinary VGPRs for the decode kernels: the
+# online-softmax rescale touches them with vector ALU ops, and AGPR
+# accumulators cost a copy in and out around every product.  The prefill
+# kernel keeps 128 accumulator registers per lane at D = 256 and needs the
+# AGPRs for them.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+
+def _flags(src: str) -> list:
+    return COMMON + ([] if src == "prefill_mfma.hip" else VGPR_FORM)
 
 
 def _compile(src: str) -> Path:
     obj = BUILD / (src + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", str(CSRC / src), "-o", str(obj)]
+    cmd = [HIPCC] + _flags(src) + ["-c", str(CSRC / src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -88,7 +94,7 @@ def build_sanitized(verbose: bool = False) -> Path:
     for src in SOURCES:
         if src in HOST_SOURCES:
             obj = BUILD / (src + ".asan.o")
-            cmd = [HIPCC] + COMMON + SAN_FLAGS + ["-c", str(CSRC / src), "-o", str(obj)]
+            cmd = [HIPCC] + _flags(src) + SAN_FLAGS + ["-c", str(CSRC / src), "-o", str(obj)]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 sys.stderr.write(r.stdout + r.stderr)

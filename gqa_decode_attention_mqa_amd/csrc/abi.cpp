@@ -345,15 +345,37 @@ mqa_status mqa_decode_attention_paged(const void* q, const void* k_pages, const 
 mqa_status mqa_prefill_attention(const void* q_seq, const void* k_cache, const void* v_cache,
                                  const int32_t* seq_lens, float* out_seq, int B, int Hq, int Hkv,
                                  int D, int Lmax, float scale, void* stream) {
-    return run(q_seq, k_cache, v_cache, seq_lens, out_seq, B, Hq, Hkv, D, Lmax, scale, stream,
-               nullptr, mqa::kCausalBlocked);
+    mqa::set_error("");
+    Plan plan;
+    mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, nullptr, mqa::kCausalPrefill, &plan);
+    if (st != MQA_OK) return st;
+    st = mqa::check_pointers(B, Lmax, q_seq, k_cache, v_cache, seq_lens, out_seq);
+    if (st != MQA_OK) return st;
+    if (plan.grid_main == 0) return MQA_OK;
+    mqa::PrefillArgs a{};
+    a.q = static_cast<const uint16_t*>(q_seq);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.seq_lens = seq_lens;
+    a.out = out_seq;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.Lmax = Lmax;
+    a.G = plan.G;
+    a.row_blocks = plan.row_blocks;
+    a.qk_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+    const hipError_t e = mqa::launch_prefill_mfma(plan, a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+    return MQA_OK;
 }
 
 mqa_status mqa_prefill_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale, mqa_plan_info* info,
-                            int* tokens_per_block) {
+                            int* rows_per_block) {
     mqa::set_error("");
     Plan p;
-    const mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, nullptr, mqa::kCausalBlocked, &p);
+    const mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, nullptr, mqa::kCausalPrefill, &p);
     if (st != MQA_OK) return st;
     if (info) {
         info->variant = p.variant;
@@ -366,7 +388,7 @@ mqa_status mqa_prefill_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale
         info->grid_combine = p.grid_combine;
         info->workspace_bytes = p.workspace_bytes;
     }
-    if (tokens_per_block) *tokens_per_block = p.T;
+    if (rows_per_block) *rows_per_block = mqa::kPrefillRows;
     return MQA_OK;
 }
 

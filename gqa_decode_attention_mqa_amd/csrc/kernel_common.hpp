@@ -56,6 +56,18 @@ struct DecodeArgs {
 
 constexpr int kCausalBlocked = 2;
 
+// Arguments of the causal prefill kernel (bf16 q, K and V; fp32 out).
+struct PrefillArgs {
+    const uint16_t* q;         // bf16 [B, Lmax, Hq, D]
+    const uint16_t* k;         // bf16 [B, Lmax, Hkv, D]
+    const uint16_t* v;         // likewise
+    const int32_t* seq_lens;   // [B], clamped to [0, Lmax]
+    float* out;                // fp32 [B, Lmax, Hq, D]
+    int B, Hq, Hkv, D, Lmax, G;
+    int row_blocks;            // workgroups per (sequence, kv head): ceil(Lmax * G / kPrefillRows)
+    float qk_log2;             // scale * log2(e)
+};
+
 struct CombineArgs {
     const uint16_t* part_o;
     const f32x2_t* part_ml;

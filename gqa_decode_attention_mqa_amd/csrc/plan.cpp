@@ -115,6 +115,29 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
 
     Plan p;
     p.G = Hq / Hkv;
+    if (causal == kCausalPrefill) {
+        // causal prefill: the Lmax * G query rows of each (sequence, kv head)
+        // in workgroups of kPrefillRows rows, each streaming its causal prefix
+        if (o.variant == MQA_VARIANT_VALU || o.window > 0 || o.kv_format != MQA_KV_BF16 || o.chunk || o.combine)
+            return fail(MQA_ERR_ARG, "the prefill form takes no variant, window, cache format, chunk or combine option");
+        if ((long long)Lmax * p.G > 0x7FFFFFFFLL - kPrefillRows)
+            return fail(MQA_ERR_UNSUPPORTED, "Lmax * Hq / Hkv too large for the prefill kernel");
+        p.variant = MQA_VARIANT_MFMA;
+        p.T = 1;
+        p.GT = p.G;
+        p.heads_per_block = kPrefillRows;
+        p.head_blocks = 1;
+        p.rows = B;
+        p.row_blocks = (int)ceil_div((long long)Lmax * p.G, kPrefillRows);
+        p.chunk = (int)round_up(Lmax > 0 ? Lmax : 1, kChunkQuantum);
+        p.max_splits = 1;
+        p.grid_main = (long long)B * Hkv * p.row_blocks;
+        p.block_main = 64 * (kPrefillRows / 32);
+        if (p.grid_main > kMaxGrid)
+            return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (grid limit)");
+        *plan = p;
+        return MQA_OK;
+    }
     if (causal) {
         // blocked causal prefill: T consecutive positions of one sequence per
         // row, so T * G query rows (up to six 16-row tiles) share each read

@@ -46,6 +46,11 @@ constexpr int kCombineFewMaxSplits = 8;
 // Most chunks per unit the fused combine handles: the same register-resident
 // merge of every chunk's slot as the few-chunk kernel.
 constexpr int kFusedMaxSplits = kCombineFewMaxSplits;
+// make_plan's `causal` argument for the causal prefill kernel.
+constexpr int kCausalPrefill = 3;
+// Query rows per workgroup of the causal prefill kernel: four compute waves of
+// 32 rows (two 16-row tiles of the matrix products each).
+constexpr int kPrefillRows = 128;
 // Query heads per workgroup of the few-chunk combine (256 threads, D/8 each).
 constexpr int combine_heads_per_block(int D) { return 2048 / D; }
 
@@ -64,6 +69,8 @@ struct Plan {
     int combine = 0;                 // 0 none, 1 separate kernel, 2 fused
     long long rows = 0;              // rows: B (decode) or B * nblk (blocked causal prefill)
     int nblk = 0;                    // blocked causal prefill: blocks of T positions per sequence
+    int row_blocks = 0;              // causal prefill: workgroups of kPrefillRows query rows per
+                                     // (sequence, kv head)
     long long grid_main = 0;         // workgroups along x of the split kernel
     int block_main = 256;
     long long grid_combine = 0;
@@ -83,7 +90,9 @@ const char* last_error();
 // a decode call (B rows of T query tokens, T = 1 for a decode step); causal =
 // 2 plans the blocked causal (prefill) form: each sequence's positions in
 // blocks of T = floor(kMfmaMaxHeads / G) (at least 1) query tokens, B * nblk
-// rows, one chunk per row (no split, no merge), the matrix-core kernel.
+// rows, one chunk per row (no split, no merge), the matrix-core kernel;
+// causal = kCausalPrefill plans the causal prefill kernel (B * Hkv *
+// row_blocks workgroups of kPrefillRows query rows, no split, no merge).
 mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                      const mqa_decode_opts* opts, int causal, Plan* plan, int T = 1);
 

@@ -283,10 +283,12 @@ mqa_status mqa_decode_attention_paged(const void *q, const void *k_pages, const 
  * the query tokens).  Row t of sequence b (t < seq_lens[b]) attends positions
  * 0..t; its result equals a decode step at length t+1 with query q_seq[b,t].
  * Rows t >= seq_lens[b] are written as zeros.
- * It runs on the matrix cores: each sequence's positions are taken in blocks
- * of T = floor(96 / (Hq/Hkv)) consecutive query tokens (at least 1), and the
- * T * Hq/Hkv query rows of a block and kv head share one read of the block's
- * causal prefix (mqa_prefill_plan reports T and the grid).  No scratch memory.
+ * It runs on the matrix cores: the query rows of a sequence and kv head are
+ * its (position, head of the group) pairs in position order, and each
+ * workgroup serves 128 consecutive rows, which share one read of their
+ * causal prefix, streamed through LDS in 64-position tiles
+ * (mqa_prefill_plan reports the rows per workgroup and the grid).  No
+ * scratch memory.
  *   q_seq    bf16 [B, Lmax, Hq, D]
  *   k_cache  bf16 [B, Lmax, Hkv, D];  v_cache likewise
  *   seq_lens int32 [B] (device)
@@ -307,10 +309,10 @@ mqa_status mqa_decode_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                            const mqa_decode_opts *opts, mqa_plan_info *info);
 
 /* The plan of a mqa_prefill_attention call (host only, no HIP call): fills
- * *info when non-NULL and the query tokens per block (T) when tokens_per_block
- * is non-NULL. */
+ * *info when non-NULL and the query rows one workgroup serves when
+ * rows_per_block is non-NULL. */
 mqa_status mqa_prefill_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale, mqa_plan_info *info,
-                            int *tokens_per_block);
+                            int *rows_per_block);
 
 /* mqa_decode_plan for a mqa_decode_attention_multi call with T tokens per
  * sequence (host only, no HIP call). */

@@ -273,10 +273,10 @@ def test_prefill_matches_oracle_causal_attention(B, Hq, Hkv, D, Lmax):
                                            (8, 1, 256, 420, 2), (48, 1, 256, 300, 2), (64, 1, 128, 200, 2),
                                            (80, 1, 64, 150, 2), (96, 1, 128, 130, 1), (112, 1, 64, 100, 2),
                                            (3, 2, 256, 257, 2), (20, 2, 128, 97, 3)])
-def test_blocked_prefill_shapes(G, Hkv, D, Lmax, B):
-    """The blocked causal form at several tiles per prefix, block sizes T = 96 // G that do not
-    divide Lmax, ragged lengths (0, 1 and Lmax among them), NaN padding, more than 96 query rows
-    per kv head (two head blocks), every head size."""
+def test_prefill_shapes(G, Hkv, D, Lmax, B):
+    """The prefill kernel at several tiles per prefix, row blocks of 128 (position, head) rows that
+    split a position's heads or do not divide Lmax * G, ragged lengths (0, 1 and Lmax among them),
+    NaN padding past each length, several kv heads, every head size."""
     Hq = G * Hkv
     w = Workload("pf-blk", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, seed=1400 + G + D + Lmax)
     inp = make_prefill_inputs(w)
@@ -285,20 +285,21 @@ def test_blocked_prefill_shapes(G, Hkv, D, Lmax, B):
     poison_padding_(inp["k"], lens)
     poison_padding_(inp["v"], lens)
     plan = binding.prefill_plan(B, Hq, Hkv, D, Lmax, inp["scale"])
-    assert plan["tokens"] == max(1, 96 // G) and plan["combine"] == 0 and plan["workspace_bytes"] == 0
+    assert plan["rows_per_block"] == 128 and plan["combine"] == 0 and plan["workspace_bytes"] == 0
+    assert plan["grid_main"] == B * Hkv * -(-Lmax * G // 128) and plan["block_main"] == 256
     ref = oracle.causal_prefill(inp["q_seq"], inp["k"], inp["v"], lens, inp["scale"])
     dev = to_dev(inp)
-    print("case blocked prefill", G, Hkv, D, Lmax, B, plan["tokens"], flush=True)
+    print("case prefill shapes", G, Hkv, D, Lmax, B, flush=True)
     out = torch.full((B, Lmax, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
     binding.prefill(dev["q_seq"], dev["k"], dev["v"], lens.to(DEV), dev["scale"], out=out)
     torch.cuda.synchronize()
-    check_close(out, ref, "blocked prefill G %d D %d Lmax %d" % (G, D, Lmax))
+    check_close(out, ref, "prefill G %d D %d Lmax %d" % (G, D, Lmax))
     for b in range(B):  # rows at or past the length are zeros
         assert torch.equal(out[b, int(lens[b]):].cpu(), torch.zeros_like(out[b, int(lens[b]):].cpu()))
 
 
 @pytest.mark.parametrize("name", ["palm", "gqa70b"])
-def test_blocked_prefill_full_size_rows(name):
+def test_prefill_full_size_rows(name):
     """Prefill of a full-size batch's sequences (the first four of the workload's B, every
     position of their Lmax), checked on sampled rows against the oracle's decode at length t + 1
     (a causal row t is the decode step at that length, pinned in the oracle's tests)."""
