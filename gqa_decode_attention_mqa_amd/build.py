@@ -26,17 +26,15 @@ SOURCES = ["abi.cpp", "plan.cpp", "decode_mfma.hip", "decode_valu.hip", "combine
 COMMON = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # matrix-core accumulators in ordinary VGPRs: the online-softmax
+          # rescale touches them with vector ALU ops, and AGPR accumulators
+          # cost a copy in and out around every product
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", str(ROOT / "include")]
-# Matrix-core accumulators in ordinary VGPRs for the decode kernels: the
-# online-softmax rescale touches them with vector ALU ops, and AGPR
-# accumulators cost a copy in and out around every product.  The prefill
-# kernel keeps 128 accumulator registers per lane at D = 256 and needs the
-# AGPRs for them.
-VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _flags(src: str) -> list:
-    return COMMON + ([] if src == "prefill_mfma.hip" else VGPR_FORM)
+    return COMMON
 
 
 def _compile(src: str) -> Path:

@@ -132,7 +132,7 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         p.chunk = (int)round_up(Lmax > 0 ? Lmax : 1, kChunkQuantum);
         p.max_splits = 1;
         p.grid_main = (long long)B * Hkv * p.row_blocks;
-        p.block_main = 64 * (kPrefillRows / 32);
+        p.block_main = 64 * (kPrefillRows / (16 * prefill_row_tiles(D)));
         if (p.grid_main > kMaxGrid)
             return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (grid limit)");
         *plan = p;

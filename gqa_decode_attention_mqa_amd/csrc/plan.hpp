@@ -51,6 +51,15 @@ constexpr int kCausalPrefill = 3;
 // Query rows per workgroup of the causal prefill kernel: four compute waves of
 // 32 rows (two 16-row tiles of the matrix products each).
 constexpr int kPrefillRows = 128;
+// 16-row tiles of query rows per compute wave of the prefill kernel (the
+// workgroup has kPrefillRows / (16 * tiles) compute waves), both forms at two
+// waves per SIMD.  D = 256: one tile per wave, eight waves (two tiles per wave
+// need more registers than two waves per SIMD leave: measured on MI355X,
+// PaLM-shaped prefill 8.6 ms against 10.2 ms at one wave per SIMD).  D <= 128:
+// two tiles per wave (each K and V^T read feeds two products) and two
+// workgroups per CU (B=32, Hkv=8, D=128, 4096 positions: 10.1 ms against
+// 11.1 ms with one tile per wave).
+constexpr int prefill_row_tiles(int D) { return D == 256 ? 1 : 2; }
 // Query heads per workgroup of the few-chunk combine (256 threads, D/8 each).
 constexpr int combine_heads_per_block(int D) { return 2048 / D; }
 

@@ -29,9 +29,9 @@
 
 namespace mqa {
 
-template <int D>
+template <int D, int RT>
 struct PrefillCfg {
-    static constexpr int WAVES = kPrefillRows / 32;  // compute waves, 32 query rows each
+    static constexpr int WAVES = kPrefillRows / (16 * RT);  // compute waves, RT 16-row tiles each
     static constexpr int STEP = 64;                  // positions per K/V tile
     static constexpr int ROWB = D * 2;               // bytes of one cached row
     static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
@@ -43,15 +43,15 @@ struct PrefillCfg {
     static constexpr int KS = D / 32;                  // k-steps of q.K
     static constexpr int MT = D / 16;                  // 16-row tiles of O^T (along d)
     static constexpr int MH = MT / 2;                  // P.V runs over two halves of d
-    static_assert(WAVES == 4, "one compute wave per SIMD");
+    static_assert(RT == 1 || RT == 2, "one or two 16-row tiles per wave");
     static_assert(LOADS % WAVES == 0, "every wave issues the same number of loads");
     static_assert(2 * LPW <= 63, "a tile's loads fit a wave's counter");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
-    using C = PrefillCfg<D>;
+template <int D, int RT>
+__global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
+    using C = PrefillCfg<D, RT>;
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
 
     const int tid = threadIdx.x;
@@ -89,12 +89,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     // attends positions below lim = min(t + 1, len); rows with t >= len are
     // computed like the others and written as zeros.  orow indexes the row in
     // q and out ([B, Lmax, Hq, D]), -1 past the last row.
-    int lim[2];
-    bool valid[2];
-    long long orow[2];
+    int lim[RT];
+    bool valid[RT];
+    long long orow[RT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int r = r0 + 32 * w + 16 * rt + li;
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = r0 + 16 * RT * w + 16 * rt + li;
         const int t = r / a.G;
         lim[rt] = min(t + 1, len);
         valid[rt] = r < nrows && t < len;
@@ -102,14 +102,14 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     }
     // the wave's first row has the smallest limit: a tile ending at or below
     // it needs no causal mask in this wave
-    const int wr = r0 + 32 * w;
+    const int wr = r0 + 16 * RT * w;
     const int lim_wave = wr < nrows ? min(wr / a.G + 1, len) : 0;
 
     // q^T operand (B of q.K) of each row tile: lane (li, kg), k-step ks holds
     // q[row li][32 ks + 8 kg .. +8]; rows past the last read as zero
-    u32x4_t qb[2][C::KS];
+    u32x4_t qb[RT][C::KS];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
         const uint16_t* qp = a.q + (orow[rt] < 0 ? 0 : orow[rt]) * D + 8 * kg;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
@@ -144,10 +144,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
         }
     };
 
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-    f32x4_t oacc[2][C::MT];  // O^T of row tile rt, 16-row tile m of d: rows d = 16m .. 16m+15
+    float m_run[RT], l_run[RT];
+    f32x4_t oacc[RT][C::MT];  // O^T of row tile rt, 16-row tile m of d: rows d = 16m .. 16m+15
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt) m_run[rt] = -INFINITY, l_run[rt] = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int m = 0; m < C::MT; ++m) oacc[rt][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const float qk = a.qk_log2;
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
 
     // O^T += V^T P^T of the tile in stage `stage` over its two 32-position
     // blocks, each in two halves of d
-    auto pv_tile = [&](int stage, const u32x4_t (&pb)[2][2]) {
+    auto pv_tile = [&](int stage, const u32x4_t (&pb)[RT][2]) {
         const uint32_t vbase = lds_addr(smem + stage * C::STAGE_BYTES + C::TILE_BYTES);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -178,8 +180,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int j = 0; j < C::MH; ++j) {
                     const u32x4_t va = u32x4_t{lo[j].x, lo[j].y, hi[j].x, hi[j].y};
-                    oacc[0][M0 + j] = mfma_16x16x32_bf16(va, pb[0][kb], oacc[0][M0 + j]);
-                    oacc[1][M0 + j] = mfma_16x16x32_bf16(va, pb[1][kb], oacc[1][M0 + j]);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        oacc[rt][M0 + j] = mfma_16x16x32_bf16(va, pb[rt][kb], oacc[rt][M0 + j]);
                 }
             };
             half(first);
@@ -193,8 +196,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     // accumulators are rescaled outside it, and the tile is finished there.
     // (A rescale inside the loop, however rarely taken, makes the compiler
     // copy all accumulators between AGPRs and VGPRs on every tile.)
-    u32x4_t pb[2][2];
-    float alpha[2];
+    u32x4_t pb[RT][2];
+    float alpha[RT];
     int tile = 0;
     if (ntiles > 0) issue_tile(0);
     while (tile < ntiles) {
@@ -212,24 +215,26 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
 
             // S^T = K q^T: accumulator (mq, rt), lane (li, kg), element e
             // holds row li of tile rt at position 16 mq + 4 kg + e
-            f32x4_t sacc[4][2];
+            f32x4_t sacc[4][RT];
 #pragma unroll
-            for (int mq = 0; mq < 4; ++mq) sacc[mq][0] = sacc[mq][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int mq = 0; mq < 4; ++mq)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) sacc[mq][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
                 for (int mq = 0; mq < 4; ++mq) {
                     const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kt + swz<D>(16 * mq + li, 4 * ks + kg));
-                    sacc[mq][0] = mfma_16x16x32_bf16(ka, qb[0][ks], sacc[mq][0]);
-                    sacc[mq][1] = mfma_16x16x32_bf16(ka, qb[1][ks], sacc[mq][1]);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) sacc[mq][rt] = mfma_16x16x32_bf16(ka, qb[rt][ks], sacc[mq][rt]);
                 }
 
             // scaled logits; the causal mask only on tiles reaching past the
             // wave's first row (a real branch: most tiles skip it)
             const int st = tile * C::STEP;
-            float s[2][4][4];
+            float s[RT][4][4];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int mq = 0; mq < 4; ++mq)
 #pragma unroll
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
             if (st + C::STEP > lim_wave) {
                 asm volatile("" ::: "memory");
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int mq = 0; mq < 4; ++mq)
 #pragma unroll
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
             // 32-position blocks kb = 0, 1
             bool moved_any = false;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
+            for (int rt = 0; rt < RT; ++rt) {
                 float mx = -INFINITY;
 #pragma unroll
                 for (int mq = 0; mq < 4; ++mq)
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
         }
         if (!rescale) break;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int m = 0; m < C::MT; ++m) oacc[rt][m] = oacc[rt][m] * alpha[rt];
         pv_tile(tile & 1, pb);
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     // Epilogue: O / l of each row, rows at or past the length as zeros; lane
     // (li, kg) writes d = 16m + 4kg .. +3 of row li (16 bytes, every m)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
         const float l = sum_xor32(sum_xor16(l_run[rt]));
         const float inv = l > 0.f ? 1.f / l : 0.f;
         if (orow[rt] >= 0) {
@@ -312,9 +317,9 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     }
 }
 
-template <int D>
+template <int D, int RT>
 static hipError_t launch_prefill_d(const Plan& p, const PrefillArgs& a, hipStream_t stream) {
-    using C = PrefillCfg<D>;
+    using C = PrefillCfg<D, RT>;
     constexpr int lds = C::LDS_BYTES;
     if (lds > 64 * 1024) {
         static std::atomic<uint64_t> done_mask{0};
@@ -323,23 +328,24 @@ static hipError_t launch_prefill_d(const Plan& p, const PrefillArgs& a, hipStrea
         if (e != hipSuccess) return e;
         const uint64_t bit = 1ull << (dev & 63);
         if (!(done_mask.load() & bit)) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_mfma_kernel<D>),
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_mfma_kernel<D, RT>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             if (e != hipSuccess) return e;
             done_mask.fetch_or(bit);
         }
     }
     if (p.block_main != 64 * C::WAVES) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_mfma_kernel<D>), dim3((unsigned)p.grid_main), dim3(64 * C::WAVES), lds, stream, a);
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, RT>), dim3((unsigned)p.grid_main), dim3(64 * C::WAVES), lds, stream,
+                       a);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_mfma(const Plan& p, const PrefillArgs& a, hipStream_t stream) {
     if (p.grid_main <= 0) return hipSuccess;
     switch (a.D) {
-        case 64: return launch_prefill_d<64>(p, a, stream);
-        case 128: return launch_prefill_d<128>(p, a, stream);
-        case 256: return launch_prefill_d<256>(p, a, stream);
+        case 64: return launch_prefill_d<64, prefill_row_tiles(64)>(p, a, stream);
+        case 128: return launch_prefill_d<128, prefill_row_tiles(128)>(p, a, stream);
+        case 256: return launch_prefill_d<256, prefill_row_tiles(256)>(p, a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -286,7 +286,7 @@ def test_prefill_shapes(G, Hkv, D, Lmax, B):
     poison_padding_(inp["v"], lens)
     plan = binding.prefill_plan(B, Hq, Hkv, D, Lmax, inp["scale"])
     assert plan["rows_per_block"] == 128 and plan["combine"] == 0 and plan["workspace_bytes"] == 0
-    assert plan["grid_main"] == B * Hkv * -(-Lmax * G // 128) and plan["block_main"] == 256
+    assert plan["grid_main"] == B * Hkv * -(-Lmax * G // 128) and plan["block_main"] in (256, 512)
     ref = oracle.causal_prefill(inp["q_seq"], inp["k"], inp["v"], lens, inp["scale"])
     dev = to_dev(inp)
     print("case prefill shapes", G, Hkv, D, Lmax, B, flush=True)
