@@ -163,11 +163,11 @@ mqa_status check_noalloc(const Plan& plan) {
 
 mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_lens, float* out,
                int B, int Hq, int Hkv, int D, int Lmax, float scale, void* stream_ptr,
-               const mqa_decode_opts* opts, int causal, const mqa::PagedCache* paged = nullptr, int T = 1,
+               const mqa_decode_opts* opts, const mqa::PagedCache* paged = nullptr, int T = 1,
                bool noalloc = false) {
     mqa::set_error("");
     Plan plan;
-    mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, causal, &plan, T);
+    mqa_status st = mqa::make_plan(B, Hq, Hkv, D, Lmax, scale, opts, 0, &plan, T);
     if (st != MQA_OK) return st;
     st = mqa::check_pointers(B, Lmax, q, k, v, seq_lens, out);
     if (st != MQA_OK) return st;
@@ -232,9 +232,6 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.GT = plan.GT;
     a.chunk = plan.chunk;
     a.max_splits = plan.max_splits;
-    a.causal = causal;
-    a.B = B;
-    a.nblk = plan.nblk;
     a.window = plan.window;
     a.qk_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
 
@@ -261,7 +258,6 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
         c.GT = plan.GT;
         c.chunk = plan.chunk;
         c.max_splits = plan.max_splits;
-        c.causal = a.causal;
         c.window = a.window;
         e = mqa::launch_combine(plan, c, stream, opts ? static_cast<hipEvent_t>(opts->ev_combine_begin) : nullptr,
                                 opts ? static_cast<hipEvent_t>(opts->ev_combine_end) : nullptr);
@@ -277,21 +273,21 @@ extern "C" {
 mqa_status mqa_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
                                 int D, int Lmax, float scale, void* stream) {
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, nullptr, 0);
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, nullptr);
 }
 
 mqa_status mqa_decode_attention_ex(const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
                                    int D, int Lmax, float scale, void* stream,
                                    const mqa_decode_opts* opts) {
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, 0);
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts);
 }
 
 mqa_status mqa_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
                                         const int32_t* seq_lens, float* out, int B, int Hq, int Hkv,
                                         int D, int Lmax, float scale, void* stream,
                                         const mqa_decode_opts* opts) {
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, 0, nullptr, 1,
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, nullptr, 1,
                true);
 }
 
@@ -304,7 +300,7 @@ mqa_status mqa_decode_attention_window(const void* q, const void* k_cache, const
     }
     mqa_decode_opts o{};
     o.window = window;
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, 0);
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o);
 }
 
 mqa_status mqa_decode_attention_quant(const void* q, const void* k_codes, const void* v_codes,
@@ -320,13 +316,13 @@ mqa_status mqa_decode_attention_quant(const void* q, const void* k_codes, const 
     o.kv_format = kv_format;
     o.k_scale = k_scale;
     o.v_scale = v_scale;
-    return run(q, k_codes, v_codes, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o, 0);
+    return run(q, k_codes, v_codes, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, &o);
 }
 
 mqa_status mqa_decode_attention_multi(const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* seq_lens, float* out, int B, int T, int Hq, int Hkv,
                                       int D, int Lmax, float scale, void* stream, const mqa_decode_opts* opts) {
-    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, 0, nullptr, T);
+    return run(q, k_cache, v_cache, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, nullptr, T);
 }
 
 mqa_status mqa_decode_attention_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -339,7 +335,7 @@ mqa_status mqa_decode_attention_paged(const void* q, const void* k_pages, const 
     int Lmax = 0;
     const mqa_status st = mqa::check_paged(B, block_table, num_pages, page_size, max_blocks, &pc, &Lmax);
     if (st != MQA_OK) return st;
-    return run(q, k_pages, v_pages, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, 0, &pc);
+    return run(q, k_pages, v_pages, seq_lens, out, B, Hq, Hkv, D, Lmax, scale, stream, opts, &pc);
 }
 
 mqa_status mqa_prefill_attention(const void* q_seq, const void* k_cache, const void* v_cache,

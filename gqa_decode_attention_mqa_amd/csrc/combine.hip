@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const long long row = rt / a.T;
     const int tok = (int)(rt % a.T);
     int b, len;
-    row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
+    row_extent(a.seq_lens, row, a.Lmax, &b, &len);
     const int nsplit = chunk_span(a.window, a.chunk, a.max_splits, len, 0).nsplit;
     if (nsplit <= 1) return;  // written directly by the split kernel
 
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void combine_few_kernel(CombineArgs a, long lo
     const int kvh = (int)(unit % a.Hkv);
     const long long gh = out_row(a, row, kvh, g);
     int b, len;
-    row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
+    row_extent(a.seq_lens, row, a.Lmax, &b, &len);
     const int nsplit = chunk_span(a.window, a.chunk, a.max_splits, len, 0).nsplit;
     if (nsplit <= 1) return;  // written directly by the split kernel
 

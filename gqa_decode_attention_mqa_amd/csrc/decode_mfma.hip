@@ -113,9 +113,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     b = __builtin_amdgcn_readfirstlane(b);
     len = __builtin_amdgcn_readfirstlane(len);
     qbase = __builtin_amdgcn_readfirstlane(qbase);
-    // query rows of the unit that exist in q and out (all T * G but in the
-    // last block of a blocked causal row)
-    const int gq = row_tokens(a, row) * a.G;
+    const int gq = a.GT;  // query rows of the unit: T tokens times G heads
     const ChunkSpan span = chunk_span(a.window, a.chunk, a.max_splits, len, s);
     if (s > 0 && span.p0 >= len) return;  // whole workgroup: this chunk is past the end
     // Sliding window: rows lo - 32 < t < lo of the first tile lie before it;
@@ -453,13 +451,12 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // Scale, mask the tail, lazy online softmax; P^T of the tile in registers.
     // Returns whether the running maximum moved (then O must be rescaled by alpha).
     // Query row of this lane's column: token i = (g0 + 16w + li) / G may
-    // attend positions below lim = qbase + i + 1, none if that position is at
-    // or past len (a blocked causal row's tokens past the sequence end); tiles
-    // reaching past tmask hold a position some column must not see, and a row
-    // with such a token masks every tile.
+    // attend positions below lim = qbase + i + 1 (none for a token before the
+    // sequence start); tiles reaching past tmask hold a position some column
+    // must not see.
     const int qpos = qbase + (g0 + 16 * w + li) / a.G;
-    const int lim = qpos < len ? min(p1, qpos + 1) : 0;
-    const int tmask = qbase + a.T > len ? -0x40000000 : p1 - a.T + 1;
+    const int lim = min(p1, qpos + 1);
+    const int tmask = p1 - a.T + 1;
     // 8-bit caches: the logit of a position is scaled by its K row's scale,
     // and its weight in P.V by its V row's scale (l sums the unscaled weights).
     // First part: scale the logits and mask the positions a column must not

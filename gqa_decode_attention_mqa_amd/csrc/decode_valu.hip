@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const int gcnt = min(GB, a.GT - g0);  // query rows (token, head) of this block
 
     int b, len;
-    row_extent(a.seq_lens, row, a.Lmax, a.causal, &b, &len);
+    row_extent(a.seq_lens, row, a.Lmax, &b, &len);
     // Workgroup-uniform; stated so the compiler keeps them (and the buffer
     // descriptors built from them) in scalar registers.
     b = __builtin_amdgcn_readfirstlane(b);

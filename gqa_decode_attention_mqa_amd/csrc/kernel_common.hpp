@@ -19,14 +19,10 @@ typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
 
 // Arguments of the split-K decode kernels, passed by value.
 //
-// A "row" is one sequence of a decode call (sequence r), or in the blocked
-// causal (prefill) form one block of T consecutive positions of a sequence:
-// row r is block nblk - 1 - r / B of sequence r % B (the longest prefixes
-// first), and its token i is position blk * T + i, attending positions
-// 0 .. blk * T + i.  A decode row brings T query tokens (T > 1: several new
-// tokens decoded at once, causal among themselves).  A "unit" is (row, kv
-// head); its T * G query rows (token, head in the group) share the unit's keys
-// and values.  A unit's positions are cut into chunks of `chunk` positions,
+// A "row" is one sequence of a decode call (sequence r), bringing T query
+// tokens (T > 1: several new tokens decoded at once, causal among
+// themselves).  A "unit" is (row, kv head); its T * G query rows (token, head
+// in the group) share the unit's keys and values.  A unit's positions are cut into chunks of `chunk` positions,
 // one workgroup per (unit, chunk, head block).
 struct DecodeArgs {
     const uint16_t* q;         // bf16 [rows, T, Hq, D]
@@ -47,14 +43,10 @@ struct DecodeArgs {
     int Hq, Hkv, D, Lmax, G;
     int T, GT;                 // query tokens per row; query rows per unit (T * G)
     int chunk, max_splits;
-    int causal;                // 0 decode, 2 blocked causal rows (prefill)
-    int B, nblk;               // blocked causal form: sequences, blocks of T positions per sequence
     int window;                // > 0: sliding window, a row of length n attends n-window .. n-1
     int fused;                 // 1: the last chunk of a unit merges the partials itself
     float qk_log2;             // scale * log2(e): logits are kept in base-2 units
 };
-
-constexpr int kCausalBlocked = 2;
 
 // Arguments of the causal prefill kernel (bf16 q, K and V; fp32 out).
 struct PrefillArgs {
@@ -76,45 +68,15 @@ struct CombineArgs {
     int Hq, Hkv, D, Lmax, G;
     int T, GT;
     int chunk, max_splits;
-    int causal;  // always 0: blocked causal rows are never split
     int window;
 };
 
-// Blocked causal form: the sequence and block of a row.
-__device__ __forceinline__ void causal_block(const DecodeArgs& a, long long row, int* b, int* blk) {
-    *b = (int)(row % a.B);
-    *blk = a.nblk - 1 - (int)(row / a.B);
-}
-
-// Index of token i's row in the [*, Hq, D] query and output arrays: row * T + i
-// for decode rows ([B, T, Hq, D]), b * Lmax + blk * T + i for blocked causal
-// rows ([B, Lmax, Hq, D]).
-__device__ __forceinline__ size_t token_row(const DecodeArgs& a, long long row, int i) {
-    if (a.causal == kCausalBlocked) {
-        int b, blk;
-        causal_block(a, row, &b, &blk);
-        return (size_t)b * a.Lmax + (size_t)blk * a.T + i;
-    }
-    return (size_t)row * a.T + i;
-}
-
-// Query tokens of a row that exist in the query and output arrays: T, or
-// fewer in the last block of a blocked causal row (positions past Lmax).
-__device__ __forceinline__ int row_tokens(const DecodeArgs& a, long long row) {
-    if (a.causal == kCausalBlocked) {
-        int b, blk;
-        causal_block(a, row, &b, &blk);
-        return min(a.T, a.Lmax - blk * a.T);
-    }
-    return a.T;
-}
-
 // Query row r (0 .. T*G - 1) of unit (row, kv head kvh) is token r / G of the
 // row's T query tokens and query head kvh * G + r % G.  Element offset of its
-// q (and output) row.
+// q (and output) row in the [rows, T, Hq, D] arrays.
 __device__ __forceinline__ size_t qrow_offset(const DecodeArgs& a, long long row, int kvh, int r) {
     const int i = r / a.G;
-    return (token_row(a, row, i) * a.Hq + (size_t)kvh * a.G + (r - i * a.G)) * (size_t)a.D;
+    return (((size_t)row * a.T + i) * a.Hq + (size_t)kvh * a.G + (r - i * a.G)) * (size_t)a.D;
 }
 // The same for decode rows (combine kernels): [rows, T, Hq, D].
 __device__ __forceinline__ size_t qrow_offset(long long row, int T, int Hq, int G, int D, int kvh, int r) {
@@ -178,34 +140,21 @@ __device__ __forceinline__ const unsigned char* row_ptr(const void* cache, const
 }
 
 // Attended length of a decode row, with seq_lens clamped to [0, Lmax].
-__device__ __forceinline__ void row_extent(const int32_t* seq_lens, long long row, int Lmax,
-                                           int causal, int* b_out, int* len_out) {
+__device__ __forceinline__ void row_extent(const int32_t* seq_lens, long long row, int Lmax, int* b_out,
+                                           int* len_out) {
     const int b = (int)row;
     const int lb = seq_lens[b];
     *b_out = b;
     *len_out = lb < 0 ? 0 : (lb > Lmax ? Lmax : lb);
 }
 
-// Extent of any row: the cache positions it reads (0 .. len - 1) and the
-// position of its token 0 (qbase; token i may attend 0 .. qbase + i).  Decode
-// rows: qbase = len - T (token i is the i-th of the T newest positions; tokens
-// before the sequence start attend nothing).  Blocked causal rows: qbase =
-// blk * T, and len = min(blk * T + T, seq_len) (0 for a block past the end);
-// tokens at or past seq_len attend nothing.
+// Extent of a row: the cache positions it reads (0 .. len - 1) and the
+// position of its token 0, qbase = len - T (token i is the i-th of the T
+// newest positions and may attend 0 .. qbase + i; tokens before the sequence
+// start attend nothing).
 __device__ __forceinline__ void row_extent(const DecodeArgs& a, long long row, int* b_out, int* len_out,
                                            int* qbase_out) {
-    if (a.causal == kCausalBlocked) {
-        int b, blk;
-        causal_block(a, row, &b, &blk);
-        int lb = a.seq_lens[b];
-        lb = lb < 0 ? 0 : (lb > a.Lmax ? a.Lmax : lb);
-        const int t0 = blk * a.T;
-        *b_out = b;
-        *len_out = t0 < lb ? min(t0 + a.T, lb) : 0;
-        *qbase_out = t0;
-        return;
-    }
-    row_extent(a.seq_lens, row, a.Lmax, 0, b_out, len_out);
+    row_extent(a.seq_lens, row, a.Lmax, b_out, len_out);
     *qbase_out = *len_out - a.T;
 }
 

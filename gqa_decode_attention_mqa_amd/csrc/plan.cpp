@@ -115,7 +115,7 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
 
     Plan p;
     p.G = Hq / Hkv;
-    if (causal == kCausalPrefill) {
+    if (causal) {
         // causal prefill: the Lmax * G query rows of each (sequence, kv head)
         // in workgroups of kPrefillRows rows, each streaming its causal prefix
         if (o.variant == MQA_VARIANT_VALU || o.window > 0 || o.kv_format != MQA_KV_BF16 || o.chunk || o.combine)
@@ -138,15 +138,6 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         *plan = p;
         return MQA_OK;
     }
-    if (causal) {
-        // blocked causal prefill: T consecutive positions of one sequence per
-        // row, so T * G query rows (up to six 16-row tiles) share each read
-        // of the block's causal prefix
-        if (o.variant == MQA_VARIANT_VALU || o.window > 0 || o.kv_format != MQA_KV_BF16 || o.chunk || o.combine)
-            return fail(MQA_ERR_ARG, "the prefill form takes no variant, window, cache format, chunk or combine option");
-        T = p.G >= kMfmaMaxHeads ? 1 : kMfmaMaxHeads / p.G;
-        o.variant = MQA_VARIANT_MFMA;
-    }
     p.T = T;
     p.GT = T * p.G;  // query rows sharing one kv head: what the head tiles hold
     p.variant = o.variant;
@@ -165,8 +156,7 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     }
     p.head_blocks = (int)ceil_div(p.GT, p.heads_per_block);
 
-    p.nblk = causal ? (int)ceil_div(Lmax, T) : 0;
-    p.rows = causal ? (long long)B * p.nblk : (long long)B;
+    p.rows = B;
     const long long units = p.rows * Hkv * p.head_blocks;
 
     // Positions one row attends: Lmax, or W with a sliding window of W
@@ -178,11 +168,7 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     p.window = o.window;
     p.kv_format = o.kv_format;
 
-    if (causal) {
-        // one chunk per row: a block's prefix is read once, and the longest
-        // prefixes are dispatched first (row order) to balance the grid
-        p.chunk = (int)round_up(span > 0 ? span : 1, kChunkQuantum);
-    } else if (o.chunk > 0) {
+    if (o.chunk > 0) {
         p.chunk = o.chunk;
     } else if (units == 0 || span == 0) {
         p.chunk = kChunkQuantum;

@@ -76,8 +76,7 @@ struct Plan {
     int window = 0;                  // sliding window (0 = none)
     int kv_format = 0;               // mqa_kv_format of the cache
     int combine = 0;                 // 0 none, 1 separate kernel, 2 fused
-    long long rows = 0;              // rows: B (decode) or B * nblk (blocked causal prefill)
-    int nblk = 0;                    // blocked causal prefill: blocks of T positions per sequence
+    long long rows = 0;              // rows (sequences) of the call: B
     int row_blocks = 0;              // causal prefill: workgroups of kPrefillRows query rows per
                                      // (sequence, kv head)
     long long grid_main = 0;         // workgroups along x of the split kernel
@@ -97,11 +96,8 @@ const char* last_error();
 
 // Checks sizes, scale and options; on success fills `plan`.  causal = 0 plans
 // a decode call (B rows of T query tokens, T = 1 for a decode step); causal =
-// 2 plans the blocked causal (prefill) form: each sequence's positions in
-// blocks of T = floor(kMfmaMaxHeads / G) (at least 1) query tokens, B * nblk
-// rows, one chunk per row (no split, no merge), the matrix-core kernel;
-// causal = kCausalPrefill plans the causal prefill kernel (B * Hkv *
-// row_blocks workgroups of kPrefillRows query rows, no split, no merge).
+// kCausalPrefill plans the causal prefill kernel (B * Hkv * row_blocks
+// workgroups of kPrefillRows query rows, no split, no merge).
 mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                      const mqa_decode_opts* opts, int causal, Plan* plan, int T = 1);
 
