@@ -298,6 +298,20 @@ def test_prefill_shapes(G, Hkv, D, Lmax, B):
         assert torch.equal(out[b, int(lens[b]):].cpu(), torch.zeros_like(out[b, int(lens[b]):].cpu()))
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.37])
+def test_prefill_scale_signs(scale):
+    """The prefill kernel folds the scale into each weight's exponent: a negative scale flips q,
+    a zero scale gives equal weights over each prefix (masked positions still excluded)."""
+    w = Workload("pf-scale", B=2, Hq=8, Hkv=2, D=128, Lmax=300, seed=1500)
+    inp = make_prefill_inputs(w, poison_padding=True)
+    ref = oracle.causal_prefill(inp["q_seq"], inp["k"], inp["v"], inp["seq_lens"], scale)
+    dev = to_dev(inp)
+    print("case prefill scale", scale, flush=True)
+    out = binding.prefill(dev["q_seq"], dev["k"], dev["v"], dev["seq_lens"], scale)
+    torch.cuda.synchronize()
+    check_close(out, ref, "prefill scale %g" % scale)
+
+
 @pytest.mark.parametrize("name", ["palm", "gqa70b"])
 def test_prefill_full_size_rows(name):
     """Prefill of a full-size batch's sequences (the first four of the workload's B, every
