@@ -20,7 +20,7 @@ namespace {
 using mqa::Plan;
 
 // Split-K scratch per (device, stream), grown on demand: one buffer for the
-// partial outputs and LSEs, and a separate one for the fused combine's arrival
+// partial outputs and LSEs, and a separate one for the fused combine's
 // counters.  The counters are zeroed when allocated and every call leaves them
 // at zero, so nothing else may ever write that buffer.
 struct Workspace {
@@ -223,6 +223,10 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     }
     a.units = plan.rows * Hkv;
     a.fused = plan.combine == 2 ? 1 : 0;
+    a.fused_wait = mqa::kFusedWaitTicks;
+    if (a.fused) {
+        if (const char* t = std::getenv("MQA_FUSED_WAIT_TICKS")) a.fused_wait = (uint32_t)std::strtoul(t, nullptr, 10);
+    }
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.D = D;

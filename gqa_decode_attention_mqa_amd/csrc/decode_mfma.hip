@@ -734,11 +734,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         }
     }
     if (direct || !a.fused) return;
-    // ---- fused combine: the last chunk of this (row, kv head, head block) merges all partials
+    // ---- fused combine: the chunks of this (row, kv head, head block) share the merge
     __syncthreads();
-    int* flag = reinterpret_cast<int*>(smem);
-    if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, flag)) return;
-    fused_combine(a, unit, row, kvh, nsplit, g0, gcnt);
+    fused_tail(a, unit, row, kvh, nsplit, g0, gcnt, a.counters + (unit * gridDim.y + blockIdx.y) * kFusedCountersPerUnit,
+               reinterpret_cast<int*>(smem));
 }
 
 template <int D, int NG, int FMT>

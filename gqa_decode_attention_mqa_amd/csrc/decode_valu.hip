@@ -373,9 +373,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         }
     }
     if (direct || !a.fused) return;
-    // Fused combine: the last chunk of this (row, kv head, head block) merges all partials.
-    if (!arrive_last(a.counters + unit * gridDim.y + blockIdx.y, nsplit, &s_flag)) return;
-    fused_combine(a, unit, row, kvh, nsplit, g0, gcnt);
+    // Fused combine: the chunks of this (row, kv head, head block) share the merge.
+    fused_tail(a, unit, row, kvh, nsplit, g0, gcnt, a.counters + (unit * gridDim.y + blockIdx.y) * kFusedCountersPerUnit,
+               &s_flag);
 }
 
 template <int D, int GB, int FMT>

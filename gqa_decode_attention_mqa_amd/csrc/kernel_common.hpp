@@ -37,14 +37,15 @@ struct DecodeArgs {
     const int32_t* block_table;  // paged cache: [B, max_blocks] physical page per block of
                                  // 2^page_shift positions; NULL for the contiguous layout
     int page_shift, max_blocks, num_pages;
-    uint32_t* counters;        // [rows * Hkv * head_blocks] arrival counters (fused combine);
-                               // zero between calls: the last arriving chunk resets its counter
+    uint32_t* counters;        // [rows * Hkv * head_blocks, kFusedCountersPerUnit] counters of the
+                               // fused combine; zero between calls (the last arriving chunk wraps its counter)
     long long units;           // rows * Hkv
     int Hq, Hkv, D, Lmax, G;
     int T, GT;                 // query tokens per row; query rows per unit (T * G)
     int chunk, max_splits;
     int window;                // > 0: sliding window, a row of length n attends n-window .. n-1
-    int fused;                 // 1: the last chunk of a unit merges the partials itself
+    int fused;                 // 1: the chunks of a unit merge the partials themselves
+    uint32_t fused_wait;       // bound of the fused combine's wait, in 100 MHz real-time ticks
     float qk_log2;             // scale * log2(e): logits are kept in base-2 units
 };
 
@@ -431,55 +432,99 @@ __device__ __forceinline__ void fused_merge_batch(const DecodeArgs& a, __amdgpu_
 
 template <int S, int IT>
 __device__ __forceinline__ void fused_merge_all(const DecodeArgs& a, __amdgpu_buffer_rsrc_t ro,
-                                                __amdgpu_buffer_rsrc_t rm, long long row, int kvh, int g0, int items,
-                                                int nsplit) {
+                                                __amdgpu_buffer_rsrc_t rm, long long row, int kvh, int g0, int begin,
+                                                int end, int nsplit) {
     const int stride = blockDim.x;
-    for (int idx0 = threadIdx.x; idx0 < items; idx0 += IT * stride)
-        fused_merge_batch<S, IT>(a, ro, rm, row, kvh, g0, items, idx0, stride, nsplit);
+    for (int idx0 = begin + threadIdx.x; idx0 < end; idx0 += IT * stride)
+        fused_merge_batch<S, IT>(a, ro, rm, row, kvh, g0, end, idx0, stride, nsplit);
 }
 
-// Fused log-sum-exp merge, run by the last chunk of a unit to arrive, over the
-// query rows g0 .. g0 + gcnt - 1 of the unit: every thread of the workgroup
-// takes (query row, 8-value slot) items, a batch of them at a time (about 144
-// registers of loads in flight per thread).  The caller has written its own
-// partial with coherent stores; the planner keeps nsplit <= 8 and the unit's
+// Fused log-sum-exp merge of the items begin .. end - 1 of a unit (an item is
+// one (query row, 8-value slot) of the query rows g0 .. g0 + gcnt - 1): every
+// thread of the workgroup takes items, a batch of them at a time (about 144
+// registers of loads in flight per thread).  Every chunk's partial has been
+// written with coherent stores; the planner keeps nsplit <= 8 and the unit's
 // partials within a 2 GiB buffer range for this form.
-__device__ __forceinline__ void fused_combine(const DecodeArgs& a, long long unit, long long row, int kvh,
-                                              int nsplit, int g0, int gcnt) {
+__device__ __forceinline__ void fused_combine_part(const DecodeArgs& a, long long unit, long long row, int kvh,
+                                                   int nsplit, int g0, int begin, int end) {
     const int D = a.D;
     const size_t first = (size_t)unit * a.max_splits * a.GT;  // (unit, split 0, query row 0)
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o + first * D, a.max_splits * a.GT * D * 2);
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.part_ml + first, a.max_splits * a.GT * 8);
-    const int items = gcnt * (D / 8);
     if (nsplit <= 2)
-        fused_merge_all<2, 8>(a, ro, rm, row, kvh, g0, items, nsplit);
+        fused_merge_all<2, 8>(a, ro, rm, row, kvh, g0, begin, end, nsplit);
     else if (nsplit <= 4)
-        fused_merge_all<4, 6>(a, ro, rm, row, kvh, g0, items, nsplit);
+        fused_merge_all<4, 6>(a, ro, rm, row, kvh, g0, begin, end, nsplit);
     else
-        fused_merge_all<kFusedMaxSplits, 3>(a, ro, rm, row, kvh, g0, items, nsplit);
+        fused_merge_all<kFusedMaxSplits, 3>(a, ro, rm, row, kvh, g0, begin, end, nsplit);
 }
 
-// Arrival bookkeeping of the fused combine: returns true in every thread of
-// the last workgroup to finish a chunk of this unit (and resets the counter).
-// The caller must have written its partial with the coherent stores above.
-// Each wave first waits until its stores are complete (acknowledged at the
-// device's coherence point), so by the time the counter shows the last
-// arrival every partial is readable with coherent loads.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, int nsplit, int* flag_lds) {
+// The fused combine's tail, run by every workgroup of a unit after it wrote its
+// partial with the coherent stores above.  The unit's items are cut into
+// nsplit equal parts, and part k is merged by the k-th workgroup to arrive:
+//   - arrival: k = counter[0], incremented with wrap-around at nsplit - 1, so
+//     the last arrival (k = nsplit - 1) leaves it at zero for the next call;
+//   - every earlier arrival waits until counter[0] <= k, which first holds when
+//     the last one has wrapped it (the chunks of a unit run side by side when
+//     the grid fits the device, and finish within microseconds of each other);
+//   - a wait is bounded (a.fused_wait).  One that times out records its part
+//     in counter[1] and reads counter[0] again: if the last arrival has come
+//     meanwhile it merges the part itself, otherwise the last arrival, which
+//     takes and clears counter[1], merges it.  Either way every part is merged
+//     at least once after all partials are written; a part merged twice is
+//     written twice with the same bits (a bit left behind in counter[1] makes
+//     the next call merge one part twice, no more).
+// Each part is merged by the same code whoever takes it, so the output does
+// not depend on the order of arrival.  Before arriving, each wave waits until
+// its stores are complete (acknowledged at the device's coherence point), so
+// once counter[0] shows every arrival each partial is readable with coherent
+// loads.
+__device__ __forceinline__ void fused_tail(const DecodeArgs& a, long long unit, long long row, int kvh, int nsplit,
+                                           int g0, int gcnt, uint32_t* counter, int* flag_lds) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
     __syncthreads();
+    const uint32_t n = (uint32_t)nsplit;
+    uint32_t given_up = 0;  // thread 0 of the last arrival: parts recorded in counter[1]
     if (threadIdx.x == 0) {
-        const uint32_t old = atomicAdd(counter, 1u);
-        const int last = old == (uint32_t)(nsplit - 1);
-        if (last) atomicExch(counter, 0u);
-        *flag_lds = last;
+        const uint32_t k = atomicInc(&counter[0], n - 1);
+        uint32_t mine = 1u << k;  // parts this workgroup merges
+        if (k == n - 1) {
+            // its value is first needed after this workgroup's own part, so
+            // the exchange's round trip overlaps that part's loads
+            given_up = atomicExch(&counter[1], 0u);
+        } else {
+            const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(&counter[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > k) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 > a.fused_wait) {
+                    // sequentially consistent, so the record is in place before
+                    // counter[0] is read again (rare: a wait that timed out)
+                    __hip_atomic_fetch_or(&counter[1], mine, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT);
+                    if (__hip_atomic_fetch_add(&counter[0], 0u, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT) > k)
+                        mine = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        *flag_lds = (int)mine;
     }
     __syncthreads();
-    const bool last = *flag_lds != 0;
+    const uint32_t mine = (uint32_t)flag_lds[0];
     asm volatile("" ::: "memory");
-    return last;
+    const int items = gcnt * (a.D / 8);
+    for (int q = 0; q < nsplit; ++q)
+        if ((mine >> q) & 1u)
+            fused_combine_part(a, unit, row, kvh, nsplit, g0, items * q / nsplit, items * (q + 1) / nsplit);
+    if (mine != 1u << (nsplit - 1)) return;  // not the last arrival (uniform across the workgroup)
+    __syncthreads();  // every thread has read flag_lds[0]
+    if (threadIdx.x == 0) flag_lds[0] = (int)given_up;
+    __syncthreads();
+    const uint32_t more = (uint32_t)flag_lds[0] & (mine - 1u);  // parts 0 .. nsplit - 2
+    for (int q = 0; q < nsplit - 1; ++q)
+        if ((more >> q) & 1u)
+            fused_combine_part(a, unit, row, kvh, nsplit, g0, items * q / nsplit, items * (q + 1) / nsplit);
 }
 
 __device__ __forceinline__ u32x4_t load_u32x4(const uint16_t* p) {

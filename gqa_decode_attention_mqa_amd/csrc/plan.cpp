@@ -203,10 +203,10 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         if (o.combine == 2 && !fusable)
             return fail(MQA_ERR_ARG, "the fused combine handles at most 8 chunks per sequence "
                                      "(and max_splits * T * G * D * 2 < 2^31)");
-        // Default: the separate combine kernel.  In the fused form the last
-        // workgroup of each unit merges the partials at the tail of the split
-        // kernel, which measured slower on MI355X (PaLM-shaped MQA step
-        // 39.7 us against 32.4 us with the separate kernel).
+        // Default: the separate combine kernel.  In the fused form the chunks
+        // of each unit merge the partials at the tail of the split kernel; on
+        // MI355X it was no faster (PaLM-shaped MQA: 29.84 us per step by wall
+        // clock for both forms), and its waits assume the grid fits the device.
         p.combine = (o.combine == 0) ? 1 : o.combine;
         if (p.combine != 1)
             p.grid_combine = 0;
@@ -220,7 +220,7 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         p.part_o_offset = 0;  // fp16 partial rows, then {lse, e} pairs
         p.part_ml_offset = round_up((long long)(parts * D * sizeof(uint16_t)), 256);
         p.workspace_bytes = p.part_ml_offset + round_up((long long)(parts * 2 * sizeof(float)), 256);
-        p.counters = (p.combine == 2) ? (size_t)p.rows * Hkv * p.head_blocks : 0;
+        p.counters = (p.combine == 2) ? (size_t)p.rows * Hkv * p.head_blocks * kFusedCountersPerUnit : 0;
     }
     *plan = p;
     return MQA_OK;

@@ -46,10 +46,17 @@ constexpr int kCombineFewMaxSplits = 8;
 // Most chunks per unit the fused combine handles: the same register-resident
 // merge of every chunk's slot as the few-chunk kernel.
 constexpr int kFusedMaxSplits = kCombineFewMaxSplits;
+// uint32 counters per unit of the fused combine (arrivals and the merge parts
+// given up by timed-out waits; padded to 16 bytes).
+constexpr int kFusedCountersPerUnit = 4;
+// How long a workgroup of the fused combine waits for the other chunks of its
+// unit before leaving its part of the merge to the last one: 20 us of the
+// 100 MHz real-time counter.  MQA_FUSED_WAIT_TICKS overrides it (tests force
+// the timed-out path with 0).
+constexpr unsigned kFusedWaitTicks = 2000;
 // make_plan's `causal` argument for the causal prefill kernel.
 constexpr int kCausalPrefill = 3;
-// Query rows per workgroup of the causal prefill kernel: four compute waves of
-// 32 rows (two 16-row tiles of the matrix products each).
+// Query rows per workgroup of the causal prefill kernel.
 constexpr int kPrefillRows = 128;
 // 16-row tiles of query rows per compute wave of the prefill kernel (the
 // workgroup has kPrefillRows / (16 * tiles) compute waves), both forms at two
@@ -85,9 +92,9 @@ struct Plan {
     size_t workspace_bytes = 0;      // partial outputs + partial LSEs
     size_t part_o_offset = 0;        // byte offsets inside the workspace
     size_t part_ml_offset = 0;
-    size_t counters = 0;             // arrival counters (uint32, one per (row, kv head, head
-                                     // block)), kept in a buffer of their own that is zero
-                                     // between calls
+    size_t counters = 0;             // fused-combine counters (uint32, kFusedCountersPerUnit per
+                                     // (row, kv head, head block)), kept in a buffer of their own
+                                     // that is zero between calls
 };
 
 // Thread-local last-error text.

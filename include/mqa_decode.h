@@ -36,8 +36,9 @@
  * enqueued on `stream`.  Split-K scratch (partial outputs and log-sum-exps) is
  * owned by the library, cached per (device, stream), grown on demand with
  * hipMalloc (which synchronises the device) and freed by
- * mqa_release_workspaces(); so are the fused combine's arrival counters,
- * zeroed once when allocated and left at zero by every call.  Warm the
+ * mqa_release_workspaces(); so are the fused combine's counters, zeroed
+ * once when allocated and left at zero by every call (up to a merge part
+ * recorded by a wait that timed out, which a later call merges again).  Warm the
  * library up with a call of the largest shape before capturing a graph.
  *
  * Errors: every argument check happens on the host before any HIP call, so
@@ -94,10 +95,13 @@ typedef struct mqa_decode_opts {
                              a positive multiple of 128 when set.                        */
     int combine;          /* 0 = planner's choice (the separate kernel),
                              1 = separate combine kernel,
-                             2 = combine fused into the split kernel: the last chunk of
-                             each (sequence, kv head) to finish merges the partials
-                             (at most 8 chunks per sequence, else MQA_ERR_ARG); both
-                             merges give the same bits                                   */
+                             2 = combine fused into the split kernel: the chunks of each
+                             (sequence, kv head) merge the partials once all have
+                             finished, the k-th to finish taking the k-th part of the
+                             heads (a bounded wait, 20 us by default or
+                             MQA_FUSED_WAIT_TICKS ticks of 10 ns; a part whose wait
+                             timed out goes to the last chunk); at most 8 chunks per
+                             sequence, else MQA_ERR_ARG; both merges give the same bits */
     void *ev_main_begin;  /* optional hipEvent_t pair recorded by the split-K kernel's own
                              dispatch (hipExtLaunchKernelGGL) at its start and end, so  */
     void *ev_main_end;    /* their interval is that kernel's execution time alone      */

@@ -13,6 +13,7 @@ five full-size workloads run in the launch configuration the benchmark uses,
 every sequence against the oracle.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -147,6 +148,42 @@ def test_fused_combine_reads_this_calls_partials(variant):
                              combine="fused")
         torch.cuda.synchronize()
         check_close(out, ref, "fused alternate %s iteration %d" % (variant, it))
+
+
+@pytest.mark.parametrize("variant", ["mfma", "valu"])
+def test_fused_combine_with_timed_out_waits(variant):
+    """The fused combine's bounded wait, forced to time out at once (MQA_FUSED_WAIT_TICKS=0, read
+    by the library on every call): workgroups that give up their part of the merge either merge it
+    themselves (the last chunk came meanwhile) or leave it to the last one.  Every call must still
+    give the separate merge's bits, and so must ordinary fused calls afterwards (a part left
+    recorded in the counters only makes a later call merge it twice)."""
+    ws = [Workload("fw%d" % i, B=8, Hq=48, Hkv=1, D=256, Lmax=1024, seed=1230 + i, len_lo=300, len_hi=1024)
+          for i in range(2)]
+    cases = []
+    for w in ws:
+        dev = to_dev(make_inputs(w, poison_padding=True))
+        ref = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant,
+                             chunk=128, combine="separate")
+        cases.append((dev, ref))
+    torch.cuda.synchronize()
+    old = os.environ.get("MQA_FUSED_WAIT_TICKS")
+    try:
+        for it in range(16):
+            if it < 8:
+                os.environ["MQA_FUSED_WAIT_TICKS"] = "0"
+            else:  # the default wait
+                os.environ.pop("MQA_FUSED_WAIT_TICKS", None)
+            dev, ref = cases[it % 2]
+            print("case fused timed-out waits", variant, it, flush=True)
+            out = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], variant=variant,
+                                 chunk=128, combine="fused")
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), "fused merge with timed-out waits, %s iteration %d" % (variant, it)
+    finally:
+        if old is None:
+            os.environ.pop("MQA_FUSED_WAIT_TICKS", None)
+        else:
+            os.environ["MQA_FUSED_WAIT_TICKS"] = old
 
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
