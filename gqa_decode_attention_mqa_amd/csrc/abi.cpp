@@ -388,7 +388,7 @@ mqa_status mqa_prefill_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale
         info->grid_combine = p.grid_combine;
         info->workspace_bytes = p.workspace_bytes;
     }
-    if (rows_per_block) *rows_per_block = mqa::kPrefillRows;
+    if (rows_per_block) *rows_per_block = p.heads_per_block;
     return MQA_OK;
 }
 

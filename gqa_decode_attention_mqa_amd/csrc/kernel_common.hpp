@@ -57,7 +57,7 @@ struct PrefillArgs {
     const int32_t* seq_lens;   // [B], clamped to [0, Lmax]
     float* out;                // fp32 [B, Lmax, Hq, D]
     int B, Hq, Hkv, D, Lmax, G;
-    int row_blocks;            // workgroups per (sequence, kv head): ceil(Lmax * G / kPrefillRows)
+    int row_blocks;            // workgroups per (sequence, kv head): ceil(Lmax * G / prefill_rows(D))
     float qk_log2;             // scale * log2(e)
 };
 

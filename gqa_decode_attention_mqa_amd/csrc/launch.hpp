@@ -21,7 +21,7 @@ hipError_t launch_decode_valu(const Plan& p, const DecodeArgs& a, hipStream_t st
 // above, recorded around the merge kernel.
 hipError_t launch_combine(const Plan& p, const CombineArgs& a, hipStream_t stream, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
-// Causal prefill on matrix cores: kPrefillRows query rows of one (sequence,
+// Causal prefill on matrix cores: prefill_rows(D) query rows of one (sequence,
 // kv head) per workgroup, the causal prefix streamed through an LDS ring.
 hipError_t launch_prefill_mfma(const Plan& p, const PrefillArgs& a, hipStream_t stream);
 // Streaming-read calibration: `workgroups` workgroups each read one

@@ -117,22 +117,22 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     p.G = Hq / Hkv;
     if (causal) {
         // causal prefill: the Lmax * G query rows of each (sequence, kv head)
-        // in workgroups of kPrefillRows rows, each streaming its causal prefix
+        // in workgroups of prefill_rows(D) rows, each streaming its causal prefix
         if (o.variant == MQA_VARIANT_VALU || o.window > 0 || o.kv_format != MQA_KV_BF16 || o.chunk || o.combine)
             return fail(MQA_ERR_ARG, "the prefill form takes no variant, window, cache format, chunk or combine option");
-        if ((long long)Lmax * p.G > 0x7FFFFFFFLL - kPrefillRows)
+        if ((long long)Lmax * p.G > 0x7FFFFFFFLL - kPrefillMaxRows)
             return fail(MQA_ERR_UNSUPPORTED, "Lmax * Hq / Hkv too large for the prefill kernel");
         p.variant = MQA_VARIANT_MFMA;
         p.T = 1;
         p.GT = p.G;
-        p.heads_per_block = kPrefillRows;
+        p.heads_per_block = prefill_rows(D);  // query rows per workgroup
         p.head_blocks = 1;
         p.rows = B;
-        p.row_blocks = (int)ceil_div((long long)Lmax * p.G, kPrefillRows);
+        p.row_blocks = (int)ceil_div((long long)Lmax * p.G, prefill_rows(D));
         p.chunk = (int)round_up(Lmax > 0 ? Lmax : 1, kChunkQuantum);
         p.max_splits = 1;
         p.grid_main = (long long)B * Hkv * p.row_blocks;
-        p.block_main = 64 * (kPrefillRows / (16 * prefill_row_tiles(D)));
+        p.block_main = 64 * (prefill_rows(D) / (16 * prefill_row_tiles(D)));
         if (p.grid_main > kMaxGrid)
             return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (grid limit)");
         *plan = p;

@@ -56,17 +56,24 @@ constexpr int kFusedCountersPerUnit = 4;
 constexpr unsigned kFusedWaitTicks = 2000;
 // make_plan's `causal` argument for the causal prefill kernel.
 constexpr int kCausalPrefill = 3;
-// Query rows per workgroup of the causal prefill kernel.
-constexpr int kPrefillRows = 128;
-// 16-row tiles of query rows per compute wave of the prefill kernel (the
-// workgroup has kPrefillRows / (16 * tiles) compute waves), both forms at two
-// waves per SIMD.  D = 256: one tile per wave, eight waves (two tiles per wave
-// need more registers than two waves per SIMD leave: measured on MI355X,
-// PaLM-shaped prefill 8.6 ms against 10.2 ms at one wave per SIMD).  D <= 128:
-// two tiles per wave (each K and V^T read feeds two products) and two
-// workgroups per CU (B=32, Hkv=8, D=128, 4096 positions: 10.1 ms against
-// 11.1 ms with one tile per wave).
+// Causal prefill kernel, per head size D: query rows per workgroup, 16-row
+// tiles of them per compute wave (the workgroup has rows / (16 * tiles)
+// compute waves), positions per K/V tile and stages of the LDS ring.
+// Measured on MI355X, PaLM-shaped (D = 256) and gqa70b-shaped (D = 128)
+// prefills:
+//   - D = 256: one tile per wave, eight waves; two tiles per wave need more
+//     registers than two waves per SIMD leave (8.6 ms against 10.2 ms at one
+//     wave per SIMD);
+//   - D <= 128: two tiles per wave (each K and V^T read feeds two products),
+//     against one: 10.1 ms against 11.1 ms;
+//   - two stages of 64-position tiles: 256 rows per workgroup, 32-position
+//     tiles or deeper rings were slower or within 2 % (LDS budget: 2 * stages
+//     * step * D * 2 bytes per workgroup, two workgroups per CU at D <= 128).
+constexpr int prefill_rows(int D) { return D > 0 ? 128 : 0; }
 constexpr int prefill_row_tiles(int D) { return D == 256 ? 1 : 2; }
+constexpr int prefill_step(int D) { return D > 0 ? 64 : 0; }
+constexpr int prefill_stages(int D) { return D > 0 ? 2 : 0; }
+constexpr int kPrefillMaxRows = 256;  // the most rows any head size's workgroup takes
 // Query heads per workgroup of the few-chunk combine (256 threads, D/8 each).
 constexpr int combine_heads_per_block(int D) { return 2048 / D; }
 
@@ -84,7 +91,7 @@ struct Plan {
     int kv_format = 0;               // mqa_kv_format of the cache
     int combine = 0;                 // 0 none, 1 separate kernel, 2 fused
     long long rows = 0;              // rows (sequences) of the call: B
-    int row_blocks = 0;              // causal prefill: workgroups of kPrefillRows query rows per
+    int row_blocks = 0;              // causal prefill: workgroups of prefill_rows(D) query rows per
                                      // (sequence, kv head)
     long long grid_main = 0;         // workgroups along x of the split kernel
     int block_main = 256;
@@ -104,7 +111,7 @@ const char* last_error();
 // Checks sizes, scale and options; on success fills `plan`.  causal = 0 plans
 // a decode call (B rows of T query tokens, T = 1 for a decode step); causal =
 // kCausalPrefill plans the causal prefill kernel (B * Hkv * row_blocks
-// workgroups of kPrefillRows query rows, no split, no merge).
+// workgroups of prefill_rows(D) query rows, no split, no merge).
 mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                      const mqa_decode_opts* opts, int causal, Plan* plan, int T = 1);
 

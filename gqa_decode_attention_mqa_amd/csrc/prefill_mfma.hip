@@ -7,18 +7,19 @@
 //
 // The query rows of one (sequence b, kv head) are the (position t, head g in
 // the group) pairs in token-major order, r = t * G + g; row r attends
-// positions 0 .. r / G.  A workgroup owns 128 consecutive rows and four
-// compute waves, one per SIMD, each with 32 rows (two 16-row tiles of the
-// matrix products).  The workgroup's causal prefix is streamed through a
-// two-stage LDS ring of 64-position K and V tiles, loaded by all four waves
-// with direct buffer-to-LDS loads while the previous tile is being used.
-// Per tile and wave:
+// positions 0 .. r / G.  A workgroup owns ROWS consecutive rows and
+// ROWS / (16 RT) compute waves, each with RT 16-row tiles of the matrix
+// products (the configuration per head size is prefill_rows, _row_tiles,
+// _step and _stages).  The workgroup's causal prefix is streamed through an
+// LDS ring of STAGES slots of STEP-position K and V tiles, loaded by all
+// waves with direct buffer-to-LDS loads, STAGES - 1 tiles ahead of the one
+// in use.  Per tile and wave:
 //   * S^T = K q^T on 16x16x32 bf16 products: every K read (16 positions x 32
-//     of d) feeds both row tiles;
+//     of d) feeds the wave's RT row tiles;
 //   * a base-2 online softmax with lazy rescaling, the row maximum reduced
 //     over the four lane groups that hold a row;
 //   * O^T += V^T P^T with the V^T operand from gfx950's transposing LDS
-//     reads; every V^T read feeds both row tiles.
+//     reads; every V^T read feeds the RT row tiles.
 // Tiles that lie wholly below the wave's first row skip the causal mask.
 // Rows at or past the sequence length are written as zeros.
 #include <atomic>
@@ -29,29 +30,42 @@
 
 namespace mqa {
 
-template <int D, int RT>
+template <int D>
 struct PrefillCfg {
-    static constexpr int WAVES = kPrefillRows / (16 * RT);  // compute waves, RT 16-row tiles each
-    static constexpr int STEP = 64;                  // positions per K/V tile
-    static constexpr int ROWB = D * 2;               // bytes of one cached row
-    static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
-    static constexpr int TILE_BYTES = STEP * ROWB;   // K (or V) bytes of a tile
+    static constexpr int ROWS = prefill_rows(D);       // query rows per workgroup
+    static constexpr int RT = prefill_row_tiles(D);    // 16-row tiles per compute wave
+    static constexpr int WAVES = ROWS / (16 * RT);     // compute waves
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int STEP = prefill_step(D);       // positions per K/V tile
+    static constexpr int STAGES = prefill_stages(D);   // LDS ring slots
+    static constexpr int NQ = STEP / 16;               // 16-position blocks of a tile (q.K products)
+    static constexpr int NKB = STEP / 32;              // 32-position blocks of a tile (P.V products)
+    static constexpr int ROWB = D * 2;                 // bytes of one cached row
+    static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+    static constexpr int TILE_BYTES = STEP * ROWB;     // K (or V) bytes of a tile
     static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;  // the tile in use and the one landing
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static constexpr int LOADS = TILE_BYTES / 1024;    // wave-wide 16-byte loads per K (or V) tile
     static constexpr int LPW = LOADS / WAVES;          // of them, per wave
     static constexpr int KS = D / 32;                  // k-steps of q.K
     static constexpr int MT = D / 16;                  // 16-row tiles of O^T (along d)
     static constexpr int MH = MT / 2;                  // P.V runs over two halves of d
     static_assert(RT == 1 || RT == 2, "one or two 16-row tiles per wave");
-    static_assert(LOADS % WAVES == 0, "every wave issues the same number of loads");
-    static_assert(2 * LPW <= 63, "a tile's loads fit a wave's counter");
+    static_assert(ROWS % (16 * RT) == 0 && THREADS <= 1024, "whole waves of row tiles");
+    static_assert(STEP == 32 || STEP == 64, "tiles of 32 or 64 positions");
+    static_assert(STAGES >= 2, "a tile in use and one landing");
+    static_assert(LOADS % WAVES == 0 && LPW > 0, "every wave issues the same number of loads");
+    static_assert(2 * LPW * (STAGES - 1) <= 63, "the ring's loads in flight fit a wave's counter");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-template <int D, int RT>
-__global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
-    using C = PrefillCfg<D, RT>;
+// Launch bound 512 threads even for smaller workgroups: the register budget
+// of two waves per SIMD, so that two smaller workgroups share a CU.
+template <int D>
+__global__ __launch_bounds__(PrefillCfg<D>::THREADS > 512 ? PrefillCfg<D>::THREADS : 512) void prefill_mfma_kernel(
+    PrefillArgs a) {
+    using C = PrefillCfg<D>;
+    constexpr int RT = C::RT;
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
 
     const int tid = threadIdx.x;
@@ -80,12 +94,12 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
     const int nrows = a.Lmax * a.G;  // query rows of (b, kvh)
     int len = a.seq_lens[b];
     len = __builtin_amdgcn_readfirstlane(len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len));
-    const int r0 = blk * kPrefillRows;
-    const int rlast = min(r0 + kPrefillRows, nrows) - 1;
+    const int r0 = blk * C::ROWS;
+    const int rlast = min(r0 + C::ROWS, nrows) - 1;
     const int kv_end = min(rlast / a.G + 1, len);  // positions any row of the block attends
     const int ntiles = kv_end > 0 ? (kv_end + C::STEP - 1) / C::STEP : 0;
 
-    // This lane's rows r = r0 + 32w + 16rt + li (rt = 0, 1): token t = r / G
+    // This lane's rows r = r0 + 16 (RT w + rt) + li: token t = r / G
     // attends positions below lim = min(t + 1, len); rows with t >= len are
     // computed like the others and written as zeros.  orow indexes the row in
     // q and out ([B, Lmax, Hq, D]), -1 past the last row.
@@ -116,19 +130,20 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
             qb[rt][ks] = orow[rt] < 0 ? u32x4_t{0u, 0u, 0u, 0u} : *reinterpret_cast<const u32x4_t*>(qp + 32 * ks);
     }
 
-    // Loads of tile `tile` into stage tile % 2: load jj (0 .. LOADS-1) covers
-    // 1 KB of the K tile and, with a second load, the same 1 KB of the V tile;
-    // wave w issues jj = w, w + 4, ....  Rows at or past kv_end are outside
-    // the buffer range and arrive as zeros.
+    // Loads of tile `tile` into stage tile % STAGES: load jj (0 .. LOADS-1)
+    // covers 1 KB of the K tile and, with a second load, the same 1 KB of the
+    // V tile; wave w issues jj = w, w + WAVES, ....  Rows at or past kv_end
+    // are outside the buffer range and arrive as zeros, so a tile past the
+    // last is loaded too (as zeros): every wave has the same loads in flight.
     const int rowbytes = a.Hkv * C::ROWB;  // bytes between consecutive positions
     const size_t kv0 = ((size_t)b * a.Lmax * a.Hkv + kvh) * D;
     auto issue_tile = [&](int tile) {
         const int t0 = tile * C::STEP;
-        const int rows = min(C::STEP, kv_end - t0);
+        const int rows = max(0, min(C::STEP, kv_end - t0));
         const size_t off = kv0 + (size_t)t0 * a.Hkv * D;
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + off, rows * rowbytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.v + off, rows * rowbytes);
-        unsigned char* stage = smem + (tile & 1) * C::STAGE_BYTES;
+        unsigned char* stage = smem + (tile % C::STAGES) * C::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::LPW; ++i) {
             const int jj = w + C::WAVES * i;
@@ -163,12 +178,12 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
     const int tr_lo = swz<D>(4 * kg + tr_j, tr_b >> 1) + (tr_b & 1) * 8;
     const int tr_hi = swz<D>(16 + 4 * kg + tr_j, tr_b >> 1) + (tr_b & 1) * 8;
 
-    // O^T += V^T P^T of the tile in stage `stage` over its two 32-position
+    // O^T += V^T P^T of the tile in stage `stage` over its 32-position
     // blocks, each in two halves of d
-    auto pv_tile = [&](int stage, const u32x4_t (&pb)[RT][2]) {
+    auto pv_tile = [&](int stage, const u32x4_t (&pb)[RT][C::NKB]) {
         const uint32_t vbase = lds_addr(smem + stage * C::STAGE_BYTES + C::TILE_BYTES);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < C::NKB; ++kb) {
             const uint32_t vb = vbase + kb * 32 * C::ROWB;  // rows 32 kb ..: the same swizzle keys
             constexpr std::integral_constant<int, 0> first{};
             constexpr std::integral_constant<int, 1> second{};
@@ -196,34 +211,39 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
     // accumulators are rescaled outside it, and the tile is finished there.
     // (A rescale inside the loop, however rarely taken, makes the compiler
     // copy all accumulators between AGPRs and VGPRs on every tile.)
-    u32x4_t pb[RT][2];
+    u32x4_t pb[RT][C::NKB];
     float alpha[RT];
     int tile = 0;
-    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 0) {
+#pragma unroll
+        for (int t = 0; t < C::STAGES - 1; ++t) issue_tile(t);
+    }
     while (tile < ntiles) {
         bool rescale = false;
         for (; tile < ntiles; ++tile) {
-            // this wave's loads of the tile have landed and its LDS reads of
-            // the previous tile have returned; after the barrier every wave's
-            // have, so the next tile may land in the previous tile's stage
-            __builtin_amdgcn_s_waitcnt(0);
+            // this wave's loads of the tile have landed (those of the
+            // STAGES - 2 tiles after it may still be in flight) and its LDS
+            // reads of the previous tile have returned; after the barrier
+            // every wave's have, so tile + STAGES - 1 may land in the previous
+            // tile's stage
+            __builtin_amdgcn_s_waitcnt(kVmcntStages<C::STAGES - 2, 2 * C::LPW>() & ~(0xF << 8));
             asm volatile("" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            if (tile + 1 < ntiles) issue_tile(tile + 1);
-            const unsigned char* kt = smem + (tile & 1) * C::STAGE_BYTES;
+            issue_tile(tile + C::STAGES - 1);
+            const unsigned char* kt = smem + (tile % C::STAGES) * C::STAGE_BYTES;
 
             // S^T = K q^T: accumulator (mq, rt), lane (li, kg), element e
             // holds row li of tile rt at position 16 mq + 4 kg + e
-            f32x4_t sacc[4][RT];
+            f32x4_t sacc[C::NQ][RT];
 #pragma unroll
-            for (int mq = 0; mq < 4; ++mq)
+            for (int mq = 0; mq < C::NQ; ++mq)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) sacc[mq][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-                for (int mq = 0; mq < 4; ++mq) {
+                for (int mq = 0; mq < C::NQ; ++mq) {
                     const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kt + swz<D>(16 * mq + li, 4 * ks + kg));
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) sacc[mq][rt] = mfma_16x16x32_bf16(ka, qb[rt][ks], sacc[mq][rt]);
@@ -232,11 +252,11 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
             // scaled logits; the causal mask only on tiles reaching past the
             // wave's first row (a real branch: most tiles skip it)
             const int st = tile * C::STEP;
-            float s[RT][4][4];
+            float s[RT][C::NQ][4];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int mq = 0; mq < 4; ++mq)
+                for (int mq = 0; mq < C::NQ; ++mq)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s[rt][mq][e] = sacc[mq][rt][e] * qk;
             if (st + C::STEP > lim_wave) {
@@ -244,20 +264,20 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                    for (int mq = 0; mq < 4; ++mq)
+                    for (int mq = 0; mq < C::NQ; ++mq)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             s[rt][mq][e] = st + 16 * mq + 4 * kg + e < lim[rt] ? s[rt][mq][e] : -INFINITY;
             }
 
             // online softmax of each row tile; P^T operands pb[rt][kb] of the
-            // 32-position blocks kb = 0, 1
+            // 32-position blocks kb
             bool moved_any = false;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 float mx = -INFINITY;
 #pragma unroll
-                for (int mq = 0; mq < 4; ++mq)
+                for (int mq = 0; mq < C::NQ; ++mq)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[rt][mq][e]);
                 mx = max_xor32(max_xor16(mx));
@@ -269,7 +289,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
                 const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
                 float lsum = 0.f;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < C::NKB; ++kb) {
                     uint32_t pk[4];
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
@@ -289,16 +309,19 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
                 rescale = true;
                 break;  // P.V of this tile after the rescale, outside the loop
             }
-            pv_tile(tile & 1, pb);
+            pv_tile(tile % C::STAGES, pb);
         }
         if (!rescale) break;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int m = 0; m < C::MT; ++m) oacc[rt][m] = oacc[rt][m] * alpha[rt];
-        pv_tile(tile & 1, pb);
+        pv_tile(tile % C::STAGES, pb);
         ++tile;
     }
+    // No buffer->LDS load of this workgroup (the ring's tail loads read
+    // nothing) may still be landing when its LDS is released.
+    __builtin_amdgcn_s_waitcnt(0);
 
     // Epilogue: O / l of each row, rows at or past the length as zeros; lane
     // (li, kg) writes d = 16m + 4kg .. +3 of row li (16 bytes, every m)
@@ -317,9 +340,9 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(PrefillArgs a) {
     }
 }
 
-template <int D, int RT>
+template <int D>
 static hipError_t launch_prefill_d(const Plan& p, const PrefillArgs& a, hipStream_t stream) {
-    using C = PrefillCfg<D, RT>;
+    using C = PrefillCfg<D>;
     constexpr int lds = C::LDS_BYTES;
     if (lds > 64 * 1024) {
         static std::atomic<uint64_t> done_mask{0};
@@ -328,24 +351,24 @@ static hipError_t launch_prefill_d(const Plan& p, const PrefillArgs& a, hipStrea
         if (e != hipSuccess) return e;
         const uint64_t bit = 1ull << (dev & 63);
         if (!(done_mask.load() & bit)) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_mfma_kernel<D, RT>),
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_mfma_kernel<D>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             if (e != hipSuccess) return e;
             done_mask.fetch_or(bit);
         }
     }
-    if (p.block_main != 64 * C::WAVES) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, RT>), dim3((unsigned)p.grid_main), dim3(64 * C::WAVES), lds, stream,
-                       a);
+    if (p.block_main != C::THREADS || a.row_blocks * (long long)C::ROWS < (long long)a.Lmax * a.G)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_mfma_kernel<D>), dim3((unsigned)p.grid_main), dim3(C::THREADS), lds, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_mfma(const Plan& p, const PrefillArgs& a, hipStream_t stream) {
     if (p.grid_main <= 0) return hipSuccess;
     switch (a.D) {
-        case 64: return launch_prefill_d<64, prefill_row_tiles(64)>(p, a, stream);
-        case 128: return launch_prefill_d<128, prefill_row_tiles(128)>(p, a, stream);
-        case 256: return launch_prefill_d<256, prefill_row_tiles(256)>(p, a, stream);
+        case 64: return launch_prefill_d<64>(p, a, stream);
+        case 128: return launch_prefill_d<128>(p, a, stream);
+        case 256: return launch_prefill_d<256>(p, a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -311,7 +311,7 @@ def test_prefill_matches_oracle_causal_attention(B, Hq, Hkv, D, Lmax):
                                            (80, 1, 64, 150, 2), (96, 1, 128, 130, 1), (112, 1, 64, 100, 2),
                                            (3, 2, 256, 257, 2), (20, 2, 128, 97, 3)])
 def test_prefill_shapes(G, Hkv, D, Lmax, B):
-    """The prefill kernel at several tiles per prefix, row blocks of 128 (position, head) rows that
+    """The prefill kernel at several tiles per prefix, row blocks of (position, head) rows that
     split a position's heads or do not divide Lmax * G, ragged lengths (0, 1 and Lmax among them),
     NaN padding past each length, several kv heads, every head size."""
     Hq = G * Hkv
@@ -322,8 +322,9 @@ def test_prefill_shapes(G, Hkv, D, Lmax, B):
     poison_padding_(inp["k"], lens)
     poison_padding_(inp["v"], lens)
     plan = binding.prefill_plan(B, Hq, Hkv, D, Lmax, inp["scale"])
-    assert plan["rows_per_block"] == 128 and plan["combine"] == 0 and plan["workspace_bytes"] == 0
-    assert plan["grid_main"] == B * Hkv * -(-Lmax * G // 128) and plan["block_main"] in (256, 512)
+    rows = plan["rows_per_block"]
+    assert rows % 16 == 0 and 64 <= rows <= 256 and plan["combine"] == 0 and plan["workspace_bytes"] == 0
+    assert plan["grid_main"] == B * Hkv * -(-Lmax * G // rows) and plan["block_main"] in (256, 512, 1024)
     ref = oracle.causal_prefill(inp["q_seq"], inp["k"], inp["v"], lens, inp["scale"])
     dev = to_dev(inp)
     print("case prefill shapes", G, Hkv, D, Lmax, B, flush=True)

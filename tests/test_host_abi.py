@@ -75,6 +75,20 @@ def test_empty_batch_is_a_no_op_even_with_null_pointers():
     assert lib.mqa_prefill_attention(0, 0, 0, 0, 0, 0, 8, 1, 64, 16, 0.125, None) == OK
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,D,Lmax", [(64, 48, 1, 256, 2048), (32, 64, 8, 128, 4096), (2, 3, 3, 64, 700),
+                                              (3, 40, 2, 128, 97), (1, 112, 1, 64, 1)])
+def test_prefill_plan_covers_every_row(B, Hq, Hkv, D, Lmax):
+    """One workgroup per block of query rows of each (sequence, kv head), the blocks covering all
+    Lmax * G rows, whole waves per workgroup, no workspace."""
+    p = binding.prefill_plan(B, Hq, Hkv, D, Lmax, 0.1)
+    rows, G = p["rows_per_block"], Hq // Hkv
+    assert rows > 0 and rows % 16 == 0
+    blocks = -(-Lmax * G // rows)
+    assert p["grid_main"] == B * Hkv * blocks and (blocks - 1) * rows < Lmax * G <= blocks * rows
+    assert p["block_main"] % 64 == 0 and 64 <= p["block_main"] <= 1024
+    assert p["workspace_bytes"] == 0 and p["max_splits"] == 1
+
+
 def test_prefill_checks_arguments_too():
     assert lib.mqa_prefill_attention(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 6, 4, 64, 16, 0.1, None) == ERR_SHAPE
 
