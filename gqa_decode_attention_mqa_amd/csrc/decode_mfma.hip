@@ -91,7 +91,12 @@ struct MfmaCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-template <int D, int NG, int FMT>
+// FUSED: the kernel form whose chunks merge the partials themselves (the
+// fused combine).  It is a separate instantiation so that the tail's code
+// cannot change how the compiler allocates and schedules the tile loop of the
+// plain form (with the tail behind a run-time flag in one kernel, MI355X
+// measured 11 % slower 8-bit loops: int8 B=4 len 131072 86.6 against 78.0 us).
+template <int D, int NG, int FMT, bool FUSED>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     using C = MfmaCfg<D, NG, FMT>;
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
@@ -369,17 +374,25 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
             i32x4_t part[2][2];  // [mq][hi or lo part of q]
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq) part[mq][0] = part[mq][1] = i32x4_t{0, 0, 0, 0};
+            // every K read of the tile first, then the products: the
+            // scheduling barrier keeps the compiler from interleaving them
+            // (it otherwise may keep only a few reads ahead, each product
+            // then waiting for its read: MI355X, int8 B=4 len 131072 83.5
+            // against 77.7 us)
+            i32x4_t ka[C::NB8][2];
+#pragma unroll
+            for (int b = 0; b < C::NB8; ++b)
+#pragma unroll
+                for (int mq = 0; mq < 2; ++mq)
+                    ka[b][mq] = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(kt + i8_off[mq][b]));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int b = 0; b < C::NB8; ++b)
 #pragma unroll
                 for (int mq = 0; mq < 2; ++mq) {
-                    const i32x4_t ka = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(kt + i8_off[mq][b]));
-                    part[mq][0] = mfma_16x16x64_i8(ka, qih[b], part[mq][0]);
-                    part[mq][1] = mfma_16x16x64_i8(ka, qil[b], part[mq][1]);
+                    part[mq][0] = mfma_16x16x64_i8(ka[b][mq], qih[b], part[mq][0]);
+                    part[mq][1] = mfma_16x16x64_i8(ka[b][mq], qil[b], part[mq][1]);
                 }
-            // every K read of the tile first, then the products
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NB8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 4 * C::NB8, 0);
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq)
 #pragma unroll
@@ -391,20 +404,26 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
             f32x4_t part[2][2];  // [mq][high or low part of q]
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq) part[mq][0] = part[mq][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // every K read of the tile first, then the products (as above)
+            u32x4_t kr[C::NH8][2][2];
+#pragma unroll
+            for (int h = 0; h < C::NH8; ++h)
+#pragma unroll
+                for (int mq = 0; mq < 2; ++mq)
+#pragma unroll
+                    for (int x = 0; x < 2; ++x)
+                        kr[h][mq][x] = *reinterpret_cast<const u32x4_t*>(kt + f8_off[mq][h][x]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int h = 0; h < C::NH8; ++h)
 #pragma unroll
                 for (int mq = 0; mq < 2; ++mq) {
-                    const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kt + f8_off[mq][h][0]);
-                    const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(kt + f8_off[mq][h][1]);
+                    const u32x4_t k0 = kr[h][mq][0], k1 = kr[h][mq][1];
                     const i32x8_t ka = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
                                         (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
                     part[mq][0] = mfma_16x16x128_fp8(ka, qh[h], part[mq][0]);
                     part[mq][1] = mfma_16x16x128_fp8(ka, ql[h], part[mq][1]);
                 }
-            // every K read of the tile first, then the products
-            __builtin_amdgcn_sched_group_barrier(0x100, 4 * C::NH8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 4 * C::NH8, 0);
             sacc[0] = part[0][0] + part[0][1];
             sacc[1] = part[1][0] + part[1][1];
             return;
@@ -733,16 +752,18 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
             }
         }
     }
-    if (direct || !a.fused) return;
-    // ---- fused combine: the chunks of this (row, kv head, head block) share the merge
-    __syncthreads();
-    fused_tail(a, unit, row, kvh, nsplit, g0, gcnt, a.counters + (unit * gridDim.y + blockIdx.y) * kFusedCountersPerUnit,
-               reinterpret_cast<int*>(smem));
+    if constexpr (FUSED) {
+        if (direct) return;
+        // ---- fused combine: the chunks of this (row, kv head, head block) share the merge
+        __syncthreads();
+        fused_tail(a, unit, row, kvh, nsplit, g0, gcnt,
+                   a.counters + (unit * gridDim.y + blockIdx.y) * kFusedCountersPerUnit, reinterpret_cast<int*>(smem));
+    }
 }
 
-template <int D, int NG, int FMT>
-static hipError_t launch_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
-                            hipEvent_t ev1) {
+template <int D, int NG, int FMT, bool FUSED>
+static hipError_t launch_mfma_form(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                                   hipEvent_t ev1) {
     using C = MfmaCfg<D, NG, FMT>;
     constexpr int lds = C::LDS_BYTES;
     if (lds > 64 * 1024) {
@@ -752,7 +773,7 @@ static hipError_t launch_mfma(const Plan& p, const DecodeArgs& a, hipStream_t st
         if (e != hipSuccess) return e;
         const uint64_t bit = 1ull << (dev & 63);
         if (!(done_mask.load() & bit)) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<D, NG, FMT>),
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<D, NG, FMT, FUSED>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             if (e != hipSuccess) return e;
             done_mask.fetch_or(bit);
@@ -761,10 +782,17 @@ static hipError_t launch_mfma(const Plan& p, const DecodeArgs& a, hipStream_t st
     const dim3 grid((unsigned)p.grid_main, (unsigned)p.head_blocks);
     const dim3 block(C::THREADS);
     if (ev0 || ev1)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<D, NG, FMT>), grid, block, lds, stream, ev0, ev1, 0, a);
+        hipExtLaunchKernelGGL((decode_mfma_kernel<D, NG, FMT, FUSED>), grid, block, lds, stream, ev0, ev1, 0, a);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<D, NG, FMT>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<D, NG, FMT, FUSED>), grid, block, lds, stream, a);
     return hipGetLastError();
+}
+
+template <int D, int NG, int FMT>
+static hipError_t launch_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+    return a.fused ? launch_mfma_form<D, NG, FMT, true>(p, a, stream, ev0, ev1)
+                   : launch_mfma_form<D, NG, FMT, false>(p, a, stream, ev0, ev1);
 }
 
 template <int D, int FMT>

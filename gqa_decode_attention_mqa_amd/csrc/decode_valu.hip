@@ -55,7 +55,9 @@ __device__ __forceinline__ float lane_value(float x, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
-template <int D, int GB, int FMT>
+// FUSED: the fused-combine form, a separate instantiation (as for the
+// matrix-core kernel) so that its tail leaves the plain form's code alone.
+template <int D, int GB, int FMT, bool FUSED>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     constexpr bool Q8 = FMT != kKvBf16;  // 8-bit codes with one scale per cached row
     constexpr int NW = 4;
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
                 const int e = scale_exponent(__uint_as_float(s_amax[gg]));
                 const size_t part = ((size_t)unit * a.max_splits + s) * a.GT + g0 + gg;
                 const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(val[k], -e));
-                if (a.fused) {
+                if constexpr (FUSED) {
                     store_coherent(a.part_o + part * D + d, h);
                     if (d == 0) store_coherent8(a.part_ml + part, f32x2_t{lse[k], (float)e});
                 } else {
@@ -372,22 +374,31 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             }
         }
     }
-    if (direct || !a.fused) return;
-    // Fused combine: the chunks of this (row, kv head, head block) share the merge.
-    fused_tail(a, unit, row, kvh, nsplit, g0, gcnt, a.counters + (unit * gridDim.y + blockIdx.y) * kFusedCountersPerUnit,
-               &s_flag);
+    if constexpr (FUSED) {
+        if (direct) return;
+        // Fused combine: the chunks of this (row, kv head, head block) share the merge.
+        fused_tail(a, unit, row, kvh, nsplit, g0, gcnt,
+                   a.counters + (unit * gridDim.y + blockIdx.y) * kFusedCountersPerUnit, &s_flag);
+    }
+}
+
+template <int D, int GB, int FMT, bool FUSED>
+static hipError_t launch_form(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                              hipEvent_t ev1) {
+    const dim3 grid((unsigned)p.grid_main, (unsigned)p.head_blocks);
+    const dim3 block(256);
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL((decode_valu_kernel<D, GB, FMT, FUSED>), grid, block, 0, stream, ev0, ev1, 0, a);
+    else
+        hipLaunchKernelGGL((decode_valu_kernel<D, GB, FMT, FUSED>), grid, block, 0, stream, a);
+    return hipGetLastError();
 }
 
 template <int D, int GB, int FMT>
 static hipError_t launch_one(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                              hipEvent_t ev1) {
-    const dim3 grid((unsigned)p.grid_main, (unsigned)p.head_blocks);
-    const dim3 block(256);
-    if (ev0 || ev1)
-        hipExtLaunchKernelGGL((decode_valu_kernel<D, GB, FMT>), grid, block, 0, stream, ev0, ev1, 0, a);
-    else
-        hipLaunchKernelGGL((decode_valu_kernel<D, GB, FMT>), grid, block, 0, stream, a);
-    return hipGetLastError();
+    return a.fused ? launch_form<D, GB, FMT, true>(p, a, stream, ev0, ev1)
+                   : launch_form<D, GB, FMT, false>(p, a, stream, ev0, ev1);
 }
 
 template <int D, int FMT>

@@ -49,7 +49,6 @@ struct PrefillCfg {
     static constexpr int LPW = LOADS / WAVES;          // of them, per wave
     static constexpr int KS = D / 32;                  // k-steps of q.K
     static constexpr int MT = D / 16;                  // 16-row tiles of O^T (along d)
-    static constexpr int MH = MT / 2;                  // P.V runs over two halves of d
     static_assert(RT == 1 || RT == 2, "one or two 16-row tiles per wave");
     static_assert(ROWS % (16 * RT) == 0 && THREADS <= 1024, "whole waves of row tiles");
     static_assert(STEP == 32 || STEP == 64, "tiles of 32 or 64 positions");
@@ -178,31 +177,42 @@ __global__ __launch_bounds__(PrefillCfg<D>::THREADS > 512 ? PrefillCfg<D>::THREA
     const int tr_lo = swz<D>(4 * kg + tr_j, tr_b >> 1) + (tr_b & 1) * 8;
     const int tr_hi = swz<D>(16 + 4 * kg + tr_j, tr_b >> 1) + (tr_b & 1) * 8;
 
-    // O^T += V^T P^T of the tile in stage `stage` over its 32-position
-    // blocks, each in two halves of d
+    // O^T += V^T P^T of the tile in stage `stage`, in steps of MS 16-row
+    // tiles of d for each 32-position block.  The V^T reads of step s + 1 are
+    // issued before the wait for those of step s, which therefore leaves the
+    // 2 MS reads of step s + 1 in flight (LDS reads complete in order; any
+    // other LDS or scalar-memory operation in flight only makes the wait
+    // longer).  Measured on MI355X against a wait for every read of each half
+    // of d: PaLM-shaped prefill 8.49 against 8.68 ms, gqa70b-shaped equal.
+    constexpr int MS = 4, SPB = C::MT / MS, NS = C::NKB * SPB;
+    static_assert(C::MT % MS == 0 && 2 * MS <= 15, "whole steps; the wait count fits lgkmcnt");
     auto pv_tile = [&](int stage, const u32x4_t (&pb)[RT][C::NKB]) {
         const uint32_t vbase = lds_addr(smem + stage * C::STAGE_BYTES + C::TILE_BYTES);
+        u32x2_t lo[2][MS], hi[2][MS];
+        auto issue = [&](auto sc) {
+            constexpr int s = decltype(sc)::value, kb = s / SPB, M0 = (s % SPB) * MS;
+            const uint32_t vb = vbase + kb * 32 * C::ROWB;
+            issue_vt_tile<M0, MS, NR>(vb + tr_lo, vb + tr_hi, lo[s & 1], hi[s & 1]);
+        };
+        issue(std::integral_constant<int, 0>{});
+        static_for<0, NS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value, kb = s / SPB, M0 = (s % SPB) * MS;
+            if constexpr (s + 1 < NS) {
+                issue(std::integral_constant<int, s + 1>{});
+                asm volatile("s_waitcnt lgkmcnt(%0)" :: "i"(2 * MS) : "memory");
+            } else {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-            const uint32_t vb = vbase + kb * 32 * C::ROWB;  // rows 32 kb ..: the same swizzle keys
-            constexpr std::integral_constant<int, 0> first{};
-            constexpr std::integral_constant<int, 1> second{};
-            auto half = [&](auto hc) {
-                constexpr int M0 = decltype(hc)::value * C::MH;
-                u32x2_t lo[C::MH], hi[C::MH];
-                issue_vt_tile<M0, C::MH, NR>(vb + tr_lo, vb + tr_hi, lo, hi);
-                wait_vt_tile<C::MH>(lo, hi);
+            for (int m = 0; m < MS; ++m) asm volatile("" : "+v"(lo[s & 1][m]), "+v"(hi[s & 1][m]));
 #pragma unroll
-                for (int j = 0; j < C::MH; ++j) {
-                    const u32x4_t va = u32x4_t{lo[j].x, lo[j].y, hi[j].x, hi[j].y};
+            for (int j = 0; j < MS; ++j) {
+                const u32x4_t va = u32x4_t{lo[s & 1][j].x, lo[s & 1][j].y, hi[s & 1][j].x, hi[s & 1][j].y};
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-                        oacc[rt][M0 + j] = mfma_16x16x32_bf16(va, pb[rt][kb], oacc[rt][M0 + j]);
-                }
-            };
-            half(first);
-            half(second);
-        }
+                for (int rt = 0; rt < RT; ++rt)
+                    oacc[rt][M0 + j] = mfma_16x16x32_bf16(va, pb[rt][kb], oacc[rt][M0 + j]);
+            }
+        });
     };
 
     // The tile loop keeps the accumulators untouched by vector instructions:
