@@ -225,7 +225,12 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.fused = plan.combine == 2 ? 1 : 0;
     a.fused_wait = mqa::kFusedWaitTicks;
     if (a.fused) {
-        if (const char* t = std::getenv("MQA_FUSED_WAIT_TICKS")) a.fused_wait = (uint32_t)std::strtoul(t, nullptr, 10);
+        if (const char* t = std::getenv("MQA_FUSED_WAIT_TICKS")) {
+            // at most 10 ms: a workgroup whose partners cannot become resident
+            // holds its CU for this long before it leaves its part to them
+            const unsigned long v = std::strtoul(t, nullptr, 10);
+            a.fused_wait = (uint32_t)(v < mqa::kFusedMaxWaitTicks ? v : mqa::kFusedMaxWaitTicks);
+        }
     }
     a.Hq = Hq;
     a.Hkv = Hkv;

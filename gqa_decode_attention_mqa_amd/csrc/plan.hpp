@@ -54,6 +54,7 @@ constexpr int kFusedCountersPerUnit = 4;
 // 100 MHz real-time counter.  MQA_FUSED_WAIT_TICKS overrides it (tests force
 // the timed-out path with 0).
 constexpr unsigned kFusedWaitTicks = 2000;
+constexpr unsigned kFusedMaxWaitTicks = 1000000;  // the most MQA_FUSED_WAIT_TICKS may ask: 10 ms
 // make_plan's `causal` argument for the causal prefill kernel.
 constexpr int kCausalPrefill = 3;
 // Causal prefill kernel, per head size D: query rows per workgroup, 16-row

@@ -99,8 +99,9 @@ typedef struct mqa_decode_opts {
                              (sequence, kv head) merge the partials once all have
                              finished, the k-th to finish taking the k-th part of the
                              heads (a bounded wait, 20 us by default or
-                             MQA_FUSED_WAIT_TICKS ticks of 10 ns; a part whose wait
-                             timed out goes to the last chunk); at most 8 chunks per
+                             MQA_FUSED_WAIT_TICKS ticks of 10 ns, at most 10 ms; a
+                             part whose wait timed out goes to the last chunk); at
+                             most 8 chunks per
                              sequence, else MQA_ERR_ARG; both merges give the same bits */
     void *ev_main_begin;  /* optional hipEvent_t pair recorded by the split-K kernel's own
                              dispatch (hipExtLaunchKernelGGL) at its start and end, so  */
