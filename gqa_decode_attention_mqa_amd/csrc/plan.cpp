@@ -26,9 +26,18 @@ mqa_status fail(mqa_status s, const std::string& msg) {
 constexpr long long kTargetWorkgroups = kComputeUnits;
 // Chunk bounds: below 256 positions the partial outputs cost more traffic than
 // the split saves; longer chunks balance a ragged batch poorly (the vector
-// kernel, an explicit variant, gets the tighter bound).
+// kernel, an explicit variant, gets the tighter bound).  A bf16 cache needs no
+// upper bound below the whole sequence: its matrix-core kernel streams at
+// one workgroup per CU, and fewer, longer chunks save the merge and the
+// partials (MI355X, 70B-class GQA B=32 Hkv=8 D=128 len 4096: 78.2 us with
+// whole sequences against 90.7 us at 2048; the same with 4 query tokens 81.6
+// against 92.7; PaLM-shaped MQA at B=256: 84.6 against 93.6 at 1024; B=16 of
+// the 131072-position MQA: 320.9 at 8192 against 389.3 at 2048).  An 8-bit
+// cache keeps 2048: its loop is bound by the compute waves, so two workgroups
+// per CU win there (the GQA shape: fp8 50.5 us at 2048 against 81.3 at 4096,
+// int8 56.9 against 95.2).
 constexpr long long kMinChunk = 256;
-constexpr long long kMaxChunkMfma = 2048;
+constexpr long long kMaxChunkMfma8 = 2048;
 constexpr long long kMaxChunkValu = 1024;
 // Largest grid the launcher accepts (work-items must stay below 2^32).
 constexpr long long kMaxGrid = (1LL << 24) - 1;
@@ -179,7 +188,9 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         const bool windowed = o.window > 0 && o.window < Lmax;
         long long c = round_up(ceil_div(span * units, kTargetWorkgroups), kChunkQuantum);
         const long long cmax = p.variant != MQA_VARIANT_MFMA ? kMaxChunkValu
-                               : (units >= kManyUnits ? kMaxChunkMfmaMany : kMaxChunkMfma);
+                               : units >= kManyUnits        ? kMaxChunkMfmaMany
+                               : o.kv_format != MQA_KV_BF16 ? kMaxChunkMfma8
+                                                            : round_up(span, kChunkQuantum);
         const long long cmin = windowed ? kChunkQuantum : kMinChunk;
         if (c < cmin) c = cmin;
         if (c > cmax) c = cmax;

@@ -134,7 +134,10 @@ def test_default_plans_of_the_five_workloads():
     assert binding.plan(64, 48, 1, 256, 2048)["chunk"] == 512
     assert binding.plan(4, 48, 1, 256, 131072)["chunk"] == 2048
     g = binding.plan(32, 64, 8, 128, 4096)
-    assert g["variant"] == "mfma" and g["chunk"] == 2048
+    assert g["variant"] == "mfma" and g["chunk"] == 4096 and g["max_splits"] == 1  # whole sequences
+    assert binding.plan(32, 64, 8, 128, 4096, kv_format="fp8")["chunk"] == 2048  # two workgroups per CU
+    assert binding.plan(32, 64, 8, 128, 4096, kv_format="int8")["chunk"] == 2048
+    assert binding.plan(16, 48, 1, 256, 131072)["chunk"] == 8192  # one workgroup per CU
     r = binding.plan(256, 32, 8, 128, 8192)
     assert r["variant"] == "mfma" and r["chunk"] == 1024
     assert binding.plan(1, 8, 1, 64, 128)["max_splits"] == 1
