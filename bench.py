@@ -109,6 +109,9 @@ def parse_args(argv=None):
                          "of the workload's shapes instead of the decode step; roofline against the bf16 "
                          "matrix-core peak")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch size B")
+    ap.add_argument("--no-host-lens", action="store_true",
+                    help="plan without the host copy of the lengths (mqa_decode_opts.host_seq_lens), so the "
+                         "planner cannot tell a uniform batch from a ragged one")
     ap.add_argument("--kernel-steps", type=int, default=None,
                     help="steps of the evented kernel pass (default: max(200, min(steps, 2000)))")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
@@ -368,6 +371,9 @@ def main(argv=None):
         make = lambda seed=None, seq_lens=None: make_inputs(w, device=dev, seed=seed, seq_lens=seq_lens)
     base = make()
     lens = base["seq_lens"]
+    # the host copy of the lengths a caller passes to the planner (it picks
+    # the chunk size from it; results never depend on it)
+    host_lens = None if args.no_host_lens else lens.cpu()
     # positions attended: all of them, or the last `window` of each sequence
     attended = [min(n, args.window) if args.window else n for n in lens.cpu().tolist()]
     q8 = args.kv_format != "bf16"
@@ -384,7 +390,7 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk, args.combine,
-                        window=args.window, kv_format=args.kv_format, tokens=args.tokens)
+                        window=args.window, kv_format=args.kv_format, tokens=args.tokens, host_seq_lens=host_lens)
 
     # 8-bit caches: each set's bf16 draw is quantized per row (the codes and
     # scales replace it); the scale pointers travel in each set's options
@@ -434,7 +440,7 @@ def main(argv=None):
     def make(i, ev_b=None, ev_e=None):  # options of a step on set i % nsets
         ks, vs = set_scales[i % nsets]
         return binding.make_opts(args.variant, args.chunk, args.combine, ev_b, ev_e, args.window,
-                                 args.kv_format, ks, vs)
+                                 args.kv_format, ks, vs, host_seq_lens=host_lens)
 
     plain_sets = [make(i) for i in range(nsets)]
     for i in range(args.warmup):
@@ -526,6 +532,7 @@ def main(argv=None):
             "attended_positions": int(sum(attended)),
             "kv_bytes_per_step": kv_bytes,
             "buffer_sets_rotated": nsets,
+            "host_lengths_to_planner": host_lens is not None,
             "plan": plan,
         },
         "roofline": {

@@ -40,7 +40,8 @@ class DecodeOpts(ctypes.Structure):
                 ("ev_main_begin", ctypes.c_void_p), ("ev_main_end", ctypes.c_void_p),
                 ("window", ctypes.c_int), ("kv_format", ctypes.c_int),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("ev_combine_begin", ctypes.c_void_p), ("ev_combine_end", ctypes.c_void_p)]
+                ("ev_combine_begin", ctypes.c_void_p), ("ev_combine_end", ctypes.c_void_p),
+                ("host_seq_lens", ctypes.c_void_p)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -120,9 +121,33 @@ def _check(status: int, where: str):
                                                    lib.mqa_last_error().decode()))
 
 
+def _host_lens(host_seq_lens):
+    """A contiguous host int32 copy of the lengths (kept alive by the caller's opts), or None."""
+    if host_seq_lens is None:
+        return None
+    t = torch.as_tensor(host_seq_lens)
+    if t.device.type != "cpu":
+        raise ValueError("host_seq_lens must be in host memory")
+    return t.to(torch.int32).contiguous()
+
+
+def _checked_lens(host_seq_lens, B):
+    if host_seq_lens is None:
+        return None
+    t = _host_lens(host_seq_lens)
+    if t.dim() != 1 or t.numel() != B:
+        raise ValueError("host_seq_lens must hold B = %d lengths, got shape %s" % (B, tuple(t.shape)))
+    return t
+
+
 def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None, window=None,
-              kv_format=None, k_scale=None, v_scale=None, ev_combine_begin=None, ev_combine_end=None) -> DecodeOpts:
+              kv_format=None, k_scale=None, v_scale=None, ev_combine_begin=None, ev_combine_end=None,
+              host_seq_lens=None) -> DecodeOpts:
+    """Options of a decode call.  ``host_seq_lens``: an optional host copy of the lengths, used by
+    the planner only to pick the chunk size (see mqa_decode_opts.host_seq_lens)."""
     o = DecodeOpts()
+    o._host_lens = _host_lens(host_seq_lens)
+    o.host_seq_lens = o._host_lens.data_ptr() if o._host_lens is not None else None
     o.ev_combine_begin = ev_combine_begin
     o.ev_combine_end = ev_combine_end
     o.window = int(window or 0)
@@ -138,12 +163,12 @@ def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None
 
 
 def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None, window=None,
-         kv_format=None, tokens=1) -> dict:
+         kv_format=None, tokens=1, host_seq_lens=None) -> dict:
     """The library's launch plan for a decode call of this shape (host only);
     ``tokens`` > 1 plans a multi-token call."""
     lib = load_library()
     info = PlanInfo()
-    opts = make_opts(variant, chunk, combine, window=window, kv_format=kv_format)
+    opts = make_opts(variant, chunk, combine, window=window, kv_format=kv_format, host_seq_lens=host_seq_lens)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.mqa_decode_plan_multi(B, int(tokens), Hq, Hkv, D, Lmax, sc, ctypes.byref(opts), ctypes.byref(info)),
            "mqa_decode_plan")
@@ -189,7 +214,7 @@ def _require(t: torch.Tensor, name: str, dtype, ndim: int, device):
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
            scale: float | None = None, out: torch.Tensor | None = None, variant=None, chunk=None,
-           combine=None, events=None, window=None) -> torch.Tensor:
+           combine=None, events=None, window=None, host_seq_lens=None) -> torch.Tensor:
     """One decode step.  q [B,Hq,D] bf16, caches [B,Lmax,Hkv,D] bf16, seq_lens [B] int32 -> fp32 [B,Hq,D].
 
     Runs on torch's current stream of q's device.  ``events`` = (begin, end)
@@ -217,7 +242,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
     ev_b = ev_e = None
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
-    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window)
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window,
+                     host_seq_lens=_checked_lens(host_seq_lens, B))
     lib = load_library()
     st = lib.mqa_decode_attention_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                      seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D, Lmax,
@@ -229,7 +255,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
 def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
                  seq_lens: torch.Tensor, scale: float | None = None, out: torch.Tensor | None = None,
                  variant=None, chunk=None, combine=None, events=None, window=None, kv_format=None,
-                 k_scale=None, v_scale=None) -> torch.Tensor:
+                 k_scale=None, v_scale=None, host_seq_lens=None) -> torch.Tensor:
     """One decode step over a paged cache.  q [B,Hq,D] bf16, pages [num_pages,page_size,Hkv,D] bf16,
     block_table [B,max_blocks] int32, seq_lens [B] int32 -> fp32 [B,Hq,D].  With ``kv_format``
     "fp8" or "int8" the pages hold 8-bit codes (uint8) and ``k_scale`` / ``v_scale`` are fp32
@@ -263,7 +289,8 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
     ev_b = ev_e = None
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
-    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window, fmt, sk, sv)
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window, fmt, sk, sv,
+                     host_seq_lens=_checked_lens(host_seq_lens, B))
     lib = load_library()
     st = lib.mqa_decode_attention_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                                         block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
@@ -276,7 +303,7 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
 def decode_quant(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor, k_scale: torch.Tensor,
                  v_scale: torch.Tensor, seq_lens: torch.Tensor, kv_format: str, scale: float | None = None,
                  out: torch.Tensor | None = None, variant=None, chunk=None, combine=None, events=None,
-                 window=None) -> torch.Tensor:
+                 window=None, host_seq_lens=None) -> torch.Tensor:
     """One decode step against an 8-bit cache through ``mqa_decode_attention_quant``.
     q [B,Hq,D] bf16; codes [B,Lmax,Hkv,D] uint8 (E4M3 for "fp8", two's complement for
     "int8"); scales [B,Hkv,Lmax] fp32; seq_lens [B] int32 -> fp32 [B,Hq,D]."""
@@ -304,7 +331,8 @@ def decode_quant(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor, 
     ev_b = ev_e = None
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
-    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window)
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e, window,
+                     host_seq_lens=_checked_lens(host_seq_lens, B))
     lib = load_library()
     st = lib.mqa_decode_attention_quant(q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(), k_scale.data_ptr(),
                                         v_scale.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D,
@@ -315,7 +343,7 @@ def decode_quant(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor, 
 
 def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
                  scale: float | None = None, out: torch.Tensor | None = None, variant=None, chunk=None,
-                 combine=None, events=None, kv_format=None, k_scale=None, v_scale=None) -> torch.Tensor:
+                 combine=None, events=None, kv_format=None, k_scale=None, v_scale=None, host_seq_lens=None) -> torch.Tensor:
     """T new tokens per sequence through ``mqa_decode_attention_multi``: q [B,T,Hq,D] bf16
     -> fp32 [B,T,Hq,D]; token i attends positions 0 .. seq_lens[b] - T + i.  Caches as for
     :func:`decode` (bf16), or 8-bit codes with ``kv_format`` and scales as for :func:`decode_quant`."""
@@ -348,7 +376,8 @@ def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     ev_b = ev_e = None
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
-    opts = make_opts(variant, chunk, combine, ev_b, ev_e, None, fmt, sk, sv)
+    opts = make_opts(variant, chunk, combine, ev_b, ev_e, None, fmt, sk, sv,
+                     host_seq_lens=_checked_lens(host_seq_lens, B))
     lib = load_library()
     st = lib.mqa_decode_attention_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
                                         out.data_ptr(), B, T, Hq, Hkv, D, Lmax, sc, _stream_ptr(dev),

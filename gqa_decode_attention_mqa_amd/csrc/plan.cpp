@@ -26,18 +26,27 @@ mqa_status fail(mqa_status s, const std::string& msg) {
 constexpr long long kTargetWorkgroups = kComputeUnits;
 // Chunk bounds: below 256 positions the partial outputs cost more traffic than
 // the split saves; longer chunks balance a ragged batch poorly (the vector
-// kernel, an explicit variant, gets the tighter bound).  A bf16 cache needs no
-// upper bound below the whole sequence: its matrix-core kernel streams at
-// one workgroup per CU, and fewer, longer chunks save the merge and the
-// partials (MI355X, 70B-class GQA B=32 Hkv=8 D=128 len 4096: 78.2 us with
-// whole sequences against 90.7 us at 2048; the same with 4 query tokens 81.6
-// against 92.7; PaLM-shaped MQA at B=256: 84.6 against 93.6 at 1024; B=16 of
-// the 131072-position MQA: 320.9 at 8192 against 389.3 at 2048).  An 8-bit
-// cache keeps 2048: its loop is bound by the compute waves, so two workgroups
-// per CU win there (the GQA shape: fp8 50.5 us at 2048 against 81.3 at 4096,
-// int8 56.9 against 95.2).
+// kernel, an explicit variant, gets the tighter bound).  Measured on MI355X:
+//   - ragged lengths U[1, 8192], B=32..96, Hkv=8, D=128: whole sequences
+//     lose (B=32: 132.1 us against 116.1 at 2048 and 102.0 at 1024);
+//   - a uniform batch on a bf16 cache wants about one chunk per CU, up to
+//     whole sequences, which also saves the merge and the partials (B=32,
+//     Hkv=8, D=128, len 4096: 78.2 us with whole sequences against 90.7 at
+//     2048; the same with 4 query tokens 81.6 against 92.7; PaLM-shaped MQA
+//     at B=256: 84.6 against 93.6 at 1024; B=16 at len 131072: 320.9 at 8192
+//     against 389.3 at 2048);
+//   - an 8-bit cache stays at 2048 even then: its loop is bound by the
+//     compute waves, so two workgroups per CU win (the uniform GQA batch:
+//     fp8 50.5 us at 2048 against 81.3 at 4096, int8 56.9 against 95.2).
+// Whether a batch is uniform is known only from the host copy of the lengths
+// the caller may pass (mqa_decode_opts.host_seq_lens).  Without it, 2048 is
+// kept (1024 from kManyUnits units on): few-unit uniform batches need the
+// longer chunks (B=4 at len 131072: 84.2 us at 2048 against 92.9 at 1024).
+// With it, a ragged batch of at least one unit per CU gets 1024 (ragged
+// B=32..96 above: 102.0 / 191.1 / 287.0 us at 1024 against 116.1 / 215.2 /
+// 318.6 at 2048).
 constexpr long long kMinChunk = 256;
-constexpr long long kMaxChunkMfma8 = 2048;
+constexpr long long kMaxChunkMfma = 2048;
 constexpr long long kMaxChunkValu = 1024;
 // Largest grid the launcher accepts (work-items must stay below 2^32).
 constexpr long long kMaxGrid = (1LL << 24) - 1;
@@ -186,11 +195,32 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         // positions (measured on MI355X, B=4, Hq=48, D=256, W=8192: 14.6 us at
         // 128 against 16.0 us at 256).
         const bool windowed = o.window > 0 && o.window < Lmax;
-        long long c = round_up(ceil_div(span * units, kTargetWorkgroups), kChunkQuantum);
-        const long long cmax = p.variant != MQA_VARIANT_MFMA ? kMaxChunkValu
-                               : units >= kManyUnits        ? kMaxChunkMfmaMany
-                               : o.kv_format != MQA_KV_BF16 ? kMaxChunkMfma8
-                                                            : round_up(span, kChunkQuantum);
+        // a uniform batch (host lengths all within one quantum of the
+        // longest) on a bf16 cache: about one chunk per CU over the positions
+        // actually attended, up to whole sequences
+        // a ragged batch (known from the host lengths) of at least one unit
+        // per CU: the short chunks of a many-unit batch
+        long long work = span;
+        bool coarse = false, ragged = false;
+        if (o.host_seq_lens && B > 0 && p.variant == MQA_VARIANT_MFMA) {
+            long long lo = span, hi = 0;
+            for (int b = 0; b < B; ++b) {
+                long long n = o.host_seq_lens[b];
+                n = n < 0 ? 0 : (n > Lmax ? Lmax : n);
+                if (o.window > 0 && n > o.window) n = o.window;
+                lo = n < lo ? n : lo;
+                hi = n > hi ? n : hi;
+            }
+            const bool uniform = hi > 0 && hi - lo < kChunkQuantum;
+            coarse = uniform && o.kv_format == MQA_KV_BF16;
+            ragged = !uniform && hi > 0;
+            if (coarse) work = hi;
+        }
+        long long c = round_up(ceil_div(work * units, kTargetWorkgroups), kChunkQuantum);
+        const long long cmax = p.variant != MQA_VARIANT_MFMA                       ? kMaxChunkValu
+                               : coarse                                        ? round_up(work, kChunkQuantum)
+                               : units >= kManyUnits || (ragged && units >= kComputeUnits) ? kMaxChunkMfmaMany
+                                                                                 : kMaxChunkMfma;
         const long long cmin = windowed ? kChunkQuantum : kMinChunk;
         if (c < cmin) c = cmin;
         if (c > cmax) c = cmax;

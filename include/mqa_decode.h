@@ -115,6 +115,14 @@ typedef struct mqa_decode_opts {
     const float *v_scale; /* 4-byte aligned); ignored for MQA_KV_BF16                      */
     void *ev_combine_begin; /* optional hipEvent_t pair recorded by the log-sum-exp merge   */
     void *ev_combine_end;   /* kernel's own dispatch (only when a merge kernel runs)      */
+    const int32_t *host_seq_lens; /* optional host copy of seq_lens (B values), read by the
+                             planner only to choose the chunk size: when every length lies
+                             within 128 positions of the longest (a uniform batch), a bf16
+                             cache is split into about one chunk per CU, up to whole
+                             sequences; otherwise, or when NULL, chunks stay short enough
+                             to balance ragged lengths.  The chunks always cover Lmax (or
+                             the window), so the result never depends on this hint, only
+                             the speed.                                                   */
 } mqa_decode_opts;
 
 /* What the planner decided for a shape (host-only query, no HIP call). */

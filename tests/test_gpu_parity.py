@@ -150,6 +150,26 @@ def test_fused_combine_reads_this_calls_partials(variant):
         check_close(out, ref, "fused alternate %s iteration %d" % (variant, it))
 
 
+@pytest.mark.parametrize("hint", ["uniform", "ragged", "wrong"])
+def test_host_lengths_hint_changes_the_plan_not_the_result(hint):
+    """The host copy of the lengths only picks the chunk size.  A uniform batch gets whole-sequence
+    chunks, a ragged one short chunks; a hint that claims a uniform batch of short sequences while
+    the device lengths are ragged up to Lmax must still give every position (chunks cover Lmax)."""
+    w = Workload("hint", B=16, Hq=32, Hkv=4, D=128, Lmax=3000, seed=1700, len_lo=1, len_hi=3000)
+    lens = {"uniform": [3000] * 16, "ragged": None, "wrong": None}[hint]
+    inp = make_inputs(w, poison_padding=True,
+                      seq_lens=None if lens is None else torch.tensor(lens, dtype=torch.int32))
+    host = inp["seq_lens"].clone() if hint != "wrong" else torch.full((16,), 200, dtype=torch.int32)
+    ref = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    dev = to_dev(inp)
+    plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, inp["scale"], host_seq_lens=host)
+    assert plan["chunk"] * plan["max_splits"] >= w.Lmax
+    print("case host lengths hint", hint, plan["chunk"], flush=True)
+    out = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], host_seq_lens=host)
+    torch.cuda.synchronize()
+    check_close(out, ref, "host lengths hint %s" % hint)
+
+
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
 def test_fused_combine_with_timed_out_waits(variant):
     """The fused combine's bounded wait, forced to time out at once (MQA_FUSED_WAIT_TICKS=0, read

@@ -8,6 +8,7 @@ import ctypes
 import math
 
 import pytest
+import torch
 
 from gqa_decode_attention_mqa_amd import binding
 
@@ -134,13 +135,40 @@ def test_default_plans_of_the_five_workloads():
     assert binding.plan(64, 48, 1, 256, 2048)["chunk"] == 512
     assert binding.plan(4, 48, 1, 256, 131072)["chunk"] == 2048
     g = binding.plan(32, 64, 8, 128, 4096)
-    assert g["variant"] == "mfma" and g["chunk"] == 4096 and g["max_splits"] == 1  # whole sequences
-    assert binding.plan(32, 64, 8, 128, 4096, kv_format="fp8")["chunk"] == 2048  # two workgroups per CU
-    assert binding.plan(32, 64, 8, 128, 4096, kv_format="int8")["chunk"] == 2048
-    assert binding.plan(16, 48, 1, 256, 131072)["chunk"] == 8192  # one workgroup per CU
+    assert g["variant"] == "mfma" and g["chunk"] == 2048
     r = binding.plan(256, 32, 8, 128, 8192)
     assert r["variant"] == "mfma" and r["chunk"] == 1024
     assert binding.plan(1, 8, 1, 64, 128)["max_splits"] == 1
+
+
+def test_host_lengths_choose_coarse_chunks_for_uniform_batches():
+    """With a host copy of the lengths the planner tells a uniform batch from a ragged one: uniform
+    on a bf16 cache gets about one chunk per CU, up to whole sequences; 8-bit caches and ragged
+    batches keep the short chunks.  The chunks always cover Lmax (or the window)."""
+    full = lambda B, n: torch.full((B,), n, dtype=torch.int32)
+    g = binding.plan(32, 64, 8, 128, 4096, host_seq_lens=full(32, 4096))
+    assert g["chunk"] == 4096 and g["max_splits"] == 1 and g["grid_combine"] == 0
+    assert binding.plan(32, 64, 8, 128, 4096, host_seq_lens=full(32, 4096), tokens=4)["chunk"] == 4096
+    assert binding.plan(32, 64, 8, 128, 4096, kv_format="fp8", host_seq_lens=full(32, 4096))["chunk"] == 2048
+    assert binding.plan(32, 64, 8, 128, 4096, kv_format="int8", host_seq_lens=full(32, 4096))["chunk"] == 2048
+    assert binding.plan(16, 48, 1, 256, 131072, host_seq_lens=full(16, 131072))["chunk"] == 8192
+    assert binding.plan(64, 48, 1, 256, 2048, host_seq_lens=full(64, 2048))["chunk"] == 512  # unchanged
+    assert binding.plan(4, 48, 1, 256, 131072, host_seq_lens=full(4, 131072))["chunk"] == 2048
+    gen = torch.Generator().manual_seed(5)
+    ragged = torch.randint(1, 4097, (32,), generator=gen, dtype=torch.int32)
+    assert binding.plan(32, 64, 8, 128, 4096, host_seq_lens=ragged)["chunk"] == 1024  # 256 units, ragged
+    assert binding.plan(16, 64, 8, 128, 4096, host_seq_lens=ragged[:16])["chunk"] == 2048  # 128 units
+    big = torch.randint(1, 8193, (256,), generator=gen, dtype=torch.int32)
+    assert binding.plan(256, 32, 8, 128, 8192, host_seq_lens=big)["chunk"] == 1024
+    # lengths within one quantum of each other count as uniform; a shorter batch keeps Lmax covered
+    near = full(32, 4000)
+    near[3] = 3900
+    p = binding.plan(32, 64, 8, 128, 8192, host_seq_lens=near)
+    assert p["chunk"] == 4096 and p["chunk"] * p["max_splits"] >= 8192
+    w = binding.plan(32, 64, 8, 128, 8192, window=1024, host_seq_lens=full(32, 8000))
+    assert w["chunk"] * w["max_splits"] >= 1024
+    with pytest.raises(ValueError):  # the binding checks the count before the planner reads B values
+        binding._checked_lens(full(31, 4096), 32)
 
 
 def test_chunk_schedule_covers_every_valid_position_once():
