@@ -195,13 +195,11 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         // positions (measured on MI355X, B=4, Hq=48, D=256, W=8192: 14.6 us at
         // 128 against 16.0 us at 256).
         const bool windowed = o.window > 0 && o.window < Lmax;
-        // a uniform batch (host lengths all within one quantum of the
-        // longest) on a bf16 cache: about one chunk per CU over the positions
-        // actually attended, up to whole sequences
-        // a ragged batch (known from the host lengths) of at least one unit
-        // per CU: the short chunks of a many-unit batch
-        long long work = span;
-        bool coarse = false, ragged = false;
+        // The host copy of the lengths, when the caller passes one, tells a
+        // uniform batch (every length within one quantum of the longest) from
+        // a ragged one; see the chunk bounds above.
+        long long work = span;  // positions per row the chunks are sized for
+        bool uniform = false, ragged = false;
         if (o.host_seq_lens && B > 0 && p.variant == MQA_VARIANT_MFMA) {
             long long lo = span, hi = 0;
             for (int b = 0; b < B; ++b) {
@@ -211,16 +209,21 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
                 lo = n < lo ? n : lo;
                 hi = n > hi ? n : hi;
             }
-            const bool uniform = hi > 0 && hi - lo < kChunkQuantum;
-            coarse = uniform && o.kv_format == MQA_KV_BF16;
+            uniform = hi > 0 && hi - lo < kChunkQuantum;
             ragged = !uniform && hi > 0;
-            if (coarse) work = hi;
+            if (uniform) work = hi;
         }
+        const bool coarse = uniform && o.kv_format == MQA_KV_BF16;
         long long c = round_up(ceil_div(work * units, kTargetWorkgroups), kChunkQuantum);
-        const long long cmax = p.variant != MQA_VARIANT_MFMA                       ? kMaxChunkValu
-                               : coarse                                        ? round_up(work, kChunkQuantum)
-                               : units >= kManyUnits || (ragged && units >= kComputeUnits) ? kMaxChunkMfmaMany
-                                                                                 : kMaxChunkMfma;
+        long long cmax;
+        if (p.variant != MQA_VARIANT_MFMA)
+            cmax = kMaxChunkValu;
+        else if (coarse)
+            cmax = round_up(work, kChunkQuantum);  // up to whole sequences
+        else if (units >= kManyUnits || (ragged && units >= kComputeUnits))
+            cmax = kMaxChunkMfmaMany;
+        else
+            cmax = kMaxChunkMfma;
         const long long cmin = windowed ? kChunkQuantum : kMinChunk;
         if (c < cmin) c = cmin;
         if (c > cmax) c = cmax;
