@@ -782,11 +782,14 @@ def test_multi_full_size(name, T):
     w = WORKLOADS[name]
     print("case full multi", name, T, flush=True)
     inp = make_multi_inputs(w, T, device=DEV, poison_padding=w.ragged)
-    out = binding.decode_multi(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
-    torch.cuda.synchronize()
     ref = oracle.decode_multi(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
-    err = check_close(out, ref, "%s T=%d" % (name, T))
-    print("full %s T=%d: all %d sequences checked, max abs err %.3g" % (name, T, w.B, err), flush=True)
+    # with the host copy of the lengths (the benchmark's plan) and without
+    for h in (inp["seq_lens"].cpu(), None):
+        out = binding.decode_multi(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], host_seq_lens=h)
+        torch.cuda.synchronize()
+        err = check_close(out, ref, "%s T=%d hint %s" % (name, T, h is not None))
+        print("full %s T=%d hint %s: all %d sequences checked, max abs err %.3g" % (name, T, h is not None, w.B, err),
+              flush=True)
 
 
 # ------------------------------------------------------ full-size workloads
@@ -800,11 +803,19 @@ def test_full_size_workload(name, variant):
     w = WORKLOADS[name]
     print("case full", name, variant, flush=True)
     inp = make_inputs(w, device=DEV, poison_padding=w.ragged)
-    out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], variant=variant)
-    torch.cuda.synchronize()
     ref = oracle.decode(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
-    err = check_close(out, ref, "%s %s" % (name, variant))
-    print("full %s %s: all %d sequences checked, max abs err %.3g" % (name, variant, w.B, err), flush=True)
+    # with the host copy of the lengths, as the benchmark plans it (a uniform
+    # batch may then get other chunks), and without
+    host = inp["seq_lens"].cpu()
+    plans = {binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, inp["scale"], variant, host_seq_lens=h)["chunk"]: h
+             for h in (host, None)}
+    for chunk, h in plans.items():
+        out = binding.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"], variant=variant,
+                             host_seq_lens=h)
+        torch.cuda.synchronize()
+        err = check_close(out, ref, "%s %s chunk %d" % (name, variant, chunk))
+        print("full %s %s chunk %d: all %d sequences checked, max abs err %.3g" % (name, variant, chunk, w.B, err),
+              flush=True)
 
 
 @pytest.mark.parametrize("name", ["tiny", "palm", "ragged"])
