@@ -118,7 +118,7 @@ def test_edge_lengths(variant):
 
 @pytest.mark.parametrize("combine", ["fused", "separate"])
 def test_many_chunks_and_shape_changes_reuse_the_workspace(combine):
-    """Fused arrival counters must be back at zero after every call, whatever the shape."""
+    """The fused combine's counters must be back at zero after every call, whatever the shape."""
     cases = [Workload("ws1", B=8, Hq=48, Hkv=1, D=256, Lmax=2000, seed=90, len_lo=1, len_hi=2000),
              Workload("ws2", B=16, Hq=16, Hkv=2, D=128, Lmax=1900, seed=91, len_lo=1000, len_hi=1900),
              Workload("ws3", B=8, Hq=48, Hkv=1, D=256, Lmax=2000, seed=92, len_lo=1, len_hi=2000)]
@@ -131,9 +131,9 @@ def test_many_chunks_and_shape_changes_reuse_the_workspace(combine):
 
 @pytest.mark.parametrize("variant", ["mfma", "valu"])
 def test_fused_combine_reads_this_calls_partials(variant):
-    """The fused combine's last workgroup reads the other chunks' partials through device-coherent
-    loads: two different input sets alternate through the same cached workspace, so a stale read
-    (the previous call's partials) would show as a wrong result."""
+    """The fused combine's workgroups read each other's partials through device-coherent loads:
+    two different input sets alternate through the same cached workspace, so a stale read (the
+    previous call's partials) would show as a wrong result."""
     ws = [Workload("fz%d" % i, B=8, Hq=48, Hkv=1, D=256, Lmax=1536, seed=1200 + i, len_lo=700, len_hi=1536)
           for i in range(2)]
     cases = []
