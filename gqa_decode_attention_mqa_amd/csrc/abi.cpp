@@ -268,6 +268,7 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
         c.chunk = plan.chunk;
         c.max_splits = plan.max_splits;
         c.window = a.window;
+        c.dsplit = plan.combine_dsplit;
         e = mqa::launch_combine(plan, c, stream, opts ? static_cast<hipEvent_t>(opts->ev_combine_begin) : nullptr,
                                 opts ? static_cast<hipEvent_t>(opts->ev_combine_end) : nullptr);
         if (e != hipSuccess) return hip_fail(e, "combine kernel launch");

@@ -10,10 +10,12 @@
 // A row with T query tokens has T * Hq query rows (token i, head h); their
 // partials sit at query row i * G + h % G of unit (row, h / G).
 //
-// Many chunks: one workgroup per (row, token, query head), 256 threads.  Thread t owns
-// a slot of four columns (t mod D/4) and the chunks s = t div (D/4), step 256/(D/4), so
-// several chunks are read in parallel; the per-thread sums are then added in a
-// fixed order through LDS, so the result is bitwise reproducible for a plan.
+// Many chunks: dsplit workgroups per (row, token, query head), each merging a
+// slice of D/dsplit columns with 256 threads (dsplit > 1 only while the grid
+// would not cover the CUs).  With S = D/(4 dsplit) four-column slots, thread t
+// owns slot t mod S and the chunks s = t div S, step 256/S, so several chunks
+// are read in parallel; the per-thread sums are then added in a fixed order
+// through LDS, so the result is bitwise reproducible for a plan.
 #include "kernel_common.hpp"
 #include "launch.hpp"
 
@@ -39,7 +41,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     __shared__ float s_w[256];
 
     const int tid = threadIdx.x;
-    const long long rh = blockIdx.x;  // (row * T + token) * Hq + h
+    const long long rh = blockIdx.x / a.dsplit;  // (row * T + token) * Hq + h
+    const int ds = (int)(blockIdx.x % a.dsplit);  // this workgroup's slice of d
     const int h = (int)(rh % a.Hq);
     const long long rt = rh / a.Hq;
     const long long row = rt / a.T;
@@ -67,16 +70,17 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
     M = M == -INFINITY ? 0.f : M;
 
-    const int slots = a.D / 4;          // 16, 32 or 64
+    const int slots = a.D / 4 / a.dsplit;  // 16-byte column slots of this workgroup's slice
     const int lanes_per_slot = 256 / slots;
     const int slot = tid % slots, sl = tid / slots;
+    const int col = ds * slots + slot;     // slot in the row
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-#pragma unroll 4
+#pragma unroll 8
     for (int s = sl; s < nsplit; s += lanes_per_slot) {
         const f32x2_t mle = ml[s * step];
         const float wgt = __builtin_amdgcn_exp2f(mle.x - M);
-        const u32x2_t hv = *reinterpret_cast<const u32x2_t*>(po + s * step * a.D + 4 * slot);
+        const u32x2_t hv = *reinterpret_cast<const u32x2_t*>(po + s * step * a.D + 4 * col);
         acc += wgt * unpack_partial4(hv, (int)mle.y);
         wsum += wgt;
     }
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
             wsum += s_w[j * slots + slot];
         }
         const __amdgpu_buffer_rsrc_t ors = make_rsrc(a.out + (size_t)rh * a.D, a.D * 4);
-        store_out16(ors, 16 * slot, acc * (wsum > 0.f ? 1.f / wsum : 0.f));
+        store_out16(ors, 16 * col, acc * (wsum > 0.f ? 1.f / wsum : 0.f));
     }
 }
 

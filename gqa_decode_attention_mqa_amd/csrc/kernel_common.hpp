@@ -70,6 +70,7 @@ struct CombineArgs {
     int T, GT;
     int chunk, max_splits;
     int window;
+    int dsplit;                // many-chunk merge: workgroups per query row, each a slice of d
 };
 
 // Query row r (0 .. T*G - 1) of unit (row, kv head kvh) is token r / G of the

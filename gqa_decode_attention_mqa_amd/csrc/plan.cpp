@@ -256,8 +256,20 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
             p.grid_combine = 0;
         else if (p.max_splits <= kCombineFewMaxSplits)  // whole head blocks of each unit
             p.grid_combine = p.rows * Hkv * ceil_div(p.GT, combine_heads_per_block(D));
-        else
-            p.grid_combine = p.rows * T * Hq;
+        else {
+            // one workgroup per query row, or up to D/64 of them per row, each
+            // merging a slice of d, until the grid covers the CUs: the merge
+            // of a row's many chunks is bound by the latency of its loads
+            // (MI355X, one sequence of 131072 positions, 48 heads, D = 256,
+            // 256 chunks: 5.2 us with 4 slices against 10.3 us with one; 8
+            // slices, or slicing on to twice the CUs, 6.3 us: the per-slot
+            // sums of more threads then take longer to add)
+            const long long rows_q = p.rows * T * Hq;
+            int ds = 1;
+            while (rows_q * ds < kComputeUnits && ds < D / 64) ds *= 2;
+            p.combine_dsplit = ds;
+            p.grid_combine = rows_q * ds;
+        }
         if (p.grid_combine > kMaxGrid)
             return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (combine grid limit)");
         const size_t parts = (size_t)p.rows * Hkv * p.max_splits * p.GT;

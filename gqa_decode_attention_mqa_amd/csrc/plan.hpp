@@ -97,6 +97,7 @@ struct Plan {
     long long grid_main = 0;         // workgroups along x of the split kernel
     int block_main = 256;
     long long grid_combine = 0;
+    int combine_dsplit = 1;          // many-chunk merge: workgroups per query row (slices of d)
     size_t workspace_bytes = 0;      // partial outputs + partial LSEs
     size_t part_o_offset = 0;        // byte offsets inside the workspace
     size_t part_ml_offset = 0;

@@ -115,8 +115,10 @@ def test_plan_invariants(B, Hq, Hkv, D, Lmax):
         assert p["combine"] == 1
         if p["max_splits"] <= 8:   # few chunks: one thread per (head, 8 columns), 2048/D heads per block
             assert p["grid_combine"] == B * Hkv * -(-G // (2048 // D))  # whole head blocks per unit
-        else:                      # many chunks: one workgroup per (row, head)
-            assert p["grid_combine"] == B * Hq
+        else:                      # many chunks: 1 .. D/64 workgroups per (row, head), a slice of d each
+            ds = p["grid_combine"] // (B * Hq)
+            assert p["grid_combine"] == B * Hq * ds and ds in (1, 2, 4) and ds <= max(1, D // 64)
+            assert ds == 1 or B * Hq * ds // 2 < 256  # slices only while the grid is below the CUs
         # fp16 partial rows plus an {lse, exponent} float pair per (chunk, head)
         assert p["workspace_bytes"] >= B * Hkv * p["max_splits"] * G * (2 * D + 8)
     else:
