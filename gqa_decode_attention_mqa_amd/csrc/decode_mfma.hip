@@ -8,10 +8,11 @@
 // w < NG owns heads 16w .. 16w+15 for every position of the chunk, so no two
 // waves ever merge softmax state; groups below 16 pad the head tile.  The
 // chunk's K and V rows are read from HBM exactly once per workgroup into an
-// LDS ring of STAGES tiles of 32 positions by two load-only waves, with
-// direct buffer-to-LDS loads (no registers hold data in flight, and
-// STAGES - 2 tiles are in flight at once); every compute wave then reads the
-// whole tile from LDS.
+// LDS ring of tiles of 32 positions by two load-only waves, with direct
+// buffer-to-LDS loads (no registers hold data in flight); every compute wave
+// then reads the whole tile from LDS.  A compute step takes PT tiles at once
+// (two for 8-bit caches at D = 256, else one); the ring holds GSTAGES steps,
+// GSTAGES - 2 of them in flight.
 //
 // Per tile, in each compute wave:
 //   * S^T = K q^T on 16x16x32 bf16 tiles: A = two 16-row K tiles (read from
@@ -56,8 +57,9 @@ struct MfmaCfg {
     // int8 caches: q.K on int8 matrix cores (16x16x64), q as 128 hi + lo
     static constexpr bool I8MMA = FMT == kKvInt8;
     static constexpr int NB8 = I8MMA ? D / 64 : 1;   // 64-wide blocks of d
-    // tiles in the LDS ring: four, i.e. two tiles in flight beyond the two
-    // in use.  bf16 D = 256 (128 KB): a fifth tile measured slower on MI355X
+    // Steps in the LDS ring: four, i.e. two steps in flight beyond the two in
+    // use (measured with one tile per step).  bf16 D = 256 (128 KB): a fifth
+    // tile measured slower on MI355X
     // (PaLM-shaped MQA 29.5 against 30.4 us per step, B=4 len 131072 87.4
     // against 88.2 us); per-workgroup timestamps show the later loop end
     // comes from the compute waves holding the ring barrier, not from loads
@@ -69,8 +71,19 @@ struct MfmaCfg {
     // 4-tile ring measured faster than deeper ones (PaLM-shaped MQA: 24.8 us
     // at 4 tiles against 29.0 us at 9; B=4, len 131072: 73.7 against 82.1 us;
     // B=32, Hkv=8, D=128: 51.6 against 53.3 us at 8 tiles)
-    static constexpr int STAGES = 4;
-    static_assert(STAGES >= 4, "two tiles in use and at least one more in flight");
+    static constexpr int GSTAGES = 4;
+    static_assert(GSTAGES >= 4, "two steps' tiles in use and at least one more in flight");
+    // Ring slots (32-position tiles) a compute step takes at once.  8-bit
+    // steps at D = 256 take two: the step's fixed chain (ring barrier, the
+    // cross-lane maximum, the rescale test, the latency of each
+    // read-product-softmax link) is then paid once per 64 positions (MI355X,
+    // split kernel, two runs: B=4 len 131072 fp8 58.7-59.8 against
+    // 63.0-63.8 us, int8 70.9-71.3 against 78.8-79.5; PaLM-shaped MQA int8
+    // 23.9-24.4 against 25.1-25.6, fp8 even).  At D = 128, where two
+    // workgroups share a CU, two slots per step measured slower (B=32, Hkv=8,
+    // len 4096, fp8: 51.0 against 46.8 us).
+    static constexpr int PT = (Q8 && D >= 256) ? 2 : 1;
+    static constexpr int STAGES = GSTAGES * PT;  // ring slots
     static constexpr int KS = D / 32;                // k-steps over d in q.K
     static constexpr int MT = D / 16;                // 16-row tiles of O^T
     static constexpr int ROWB = D * EB;              // bytes of one cached row
@@ -86,7 +99,7 @@ struct MfmaCfg {
     static constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
     static_assert(D >= 64 && D % 64 == 0, "head size");
     static_assert(LOADS % NL == 0, "every loader issues the same number of loads");
-    static_assert((STAGES - 2) * PER_WAVE <= 63, "loads in flight fit a wave's counter");
+    static_assert((GSTAGES - 2) * PT * PER_WAVE <= 63, "loads in flight fit a wave's counter");
     static_assert(NG >= 1 && NG <= 6, "one to six 16-row tiles of query rows");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
@@ -125,6 +138,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // they are loaded as zeros and masked.
     const int lo = span.lo, p0 = span.p0, p1 = span.p1, nsplit = span.nsplit;
     const int ntiles = p1 > p0 ? (p1 - p0 + C::STEP - 1) / C::STEP : 0;
+    const int nsteps = (ntiles + C::PT - 1) / C::PT;  // compute steps of PT tiles (the last may run past the end)
 
     const int rowbytes = a.Hkv * C::ROWB;  // bytes between consecutive positions of a cache
 
@@ -314,13 +328,19 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
                                                          lane < skip ? kOutOfRange : lane * 4, 0, 0, kCachePolicyNT);
         }
     };
-    // In a loader, the next tile and everything before it have landed once
-    // at most STAGES - 3 later tiles are outstanding; in every wave no LDS read
-    // is pending.  The barrier then publishes the loaders' tiles and frees the
-    // slot refilled next.  A plain s_barrier, not __syncthreads: the latter's
-    // release fence would also wait for the loads still in flight to the ring.
+    // A step's PT tiles go into ring slots PT (step mod GSTAGES) .. +PT-1.
+    auto issue_step = [&](int step) {
+#pragma unroll
+        for (int u = 0; u < C::PT; ++u) issue_tile(C::PT * step + u);
+    };
+    // In a loader, the next step's tiles and everything before them have
+    // landed once at most GSTAGES - 3 later steps are outstanding; in every
+    // wave no LDS read is pending.  The barrier then publishes the loaders'
+    // tiles and frees the slots refilled next.  A plain s_barrier, not
+    // __syncthreads: the latter's release fence would also wait for the loads
+    // still in flight to the ring.
     auto ring_sync = [&]() {
-        __builtin_amdgcn_s_waitcnt(kVmcntStages<C::STAGES - 3, C::PER_WAVE>() & ~(0xF << 8));
+        __builtin_amdgcn_s_waitcnt(kVmcntStages<C::GSTAGES - 3, C::PT * C::PER_WAVE>() & ~(0xF << 8));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -509,9 +529,16 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     };
     // Second part: the online softmax proper, free of branches so that it can
     // share a basic block (and the issue slots) with the matrix products.
-    auto softmax_finish = [&](f32x4_t (&sacc)[2], const f32x4_t (&vsc)[2], u32x4_t& pb, float& alpha) {
-        float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    // It takes the PT tiles of a step at once: one maximum, one rescale test.
+    auto softmax_finish = [&](f32x4_t (&sacc)[C::PT][2], const f32x4_t (&vsc)[C::PT][2], u32x4_t (&pb)[C::PT],
+                              float& alpha) {
+        auto tile_max = [](const f32x4_t (&x)[2]) {
+            return fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+        };
+        float mx = tile_max(sacc[0]);
+#pragma unroll
+        for (int u = 1; u < C::PT; ++u) mx = fmaxf(mx, tile_max(sacc[u]));
         mx = max_xor32(max_xor16(mx));
         const bool moved = mx > m_run + kRescaleSlack;
         alpha = moved ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
@@ -521,33 +548,30 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float lsum = 0.f;
 #pragma unroll
-        for (int mq = 0; mq < 2; ++mq) {
-            if constexpr (C::Q8) {
-                float pr[4];
+        for (int u = 0; u < C::PT; ++u)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pr[r] = __builtin_amdgcn_exp2f(sacc[mq][r] - m_use);
-                    lsum += pr[r];
+            for (int mq = 0; mq < 2; ++mq) {
+                if constexpr (C::Q8) {
+                    float pr[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pr[r] = __builtin_amdgcn_exp2f(sacc[u][mq][r] - m_use);
+                        lsum += pr[r];
+                    }
+                    pb[u][2 * mq] = pack2_bf16_rne(pr[0] * vsc[u][mq][0], pr[1] * vsc[u][mq][1]);
+                    pb[u][2 * mq + 1] = pack2_bf16_rne(pr[2] * vsc[u][mq][2], pr[3] * vsc[u][mq][3]);
+                } else {
+                    const uint32_t lo = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[u][mq][0] - m_use),
+                                                       __builtin_amdgcn_exp2f(sacc[u][mq][1] - m_use));
+                    const uint32_t hi = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[u][mq][2] - m_use),
+                                                       __builtin_amdgcn_exp2f(sacc[u][mq][3] - m_use));
+                    pb[u][2 * mq] = lo;
+                    pb[u][2 * mq + 1] = hi;
+                    lsum += (bf16_lo_f32(lo) + bf16_hi_f32(lo)) + (bf16_lo_f32(hi) + bf16_hi_f32(hi));
                 }
-                pb[2 * mq] = pack2_bf16_rne(pr[0] * vsc[mq][0], pr[1] * vsc[mq][1]);
-                pb[2 * mq + 1] = pack2_bf16_rne(pr[2] * vsc[mq][2], pr[3] * vsc[mq][3]);
-            } else {
-                const uint32_t lo = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][0] - m_use),
-                                                   __builtin_amdgcn_exp2f(sacc[mq][1] - m_use));
-                const uint32_t hi = pack2_bf16_rne(__builtin_amdgcn_exp2f(sacc[mq][2] - m_use),
-                                                   __builtin_amdgcn_exp2f(sacc[mq][3] - m_use));
-                pb[2 * mq] = lo;
-                pb[2 * mq + 1] = hi;
-                lsum += (bf16_lo_f32(lo) + bf16_hi_f32(lo)) + (bf16_lo_f32(hi) + bf16_hi_f32(hi));
             }
-        }
         l_run = l_run * alpha + lsum;
         return __any(moved);
-    };
-    auto softmax_tile = [&](int tile, int soff, f32x4_t (&sacc)[2], u32x4_t& pb, float& alpha) {
-        f32x4_t vsc[2];
-        softmax_prep(tile, soff, sacc, vsc);
-        return softmax_finish(sacc, vsc, pb, alpha);
     };
     // O^T += V^T P^T for one tile.  The A operand (row d = 16m + li, eight
     // positions per lane group) comes straight from LDS with transposing
@@ -601,70 +625,87 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         }
     };
 
-    // Prologue: tiles 0 .. STAGES-3 in flight (tiles past the end read nothing).
+    // Prologue: steps 0 .. GSTAGES-3 in flight (tiles past the end read nothing).
 #pragma unroll
-    for (int t = 0; t < C::STAGES - 2; ++t) issue_tile(t);
+    for (int st = 0; st < C::GSTAGES - 2; ++st) issue_step(st);
 
-    // Software pipeline: step `tile` computes q.K of `tile` + 1 with its
-    // softmax and P.V of `tile` (P^T made in the previous step), so the matrix
+    // Software pipeline: step `step` computes q.K of step + 1 with its
+    // softmax and P.V of `step` (P^T made in the previous step), so the matrix
     // pipe and the vector ALU overlap inside each wave.  Order inside a step:
-    // q.K of the next tile (its K reads kept eight ahead), the V^T reads of
+    // q.K of the next step (its K reads kept eight ahead), the V^T reads of
     // the first half of d and the logit scaling while they land; then, in one
     // basic block, P.V of the first half with the second half's V^T reads in
     // its shadow, the rest of the softmax while those land, P.V of the second
     // half.  A wave issues in order, and one 16x16x32 product takes about 17
     // cycles to issue but about 50 before a dependent one may start (MI355X),
     // so the order decides how much of the step is waiting.  Ring slots in use
-    // during a step: `tile` and `tile` + 1; the step refills the slot of
-    // `tile` - 1 with `tile` + STAGES - 1, so STAGES - 2 tiles stay in flight.
-    u32x4_t pb = {0u, 0u, 0u, 0u};
-    if (ntiles > 0) {
-        ring_sync();  // tile 0 landed
-        issue_tile(C::STAGES - 2);
+    // during a step: those of `step` and step + 1; the step refills the slots
+    // of step - 1 with step + GSTAGES - 1, so GSTAGES - 2 steps stay in flight.
+    constexpr std::integral_constant<int, 0> first_half{};
+    constexpr std::integral_constant<int, 1> second_half{};
+    auto slot_off = [](int tile) { return (tile % C::STAGES) * C::STAGE_BYTES; };
+    u32x4_t pb[C::PT];
+#pragma unroll
+    for (int u = 0; u < C::PT; ++u) pb[u] = u32x4_t{0u, 0u, 0u, 0u};
+    if (nsteps > 0) {
+        ring_sync();  // step 0 landed
+        issue_step(C::GSTAGES - 2);
         if (w < NG) {
-            f32x4_t sacc[2];
-            qk_tile(0, sacc);
+            f32x4_t sacc[C::PT][2], vsc[C::PT][2];
+#pragma unroll
+            for (int u = 0; u < C::PT; ++u) qk_tile(slot_off(u), sacc[u]);
+#pragma unroll
+            for (int u = 0; u < C::PT; ++u) softmax_prep(u, slot_off(u), sacc[u], vsc[u]);
             float alpha;
-            softmax_tile(0, 0, sacc, pb, alpha);  // O is still zero: no rescale
+            softmax_finish(sacc, vsc, pb, alpha);  // O is still zero: no rescale
         }
     }
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int soff = (tile % C::STAGES) * C::STAGE_BYTES, soff_next = ((tile + 1) % C::STAGES) * C::STAGE_BYTES;
-        ring_sync();  // tile + 1 landed (a no-op read past the end)
-        issue_tile(tile + C::STAGES - 1);
+    for (int step = 0; step < nsteps; ++step) {
+        const int t0 = C::PT * step, t1 = t0 + C::PT;  // first tile of this step and of the next
+        ring_sync();  // step + 1 landed (no-op reads past the end)
+        issue_step(step + C::GSTAGES - 1);
         if (w >= NG) continue;  // the load-only wave
-        constexpr std::integral_constant<int, 0> first_half{};
-        constexpr std::integral_constant<int, 1> second_half{};
-        u32x2_t vlo[MH], vhi[MH];
-        f32x4_t sacc[2], vsc[2];
-        if (tile + 1 < ntiles) {
-            // q.K of the next tile first: the V^T reads issued after its
+        u32x2_t vlo[C::PT][MH], vhi[C::PT][MH];
+        f32x4_t sacc[C::PT][2], vsc[C::PT][2];
+        if (step + 1 < nsteps) {
+            // q.K of the next step first: the V^T reads issued after its
             // K reads land while its products and the logit scaling run
-            qk_tile(soff_next, sacc);
-            pv_issue(soff, first_half, vlo, vhi);
-            softmax_prep(tile + 1, soff_next, sacc, vsc);
+#pragma unroll
+            for (int u = 0; u < C::PT; ++u) qk_tile(slot_off(t1 + u), sacc[u]);
+#pragma unroll
+            for (int u = 0; u < C::PT; ++u) pv_issue(slot_off(t0 + u), first_half, vlo[u], vhi[u]);
+#pragma unroll
+            for (int u = 0; u < C::PT; ++u) softmax_prep(t1 + u, slot_off(t1 + u), sacc[u], vsc[u]);
         } else {
-            pv_issue(soff, first_half, vlo, vhi);
-            // past the last tile: all logits -inf, so the softmax step below
+#pragma unroll
+            for (int u = 0; u < C::PT; ++u) pv_issue(slot_off(t0 + u), first_half, vlo[u], vhi[u]);
+            // past the last step: all logits -inf, so the softmax step below
             // leaves m and l unchanged (the max does not move, every weight is 0)
 #pragma unroll
-            for (int mq = 0; mq < 2; ++mq) {
-                sacc[mq] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                vsc[mq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int u = 0; u < C::PT; ++u)
+#pragma unroll
+                for (int mq = 0; mq < 2; ++mq) {
+                    sacc[u][mq] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                    vsc[u][mq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
         }
         // One basic block from here (the softmax finish is branch-free): P.V of
-        // this tile and the softmax of the next, whose vector instructions
+        // this step and the softmax of the next, whose vector instructions
         // issue while the products run.
-        pv_mma(pb, first_half, vlo, vhi);
-        pv_issue(soff, second_half, vlo, vhi);
-        u32x4_t pb_next;
+#pragma unroll
+        for (int u = 0; u < C::PT; ++u) pv_mma(pb[u], first_half, vlo[u], vhi[u]);
+#pragma unroll
+        for (int u = 0; u < C::PT; ++u) pv_issue(slot_off(t0 + u), second_half, vlo[u], vhi[u]);
+        u32x4_t pb_next[C::PT];
         float alpha;
         const bool moved = softmax_finish(sacc, vsc, pb_next, alpha);
         // tie the softmax results here so the compiler cannot sink their
         // computation below the products (or past the rescale branch)
-        asm volatile("" : "+v"(pb_next), "+v"(l_run), "+v"(alpha));
-        pv_mma(pb, second_half, vlo, vhi);
+#pragma unroll
+        for (int u = 0; u < C::PT; ++u) asm volatile("" : "+v"(pb_next[u]));
+        asm volatile("" : "+v"(l_run), "+v"(alpha));
+#pragma unroll
+        for (int u = 0; u < C::PT; ++u) pv_mma(pb[u], second_half, vlo[u], vhi[u]);
         if constexpr (!C::Q8) {
             // products and vector instructions alternate
             static_for<0, 2 * MH>([&](auto) {
@@ -672,7 +713,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
             });
         }
-        pb = pb_next;
+#pragma unroll
+        for (int u = 0; u < C::PT; ++u) pb[u] = pb_next[u];
         if (moved) {
 #pragma unroll
             for (int m = 0; m < C::MT; ++m) oacc[m] = oacc[m] * alpha;
