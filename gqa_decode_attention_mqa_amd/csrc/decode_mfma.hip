@@ -5,14 +5,15 @@
 // Layer Partitioning", the 8-head groups of grouped-query attention) and
 // every cache format (bf16, E4M3 or int8 codes) a workgroup owns (query row, kv
 // head, chunk of positions, block of 16*NG query rows, NG = 1..6).  Compute wave
-// w < NG owns heads 16w .. 16w+15 for every position of the chunk, so no two
-// waves ever merge softmax state; groups below 16 pad the head tile.  The
-// chunk's K and V rows are read from HBM exactly once per workgroup into an
-// LDS ring of tiles of 32 positions by two load-only waves, with direct
-// buffer-to-LDS loads (no registers hold data in flight); every compute wave
-// then reads the whole tile from LDS.  A compute step takes PT tiles at once
-// (two for 8-bit caches at D = 256, else one); the ring holds GSTAGES steps,
-// GSTAGES - 2 of them in flight.
+// w < NG owns heads 16w .. 16w+15 for every position of the chunk; groups
+// below 16 pad the head tile.  The chunk's K and V rows are read from HBM
+// exactly once per workgroup into an LDS ring of tiles of 32 positions by two
+// load-only waves, with direct buffer-to-LDS loads (no registers hold data in
+// flight); every compute wave then reads the whole tile from LDS.  A compute
+// step takes PT tiles at once (two for 8-bit caches at D = 256, else one); the
+// ring holds GSTAGES steps, GSTAGES - 2 of them in flight.  8-bit caches at
+// D = 256 with NG <= 3 give each 16-row tile two compute waves, one per tile
+// of a step, whose softmax states are merged once after the loop.
 //
 // Per tile, in each compute wave:
 //   * S^T = K q^T on 16x16x32 bf16 tiles: A = two 16-row K tiles (read from
@@ -45,8 +46,6 @@ struct MfmaCfg {
     // kept off the compute waves.  Two loaders keep three tiles in flight
     // within the 63 loads a wave can have outstanding.
     static constexpr int NL = 2;
-    static constexpr int NW = NG + NL;
-    static constexpr int THREADS = 64 * NW;
     static constexpr int STEP = 32;                  // positions per tile
     static constexpr bool Q8 = FMT != kKvBf16;       // 8-bit codes with a scale per row
     static constexpr int EB = Q8 ? 1 : 2;            // bytes per cached element
@@ -84,6 +83,18 @@ struct MfmaCfg {
     // len 4096, fp8: 51.0 against 46.8 us).
     static constexpr int PT = (Q8 && D >= 256) ? 2 : 1;
     static constexpr int STAGES = GSTAGES * PT;  // ring slots
+    // Compute waves per 16-row tile of query rows: SUBS > 1 splits a step's
+    // tiles between that many waves, each with its own softmax state, merged
+    // once after the loop (while the workgroup stays within 8 waves).  Each
+    // wave's chain of dependent work is then one tile per step, and two
+    // chains share a SIMD (MI355X, split kernel, two runs: B=4 len 131072
+    // fp8 51.9-52.8 against 59.1-59.4 us with one wave per tile, int8 66.0
+    // against 70.9-71.1; PaLM-shaped MQA even).
+    static constexpr int SUBS = (PT > 1 && NG <= 3) ? PT : 1;
+    static constexpr int NU = PT / SUBS;  // tiles of a step per compute wave
+    static constexpr int NC = NG * SUBS;  // compute waves
+    static constexpr int NW = NC + NL;
+    static constexpr int THREADS = 64 * NW;
     static constexpr int KS = D / 32;                // k-steps over d in q.K
     static constexpr int MT = D / 16;                // 16-row tiles of O^T
     static constexpr int ROWB = D * EB;              // bytes of one cached row
@@ -101,6 +112,7 @@ struct MfmaCfg {
     static_assert(LOADS % NL == 0, "every loader issues the same number of loads");
     static_assert((GSTAGES - 2) * PT * PER_WAVE <= 63, "loads in flight fit a wave's counter");
     static_assert(NG >= 1 && NG <= 6, "one to six 16-row tiles of query rows");
+    static_assert(NW <= 8, "the launch bound");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
@@ -117,6 +129,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, kg = lane >> 4;
+    // compute wave w < NC: 16-row tile hw of the block's query rows, and
+    // tiles u0 .. u0 + NU - 1 of each step
+    const int hw = w % NG, u0 = (w / NG) * C::NU;
 
     long long unit;
     int s;
@@ -159,13 +174,13 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // in [2^12, 2^13): each q is rounded to 2^-13 of the head's largest |q|.
     i32x4_t qih[C::NB8], qil[C::NB8];
     float qk8 = 1.f;
-    if (w >= NG) {
+    if (w >= C::NC) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qb[ks] = u32x4_t{0u, 0u, 0u, 0u};
     } else if constexpr (C::F8MMA) {
         const size_t q0 = qrow_offset(a, row, kvh, 0);
         const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(a, row, kvh, gq - 1) - q0 + D) * 2);
-        const int r = g0 + 16 * w + li;
+        const int r = g0 + 16 * hw + li;
         const int qoff = r < gq ? (int)(qrow_offset(a, row, kvh, r) - q0) * 2 : kOutOfRange;
         u32x4_t raw[C::NH8][4];
 #pragma unroll
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     } else if constexpr (C::I8MMA) {
         const size_t q0 = qrow_offset(a, row, kvh, 0);
         const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(a, row, kvh, gq - 1) - q0 + D) * 2);
-        const int r = g0 + 16 * w + li;
+        const int r = g0 + 16 * hw + li;
         const int qoff = r < gq ? (int)(qrow_offset(a, row, kvh, r) - q0) * 2 : kOutOfRange;
         u32x4_t raw[C::NB8][2];
 #pragma unroll
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         // the unit's query rows span T tokens, Hq * D elements apart
         const size_t q0 = qrow_offset(a, row, kvh, 0);
         const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + q0, (int)(qrow_offset(a, row, kvh, gq - 1) - q0 + D) * 2);
-        const int r = g0 + 16 * w + li;
+        const int r = g0 + 16 * hw + li;
         const int qoff = r < gq ? (int)(qrow_offset(a, row, kvh, r) - q0) * 2 : kOutOfRange;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
@@ -287,7 +302,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     const int nblk = (a.block_table && p1 > p0) ? ((p1 - 1) >> a.page_shift) - blk0 + 1 : 0;
     const bool pages_in_lanes = nblk > 0 && nblk <= 64;
     int chunk_page = 0;
-    if (pages_in_lanes && w >= NG) {
+    if (pages_in_lanes && w >= C::NC) {
         if (lane < nblk) chunk_page = a.block_table[(size_t)b * a.max_blocks + blk0 + lane];
         // the first tile's address needs it anyway; waiting here also tells the
         // compiler that no load into it is pending inside the loop
@@ -299,7 +314,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         return kv_loc(a, b, kvh, t0);
     };
     auto issue_tile = [&](int tile) {
-        if (w < NG) return;
+        if (w < C::NC) return;
         const int t0 = p0 + tile * C::STEP;
         const int rows = max(0, min(C::STEP, p1 - t0));
         const int skip = lo - t0;  // rows before a sliding window (> 0 in the first tile only)
@@ -309,7 +324,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         unsigned char* slot = smem + (tile % C::STAGES) * C::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < C::KPW; ++i) {
-            const int jj = (w - NG) + C::NL * i;
+            const int jj = (w - C::NC) + C::NL * i;
             const int p = jj * 64 + lane;  // 16-byte LDS slot in the tile
             const int t = p / C::CPR, cs = p % C::CPR;
             const int voff = t < skip ? kOutOfRange : t * rowbytes + ((cs ^ tile_key<FMT, D>(t)) * 16);
@@ -321,10 +336,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         if constexpr (C::Q8) {
             // the tile rows' scales (contiguous per kv head): loader 0 the K
             // scales, loader 1 the V scales, one dword per lane of the first 32
-            const float* sc = (w == NG ? a.k_scale : a.v_scale) + loc.scale;
+            const float* sc = (w == C::NC ? a.k_scale : a.v_scale) + loc.scale;
             const __amdgpu_buffer_rsrc_t srs = make_rsrc(sc, rows * 4);
             if (lane < C::STEP)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_ptr_t)(slot + 2 * C::TILE_BYTES + (w - NG) * 128), 4,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_ptr_t)(slot + 2 * C::TILE_BYTES + (w - C::NC) * 128), 4,
                                                          lane < skip ? kOutOfRange : lane * 4, 0, 0, kCachePolicyNT);
         }
     };
@@ -493,7 +508,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // attend positions below lim = qbase + i + 1 (none for a token before the
     // sequence start); tiles reaching past tmask hold a position some column
     // must not see.
-    const int qpos = qbase + (g0 + 16 * w + li) / a.G;
+    const int qpos = qbase + (g0 + 16 * hw + li) / a.G;
     const int lim = min(p1, qpos + 1);
     const int tmask = p1 - a.T + 1;
     // 8-bit caches: the logit of a position is scaled by its K row's scale,
@@ -530,7 +545,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // Second part: the online softmax proper, free of branches so that it can
     // share a basic block (and the issue slots) with the matrix products.
     // It takes the PT tiles of a step at once: one maximum, one rescale test.
-    auto softmax_finish = [&](f32x4_t (&sacc)[C::PT][2], const f32x4_t (&vsc)[C::PT][2], u32x4_t (&pb)[C::PT],
+    auto softmax_finish = [&](f32x4_t (&sacc)[C::NU][2], const f32x4_t (&vsc)[C::NU][2], u32x4_t (&pb)[C::NU],
                               float& alpha) {
         auto tile_max = [](const f32x4_t (&x)[2]) {
             return fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
@@ -538,7 +553,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         };
         float mx = tile_max(sacc[0]);
 #pragma unroll
-        for (int u = 1; u < C::PT; ++u) mx = fmaxf(mx, tile_max(sacc[u]));
+        for (int u = 1; u < C::NU; ++u) mx = fmaxf(mx, tile_max(sacc[u]));
         mx = max_xor32(max_xor16(mx));
         const bool moved = mx > m_run + kRescaleSlack;
         alpha = moved ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
@@ -548,7 +563,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float lsum = 0.f;
 #pragma unroll
-        for (int u = 0; u < C::PT; ++u)
+        for (int u = 0; u < C::NU; ++u)
 #pragma unroll
             for (int mq = 0; mq < 2; ++mq) {
                 if constexpr (C::Q8) {
@@ -644,45 +659,45 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     constexpr std::integral_constant<int, 0> first_half{};
     constexpr std::integral_constant<int, 1> second_half{};
     auto slot_off = [](int tile) { return (tile % C::STAGES) * C::STAGE_BYTES; };
-    u32x4_t pb[C::PT];
+    u32x4_t pb[C::NU];
 #pragma unroll
-    for (int u = 0; u < C::PT; ++u) pb[u] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int u = 0; u < C::NU; ++u) pb[u] = u32x4_t{0u, 0u, 0u, 0u};
     if (nsteps > 0) {
         ring_sync();  // step 0 landed
         issue_step(C::GSTAGES - 2);
-        if (w < NG) {
-            f32x4_t sacc[C::PT][2], vsc[C::PT][2];
+        if (w < C::NC) {
+            f32x4_t sacc[C::NU][2], vsc[C::NU][2];
 #pragma unroll
-            for (int u = 0; u < C::PT; ++u) qk_tile(slot_off(u), sacc[u]);
+            for (int u = 0; u < C::NU; ++u) qk_tile(slot_off(u0 + u), sacc[u]);
 #pragma unroll
-            for (int u = 0; u < C::PT; ++u) softmax_prep(u, slot_off(u), sacc[u], vsc[u]);
+            for (int u = 0; u < C::NU; ++u) softmax_prep(u0 + u, slot_off(u0 + u), sacc[u], vsc[u]);
             float alpha;
             softmax_finish(sacc, vsc, pb, alpha);  // O is still zero: no rescale
         }
     }
     for (int step = 0; step < nsteps; ++step) {
-        const int t0 = C::PT * step, t1 = t0 + C::PT;  // first tile of this step and of the next
+        const int t0 = C::PT * step + u0, t1 = t0 + C::PT;  // this wave's first tile of this step and of the next
         ring_sync();  // step + 1 landed (no-op reads past the end)
         issue_step(step + C::GSTAGES - 1);
-        if (w >= NG) continue;  // the load-only wave
-        u32x2_t vlo[C::PT][MH], vhi[C::PT][MH];
-        f32x4_t sacc[C::PT][2], vsc[C::PT][2];
+        if (w >= C::NC) continue;  // the load-only wave
+        u32x2_t vlo[C::NU][MH], vhi[C::NU][MH];
+        f32x4_t sacc[C::NU][2], vsc[C::NU][2];
         if (step + 1 < nsteps) {
             // q.K of the next step first: the V^T reads issued after its
             // K reads land while its products and the logit scaling run
 #pragma unroll
-            for (int u = 0; u < C::PT; ++u) qk_tile(slot_off(t1 + u), sacc[u]);
+            for (int u = 0; u < C::NU; ++u) qk_tile(slot_off(t1 + u), sacc[u]);
 #pragma unroll
-            for (int u = 0; u < C::PT; ++u) pv_issue(slot_off(t0 + u), first_half, vlo[u], vhi[u]);
+            for (int u = 0; u < C::NU; ++u) pv_issue(slot_off(t0 + u), first_half, vlo[u], vhi[u]);
 #pragma unroll
-            for (int u = 0; u < C::PT; ++u) softmax_prep(t1 + u, slot_off(t1 + u), sacc[u], vsc[u]);
+            for (int u = 0; u < C::NU; ++u) softmax_prep(t1 + u, slot_off(t1 + u), sacc[u], vsc[u]);
         } else {
 #pragma unroll
-            for (int u = 0; u < C::PT; ++u) pv_issue(slot_off(t0 + u), first_half, vlo[u], vhi[u]);
+            for (int u = 0; u < C::NU; ++u) pv_issue(slot_off(t0 + u), first_half, vlo[u], vhi[u]);
             // past the last step: all logits -inf, so the softmax step below
             // leaves m and l unchanged (the max does not move, every weight is 0)
 #pragma unroll
-            for (int u = 0; u < C::PT; ++u)
+            for (int u = 0; u < C::NU; ++u)
 #pragma unroll
                 for (int mq = 0; mq < 2; ++mq) {
                     sacc[u][mq] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -693,19 +708,19 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         // this step and the softmax of the next, whose vector instructions
         // issue while the products run.
 #pragma unroll
-        for (int u = 0; u < C::PT; ++u) pv_mma(pb[u], first_half, vlo[u], vhi[u]);
+        for (int u = 0; u < C::NU; ++u) pv_mma(pb[u], first_half, vlo[u], vhi[u]);
 #pragma unroll
-        for (int u = 0; u < C::PT; ++u) pv_issue(slot_off(t0 + u), second_half, vlo[u], vhi[u]);
-        u32x4_t pb_next[C::PT];
+        for (int u = 0; u < C::NU; ++u) pv_issue(slot_off(t0 + u), second_half, vlo[u], vhi[u]);
+        u32x4_t pb_next[C::NU];
         float alpha;
         const bool moved = softmax_finish(sacc, vsc, pb_next, alpha);
         // tie the softmax results here so the compiler cannot sink their
         // computation below the products (or past the rescale branch)
 #pragma unroll
-        for (int u = 0; u < C::PT; ++u) asm volatile("" : "+v"(pb_next[u]));
+        for (int u = 0; u < C::NU; ++u) asm volatile("" : "+v"(pb_next[u]));
         asm volatile("" : "+v"(l_run), "+v"(alpha));
 #pragma unroll
-        for (int u = 0; u < C::PT; ++u) pv_mma(pb[u], second_half, vlo[u], vhi[u]);
+        for (int u = 0; u < C::NU; ++u) pv_mma(pb[u], second_half, vlo[u], vhi[u]);
         if constexpr (!C::Q8) {
             // products and vector instructions alternate
             static_for<0, 2 * MH>([&](auto) {
@@ -714,7 +729,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
             });
         }
 #pragma unroll
-        for (int u = 0; u < C::PT; ++u) pb[u] = pb_next[u];
+        for (int u = 0; u < C::NU; ++u) pb[u] = pb_next[u];
         if (moved) {
 #pragma unroll
             for (int m = 0; m < C::MT; ++m) oacc[m] = oacc[m] * alpha;
@@ -724,6 +739,39 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // No buffer->LDS load of this workgroup may still be landing when its LDS
     // is released (the ring's tail loads read nothing, so this is quick).
     __builtin_amdgcn_s_waitcnt(0);
+
+    // Tiles split between waves: the second wave of each 16-row tile hands
+    // its state (m, the lane's part of l, O) to the first through LDS, which
+    // merges the two online softmaxes.
+    if constexpr (C::SUBS > 1) {
+        static_assert(C::SUBS == 2, "pairs of waves");
+        constexpr int XF = 4 * C::MT + 2;  // floats per lane
+        static_assert(NG * 64 * XF * 4 <= C::LDS_BYTES, "exchange area");
+        float* xo = reinterpret_cast<float*>(smem) + hw * 64 * XF + lane;
+        __syncthreads();  // every wave is done with the ring
+        if (w >= NG && w < C::NC) {
+#pragma unroll
+            for (int m = 0; m < C::MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xo[64 * (4 * m + r)] = oacc[m][r];
+            xo[64 * (4 * C::MT)] = m_run;
+            xo[64 * (4 * C::MT + 1)] = l_run;
+        }
+        __syncthreads();
+        if (w < NG) {
+            const float m1 = xo[64 * (4 * C::MT)], l1 = xo[64 * (4 * C::MT + 1)];
+            const float mm = fmaxf(m_run, m1);
+            // a side that saw no position has m = -inf, l = 0 and O = 0
+            const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+            for (int m = 0; m < C::MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oacc[m][r] = oacc[m][r] * a0 + xo[64 * (4 * m + r)] * a1;
+            l_run = l_run * a0 + l1 * a1;
+            m_run = mm;
+        }
+    }
 
     // ---- epilogue: this wave's 16 heads, no merge with other waves.  The
     // accumulators hold four consecutive d of one head per lane; they go

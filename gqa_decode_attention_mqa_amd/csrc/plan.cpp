@@ -235,8 +235,15 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     if (p.max_splits < 1) p.max_splits = 1;
 
     p.grid_main = p.rows * Hkv * p.max_splits;
-    // matrix cores: one compute wave per 16 heads plus two load-only waves
-    p.block_main = p.variant == MQA_VARIANT_MFMA ? 64 * (p.heads_per_block / kMfmaHeadsPerTile + 2) : 256;
+    // matrix cores: one compute wave per 16 heads (two on 8-bit caches at
+    // D = 256 with up to 48 heads per block) plus two load-only waves
+    if (p.variant == MQA_VARIANT_MFMA) {
+        const int tiles = p.heads_per_block / kMfmaHeadsPerTile;
+        const int per_tile = (o.kv_format != MQA_KV_BF16 && D >= 256 && tiles <= 3) ? 2 : 1;
+        p.block_main = 64 * (tiles * per_tile + 2);
+    } else {
+        p.block_main = 256;
+    }
     if (p.grid_main > kMaxGrid || p.head_blocks > 65535)
         return fail(MQA_ERR_UNSUPPORTED, "problem too large for one launch (grid limit)");
 

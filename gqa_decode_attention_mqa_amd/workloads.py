@@ -147,13 +147,16 @@ def make_inputs(w: Workload, device="cpu", seed: int | None = None,
 
 
 def make_multi_inputs(w: Workload, tokens: int, device="cpu", seed: int | None = None,
-                      poison_padding: bool = False) -> dict:
+                      poison_padding: bool = False, seq_lens=None) -> dict:
     """Like :func:`make_inputs` but with ``tokens`` new query tokens per sequence:
-    q [B, tokens, Hq, D] (their keys and values sit at the last ``tokens`` cached positions)."""
+    q [B, tokens, Hq, D] (their keys and values sit at the last ``tokens`` cached positions).
+    ``seq_lens`` overrides the drawn lengths as in :func:`make_inputs`."""
     device = torch.device(device)
     gen = torch.Generator(device=device)
     gen.manual_seed(int(w.seed if seed is None else seed))
     lens = draw_lengths(w, gen, device)
+    if seq_lens is not None:
+        lens = torch.as_tensor(seq_lens, dtype=torch.int32).to(device).reshape(w.B).contiguous()
     q = _randn_bf16((w.B, tokens, w.Hq, w.D), gen, device)
     if w.q_mult != 1.0:
         q = q * w.q_mult

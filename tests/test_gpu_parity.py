@@ -654,6 +654,79 @@ def test_quant_paged_window(kv_format, variant, page_size, window):
                     % (kv_format, variant, page_size, window, chunk, combine))
 
 
+D256_LENS = [0, 1, 31, 32, 33, 63, 64, 65, 95, 129, 700]
+
+
+@pytest.mark.parametrize("kv_format", ["fp8", "int8"])
+@pytest.mark.parametrize("Hq", [16, 48, 64])
+def test_quant_d256_steps_of_two_tiles(kv_format, Hq):
+    """8-bit caches at D = 256: a compute step takes two 32-position tiles, and for up to 48 heads per
+    block the two tiles go to two waves per 16-head tile whose softmax states merge after the loop
+    (64 heads: one wave takes both).  Lengths sit on and around tile and step boundaries (a chunk of
+    at most 32 positions, as in lengths 1, 32 and 129 with 128-position chunks, leaves the second
+    wave nothing); the chunk is the default, or 128 positions with both merge forms; then a paged pool
+    of 32-position pages (the two tiles of a step on different pages) with a window that is not a
+    multiple of 32, and three query tokens per sequence."""
+    w = Workload("q8d256", B=len(D256_LENS), Hq=Hq, Hkv=1, D=256, Lmax=704, seed=1200 + Hq)
+    inp = make_inputs(w, seq_lens=D256_LENS, poison_padding=True)
+    qc = quantize_cache(inp, kv_format)
+    ref = oracle.decode_quant(inp["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
+                              inp["seq_lens"], kv_format, inp["scale"])
+    dev, dq = to_dev(inp), to_dev(qc)
+    for chunk, combine in ((None, None), (128, "separate"), (128, "fused")):
+        print("case quant d256", kv_format, Hq, chunk, combine, flush=True)
+        out = binding.decode_quant(dev["q"], dq["k_codes"], dq["v_codes"], dq["k_scale"], dq["v_scale"],
+                                   dev["seq_lens"], kv_format, dev["scale"], variant="mfma", chunk=chunk,
+                                   combine=combine)
+        torch.cuda.synchronize()
+        check_close(out, ref, "quant d256 %s Hq %d chunk %s %s" % (kv_format, Hq, chunk, combine))
+
+    # paged pool of 32-position pages with a sliding window of 100 positions
+    window = 100
+    lens = inp["seq_lens"]
+    lo = torch.clamp(lens.to(torch.int64) - window, min=0)
+    bad_code = 0x7F if kv_format == "fp8" else 0
+    shifted = {key: torch.full_like(qc[key], bad_code) for key in ("k_codes", "v_codes")}
+    shifted.update({key: torch.full_like(qc[key], float("nan")) for key in ("k_scale", "v_scale")})
+    wq = {key: qc[key].clone() for key in qc}
+    for b in range(w.B):
+        n, a0 = int(lens[b]), int(lo[b])
+        for key in ("k_codes", "v_codes"):
+            shifted[key][b, :n - a0] = qc[key][b, a0:n]
+            wq[key][b, :a0] = bad_code
+        for key in ("k_scale", "v_scale"):
+            shifted[key][b, :, :n - a0] = qc[key][b, :, a0:n]
+            wq[key][b, :, :a0] = float("nan")       # positions before the window: NaN scales
+    ref_w = oracle.decode_quant(inp["q"], shifted["k_codes"], shifted["v_codes"], shifted["k_scale"],
+                                shifted["v_scale"], (lens - lo).to(torch.int32), kv_format, inp["scale"])
+    pg = to_dev(page_quant_cache(inp, wq, 32, seed=1200 + Hq, spare_pages=2))
+    for chunk in (None, 128):
+        print("case quant d256 paged window", kv_format, Hq, chunk, flush=True)
+        out = binding.decode_paged(dev["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], dev["seq_lens"],
+                                   dev["scale"], variant="mfma", chunk=chunk, window=window, kv_format=kv_format,
+                                   k_scale=pg["k_scale_pages"], v_scale=pg["v_scale_pages"])
+        torch.cuda.synchronize()
+        check_close(out, ref_w, "quant d256 paged window %s Hq %d chunk %s" % (kv_format, Hq, chunk))
+
+    # three query tokens per sequence, each an 8-bit decode with its own length
+    T = 3
+    wm = Workload("q8d256m", B=len(D256_LENS), Hq=Hq, Hkv=1, D=256, Lmax=704, seed=1250 + Hq)
+    mi = make_multi_inputs(wm, T, seq_lens=D256_LENS, poison_padding=True)
+    mq = quantize_cache(mi, kv_format)
+    ml = mi["seq_lens"]
+    ref_m = np.stack([oracle.decode_quant(mi["q"][:, i], mq["k_codes"], mq["v_codes"], mq["k_scale"], mq["v_scale"],
+                                          torch.clamp(ml - T + 1 + i, min=0), kv_format, mi["scale"])
+                      for i in range(T)], 1)
+    md, mqd = to_dev(mi), to_dev(mq)
+    for chunk in (None, 128):
+        print("case quant d256 multi", kv_format, Hq, chunk, flush=True)
+        out = binding.decode_multi(md["q"], mqd["k_codes"], mqd["v_codes"], md["seq_lens"], md["scale"],
+                                   variant="mfma", chunk=chunk, kv_format=kv_format, k_scale=mqd["k_scale"],
+                                   v_scale=mqd["v_scale"])
+        torch.cuda.synchronize()
+        check_close(out, ref_m, "quant d256 multi %s Hq %d chunk %s" % (kv_format, Hq, chunk))
+
+
 @pytest.mark.parametrize("name,kv_format", [("palm", "fp8"), ("gqa70b", "fp8"), ("ragged", "fp8"), ("long", "fp8"),
                                             ("ragged", "int8"), ("palm", "int8"), ("long", "int8"), ("gqa70b", "int8")])
 def test_quant_full_size(name, kv_format):

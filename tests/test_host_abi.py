@@ -132,6 +132,19 @@ def test_forced_variant_and_chunk_are_honoured():
     assert p["variant"] == "valu" and p["head_blocks"] == 6
 
 
+def test_block_size_counts_the_compute_and_load_waves():
+    """One compute wave per 16 heads plus two loaders; 8-bit caches at D = 256
+    with up to 48 heads per block give each 16-head tile two compute waves."""
+    assert binding.plan(64, 48, 1, 256, 2048)["block_main"] == 64 * (3 + 2)
+    for fmt in ("fp8", "int8"):
+        assert binding.plan(64, 48, 1, 256, 2048, kv_format=fmt)["block_main"] == 64 * (6 + 2)
+        assert binding.plan(4, 16, 1, 256, 4096, kv_format=fmt)["block_main"] == 64 * (2 + 2)
+        assert binding.plan(32, 64, 8, 128, 4096, kv_format=fmt)["block_main"] == 64 * (1 + 2)
+    p = binding.plan(2, 96, 1, 256, 4096, kv_format="fp8")  # 96 heads per block: one wave per tile
+    assert p["head_blocks"] == 1 and p["block_main"] == 64 * (6 + 2)
+    assert binding.plan(32, 64, 8, 128, 4096)["block_main"] == 64 * (1 + 2)
+
+
 def test_default_plans_of_the_five_workloads():
     """The defaults are the measured best choices on MI355X."""
     assert binding.plan(64, 48, 1, 256, 2048)["chunk"] == 512
@@ -266,9 +279,11 @@ def test_quant_plan():
     p = binding.plan(4, 16, 2, 128, 512, variant="valu", kv_format="fp8")
     assert p["head_blocks"] == 2 and p["block_main"] == 256
     assert binding.plan(4, 16, 2, 128, 512, variant="valu")["head_blocks"] == 1
-    # the matrix-core plan does not depend on the format
+    # the matrix-core plan depends on the format only through the workgroup
+    # size (two compute waves per 16-head tile on 8-bit caches at D = 256)
     a = binding.plan(64, 48, 1, 256, 2048, kv_format="fp8")
     b = binding.plan(64, 48, 1, 256, 2048)
+    assert a.pop("block_main") == 512 and b.pop("block_main") == 320
     assert a == b
 
 
