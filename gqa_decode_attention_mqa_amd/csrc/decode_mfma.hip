@@ -40,11 +40,11 @@ namespace mqa {
 
 template <int D, int NG, int FMT>
 struct MfmaCfg {
-    // NG compute waves (one per 16-head tile) and NL load-only waves.  The
-    // loads of a tile all leave right after the ring barrier and queue in the
-    // CU's address unit; a wave stalls until its own are accepted, so they are
-    // kept off the compute waves.  Two loaders keep three tiles in flight
-    // within the 63 loads a wave can have outstanding.
+    // NC compute waves (SUBS per 16-head tile, below) and NL load-only waves.
+    // The loads of a tile all leave right after the ring barrier and queue in
+    // the CU's address unit; a wave stalls until its own are accepted, so they
+    // are kept off the compute waves.  Two loaders keep the ring's steps in
+    // flight within the 63 loads a wave can have outstanding.
     static constexpr int NL = 2;
     static constexpr int STEP = 32;                  // positions per tile
     static constexpr bool Q8 = FMT != kKvBf16;       // 8-bit codes with a scale per row

@@ -272,6 +272,17 @@ def test_bitwise_deterministic(variant):
         assert torch.equal(o, outs[0])
 
 
+@pytest.mark.parametrize("kv_format", ["fp8", "int8"])
+def test_bitwise_deterministic_8bit(kv_format):
+    """The 8-bit kernel at D = 256 (two waves per 16-head tile, merged in a fixed order), repeated."""
+    w = Workload("det8", B=4, Hq=48, Hkv=1, D=256, Lmax=1500, seed=81, len_lo=1, len_hi=1500)
+    dev, qc, _ = quant_case(w, kv_format)
+    outs = [binding.decode_quant(dev["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
+                                 dev["seq_lens"], kv_format, dev["scale"], chunk=256).clone() for _ in range(5)]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
 def test_identical_keys_give_mean_of_values():
     w = Workload("same-k", B=2, Hq=48, Hkv=1, D=256, Lmax=1000, seed=80, len_lo=500, len_hi=1000)
     inp = to_dev(make_inputs(w))
@@ -652,6 +663,22 @@ def test_quant_paged_window(kv_format, variant, page_size, window):
         torch.cuda.synchronize()
         check_close(out, ref, "quant paged window %s %s page %d W %d chunk %s %s"
                     % (kv_format, variant, page_size, window, chunk, combine))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,Lmax,seed", _random_shapes(10, 2))
+def test_quant_random_shapes(B, Hq, Hkv, D, Lmax, seed):
+    """Seeded random shapes (groups 1..48, D 64..256, lengths 0..Lmax) on both 8-bit formats, with
+    the planner's chunk, 128-position chunks and the fused merge (at most 8 chunks per sequence)."""
+    kv_format = ("fp8", "int8")[seed % 2]
+    w = Workload("q8rand", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, seed=seed, len_lo=0, len_hi=Lmax)
+    dev, qc, ref = quant_case(w, kv_format)
+    fused_chunk = 128 * -(-Lmax // (8 * 128))
+    for chunk, combine in ((None, None), (128, "separate"), (fused_chunk, "fused")):
+        print("case quant random", kv_format, B, Hq, Hkv, D, Lmax, seed, chunk, combine, flush=True)
+        out = binding.decode_quant(dev["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
+                                   dev["seq_lens"], kv_format, dev["scale"], chunk=chunk, combine=combine)
+        torch.cuda.synchronize()
+        check_close(out, ref, "quant random %s %s chunk %s %s" % (kv_format, (B, Hq, Hkv, D, Lmax), chunk, combine))
 
 
 D256_LENS = [0, 1, 31, 32, 33, 63, 64, 65, 95, 129, 700]
