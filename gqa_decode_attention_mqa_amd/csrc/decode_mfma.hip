@@ -110,7 +110,7 @@ struct MfmaCfg {
     static constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
     static_assert(D >= 64 && D % 64 == 0, "head size");
     static_assert(LOADS % NL == 0, "every loader issues the same number of loads");
-    static_assert((GSTAGES - 2) * PT * PER_WAVE <= 63, "loads in flight fit a wave's counter");
+    static_assert((GSTAGES - 1) * PT * PER_WAVE <= 63, "loads in flight fit a wave's counter");
     static_assert(NG >= 1 && NG <= 6, "one to six 16-row tiles of query rows");
     static_assert(NW <= 8, "the launch bound");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of a gfx950 CU");
@@ -354,8 +354,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // tiles and frees the slots refilled next.  A plain s_barrier, not
     // __syncthreads: the latter's release fence would also wait for the loads
     // still in flight to the ring.
-    auto ring_sync = [&]() {
-        __builtin_amdgcn_s_waitcnt(kVmcntStages<C::GSTAGES - 3, C::PT * C::PER_WAVE>() & ~(0xF << 8));
+    // The first sync allows one more step outstanding: the prologue issued
+    // every free slot's step.
+    auto ring_sync = [&](auto later_steps) {
+        constexpr int N = decltype(later_steps)::value;
+        __builtin_amdgcn_s_waitcnt(kVmcntStages<N, C::PT * C::PER_WAVE>() & ~(0xF << 8));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -640,9 +643,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         }
     };
 
-    // Prologue: steps 0 .. GSTAGES-3 in flight (tiles past the end read nothing).
+    // Prologue: steps 0 .. GSTAGES-2 in flight, every slot the loop does not
+    // refill first (tiles past the end read nothing).  They are issued before
+    // the first barrier, which waits for the compute waves' q as well.
 #pragma unroll
-    for (int st = 0; st < C::GSTAGES - 2; ++st) issue_step(st);
+    for (int st = 0; st < C::GSTAGES - 1; ++st) issue_step(st);
 
     // Software pipeline: step `step` computes q.K of step + 1 with its
     // softmax and P.V of `step` (P^T made in the previous step), so the matrix
@@ -663,8 +668,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < C::NU; ++u) pb[u] = u32x4_t{0u, 0u, 0u, 0u};
     if (nsteps > 0) {
-        ring_sync();  // step 0 landed
-        issue_step(C::GSTAGES - 2);
+        ring_sync(std::integral_constant<int, C::GSTAGES - 2>{});  // step 0 landed
         if (w < C::NC) {
             f32x4_t sacc[C::NU][2], vsc[C::NU][2];
 #pragma unroll
@@ -677,7 +681,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     }
     for (int step = 0; step < nsteps; ++step) {
         const int t0 = C::PT * step + u0, t1 = t0 + C::PT;  // this wave's first tile of this step and of the next
-        ring_sync();  // step + 1 landed (no-op reads past the end)
+        ring_sync(std::integral_constant<int, C::GSTAGES - 3>{});  // step + 1 landed (no-op reads past the end)
         issue_step(step + C::GSTAGES - 1);
         if (w >= C::NC) continue;  // the load-only wave
         u32x2_t vlo[C::NU][MH], vhi[C::NU][MH];
@@ -745,29 +749,25 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
     // merges the two online softmaxes.
     if constexpr (C::SUBS > 1) {
         static_assert(C::SUBS == 2, "pairs of waves");
-        constexpr int XF = 4 * C::MT + 2;  // floats per lane
-        static_assert(NG * 64 * XF * 4 <= C::LDS_BYTES, "exchange area");
-        float* xo = reinterpret_cast<float*>(smem) + hw * 64 * XF + lane;
+        constexpr int XV = C::MT + 1;  // 16-byte values per lane: O, then {m, l}
+        static_assert(NG * 64 * XV * 16 <= C::LDS_BYTES, "exchange area");
+        f32x4_t* xo = reinterpret_cast<f32x4_t*>(smem) + hw * 64 * XV + lane;
         __syncthreads();  // every wave is done with the ring
         if (w >= NG && w < C::NC) {
 #pragma unroll
-            for (int m = 0; m < C::MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) xo[64 * (4 * m + r)] = oacc[m][r];
-            xo[64 * (4 * C::MT)] = m_run;
-            xo[64 * (4 * C::MT + 1)] = l_run;
+            for (int m = 0; m < C::MT; ++m) xo[64 * m] = oacc[m];
+            xo[64 * C::MT] = f32x4_t{m_run, l_run, 0.f, 0.f};
         }
         __syncthreads();
         if (w < NG) {
-            const float m1 = xo[64 * (4 * C::MT)], l1 = xo[64 * (4 * C::MT + 1)];
+            const f32x4_t ml = xo[64 * C::MT];
+            const float m1 = ml[0], l1 = ml[1];
             const float mm = fmaxf(m_run, m1);
             // a side that saw no position has m = -inf, l = 0 and O = 0
             const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
             const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
 #pragma unroll
-            for (int m = 0; m < C::MT; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) oacc[m][r] = oacc[m][r] * a0 + xo[64 * (4 * m + r)] * a1;
+            for (int m = 0; m < C::MT; ++m) oacc[m] = oacc[m] * a0 + xo[64 * m] * a1;
             l_run = l_run * a0 + l1 * a1;
             m_run = mm;
         }
