@@ -92,6 +92,9 @@ def parse_args(argv=None):
     ap.add_argument("--variant", default=None, choices=[None, "auto", "valu", "mfma"])
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--combine", default=None, choices=[None, "auto", "separate", "fused"])
+    ap.add_argument("--schedule", default=None, choices=[None, "auto", "per_item", "persistent"],
+                    help="work items of the split kernel: one workgroup each, or a resident grid taking them "
+                         "from a queue; default: the planner's choice")
     ap.add_argument("--page-size", type=int, default=0,
                     help="run the paged-cache entry point on a pool of pages of this many positions "
                          "(a power of two >= 32; the pool holds the used pages only); 0 = contiguous cache")
@@ -390,7 +393,8 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     plan = binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, w.scale, args.variant, args.chunk, args.combine,
-                        window=args.window, kv_format=args.kv_format, tokens=args.tokens, host_seq_lens=host_lens)
+                        window=args.window, kv_format=args.kv_format, tokens=args.tokens, host_seq_lens=host_lens,
+                        schedule=args.schedule)
 
     # 8-bit caches: each set's bf16 draw is quantized per row (the codes and
     # scales replace it); the scale pointers travel in each set's options
@@ -440,7 +444,7 @@ def main(argv=None):
     def make(i, ev_b=None, ev_e=None):  # options of a step on set i % nsets
         ks, vs = set_scales[i % nsets]
         return binding.make_opts(args.variant, args.chunk, args.combine, ev_b, ev_e, args.window,
-                                 args.kv_format, ks, vs, host_seq_lens=host_lens)
+                                 args.kv_format, ks, vs, host_seq_lens=host_lens, schedule=args.schedule)
 
     plain_sets = [make(i) for i in range(nsets)]
     for i in range(args.warmup):

@@ -26,6 +26,7 @@ MQA_OK = 0
 VARIANTS = {"auto": 0, "valu": 1, "mfma": 2}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 COMBINE = {"auto": 0, "separate": 1, "fused": 2}
+SCHEDULES = {None: 0, "auto": 0, "per_item": 1, "persistent": 2}
 KV_FORMATS = {"bf16": 0, "fp8": 1, "int8": 2}
 
 
@@ -41,14 +42,15 @@ class DecodeOpts(ctypes.Structure):
                 ("window", ctypes.c_int), ("kv_format", ctypes.c_int),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
                 ("ev_combine_begin", ctypes.c_void_p), ("ev_combine_end", ctypes.c_void_p),
-                ("host_seq_lens", ctypes.c_void_p)]
+                ("host_seq_lens", ctypes.c_void_p), ("schedule", ctypes.c_int)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int), ("chunk", ctypes.c_int), ("max_splits", ctypes.c_int),
                 ("combine", ctypes.c_int), ("head_blocks", ctypes.c_int),
                 ("grid_main", ctypes.c_longlong), ("block_main", ctypes.c_int),
-                ("grid_combine", ctypes.c_longlong), ("workspace_bytes", ctypes.c_size_t)]
+                ("grid_combine", ctypes.c_longlong), ("workspace_bytes", ctypes.c_size_t),
+                ("persistent", ctypes.c_int)]
 
 
 _lib = None
@@ -142,10 +144,12 @@ def _checked_lens(host_seq_lens, B):
 
 def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None, window=None,
               kv_format=None, k_scale=None, v_scale=None, ev_combine_begin=None, ev_combine_end=None,
-              host_seq_lens=None) -> DecodeOpts:
+              host_seq_lens=None, schedule=None) -> DecodeOpts:
     """Options of a decode call.  ``host_seq_lens``: an optional host copy of the lengths, used by
-    the planner only to pick the chunk size (see mqa_decode_opts.host_seq_lens)."""
+    the planner only to pick the chunk size (see mqa_decode_opts.host_seq_lens).  ``schedule``:
+    None / "auto", "per_item" or "persistent" (see mqa_decode_opts.schedule)."""
     o = DecodeOpts()
+    o.schedule = SCHEDULES[schedule] if isinstance(schedule, str) or schedule is None else int(schedule)
     o._host_lens = _host_lens(host_seq_lens)
     o.host_seq_lens = o._host_lens.data_ptr() if o._host_lens is not None else None
     o.ev_combine_begin = ev_combine_begin
@@ -163,19 +167,21 @@ def make_opts(variant=None, chunk=None, combine=None, ev_begin=None, ev_end=None
 
 
 def plan(B, Hq, Hkv, D, Lmax, scale=None, variant=None, chunk=None, combine=None, window=None,
-         kv_format=None, tokens=1, host_seq_lens=None) -> dict:
+         kv_format=None, tokens=1, host_seq_lens=None, schedule=None) -> dict:
     """The library's launch plan for a decode call of this shape (host only);
     ``tokens`` > 1 plans a multi-token call."""
     lib = load_library()
     info = PlanInfo()
-    opts = make_opts(variant, chunk, combine, window=window, kv_format=kv_format, host_seq_lens=host_seq_lens)
+    opts = make_opts(variant, chunk, combine, window=window, kv_format=kv_format, host_seq_lens=host_seq_lens,
+                     schedule=schedule)
     sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.mqa_decode_plan_multi(B, int(tokens), Hq, Hkv, D, Lmax, sc, ctypes.byref(opts), ctypes.byref(info)),
            "mqa_decode_plan")
     return {"variant": VARIANT_NAMES.get(info.variant, info.variant), "chunk": info.chunk,
             "max_splits": info.max_splits, "combine": info.combine, "head_blocks": info.head_blocks,
             "grid_main": info.grid_main, "block_main": info.block_main,
-            "grid_combine": info.grid_combine, "workspace_bytes": info.workspace_bytes}
+            "grid_combine": info.grid_combine, "workspace_bytes": info.workspace_bytes,
+            "persistent": bool(info.persistent)}
 
 
 def prefill_plan(B, Hq, Hkv, D, Lmax, scale=None) -> dict:
@@ -214,7 +220,7 @@ def _require(t: torch.Tensor, name: str, dtype, ndim: int, device):
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
            scale: float | None = None, out: torch.Tensor | None = None, variant=None, chunk=None,
-           combine=None, events=None, window=None, host_seq_lens=None) -> torch.Tensor:
+           combine=None, events=None, window=None, host_seq_lens=None, schedule=None) -> torch.Tensor:
     """One decode step.  q [B,Hq,D] bf16, caches [B,Lmax,Hkv,D] bf16, seq_lens [B] int32 -> fp32 [B,Hq,D].
 
     Runs on torch's current stream of q's device.  ``events`` = (begin, end)
@@ -243,7 +249,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
     opts = make_opts(variant, chunk, combine, ev_b, ev_e, window,
-                     host_seq_lens=_checked_lens(host_seq_lens, B))
+                     host_seq_lens=_checked_lens(host_seq_lens, B), schedule=schedule)
     lib = load_library()
     st = lib.mqa_decode_attention_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                      seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D, Lmax,
@@ -255,7 +261,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_le
 def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
                  seq_lens: torch.Tensor, scale: float | None = None, out: torch.Tensor | None = None,
                  variant=None, chunk=None, combine=None, events=None, window=None, kv_format=None,
-                 k_scale=None, v_scale=None, host_seq_lens=None) -> torch.Tensor:
+                 k_scale=None, v_scale=None, host_seq_lens=None, schedule=None) -> torch.Tensor:
     """One decode step over a paged cache.  q [B,Hq,D] bf16, pages [num_pages,page_size,Hkv,D] bf16,
     block_table [B,max_blocks] int32, seq_lens [B] int32 -> fp32 [B,Hq,D].  With ``kv_format``
     "fp8" or "int8" the pages hold 8-bit codes (uint8) and ``k_scale`` / ``v_scale`` are fp32
@@ -290,7 +296,7 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
     opts = make_opts(variant, chunk, combine, ev_b, ev_e, window, fmt, sk, sv,
-                     host_seq_lens=_checked_lens(host_seq_lens, B))
+                     host_seq_lens=_checked_lens(host_seq_lens, B), schedule=schedule)
     lib = load_library()
     st = lib.mqa_decode_attention_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                                         block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
@@ -303,7 +309,7 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
 def decode_quant(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor, k_scale: torch.Tensor,
                  v_scale: torch.Tensor, seq_lens: torch.Tensor, kv_format: str, scale: float | None = None,
                  out: torch.Tensor | None = None, variant=None, chunk=None, combine=None, events=None,
-                 window=None, host_seq_lens=None) -> torch.Tensor:
+                 window=None, host_seq_lens=None, schedule=None) -> torch.Tensor:
     """One decode step against an 8-bit cache through ``mqa_decode_attention_quant``.
     q [B,Hq,D] bf16; codes [B,Lmax,Hkv,D] uint8 (E4M3 for "fp8", two's complement for
     "int8"); scales [B,Hkv,Lmax] fp32; seq_lens [B] int32 -> fp32 [B,Hq,D]."""
@@ -332,7 +338,7 @@ def decode_quant(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor, 
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
     opts = make_opts(variant, chunk, combine, ev_b, ev_e, window,
-                     host_seq_lens=_checked_lens(host_seq_lens, B))
+                     host_seq_lens=_checked_lens(host_seq_lens, B), schedule=schedule)
     lib = load_library()
     st = lib.mqa_decode_attention_quant(q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(), k_scale.data_ptr(),
                                         v_scale.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, D,
@@ -343,7 +349,7 @@ def decode_quant(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor, 
 
 def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
                  scale: float | None = None, out: torch.Tensor | None = None, variant=None, chunk=None,
-                 combine=None, events=None, kv_format=None, k_scale=None, v_scale=None, host_seq_lens=None) -> torch.Tensor:
+                 combine=None, events=None, kv_format=None, k_scale=None, v_scale=None, host_seq_lens=None, schedule=None) -> torch.Tensor:
     """T new tokens per sequence through ``mqa_decode_attention_multi``: q [B,T,Hq,D] bf16
     -> fp32 [B,T,Hq,D]; token i attends positions 0 .. seq_lens[b] - T + i.  Caches as for
     :func:`decode` (bf16), or 8-bit codes with ``kv_format`` and scales as for :func:`decode_quant`."""
@@ -377,7 +383,7 @@ def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     if events is not None:
         ev_b, ev_e = events[0].cuda_event, events[1].cuda_event
     opts = make_opts(variant, chunk, combine, ev_b, ev_e, None, fmt, sk, sv,
-                     host_seq_lens=_checked_lens(host_seq_lens, B))
+                     host_seq_lens=_checked_lens(host_seq_lens, B), schedule=schedule)
     lib = load_library()
     st = lib.mqa_decode_attention_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
                                         out.data_ptr(), B, T, Hq, Hkv, D, Lmax, sc, _stream_ptr(dev),

@@ -186,6 +186,16 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     if (noalloc) {
         st = check_noalloc(plan);
         if (st != MQA_OK) return st;
+        // the persistent schedule's queue needs memory that starts at zero
+        if (opts && opts->schedule == 2) {
+            mqa::set_error("the no-allocation entry point runs one workgroup per work item (schedule 2 is not "
+                           "available)");
+            return MQA_ERR_ARG;
+        }
+        if (plan.persist) {
+            plan.persist = 0;
+            plan.counters -= mqa::kPersistCounters;
+        }
     }
     if (B == 0) return MQA_OK;
 
@@ -215,6 +225,11 @@ mqa_status run(const void* q, const void* k, const void* v, const int32_t* seq_l
     a.part_o = ws ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + plan.part_o_offset) : nullptr;
     a.part_ml = ws ? reinterpret_cast<mqa::f32x2_t*>(static_cast<char*>(ws) + plan.part_ml_offset) : nullptr;
     a.counters = counters;
+    if (plan.persist) {
+        a.queue = counters + (plan.counters - mqa::kPersistCounters);
+        a.items = plan.grid_main * plan.head_blocks;
+        a.grid_x = plan.grid_main;
+    }
     if (paged) {
         a.block_table = paged->block_table;
         a.page_shift = paged->page_shift;
@@ -393,6 +408,7 @@ mqa_status mqa_prefill_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale
         info->block_main = p.block_main;
         info->grid_combine = p.grid_combine;
         info->workspace_bytes = p.workspace_bytes;
+        info->persistent = p.persist;
     }
     if (rows_per_block) *rows_per_block = p.heads_per_block;
     return MQA_OK;
@@ -419,6 +435,7 @@ mqa_status mqa_decode_plan_multi(int B, int T, int Hq, int Hkv, int D, int Lmax,
         info->block_main = p.block_main;
         info->grid_combine = p.grid_combine;
         info->workspace_bytes = p.workspace_bytes;
+        info->persistent = p.persist;
     }
     return MQA_OK;
 }

@@ -121,8 +121,9 @@ struct MfmaCfg {
 // cannot change how the compiler allocates and schedules the tile loop of the
 // plain form (with the tail behind a run-time flag in one kernel, MI355X
 // measured 11 % slower 8-bit loops: int8 B=4 len 131072 86.6 against 78.0 us).
+// One work item: the (unit, chunk) of x-index bx and the head block by.
 template <int D, int NG, int FMT, bool FUSED>
-__global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, long long bx, int by) {
     using C = MfmaCfg<D, NG, FMT>;
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
 
@@ -135,10 +136,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 
     long long unit;
     int s;
-    map_block(blockIdx.x, a.units, a.max_splits, &unit, &s);
+    map_block(bx, a.units, a.max_splits, &unit, &s);
     const int kvh = (int)(unit % a.Hkv);
     const long long row = unit / a.Hkv;
-    const int g0 = blockIdx.y * 16 * NG;
+    const int g0 = by * 16 * NG;
     const int gcnt = min(16 * NG, a.GT - g0);  // query rows (token, head) of this block
 
     int b, len, qbase;
@@ -847,7 +848,50 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
         // ---- fused combine: the chunks of this (row, kv head, head block) share the merge
         __syncthreads();
         fused_tail(a, unit, row, kvh, nsplit, g0, gcnt,
-                   a.counters + (unit * gridDim.y + blockIdx.y) * kFusedCountersPerUnit, reinterpret_cast<int*>(smem));
+                   a.counters + (unit * gridDim.y + by) * kFusedCountersPerUnit, reinterpret_cast<int*>(smem));
+    }
+}
+
+template <int D, int NG, int FMT, bool FUSED>
+__global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
+    decode_item<D, NG, FMT, FUSED>(a, blockIdx.x, blockIdx.y);
+}
+
+// Persistent form: gridDim.x workgroups (as many as are resident at once)
+// keep taking work items until none is left, so a workgroup that finishes a
+// short chunk starts the next item at once instead of waiting for the
+// hardware to dispatch a new workgroup in grid order, and a faster XCD takes
+// more items than a slower one.  Workgroup x first takes item x, then items
+// gridDim.x + k for k from the queue counter.  (Device-scope atomics on one
+// address are serialized; the static first item keeps them off the start of
+// the kernel's critical path.)  Thread 0 fetches the following item while the
+// current one runs; the item number reaches the other waves through the 16
+// bytes after the kernel's LDS block.  The last workgroup to leave puts both
+// counters back to zero for the next call.  Items do not depend on which
+// workgroup runs them, so the result is the plain form's, bit for bit.
+template <int D, int NG, int FMT>
+__global__ __launch_bounds__(512) void decode_mfma_persistent_kernel(DecodeArgs a) {
+    using C = MfmaCfg<D, NG, FMT>;
+    extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
+    volatile long long* slot = reinterpret_cast<volatile long long*>(smem + C::LDS_BYTES);
+    const int tid = threadIdx.x;
+    long long item = blockIdx.x;
+    long long next = 0;
+    if (tid == 0 && item < a.items) next = (long long)gridDim.x + atomicAdd(&a.queue[0], 1u);
+    while (item < a.items) {
+        decode_item<D, NG, FMT, false>(a, item % a.grid_x, (int)(item / a.grid_x));
+        __syncthreads();  // every wave is done with this item's LDS
+        if (tid == 0) slot[0] = next;
+        __syncthreads();
+        item = slot[0];
+        if (tid == 0 && item < a.items) next = (long long)gridDim.x + atomicAdd(&a.queue[0], 1u);
+    }
+    if (tid == 0) {
+        // every workgroup's last fetch came before its arrival here
+        if (atomicAdd(&a.queue[1], 1u) == gridDim.x - 1) {
+            atomicExch(&a.queue[0], 0u);
+            atomicExch(&a.queue[1], 0u);
+        }
     }
 }
 
@@ -879,8 +923,46 @@ static hipError_t launch_mfma_form(const Plan& p, const DecodeArgs& a, hipStream
 }
 
 template <int D, int NG, int FMT>
+static hipError_t launch_mfma_persistent(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
+                                         hipEvent_t ev1) {
+    using C = MfmaCfg<D, NG, FMT>;
+    constexpr int lds = C::LDS_BYTES + 16;  // + the item slot
+    static_assert(lds <= 160 * 1024, "LDS budget of a gfx950 CU");
+    const void* fn = reinterpret_cast<const void*>(&decode_mfma_persistent_kernel<D, NG, FMT>);
+    // workgroups resident at once on each device (0 until known)
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> resident[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int wgs = resident[dev].load();
+    if (wgs == 0) {
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        int per_cu = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, C::THREADS, lds);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        wgs = per_cu * cus;
+        if (wgs <= 0) return hipErrorInvalidConfiguration;
+        resident[dev].store(wgs);
+    }
+    const long long items = p.grid_main * p.head_blocks;
+    const dim3 grid((unsigned)(items < wgs ? items : wgs));
+    const dim3 block(C::THREADS);
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL((decode_mfma_persistent_kernel<D, NG, FMT>), grid, block, lds, stream, ev0, ev1, 0, a);
+    else
+        hipLaunchKernelGGL((decode_mfma_persistent_kernel<D, NG, FMT>), grid, block, lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, int NG, int FMT>
 static hipError_t launch_mfma(const Plan& p, const DecodeArgs& a, hipStream_t stream, hipEvent_t ev0,
                             hipEvent_t ev1) {
+    if (p.persist > 0 && !a.fused) return launch_mfma_persistent<D, NG, FMT>(p, a, stream, ev0, ev1);
     return a.fused ? launch_mfma_form<D, NG, FMT, true>(p, a, stream, ev0, ev1)
                    : launch_mfma_form<D, NG, FMT, false>(p, a, stream, ev0, ev1);
 }

@@ -47,6 +47,11 @@ struct DecodeArgs {
     int fused;                 // 1: the chunks of a unit merge the partials themselves
     uint32_t fused_wait;       // bound of the fused combine's wait, in 100 MHz real-time ticks
     float qk_log2;             // scale * log2(e): logits are kept in base-2 units
+    // Persistent form: a fixed grid of workgroups takes work items (the plain
+    // form's workgroups, x fastest) from a queue counter in turn.
+    uint32_t* queue;           // {item counter, workgroups done}; zero between calls
+    long long items;           // work items: grid_x * head blocks
+    long long grid_x;
 };
 
 // Arguments of the causal prefill kernel (bf16 q, K and V; fp32 out).

@@ -116,6 +116,8 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         return fail(MQA_ERR_ARG, "chunk must be 0 or a positive multiple of 128");
     if (o.combine < 0 || o.combine > 2)
         return fail(MQA_ERR_ARG, "combine must be 0, 1 or 2");
+    if (o.schedule < 0 || o.schedule > 2)
+        return fail(MQA_ERR_ARG, "schedule must be 0, 1 or 2");
     if (o.window < 0)
         return fail(MQA_ERR_ARG, "window must be >= 0 (0 = no window)");
     if (o.kv_format < MQA_KV_BF16 || o.kv_format > MQA_KV_INT8)
@@ -136,8 +138,10 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     if (causal) {
         // causal prefill: the Lmax * G query rows of each (sequence, kv head)
         // in workgroups of prefill_rows(D) rows, each streaming its causal prefix
-        if (o.variant == MQA_VARIANT_VALU || o.window > 0 || o.kv_format != MQA_KV_BF16 || o.chunk || o.combine)
-            return fail(MQA_ERR_ARG, "the prefill form takes no variant, window, cache format, chunk or combine option");
+        if (o.variant == MQA_VARIANT_VALU || o.window > 0 || o.kv_format != MQA_KV_BF16 || o.chunk || o.combine ||
+            o.schedule)
+            return fail(MQA_ERR_ARG,
+                        "the prefill form takes no variant, window, cache format, chunk, combine or schedule option");
         if ((long long)Lmax * p.G > 0x7FFFFFFFLL - kPrefillMaxRows)
             return fail(MQA_ERR_UNSUPPORTED, "Lmax * Hq / Hkv too large for the prefill kernel");
         p.variant = MQA_VARIANT_MFMA;
@@ -284,6 +288,16 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
         p.part_ml_offset = round_up((long long)(parts * D * sizeof(uint16_t)), 256);
         p.workspace_bytes = p.part_ml_offset + round_up((long long)(parts * 2 * sizeof(float)), 256);
         p.counters = (p.combine == 2) ? (size_t)p.rows * Hkv * p.head_blocks * kFusedCountersPerUnit : 0;
+    }
+    // Persistent schedule: grids of many work items, whose workgroups would
+    // otherwise wait on the hardware's in-order dispatch behind longer ones.
+    const long long items = p.grid_main * p.head_blocks;
+    if (o.schedule == 2 && (p.variant != MQA_VARIANT_MFMA || p.combine == 2))
+        return fail(MQA_ERR_ARG, "the persistent schedule needs the MFMA variant and the separate merge");
+    if (items > 0 && (o.schedule == 2 || (o.schedule == 0 && p.variant == MQA_VARIANT_MFMA && p.combine != 2 &&
+                                          items >= kPersistMinItems))) {
+        p.persist = 1;
+        p.counters += kPersistCounters;  // the queue after the fused counters (none then)
     }
     *plan = p;
     return MQA_OK;

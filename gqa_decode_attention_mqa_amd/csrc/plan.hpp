@@ -49,6 +49,13 @@ constexpr int kFusedMaxSplits = kCombineFewMaxSplits;
 // uint32 counters per unit of the fused combine (arrivals and the merge parts
 // given up by timed-out waits; padded to 16 bytes).
 constexpr int kFusedCountersPerUnit = 4;
+// The split kernel's persistent form: its item counter and a count of the
+// workgroups that have left.  The planner chooses it for grids of at least
+// kPersistMinItems work items (MI355X, persistent against one workgroup per
+// item: the ragged GQA batch, 16384 items, 694 against 761 us, on fp8 394
+// against 465; the PaLM-shaped MQA step, 256 items, 28.4 against 25.5).
+constexpr int kPersistCounters = 2;
+constexpr long long kPersistMinItems = 2048;
 // How long a workgroup of the fused combine waits for the other chunks of its
 // unit before leaving its part of the merge to the last one: 20 us of the
 // 100 MHz real-time counter.  MQA_FUSED_WAIT_TICKS overrides it (tests force
@@ -103,7 +110,9 @@ struct Plan {
     size_t part_ml_offset = 0;
     size_t counters = 0;             // fused-combine counters (uint32, kFusedCountersPerUnit per
                                      // (row, kv head, head block)), kept in a buffer of their own
-                                     // that is zero between calls
+                                     // that is zero between calls; then the persistent form's queue
+    int persist = 0;                 // 1: the split kernel's persistent form (as many workgroups as are
+                                     // resident at once take the grid_main * head_blocks items)
 };
 
 // Thread-local last-error text.

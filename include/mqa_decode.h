@@ -123,6 +123,15 @@ typedef struct mqa_decode_opts {
                              to balance ragged lengths.  The chunks always cover Lmax (or
                              the window), so the result never depends on this hint, only
                              the speed.                                                   */
+    int schedule;         /* how the split-K kernel's work items (chunk of a sequence and
+                             kv head, head block) reach workgroups: 0 = planner's choice,
+                             1 = one workgroup per item (grid_main x head_blocks
+                             workgroups), 2 = persistent: as many workgroups as the GPU
+                             holds at once take items in order from a queue counter in the
+                             call's workspace (MFMA variant and separate merge only, else
+                             MQA_ERR_ARG; not with mqa_decode_attention_noalloc).  The
+                             planner picks 2 for grids of at least 2048 items.  Both give
+                             the same bits.                                                */
 } mqa_decode_opts;
 
 /* What the planner decided for a shape (host-only query, no HIP call). */
@@ -137,6 +146,9 @@ typedef struct mqa_plan_info {
     int block_main;           /* threads per workgroup of the split-K kernel           */
     long long grid_combine;   /* workgroups of the combine kernel (0 if none)          */
     size_t workspace_bytes;   /* split-K scratch the call needs                        */
+    int persistent;           /* 1 = the split-K kernel runs persistent (schedule 2):
+                                 grid_main x head_blocks work items over as many
+                                 workgroups as are resident at once                    */
 } mqa_plan_info;
 
 /*

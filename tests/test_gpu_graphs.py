@@ -5,6 +5,8 @@ workspace on the first call per (device, stream), so the call is warmed up on th
 stream first; the captured kernels then keep that workspace's address.  Each replay runs after eager
 work of this test (new inputs copied into the captured tensors, an eager decode call on another
 stream) and must give the eager call's bits; one replay per case is also checked against the oracle.
+The persistent schedule's queue counter lives in the same workspace and is back at zero after every
+replay.
 """
 import numpy as np
 import pytest
@@ -30,9 +32,9 @@ def _inputs(w, i):
     return {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in inp.items()}, inp
 
 
-@pytest.mark.parametrize("combine", [None, "fused"])
+@pytest.mark.parametrize("combine,schedule", [(None, None), ("fused", None), (None, "persistent")])
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_graph_replays_give_the_eager_bits(case, combine):
+def test_graph_replays_give_the_eager_bits(case, combine, schedule):
     w = CASES[case]
     sets = [_inputs(w, i) for i in range(3)]
     static = {k: sets[0][0][k].clone() for k in ("q", "k", "v", "seq_lens")}
@@ -41,7 +43,7 @@ def test_graph_replays_give_the_eager_bits(case, combine):
 
     def step():
         binding.decode(static["q"], static["k"], static["v"], static["seq_lens"], scale, out=out, chunk=256,
-                       combine=combine)
+                       combine=combine, schedule=schedule)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -50,7 +52,7 @@ def test_graph_replays_give_the_eager_bits(case, combine):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    print("case graph capture", case, combine, flush=True)
+    print("case graph capture", case, combine, schedule, flush=True)
     with torch.cuda.graph(graph, stream=side):
         step()
     torch.cuda.synchronize()
@@ -59,12 +61,14 @@ def test_graph_replays_give_the_eager_bits(case, combine):
         for k in static:
             static[k].copy_(dev[k])
         out.fill_(float("nan"))
-        print("case graph replay", case, combine, it, flush=True)
+        print("case graph replay", case, combine, schedule, it, flush=True)
         graph.replay()
         torch.cuda.synchronize()
-        ref = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], scale, chunk=256, combine=combine)
+        ref = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], scale, chunk=256, combine=combine,
+                             schedule=schedule)
         torch.cuda.synchronize()
-        assert torch.equal(out, ref), "replay %d of %s / %s differs from the eager call" % (it, case, combine)
+        assert torch.equal(out, ref), "replay %d of %s / %s / %s differs from the eager call" % (it, case, combine,
+                                                                                              schedule)
         if it == 4:
             exp = oracle.decode(cpu["q"], cpu["k"], cpu["v"], cpu["seq_lens"], scale)
             got = out.cpu().double().numpy()

@@ -939,3 +939,79 @@ def test_plain_entry_point(name):
     assert torch.equal(plain, ex)
     ref = oracle.decode(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(), inp["seq_lens"].cpu(), inp["scale"])
     check_close(plain, ref, "plain entry point %s" % name)
+
+
+# ------------------------------------------------------ persistent schedule
+
+PERSIST_CASES = {
+    # 40 sequences x 8 kv heads x 16 chunks of 128 = 5120 items: persistent by default
+    "gqa": Workload("persist-gqa", B=40, Hq=32, Hkv=8, D=128, Lmax=2000, seed=1300, len_lo=0, len_hi=2000),
+    # MQA at D = 256 (one workgroup per CU), forced persistent
+    "mqa": Workload("persist-mqa", B=12, Hq=48, Hkv=1, D=256, Lmax=1500, seed=1301, len_lo=1, len_hi=1500),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PERSIST_CASES))
+def test_persistent_schedule_gives_the_per_item_bits(case):
+    """Workgroups that take work items from a queue compute each item exactly as one workgroup per item
+    does: bf16, an 8-bit cache, a paged pool, a window and two query tokens, each bit for bit, and the
+    oracle's values; repeated calls find the queue back at zero."""
+    w = PERSIST_CASES[case]
+    inp = make_inputs(w, poison_padding=True)
+    dev = to_dev(inp)
+    ref = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    for rep in range(3):
+        print("case persistent bf16", case, rep, flush=True)
+        outs = {s: binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], chunk=128,
+                                  schedule=s) for s in ("per_item", "persistent", None)}
+        torch.cuda.synchronize()
+        assert torch.equal(outs["persistent"], outs["per_item"]) and torch.equal(outs[None], outs["per_item"])
+        check_close(outs["persistent"], ref, "persistent %s" % case)
+
+    qc = quantize_cache(inp, "fp8")
+    dq = to_dev(qc)
+    ref8 = oracle.decode_quant(inp["q"], qc["k_codes"], qc["v_codes"], qc["k_scale"], qc["v_scale"],
+                               inp["seq_lens"], "fp8", inp["scale"])
+    print("case persistent fp8", case, flush=True)
+    o8 = {s: binding.decode_quant(dev["q"], dq["k_codes"], dq["v_codes"], dq["k_scale"], dq["v_scale"],
+                                  dev["seq_lens"], "fp8", dev["scale"], chunk=128, schedule=s)
+          for s in ("per_item", "persistent")}
+    torch.cuda.synchronize()
+    assert torch.equal(o8["persistent"], o8["per_item"])
+    check_close(o8["persistent"], ref8, "persistent fp8 %s" % case)
+
+    pg = to_dev(page_contiguous_cache(inp, 64, seed=1302))
+    print("case persistent paged window", case, flush=True)
+    op = {s: binding.decode_paged(dev["q"], pg["k_pages"], pg["v_pages"], pg["block_table"], dev["seq_lens"],
+                                  dev["scale"], chunk=128, window=300, schedule=s) for s in ("per_item", "persistent")}
+    ow = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], chunk=128, window=300,
+                        schedule="per_item")
+    torch.cuda.synchronize()
+    assert torch.equal(op["persistent"], op["per_item"]) and torch.equal(op["persistent"], ow)
+
+    T = 2
+    mi = make_multi_inputs(w, T, seed=1303, poison_padding=True)
+    md = to_dev(mi)
+    refm = oracle.decode_multi(mi["q"], mi["k"], mi["v"], mi["seq_lens"], mi["scale"])
+    print("case persistent multi", case, flush=True)
+    om = {s: binding.decode_multi(md["q"], md["k"], md["v"], md["seq_lens"], md["scale"], chunk=128, schedule=s)
+          for s in ("per_item", "persistent")}
+    torch.cuda.synchronize()
+    assert torch.equal(om["persistent"], om["per_item"])
+    check_close(om["persistent"], refm, "persistent multi %s" % case)
+
+
+def test_persistent_schedule_with_fewer_items_than_workgroups_and_a_larger_grid_after():
+    """Two items (fewer than the resident workgroups), then a grid of thousands: the queue left by
+    each call is back at zero for the next."""
+    small = Workload("persist-small", B=1, Hq=8, Hkv=2, D=64, Lmax=100, seed=1304, len_lo=1, len_hi=100)
+    big = PERSIST_CASES["gqa"]
+    for w in (small, big, small, big):
+        inp = make_inputs(w, poison_padding=True)
+        dev = to_dev(inp)
+        print("case persistent sequence", w.name, flush=True)
+        out = binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], chunk=128,
+                             schedule="persistent")
+        torch.cuda.synchronize()
+        ref = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+        check_close(out, ref, "persistent %s" % w.name)

@@ -424,3 +424,39 @@ def test_workspace_allocation_failure_is_reported(monkeypatch):
                                           ctypes.byref(opts)) == ERR_WORKSPACE
     # B == 0 never allocates
     assert call(q=0, k=0, v=0, lens=0, out=0, B=0, Lmax=4096, opts=opts) == OK
+
+
+def test_persistent_schedule_for_grids_of_many_items():
+    """The planner runs the split kernel persistent (a resident grid taking work items from a queue)
+    for grids of at least 2048 items, and one workgroup per item otherwise."""
+    ragged = binding.plan(256, 32, 8, 128, 8192)
+    assert ragged["persistent"] and ragged["grid_main"] >= 2048
+    assert binding.plan(256, 32, 8, 128, 8192, kv_format="fp8")["persistent"]
+    assert binding.plan(256, 32, 8, 128, 8192, window=4096)["persistent"]
+    for shape in ((64, 48, 1, 256, 2048), (4, 48, 1, 256, 131072), (32, 64, 8, 128, 4096), (1, 8, 1, 64, 128)):
+        p = binding.plan(*shape)
+        assert not p["persistent"] and p["grid_main"] < 2048, shape
+    # the fused merge and the vector kernel run one workgroup per item
+    assert not binding.plan(256, 32, 8, 128, 1024, chunk=128, combine="fused")["persistent"]
+    assert not binding.plan(256, 32, 8, 128, 8192, variant="valu")["persistent"]
+    # forced either way; the rest of the plan does not change
+    a = binding.plan(256, 32, 8, 128, 8192, schedule="per_item")
+    b = binding.plan(256, 32, 8, 128, 8192, schedule="persistent")
+    assert not a.pop("persistent") and b.pop("persistent")
+    assert a.pop("workspace_bytes") == b.pop("workspace_bytes") and a == b
+    assert binding.plan(64, 48, 1, 256, 2048, schedule="persistent")["persistent"]
+
+
+def test_schedule_option_checks():
+    assert call(opts=binding.make_opts(schedule=3)) == ERR_ARG
+    assert call(opts=binding.make_opts(schedule=-1)) == ERR_ARG
+    assert call(Lmax=1024, opts=binding.make_opts(chunk=128, combine=2, schedule=2)) == ERR_ARG
+    assert call(opts=binding.make_opts(variant="valu", schedule=2)) == ERR_ARG
+    with pytest.raises(binding.MqaError):
+        binding.plan(2, 8, 2, 128, 64, schedule=3)
+
+
+def test_noalloc_rejects_the_persistent_schedule():
+    """Its queue would need memory that starts at zero; the planner's choice falls back silently."""
+    assert call_noalloc(opts=binding.make_opts(schedule=2)) == ERR_ARG
+    assert call_noalloc(opts=binding.make_opts(schedule=2, chunk=128)) == ERR_ARG
