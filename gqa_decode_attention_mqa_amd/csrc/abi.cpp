@@ -503,6 +503,6 @@ mqa_status mqa_stream_read_probe(const void* buf, size_t bytes, int workgroups, 
     return MQA_OK;
 }
 
-int mqa_version(void) { return 150; }
+int mqa_version(void) { return 10600; }  // 1.6.0
 
 }  // extern "C"

@@ -28,7 +28,7 @@ def test_status_strings_and_version():
     for s in range(8):
         assert lib.mqa_status_string(s)
     assert lib.mqa_status_string(99) == b"unknown status"
-    assert lib.mqa_version() >= 100
+    assert lib.mqa_version() == 10600  # 1.6.0, as MAJOR*10000 + MINOR*100 + PATCH
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails its checks first
