@@ -122,8 +122,10 @@ struct MfmaCfg {
 // plain form (with the tail behind a run-time flag in one kernel, MI355X
 // measured 11 % slower 8-bit loops: int8 B=4 len 131072 86.6 against 78.0 us).
 // One work item: the (unit, chunk) of x-index bx and the head block by.
+// next != nullptr (persistent form): thread 0 also fetches the workgroup's
+// following item into *next, once its wave has its q.
 template <int D, int NG, int FMT, bool FUSED>
-__device__ __forceinline__ void decode_item(const DecodeArgs& a, long long bx, int by) {
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, long long bx, int by, long long* next) {
     using C = MfmaCfg<D, NG, FMT>;
     extern __shared__ __attribute__((aligned(256))) unsigned char smem[];
 
@@ -149,7 +151,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, long long bx, i
     qbase = __builtin_amdgcn_readfirstlane(qbase);
     const int gq = a.GT;  // query rows of the unit: T tokens times G heads
     const ChunkSpan span = chunk_span(a.window, a.chunk, a.max_splits, len, s);
-    if (s > 0 && span.p0 >= len) return;  // whole workgroup: this chunk is past the end
+    if (s > 0 && span.p0 >= len) {  // whole workgroup: this chunk is past the end
+        if (next != nullptr && tid == 0) *next = (long long)gridDim.x + atomicAdd(&a.queue[0], 1u);
+        return;
+    }
     // Sliding window: rows lo - 32 < t < lo of the first tile lie before it;
     // they are loaded as zeros and masked.
     const int lo = span.lo, p0 = span.p0, p1 = span.p1, nsplit = span.nsplit;
@@ -291,6 +296,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, long long bx, i
         // compiler that no load is pending into registers the loop reads.
         __builtin_amdgcn_s_waitcnt(kVmcntStages<0, 0>());
     }
+
+    // The fetch waits in the memory system behind other workgroups' fetches;
+    // issued here, after this wave's last wait for loads before the loop
+    // ends, it delays nothing until then.
+    if (next != nullptr && tid == 0) *next = (long long)gridDim.x + atomicAdd(&a.queue[0], 1u);
 
     // Issue a loader's share of the loads of tile `tile` into ring slot
     // tile % STAGES (compute waves issue nothing).  Load jj (0 .. LOADS-1)
@@ -854,7 +864,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, long long bx, i
 
 template <int D, int NG, int FMT, bool FUSED>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
-    decode_item<D, NG, FMT, FUSED>(a, blockIdx.x, blockIdx.y);
+    decode_item<D, NG, FMT, FUSED>(a, blockIdx.x, blockIdx.y, nullptr);
 }
 
 // Persistent form: gridDim.x workgroups (as many as are resident at once)
@@ -865,7 +875,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a) {
 // gridDim.x + k for k from the queue counter.  (Device-scope atomics on one
 // address are serialized; the static first item keeps them off the start of
 // the kernel's critical path.)  Thread 0 fetches the following item while the
-// current one runs; the item number reaches the other waves through the 16
+// current one runs (once its wave has q, or at once for a chunk past the
+// sequence's end); the item number reaches the other waves through the 16
 // bytes after the kernel's LDS block.  The last workgroup to leave puts both
 // counters back to zero for the next call.  Items do not depend on which
 // workgroup runs them, so the result is the plain form's, bit for bit.
@@ -876,15 +887,14 @@ __global__ __launch_bounds__(512) void decode_mfma_persistent_kernel(DecodeArgs 
     volatile long long* slot = reinterpret_cast<volatile long long*>(smem + C::LDS_BYTES);
     const int tid = threadIdx.x;
     long long item = blockIdx.x;
-    long long next = 0;
-    if (tid == 0 && item < a.items) next = (long long)gridDim.x + atomicAdd(&a.queue[0], 1u);
+    long long next;  // thread 0: the following item, fetched inside each item
     while (item < a.items) {
-        decode_item<D, NG, FMT, false>(a, item % a.grid_x, (int)(item / a.grid_x));
+        next = a.items;  // (every path through an item fetches; this only ends the loop if one did not)
+        decode_item<D, NG, FMT, false>(a, item % a.grid_x, (int)(item / a.grid_x), &next);
         __syncthreads();  // every wave is done with this item's LDS
         if (tid == 0) slot[0] = next;
         __syncthreads();
         item = slot[0];
-        if (tid == 0 && item < a.items) next = (long long)gridDim.x + atomicAdd(&a.queue[0], 1u);
     }
     if (tid == 0) {
         // every workgroup's last fetch came before its arrival here
