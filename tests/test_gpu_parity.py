@@ -1015,3 +1015,20 @@ def test_persistent_schedule_with_fewer_items_than_workgroups_and_a_larger_grid_
         torch.cuda.synchronize()
         ref = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
         check_close(out, ref, "persistent %s" % w.name)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,Lmax,seed", _random_shapes(10, 3))
+def test_random_shapes_persistent(B, Hq, Hkv, D, Lmax, seed):
+    """Seeded random shapes run persistent (forced: most of them have fewer items than resident
+    workgroups), bit for bit the per-item result, and within the oracle's tolerance."""
+    w = Workload("rand-persist", B=B, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, seed=seed, len_lo=0, len_hi=Lmax)
+    inp = make_inputs(w, poison_padding=True)
+    dev = to_dev(inp)
+    ref = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    for chunk in (None, 128):
+        print("case random persistent", B, Hq, Hkv, D, Lmax, seed, chunk, flush=True)
+        outs = [binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], chunk=chunk,
+                               variant="mfma", schedule=s) for s in ("per_item", "persistent")]
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1])
+        check_close(outs[1], ref, "random persistent chunk %s" % chunk)
