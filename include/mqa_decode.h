@@ -36,9 +36,10 @@
  * enqueued on `stream`.  Split-K scratch (partial outputs and log-sum-exps) is
  * owned by the library, cached per (device, stream), grown on demand with
  * hipMalloc (which synchronises the device) and freed by
- * mqa_release_workspaces(); so are the fused combine's counters, zeroed
- * once when allocated and left at zero by every call (up to a merge part
- * recorded by a wait that timed out, which a later call merges again).  Warm the
+ * mqa_release_workspaces(); so are the fused combine's counters and the
+ * persistent schedule's queue counters, zeroed once when allocated and left at
+ * zero by every call (up to a merge part recorded by a wait that timed out,
+ * which a later call merges again).  Warm the
  * library up with a call of the largest shape before capturing a graph.
  *
  * Errors: every argument check happens on the host before any HIP call, so
@@ -179,13 +180,16 @@ mqa_status mqa_decode_attention_ex(const void *q, const void *k_cache, const voi
  * the split-K partials live in a static device array of the library,
  * MQA_NOALLOC_SCRATCH_BYTES bytes on each device it runs on, held until the
  * process ends.  Arguments, semantics and results are those of
- * mqa_decode_attention_ex (the same kernels and plan, so the same bits), with
- * two extra checks made on the host before any HIP call:
+ * mqa_decode_attention_ex (the same kernels and plan, so the same bits; a grid
+ * the planner would run persistent runs one workgroup per work item here), with
+ * three extra checks made on the host before any HIP call:
  *   - a call whose split workspace (mqa_plan_info.workspace_bytes) exceeds
  *     MQA_NOALLOC_SCRATCH_BYTES is MQA_ERR_WORKSPACE (choose longer chunks, or
  *     use mqa_decode_attention_ex);
  *   - opts->combine == 2 (the fused merge, whose counters would have to
- *     start at zero) is MQA_ERR_ARG; the separate merge kernel is used.
+ *     start at zero) is MQA_ERR_ARG; the separate merge kernel is used;
+ *   - opts->schedule == 2 (the persistent schedule, whose queue counter would
+ *     have to start at zero) is MQA_ERR_ARG.
  * Every call on a device shares that device's scratch and leaves its contents
  * behind (nothing in it needs clearing: each call writes every partial it
  * reads).  Calls that overlap on one device (several streams, or several host
