@@ -1032,3 +1032,29 @@ def test_random_shapes_persistent(B, Hq, Hkv, D, Lmax, seed):
         torch.cuda.synchronize()
         assert torch.equal(outs[0], outs[1])
         check_close(outs[1], ref, "random persistent chunk %s" % chunk)
+
+
+def test_persistent_schedule_with_several_head_blocks():
+    """Items cover head blocks too (item = head block * grid_x + x): 128 heads per kv head take two
+    blocks of 96 and 32 rows, and two query tokens of 64 heads the same."""
+    w = Workload("persist-hb", B=3, Hq=128, Hkv=1, D=128, Lmax=1000, seed=1310, len_lo=1, len_hi=1000)
+    assert binding.plan(w.B, w.Hq, w.Hkv, w.D, w.Lmax, chunk=128, schedule="persistent")["head_blocks"] == 2
+    inp = make_inputs(w, poison_padding=True)
+    dev = to_dev(inp)
+    ref = oracle.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["scale"])
+    print("case persistent head blocks", flush=True)
+    outs = [binding.decode(dev["q"], dev["k"], dev["v"], dev["seq_lens"], dev["scale"], chunk=128, schedule=s)
+            for s in ("per_item", "persistent")]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    check_close(outs[1], ref, "persistent head blocks")
+    wm = Workload("persist-hb-multi", B=3, Hq=64, Hkv=1, D=128, Lmax=1000, seed=1311, len_lo=1, len_hi=1000)
+    mi = make_multi_inputs(wm, 2, poison_padding=True)
+    md = to_dev(mi)
+    refm = oracle.decode_multi(mi["q"], mi["k"], mi["v"], mi["seq_lens"], mi["scale"])
+    print("case persistent head blocks multi", flush=True)
+    om = [binding.decode_multi(md["q"], md["k"], md["v"], md["seq_lens"], md["scale"], chunk=128, schedule=s)
+          for s in ("per_item", "persistent")]
+    torch.cuda.synchronize()
+    assert torch.equal(om[0], om[1])
+    check_close(om[1], refm, "persistent head blocks multi")
