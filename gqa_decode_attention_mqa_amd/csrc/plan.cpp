@@ -294,8 +294,11 @@ mqa_status make_plan(int B, int Hq, int Hkv, int D, int Lmax, float scale,
     const long long items = p.grid_main * p.head_blocks;
     if (o.schedule == 2 && (p.variant != MQA_VARIANT_MFMA || p.combine == 2))
         return fail(MQA_ERR_ARG, "the persistent schedule needs the MFMA variant and the separate merge");
+    // its 32-bit queue counter must not wrap before every workgroup has seen the end
+    if (o.schedule == 2 && items >= kPersistMaxItems)
+        return fail(MQA_ERR_UNSUPPORTED, "too many work items for the persistent schedule");
     if (items > 0 && (o.schedule == 2 || (o.schedule == 0 && p.variant == MQA_VARIANT_MFMA && p.combine != 2 &&
-                                          items >= kPersistMinItems))) {
+                                          items >= kPersistMinItems && items < kPersistMaxItems))) {
         p.persist = 1;
         p.counters += kPersistCounters;  // the queue after the fused counters (none then)
     }

@@ -56,6 +56,7 @@ constexpr int kFusedCountersPerUnit = 4;
 // against 465; the PaLM-shaped MQA step, 256 items, 28.4 against 25.5).
 constexpr int kPersistCounters = 2;
 constexpr long long kPersistMinItems = 2048;
+constexpr long long kPersistMaxItems = 1LL << 31;  // the queue counter is 32 bits wide
 // How long a workgroup of the fused combine waits for the other chunks of its
 // unit before leaving its part of the merge to the last one: 20 us of the
 // 100 MHz real-time counter.  MQA_FUSED_WAIT_TICKS overrides it (tests force

@@ -130,9 +130,10 @@ typedef struct mqa_decode_opts {
                              workgroups), 2 = persistent: as many workgroups as the GPU
                              holds at once take items in order from a queue counter in the
                              call's workspace (MFMA variant and separate merge only, else
-                             MQA_ERR_ARG; not with mqa_decode_attention_noalloc).  The
-                             planner picks 2 for grids of at least 2048 items.  Both give
-                             the same bits.                                                */
+                             MQA_ERR_ARG; fewer than 2^31 items, else MQA_ERR_UNSUPPORTED;
+                             not with mqa_decode_attention_noalloc).  The planner picks 2
+                             for grids of 2048 to 2^31 - 1 items.  Both give the same
+                             bits.                                                         */
 } mqa_decode_opts;
 
 /* What the planner decided for a shape (host-only query, no HIP call). */

@@ -447,6 +447,16 @@ def test_persistent_schedule_for_grids_of_many_items():
     assert binding.plan(64, 48, 1, 256, 2048, schedule="persistent")["persistent"]
 
 
+def test_persistent_schedule_stays_within_its_32_bit_queue():
+    """A grid of 2^31 items or more (here 2^24 - 1 split workgroups times 129 head blocks) runs one
+    workgroup per item; forcing the persistent schedule on it is refused."""
+    p = binding.plan(16777215, 12384, 1, 64, 128)
+    assert p["head_blocks"] == 129 and p["grid_main"] >= 2 ** 31 and not p["persistent"]
+    with pytest.raises(binding.MqaError):
+        binding.plan(16777215, 12384, 1, 64, 128, schedule="persistent")
+    assert binding.plan(16777215, 12288, 1, 64, 128)["persistent"]  # 2^31 - 128 items
+
+
 def test_schedule_option_checks():
     assert call(opts=binding.make_opts(schedule=3)) == ERR_ARG
     assert call(opts=binding.make_opts(schedule=-1)) == ERR_ARG
